@@ -1,0 +1,214 @@
+"""fp64 CPU oracle of the speculative-decoding verify step (ctypes wrapper of oracle.c).
+
+TEST INFRASTRUCTURE ONLY: tests/, __graft_entry__.smoke() and the cpu_baseline
+leg of bench.py are the only callers.  It shares no code with the HIP library
+and never imports it.  See oracle.c for the definitions and their sources.
+
+Pins (tests/test_oracle_*.py): Philox against NumPy's independent Philox and the
+published known answer; the tree mask against the worked example of the
+textbook page ("Token tree and tree attention" box) and the Cartesian counts of
+the Medusa page; attention against torch's float64 scaled_dot_product_attention
+on CPU and against per-path brute force; acceptance against the three-token
+worked example, alpha = 1 - TV, the special cases, chi-square of the output law
+and E[J] = sum_i prod_{j<=i} alpha_j; the tree walk against brute force and the
+closed-form node-acceptance probabilities.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_SO = os.path.join(_HERE, "liboracle.so")
+
+TAG_ACCEPT = 0x53560001
+TAG_WALK = 0x53560002
+GREEDY, SAMPLE = 0, 1
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc (fp64, no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_SO):
+        tmp = _SO + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+                               "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _SO)
+    return _SO
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO):
+            build()
+        _lib = _typed(ctypes.CDLL(_SO))
+    return _lib
+
+
+def _typed(L):
+    P = ctypes.c_void_p
+    i32, i64, u64, f32, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float, ctypes.c_double
+    L.orc_philox4x64_10.argtypes = [P, P, P]
+    L.orc_philox4x64_10.restype = None
+    L.orc_uniform.argtypes = [u64, u64, u64, u64, u64]
+    L.orc_uniform.restype = f64
+    L.orc_tree_mask.argtypes = [P, i32, i32, P, i32, P, P]
+    L.orc_tree_mask.restype = i32
+    L.orc_attention.argtypes = [i32, i32, i32, i32, i32, i32, f64, i32, P, i64, i64, i64, P, P, P,
+                                i64, i64, P, P, i64, i32, P, i64, P, P]
+    L.orc_attention.restype = i32
+    L.orc_spec_accept.argtypes = [i32, i32, i32, i32, f32, P, P, P, u64, u64, P, P, P, P, P]
+    L.orc_spec_accept.restype = i32
+    L.orc_tree_walk.argtypes = [i32, i32, i32, i32, i32, f32, P, P, P, u64, u64, P, P, P, P, P]
+    L.orc_tree_walk.restype = i32
+    return L
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def set_threads(n: int) -> None:
+    """Threads for the OpenMP loops over independent outputs (OMP_NUM_THREADS)."""
+    try:
+        import ctypes.util
+        gomp = ctypes.CDLL(ctypes.util.find_library("gomp") or "libgomp.so.1")
+        gomp.omp_set_num_threads(int(n))
+    except OSError:
+        os.environ["OMP_NUM_THREADS"] = str(int(n))
+
+
+# --------------------------------------------------------------------------- #
+def philox4x64_10(counter, key) -> np.ndarray:
+    c = _c(counter, np.uint64)
+    k = _c(key, np.uint64)
+    out = np.zeros(4, dtype=np.uint64)
+    lib().orc_philox4x64_10(_p(c), _p(k), _p(out))
+    return out
+
+
+def uniform(seed: int, c0: int, step: int, stream: int, tag: int) -> float:
+    return lib().orc_uniform(seed, c0, step, stream, tag)
+
+
+def tree_mask(parents, prefix_len: int):
+    """-> (bits uint32 [n][ceil(n/32)], depth int32 [n], pos int64 [n]); raises on a bad parent."""
+    par = _c(parents, np.int32)
+    n = len(par)
+    words = (n + 31) // 32
+    bits = np.zeros((n, words), dtype=np.uint32)
+    depth = np.zeros(n, dtype=np.int32)
+    pos = np.zeros(n, dtype=np.int64)
+    st = lib().orc_tree_mask(_p(par), n, int(prefix_len), _p(bits), words, _p(depth), _p(pos))
+    if st != 0:
+        raise ValueError("bad parent at node %d" % (st - 1))
+    return bits, depth, pos
+
+
+def dense_mask(bits: np.ndarray, n: int, prefix_len: int) -> np.ndarray:
+    """Expand bit rows to the boolean (n, P + n) mask (prefix block all ones)."""
+    j = np.arange(n)
+    node = ((bits[:, j >> 5] >> (j & 31).astype(np.uint32)) & 1).astype(bool)
+    return np.concatenate([np.ones((n, prefix_len), dtype=bool), node], axis=1)
+
+
+def attention(inp: dict, *, scale: float, tree_bits=None, tree_sb: int = 0, rows=None):
+    """fp64 attention for the listed (b, i, h) rows (all rows when None).
+
+    ``inp`` is a synth.attention_inputs dict (float32 or bf16-bit arrays).
+    Returns (out [n_rows][D] float64, lse [n_rows] float64, rows int32 [n_rows][3]).
+    """
+    B, n_q, Hq, Hkv, D = inp["B"], inp["n_q"], inp["Hq"], inp["Hkv"], inp["D"]
+    dt = 0 if inp["dtype"] == "f32" else 1
+    edt = np.float32 if dt == 0 else np.uint16
+    q, k, v = _c(inp["q"], edt), _c(inp["k"], edt), _c(inp["v"], edt)
+    if rows is None:
+        bb, ii, hh = np.meshgrid(np.arange(B), np.arange(n_q), np.arange(Hq), indexing="ij")
+        rows = np.stack([bb.ravel(), ii.ravel(), hh.ravel()], axis=1)
+    rows = _c(rows, np.int32).reshape(-1, 3)
+    nr = rows.shape[0]
+    out = np.zeros((nr, D), dtype=np.float64)
+    lse = np.zeros(nr, dtype=np.float64)
+    kv_off = _c(inp["kv_off"], np.int64)
+    pl = _c(inp["prefix_len"], np.int32)
+    tb = None if tree_bits is None else _c(tree_bits, np.uint32)
+    words = 0 if tb is None else tb.shape[-1]
+    st = lib().orc_attention(dt, B, n_q, Hq, Hkv, D, float(scale), 0 if tb is None else 1,
+                             _p(q), inp["q_sb"], inp["q_st"], inp["q_sh"], _p(k), _p(v), _p(kv_off),
+                             inp["kv_sh"], inp["kv_st"], _p(pl), _p(tb), int(tree_sb), words,
+                             _p(rows), nr, _p(out), _p(lse))
+    if st != 0:
+        raise ValueError("orc_attention status %d" % st)
+    return out, lse, rows
+
+
+def compile_variant(replacements: dict, tag: str):
+    """Build a copy of oracle.c with literal source replacements into a temporary
+    library (used by tests that plant a known mistake in the oracle, on the CPU).
+    Every replacement must match exactly once.  Returns a loaded ctypes handle."""
+    import tempfile
+    src = open(_SRC).read()
+    for old, new in replacements.items():
+        if src.count(old) != 1:
+            raise ValueError("replacement must match exactly once: %r" % old)
+        src = src.replace(old, new)
+    d = tempfile.mkdtemp(prefix="oracle_%s_" % tag)
+    c, so = os.path.join(d, "variant.c"), os.path.join(d, "libvariant.so")
+    with open(c, "w") as f:
+        f.write(src)
+    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared", "-o", so, c, "-lm"])
+    return _typed(ctypes.CDLL(so))
+
+
+def spec_accept(mode: int, target, draft, draft_tokens, temperature: float, seed: int, step: int = 0,
+                stream_ids=None, want_alpha: bool = False, handle=None):
+    """-> dict(accept_len [B], out_tokens [B][gamma+1], alpha [B][gamma] or None, flags [B])."""
+    tgt = _c(target, np.float32)
+    B, g1, V = tgt.shape
+    gamma = g1 - 1
+    dr = None if draft is None else _c(draft, np.float32)
+    if dr is None and not (mode == GREEDY or temperature == 0.0):
+        raise ValueError("sampling needs draft logits")
+    toks = _c(draft_tokens, np.int32).reshape(B, gamma)
+    sid = None if stream_ids is None else _c(stream_ids, np.uint64)
+    acc = np.zeros(B, dtype=np.int32)
+    out = np.zeros((B, gamma + 1), dtype=np.int32)
+    alpha = np.zeros((B, gamma), dtype=np.float64) if want_alpha else None
+    flags = np.zeros(B, dtype=np.int32)
+    st = (handle or lib()).orc_spec_accept(int(mode), B, gamma, V, float(temperature), _p(tgt), _p(dr), _p(toks),
+                               int(seed), int(step), _p(sid), _p(acc), _p(out), _p(alpha), _p(flags))
+    if st != 0:
+        raise ValueError("orc_spec_accept status %d" % st)
+    return dict(accept_len=acc, out_tokens=out, alpha=alpha, flags=flags)
+
+
+def tree_walk(mode: int, logits, tokens, parents, temperature: float, seed: int, step: int = 0,
+              stream_ids=None, max_depth=None):
+    """-> dict(accept_len [B], path [B][max_depth+1], out_tokens [B][max_depth+1], flags [B])."""
+    lg = _c(logits, np.float32)
+    B, n, V = lg.shape
+    tk = _c(tokens, np.int32).reshape(B, n)
+    par = _c(parents, np.int32)
+    if max_depth is None:
+        _, depth, _ = tree_mask(par, 0)
+        max_depth = int(depth.max())
+    sid = None if stream_ids is None else _c(stream_ids, np.uint64)
+    acc = np.zeros(B, dtype=np.int32)
+    path = np.zeros((B, max_depth + 1), dtype=np.int32)
+    out = np.zeros((B, max_depth + 1), dtype=np.int32)
+    flags = np.zeros(B, dtype=np.int32)
+    st = lib().orc_tree_walk(int(mode), B, n, V, int(max_depth), float(temperature), _p(lg), _p(tk), _p(par),
+                             int(seed), int(step), _p(sid), _p(acc), _p(path), _p(out), _p(flags))
+    if st != 0:
+        raise ValueError("orc_tree_walk status %d" % st)
+    return dict(accept_len=acc, path=path, out_tokens=out, flags=flags)

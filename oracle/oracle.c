@@ -1,0 +1,409 @@
+/*
+ * oracle.c -- plain, slow, fp64 CPU oracle for the speculative-decoding verify step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and the
+ * cpu_baseline leg of bench.py may load this library.  It shares no code,
+ * header, table or helper with the HIP library under
+ * draft_token_verification_attention_amd/, and neither side includes the other.
+ *
+ * Sources (the pages this follows, cited by title and section):
+ *   [TB]  "Speculative decoding", Zero to Frontier textbook, chapter 20, section 20.5.
+ *   [MED] "Speculative-Decoding" (s1mplewind blog, Medusa reading notes).
+ *   [AG]  "Speculative Decoding: The Art of Guessing Well" (astralord blog).
+ *   [PHX] Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11
+ *         (the Philox4x64-10 generator; the pages name no generator).
+ *
+ * Every floating-point quantity is computed in double precision.  Logits arrive
+ * as fp32 and attention inputs as fp32 or bf16; both widen exactly to double.
+ * Loops are the definitions written out: no blocking, no fusion, no reordering
+ * beyond what the definition states.  OpenMP is used only across independent
+ * outputs (sequences, attention rows); it never splits a single sum.
+ *
+ * Pins: every function here is pinned by tests in tests/test_oracle_*.py
+ * against values the pages print, closed forms, library routines and brute force.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_EXPORT __attribute__((visibility("default")))
+
+/* ------------------------------------------------------------------------- */
+/* Philox4x64-10 [PHX].  A counter-based generator: block = f_key(counter).   */
+/* Round: two 64x64->128 products of counter words 0 and 2 with fixed          */
+/* multipliers, XOR-mixed with the other words and the key; the key is bumped  */
+/* by two Weyl constants between rounds.  Constants are the published ones.    */
+/* ------------------------------------------------------------------------- */
+static const uint64_t PHX_M0 = 0xD2E7470EE14C6C93ULL;
+static const uint64_t PHX_M1 = 0xCA5A826395121157ULL;
+static const uint64_t PHX_W0 = 0x9E3779B97F4A7C15ULL; /* golden ratio */
+static const uint64_t PHX_W1 = 0xBB67AE8584CAA73BULL; /* sqrt(3) - 1 */
+
+ORC_EXPORT void orc_philox4x64_10(const uint64_t ctr_in[4], const uint64_t key_in[2], uint64_t out[4])
+{
+    uint64_t c0 = ctr_in[0], c1 = ctr_in[1], c2 = ctr_in[2], c3 = ctr_in[3];
+    uint64_t k0 = key_in[0], k1 = key_in[1];
+    for (int round = 0; round < 10; ++round) {
+        unsigned __int128 p0 = (unsigned __int128)PHX_M0 * c0;
+        unsigned __int128 p1 = (unsigned __int128)PHX_M1 * c2;
+        uint64_t hi0 = (uint64_t)(p0 >> 64), lo0 = (uint64_t)p0;
+        uint64_t hi1 = (uint64_t)(p1 >> 64), lo1 = (uint64_t)p1;
+        uint64_t n0 = hi1 ^ c1 ^ k0;
+        uint64_t n1 = lo1;
+        uint64_t n2 = hi0 ^ c3 ^ k1;
+        uint64_t n3 = lo0;
+        c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+        k0 += PHX_W0;
+        k1 += PHX_W1;
+    }
+    out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* Uniform on (0,1) from the first output word: (2*(w0>>12)+1) * 2^-53.
+ * Every value is exact in double, never 0 and never 1.
+ * Counter = (c0, step, stream, tag), key = (seed, 0).                          */
+ORC_EXPORT double orc_uniform(uint64_t seed, uint64_t c0, uint64_t step, uint64_t stream, uint64_t tag)
+{
+    uint64_t ctr[4] = {c0, step, stream, tag};
+    uint64_t key[2] = {seed, 0};
+    uint64_t out[4];
+    orc_philox4x64_10(ctr, key, out);
+    return (double)(2 * (out[0] >> 12) + 1) * 0x1p-53;
+}
+
+#define ORC_TAG_ACCEPT 0x53560001ULL
+#define ORC_TAG_WALK   0x53560002ULL
+#define ORC_NEAR       1e-6
+
+/* ------------------------------------------------------------------------- */
+/* Token tree -> ancestor-or-self mask, depth and position ids.               */
+/* [TB] section "Token trees check several guesses at once", box "Token tree  */
+/* and tree attention", and the exercise "The tree attention mask": par(i) is  */
+/* -1 or an earlier node; node i sees every prefix position, itself and its    */
+/* ancestors; depth = number of ancestors; position id = P + depth.            */
+/* bits: n rows of `words` uint32; bit (j%32) of word j/32 of row i is set iff */
+/* j == i or j is an ancestor of i.  Returns 0, or 1 + the first bad node.     */
+/* ------------------------------------------------------------------------- */
+ORC_EXPORT int32_t orc_tree_mask(const int32_t *parents, int32_t n, int32_t prefix_len,
+                                 uint32_t *bits, int32_t words, int32_t *depth, int64_t *pos)
+{
+    for (int32_t i = 0; i < n; ++i)
+        if (parents[i] < -1 || parents[i] >= i) return i + 1;
+    for (int32_t i = 0; i < n; ++i) {
+        depth[i] = parents[i] < 0 ? 0 : depth[parents[i]] + 1;
+        pos[i] = (int64_t)prefix_len + depth[i];
+        uint32_t *row = bits + (int64_t)i * words;
+        for (int32_t w = 0; w < words; ++w) row[w] = 0;
+        for (int32_t j = i; j >= 0; j = parents[j])      /* self, then each ancestor */
+            row[j >> 5] |= 1u << (j & 31);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Verify attention, fp64.                                                    */
+/* [TB] section "Checking several tokens costs about as much as writing one": */
+/* each new token attends to the whole cache and to the new tokens before it   */
+/* (a causal mask aligned to the bottom-right corner).  Trees: box "Token tree */
+/* and tree attention" -- every prefix position plus ancestors-or-self.        */
+/* Query head h reads KV head h / G with G = Hq / Hkv (grouped queries).       */
+/* Softmax: s_j = scale*<q,k_j>, m = max s, w = exp(s - m),                    */
+/* o = sum w v / sum w, lse = m + log(sum w).                                  */
+/* dtype: 0 = fp32, 1 = bf16 (raw 16-bit patterns; widened exactly).           */
+/* Rows: a list of (b, i, h) triples; out is [n_rows][D], lse [n_rows].        */
+/* ------------------------------------------------------------------------- */
+static double widen(const void *base, int dtype, int64_t idx)
+{
+    if (dtype == 0) return (double)((const float *)base)[idx];
+    uint32_t u = (uint32_t)((const uint16_t *)base)[idx] << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+ORC_EXPORT int32_t orc_attention(int32_t dtype, int32_t B, int32_t n_q, int32_t Hq, int32_t Hkv, int32_t D,
+                                 double scale, int32_t tree,
+                                 const void *q, int64_t q_sb, int64_t q_st, int64_t q_sh,
+                                 const void *k, const void *v, const int64_t *kv_off,
+                                 int64_t kv_sh, int64_t kv_st,
+                                 const int32_t *prefix_len,
+                                 const uint32_t *tree_bits, int64_t tree_sb, int32_t words,
+                                 const int32_t *rows, int64_t n_rows,
+                                 double *out, double *lse)
+{
+    if (Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || n_q <= 0) return 1;
+    const int32_t G = Hq / Hkv;
+    int32_t bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        const int32_t b = rows[3 * r], i = rows[3 * r + 1], h = rows[3 * r + 2];
+        if (b < 0 || b >= B || i < 0 || i >= n_q || h < 0 || h >= Hq) {
+#pragma omp atomic write
+            bad = 1;
+            continue;
+        }
+        const int32_t g = h / G;
+        const int64_t P = prefix_len[b];
+        const int64_t nkeys = P + n_q;
+        const int64_t qbase = (int64_t)b * q_sb + (int64_t)i * q_st + (int64_t)h * q_sh;
+        const int64_t kvbase = kv_off[b] + (int64_t)g * kv_sh;
+        const uint32_t *mrow = tree ? tree_bits + (int64_t)b * tree_sb + (int64_t)i * words : NULL;
+        double *o = out + r * D;
+        double *s = (double *)malloc(sizeof(double) * (size_t)nkeys);
+        char *vis = (char *)malloc((size_t)nkeys);
+        double m = -INFINITY;
+        for (int64_t t = 0; t < nkeys; ++t) {
+            int visible;
+            if (t < P) visible = 1;
+            else {
+                int64_t j = t - P;
+                visible = tree ? (int)((mrow[j >> 5] >> (j & 31)) & 1u) : (j <= i);
+            }
+            vis[t] = (char)visible;
+            if (!visible) continue;
+            double dot = 0.0;
+            for (int32_t d = 0; d < D; ++d)
+                dot += widen(q, dtype, qbase + d) * widen(k, dtype, kvbase + t * kv_st + d);
+            s[t] = scale * dot;
+            if (s[t] > m) m = s[t];
+        }
+        double l = 0.0;
+        for (int32_t d = 0; d < D; ++d) o[d] = 0.0;
+        for (int64_t t = 0; t < nkeys; ++t) {
+            if (!vis[t]) continue;
+            double w = exp(s[t] - m);
+            l += w;
+            for (int32_t d = 0; d < D; ++d) o[d] += w * widen(v, dtype, kvbase + t * kv_st + d);
+        }
+        for (int32_t d = 0; d < D; ++d) o[d] /= l;
+        if (lse) lse[r] = m + log(l);
+        free(s);
+        free(vis);
+    }
+    return bad ? 2 : 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Temperature softmax of one fp32 logit row, in double:                      */
+/* p(x) = exp((l(x) - max l)/tau) / sum_x' exp((l(x') - max l)/tau).          */
+/* [TB] section "When the target samples...": both models sample at the same  */
+/* temperature tau; tau -> 0 is the argmax.                                    */
+/* ------------------------------------------------------------------------- */
+static void softmax_row(const float *logits, int32_t V, double tau, double *p)
+{
+    double m = -INFINITY;
+    for (int32_t x = 0; x < V; ++x) if ((double)logits[x] > m) m = (double)logits[x];
+    double z = 0.0;
+    for (int32_t x = 0; x < V; ++x) { p[x] = exp(((double)logits[x] - m) / tau); z += p[x]; }
+    for (int32_t x = 0; x < V; ++x) p[x] /= z;
+}
+
+/* First index of the largest raw logit (ties go to the lowest token id).     */
+static int32_t argmax_row(const float *logits, int32_t V)
+{
+    int32_t best = 0;
+    for (int32_t x = 1; x < V; ++x) if (logits[x] > logits[best]) best = x;
+    return best;
+}
+
+/* Inverse CDF in ascending token-id order: the smallest y with C_y > u * Z,
+ * C the running sum of w, Z the total.  *near is set when u*Z lies within
+ * 1e-6*Z of C_{y-1} or C_y (a draw whose token could flip under rounding).
+ * Returns -1 when Z is not positive.                                          */
+static int32_t inverse_cdf(const double *w, int32_t V, double u, int32_t *near)
+{
+    double z = 0.0;
+    for (int32_t x = 0; x < V; ++x) z += w[x];
+    if (!(z > 0.0)) return -1;
+    const double target = u * z;
+    double c = 0.0, prev = 0.0;
+    int32_t y = -1;
+    for (int32_t x = 0; x < V; ++x) {
+        prev = c;
+        c += w[x];
+        if (c > target) { y = x; break; }
+    }
+    if (y < 0) { /* rounding left the total just below u*Z: take the last token with mass */
+        for (int32_t x = V - 1; x >= 0; --x) if (w[x] > 0.0) { y = x; break; }
+        prev = c;
+    }
+    if (near) *near = (fabs(target - prev) < ORC_NEAR * z) || (fabs(c - target) < ORC_NEAR * z);
+    return y;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Acceptance of one round, per sequence.                                     */
+/*                                                                             */
+/* GREEDY (mode 0) -- [TB] box "A round of greedy speculative decoding":       */
+/*   z_i = argmax of target row i (raw logits; ties -> lowest id),             */
+/*   J = number of leading drafts with x_i == z_i, emit x_1..x_J then z_{J+1}. */
+/*   Draft logits are not read and no uniform is drawn.                        */
+/*                                                                             */
+/* SAMPLE (mode 1) -- [TB] box "A round of speculative sampling" and box       */
+/* "The speculative sampling rule"; [AG] section "Speculative sampling":       */
+/*   p_i = softmax(target_i / tau), q_i = softmax(draft_i / tau);             */
+/*   for i = 0..gamma-1 in order, u_i = U(seed; i, step, stream, ACCEPT);      */
+/*   accept x_i iff u_i * q_i(x_i) < p_i(x_i) (u < p/q written without a       */
+/*   division; a token with q = 0 is never drafted, and then the test passes   */
+/*   iff p > 0); stop at the first failure; J = number accepted.               */
+/*   The extra token is drawn from r = max(0, p_J - q_J), or from p_gamma     */
+/*   when J = gamma (a zero draft row after the last draft, as in the          */
+/*   "Speculative verification in PyTorch" section), by inverse CDF with the   */
+/*   dedicated uniform u* = U(seed; gamma, step, stream, ACCEPT).              */
+/*   A zero residual (impossible in exact arithmetic after a rejection) falls  */
+/*   back to p_J.                                                              */
+/* tau == 0 in SAMPLE mode is treated as GREEDY ([TB]: tau -> 0 is greedy).    */
+/*                                                                             */
+/* Outputs: accept_len[B]; out_tokens[B][gamma+1] (J drafts, the extra token,  */
+/* then -1); alpha[B][gamma] = sum_x min(p_i, q_i) when non-null (SAMPLE);     */
+/* flags[B]: bit0 = an evaluated ratio test had |u - p/q| < 1e-6,              */
+/* bit1 = the extra draw lay within 1e-6*Z of a CDF boundary.                  */
+/* ------------------------------------------------------------------------- */
+ORC_EXPORT int32_t orc_spec_accept(int32_t mode, int32_t B, int32_t gamma, int32_t V, float temperature,
+                                   const float *target, const float *draft, const int32_t *draft_tokens,
+                                   uint64_t seed, uint64_t step, const uint64_t *stream_ids,
+                                   int32_t *accept_len, int32_t *out_tokens, double *alpha, int32_t *flags)
+{
+    if (B < 0 || gamma < 0 || V <= 0) return 1;
+    const int greedy = (mode == 0) || (temperature == 0.0f);
+    const double tau = (double)temperature;
+    int32_t bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int32_t b = 0; b < B; ++b) {
+        const float *tb = target + (int64_t)b * (gamma + 1) * V;
+        const int32_t *xb = draft_tokens + (int64_t)b * gamma;
+        int32_t *ob = out_tokens + (int64_t)b * (gamma + 1);
+        int32_t fl = 0;
+        for (int32_t i = 0; i < gamma; ++i)
+            if (xb[i] < 0 || xb[i] >= V) {
+#pragma omp atomic write
+                bad = 1;
+            }
+        for (int32_t i = 0; i <= gamma; ++i) ob[i] = -1;
+        if (greedy) {
+            int32_t J = 0;
+            while (J < gamma && xb[J] == argmax_row(tb + (int64_t)J * V, V)) ++J;
+            for (int32_t i = 0; i < J; ++i) ob[i] = xb[i];
+            ob[J] = argmax_row(tb + (int64_t)J * V, V);
+            accept_len[b] = J;
+            if (flags) flags[b] = 0;
+            if (alpha) for (int32_t i = 0; i < gamma; ++i) alpha[(int64_t)b * gamma + i] = NAN;
+            continue;
+        }
+        const float *db = draft + (int64_t)b * gamma * V;
+        const uint64_t stream = stream_ids ? stream_ids[b] : (uint64_t)b;
+        double *p = (double *)malloc(sizeof(double) * (size_t)V);
+        double *q = (double *)malloc(sizeof(double) * (size_t)V);
+        if (alpha) {
+            for (int32_t i = 0; i < gamma; ++i) {
+                softmax_row(tb + (int64_t)i * V, V, tau, p);
+                softmax_row(db + (int64_t)i * V, V, tau, q);
+                double a = 0.0;
+                for (int32_t x = 0; x < V; ++x) a += fmin(p[x], q[x]);
+                alpha[(int64_t)b * gamma + i] = a;
+            }
+        }
+        int32_t J = 0;
+        for (; J < gamma; ++J) {
+            softmax_row(tb + (int64_t)J * V, V, tau, p);
+            softmax_row(db + (int64_t)J * V, V, tau, q);
+            const int32_t x = xb[J];
+            const double u = orc_uniform(seed, (uint64_t)J, step, stream, ORC_TAG_ACCEPT);
+            const double px = p[x], qx = q[x];
+            if (qx > 0.0 && fabs(u - px / qx) < ORC_NEAR) fl |= 1;
+            if (!(u * qx < px)) break;
+        }
+        /* the extra token */
+        softmax_row(tb + (int64_t)J * V, V, tau, p);
+        if (J < gamma) {
+            softmax_row(db + (int64_t)J * V, V, tau, q);
+            for (int32_t x = 0; x < V; ++x) q[x] = fmax(0.0, p[x] - q[x]);
+        } else {
+            memcpy(q, p, sizeof(double) * (size_t)V);
+        }
+        const double ustar = orc_uniform(seed, (uint64_t)gamma, step, stream, ORC_TAG_ACCEPT);
+        int32_t near = 0;
+        int32_t y = inverse_cdf(q, V, ustar, &near);
+        if (y < 0) y = inverse_cdf(p, V, ustar, &near);
+        if (near) fl |= 2;
+        for (int32_t i = 0; i < J; ++i) ob[i] = xb[i];
+        ob[J] = y;
+        accept_len[b] = J;
+        if (flags) flags[b] = fl;
+        free(p);
+        free(q);
+    }
+    return bad ? 2 : 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Tree walk, per sequence.                                                   */
+/* Node 0 is the root (the last committed token, parent -1); logits row v is   */
+/* the target's next-token distribution after node v.  Starting at v = 0, for  */
+/* d = 0, 1, ...: y = argmax of row v (GREEDY) or an inverse-CDF draw from     */
+/* softmax(row v / tau) with u = U(seed; d, step, stream, WALK) (SAMPLE);      */
+/* move to the first child of v (in node order) whose token is y; when there   */
+/* is none, emit y and stop.                                                   */
+/* GREEDY: [TB] section "Token trees check several guesses at once" (the walk  */
+/* after the mask exercise).  SAMPLE: [MED] section "Attention Tree" -- sample */
+/* from the target at the node, look for that token among the children, and    */
+/* go down level by level until no child matches.                              */
+/* Outputs: accept_len[B] = J; path[B][max_depth+1] = (0, n_1, ..., n_J, -1..);*/
+/* out_tokens[B][max_depth+1] = (tokens of n_1..n_J, y, -1..); flags[B] bit1   */
+/* = some draw lay within 1e-6*Z of a CDF boundary.                            */
+/* Returns 0; 3 if a walk would pass max_depth; 2 on a bad token/parent.       */
+/* ------------------------------------------------------------------------- */
+ORC_EXPORT int32_t orc_tree_walk(int32_t mode, int32_t B, int32_t n, int32_t V, int32_t max_depth,
+                                 float temperature, const float *logits, const int32_t *tokens,
+                                 const int32_t *parents, uint64_t seed, uint64_t step,
+                                 const uint64_t *stream_ids, int32_t *accept_len, int32_t *path,
+                                 int32_t *out_tokens, int32_t *flags)
+{
+    if (B < 0 || n <= 0 || V <= 0 || max_depth < 0) return 1;
+    if (parents[0] != -1) return 2;
+    for (int32_t i = 1; i < n; ++i) if (parents[i] < -1 || parents[i] >= i) return 2;
+    const int greedy = (mode == 0) || (temperature == 0.0f);
+    const double tau = (double)temperature;
+    int32_t status = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int32_t b = 0; b < B; ++b) {
+        const float *lb = logits + (int64_t)b * n * V;
+        const int32_t *tk = tokens + (int64_t)b * n;
+        int32_t *pb = path + (int64_t)b * (max_depth + 1);
+        int32_t *ob = out_tokens + (int64_t)b * (max_depth + 1);
+        const uint64_t stream = stream_ids ? stream_ids[b] : (uint64_t)b;
+        double *p = greedy ? NULL : (double *)malloc(sizeof(double) * (size_t)V);
+        for (int32_t d = 0; d <= max_depth; ++d) { pb[d] = -1; ob[d] = -1; }
+        int32_t fl = 0, v = 0, d = 0;
+        pb[0] = 0;
+        for (;;) {
+            const float *row = lb + (int64_t)v * V;
+            int32_t y;
+            if (greedy) y = argmax_row(row, V);
+            else {
+                softmax_row(row, V, tau, p);
+                int32_t near = 0;
+                y = inverse_cdf(p, V, orc_uniform(seed, (uint64_t)d, step, stream, ORC_TAG_WALK), &near);
+                if (near) fl |= 2;
+            }
+            int32_t child = -1;
+            for (int32_t c = v + 1; c < n; ++c)
+                if (parents[c] == v && tk[c] == y) { child = c; break; }
+            if (child < 0) { ob[d] = y; break; }
+            if (d + 1 > max_depth) {
+#pragma omp atomic write
+                status = 3;
+                break;
+            }
+            ob[d] = tk[child];
+            v = child;
+            ++d;
+            pb[d] = child;
+        }
+        accept_len[b] = d;
+        if (flags) flags[b] = fl;
+        free(p);
+    }
+    return status;
+}
