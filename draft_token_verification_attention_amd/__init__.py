@@ -1,0 +1,255 @@
+"""Python binding of libspecverify (the verify step of speculative decoding, HIP on gfx950).
+
+Argument marshalling only: every step of the path runs in the library's kernels.
+PyTorch supplies device memory and the current HIP stream.  The names mirror the
+C entry points declared in include/specverify.h.
+
+The library must be built in-tree (``python -m draft_token_verification_attention_amd._build``);
+importing this package without it raises ImportError -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libspecverify.so")
+
+SV_OK, SV_ERR_INVALID_ARG, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_HIP = range(5)
+SV_F32, SV_BF16 = 0, 1
+SV_GREEDY, SV_SAMPLE = 0, 1
+SV_MASK_CAUSAL, SV_MASK_TREE = 0, 1
+
+_P = ctypes.c_void_p
+_i32, _i64, _u64, _f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float
+
+
+class sv_philox(ctypes.Structure):
+    _fields_ = [("seed", _u64), ("step", _u64), ("stream_ids", _P)]
+
+
+class sv_attn_desc(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int), ("mask", ctypes.c_int),
+                ("B", _i32), ("n_q", _i32), ("Hq", _i32), ("Hkv", _i32), ("D", _i32),
+                ("max_prefix", _i32), ("split_keys", _i32), ("scale", _f32),
+                ("q", _P), ("q_sb", _i64), ("q_st", _i64), ("q_sh", _i64),
+                ("k", _P), ("v", _P), ("kv_off", _P), ("kv_sh", _i64), ("kv_st", _i64),
+                ("prefix_len", _P), ("tree_bits", _P), ("tree_sb", _i64),
+                ("out", _P), ("o_sb", _i64), ("o_st", _i64), ("o_sh", _i64), ("lse", _P)]
+
+
+class sv_accept_desc(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int), ("B", _i32), ("gamma", _i32), ("V", _i32), ("temperature", _f32),
+                ("target_logits", _P), ("draft_logits", _P), ("draft_tokens", _P), ("rng", sv_philox),
+                ("accept_len", _P), ("out_tokens", _P), ("alpha", _P), ("dev_status", _P)]
+
+
+class sv_walk_desc(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int), ("B", _i32), ("n", _i32), ("V", _i32), ("max_depth", _i32),
+                ("temperature", _f32), ("logits", _P), ("tokens", _P), ("parents", _P), ("rng", sv_philox),
+                ("accept_len", _P), ("path", _P), ("out_tokens", _P), ("dev_status", _P)]
+
+
+EXPORTS = ("sv_build_tree_mask", "sv_verify_attention_workspace", "sv_verify_attention",
+           "sv_spec_accept_workspace", "sv_spec_accept", "sv_tree_walk_workspace", "sv_tree_walk",
+           "sv_status_string")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libspecverify.so is not built: run "
+                          "`python -m draft_token_verification_attention_amd._build` (%s)" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    L.sv_build_tree_mask.argtypes = [_P, _i32, _i32, _P, _P, _P, _P, _P]
+    L.sv_build_tree_mask.restype = ctypes.c_int
+    L.sv_verify_attention_workspace.argtypes = [ctypes.POINTER(sv_attn_desc)]
+    L.sv_verify_attention_workspace.restype = ctypes.c_size_t
+    L.sv_verify_attention.argtypes = [ctypes.POINTER(sv_attn_desc), _P, ctypes.c_size_t, _P]
+    L.sv_verify_attention.restype = ctypes.c_int
+    L.sv_spec_accept_workspace.argtypes = [ctypes.POINTER(sv_accept_desc)]
+    L.sv_spec_accept_workspace.restype = ctypes.c_size_t
+    L.sv_spec_accept.argtypes = [ctypes.POINTER(sv_accept_desc), _P, ctypes.c_size_t, _P]
+    L.sv_spec_accept.restype = ctypes.c_int
+    L.sv_tree_walk_workspace.argtypes = [ctypes.POINTER(sv_walk_desc)]
+    L.sv_tree_walk_workspace.restype = ctypes.c_size_t
+    L.sv_tree_walk.argtypes = [ctypes.POINTER(sv_walk_desc), _P, ctypes.c_size_t, _P]
+    L.sv_tree_walk.restype = ctypes.c_int
+    L.sv_status_string.argtypes = [ctypes.c_int]
+    L.sv_status_string.restype = ctypes.c_char_p
+    return L
+
+
+lib = _load()
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__("%s: %s" % (where, lib.sv_status_string(status).decode()))
+        self.status = status
+
+
+def _check(status: int, where: str) -> None:
+    if status != SV_OK:
+        raise SpecVerifyError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("libspecverify takes device tensors")
+
+
+# workspaces: zeroed once when created; every call leaves them zeroed again
+_workspaces: dict = {}
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """A zero-filled, 256-byte aligned device buffer of at least nbytes, reused per
+    (device, stream).  Calls that share it must not overlap."""
+    key = (torch.device(device).index, torch.cuda.current_stream(device).cuda_stream)
+    buf = _workspaces.get(key)
+    if buf is None or buf.numel() < nbytes + 256:
+        buf = torch.zeros(max(nbytes, 1) + 256, dtype=torch.uint8, device=device)
+        _workspaces[key] = buf
+    off = (-buf.data_ptr()) % 256
+    return buf[off:off + max(nbytes, 1)]
+
+
+# --------------------------------------------------------------------------- #
+def sv_build_tree_mask(parents: torch.Tensor, prefix_len: int):
+    """-> (bits uint32-as-int32 [n][ceil(n/32)], depth int32 [n], pos int64 [n], status int32 [1])."""
+    _need_cuda(parents)
+    parents = parents.contiguous().to(torch.int32)
+    n = parents.numel()
+    dev = parents.device
+    bits = torch.empty((n, (n + 31) // 32), dtype=torch.int32, device=dev)
+    depth = torch.empty(n, dtype=torch.int32, device=dev)
+    pos = torch.empty(n, dtype=torch.int64, device=dev)
+    status = torch.empty(1, dtype=torch.int32, device=dev)
+    _check(lib.sv_build_tree_mask(_ptr(parents), n, int(prefix_len), _ptr(bits), _ptr(depth), _ptr(pos),
+                                  _ptr(status), _stream(dev)), "sv_build_tree_mask")
+    return bits, depth, pos, status
+
+
+def attn_desc(q, k, v, kv_off, prefix_len, *, Hkv: int, max_prefix: int, scale: float,
+              kv_sh: int, kv_st: int, out, lse=None, tree_bits=None, tree_sb: int = 0,
+              split_keys: int = 0) -> sv_attn_desc:
+    B, n_q, Hq, D = q.shape
+    d = sv_attn_desc()
+    d.dtype = SV_BF16 if q.dtype == torch.bfloat16 else SV_F32
+    d.mask = SV_MASK_TREE if tree_bits is not None else SV_MASK_CAUSAL
+    d.B, d.n_q, d.Hq, d.Hkv, d.D = B, n_q, Hq, Hkv, D
+    d.max_prefix, d.split_keys, d.scale = int(max_prefix), int(split_keys), float(scale)
+    d.q = q.data_ptr()
+    d.q_sb, d.q_st, d.q_sh = q.stride(0), q.stride(1), q.stride(2)
+    d.k, d.v = k.data_ptr(), v.data_ptr()
+    d.kv_off = kv_off.data_ptr()
+    d.kv_sh, d.kv_st = int(kv_sh), int(kv_st)
+    d.prefix_len = prefix_len.data_ptr()
+    d.tree_bits = None if tree_bits is None else tree_bits.data_ptr()
+    d.tree_sb = int(tree_sb)
+    d.out = out.data_ptr()
+    d.o_sb, d.o_st, d.o_sh = out.stride(0), out.stride(1), out.stride(2)
+    d.lse = None if lse is None else lse.data_ptr()
+    return d
+
+
+def sv_verify_attention(q, k, v, kv_off, prefix_len, *, Hkv: int, max_prefix: int, scale: float,
+                        kv_sh: int, kv_st: int, tree_bits=None, tree_sb: int = 0, out=None,
+                        want_lse: bool = False, split_keys: int = 0):
+    """q [B][n_q][Hq][D] (bf16 or fp32, D contiguous); k, v flat caches of the same dtype;
+    kv_off int64 [B]; prefix_len int32 [B]; tree_bits int32 rows from sv_build_tree_mask
+    (TREE) or None (CAUSAL).  Returns (out [B][n_q][Hq][D], lse fp32 [B][n_q][Hq] or None)."""
+    _need_cuda(q, k, v, kv_off, prefix_len, tree_bits)
+    if q.stride(-1) != 1:
+        raise ValueError("q must have a contiguous head dimension")
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if want_lse else None
+    d = attn_desc(q, k, v, kv_off, prefix_len, Hkv=Hkv, max_prefix=max_prefix, scale=scale, kv_sh=kv_sh,
+                  kv_st=kv_st, out=out, lse=lse, tree_bits=tree_bits, tree_sb=tree_sb, split_keys=split_keys)
+    nb = lib.sv_verify_attention_workspace(ctypes.byref(d))
+    ws = workspace(nb, q.device)
+    _check(lib.sv_verify_attention(ctypes.byref(d), _ptr(ws), nb, _stream(q.device)), "sv_verify_attention")
+    return out, lse
+
+
+def accept_desc(mode, target, draft, draft_tokens, temperature, seed, step, stream_ids,
+                accept_len, out_tokens, alpha, dev_status) -> sv_accept_desc:
+    B, g1, V = target.shape
+    d = sv_accept_desc()
+    d.mode, d.B, d.gamma, d.V, d.temperature = int(mode), B, g1 - 1, V, float(temperature)
+    d.target_logits = target.data_ptr()
+    d.draft_logits = None if draft is None else draft.data_ptr()
+    d.draft_tokens = draft_tokens.data_ptr()
+    d.rng = sv_philox(int(seed), int(step), None if stream_ids is None else stream_ids.data_ptr())
+    d.accept_len, d.out_tokens = accept_len.data_ptr(), out_tokens.data_ptr()
+    d.alpha = None if alpha is None else alpha.data_ptr()
+    d.dev_status = None if dev_status is None else dev_status.data_ptr()
+    return d
+
+
+def sv_spec_accept(mode: int, target, draft, draft_tokens, temperature: float, seed: int, step: int = 0,
+                   stream_ids=None, want_alpha: bool = False):
+    """target fp32 [B][gamma+1][V]; draft fp32 [B][gamma][V] (SAMPLE); draft_tokens int32 [B][gamma].
+    Returns dict(accept_len, out_tokens, alpha or None, status) as device tensors."""
+    _need_cuda(target, draft, draft_tokens, stream_ids)
+    target = target.contiguous()
+    draft = None if draft is None else draft.contiguous()
+    draft_tokens = draft_tokens.to(torch.int32).contiguous()
+    B, g1, V = target.shape
+    dev = target.device
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    out = torch.empty((B, g1), dtype=torch.int32, device=dev)
+    alpha = torch.empty((B, g1 - 1), dtype=torch.float32, device=dev) if want_alpha else None
+    status = torch.empty(B, dtype=torch.int32, device=dev)
+    sid = None if stream_ids is None else stream_ids.to(torch.int64).contiguous()
+    d = accept_desc(mode, target, draft, draft_tokens, temperature, seed, step, sid, acc, out, alpha, status)
+    nb = lib.sv_spec_accept_workspace(ctypes.byref(d))
+    ws = workspace(nb, dev)
+    _check(lib.sv_spec_accept(ctypes.byref(d), _ptr(ws), nb, _stream(dev)), "sv_spec_accept")
+    return dict(accept_len=acc, out_tokens=out, alpha=alpha, status=status)
+
+
+def walk_desc(mode, logits, tokens, parents, max_depth, temperature, seed, step, stream_ids,
+              accept_len, path, out_tokens, dev_status) -> sv_walk_desc:
+    B, n, V = logits.shape
+    d = sv_walk_desc()
+    d.mode, d.B, d.n, d.V, d.max_depth, d.temperature = int(mode), B, n, V, int(max_depth), float(temperature)
+    d.logits, d.tokens, d.parents = logits.data_ptr(), tokens.data_ptr(), parents.data_ptr()
+    d.rng = sv_philox(int(seed), int(step), None if stream_ids is None else stream_ids.data_ptr())
+    d.accept_len, d.path, d.out_tokens = accept_len.data_ptr(), path.data_ptr(), out_tokens.data_ptr()
+    d.dev_status = None if dev_status is None else dev_status.data_ptr()
+    return d
+
+
+def sv_tree_walk(mode: int, logits, tokens, parents, max_depth: int, temperature: float, seed: int,
+                 step: int = 0, stream_ids=None):
+    """logits fp32 [B][n][V]; tokens int32 [B][n]; parents int32 [n].
+    Returns dict(accept_len, path, out_tokens, status) as device tensors."""
+    _need_cuda(logits, tokens, parents, stream_ids)
+    logits = logits.contiguous()
+    tokens = tokens.to(torch.int32).contiguous()
+    parents = parents.to(torch.int32).contiguous()
+    B, n, V = logits.shape
+    dev = logits.device
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    path = torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev)
+    out = torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev)
+    status = torch.empty(B, dtype=torch.int32, device=dev)
+    sid = None if stream_ids is None else stream_ids.to(torch.int64).contiguous()
+    d = walk_desc(mode, logits, tokens, parents, max_depth, temperature, seed, step, sid, acc, path, out, status)
+    nb = lib.sv_tree_walk_workspace(ctypes.byref(d))
+    ws = workspace(nb, dev)
+    _check(lib.sv_tree_walk(ctypes.byref(d), _ptr(ws), nb, _stream(dev)), "sv_tree_walk")
+    return dict(accept_len=acc, path=path, out_tokens=out, status=status)

@@ -1,0 +1,652 @@
+// attention.hip -- the multi-token attention of a verification pass.
+//
+// Sources: "Speculative decoding" (Zero to Frontier textbook, ch. 20, section 20.5):
+// section "Checking several tokens costs about as much as writing one" (each new token
+// attends to the whole cache and to the new tokens before it, a causal mask aligned to
+// its bottom-right corner; the cost is reading the cache, which does not grow with k)
+// and box "Token tree and tree attention" (node i sees the prefix, itself and its
+// ancestors).  "Speculative-Decoding" (Medusa notes), section "Attention Tree".
+//
+// bf16 path (MFMA, gfx950 v_mfma_f32_32x32x16_bf16):
+//   * The rows of one KV head are the n_q x G query rows that read it (grouped-query
+//     packing, row n = i * G + g), so every K/V tile is read once for all of them.
+//   * A block owns (sequence, KV head, row tile of 32*NWR rows, key split).  Its waves
+//     form NWK key groups x NWR row waves: a key group stages 32-key tiles of K and V
+//     through LDS (coalesced 16-byte loads, register double buffering), and each row
+//     wave of the group computes S^T = K Q^T and O^T += V^T P^T for its 32 rows on MFMA.
+//   * Online softmax in registers (log2 domain).  Key groups merge through LDS; key
+//     splits merge through a workspace by the last-arriving block (log-sum-exp combine).
+//   * Tiles the mask hides from every row of the block are never loaded (tree nodes of
+//     other branches; chain positions after the block's last row).
+//   * Blocks are numbered so that all blocks of one (sequence, KV head) run on the same
+//     XCD (workgroup id mod 8), keeping its partial results and K/V reuse in one L2.
+// fp32 path: one wave per query row, lanes across the head dimension (VALU).
+#include "sv_common.h"
+
+namespace {
+
+using namespace sv;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kTileKeys = 32;
+constexpr int kMaxTiles = 1024;  // tiles per split (split_keys <= 32768)
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+struct AttnArgs {
+    const void *q;
+    int64_t q_sb, q_st, q_sh;
+    const void *k, *v;
+    const int64_t *kv_off;
+    int64_t kv_sh, kv_st;
+    const int32_t *prefix_len;
+    const uint32_t *tree_bits;
+    int64_t tree_sb;
+    int words, tree;
+    void *out;
+    int64_t o_sb, o_st, o_sh;
+    float *lse;
+    int B, n_q, Hq, Hkv, G, rows, RT, KG, nsplit, split_keys;
+    float scale_log2;
+    float *part;  // [KG*RT][nsplit][32*NWR][D + 4]: o[D], max, sum, pad (16-byte rows)
+    int *cnt;     // [KG*RT]
+};
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u)
+{
+    return __builtin_bit_cast(bf16x8, u);
+}
+
+__device__ __forceinline__ bool node_visible(const AttnArgs &a, const uint32_t *bits_row, int i, int j)
+{
+    // j = position among the new tokens (0 <= j < n_q)
+    if (a.tree) return (bits_row[j >> 5] >> (j & 31)) & 1u;
+    return j <= i;
+}
+
+// ---------------------------------------------------------------------------
+template <int DH, int NWR, int NWK>
+__global__ __launch_bounds__(64 * NWR * NWK) void attn_bf16_kernel(AttnArgs a)
+{
+    constexpr int NT = 64 * NWR * NWK;
+    constexpr int ROWS_BLK = 32 * NWR;
+    constexpr int KROW = DH * 2 + 16;                   // LDS bytes per key row (16 B pad)
+    constexpr int TILE_BYTES = kTileKeys * KROW;
+    constexpr int GROUP_BYTES = 2 * TILE_BYTES;         // K then V
+    constexpr int TILES_LDS = NWK * GROUP_BYTES;
+    constexpr int NDB = DH / 32;                        // 32-wide d blocks of O^T
+    constexpr int NKC = DH / 16;                        // 16-deep d chunks of S^T
+    constexpr int COMB_FLOATS_PER_WAVE = 64 * (NDB * 16 + 2);
+    constexpr int COMB_LDS = (NWK > 1) ? (NWK - 1) * NWR * COMB_FLOATS_PER_WAVE * 4 : 0;
+    constexpr int SMEM = TILES_LDS > COMB_LDS ? TILES_LDS : COMB_LDS;
+    constexpr int LPR = DH / 8;                         // lanes per key row in a 16 B load
+    constexpr int KPI = 64 / LPR;                       // key rows per wave load instruction
+    constexpr int KPW = kTileKeys / NWR;                // key rows loaded per wave
+    constexpr int NI = KPW / KPI;                       // load instructions per wave and tensor
+    static_assert(NI >= 1 && KPW % KPI == 0, "tile split");
+
+    __shared__ __align__(16) char smem[SMEM];
+    __shared__ uint16_t tile_list[kMaxTiles];
+    __shared__ int s_count, s_last;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wk = wave % NWK;
+    const int wr = wave / NWK;
+    const int h = lane >> 5;          // half of the wave
+    const int l32 = lane & 31;
+
+    // ---- block -> (kv group, row tile, split); XCD = workgroup id mod 8 ----
+    const int L = blockIdx.x;
+    const int xcd = L & 7;
+    const int slot = L >> 3;
+    const int per_kg = a.RT * a.nsplit;
+    const int kg = (slot / per_kg) * 8 + xcd;
+    const int rem = slot % per_kg;
+    const int rt = rem / a.nsplit;
+    const int s = rem % a.nsplit;
+    if (kg >= a.KG) return;
+    const int b = kg / a.Hkv;
+    const int kvh = kg % a.Hkv;
+    const int P = a.prefix_len[b];
+    const int T = P + a.n_q;
+    const int SK = a.split_keys;
+    const bool overflow = (int64_t)T > (int64_t)a.nsplit * SK;
+    const int ns = overflow ? a.nsplit : (T + SK - 1) / SK;
+    if (s >= ns) return;
+    const int kstart = s * SK;
+    const int kend = min(kstart + SK, T);
+    const int rowbase = rt * ROWS_BLK;
+    const int row_hi = min(rowbase + ROWS_BLK, a.rows) - 1;
+    const int i_lo = rowbase / a.G, i_hi = row_hi / a.G;
+
+    const uint16_t *kbase = (const uint16_t *)a.k + a.kv_off[b] + (int64_t)kvh * a.kv_sh;
+    const uint16_t *vbase = (const uint16_t *)a.v + a.kv_off[b] + (int64_t)kvh * a.kv_sh;
+    const uint32_t *bits_b = a.tree ? a.tree_bits + (int64_t)b * a.tree_sb : nullptr;
+
+    // ---- the list of tiles some row of this block can see (wave 0, ballot compaction) ----
+    if (wave == 0) {
+        const int ntile = (kend - kstart + kTileKeys - 1) / kTileKeys;
+        int count = 0;
+        for (int t0i = 0; t0i < ntile; t0i += 64) {
+            const int tt = t0i + lane;
+            bool inc = false;
+            if (tt < ntile) {
+                const int t0 = kstart + tt * kTileKeys;
+                if (t0 < P) {
+                    inc = true;
+                } else {
+                    const int j0 = t0 - P;
+                    if (!a.tree) {
+                        inc = j0 <= i_hi;
+                    } else {
+                        const int jl = min(j0 + kTileKeys, a.n_q) - 1;
+                        for (int i = i_lo; i <= i_hi && !inc; ++i) {
+                            const uint32_t *br = bits_b + (int64_t)i * a.words;
+                            for (int w = j0 >> 5; w <= (jl >> 5) && !inc; ++w) {
+                                uint32_t word = br[w];
+                                const int lo = max(j0 - 32 * w, 0), hi = min(jl - 32 * w, 31);
+                                const uint32_t m_hi = hi == 31 ? 0xffffffffu : ((1u << (hi + 1)) - 1u);
+                                const uint32_t m_lo = ~((1u << lo) - 1u);
+                                if (word & m_hi & m_lo) inc = true;
+                            }
+                        }
+                    }
+                }
+            }
+            const uint64_t mask = __ballot(inc);
+            const int pos = count + __popcll(mask & ((1ull << lane) - 1ull));
+            if (inc) tile_list[pos] = (uint16_t)tt;
+            count += __popcll(mask);
+        }
+        if (lane == 0) s_count = count;
+    }
+    __syncthreads();
+    const int count = s_count;
+    const int niter = (count + NWK - 1) / NWK;
+
+    // ---- this wave's 32 query rows: B operand of S^T = K Q^T ----
+    const int my_row = rowbase + wr * 32 + l32;
+    const bool row_ok = my_row < a.rows;
+    const int my_i = row_ok ? my_row / a.G : 0;
+    bf16x8 qf[NKC];
+    {
+        const uint16_t *qrow = (const uint16_t *)a.q + (int64_t)b * a.q_sb + (int64_t)my_i * a.q_st +
+                               (int64_t)(kvh * a.G + (row_ok ? my_row % a.G : 0)) * a.q_sh;
+#pragma unroll
+        for (int c = 0; c < NKC; ++c) {
+            uint4 u = make_uint4(0, 0, 0, 0);
+            if (row_ok) u = *reinterpret_cast<const uint4 *>(qrow + 16 * c + 8 * h);
+            qf[c] = as_bf16x8(u);
+        }
+    }
+    const uint32_t *my_bits = a.tree ? bits_b + (int64_t)my_i * a.words : nullptr;
+
+    // ---- staging registers for this wave's share of a K/V tile ----
+    uint4 kreg[NI], vreg[NI];
+    const int ld_key0 = wr * KPW + lane / LPR;
+    const int ld_dc = lane % LPR;
+    auto issue_loads = [&](int it) {
+        const int li = it * NWK + wk;
+        if (li < count) {
+            const int t0 = kstart + (int)tile_list[li] * kTileKeys;
+#pragma unroll
+            for (int j = 0; j < NI; ++j) {
+                const int t = t0 + ld_key0 + j * KPI;
+                if (t < T) {
+                    kreg[j] = *reinterpret_cast<const uint4 *>(kbase + (int64_t)t * a.kv_st + 8 * ld_dc);
+                    vreg[j] = *reinterpret_cast<const uint4 *>(vbase + (int64_t)t * a.kv_st + 8 * ld_dc);
+                } else {
+                    kreg[j] = make_uint4(0, 0, 0, 0);
+                    vreg[j] = make_uint4(0, 0, 0, 0);
+                }
+            }
+        }
+    };
+
+    char *gK = smem + wk * GROUP_BYTES;
+    char *gV = gK + TILE_BYTES;
+
+    f32x16 oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[db][v] = 0.0f;
+    float m_run = -INFINITY;
+    float l_run = 0.0f;
+
+    if (niter > 0) issue_loads(0);
+    for (int it = 0; it < niter; ++it) {
+        const int li = it * NWK + wk;
+        const bool have = li < count;
+        __syncthreads();  // the previous tile is no longer read
+        if (have) {
+#pragma unroll
+            for (int j = 0; j < NI; ++j) {
+                const int key = ld_key0 + j * KPI;
+                *reinterpret_cast<uint4 *>(gK + key * KROW + 16 * ld_dc) = kreg[j];
+                *reinterpret_cast<uint4 *>(gV + key * KROW + 16 * ld_dc) = vreg[j];
+            }
+        }
+        __syncthreads();
+        if (it + 1 < niter) issue_loads(it + 1);
+        if (!have) continue;
+        const int t0 = kstart + (int)tile_list[li] * kTileKeys;
+
+        // S^T (32 keys x 32 rows) = K (keys x d) . Q^T (d x rows)
+        f32x16 sacc;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sacc[v] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NKC; ++c) {
+            const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(gK + l32 * KROW + (16 * c + 8 * h) * 2);
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], sacc, 0, 0, 0);
+        }
+        // lane (row l32, half h) holds keys 8*(v/4) + 4*h + v%4
+        float sv[16];
+        const bool need_mask = (t0 + kTileKeys > P);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            float x = sacc[v] * a.scale_log2;
+            if (need_mask) {
+                const int t = t0 + 8 * (v >> 2) + 4 * h + (v & 3);
+                bool vis = t < T;
+                if (vis && t >= P && row_ok) vis = node_visible(a, my_bits, my_i, t - P);
+                if (!vis) x = -INFINITY;
+            }
+            sv[v] = x;
+        }
+        float mloc = sv[0];
+#pragma unroll
+        for (int v = 1; v < 16; ++v) mloc = fmaxf(mloc, sv[v]);
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+        const float m_new = fmaxf(m_run, mloc);
+        float alpha = 1.0f;
+        float p[16];
+        if (m_new == -INFINITY) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) p[v] = 0.0f;
+        } else {
+            alpha = exp2f(m_run - m_new);  // m_run == -inf gives 0
+#pragma unroll
+            for (int v = 0; v < 16; ++v) p[v] = exp2f(sv[v] - m_new);
+        }
+        float psum = 0.0f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) psum += p[v];
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
+
+        // P^T as the B operand: k index 8*h + j <-> key 16*c + 8*(j/4) + 4*h + j%4
+        bf16x8 pb[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) pb[c][j] = (__bf16)p[8 * c + j];
+
+        // O^T (d x rows) += V^T (d x keys) . P^T (keys x rows)
+        const uint16_t *vt = reinterpret_cast<const uint16_t *>(gV);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                uint32_t wv[4];
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int j0 = 2 * jj, j1 = 2 * jj + 1;
+                    const int key0 = 16 * c + 8 * (j0 >> 2) + 4 * h + (j0 & 3);
+                    const int key1 = 16 * c + 8 * (j1 >> 2) + 4 * h + (j1 & 3);
+                    const uint32_t lo = vt[(key0 * KROW) / 2 + 32 * db + l32];
+                    const uint32_t hi = vt[(key1 * KROW) / 2 + 32 * db + l32];
+                    wv[jj] = lo | (hi << 16);
+                }
+                const bf16x8 vf = as_bf16x8(make_uint4(wv[0], wv[1], wv[2], wv[3]));
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[c], oacc[db], 0, 0, 0);
+            }
+        }
+    }
+
+    // ---- merge the NWK key groups of each row wave (through LDS) ----
+    // Every wave stays to the end of the kernel so that each barrier sees the whole block.
+    const bool active = (wk == 0);  // after the merge, these waves hold the block's rows
+    if (NWK > 1) {
+        __syncthreads();
+        float *comb = reinterpret_cast<float *>(smem);
+        if (!active) {
+            float *mine = comb + ((wr * (NWK - 1)) + (wk - 1)) * COMB_FLOATS_PER_WAVE;
+            mine[lane] = m_run;
+            mine[64 + lane] = l_run;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) mine[128 + (db * 16 + v) * 64 + lane] = oacc[db][v];
+        }
+        __syncthreads();
+        if (active) {
+            for (int o = 0; o < NWK - 1; ++o) {
+                const float *oth = comb + (wr * (NWK - 1) + o) * COMB_FLOATS_PER_WAVE;
+                const float m2 = oth[lane];
+                const float mm = fmaxf(m_run, m2);
+                if (mm == -INFINITY) continue;
+                const float f1 = exp2f(m_run - mm), f2 = exp2f(m2 - mm);
+                l_run = l_run * f1 + oth[64 + lane] * f2;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        oacc[db][v] = oacc[db][v] * f1 + oth[128 + (db * 16 + v) * 64 + lane] * f2;
+                m_run = mm;
+            }
+        }
+    }
+    const float l_row = l_run + __shfl_xor(l_run, 32);
+    const int gidx = kg * a.RT + rt;
+
+    if (ns == 1 && !overflow) {
+        // a single split: normalize and store straight from the accumulators
+        if (!active || !row_ok) return;
+        const float inv = 1.0f / l_row;
+        const int hq = kvh * a.G + my_row % a.G;
+        const int64_t obase = (int64_t)b * a.o_sb + (int64_t)my_i * a.o_st + (int64_t)hq * a.o_sh;
+        uint16_t *o = (uint16_t *)a.out + obase;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4) {
+                const int d = 32 * db + 8 * a4 + 4 * h;
+                uint2 pk;
+                pk.x = (uint32_t)f32_to_bf16(oacc[db][4 * a4 + 0] * inv) |
+                       ((uint32_t)f32_to_bf16(oacc[db][4 * a4 + 1] * inv) << 16);
+                pk.y = (uint32_t)f32_to_bf16(oacc[db][4 * a4 + 2] * inv) |
+                       ((uint32_t)f32_to_bf16(oacc[db][4 * a4 + 3] * inv) << 16);
+                *reinterpret_cast<uint2 *>(o + d) = pk;
+            }
+        if (a.lse && h == 0) a.lse[((int64_t)b * a.n_q + my_i) * a.Hq + hq] = (m_run + log2f(l_row)) * kLn2;
+        return;
+    }
+
+    // ---- split partial: unnormalized o, running max (log2 units), sum ----
+    if (active) {
+        float *pr = a.part + (((int64_t)gidx * a.nsplit + s) * ROWS_BLK + wr * 32 + l32) * (DH + 4);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4) {
+                const int d = 32 * db + 8 * a4 + 4 * h;
+                *reinterpret_cast<float4 *>(pr + d) =
+                    make_float4(oacc[db][4 * a4 + 0], oacc[db][4 * a4 + 1], oacc[db][4 * a4 + 2], oacc[db][4 * a4 + 3]);
+            }
+        if (h == 0) {
+            pr[DH] = m_run;
+            pr[DH + 1] = l_row;
+        }
+    }
+    if (!arrive_last(&a.cnt[gidx], ns, &s_last)) return;
+
+    // ---- last block: combine the ns partials of every row ----
+    const float *pg = a.part + (int64_t)gidx * a.nsplit * ROWS_BLK * (DH + 4);
+    for (int item = threadIdx.x; item < ROWS_BLK * (DH / 4); item += NT) {
+        const int r = item / (DH / 4);
+        const int d4 = item % (DH / 4);
+        const int row = rowbase + r;
+        if (row >= a.rows) continue;
+        float M = -INFINITY;
+        for (int ss = 0; ss < ns; ++ss) M = fmaxf(M, pg[((int64_t)ss * ROWS_BLK + r) * (DH + 4) + DH]);
+        float Lsum = 0.0f;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int ss = 0; ss < ns; ++ss) {
+            const float *pr = pg + ((int64_t)ss * ROWS_BLK + r) * (DH + 4);
+            const float ms = pr[DH];
+            if (ms == -INFINITY) continue;
+            const float f = exp2f(ms - M);
+            Lsum += pr[DH + 1] * f;
+            const float4 o4 = *reinterpret_cast<const float4 *>(pr + 4 * d4);
+            acc.x += o4.x * f;
+            acc.y += o4.y * f;
+            acc.z += o4.z * f;
+            acc.w += o4.w * f;
+        }
+        float inv = 1.0f / Lsum;
+        if (overflow) inv = __int_as_float(0x7fc00000);
+        const int i = row / a.G;
+        const int hq = kvh * a.G + row % a.G;
+        uint16_t *o = (uint16_t *)a.out + (int64_t)b * a.o_sb + (int64_t)i * a.o_st + (int64_t)hq * a.o_sh + 4 * d4;
+        uint2 pk;
+        pk.x = (uint32_t)f32_to_bf16(acc.x * inv) | ((uint32_t)f32_to_bf16(acc.y * inv) << 16);
+        pk.y = (uint32_t)f32_to_bf16(acc.z * inv) | ((uint32_t)f32_to_bf16(acc.w * inv) << 16);
+        *reinterpret_cast<uint2 *>(o) = pk;
+        if (a.lse && d4 == 0)
+            a.lse[((int64_t)b * a.n_q + i) * a.Hq + hq] =
+                overflow ? __int_as_float(0x7fc00000) : (M + log2f(Lsum)) * kLn2;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32: one wave per (sequence, row, query head); lane owns d = lane (+64)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a, int D)
+{
+    const int r = blockIdx.x;
+    const int h = r % a.Hq;
+    const int i = (r / a.Hq) % a.n_q;
+    const int b = r / (a.Hq * a.n_q);
+    const int lane = threadIdx.x;
+    const int kvh = h / a.G;
+    const int P = a.prefix_len[b];
+    const int T = P + a.n_q;
+    const float *q = (const float *)a.q + (int64_t)b * a.q_sb + (int64_t)i * a.q_st + (int64_t)h * a.q_sh;
+    const float *kb = (const float *)a.k + a.kv_off[b] + (int64_t)kvh * a.kv_sh;
+    const float *vb = (const float *)a.v + a.kv_off[b] + (int64_t)kvh * a.kv_sh;
+    const uint32_t *bits = a.tree ? a.tree_bits + (int64_t)b * a.tree_sb + (int64_t)i * a.words : nullptr;
+    const bool two = D > 64;
+    const float q0 = q[lane];
+    const float q1 = two ? q[lane + 64] : 0.0f;
+    float m = -INFINITY, l = 0.0f, o0 = 0.0f, o1 = 0.0f;
+    for (int t = 0; t < T; ++t) {
+        if (t >= P) {
+            const int j = t - P;
+            const bool vis = a.tree ? ((bits[j >> 5] >> (j & 31)) & 1u) : (j <= i);
+            if (!vis) continue;
+        }
+        const float *kr = kb + (int64_t)t * a.kv_st;
+        float part = q0 * kr[lane];
+        if (two) part += q1 * kr[lane + 64];
+        const float sc = wave_sum(part) * a.scale_log2;
+        const float mn = fmaxf(m, sc);
+        const float f = exp2f(m - mn);
+        const float pw = exp2f(sc - mn);
+        const float *vr = vb + (int64_t)t * a.kv_st;
+        l = l * f + pw;
+        o0 = o0 * f + pw * vr[lane];
+        if (two) o1 = o1 * f + pw * vr[lane + 64];
+        m = mn;
+    }
+    float *o = (float *)a.out + (int64_t)b * a.o_sb + (int64_t)i * a.o_st + (int64_t)h * a.o_sh;
+    o[lane] = o0 / l;
+    if (two) o[lane + 64] = o1 / l;
+    if (a.lse && lane == 0) a.lse[((int64_t)b * a.n_q + i) * a.Hq + h] = (m + log2f(l)) * kLn2;
+}
+
+// ---------------------------------------------------------------------------
+// launch planning (host)
+// ---------------------------------------------------------------------------
+struct Plan {
+    int variant;  // 0: fp32, 1: (NWR=1, NWK=4), 2: (NWR=2, NWK=2), 3: (NWR=4, NWK=1)
+    int NWR, NWK, rows, RT, KG, nsplit, split_keys, kg_pad;
+    size_t part_bytes, cnt_bytes, total;
+    unsigned blocks;
+};
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static bool plan_attention(const sv_attn_desc *d, Plan &p)
+{
+    p = Plan{};
+    if (d->dtype == SV_F32) {
+        p.variant = 0;
+        p.total = 0;
+        return true;
+    }
+    const int G = d->Hq / d->Hkv;
+    p.rows = d->n_q * G;
+    if (p.rows <= 32) {
+        p.variant = 1; p.NWR = 1; p.NWK = 4;
+    } else if (p.rows <= 64) {
+        p.variant = 2; p.NWR = 2; p.NWK = 2;
+    } else {
+        p.variant = 3; p.NWR = 4; p.NWK = 1;
+    }
+    const int rows_blk = 32 * p.NWR;
+    p.RT = (p.rows + rows_blk - 1) / rows_blk;
+    p.KG = d->B * d->Hkv;
+    p.kg_pad = (p.KG + 7) / 8 * 8;
+    const int64_t Tmax = (int64_t)d->max_prefix + d->n_q;
+    const int unit = kTileKeys * p.NWK;  // split granularity
+    int64_t sk;
+    if (d->split_keys > 0) {
+        sk = ((int64_t)d->split_keys + unit - 1) / unit * unit;
+    } else {
+        // enough blocks to cover the chip twice over (256 CUs), at least one tile per wave
+        const int64_t want_blocks = 512;
+        const int64_t groups = (int64_t)p.KG * p.RT > 0 ? (int64_t)p.KG * p.RT : 1;
+        int64_t nsp = (want_blocks + groups - 1) / groups;
+        if (nsp < 1) nsp = 1;
+        sk = (Tmax + nsp - 1) / nsp;
+        sk = (sk + unit - 1) / unit * unit;
+        if (sk < unit) sk = unit;
+    }
+    if (sk > (int64_t)kMaxTiles * kTileKeys) sk = (int64_t)kMaxTiles * kTileKeys / unit * unit;
+    p.split_keys = (int)sk;
+    const int64_t nsplit = (Tmax + sk - 1) / sk;
+    if (nsplit > 65535) return false;
+    p.nsplit = (int)(nsplit < 1 ? 1 : nsplit);
+    const int64_t blocks = (int64_t)p.kg_pad * p.RT * p.nsplit;
+    if (blocks > 0x7fffffff) return false;
+    p.blocks = (unsigned)blocks;
+    const size_t D = (size_t)d->D;
+    p.cnt_bytes = align256((size_t)p.KG * p.RT * sizeof(int));
+    // partials exist even for one split: a sequence longer than max_prefix still merges
+    // through them (to report NaN rows)
+    p.part_bytes = align256((size_t)p.KG * p.RT * p.nsplit * rows_blk * (D + 4) * sizeof(float));
+    p.total = p.cnt_bytes + p.part_bytes;
+    return true;
+}
+
+static sv_status check_attention(const sv_attn_desc *d)
+{
+    if (!d) return SV_ERR_INVALID_ARG;
+    if (d->dtype != SV_F32 && d->dtype != SV_BF16) return SV_ERR_INVALID_ARG;
+    if (d->mask != SV_MASK_CAUSAL && d->mask != SV_MASK_TREE) return SV_ERR_INVALID_ARG;
+    if (d->B < 0 || d->n_q < 1 || d->Hq < 1 || d->Hkv < 1 || d->D < 1 || d->max_prefix < 0) return SV_ERR_INVALID_ARG;
+    if (d->Hq % d->Hkv != 0) return SV_ERR_INVALID_ARG;
+    if (!(d->scale == d->scale)) return SV_ERR_INVALID_ARG;
+    if (d->split_keys < 0) return SV_ERR_INVALID_ARG;
+    if (!d->q || !d->k || !d->v || !d->kv_off || !d->prefix_len || !d->out) return SV_ERR_INVALID_ARG;
+    if (d->mask == SV_MASK_TREE && !d->tree_bits) return SV_ERR_INVALID_ARG;
+    if (d->q_sb < 0 || d->q_st < 0 || d->q_sh < 0 || d->kv_sh < 0 || d->kv_st < 0 || d->o_sb < 0 || d->o_st < 0 ||
+        d->o_sh < 0 || d->tree_sb < 0)
+        return SV_ERR_INVALID_ARG;
+    if (d->D != 64 && d->D != 128) return SV_ERR_UNSUPPORTED;
+    if (d->mask == SV_MASK_TREE && d->n_q > 32768) return SV_ERR_UNSUPPORTED;
+    if ((int64_t)d->max_prefix + d->n_q > 0x7fffffffLL) return SV_ERR_UNSUPPORTED;
+    if (d->dtype == SV_BF16) {
+        // 16-byte vector access of q, k, v rows; 8-byte stores of out
+        const int64_t s16[] = {d->q_sb, d->q_st, d->q_sh, d->kv_sh, d->kv_st};
+        for (int64_t x : s16)
+            if (x % 8) return SV_ERR_UNSUPPORTED;
+        if (((uintptr_t)d->q | (uintptr_t)d->k | (uintptr_t)d->v) & 15) return SV_ERR_UNSUPPORTED;
+        if ((d->o_sb | d->o_st | d->o_sh) % 4 || ((uintptr_t)d->out & 7)) return SV_ERR_UNSUPPORTED;
+    }
+    return SV_OK;
+}
+
+template <int DH>
+static hipError_t launch_bf16(const Plan &p, const AttnArgs &a, hipStream_t s)
+{
+    switch (p.variant) {
+    case 1:
+        hipLaunchKernelGGL((attn_bf16_kernel<DH, 1, 4>), dim3(p.blocks), dim3(256), 0, s, a);
+        break;
+    case 2:
+        hipLaunchKernelGGL((attn_bf16_kernel<DH, 2, 2>), dim3(p.blocks), dim3(256), 0, s, a);
+        break;
+    default:
+        hipLaunchKernelGGL((attn_bf16_kernel<DH, 4, 1>), dim3(p.blocks), dim3(256), 0, s, a);
+        break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" size_t sv_verify_attention_workspace(const sv_attn_desc *d)
+{
+    if (check_attention(d) != SV_OK) return 0;
+    Plan p;
+    if (!plan_attention(d, p)) return 0;
+    return p.total;
+}
+
+extern "C" sv_status sv_verify_attention(const sv_attn_desc *d, void *workspace, size_t workspace_bytes, void *stream)
+{
+    const sv_status st = check_attention(d);
+    if (st != SV_OK) return st;
+    if (d->B == 0) return SV_OK;
+    Plan p;
+    if (!plan_attention(d, p)) return SV_ERR_UNSUPPORTED;
+    if (p.total > 0 && (!workspace || workspace_bytes < p.total || ((uintptr_t)workspace & 255)))
+        return SV_ERR_WORKSPACE;
+
+    AttnArgs a;
+    a.q = d->q;
+    a.q_sb = d->q_sb;
+    a.q_st = d->q_st;
+    a.q_sh = d->q_sh;
+    a.k = d->k;
+    a.v = d->v;
+    a.kv_off = d->kv_off;
+    a.kv_sh = d->kv_sh;
+    a.kv_st = d->kv_st;
+    a.prefix_len = d->prefix_len;
+    a.tree_bits = d->tree_bits;
+    a.tree_sb = d->tree_sb;
+    a.words = (d->n_q + 31) / 32;
+    a.tree = d->mask == SV_MASK_TREE;
+    a.out = d->out;
+    a.o_sb = d->o_sb;
+    a.o_st = d->o_st;
+    a.o_sh = d->o_sh;
+    a.lse = d->lse;
+    a.B = d->B;
+    a.n_q = d->n_q;
+    a.Hq = d->Hq;
+    a.Hkv = d->Hkv;
+    a.G = d->Hq / d->Hkv;
+    a.rows = p.rows;
+    a.RT = p.RT;
+    a.KG = p.KG;
+    a.nsplit = p.nsplit;
+    a.split_keys = p.split_keys;
+    a.scale_log2 = d->scale * kLog2e;
+    a.cnt = p.total ? (int *)workspace : nullptr;
+    a.part = p.part_bytes ? (float *)((char *)workspace + p.cnt_bytes) : nullptr;
+
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();
+    hipError_t e;
+    if (p.variant == 0) {
+        const int64_t nrows = (int64_t)d->B * d->n_q * d->Hq;
+        if (nrows > 0x7fffffffLL) return SV_ERR_UNSUPPORTED;
+        hipLaunchKernelGGL(attn_f32_kernel, dim3((unsigned)nrows), dim3(64), 0, s, a, d->D);
+        e = hipGetLastError();
+    } else {
+        e = d->D == 128 ? launch_bf16<128>(p, a, s) : launch_bf16<64>(p, a, s);
+    }
+    return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+}

@@ -1,0 +1,124 @@
+// sv_common.h -- device helpers shared by the libspecverify kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "specverify.h"
+
+namespace sv {
+
+constexpr int kWave = 64;
+constexpr uint64_t kTagAccept = 0x53560001ULL;
+constexpr uint64_t kTagWalk = 0x53560002ULL;
+
+// ---------------------------------------------------------------------------
+// Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy
+// as 1, 2, 3", SC'11).  Each round multiplies counter words 0 and 2 by two fixed
+// 64-bit constants (full 128-bit products), swaps the halves into the output
+// words XOR-ed with the other counter words and the key, and the key advances by
+// two Weyl increments.  Ten rounds.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void philox4x64_10(uint64_t c[4], uint64_t k0, uint64_t k1)
+{
+    const uint64_t M0 = 0xD2E7470EE14C6C93ULL, M1 = 0xCA5A826395121157ULL;
+    const uint64_t W0 = 0x9E3779B97F4A7C15ULL, W1 = 0xBB67AE8584CAA73BULL;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t lo0 = M0 * c[0], hi0 = __umul64hi(M0, c[0]);
+        const uint64_t lo1 = M1 * c[2], hi1 = __umul64hi(M1, c[2]);
+        const uint64_t n0 = hi1 ^ c[1] ^ k0;
+        const uint64_t n2 = hi0 ^ c[3] ^ k1;
+        c[0] = n0;
+        c[1] = lo1;
+        c[2] = n2;
+        c[3] = lo0;
+        k0 += W0;
+        k1 += W1;
+    }
+}
+
+// Uniform in (0,1): counter (index, step, stream, tag), key (seed, 0), first word
+// mapped to (2*(w >> 12) + 1) * 2^-53 -- exact in fp64, never 0 or 1.
+__device__ __forceinline__ double philox_uniform(uint64_t seed, uint64_t index, uint64_t step,
+                                                 uint64_t stream, uint64_t tag)
+{
+    uint64_t c[4] = {index, step, stream, tag};
+    philox4x64_10(c, seed, 0);
+    return (double)(2 * (c[0] >> 12) + 1) * 0x1p-53;
+}
+
+// ---------------------------------------------------------------------------
+// wave64 reductions
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ T wave_sum(T x)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_max(T x)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = fmax(x, __shfl_xor(x, o));
+    return x;
+}
+
+// (value, index) with the larger value winning and ties going to the lower index.
+__device__ __forceinline__ void argmax_merge(float &v, int &i, float v2, int i2)
+{
+    if (v2 > v || (v2 == v && i2 < i)) {
+        v = v2;
+        i = i2;
+    }
+}
+
+__device__ __forceinline__ void wave_argmax(float &v, int &i)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float v2 = __shfl_xor(v, o);
+        const int i2 = __shfl_xor(i, o);
+        argmax_merge(v, i, v2, i2);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32 (raw 16-bit patterns; round to nearest even on the way down)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t h)
+{
+    return __uint_as_float((uint32_t)h << 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)0x7fc0;  // NaN stays NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Last-arriving block detection.  Every block of a group stores its partial
+// result, then calls this; exactly one caller (the last) gets true and may read
+// every partial.  The counter is reset to zero for the next call.
+__device__ __forceinline__ bool arrive_last(int *counter, int expected, int *lds_flag)
+{
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int old = atomicAdd(counter, 1);
+        const bool last = (old == expected - 1);
+        if (last) atomicExch(counter, 0);
+        *lds_flag = last ? 1 : 0;
+    }
+    __syncthreads();
+    const bool last = *lds_flag != 0;
+    if (last) __threadfence();
+    return last;
+}
+
+}  // namespace sv

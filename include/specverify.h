@@ -1,0 +1,238 @@
+/*
+ * specverify.h -- C ABI of libspecverify, the verify step of speculative decoding
+ * on one AMD Instinct MI355X (gfx950).
+ *
+ * The verify step (sources cited by page title and section):
+ *   - "Speculative decoding" (Zero to Frontier textbook, ch. 20, section 20.5), below [TB];
+ *   - "Speculative-Decoding" (s1mplewind blog, Medusa notes), below [MED];
+ *   - "Speculative Decoding: The Art of Guessing Well" (astralord blog), below [AG].
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is DEVICE memory owned by the caller, unless marked "host".
+ *     Descriptors are read on the host during the call and not kept.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL is the null stream)
+ *     and never synchronizes the host.
+ *   - Argument checks run on the host before any launch and return SV_ERR_INVALID_ARG,
+ *     SV_ERR_UNSUPPORTED or SV_ERR_WORKSPACE without touching the device.  Errors that
+ *     only the data can show (a bad parent, a token id out of range) are written to the
+ *     device status words the calls document.  A failed launch returns SV_ERR_HIP.
+ *   - Workspaces: `*_workspace()` returns the byte size a call needs for a descriptor.
+ *     The caller allocates it (device memory, 256-byte aligned) and must ZERO it once
+ *     before its first use; every call leaves the workspace zeroed again.  A workspace
+ *     may be reused by later calls on the same stream, never by overlapping calls.
+ *   - The library allocates no memory and keeps no global state.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define SV_API __attribute__((visibility("default")))
+#else
+#define SV_API
+#endif
+
+typedef enum sv_status {
+    SV_OK = 0,
+    SV_ERR_INVALID_ARG = 1,  /* a null pointer, a negative size, inconsistent shapes      */
+    SV_ERR_UNSUPPORTED = 2,  /* a valid request this build does not implement (e.g. D=96) */
+    SV_ERR_WORKSPACE = 3,    /* workspace pointer null or smaller than *_workspace()     */
+    SV_ERR_HIP = 4           /* a HIP launch failed                                       */
+} sv_status;
+
+typedef enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+
+/* GREEDY: argmax decisions on raw logits.  SAMPLE: temperature softmax and speculative
+ * sampling; SAMPLE with temperature == 0 is GREEDY ([TB] "When the target samples...":
+ * as the temperature goes to 0 both models approach their argmax).                      */
+typedef enum sv_mode { SV_GREEDY = 0, SV_SAMPLE = 1 } sv_mode;
+
+/* CAUSAL: bottom-right-aligned causal mask of a chain ([TB] "Checking several tokens costs
+ * about as much as writing one").  TREE: ancestor-or-self mask of a token tree ([TB] box
+ * "Token tree and tree attention"; [MED] "Attention Tree").                              */
+typedef enum sv_mask { SV_MASK_CAUSAL = 0, SV_MASK_TREE = 1 } sv_mask;
+
+/* Counter-based uniforms: Philox4x64-10 (Salmon et al., SC'11) with key (seed, 0) and
+ * counter (index, step, stream, tag); u = (2*(w0 >> 12) + 1) * 2^-53, exact in fp64 and
+ * inside (0,1).  The pages ask for independent uniforms and name no generator.
+ * stream_ids: device [B] uint64 stream of each sequence, or NULL for stream = b.          */
+typedef struct sv_philox {
+    uint64_t seed;
+    uint64_t step;
+    const uint64_t *stream_ids;
+} sv_philox;
+
+/* ---------------------------------------------------------------------------------- */
+/* sv_build_tree_mask -- [TB] box "Token tree and tree attention" and exercise "The tree */
+/* attention mask".  A tree of n nodes is a parent array, par(i) in {-1, 0, ..., i-1}    */
+/* (parents listed before children; -1 follows the last committed token; several -1     */
+/* entries make a forest).  Node i may attend to every prefix position and to node j     */
+/* exactly when j == i or j is an ancestor of i; its position id is prefix_len + depth(i),*/
+/* depth = number of ancestors.                                                          */
+/*   parents    device int32 [n]                                                         */
+/*   bits       device uint32 [n][ceil(n/32)]: bit (j % 32) of word j / 32 of row i is    */
+/*              set iff node i sees node j (the node-to-node block; the prefix block is  */
+/*              all ones and is not stored).  This is the tree_bits layout of            */
+/*              sv_verify_attention.                                                     */
+/*   depth      device int32 [n];  pos  device int64 [n] = prefix_len + depth            */
+/*   dev_status device int32 [1]: 0 when every parent is valid, else 1 + the first node   */
+/*              whose parent is not in [-1, i).  Rows of such trees are unspecified.     */
+/* Errors: n < 1 or prefix_len < 0 or a null pointer -> SV_ERR_INVALID_ARG.              */
+/* ---------------------------------------------------------------------------------- */
+SV_API sv_status sv_build_tree_mask(const int32_t *parents, int32_t n, int32_t prefix_len,
+                             uint32_t *bits, int32_t *depth, int64_t *pos,
+                             int32_t *dev_status, void *stream);
+
+/* ---------------------------------------------------------------------------------- */
+/* sv_verify_attention -- the multi-token attention of a verification pass.             */
+/* [TB] "Checking several tokens costs about as much as writing one": each new token     */
+/* attends to the whole cache and to the new tokens before it; [TB] box "Token tree and  */
+/* tree attention" for trees; query head h reads KV head h / (Hq / Hkv).                 */
+/* For sequence b with P = prefix_len[b], row i in [0, n_q) of query head h computes     */
+/*   s_t = scale * <q[b][i][h], k_t>,  t visible;  o = sum_t softmax(s)_t v_t            */
+/* over t in [0, P) plus t = P + j for new token j visible from i: j <= i (CAUSAL) or    */
+/* bit j of tree row i (TREE).  lse = log sum_t exp(s_t) (natural log).                  */
+/* Layout (element strides; the D elements of a row are contiguous):                     */
+/*   q    [B][n_q][Hq][D] at q + b*q_sb + i*q_st + h*q_sh                                */
+/*   k, v cache of sequence b starts at element kv_off[b] (device int64 [B]); token t of */
+/*        KV head g is at kv_off[b] + g*kv_sh + t*kv_st.  The cache must hold P + n_q     */
+/*        tokens: the keys/values of the n_q new tokens are written before this call.    */
+/*   prefix_len  device int32 [B];  max_prefix (host) must bound every prefix_len[b]:    */
+/*        it sizes the launch; a sequence whose P exceeds it gets NaN output rows.        */
+/*   tree_bits   TREE only: device uint32 rows as produced by sv_build_tree_mask, for    */
+/*        n_q nodes; sequence b uses tree_bits + b*tree_sb (tree_sb = 0: one shared tree).*/
+/*   out  [B][n_q][Hq][D] of `dtype` at out + b*o_sb + i*o_st + h*o_sh                   */
+/*   lse  optional fp32 [B][n_q][Hq] contiguous, or NULL                                 */
+/* dtype: SV_BF16 (bf16 in and out, fp32 accumulation, MFMA) or SV_F32 (fp32 throughout).*/
+/* split_keys: keys per work split (a tuning knob, rounded up to the kernel's tile        */
+/*        granularity); 0 picks a split that fills the GPU.                              */
+/* Supported: D in {64, 128}; Hq % Hkv == 0; n_q >= 1.  bf16 also needs 16-byte aligned  */
+/* q, k, v, strides and kv_off[b] that are multiples of 8 elements, and out and its      */
+/* strides aligned to 4 elements (else SV_ERR_UNSUPPORTED; kv_off is not checked).       */
+/* ---------------------------------------------------------------------------------- */
+typedef struct sv_attn_desc {
+    sv_dtype dtype;
+    sv_mask mask;
+    int32_t B, n_q, Hq, Hkv, D;
+    int32_t max_prefix;
+    int32_t split_keys;
+    float scale;
+    const void *q;
+    int64_t q_sb, q_st, q_sh;
+    const void *k;
+    const void *v;
+    const int64_t *kv_off;
+    int64_t kv_sh, kv_st;
+    const int32_t *prefix_len;
+    const uint32_t *tree_bits;
+    int64_t tree_sb;
+    void *out;
+    int64_t o_sb, o_st, o_sh;
+    float *lse;
+} sv_attn_desc;
+
+SV_API size_t sv_verify_attention_workspace(const sv_attn_desc *desc);
+SV_API sv_status sv_verify_attention(const sv_attn_desc *desc, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+/* ---------------------------------------------------------------------------------- */
+/* sv_spec_accept -- acceptance of one round for B sequences of gamma drafts each.       */
+/* GREEDY: [TB] box "A round of greedy speculative decoding": z_i = argmax of target row */
+/*   i (raw fp32 logits, ties -> lowest id); J = number of leading drafts with x_i = z_i;*/
+/*   emit x_0..x_{J-1} then z_J.  Draft logits are not read (may be NULL).               */
+/* SAMPLE: [TB] boxes "The speculative sampling rule" and "A round of speculative        */
+/*   sampling"; [AG] "Speculative sampling".  p_i = softmax(target_i / T),               */
+/*   q_i = softmax(draft_i / T) (the same temperature on both models);                   */
+/*   for i = 0..gamma-1 accept x_i iff u_i * q_i(x_i) < p_i(x_i), u_i the Philox uniform */
+/*   (index i, tag 0x53560001), stopping at the first rejection; J = number accepted.    */
+/*   The extra token is an inverse-CDF draw in token-id order, with the uniform of index */
+/*   gamma, from r = max(0, p_J - q_J) when J < gamma, else from p_gamma ([TB] section   */
+/*   "Speculative verification in PyTorch": a zero draft row after the last draft).      */
+/*   A residual with zero mass falls back to p_J.                                        */
+/* Precision: exponentials in fp32, sums and the CDF in fp64; a decision can differ from */
+/* exact arithmetic only when its uniform lies within about 1e-6 of its threshold.       */
+/*   target_logits device fp32 [B][gamma+1][V]; draft_logits fp32 [B][gamma][V] (SAMPLE)*/
+/*   draft_tokens  device int32 [B][gamma], each in [0, V)                               */
+/*   accept_len    device int32 [B] = J                                                  */
+/*   out_tokens    device int32 [B][gamma+1]: J accepted drafts, the extra token, then -1*/
+/*   alpha         optional device fp32 [B][gamma]: sum_x min(p_i, q_i) ([TB] "The       */
+/*                 speculative sampling rule"); SAMPLE only (NaN under GREEDY); NULL     */
+/*                 skips its extra pass over the rows                                    */
+/*   dev_status    optional device int32 [B]: 0, or 2 when a draft token is outside      */
+/*                 [0, V) (that sequence's outputs are then unspecified)                 */
+/* Supported: 1 <= gamma <= 64, 1 <= V.                                                  */
+/* ---------------------------------------------------------------------------------- */
+typedef struct sv_accept_desc {
+    sv_mode mode;
+    int32_t B, gamma, V;
+    float temperature;
+    const float *target_logits;
+    const float *draft_logits;
+    const int32_t *draft_tokens;
+    sv_philox rng;
+    int32_t *accept_len;
+    int32_t *out_tokens;
+    float *alpha;
+    int32_t *dev_status;
+} sv_accept_desc;
+
+SV_API size_t sv_spec_accept_workspace(const sv_accept_desc *desc);
+SV_API sv_status sv_spec_accept(const sv_accept_desc *desc, void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+/* ---------------------------------------------------------------------------------- */
+/* sv_tree_walk -- verification of a token tree by a walk from the root.                 */
+/* GREEDY: [TB] section "Token trees check several guesses at once": start at the root,  */
+/*   move to the child equal to the target's choice, repeat, and at the first node with  */
+/*   no such child emit the target's choice.  SAMPLE: [MED] section "Attention Tree":    */
+/*   sample from the target at the node, look for that token among its children, and go  */
+/*   down level by level until no child matches.                                         */
+/* Node 0 is the root (the last committed token, parent -1); row v of the logits is the  */
+/* target's next-token distribution after node v.  At depth d the choice at node v is    */
+/* argmax(logits[v]) (GREEDY) or an inverse-CDF draw from softmax(logits[v] / T) with    */
+/* the Philox uniform (index d, tag 0x53560002) (SAMPLE); the walk moves to the first    */
+/* child of v in node order whose token equals it.                                       */
+/*   logits   device fp32 [B][n][V];  tokens device int32 [B][n];                        */
+/*   parents  device int32 [n], shared by the batch (parents[0] == -1, parents[i] < i)   */
+/*   max_depth (host): the depth of the deepest node (capacity of path and out_tokens)   */
+/*   accept_len device int32 [B] = J (accepted nodes)                                    */
+/*   path       device int32 [B][max_depth+1] = (0, n_1, ..., n_J, -1, ...)              */
+/*   out_tokens device int32 [B][max_depth+1] = (tokens of n_1..n_J, the choice at n_J,  */
+/*              -1, ...)                                                                 */
+/*   dev_status optional device int32 [B]: 0, or 3 when the walk would go below         */
+/*              max_depth (outputs then stop at max_depth)                               */
+/* Supported: 1 <= n, 0 <= max_depth <= 63, 1 <= V.                                      */
+/* ---------------------------------------------------------------------------------- */
+typedef struct sv_walk_desc {
+    sv_mode mode;
+    int32_t B, n, V, max_depth;
+    float temperature;
+    const float *logits;
+    const int32_t *tokens;
+    const int32_t *parents;
+    sv_philox rng;
+    int32_t *accept_len;
+    int32_t *path;
+    int32_t *out_tokens;
+    int32_t *dev_status;
+} sv_walk_desc;
+
+SV_API size_t sv_tree_walk_workspace(const sv_walk_desc *desc);
+SV_API sv_status sv_tree_walk(const sv_walk_desc *desc, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+/* Human-readable name of a status code (static storage). */
+SV_API const char *sv_status_string(sv_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

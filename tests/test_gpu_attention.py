@@ -1,0 +1,175 @@
+"""GPU parity of sv_verify_attention against the fp64 oracle.
+
+Tolerances (max-abs against fp64): 2e-2 for bf16 inputs, 1e-4 for fp32; the log-sum-exp
+within 1e-3 (bf16) / 1e-5 (fp32).  Besides the workloads' own input scale, every shape
+also runs with unscaled N(0,1) Q/K/V and with a 3x query scale, so the softmax is far
+from uniform and the running-max rescaling is exercised.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from svgpu import attention_on_gpu, rows_of  # noqa: E402
+
+BF16_TOL, F32_TOL = 2e-2, 1e-4
+
+
+def _compare(inp, scale, tree_bits=None, tree_sb=0, rows=None, split_keys=0, max_prefix=None):
+    tol = BF16_TOL if inp["dtype"] == "bf16" else F32_TOL
+    ltol = 1e-3 if inp["dtype"] == "bf16" else 1e-5
+    ref, ref_lse, rows = oracle.attention(inp, scale=scale, tree_bits=tree_bits, tree_sb=tree_sb, rows=rows)
+    out, lse = attention_on_gpu(inp, scale, tree_bits=tree_bits, tree_sb=tree_sb, split_keys=split_keys,
+                                max_prefix=max_prefix)
+    got = rows_of(out, rows)
+    got_lse = rows_of(lse, rows)
+    err = np.abs(got - ref).max()
+    lerr = np.abs(got_lse - ref_lse).max()
+    print("rows=%d max_abs=%.3g (max|O|=%.3g) lse_err=%.3g" % (len(rows), err, np.abs(ref).max(), lerr))
+    assert np.isfinite(got).all()
+    assert err <= tol, err
+    assert lerr <= ltol, lerr
+    return err
+
+
+CHAIN_SHAPES = [
+    # B, n_q, Hq, Hkv, D, prefix lengths
+    (1, 5, 2, 2, 64, [128]),
+    (1, 1, 8, 8, 128, [0]),
+    (1, 6, 32, 8, 128, [4096]),
+    (2, 2, 4, 1, 64, [1, 63]),
+    (3, 5, 32, 8, 128, [64, 65, 1000]),
+    (1, 17, 8, 2, 128, [333]),
+    (2, 8, 8, 1, 64, [31, 2047]),
+    (1, 5, 4, 4, 128, [5000]),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", CHAIN_SHAPES, ids=lambda s: "B%d_nq%d_H%d-%d_D%d_P%s" % (s[0], s[1], s[2], s[3], s[4], s[5]))
+@pytest.mark.parametrize("qkv", ["unit", "workload", "sharp"])
+def test_chain_parity(dtype, shape, qkv):
+    B, n_q, Hq, Hkv, D, P = shape
+    qkv_scale = {"unit": 1.0, "workload": 1 / math.sqrt(128), "sharp": 1.0}[qkv]
+    q_scale = 3.0 if qkv == "sharp" else 1.0
+    inp = synth.attention_inputs(7 + B + n_q, B=B, n_q=n_q, Hq=Hq, Hkv=Hkv, D=D, prefix_len=P, dtype=dtype,
+                                 qkv_scale=qkv_scale, q_scale=q_scale)
+    _compare(inp, 1.0 / math.sqrt(D))
+
+
+@pytest.mark.parametrize("split_keys", [32, 128, 1000, 8192])
+def test_chain_split_variants(split_keys):
+    inp = synth.attention_inputs(21, B=2, n_q=6, Hq=32, Hkv=8, D=128, prefix_len=[4096, 777], dtype="bf16")
+    _compare(inp, 1 / math.sqrt(128), split_keys=split_keys)
+
+
+def test_workload_8b_chain_full():
+    cfg = synth.WORKLOADS[2]
+    n_q = cfg["gamma"] + 1
+    inp = synth.attention_inputs(2, B=1, n_q=n_q, Hq=cfg["Hq"], Hkv=cfg["Hkv"], D=cfg["D"],
+                                 prefix_len=synth.prefix_lengths(2, cfg), dtype="bf16", qkv_scale=cfg["qkv_scale"])
+    _compare(inp, 1 / math.sqrt(cfg["D"]))
+
+
+def test_workload_tiny_fp32_full():
+    cfg = synth.WORKLOADS[1]
+    inp = synth.attention_inputs(1, B=1, n_q=cfg["gamma"] + 1, Hq=cfg["Hq"], Hkv=cfg["Hkv"], D=cfg["D"],
+                                 prefix_len=synth.prefix_lengths(1, cfg), dtype="f32")
+    _compare(inp, 1 / math.sqrt(cfg["D"]))
+
+
+def test_workload_batched_chain_sampled_rows():
+    cfg = synth.WORKLOADS[4]
+    n_q = cfg["gamma"] + 1
+    P = synth.prefix_lengths(4, cfg)
+    inp = synth.attention_inputs(4, B=cfg["B"], n_q=n_q, Hq=cfg["Hq"], Hkv=cfg["Hkv"], D=cfg["D"], prefix_len=P,
+                                 dtype="bf16", qkv_scale=1.0)
+    r = np.random.default_rng(0)
+    rows = np.stack([r.integers(0, cfg["B"], 400), r.integers(0, n_q, 400), r.integers(0, cfg["Hq"], 400)], 1)
+    _compare(inp, 1 / math.sqrt(cfg["D"]), rows=rows, max_prefix=cfg["P_hi"])
+
+
+TREE_CASES = [
+    # seed, n, P, Hq, Hkv, D, branch
+    (0, 6, 7, 2, 1, 64, 0.7),
+    (1, 33, 100, 8, 2, 128, 0.6),
+    (2, 65, 2048, 32, 8, 128, 0.8),
+    (3, 200, 64, 4, 4, 64, 0.9),
+    (4, 1, 50, 8, 8, 128, 0.5),
+]
+
+
+@pytest.mark.parametrize("case", TREE_CASES, ids=lambda c: "n%d_P%d_H%d-%d_D%d" % c[1:6])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_tree_parity(case, dtype):
+    seed, n, P, Hq, Hkv, D, br = case
+    parents = synth.random_tree(seed, n, branch_p=br)
+    if n > 10:
+        parents[7] = -1                           # a forest
+    bits, _, _ = oracle.tree_mask(parents, P)
+    inp = synth.attention_inputs(seed, B=2, n_q=n, Hq=Hq, Hkv=Hkv, D=D, prefix_len=[P, P // 2 + 1], dtype=dtype)
+    _compare(inp, 1 / math.sqrt(D), tree_bits=bits, tree_sb=0)
+
+
+def test_tree_per_sequence_masks():
+    n, P = 40, 300
+    bits = [oracle.tree_mask(synth.random_tree(s, n, branch_p=0.5 + 0.1 * s), P)[0] for s in range(3)]
+    tb = np.stack(bits)
+    inp = synth.attention_inputs(9, B=3, n_q=n, Hq=16, Hkv=4, D=128, prefix_len=[P, P, P], dtype="bf16")
+    _compare(inp, 1 / math.sqrt(128), tree_bits=tb, tree_sb=tb.shape[1] * tb.shape[2])
+
+
+def test_chain_equals_tree_of_chain_on_gpu():
+    n, P = 9, 500
+    inp = synth.attention_inputs(5, B=2, n_q=n, Hq=8, Hkv=2, D=128, prefix_len=[P, P], dtype="bf16", qkv_scale=1.0)
+    bits, _, _ = oracle.tree_mask(np.arange(n) - 1, P)
+    a, la = attention_on_gpu(inp, 0.1)
+    b, lb = attention_on_gpu(inp, 0.1, tree_bits=bits)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def test_workload_medusa_tree_full():
+    cfg = synth.WORKLOADS[3]
+    parents, _ = synth.build_tree(cfg)
+    n = len(parents)
+    bits, _, _ = oracle.tree_mask(parents, cfg["P"])
+    inp = synth.attention_inputs(3, B=1, n_q=n, Hq=cfg["Hq"], Hkv=cfg["Hkv"], D=cfg["D"],
+                                 prefix_len=[cfg["P"]], dtype="bf16", qkv_scale=1.0)
+    _compare(inp, 1 / math.sqrt(cfg["D"]), tree_bits=bits)
+
+
+def test_workload_cartesian_tree_sampled_rows():
+    cfg = synth.WORKLOADS[5]
+    parents, _ = synth.build_tree(cfg)
+    n = len(parents)
+    bits, _, _ = oracle.tree_mask(parents, cfg["P"])
+    inp = synth.attention_inputs(5, B=1, n_q=n, Hq=cfg["Hq"], Hkv=cfg["Hkv"], D=cfg["D"],
+                                 prefix_len=[cfg["P"]], dtype="bf16", qkv_scale=1.0)
+    r = np.random.default_rng(1)
+    nodes = np.concatenate([np.arange(10), r.integers(0, n, 150), np.arange(n - 10, n)])
+    rows = np.stack([np.zeros_like(nodes), nodes, r.integers(0, cfg["Hq"], len(nodes))], 1)
+    _compare(inp, 1 / math.sqrt(cfg["D"]), tree_bits=bits, rows=rows)
+
+
+def test_prefix_beyond_bound_gives_nan():
+    inp = synth.attention_inputs(6, B=2, n_q=4, Hq=8, Hkv=2, D=128, prefix_len=[100, 900], dtype="bf16")
+    out, lse = attention_on_gpu(inp, 0.1, max_prefix=100, split_keys=128)
+    assert np.isfinite(out[0]).all()
+    assert np.isnan(out[1]).all() and np.isnan(lse[1]).all()
+
+
+def test_deterministic_repeats():
+    inp = synth.attention_inputs(8, B=1, n_q=6, Hq=32, Hkv=8, D=128, prefix_len=[4096], dtype="bf16")
+    first, fl = attention_on_gpu(inp, 0.088)
+    for _ in range(5):
+        o, l = attention_on_gpu(inp, 0.088)
+        assert np.array_equal(o, first) and np.array_equal(l, fl)

@@ -1,0 +1,136 @@
+"""GPU parity of sv_build_tree_mask and sv_tree_walk against the fp64 oracle.
+
+Masks, depths and position ids are bit-exact; walk paths and tokens are bit-exact except
+in sequences the oracle flags as near-threshold draws (counted and reported).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import draft_token_verification_attention_amd as sv  # noqa: E402
+from svgpu import dev_array, to_host  # noqa: E402
+
+GREEDY, SAMPLE = sv.SV_GREEDY, sv.SV_SAMPLE
+
+
+def _mask_on_gpu(parents, P):
+    bits, depth, pos, st = sv.sv_build_tree_mask(dev_array(np.asarray(parents, np.int32)), P)
+    torch.cuda.synchronize()
+    return bits.cpu().numpy().view(np.uint32), depth.cpu().numpy(), pos.cpu().numpy(), int(st.cpu()[0])
+
+
+@pytest.mark.parametrize("case", ["page", "chain1", "chain70", "random513", "forest", "medusa", "cartesian"])
+def test_tree_mask_parity(case):
+    P = 17
+    if case == "page":
+        parents = np.array([-1, -1, 0, 0, 1, 2])
+    elif case == "chain1":
+        parents = np.array([-1])
+    elif case == "chain70":
+        parents = np.arange(70) - 1
+    elif case == "random513":
+        parents = synth.random_tree(3, 513, branch_p=0.8)
+    elif case == "forest":
+        parents = synth.random_tree(4, 300, branch_p=0.5)
+        parents[[10, 77, 200]] = -1
+    elif case == "medusa":
+        parents, _ = synth.build_tree(synth.WORKLOADS[3])
+    else:
+        parents, _ = synth.build_tree(synth.WORKLOADS[5])
+    bits, depth, pos = oracle.tree_mask(parents, P)
+    gb, gd, gp, st = _mask_on_gpu(parents, P)
+    assert st == 0
+    assert np.array_equal(gb, bits) and np.array_equal(gd, depth) and np.array_equal(gp, pos)
+
+
+@pytest.mark.parametrize("bad,first", [([-1, 0, 5, 1], 3), ([-1, 0, 1, -2, 7], 4), ([0], 1), ([-1, 1], 2)])
+def test_tree_mask_bad_parents(bad, first):
+    _, _, _, st = _mask_on_gpu(bad, 3)
+    assert st == first
+
+
+def _walk_both(mode, lg, toks, parents, tau, seed, step=0, stream_ids=None, max_depth=None):
+    if max_depth is None:
+        max_depth = int(oracle.tree_mask(parents, 0)[1].max())
+    ref = oracle.tree_walk(mode, lg, toks, parents, tau, seed=seed, step=step, stream_ids=stream_ids,
+                           max_depth=max_depth)
+    got = to_host(sv.sv_tree_walk(mode, dev_array(lg), dev_array(toks.astype(np.int32)),
+                                  dev_array(np.asarray(parents, np.int32)), max_depth, tau, seed, step,
+                                  None if stream_ids is None else dev_array(np.asarray(stream_ids, np.int64))))
+    return ref, got
+
+
+def _assert_walk_parity(ref, got, label=""):
+    flagged = ref["flags"] != 0
+    same = ((ref["accept_len"] == got["accept_len"]) & np.all(ref["path"] == got["path"], 1)
+            & np.all(ref["out_tokens"] == got["out_tokens"], 1))
+    bad = ~same & ~flagged
+    print("%s walks=%d near-threshold=%d mismatched(near)=%d mismatched(other)=%d mean J=%.3f"
+          % (label, len(same), flagged.sum(), (~same & flagged).sum(), bad.sum(), got["accept_len"].mean()))
+    assert not bad.any(), np.nonzero(bad)[0][:10]
+    assert np.all(got["status"] == 0)
+
+
+@pytest.mark.parametrize("mode", [GREEDY, SAMPLE])
+@pytest.mark.parametrize("seed,n,V,br", [(0, 12, 16, 0.5), (1, 65, 1000, 0.8), (2, 200, 4097, 0.9), (3, 40, 7, 0.3)])
+def test_walk_parity_random_trees(mode, seed, n, V, br):
+    parents = synth.random_tree(seed, n, branch_p=br)
+    B = 32
+    lg = synth.tree_logits(seed, B, n, V, 3.0)
+    toks = synth.node_tokens(seed, lg, parents)
+    for step in range(3):
+        ref, got = _walk_both(mode, lg, toks, parents, 0.7, seed=21, step=step)
+        _assert_walk_parity(ref, got, "seed %d step %d" % (seed, step))
+
+
+@pytest.mark.parametrize("mode", [GREEDY, SAMPLE])
+def test_walk_workload_medusa(mode):
+    cfg = synth.WORKLOADS[3]
+    parents, paths = synth.build_tree(cfg)
+    n = len(parents)
+    lg = synth.tree_logits(3, 1, n, cfg["V"], cfg["target_var"])
+    toks = synth.node_tokens(3, lg, parents, synth.path_ranks(paths))
+    for step in range(10):
+        ref, got = _walk_both(mode, lg, toks, parents, cfg["tau"], seed=1003, step=step)
+        _assert_walk_parity(ref, got, "medusa step %d" % step)
+
+
+@pytest.mark.parametrize("mode", [GREEDY, SAMPLE])
+def test_walk_workload_cartesian_full(mode):
+    cfg = synth.WORKLOADS[5]
+    parents, paths = synth.build_tree(cfg)
+    n = len(parents)
+    lg = synth.tree_logits(5, 1, n, cfg["V"], cfg["target_var"])
+    toks = synth.node_tokens(5, lg, parents, synth.path_ranks(paths))
+    for step in range(4):
+        ref, got = _walk_both(mode, lg, toks, parents, cfg["tau"], seed=1005, step=step)
+        _assert_walk_parity(ref, got, "cartesian step %d" % step)
+
+
+def test_walk_too_deep_sets_status():
+    parents = np.arange(4) - 1
+    lg = np.zeros((1, 4, 3), dtype=np.float32)
+    lg[0, :, 1] = 5.0
+    toks = np.ones((1, 4), dtype=np.int32)
+    got = to_host(sv.sv_tree_walk(GREEDY, dev_array(lg), dev_array(toks), dev_array(parents.astype(np.int32)),
+                                  2, 1.0, 0))
+    assert got["status"][0] == 3 and got["accept_len"][0] == 2
+
+
+def test_chain_tree_walk_equals_greedy_accept_on_gpu():
+    B, gamma, V = 64, 5, 3000
+    a = synth.accept_inputs(6, B=B, gamma=gamma, V=V, target_var=3.0, noise_var=0.2, tau=1.0, greedy_drafts=True)
+    toks = np.concatenate([np.zeros((B, 1), np.int32), a["draft_tokens"]], 1)
+    w = to_host(sv.sv_tree_walk(GREEDY, dev_array(a["target"]), dev_array(toks),
+                                dev_array((np.arange(gamma + 1) - 1).astype(np.int32)), gamma, 1.0, 0))
+    g = to_host(sv.sv_spec_accept(GREEDY, dev_array(a["target"]), None, dev_array(a["draft_tokens"]), 1.0, 0))
+    assert np.array_equal(w["accept_len"], g["accept_len"])
+    assert np.array_equal(w["out_tokens"], g["out_tokens"])
