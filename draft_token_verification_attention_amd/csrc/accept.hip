@@ -45,7 +45,7 @@ struct ResPart {
 };
 
 struct AcceptWs {
-    int *cnt_stats, *cnt_alpha, *cnt_sample;
+    int *cnt;  // [B]: one completion counter per sequence, shared by the call's kernels in turn
     RowPart *part;      // [B][rows][nchunk]
     RowStat *rowstat;   // [B][rows]
     SeqState *seq;      // [B]
@@ -80,7 +80,7 @@ static WsLayout accept_layout(int B, int gamma, int V)
     WsLayout L;
     size_t o = 0;
     L.cnt = o;
-    o += align256(3 * (size_t)B * sizeof(int));
+    o += kCounterBytes;
     L.part = o;
     o += align256((size_t)B * rows * nchunk * sizeof(RowPart));
     L.rowstat = o;
@@ -118,12 +118,12 @@ __device__ void decide_greedy(const AcceptArgs &a, const AcceptWs &w, int b)
         firstbad = g;
         bad = 0;
     }
-    for (int r = threadIdx.x; r <= g; r += blockDim.x) {
-        const RowPart *pp = w.part + ((int64_t)b * a.rows + r) * a.nchunk;
-        float v = pp[0].m;
-        int idx = pp[0].arg;
-        for (int c = 1; c < a.nchunk; ++c) argmax_merge(v, idx, pp[c].m, pp[c].arg);
-        z[r] = idx;
+    const int wave = threadIdx.x / kWave, nwaves = blockDim.x / kWave;
+    for (int r = wave; r <= g; r += nwaves) {
+        float v;
+        int idx;
+        wave_combine_argmax(w.part + ((int64_t)b * a.rows + r) * a.nchunk, a.nchunk, v, idx);
+        if (threadIdx.x % kWave == 0) z[r] = idx;
     }
     __syncthreads();
     for (int i = threadIdx.x; i < g; i += blockDim.x) {
@@ -153,16 +153,16 @@ __device__ void decide_sample(const AcceptArgs &a, const AcceptWs &w, int b)
         firstbad = g;
         bad = 0;
     }
-    for (int r = threadIdx.x; r < a.rows; r += blockDim.x) {
-        const RowPart *pp = w.part + ((int64_t)b * a.rows + r) * a.nchunk;
-        float M = pp[0].m;
-        for (int c = 1; c < a.nchunk; ++c) M = fmaxf(M, pp[c].m);
-        double Z = 0.0;
-        for (int c = 0; c < a.nchunk; ++c)
-            if (pp[c].s > 0.0) Z += pp[c].s * exp2(((double)pp[c].m - (double)M) * a.kd);
-        sM[r] = (double)M;
-        sZ[r] = Z;
-        w.rowstat[(int64_t)b * a.rows + r] = RowStat{(double)M, Z};
+    const int wave = threadIdx.x / kWave, nwaves = blockDim.x / kWave;
+    for (int r = wave; r < a.rows; r += nwaves) {
+        float M;
+        double Z;
+        wave_combine_softmax(w.part + ((int64_t)b * a.rows + r) * a.nchunk, a.nchunk, a.kd, M, Z);
+        if (threadIdx.x % kWave == 0) {
+            sM[r] = (double)M;
+            sZ[r] = Z;
+            w.rowstat[(int64_t)b * a.rows + r] = RowStat{(double)M, Z};
+        }
     }
     __syncthreads();
     const uint64_t stream = stream_of(a, b);
@@ -240,8 +240,13 @@ __global__ __launch_bounds__(kRowThreads) void accept_stats_kernel(AcceptArgs a,
         part.arg = 0;
         part.s = s;
     }
-    if (threadIdx.x == 0) w.part[((int64_t)b * a.rows + r) * a.nchunk + c] = part;
-    if (!arrive_last(&w.cnt_stats[b], a.rows * a.nchunk, &last_flag)) return;
+    if (threadIdx.x == 0) {
+        RowPart *dst = w.part + ((int64_t)b * a.rows + r) * a.nchunk + c;
+        st_coherent(&dst->m, part.m);
+        st_coherent(&dst->arg, part.arg);
+        st_coherent(&dst->s, part.s);
+    }
+    if (!arrive_last(&w.cnt[b], a.rows * a.nchunk, &last_flag)) return;
     if (SAMPLE)
         decide_sample(a, w, b);
     else
@@ -273,8 +278,8 @@ __global__ __launch_bounds__(kRowThreads) void accept_alpha_kernel(AcceptArgs a,
         s += fmin(p, q);
     }
     s = block_sum(s, dscr);
-    if (threadIdx.x == 0) w.apart[((int64_t)b * g + i) * a.nchunk + c] = s;
-    if (!arrive_last(&w.cnt_alpha[b], g * a.nchunk, &last_flag)) return;
+    if (threadIdx.x == 0) st_coherent(&w.apart[((int64_t)b * g + i) * a.nchunk + c], s);
+    if (!arrive_last(&w.cnt[b], g * a.nchunk, &last_flag)) return;
     for (int j = threadIdx.x; j < g; j += blockDim.x) {
         double t = 0.0;
         for (int cc = 0; cc < a.nchunk; ++cc) t += w.apart[((int64_t)b * g + j) * a.nchunk + cc];
@@ -318,41 +323,34 @@ __global__ __launch_bounds__(kRowThreads) void accept_sample_kernel(AcceptArgs a
     }
     rs = block_sum(rs, dscr);
     ps = block_sum(ps, dscr);
-    if (threadIdx.x == 0) w.res[(int64_t)b * a.nchunk + c] = ResPart{rs, ps};
-    if (!arrive_last(&w.cnt_sample[b], a.nchunk, &last_flag)) return;
-
-    // last block: locate the chunk holding u* Z, then scan it in token order
     if (threadIdx.x == 0) {
+        st_coherent(&w.res[(int64_t)b * a.nchunk + c].r, rs);
+        st_coherent(&w.res[(int64_t)b * a.nchunk + c].p, ps);
+    }
+    if (!arrive_last(&w.cnt[b], a.nchunk, &last_flag)) return;
+
+    // last block: locate the chunk holding u* Z (wave 0), then scan it in token order
+    if (threadIdx.x < kWave) {
         const ResPart *rp = w.res + (int64_t)b * a.nchunk;
-        double Zr = 0.0;
-        for (int cc = 0; cc < a.nchunk; ++cc) Zr += rp[cc].r;
-        const int usep = !(Zr > 0.0);
-        double Z = 0.0;
-        if (usep)
-            for (int cc = 0; cc < a.nchunk; ++cc) Z += rp[cc].p;
-        else
-            Z = Zr;
-        const double u = philox_uniform(a.seed, (uint64_t)g, a.step, stream_of(a, b), kTagAccept);
-        const double target = u * Z;
-        double cum = 0.0;
-        int found = -1, lastpos = 0;
-        double base_found = 0.0, base_last = 0.0;
-        for (int cc = 0; cc < a.nchunk; ++cc) {
-            const double wgt = usep ? rp[cc].p : rp[cc].r;
-            if (wgt > 0.0) {
-                lastpos = cc;
-                base_last = cum;
-            }
-            if (found < 0 && cum + wgt > target) {
-                found = cc;
-                base_found = cum;
-            }
-            cum += wgt;
+        double zr = 0.0, zp = 0.0;
+        for (int cc = threadIdx.x; cc < a.nchunk; cc += kWave) {
+            zr += rp[cc].r;
+            zp += rp[cc].p;
         }
-        s_chunk = found >= 0 ? found : lastpos;
-        s_base = found >= 0 ? base_found : base_last;
-        s_target = target;
-        s_usep = usep;
+        zr = wave_sum(zr);
+        zp = wave_sum(zp);
+        const bool usep = !(zr > 0.0);
+        const double u = philox_uniform(a.seed, (uint64_t)g, a.step, stream_of(a, b), kTagAccept);
+        const double target = u * (usep ? zp : zr);
+        int chunk;
+        double cbase;
+        wave_find_chunk(a.nchunk, target, [&](int cc) { return usep ? rp[cc].p : rp[cc].r; }, chunk, cbase);
+        if (threadIdx.x == 0) {
+            s_chunk = chunk;
+            s_base = cbase;
+            s_target = target;
+            s_usep = usep;
+        }
     }
     __syncthreads();
     const int cs = s_chunk;
@@ -401,14 +399,13 @@ extern "C" sv_status sv_spec_accept(const sv_accept_desc *d, void *workspace, si
     if (!d->target_logits || !d->draft_tokens || !d->accept_len || !d->out_tokens) return SV_ERR_INVALID_ARG;
     if (sample && !d->draft_logits) return SV_ERR_INVALID_ARG;
     if (d->B == 0) return SV_OK;
+    if (d->B > kMaxCounters) return SV_ERR_UNSUPPORTED;
     const WsLayout L = accept_layout(d->B, d->gamma, d->V);
     if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace & 255)) return SV_ERR_WORKSPACE;
 
     char *ws = (char *)workspace;
     AcceptWs w;
-    w.cnt_stats = (int *)(ws + L.cnt);
-    w.cnt_alpha = w.cnt_stats + d->B;
-    w.cnt_sample = w.cnt_alpha + d->B;
+    w.cnt = (int *)(ws + L.cnt);
     w.part = (RowPart *)(ws + L.part);
     w.rowstat = (RowStat *)(ws + L.rowstat);
     w.seq = (SeqState *)(ws + L.seq);

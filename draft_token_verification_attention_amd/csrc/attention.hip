@@ -372,48 +372,67 @@ __global__ __launch_bounds__(64 * NWR * NWK) void attn_bf16_kernel(AttnArgs a)
     }
 
     // ---- split partial: unnormalized o, running max (log2 units), sum ----
-    if (active) {
+    if (active && row_ok) {
         float *pr = a.part + (((int64_t)gidx * a.nsplit + s) * ROWS_BLK + wr * 32 + l32) * (DH + 4);
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int a4 = 0; a4 < 4; ++a4) {
                 const int d = 32 * db + 8 * a4 + 4 * h;
-                *reinterpret_cast<float4 *>(pr + d) =
-                    make_float4(oacc[db][4 * a4 + 0], oacc[db][4 * a4 + 1], oacc[db][4 * a4 + 2], oacc[db][4 * a4 + 3]);
+                st_coherent4(pr + d, make_float4(oacc[db][4 * a4 + 0], oacc[db][4 * a4 + 1], oacc[db][4 * a4 + 2],
+                                                 oacc[db][4 * a4 + 3]));
             }
         if (h == 0) {
-            pr[DH] = m_run;
-            pr[DH + 1] = l_row;
+            st_coherent(pr + DH, m_run);
+            st_coherent(pr + DH + 1, l_row);
         }
     }
     if (!arrive_last(&a.cnt[gidx], ns, &s_last)) return;
 
-    // ---- last block: combine the ns partials of every row ----
+    // ---- last block: combine the ns partials of every row of the tile ----
+    // Per row: M = max_s m_s, L = sum_s l_s 2^(m_s - M); then O = sum_s o_s 2^(m_s - M) / L.
+    float *sM = reinterpret_cast<float *>(smem);
+    float *sInvL = sM + ROWS_BLK;
     const float *pg = a.part + (int64_t)gidx * a.nsplit * ROWS_BLK * (DH + 4);
-    for (int item = threadIdx.x; item < ROWS_BLK * (DH / 4); item += NT) {
-        const int r = item / (DH / 4);
-        const int d4 = item % (DH / 4);
-        const int row = rowbase + r;
-        if (row >= a.rows) continue;
+    const int nrows_tile = row_hi - rowbase + 1;
+    for (int r = threadIdx.x; r < nrows_tile; r += NT) {
         float M = -INFINITY;
+#pragma unroll 4
         for (int ss = 0; ss < ns; ++ss) M = fmaxf(M, pg[((int64_t)ss * ROWS_BLK + r) * (DH + 4) + DH]);
         float Lsum = 0.0f;
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
         for (int ss = 0; ss < ns; ++ss) {
             const float *pr = pg + ((int64_t)ss * ROWS_BLK + r) * (DH + 4);
             const float ms = pr[DH];
-            if (ms == -INFINITY) continue;
-            const float f = exp2f(ms - M);
-            Lsum += pr[DH + 1] * f;
+            if (ms != -INFINITY) Lsum += pr[DH + 1] * exp2f(ms - M);
+        }
+        sM[r] = M;
+        sInvL[r] = overflow ? __int_as_float(0x7fc00000) : 1.0f / Lsum;
+        if (a.lse) {
+            const int row = rowbase + r;
+            a.lse[((int64_t)b * a.n_q + row / a.G) * a.Hq + kvh * a.G + row % a.G] =
+                overflow ? __int_as_float(0x7fc00000) : (M + log2f(Lsum)) * kLn2;
+        }
+    }
+    __syncthreads();
+    for (int item = threadIdx.x; item < nrows_tile * (DH / 4); item += NT) {
+        const int r = item / (DH / 4);
+        const int d4 = item % (DH / 4);
+        const float M = sM[r];
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+        for (int ss = 0; ss < ns; ++ss) {
+            const float *pr = pg + ((int64_t)ss * ROWS_BLK + r) * (DH + 4);
+            const float ms = pr[DH];
             const float4 o4 = *reinterpret_cast<const float4 *>(pr + 4 * d4);
+            const float f = ms == -INFINITY ? 0.0f : exp2f(ms - M);
             acc.x += o4.x * f;
             acc.y += o4.y * f;
             acc.z += o4.z * f;
             acc.w += o4.w * f;
         }
-        float inv = 1.0f / Lsum;
-        if (overflow) inv = __int_as_float(0x7fc00000);
+        const float inv = sInvL[r];
+        const int row = rowbase + r;
         const int i = row / a.G;
         const int hq = kvh * a.G + row % a.G;
         uint16_t *o = (uint16_t *)a.out + (int64_t)b * a.o_sb + (int64_t)i * a.o_st + (int64_t)hq * a.o_sh + 4 * d4;
@@ -421,9 +440,6 @@ __global__ __launch_bounds__(64 * NWR * NWK) void attn_bf16_kernel(AttnArgs a)
         pk.x = (uint32_t)f32_to_bf16(acc.x * inv) | ((uint32_t)f32_to_bf16(acc.y * inv) << 16);
         pk.y = (uint32_t)f32_to_bf16(acc.z * inv) | ((uint32_t)f32_to_bf16(acc.w * inv) << 16);
         *reinterpret_cast<uint2 *>(o) = pk;
-        if (a.lse && d4 == 0)
-            a.lse[((int64_t)b * a.n_q + i) * a.Hq + hq] =
-                overflow ? __int_as_float(0x7fc00000) : (M + log2f(Lsum)) * kLn2;
     }
 }
 
@@ -507,21 +523,33 @@ static bool plan_attention(const sv_attn_desc *d, Plan &p)
     p.KG = d->B * d->Hkv;
     p.kg_pad = (p.KG + 7) / 8 * 8;
     const int64_t Tmax = (int64_t)d->max_prefix + d->n_q;
-    const int unit = kTileKeys * p.NWK;  // split granularity
+    const int64_t groups = (int64_t)p.KG * p.RT > 0 ? (int64_t)p.KG * p.RT : 1;
+    const int64_t unit = kTileKeys;
     int64_t sk;
     if (d->split_keys > 0) {
         sk = ((int64_t)d->split_keys + unit - 1) / unit * unit;
-    } else {
-        // enough blocks to cover the chip twice over (256 CUs), at least one tile per wave
-        const int64_t want_blocks = 512;
-        const int64_t groups = (int64_t)p.KG * p.RT > 0 ? (int64_t)p.KG * p.RT : 1;
-        int64_t nsp = (want_blocks + groups - 1) / groups;
-        if (nsp < 1) nsp = 1;
+    } else if (p.variant == 1) {
+        // Few query rows: splitting keys is cheap (a partial is at most 32 rows), so cut
+        // each sequence until the groups fill one wave of blocks on the 256 CUs (one
+        // 4-wave block per CU fits), keeping splits between 128 and 4096 keys.
+        const int64_t nsp = (256 + groups - 1) / groups;
         sk = (Tmax + nsp - 1) / nsp;
+        sk = (sk + unit - 1) / unit * unit;
+        if (sk < 128) sk = 128;
+        if (sk > 4096) sk = 4096;
+    } else {
+        // Many rows per block: a partial costs as much as the keys it summarizes, so split
+        // only when there are too few row tiles to occupy the chip.
+        if (groups >= 256) {
+            sk = Tmax;
+        } else {
+            const int64_t nsp = (256 + groups - 1) / groups;
+            sk = (Tmax + nsp - 1) / nsp;
+        }
         sk = (sk + unit - 1) / unit * unit;
         if (sk < unit) sk = unit;
     }
-    if (sk > (int64_t)kMaxTiles * kTileKeys) sk = (int64_t)kMaxTiles * kTileKeys / unit * unit;
+    if (sk > (int64_t)kMaxTiles * kTileKeys) sk = (int64_t)kMaxTiles * kTileKeys;
     p.split_keys = (int)sk;
     const int64_t nsplit = (Tmax + sk - 1) / sk;
     if (nsplit > 65535) return false;
@@ -530,7 +558,8 @@ static bool plan_attention(const sv_attn_desc *d, Plan &p)
     if (blocks > 0x7fffffff) return false;
     p.blocks = (unsigned)blocks;
     const size_t D = (size_t)d->D;
-    p.cnt_bytes = align256((size_t)p.KG * p.RT * sizeof(int));
+    if ((int64_t)p.KG * p.RT > kMaxCounters) return false;
+    p.cnt_bytes = kCounterBytes;
     // partials exist even for one split: a sequence longer than max_prefix still merges
     // through them (to report NaN rows)
     p.part_bytes = align256((size_t)p.KG * p.RT * p.nsplit * rows_blk * (D + 4) * sizeof(float));

@@ -9,6 +9,13 @@
 namespace sv {
 
 constexpr int kWave = 64;
+
+// Every workspace starts with this fixed region of completion counters.  It must be zero
+// when a workspace is first used; every call leaves it zero again.  Partial results live
+// after it, so calls of any entry point and any shape can share one workspace (if they do
+// not overlap in time) without finding stale data where a counter should be.
+constexpr size_t kCounterBytes = 128 * 1024;
+constexpr int kMaxCounters = (int)(kCounterBytes / sizeof(int));
 constexpr uint64_t kTagAccept = 0x53560001ULL;
 constexpr uint64_t kTagWalk = 0x53560002ULL;
 
@@ -102,22 +109,55 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f)
     return (uint16_t)(u >> 16);
 }
 
-// Last-arriving block detection.  Every block of a group stores its partial
-// result, then calls this; exactly one caller (the last) gets true and may read
-// every partial.  The counter is reset to zero for the next call.
+// ---------------------------------------------------------------------------
+// Cross-block hand-off inside one kernel ("last block done").
+//
+// The L2 caches of the eight XCDs are not coherent with each other, and a device-scope
+// release fence (a full L2 writeback) per block serializes across the GPU at ~0.1 us per
+// block.  So the blocks that publish partial results write them with coherent stores
+// (agent-scope relaxed atomic stores: written through to the memory side), wait until
+// those stores are complete, and only then bump the group's counter.  The one block that
+// arrives last invalidates its own stale cache lines (agent-scope acquire) before it
+// reads the partials with ordinary loads.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void st_coherent(float *p, float v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coherent(int *p, int v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coherent(double *p, double v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coherent4(float *p, float4 v)
+{
+    st_coherent(p + 0, v.x);
+    st_coherent(p + 1, v.y);
+    st_coherent(p + 2, v.z);
+    st_coherent(p + 3, v.w);
+}
+
+// Every block of a group publishes its partial with st_coherent*, then calls this;
+// exactly one caller (the last) gets true and may then read every partial.  The
+// counter is reset to zero for the next use.
 __device__ __forceinline__ bool arrive_last(int *counter, int expected, int *lds_flag)
 {
-    __threadfence();
+    // this wave's coherent stores are complete (vector-memory counter drained) ...
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // ... and so are every other wave's
     __syncthreads();
     if (threadIdx.x == 0) {
-        const int old = atomicAdd(counter, 1);
+        const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const bool last = (old == expected - 1);
-        if (last) atomicExch(counter, 0);
+        if (last) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         *lds_flag = last ? 1 : 0;
     }
     __syncthreads();
     const bool last = *lds_flag != 0;
-    if (last) __threadfence();
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     return last;
 }
 

@@ -165,4 +165,73 @@ __device__ __forceinline__ int chunk_inverse_cdf(int chunk_base, int V, double b
     return r == 0x7fffffff ? -1 : r;
 }
 
+// Combine per-chunk row statistics with one wave: lanes stride over the chunks.
+//   max_arg: (largest value, lowest index among equals)
+//   softmax: M = max m_c, Z = sum_c S_c 2^((m_c - M) k)
+// Must be called by a whole wave; every lane gets the result.
+template <typename Part>
+__device__ __forceinline__ void wave_combine_argmax(const Part *pp, int nchunk, float &v, int &idx)
+{
+    const int lane = threadIdx.x % kWave;
+    v = -INFINITY;
+    idx = 0x7fffffff;
+    for (int c = lane; c < nchunk; c += kWave) argmax_merge(v, idx, pp[c].m, pp[c].arg);
+    wave_argmax(v, idx);
+}
+
+template <typename Part>
+__device__ __forceinline__ void wave_combine_softmax(const Part *pp, int nchunk, double kd, float &M, double &Z)
+{
+    const int lane = threadIdx.x % kWave;
+    float m = -INFINITY;
+    for (int c = lane; c < nchunk; c += kWave) m = fmaxf(m, pp[c].m);
+    M = wave_max(m);
+    double z = 0.0;
+    for (int c = lane; c < nchunk; c += kWave)
+        if (pp[c].s > 0.0) z += pp[c].s * exp2(((double)pp[c].m - (double)M) * kd);
+    // fixed-order reduction: deterministic
+    Z = wave_sum(z);
+}
+
+// Find the first chunk whose running weight passes `target` (one wave; chunk weights
+// come from weight(c)).  Returns the chunk and the running weight before it; when
+// rounding leaves every prefix at or below target, the last chunk with weight.
+template <typename WFn>
+__device__ __forceinline__ void wave_find_chunk(int nchunk, double target, WFn weight, int &chunk, double &base)
+{
+    const int lane = threadIdx.x % kWave;
+    double carry = 0.0;
+    int last_pos = -1;
+    double last_base = 0.0;
+    chunk = -1;
+    for (int c0 = 0; c0 < nchunk; c0 += kWave) {
+        const int c = c0 + lane;
+        const double w = c < nchunk ? weight(c) : 0.0;
+        // inclusive scan across the wave (fixed order)
+        double incl = w;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const double t = __shfl_up(incl, o);
+            if (lane >= o) incl += t;
+        }
+        const double excl = carry + incl - w;
+        const uint64_t pass = __ballot(c < nchunk && w > 0.0 && carry + incl > target);
+        const uint64_t pos = __ballot(c < nchunk && w > 0.0);
+        if (pos) {
+            const int lp = 63 - __clzll((unsigned long long)pos);
+            last_pos = c0 + lp;
+            last_base = __shfl(excl, lp);
+        }
+        if (pass) {
+            const int fl = __ffsll((unsigned long long)pass) - 1;
+            chunk = c0 + fl;
+            base = __shfl(excl, fl);
+            return;
+        }
+        carry += __shfl(incl, kWave - 1);
+    }
+    chunk = last_pos < 0 ? nchunk - 1 : last_pos;
+    base = last_pos < 0 ? 0.0 : last_base;
+}
+
 }  // namespace sv

@@ -54,7 +54,7 @@ static WalkLayout walk_layout(int B, int V)
     WalkLayout L;
     size_t o = 0;
     L.cnt = o;
-    o += align256((size_t)B * sizeof(int));
+    o += kCounterBytes;
     L.cur = o;
     o += align256((size_t)B * sizeof(int));
     L.done = o;
@@ -115,47 +115,44 @@ __global__ __launch_bounds__(kRowThreads) void walk_level_kernel(WalkArgs a, Wal
         part.arg = 0;
         part.s = s;
     }
-    if (threadIdx.x == 0) w.part[(int64_t)b * a.nchunk + c] = part;
+    if (threadIdx.x == 0) {
+        WalkPart *dst = w.part + (int64_t)b * a.nchunk + c;
+        st_coherent(&dst->m, part.m);
+        st_coherent(&dst->arg, part.arg);
+        st_coherent(&dst->s, part.s);
+    }
     if (!arrive_last(&w.cnt[b], a.nchunk, &last_flag)) return;
 
     // ---- last block of this sequence: the choice at node v ----
     const WalkPart *pp = w.part + (int64_t)b * a.nchunk;
     if (!SAMPLE) {
-        if (threadIdx.x == 0) {
-            float mv = pp[0].m;
-            int idx = pp[0].arg;
-            for (int cc = 1; cc < a.nchunk; ++cc) argmax_merge(mv, idx, pp[cc].m, pp[cc].arg);
-            s_y = idx;
+        if (threadIdx.x < kWave) {
+            float mv;
+            int idx;
+            wave_combine_argmax(pp, a.nchunk, mv, idx);
+            if (threadIdx.x == 0) s_y = idx;
         }
         __syncthreads();
     } else {
-        if (threadIdx.x == 0) {
-            float M = pp[0].m;
-            for (int cc = 1; cc < a.nchunk; ++cc) M = fmaxf(M, pp[cc].m);
-            double Z = 0.0;
-            for (int cc = 0; cc < a.nchunk; ++cc) Z += pp[cc].s * exp2(((double)pp[cc].m - (double)M) * a.kd);
+        if (threadIdx.x < kWave) {
+            float M;
+            double Z;
+            wave_combine_softmax(pp, a.nchunk, a.kd, M, Z);
             const uint64_t stream = a.stream_ids ? a.stream_ids[b] : (uint64_t)b;
             const double u = philox_uniform(a.seed, (uint64_t)d, a.step, stream, kTagWalk);
             const double target = u * Z;
-            double cum = 0.0;
-            int found = -1;
-            for (int cc = 0; cc < a.nchunk; ++cc) {
-                const double wc = pp[cc].s * exp2(((double)pp[cc].m - (double)M) * a.kd);
-                if (cum + wc > target) {
-                    found = cc;
-                    break;
-                }
-                cum += wc;
+            int found;
+            double cum;
+            wave_find_chunk(a.nchunk, target,
+                            [&](int cc) { return pp[cc].s * exp2(((double)pp[cc].m - (double)M) * a.kd); }, found,
+                            cum);
+            if (threadIdx.x == 0) {
+                s_chunk = found;
+                s_base = cum;
+                s_target = target;
+                s_factor = exp2(((double)pp[found].m - (double)M) * a.kd);
+                s_mc = pp[found].m;
             }
-            if (found < 0) {  // rounding: u*Z at the very top of the row
-                found = a.nchunk - 1;
-                cum -= pp[found].s * exp2(((double)pp[found].m - (double)M) * a.kd);
-            }
-            s_chunk = found;
-            s_base = cum;
-            s_target = target;
-            s_factor = exp2(((double)pp[found].m - (double)M) * a.kd);
-            s_mc = pp[found].m;
         }
         __syncthreads();
         const int cb = s_chunk * kChunk;
@@ -239,6 +236,7 @@ extern "C" sv_status sv_tree_walk(const sv_walk_desc *d, void *workspace, size_t
     if (!d->logits || !d->tokens || !d->parents || !d->accept_len || !d->path || !d->out_tokens)
         return SV_ERR_INVALID_ARG;
     if (d->B == 0) return SV_OK;
+    if (d->B > kMaxCounters) return SV_ERR_UNSUPPORTED;
     const WalkLayout L = walk_layout(d->B, d->V);
     if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace & 255)) return SV_ERR_WORKSPACE;
     char *ws = (char *)workspace;

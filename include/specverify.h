@@ -16,10 +16,13 @@
  *     SV_ERR_UNSUPPORTED or SV_ERR_WORKSPACE without touching the device.  Errors that
  *     only the data can show (a bad parent, a token id out of range) are written to the
  *     device status words the calls document.  A failed launch returns SV_ERR_HIP.
- *   - Workspaces: `*_workspace()` returns the byte size a call needs for a descriptor.
- *     The caller allocates it (device memory, 256-byte aligned) and must ZERO it once
- *     before its first use; every call leaves the workspace zeroed again.  A workspace
- *     may be reused by later calls on the same stream, never by overlapping calls.
+ *   - Workspaces: `*_workspace()` returns the byte size a call needs for a descriptor
+ *     (0 for a call that needs none, or for a descriptor the call would reject).  The
+ *     caller allocates it (device memory, 256-byte aligned).  Its first 128 KiB hold the
+ *     call's completion counters: they must be zero when the workspace is first used, and
+ *     every call leaves them zero again (partial results live after them).  So one
+ *     workspace, zero-filled once, may serve any sequence of calls of any entry point and
+ *     shape, provided the calls do not overlap in time (e.g. they share one stream).
  *   - The library allocates no memory and keeps no global state.
  *   - No C++ exception crosses this interface.
  */
@@ -167,7 +170,7 @@ SV_API sv_status sv_verify_attention(const sv_attn_desc *desc, void *workspace, 
 /*                 skips its extra pass over the rows                                    */
 /*   dev_status    optional device int32 [B]: 0, or 2 when a draft token is outside      */
 /*                 [0, V) (that sequence's outputs are then unspecified)                 */
-/* Supported: 1 <= gamma <= 64, 1 <= V.                                                  */
+/* Supported: 1 <= gamma <= 64, 1 <= V, B <= 32768.                                      */
 /* ---------------------------------------------------------------------------------- */
 typedef struct sv_accept_desc {
     sv_mode mode;
@@ -208,7 +211,7 @@ SV_API sv_status sv_spec_accept(const sv_accept_desc *desc, void *workspace, siz
 /*              -1, ...)                                                                 */
 /*   dev_status optional device int32 [B]: 0, or 3 when the walk would go below         */
 /*              max_depth (outputs then stop at max_depth)                               */
-/* Supported: 1 <= n, 0 <= max_depth <= 63, 1 <= V.                                      */
+/* Supported: 1 <= n, 0 <= max_depth <= 63, 1 <= V, B <= 32768.                          */
 /* ---------------------------------------------------------------------------------- */
 typedef struct sv_walk_desc {
     sv_mode mode;

@@ -126,9 +126,12 @@ def test_output_law_chi_square_on_gpu():
     q = special.softmax(dr1.astype(np.float64), axis=-1)
     x = np.stack([(np.cumsum(q[i])[None, :] < r.random(N)[:, None]).sum(1) for i in range(gamma)], 1)
     x = np.minimum(x, V - 1).astype(np.int32)
-    tgt = torch.from_numpy(tgt1).cuda().expand(N, gamma + 1, V).contiguous()
-    dr = torch.from_numpy(dr1).cuda().expand(N, gamma, V).contiguous()
-    got = to_host(sv.sv_spec_accept(SAMPLE, tgt, dr, dev_array(x), 1.0, 31))
+    per = 25_000                      # rounds per call; each call uses its own Philox step
+    tgt = torch.from_numpy(tgt1).cuda().expand(per, gamma + 1, V).contiguous()
+    dr = torch.from_numpy(dr1).cuda().expand(per, gamma, V).contiguous()
+    parts = [to_host(sv.sv_spec_accept(SAMPLE, tgt, dr, dev_array(x[k:k + per]), 1.0, 31, k // per))
+             for k in range(0, N, per)]
+    got = {key: np.concatenate([p[key] for p in parts]) for key in ("out_tokens", "accept_len")}
     counts = np.bincount(got["out_tokens"][:, 0], minlength=V)
     p1 = special.softmax(tgt1[0].astype(np.float64))
     assert stats.chisquare(counts, p1 * N).pvalue > 1e-4
@@ -144,3 +147,33 @@ def test_deterministic_repeats():
     for _ in range(10):
         again = to_host(sv.sv_spec_accept(*args))
         assert np.array_equal(first["out_tokens"], again["out_tokens"])
+
+
+def test_shared_workspace_across_entry_points_and_shapes():
+    """One zero-filled workspace serves a sequence of calls of every entry point and shape
+    (regression: a later call once found an earlier call's partial results where its own
+    completion counters lived)."""
+    cases = [(4, 5, 5000, SAMPLE), (128, 4, 1000, GREEDY), (64, 4, 3000, SAMPLE), (2, 16, 128256, SAMPLE),
+             (200, 1, 77, GREEDY), (7, 3, 9000, SAMPLE)]
+    parents = synth.random_tree(9, 30, branch_p=0.6)
+    for k, (B, gamma, V, mode) in enumerate(cases):
+        a = synth.accept_inputs(50 + k, B=B, gamma=gamma, V=V, target_var=3.0, noise_var=0.5, tau=0.9,
+                                greedy_drafts=(mode == GREEDY))
+        ref, got = _run_both(mode, a["target"], a["draft"] if mode == SAMPLE else None, a["draft_tokens"], 0.9,
+                             seed=3, step=k)
+        _assert_parity(ref, got, "shared workspace case %d" % k)
+        # a tree walk and an attention call on the same workspace between acceptance calls
+        lg = synth.tree_logits(k, 3, 30, 700 + 13 * k, 3.0)
+        tk = synth.node_tokens(k, lg, parents)
+        maxd = int(oracle.tree_mask(parents, 0)[1].max())
+        w = to_host(sv.sv_tree_walk(SAMPLE, dev_array(lg), dev_array(tk), dev_array(parents.astype(np.int32)), maxd,
+                                    0.7, 5, k))
+        r = oracle.tree_walk(SAMPLE, lg, tk, parents, 0.7, seed=5, step=k, max_depth=maxd)
+        ok = (r["flags"] != 0) | np.all(w["path"] == r["path"], axis=1)
+        assert ok.all()
+        inp = synth.attention_inputs(k, B=2, n_q=5, Hq=8, Hkv=2, D=128, prefix_len=[300 + 97 * k, 40],
+                                     dtype="bf16")
+        ref_o, _, rows = oracle.attention(inp, scale=0.09)
+        from svgpu import attention_on_gpu, rows_of
+        out, _ = attention_on_gpu(inp, 0.09, split_keys=128)
+        assert np.abs(rows_of(out, rows) - ref_o).max() <= 2e-2
