@@ -39,11 +39,29 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--split-keys", type=int, default=0)
     ap.add_argument("--rotate-bytes", type=float, default=1.1e9)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy 5 times (reference for the HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain device-to-device copy of a known size: FETCH_SIZE / WRITE_SIZE of this
+    kernel divided by 256 MiB gives the counters' scale factor on this GPU."""
+    import torch
+    n = 256 * 1024 * 1024 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": 4 * n, "launches": 5}))
 
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (see DESIGN.md on sharding); "
               "run with --gpus 1", file=sys.stderr)

@@ -32,6 +32,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kTileKeys = 32;
 constexpr int kMaxTiles = 1024;  // tiles per split (split_keys <= 32768)
+constexpr int kMaxSplits = 64;   // key splits per sequence
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 
@@ -68,9 +69,8 @@ __device__ __forceinline__ bool node_visible(const AttnArgs &a, const uint32_t *
 
 // ---------------------------------------------------------------------------
 template <int DH, int NWR, int NWK>
-__global__ __launch_bounds__(64 * NWR * NWK) void attn_bf16_kernel(AttnArgs a)
+__global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a)
 {
-    constexpr int NT = 64 * NWR * NWK;
     constexpr int ROWS_BLK = 32 * NWR;
     constexpr int KROW = DH * 2 + 16;                   // LDS bytes per key row (16 B pad)
     constexpr int TILE_BYTES = kTileKeys * KROW;
@@ -89,7 +89,7 @@ __global__ __launch_bounds__(64 * NWR * NWK) void attn_bf16_kernel(AttnArgs a)
 
     __shared__ __align__(16) char smem[SMEM];
     __shared__ uint16_t tile_list[kMaxTiles];
-    __shared__ int s_count, s_last;
+    __shared__ int s_count;
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -126,8 +126,18 @@ __global__ __launch_bounds__(64 * NWR * NWK) void attn_bf16_kernel(AttnArgs a)
     const uint16_t *vbase = (const uint16_t *)a.v + a.kv_off[b] + (int64_t)kvh * a.kv_sh;
     const uint32_t *bits_b = a.tree ? a.tree_bits + (int64_t)b * a.tree_sb : nullptr;
 
-    // ---- the list of tiles some row of this block can see (wave 0, ballot compaction) ----
-    if (wave == 0) {
+    // ---- the tiles some row of this block can see ----
+    // One row wave (few rows): every tile from the split start up to the block's last
+    // visible key, in order (small trees keep all their node tiles; the mask hides keys).
+    // Several row waves: an explicit list (wave 0, ballot compaction), which skips the
+    // node tiles that no row of the block can see.
+    constexpr bool kDecode = (NWR == 1);
+    int count;
+    if (kDecode) {
+        const int vis_end = a.tree ? kend : min(kend, P + i_hi + 1);
+        count = vis_end > kstart ? (vis_end - kstart + kTileKeys - 1) / kTileKeys : 0;
+    }
+    if (!kDecode && wave == 0) {
         const int ntile = (kend - kstart + kTileKeys - 1) / kTileKeys;
         int count = 0;
         for (int t0i = 0; t0i < ntile; t0i += 64) {
@@ -163,9 +173,12 @@ __global__ __launch_bounds__(64 * NWR * NWK) void attn_bf16_kernel(AttnArgs a)
         }
         if (lane == 0) s_count = count;
     }
-    __syncthreads();
-    const int count = s_count;
+    if (!kDecode) {
+        __syncthreads();
+        count = s_count;
+    }
     const int niter = (count + NWK - 1) / NWK;
+    auto tile_start = [&](int li) { return kstart + (kDecode ? li : (int)tile_list[li]) * kTileKeys; };
 
     // ---- this wave's 32 query rows: B operand of S^T = K Q^T ----
     const int my_row = rowbase + wr * 32 + l32;
@@ -191,7 +204,7 @@ __global__ __launch_bounds__(64 * NWR * NWK) void attn_bf16_kernel(AttnArgs a)
     auto issue_loads = [&](int it) {
         const int li = it * NWK + wk;
         if (li < count) {
-            const int t0 = kstart + (int)tile_list[li] * kTileKeys;
+            const int t0 = tile_start(li);
 #pragma unroll
             for (int j = 0; j < NI; ++j) {
                 const int t = t0 + ld_key0 + j * KPI;
@@ -217,11 +230,15 @@ __global__ __launch_bounds__(64 * NWR * NWK) void attn_bf16_kernel(AttnArgs a)
     float m_run = -INFINITY;
     float l_run = 0.0f;
 
+    // One row wave: each wave streams its own tiles through its own LDS buffers, so the
+    // loop needs no block barrier (a wave's LDS accesses complete in issue order).
+    // Several row waves share a tile: barriers around the LDS writes.
     if (niter > 0) issue_loads(0);
-    for (int it = 0; it < niter; ++it) {
+    const int my_iters = kDecode ? (count - wk + NWK - 1) / NWK : niter;
+    for (int it = 0; it < my_iters; ++it) {
         const int li = it * NWK + wk;
         const bool have = li < count;
-        __syncthreads();  // the previous tile is no longer read
+        if (!kDecode) __syncthreads();  // the previous tile is no longer read
         if (have) {
 #pragma unroll
             for (int j = 0; j < NI; ++j) {
@@ -230,10 +247,10 @@ __global__ __launch_bounds__(64 * NWR * NWK) void attn_bf16_kernel(AttnArgs a)
                 *reinterpret_cast<uint4 *>(gV + key * KROW + 16 * ld_dc) = vreg[j];
             }
         }
-        __syncthreads();
-        if (it + 1 < niter) issue_loads(it + 1);
+        if (!kDecode) __syncthreads();
+        if (it + 1 < my_iters) issue_loads(it + 1);
         if (!have) continue;
-        const int t0 = kstart + (int)tile_list[li] * kTileKeys;
+        const int t0 = tile_start(li);
 
         // S^T (32 keys x 32 rows) = K (keys x d) . Q^T (d x rows)
         f32x16 sacc;
@@ -346,15 +363,13 @@ __global__ __launch_bounds__(64 * NWR * NWK) void attn_bf16_kernel(AttnArgs a)
         }
     }
     const float l_row = l_run + __shfl_xor(l_run, 32);
-    const int gidx = kg * a.RT + rt;
+    if (!active || !row_ok) return;
+    const int hq = kvh * a.G + my_row % a.G;
 
-    if (ns == 1 && !overflow) {
-        // a single split: normalize and store straight from the accumulators
-        if (!active || !row_ok) return;
-        const float inv = 1.0f / l_row;
-        const int hq = kvh * a.G + my_row % a.G;
-        const int64_t obase = (int64_t)b * a.o_sb + (int64_t)my_i * a.o_st + (int64_t)hq * a.o_sh;
-        uint16_t *o = (uint16_t *)a.out + obase;
+    if (a.nsplit == 1) {
+        // one split: normalize and store straight from the accumulators
+        const float inv = overflow ? __int_as_float(0x7fc00000) : 1.0f / l_row;
+        uint16_t *o = (uint16_t *)a.out + (int64_t)b * a.o_sb + (int64_t)my_i * a.o_st + (int64_t)hq * a.o_sh;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -367,80 +382,101 @@ __global__ __launch_bounds__(64 * NWR * NWK) void attn_bf16_kernel(AttnArgs a)
                        ((uint32_t)f32_to_bf16(oacc[db][4 * a4 + 3] * inv) << 16);
                 *reinterpret_cast<uint2 *>(o + d) = pk;
             }
-        if (a.lse && h == 0) a.lse[((int64_t)b * a.n_q + my_i) * a.Hq + hq] = (m_run + log2f(l_row)) * kLn2;
+        if (a.lse && h == 0)
+            a.lse[((int64_t)b * a.n_q + my_i) * a.Hq + hq] =
+                overflow ? __int_as_float(0x7fc00000) : (m_run + log2f(l_row)) * kLn2;
         return;
     }
 
-    // ---- split partial: unnormalized o, running max (log2 units), sum ----
-    if (active && row_ok) {
-        float *pr = a.part + (((int64_t)gidx * a.nsplit + s) * ROWS_BLK + wr * 32 + l32) * (DH + 4);
+    // several splits: store this split's partial -- unnormalized o, running max (log2
+    // units), sum -- for the combine kernel, which runs after this kernel completes
+    const int gidx = kg * a.RT + rt;
+    float *pr = a.part + (((int64_t)gidx * a.nsplit + s) * ROWS_BLK + wr * 32 + l32) * (DH + 4);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int a4 = 0; a4 < 4; ++a4) {
-                const int d = 32 * db + 8 * a4 + 4 * h;
-                st_coherent4(pr + d, make_float4(oacc[db][4 * a4 + 0], oacc[db][4 * a4 + 1], oacc[db][4 * a4 + 2],
-                                                 oacc[db][4 * a4 + 3]));
-            }
-        if (h == 0) {
-            st_coherent(pr + DH, m_run);
-            st_coherent(pr + DH + 1, l_row);
+        for (int a4 = 0; a4 < 4; ++a4) {
+            const int d = 32 * db + 8 * a4 + 4 * h;
+            *reinterpret_cast<float4 *>(pr + d) =
+                make_float4(oacc[db][4 * a4 + 0], oacc[db][4 * a4 + 1], oacc[db][4 * a4 + 2], oacc[db][4 * a4 + 3]);
         }
-    }
-    if (!arrive_last(&a.cnt[gidx], ns, &s_last)) return;
+    if (h == 0) *reinterpret_cast<float2 *>(pr + DH) = make_float2(m_run, l_row);
+}
 
-    // ---- last block: combine the ns partials of every row of the tile ----
-    // Per row: M = max_s m_s, L = sum_s l_s 2^(m_s - M); then O = sum_s o_s 2^(m_s - M) / L.
-    float *sM = reinterpret_cast<float *>(smem);
-    float *sInvL = sM + ROWS_BLK;
+// ---------------------------------------------------------------------------
+// Split combine: one thread per output float4 of a row, every split's partial loaded at
+// once.  Per row: M = max_s m_s, L = sum_s l_s 2^(m_s - M), O = sum_s o_s 2^(m_s - M) / L.
+// Grid: (row chunk, kv group x row tile); a block covers CR rows x DH/4 float4 columns.
+// ---------------------------------------------------------------------------
+template <int DH, int ROWS_BLK>
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a)
+{
+    constexpr int C4 = DH / 4;          // float4 per row
+    constexpr int CR = 256 / C4;        // rows per block
+    constexpr int UNROLL = 32;
+    __shared__ float sw[CR][kMaxSplits + 1];  // per-split weights of this block's rows
+    const int gidx = blockIdx.y;
+    const int kg = gidx / a.RT, rt = gidx % a.RT;
+    const int b = kg / a.Hkv, kvh = kg % a.Hkv;
+    const int P = a.prefix_len[b];
+    const int T = P + a.n_q;
+    const bool overflow = (int64_t)T > (int64_t)a.nsplit * a.split_keys;
+    const int ns = overflow ? a.nsplit : (T + a.split_keys - 1) / a.split_keys;
+    const int r = blockIdx.x * CR + threadIdx.x / C4;   // row within the tile
+    const int d4 = threadIdx.x % C4;
+    const int row = rt * ROWS_BLK + r;
+    const bool ok = r < ROWS_BLK && row < a.rows;
     const float *pg = a.part + (int64_t)gidx * a.nsplit * ROWS_BLK * (DH + 4);
-    const int nrows_tile = row_hi - rowbase + 1;
-    for (int r = threadIdx.x; r < nrows_tile; r += NT) {
-        float M = -INFINITY;
-#pragma unroll 4
-        for (int ss = 0; ss < ns; ++ss) M = fmaxf(M, pg[((int64_t)ss * ROWS_BLK + r) * (DH + 4) + DH]);
-        float Lsum = 0.0f;
-#pragma unroll 4
-        for (int ss = 0; ss < ns; ++ss) {
-            const float *pr = pg + ((int64_t)ss * ROWS_BLK + r) * (DH + 4);
-            const float ms = pr[DH];
-            if (ms != -INFINITY) Lsum += pr[DH + 1] * exp2f(ms - M);
+
+    // weights: the C4 lanes of a row (all in one wave) split the partials among them
+    const int rl = threadIdx.x / C4;
+    float mloc = -INFINITY;
+    for (int ss = d4; ss < ns; ss += C4)
+        if (ok) mloc = fmaxf(mloc, pg[((int64_t)ss * ROWS_BLK + r) * (DH + 4) + DH]);
+#pragma unroll
+    for (int o = C4 / 2; o > 0; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o));
+    const float M = mloc;
+    float lloc = 0.0f;
+    for (int ss = d4; ss < ns; ss += C4) {
+        float w = 0.0f;
+        if (ok) {
+            const float2 ml = *reinterpret_cast<const float2 *>(pg + ((int64_t)ss * ROWS_BLK + r) * (DH + 4) + DH);
+            w = ml.x == -INFINITY ? 0.0f : exp2f(ml.x - M);
+            lloc += ml.y * w;
         }
-        sM[r] = M;
-        sInvL[r] = overflow ? __int_as_float(0x7fc00000) : 1.0f / Lsum;
-        if (a.lse) {
-            const int row = rowbase + r;
-            a.lse[((int64_t)b * a.n_q + row / a.G) * a.Hq + kvh * a.G + row % a.G] =
-                overflow ? __int_as_float(0x7fc00000) : (M + log2f(Lsum)) * kLn2;
-        }
+        sw[rl][ss] = w;
     }
+#pragma unroll
+    for (int o = C4 / 2; o > 0; o >>= 1) lloc += __shfl_xor(lloc, o);
     __syncthreads();
-    for (int item = threadIdx.x; item < nrows_tile * (DH / 4); item += NT) {
-        const int r = item / (DH / 4);
-        const int d4 = item % (DH / 4);
-        const float M = sM[r];
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
-        for (int ss = 0; ss < ns; ++ss) {
-            const float *pr = pg + ((int64_t)ss * ROWS_BLK + r) * (DH + 4);
-            const float ms = pr[DH];
-            const float4 o4 = *reinterpret_cast<const float4 *>(pr + 4 * d4);
-            const float f = ms == -INFINITY ? 0.0f : exp2f(ms - M);
-            acc.x += o4.x * f;
-            acc.y += o4.y * f;
-            acc.z += o4.z * f;
-            acc.w += o4.w * f;
+    if (!ok) return;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s0 = 0; s0 < ns; s0 += UNROLL) {
+        float4 v[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u)
+            if (s0 + u < ns) v[u] = *reinterpret_cast<const float4 *>(pg + ((int64_t)(s0 + u) * ROWS_BLK + r) * (DH + 4) + 4 * d4);
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            if (s0 + u >= ns) break;
+            const float w = sw[rl][s0 + u];
+            acc.x += v[u].x * w;
+            acc.y += v[u].y * w;
+            acc.z += v[u].z * w;
+            acc.w += v[u].w * w;
         }
-        const float inv = sInvL[r];
-        const int row = rowbase + r;
-        const int i = row / a.G;
-        const int hq = kvh * a.G + row % a.G;
-        uint16_t *o = (uint16_t *)a.out + (int64_t)b * a.o_sb + (int64_t)i * a.o_st + (int64_t)hq * a.o_sh + 4 * d4;
-        uint2 pk;
-        pk.x = (uint32_t)f32_to_bf16(acc.x * inv) | ((uint32_t)f32_to_bf16(acc.y * inv) << 16);
-        pk.y = (uint32_t)f32_to_bf16(acc.z * inv) | ((uint32_t)f32_to_bf16(acc.w * inv) << 16);
-        *reinterpret_cast<uint2 *>(o) = pk;
     }
+    const float L = lloc;
+    const float inv = overflow ? __int_as_float(0x7fc00000) : 1.0f / L;
+    const int i = row / a.G;
+    const int hq = kvh * a.G + row % a.G;
+    uint16_t *o = (uint16_t *)a.out + (int64_t)b * a.o_sb + (int64_t)i * a.o_st + (int64_t)hq * a.o_sh + 4 * d4;
+    uint2 pk;
+    pk.x = (uint32_t)f32_to_bf16(acc.x * inv) | ((uint32_t)f32_to_bf16(acc.y * inv) << 16);
+    pk.y = (uint32_t)f32_to_bf16(acc.z * inv) | ((uint32_t)f32_to_bf16(acc.w * inv) << 16);
+    *reinterpret_cast<uint2 *>(o) = pk;
+    if (a.lse && d4 == 0)
+        a.lse[((int64_t)b * a.n_q + i) * a.Hq + hq] = overflow ? __int_as_float(0x7fc00000) : (M + log2f(L)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -530,9 +566,9 @@ static bool plan_attention(const sv_attn_desc *d, Plan &p)
         sk = ((int64_t)d->split_keys + unit - 1) / unit * unit;
     } else if (p.variant == 1) {
         // Few query rows: splitting keys is cheap (a partial is at most 32 rows), so cut
-        // each sequence until the groups fill one wave of blocks on the 256 CUs (one
-        // 4-wave block per CU fits), keeping splits between 128 and 4096 keys.
-        const int64_t nsp = (256 + groups - 1) / groups;
+        // each sequence until the groups fill one wave of blocks on the 256 CUs (two
+        // 4-wave blocks fit per CU), keeping splits between 128 and 4096 keys.
+        const int64_t nsp = (512 + groups - 1) / groups;
         sk = (Tmax + nsp - 1) / nsp;
         sk = (sk + unit - 1) / unit * unit;
         if (sk < 128) sk = 128;
@@ -540,19 +576,20 @@ static bool plan_attention(const sv_attn_desc *d, Plan &p)
     } else {
         // Many rows per block: a partial costs as much as the keys it summarizes, so split
         // only when there are too few row tiles to occupy the chip.
-        if (groups >= 256) {
+        if (groups >= 512) {
             sk = Tmax;
         } else {
-            const int64_t nsp = (256 + groups - 1) / groups;
+            const int64_t nsp = (512 + groups - 1) / groups;
             sk = (Tmax + nsp - 1) / nsp;
         }
         sk = (sk + unit - 1) / unit * unit;
         if (sk < unit) sk = unit;
     }
-    if (sk > (int64_t)kMaxTiles * kTileKeys) sk = (int64_t)kMaxTiles * kTileKeys;
+    if ((Tmax + sk - 1) / sk > kMaxSplits) sk = ((Tmax + kMaxSplits - 1) / kMaxSplits + unit - 1) / unit * unit;
+    if (sk > (int64_t)kMaxTiles * kTileKeys) return false;
     p.split_keys = (int)sk;
     const int64_t nsplit = (Tmax + sk - 1) / sk;
-    if (nsplit > 65535) return false;
+    if (nsplit > kMaxSplits) return false;
     p.nsplit = (int)(nsplit < 1 ? 1 : nsplit);
     const int64_t blocks = (int64_t)p.kg_pad * p.RT * p.nsplit;
     if (blocks > 0x7fffffff) return false;
@@ -595,21 +632,27 @@ static sv_status check_attention(const sv_attn_desc *d)
     return SV_OK;
 }
 
+template <int DH, int NWR, int NWK>
+static hipError_t launch_variant(const Plan &p, const AttnArgs &a, hipStream_t s)
+{
+    hipLaunchKernelGGL((attn_bf16_kernel<DH, NWR, NWK>), dim3(p.blocks), dim3(256), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.nsplit == 1) return e;
+    constexpr int ROWS_BLK = 32 * NWR;
+    constexpr int CR = 256 / (DH / 4);
+    hipLaunchKernelGGL((attn_combine_kernel<DH, ROWS_BLK>), dim3((ROWS_BLK + CR - 1) / CR, p.KG * p.RT), dim3(256), 0,
+                       s, a);
+    return hipGetLastError();
+}
+
 template <int DH>
 static hipError_t launch_bf16(const Plan &p, const AttnArgs &a, hipStream_t s)
 {
     switch (p.variant) {
-    case 1:
-        hipLaunchKernelGGL((attn_bf16_kernel<DH, 1, 4>), dim3(p.blocks), dim3(256), 0, s, a);
-        break;
-    case 2:
-        hipLaunchKernelGGL((attn_bf16_kernel<DH, 2, 2>), dim3(p.blocks), dim3(256), 0, s, a);
-        break;
-    default:
-        hipLaunchKernelGGL((attn_bf16_kernel<DH, 4, 1>), dim3(p.blocks), dim3(256), 0, s, a);
-        break;
+    case 1: return launch_variant<DH, 1, 4>(p, a, s);
+    case 2: return launch_variant<DH, 2, 2>(p, a, s);
+    default: return launch_variant<DH, 4, 1>(p, a, s);
     }
-    return hipGetLastError();
 }
 
 }  // namespace
