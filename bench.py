@@ -39,6 +39,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--split-keys", type=int, default=0)
     ap.add_argument("--rotate-bytes", type=float, default=1.1e9)
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of replaying HIP graphs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy 5 times (reference for the HBM byte counters)")
     return ap.parse_args()
@@ -131,31 +132,52 @@ def main():
     stream = torch.cuda.current_stream(dev)
     sh = ctypes.c_void_p(stream.cuda_stream)
 
-    def step(i, ev=None):
-        r = i % R
+    def launch(r, sh, ev=None):
         if ev is not None:
-            ev[0].record(stream)
+            ev[0].record()
         st = sv.lib.sv_verify_attention(ctypes.byref(adescs[r]), pa, ws_a, sh)
         if ev is not None:
-            ev[1].record(stream)
+            ev[1].record()
         st2 = sv.lib.sv_spec_accept(ctypes.byref(sdescs[r]), ps, ws_s, sh)
         if ev is not None:
-            ev[2].record(stream)
+            ev[2].record()
         if st or st2:
             raise RuntimeError("launch failed: %d %d" % (st, st2))
 
     for i in range(args.warmup):
-        step(i)
+        launch(i % R, sh)
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # One HIP graph per input copy: a step is one graph replay (the attention kernels and the
+    # acceptance kernels, captured on torch's capture stream; no memset nodes).
+    graphs = []
+    if not args.eager:
+        for r in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                launch(r, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % R].replay()
+        torch.cuda.synchronize()
+
+    # timed region: exactly K steps
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, events[i])
+        if graphs:
+            graphs[(args.warmup + i) % R].replay()
+        else:
+            launch((args.warmup + i) % R, sh)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # kernel durations: HIP events on the launch stream around each call, same K steps
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        launch((args.warmup + i) % R, sh, events[i])
+    torch.cuda.synchronize()
     att_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
     acc_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
 
@@ -181,7 +203,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg["name"], "batch": B, "gamma": gamma, "cached_context": int(P.max()),
                    "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "vocab": V, "temperature": tau,
-                   "mode": "sample", "rotated_input_copies": R},
+                   "mode": "sample", "rotated_input_copies": R, "launch": "eager" if args.eager else "hip_graph"},
         "roofline": {"bound": "hbm", "achieved": round(att_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(att_gbs / HBM_PEAK_GBS, 4), "traffic": None,
                      "kernel": "attn_bf16_kernel", "kernel_ms": round(att_ms, 5),

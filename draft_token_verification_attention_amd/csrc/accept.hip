@@ -25,6 +25,11 @@ namespace {
 
 using namespace sv;
 
+// A block reads 4096 (PER = 16) or 16384 (PER = 64) logits of one row, all loaded
+// before any reduction: the larger chunk when the call has blocks to spare (big batches),
+// the smaller one when latency matters (a single sequence).
+constexpr int kMinChunk = 16 * kRowThreads;
+
 struct RowPart {
     float m;
     int32_t arg;
@@ -76,7 +81,7 @@ struct WsLayout {
 static WsLayout accept_layout(int B, int gamma, int V)
 {
     const size_t rows = 2 * (size_t)gamma + 1;
-    const size_t nchunk = ((size_t)V + kChunk - 1) / kChunk;
+    const size_t nchunk = ((size_t)V + kMinChunk - 1) / kMinChunk;  // the larger of the two chunk counts
     WsLayout L;
     size_t o = 0;
     L.cnt = o;
@@ -200,9 +205,11 @@ __device__ void decide_sample(const AcceptArgs &a, const AcceptWs &w, int b)
 }
 
 // ---------------------------------------------------------------------------
-template <bool VEC, bool SAMPLE>
+template <bool VEC, bool SAMPLE, int PER>
 __global__ __launch_bounds__(kRowThreads) void accept_stats_kernel(AcceptArgs a, AcceptWs w)
 {
+    constexpr int kChunk = PER * kRowThreads;
+    constexpr int kPerThread = PER;
     __shared__ float fscr[kRowThreads / kWave];
     __shared__ int iscr[kRowThreads / kWave];
     __shared__ double dscr[kRowThreads / kWave];
@@ -211,7 +218,7 @@ __global__ __launch_bounds__(kRowThreads) void accept_stats_kernel(AcceptArgs a,
     const float *row = row_ptr(a, b, r);
     const int base = c * kChunk;
     float x[kPerThread];
-    load_chunk<VEC>(row, base, a.V, x);
+    load_chunk<VEC, kPerThread>(row, base, a.V, x);
 
     RowPart part;
     if (!SAMPLE) {
@@ -227,15 +234,17 @@ __global__ __launch_bounds__(kRowThreads) void accept_stats_kernel(AcceptArgs a,
         part.arg = idx;
         part.s = 0.0;
     } else {
-        float m = -INFINITY;
+        // each thread: its own max and its sum relative to it (no barrier); then the block
+        // rescales the per-thread sums to the chunk max in fp64
+        float mt = -INFINITY;
 #pragma unroll
-        for (int k = 0; k < kPerThread; ++k) m = fmaxf(m, x[k]);
-        m = block_max(m, fscr);
-        double s = 0.0;
+        for (int k = 0; k < kPerThread; ++k) mt = fmaxf(mt, x[k]);
+        double st = 0.0;
 #pragma unroll
         for (int k = 0; k < kPerThread; ++k)
-            if (x[k] != -INFINITY) s += (double)exp2f((x[k] - m) * a.kf);
-        s = block_sum(s, dscr);
+            if (x[k] != -INFINITY) st += (double)exp2f((x[k] - mt) * a.kf);
+        const float m = block_max(mt, fscr);
+        const double s = block_sum(st > 0.0 ? st * exp2(((double)mt - (double)m) * a.kd) : 0.0, dscr);
         part.m = m;
         part.arg = 0;
         part.s = s;
@@ -254,9 +263,11 @@ __global__ __launch_bounds__(kRowThreads) void accept_stats_kernel(AcceptArgs a,
 }
 
 // ---------------------------------------------------------------------------
-template <bool VEC>
+template <bool VEC, int PER>
 __global__ __launch_bounds__(kRowThreads) void accept_alpha_kernel(AcceptArgs a, AcceptWs w)
 {
+    constexpr int kChunk = PER * kRowThreads;
+    constexpr int kPerThread = PER;
     __shared__ double dscr[kRowThreads / kWave];
     __shared__ int last_flag;
     const int c = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
@@ -267,8 +278,8 @@ __global__ __launch_bounds__(kRowThreads) void accept_alpha_kernel(AcceptArgs a,
     const double iZp = 1.0 / sp.Z, iZq = 1.0 / sq.Z;
     float xp[kPerThread], xq[kPerThread];
     const int base = c * kChunk;
-    load_chunk<VEC>(row_ptr(a, b, i), base, a.V, xp);
-    load_chunk<VEC>(row_ptr(a, b, g + 1 + i), base, a.V, xq);
+    load_chunk<VEC, kPerThread>(row_ptr(a, b, i), base, a.V, xp);
+    load_chunk<VEC, kPerThread>(row_ptr(a, b, g + 1 + i), base, a.V, xq);
     double s = 0.0;
 #pragma unroll
     for (int k = 0; k < kPerThread; ++k) {
@@ -288,9 +299,11 @@ __global__ __launch_bounds__(kRowThreads) void accept_alpha_kernel(AcceptArgs a,
 }
 
 // ---------------------------------------------------------------------------
-template <bool VEC>
+template <bool VEC, int PER>
 __global__ __launch_bounds__(kRowThreads) void accept_sample_kernel(AcceptArgs a, AcceptWs w)
 {
+    constexpr int kChunk = PER * kRowThreads;
+    constexpr int kPerThread = PER;
     __shared__ double dscr[kRowThreads / kWave];
     __shared__ double scan[kRowThreads];
     __shared__ int iscr[kRowThreads / kWave];
@@ -311,7 +324,7 @@ __global__ __launch_bounds__(kRowThreads) void accept_sample_kernel(AcceptArgs a
     auto q_of = [&](float l) { return (double)exp2f((l - Mq) * a.kf) * iZq; };
 
     float xp[kPerThread], xq[kPerThread];
-    load_chunk<VEC>(prow, base, a.V, xp);
+    load_chunk<VEC, kPerThread>(prow, base, a.V, xp);
     if (qrow) load_chunk<VEC>(qrow, base, a.V, xq);
     double rs = 0.0, ps = 0.0;
 #pragma unroll
@@ -356,17 +369,17 @@ __global__ __launch_bounds__(kRowThreads) void accept_sample_kernel(AcceptArgs a
     const int cs = s_chunk;
     const bool usep = s_usep != 0;
     const int cbase = cs * kChunk;
-    auto weight = [&](int e) -> double {
-        const double p = p_of(prow[e]);
-        if (usep || !qrow) return p;
-        return fmax(0.0, p - q_of(qrow[e]));
+    const bool twor = !usep && qrow;
+    auto weight = [&](float lp, float lq) -> double {
+        const double p = p_of(lp);
+        return twor ? fmax(0.0, p - q_of(lq)) : p;
     };
-    int y = chunk_inverse_cdf(cbase, a.V, s_base, s_target, weight, scan, iscr);
+    int y = chunk_inverse_cdf<PER, VEC>(prow, twor ? qrow : nullptr, cbase, a.V, s_base, s_target, weight, scan, iscr);
     if (y < 0) {
         // rounding left the running sum just short of u* Z: take the last token with mass
         int lastpos = -1;
         for (int e = cbase + (int)threadIdx.x; e < min(cbase + kChunk, a.V); e += kRowThreads)
-            if (weight(e) > 0.0) lastpos = max(lastpos, e);
+            if (weight(prow[e], twor ? qrow[e] : prow[e]) > 0.0) lastpos = max(lastpos, e);
         y = block_max_int(lastpos, iscr);
         if (y < 0) y = cbase;
     }
@@ -378,6 +391,18 @@ static hipError_t launch(K kernel, dim3 grid, hipStream_t s, const AcceptArgs &a
 {
     hipLaunchKernelGGL(kernel, grid, dim3(kRowThreads), 0, s, a, w);
     return hipGetLastError();
+}
+
+template <bool VEC, int PER>
+static sv_status run_accept(const AcceptArgs &a, const AcceptWs &w, hipStream_t s, bool sample, bool alpha)
+{
+    const dim3 gstats(a.nchunk, a.rows, a.B);
+    if (!sample)
+        return launch(accept_stats_kernel<VEC, false, PER>, gstats, s, a, w) == hipSuccess ? SV_OK : SV_ERR_HIP;
+    if (launch(accept_stats_kernel<VEC, true, PER>, gstats, s, a, w) != hipSuccess) return SV_ERR_HIP;
+    if (alpha && launch(accept_alpha_kernel<VEC, PER>, dim3(a.nchunk, a.gamma, a.B), s, a, w) != hipSuccess)
+        return SV_ERR_HIP;
+    return launch(accept_sample_kernel<VEC, PER>, dim3(a.nchunk, a.B), s, a, w) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
 }  // namespace
@@ -417,7 +442,6 @@ extern "C" sv_status sv_spec_accept(const sv_accept_desc *d, void *workspace, si
     a.gamma = d->gamma;
     a.V = d->V;
     a.rows = sample ? 2 * d->gamma + 1 : d->gamma + 1;
-    a.nchunk = (d->V + kChunk - 1) / kChunk;
     a.sample = sample;
     const double T = sample ? (double)d->temperature : 1.0;
     a.kd = 1.4426950408889634 / T;
@@ -436,24 +460,13 @@ extern "C" sv_status sv_spec_accept(const sv_accept_desc *d, void *workspace, si
 
     const bool vec = (d->V % 4 == 0) && (((uintptr_t)d->target_logits & 15) == 0) &&
                      (!sample || ((uintptr_t)d->draft_logits & 15) == 0);
+    const int big_chunks = (d->V + 4 * kMinChunk - 1) / (4 * kMinChunk);
+    const bool wide = (int64_t)a.B * a.rows * big_chunks >= 1024;
+    a.nchunk = wide ? big_chunks : (d->V + kMinChunk - 1) / kMinChunk;
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
-    const dim3 gstats(a.nchunk, a.rows, a.B);
-    hipError_t e;
-    if (!sample) {
-        e = vec ? launch(accept_stats_kernel<true, false>, gstats, s, a, w)
-                : launch(accept_stats_kernel<false, false>, gstats, s, a, w);
-        return e == hipSuccess ? SV_OK : SV_ERR_HIP;
-    }
-    e = vec ? launch(accept_stats_kernel<true, true>, gstats, s, a, w)
-            : launch(accept_stats_kernel<false, true>, gstats, s, a, w);
-    if (e != hipSuccess) return SV_ERR_HIP;
-    if (d->alpha) {
-        const dim3 ga(a.nchunk, a.gamma, a.B);
-        e = vec ? launch(accept_alpha_kernel<true>, ga, s, a, w) : launch(accept_alpha_kernel<false>, ga, s, a, w);
-        if (e != hipSuccess) return SV_ERR_HIP;
-    }
-    const dim3 gs(a.nchunk, a.B);
-    e = vec ? launch(accept_sample_kernel<true>, gs, s, a, w) : launch(accept_sample_kernel<false>, gs, s, a, w);
-    return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+    return wide ? (vec ? run_accept<true, 64>(a, w, s, sample, d->alpha != nullptr)
+                       : run_accept<false, 64>(a, w, s, sample, d->alpha != nullptr))
+                : (vec ? run_accept<true, 16>(a, w, s, sample, d->alpha != nullptr)
+                       : run_accept<false, 16>(a, w, s, sample, d->alpha != nullptr));
 }

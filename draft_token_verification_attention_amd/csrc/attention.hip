@@ -29,6 +29,8 @@ using namespace sv;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+// Native 16-byte vector: arrays of it stay in registers (arrays of the uint4 struct do not).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTileKeys = 32;
 constexpr int kMaxTiles = 1024;  // tiles per split (split_keys <= 32768)
@@ -60,6 +62,10 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u)
     return __builtin_bit_cast(bf16x8, u);
 }
 
+// s_waitcnt immediate that waits until at most n vector-memory loads are outstanding
+// (vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their no-wait maxima).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+
 __device__ __forceinline__ bool node_visible(const AttnArgs &a, const uint32_t *bits_row, int i, int j)
 {
     // j = position among the new tokens (0 <= j < n_q)
@@ -78,8 +84,7 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
     constexpr int TILES_LDS = NWK * GROUP_BYTES;
     constexpr int NDB = DH / 32;                        // 32-wide d blocks of O^T
     constexpr int NKC = DH / 16;                        // 16-deep d chunks of S^T
-    constexpr int COMB_FLOATS_PER_WAVE = 64 * (NDB * 16 + 2);
-    constexpr int COMB_LDS = (NWK > 1) ? (NWK - 1) * NWR * COMB_FLOATS_PER_WAVE * 4 : 0;
+    constexpr int COMB_LDS = NWR * NWK * 64 * (2 + (NWK > 1 ? NDB * 16 : 0)) * 4;
     constexpr int SMEM = TILES_LDS > COMB_LDS ? TILES_LDS : COMB_LDS;
     constexpr int LPR = DH / 8;                         // lanes per key row in a 16 B load
     constexpr int KPI = 64 / LPR;                       // key rows per wave load instruction
@@ -92,24 +97,53 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
     __shared__ int s_count;
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar tile math
     const int wk = wave % NWK;
     const int wr = wave / NWK;
     const int h = lane >> 5;          // half of the wave
     const int l32 = lane & 31;
 
-    // ---- block -> (kv group, row tile, split); XCD = workgroup id mod 8 ----
-    const int L = blockIdx.x;
-    const int xcd = L & 7;
-    const int slot = L >> 3;
-    const int per_kg = a.RT * a.nsplit;
-    const int kg = (slot / per_kg) * 8 + xcd;
-    const int rem = slot % per_kg;
-    const int rt = rem / a.nsplit;
-    const int s = rem % a.nsplit;
-    if (kg >= a.KG) return;
-    const int b = kg / a.Hkv;
-    const int kvh = kg % a.Hkv;
+    constexpr bool kDecode = (NWR == 1);
+    // ---- block -> (kv group, row tile, split) ----
+    // One row wave: a plain (split, KV head, sequence) grid.  Several row waves: all blocks
+    // of a KV head are numbered onto one XCD (workgroup id mod 8), so the row tiles that
+    // re-read its K/V share that XCD's L2.
+    int kg, rt, s, b, kvh;
+    if (kDecode) {
+        s = blockIdx.x;
+        kvh = blockIdx.y;
+        b = blockIdx.z;
+        kg = b * a.Hkv + kvh;
+        rt = 0;
+    } else {
+        const int L = blockIdx.x;
+        const int xcd = L & 7;
+        const int slot = L >> 3;
+        const int per_kg = a.RT * a.nsplit;
+        kg = (slot / per_kg) * 8 + xcd;
+        const int rem = slot % per_kg;
+        rt = rem / a.nsplit;
+        s = rem % a.nsplit;
+        if (kg >= a.KG) return;
+        b = kg / a.Hkv;
+        kvh = kg % a.Hkv;
+    }
+    // this wave's 32 query rows (B operand of S^T = K Q^T): issued before anything waits
+    const int rowbase = rt * ROWS_BLK;
+    const int my_row = rowbase + wr * 32 + l32;
+    const bool row_ok = my_row < a.rows;
+    const int my_i = row_ok ? my_row / a.G : 0;
+    bf16x8 qf[NKC];
+    {
+        const uint16_t *qrow = (const uint16_t *)a.q + (int64_t)b * a.q_sb + (int64_t)my_i * a.q_st +
+                               (int64_t)(kvh * a.G + (row_ok ? my_row % a.G : 0)) * a.q_sh;
+#pragma unroll
+        for (int c = 0; c < NKC; ++c) {
+            uint4 u = make_uint4(0, 0, 0, 0);
+            if (row_ok) u = *reinterpret_cast<const uint4 *>(qrow + 16 * c + 8 * h);
+            qf[c] = as_bf16x8(u);
+        }
+    }
     const int P = a.prefix_len[b];
     const int T = P + a.n_q;
     const int SK = a.split_keys;
@@ -118,7 +152,6 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
     if (s >= ns) return;
     const int kstart = s * SK;
     const int kend = min(kstart + SK, T);
-    const int rowbase = rt * ROWS_BLK;
     const int row_hi = min(rowbase + ROWS_BLK, a.rows) - 1;
     const int i_lo = rowbase / a.G, i_hi = row_hi / a.G;
 
@@ -131,7 +164,6 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
     // visible key, in order (small trees keep all their node tiles; the mask hides keys).
     // Several row waves: an explicit list (wave 0, ballot compaction), which skips the
     // node tiles that no row of the block can see.
-    constexpr bool kDecode = (NWR == 1);
     int count;
     if (kDecode) {
         const int vis_end = a.tree ? kend : min(kend, P + i_hi + 1);
@@ -178,43 +210,37 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
         count = s_count;
     }
     const int niter = (count + NWK - 1) / NWK;
-    auto tile_start = [&](int li) { return kstart + (kDecode ? li : (int)tile_list[li]) * kTileKeys; };
+    auto tile_start = [&](int li) {
+        return kstart + (kDecode ? li : __builtin_amdgcn_readfirstlane((int)tile_list[li])) * kTileKeys;
+    };
 
-    // ---- this wave's 32 query rows: B operand of S^T = K Q^T ----
-    const int my_row = rowbase + wr * 32 + l32;
-    const bool row_ok = my_row < a.rows;
-    const int my_i = row_ok ? my_row / a.G : 0;
-    bf16x8 qf[NKC];
-    {
-        const uint16_t *qrow = (const uint16_t *)a.q + (int64_t)b * a.q_sb + (int64_t)my_i * a.q_st +
-                               (int64_t)(kvh * a.G + (row_ok ? my_row % a.G : 0)) * a.q_sh;
-#pragma unroll
-        for (int c = 0; c < NKC; ++c) {
-            uint4 u = make_uint4(0, 0, 0, 0);
-            if (row_ok) u = *reinterpret_cast<const uint4 *>(qrow + 16 * c + 8 * h);
-            qf[c] = as_bf16x8(u);
-        }
-    }
     const uint32_t *my_bits = a.tree ? bits_b + (int64_t)my_i * a.words : nullptr;
 
     // ---- staging registers for this wave's share of a K/V tile ----
-    uint4 kreg[NI], vreg[NI];
+    u32x4 kreg[NI], vreg[NI];
     const int ld_key0 = wr * KPW + lane / LPR;
     const int ld_dc = lane % LPR;
+    // Tile loads address a uniform tile base (scalar registers) plus per-lane byte offsets
+    // that are the same for every full tile.  In the last, partial tile, key rows past the
+    // end of the cache re-read the last valid row (in bounds); the mask hides those keys,
+    // so their finite values add 0.
+    uint32_t voff[NI];
+#pragma unroll
+    for (int j = 0; j < NI; ++j) voff[j] = 2u * ((uint32_t)(ld_key0 + j * KPI) * (uint32_t)a.kv_st + 8u * ld_dc);
     auto issue_loads = [&](int it) {
         const int li = it * NWK + wk;
         if (li < count) {
             const int t0 = tile_start(li);
+            const char *kb = reinterpret_cast<const char *>(kbase + (int64_t)t0 * a.kv_st);
+            const char *vb = reinterpret_cast<const char *>(vbase + (int64_t)t0 * a.kv_st);
+            const int lim = T - 1 - t0;  // >= 0: every tile starts inside the cache
 #pragma unroll
             for (int j = 0; j < NI; ++j) {
-                const int t = t0 + ld_key0 + j * KPI;
-                if (t < T) {
-                    kreg[j] = *reinterpret_cast<const uint4 *>(kbase + (int64_t)t * a.kv_st + 8 * ld_dc);
-                    vreg[j] = *reinterpret_cast<const uint4 *>(vbase + (int64_t)t * a.kv_st + 8 * ld_dc);
-                } else {
-                    kreg[j] = make_uint4(0, 0, 0, 0);
-                    vreg[j] = make_uint4(0, 0, 0, 0);
-                }
+                const uint32_t o = (t0 + kTileKeys <= T)
+                                       ? voff[j]
+                                       : 2u * ((uint32_t)min(ld_key0 + j * KPI, lim) * (uint32_t)a.kv_st + 8u * ld_dc);
+                kreg[j] = *reinterpret_cast<const u32x4 *>(kb + o);
+                vreg[j] = *reinterpret_cast<const u32x4 *>(vb + o);
             }
         }
     };
@@ -233,6 +259,10 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
     // One row wave: each wave streams its own tiles through its own LDS buffers, so the
     // loop needs no block barrier (a wave's LDS accesses complete in issue order).
     // Several row waves share a tile: barriers around the LDS writes.
+    // Wait for Q here, before the first tile's loads are issued (it was issued first and has
+    // mostly landed by now).  Left to the compiler, the wait for Q merges into the first MFMA
+    // of every tile as a wait for all outstanding loads, which defeats the prefetch.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     if (niter > 0) issue_loads(0);
     const int my_iters = kDecode ? (count - wk + NWK - 1) / NWK : niter;
     for (int it = 0; it < my_iters; ++it) {
@@ -243,8 +273,8 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
 #pragma unroll
             for (int j = 0; j < NI; ++j) {
                 const int key = ld_key0 + j * KPI;
-                *reinterpret_cast<uint4 *>(gK + key * KROW + 16 * ld_dc) = kreg[j];
-                *reinterpret_cast<uint4 *>(gV + key * KROW + 16 * ld_dc) = vreg[j];
+                *reinterpret_cast<u32x4 *>(gK + key * KROW + 16 * ld_dc) = kreg[j];
+                *reinterpret_cast<u32x4 *>(gV + key * KROW + 16 * ld_dc) = vreg[j];
             }
         }
         if (!kDecode) __syncthreads();
@@ -295,10 +325,14 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
         for (int v = 0; v < 16; ++v) psum += p[v];
         l_run = l_run * alpha + psum;
         m_run = m_new;
+        // rescale the accumulators only when some row's running max moved (never needed on
+        // a wave's first tile, where they are still zero)
+        if (it > 0 && __ballot(alpha != 1.0f)) {
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+            for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
+                for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
+        }
 
         // P^T as the B operand: k index 8*h + j <-> key 16*c + 8*(j/4) + 4*h + j%4
         bf16x8 pb[2];
@@ -330,91 +364,113 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
     }
 
     // ---- merge the NWK key groups of each row wave (through LDS) ----
-    // Every wave stays to the end of the kernel so that each barrier sees the whole block.
-    const bool active = (wk == 0);  // after the merge, these waves hold the block's rows
-    if (NWK > 1) {
-        __syncthreads();
-        float *comb = reinterpret_cast<float *>(smem);
-        if (!active) {
-            float *mine = comb + ((wr * (NWK - 1)) + (wk - 1)) * COMB_FLOATS_PER_WAVE;
-            mine[lane] = m_run;
-            mine[64 + lane] = l_run;
+    // Every wave rescales its accumulators to the common row max, writes them to LDS, and
+    // then sums (in fixed wave order: deterministic) and stores one NWK-th of the row
+    // wave's output elements.  Element e = db*16 + v of lane (row l32, half h) is
+    // d = 32*db + 8*(v/4) + 4*h + v%4.
+    constexpr int NE = NDB * 16;                 // accumulator elements per lane
+    constexpr int EPW = NE / NWK;                // elements each key wave stores
+    static_assert(NE % NWK == 0 && EPW % 4 == 0, "merge split");
+    float *mls = reinterpret_cast<float *>(smem);                       // [NWR][NWK][2][64]
+    float *accs = mls + NWR * NWK * 2 * 64;                             // [NWR][NWK][NE][64]
+    float row_inv_l, row_m;
+    float mrg[EPW];                              // this wave's merged share (NWK > 1)
+    {
+        // the merge scratch overlays the tile buffers: wait until no wave reads a tile
+        if (NWK > 1 || NWR > 1) __syncthreads();
+        float *my_ml = mls + ((wr * NWK + wk) * 2) * 64;
+        my_ml[lane] = m_run;
+        my_ml[64 + lane] = l_run;
+        if (NWK > 1) __syncthreads();
+        float M = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < NWK; ++k) M = fmaxf(M, mls[((wr * NWK + k) * 2) * 64 + lane]);
+        float Lr = 0.0f;
+#pragma unroll
+        for (int k = 0; k < NWK; ++k) {
+            const float mk = mls[((wr * NWK + k) * 2) * 64 + lane];
+            const float lk = mls[((wr * NWK + k) * 2) * 64 + 64 + lane];
+            Lr += (mk == -INFINITY) ? 0.0f : lk * exp2f(mk - M);
+        }
+        Lr += __shfl_xor(Lr, 32);  // the other half of the row's keys
+        row_m = M;
+        row_inv_l = Lr;
+        if (NWK > 1) {
+            const float f = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - M);
+            float *my_acc = accs + ((wr * NWK + wk) * NE) * 64;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) mine[128 + (db * 16 + v) * 64 + lane] = oacc[db][v];
-        }
-        __syncthreads();
-        if (active) {
-            for (int o = 0; o < NWK - 1; ++o) {
-                const float *oth = comb + (wr * (NWK - 1) + o) * COMB_FLOATS_PER_WAVE;
-                const float m2 = oth[lane];
-                const float mm = fmaxf(m_run, m2);
-                if (mm == -INFINITY) continue;
-                const float f1 = exp2f(m_run - mm), f2 = exp2f(m2 - mm);
-                l_run = l_run * f1 + oth[64 + lane] * f2;
+                for (int v = 0; v < 16; ++v) my_acc[(db * 16 + v) * 64 + lane] = oacc[db][v] * f;
+            __syncthreads();
+            // this wave's share: elements [wk*EPW, (wk+1)*EPW), summed over the key waves
 #pragma unroll
-                for (int db = 0; db < NDB; ++db)
+            for (int e = 0; e < EPW; ++e) {
+                float sum = 0.0f;
 #pragma unroll
-                    for (int v = 0; v < 16; ++v)
-                        oacc[db][v] = oacc[db][v] * f1 + oth[128 + (db * 16 + v) * 64 + lane] * f2;
-                m_run = mm;
+                for (int k = 0; k < NWK; ++k) sum += accs[((wr * NWK + k) * NE + wk * EPW + e) * 64 + lane];
+                mrg[e] = sum;  // element wk*EPW + e
             }
         }
     }
-    const float l_row = l_run + __shfl_xor(l_run, 32);
-    if (!active || !row_ok) return;
+    const int e0 = (NWK > 1) ? wk * EPW : 0;      // first element this wave stores
+    const int ne = (NWK > 1) ? EPW : NE;           // elements this wave stores
+    auto elem = [&](int j) -> float {              // j-th element this wave stores
+        return (NWK > 1) ? mrg[j] : oacc[j / 16][j % 16];
+    };
+    const float l_row = row_inv_l;
+    if (!row_ok) return;
     const int hq = kvh * a.G + my_row % a.G;
 
     if (a.nsplit == 1) {
-        // one split: normalize and store straight from the accumulators
+        // one split: normalize and store straight from registers
         const float inv = overflow ? __int_as_float(0x7fc00000) : 1.0f / l_row;
         uint16_t *o = (uint16_t *)a.out + (int64_t)b * a.o_sb + (int64_t)my_i * a.o_st + (int64_t)hq * a.o_sh;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int a4 = 0; a4 < 4; ++a4) {
-                const int d = 32 * db + 8 * a4 + 4 * h;
-                uint2 pk;
-                pk.x = (uint32_t)f32_to_bf16(oacc[db][4 * a4 + 0] * inv) |
-                       ((uint32_t)f32_to_bf16(oacc[db][4 * a4 + 1] * inv) << 16);
-                pk.y = (uint32_t)f32_to_bf16(oacc[db][4 * a4 + 2] * inv) |
-                       ((uint32_t)f32_to_bf16(oacc[db][4 * a4 + 3] * inv) << 16);
-                *reinterpret_cast<uint2 *>(o + d) = pk;
-            }
-        if (a.lse && h == 0)
+        for (int j = 0; j < ne; j += 4) {
+            const int e = e0 + j;
+            const int d = 32 * (e / 16) + 8 * ((e % 16) / 4) + 4 * h;
+            uint2 pk;
+            pk.x = (uint32_t)f32_to_bf16(elem(j) * inv) | ((uint32_t)f32_to_bf16(elem(j + 1) * inv) << 16);
+            pk.y = (uint32_t)f32_to_bf16(elem(j + 2) * inv) | ((uint32_t)f32_to_bf16(elem(j + 3) * inv) << 16);
+            *reinterpret_cast<uint2 *>(o + d) = pk;
+        }
+        if (a.lse && h == 0 && wk == 0)
             a.lse[((int64_t)b * a.n_q + my_i) * a.Hq + hq] =
-                overflow ? __int_as_float(0x7fc00000) : (m_run + log2f(l_row)) * kLn2;
+                overflow ? __int_as_float(0x7fc00000) : (row_m + log2f(l_row)) * kLn2;
         return;
     }
 
-    // several splits: store this split's partial -- unnormalized o, running max (log2
-    // units), sum -- for the combine kernel, which runs after this kernel completes
+    // several splits: store this split's partial -- unnormalized o, max (log2 units), sum --
+    // for the combine kernel, which runs after this kernel completes
     const int gidx = kg * a.RT + rt;
     float *pr = a.part + (((int64_t)gidx * a.nsplit + s) * ROWS_BLK + wr * 32 + l32) * (DH + 4);
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-            const int d = 32 * db + 8 * a4 + 4 * h;
-            *reinterpret_cast<float4 *>(pr + d) =
-                make_float4(oacc[db][4 * a4 + 0], oacc[db][4 * a4 + 1], oacc[db][4 * a4 + 2], oacc[db][4 * a4 + 3]);
-        }
-    if (h == 0) *reinterpret_cast<float2 *>(pr + DH) = make_float2(m_run, l_row);
+    for (int j = 0; j < ne; j += 4) {
+        const int e = e0 + j;
+        const int d = 32 * (e / 16) + 8 * ((e % 16) / 4) + 4 * h;
+        *reinterpret_cast<float4 *>(pr + d) = make_float4(elem(j), elem(j + 1), elem(j + 2), elem(j + 3));
+    }
+    if (h == 0 && wk == 0) *reinterpret_cast<float2 *>(pr + DH) = make_float2(row_m, l_row);
 }
 
 // ---------------------------------------------------------------------------
-// Split combine: one thread per output float4 of a row, every split's partial loaded at
-// once.  Per row: M = max_s m_s, L = sum_s l_s 2^(m_s - M), O = sum_s o_s 2^(m_s - M) / L.
+// Split combine: one thread per output float4 of a row.  Per row: M = max_s m_s,
+// L = sum_s l_s 2^(m_s - M), O = sum_s o_s 2^(m_s - M) / L.  The partials are read in
+// chunks of kCombChunk splits (all of a chunk's loads in flight at once); the first
+// chunk is issued before the (max, sum) pairs, so a combine of up to kCombChunk splits
+// costs one memory round trip.
 // Grid: (row chunk, kv group x row tile); a block covers CR rows x DH/4 float4 columns.
 // ---------------------------------------------------------------------------
+constexpr int kCombThreads = 256;
+constexpr int kCombChunk = 8;
+
 template <int DH, int ROWS_BLK>
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a)
+__global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a)
 {
-    constexpr int C4 = DH / 4;          // float4 per row
-    constexpr int CR = 256 / C4;        // rows per block
-    constexpr int UNROLL = 32;
-    __shared__ float sw[CR][kMaxSplits + 1];  // per-split weights of this block's rows
+    constexpr int C4 = DH / 4;                 // float4 per row (lanes of one row, inside a wave)
+    constexpr int CR = kCombThreads / C4;      // rows per block
+    __shared__ float sw[CR][kMaxSplits + 1];   // per-split weights of this block's rows
     const int gidx = blockIdx.y;
     const int kg = gidx / a.RT, rt = gidx % a.RT;
     const int b = kg / a.Hkv, kvh = kg % a.Hkv;
@@ -422,48 +478,54 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a)
     const int T = P + a.n_q;
     const bool overflow = (int64_t)T > (int64_t)a.nsplit * a.split_keys;
     const int ns = overflow ? a.nsplit : (T + a.split_keys - 1) / a.split_keys;
-    const int r = blockIdx.x * CR + threadIdx.x / C4;   // row within the tile
+    const int rl = threadIdx.x / C4;           // row within the block
     const int d4 = threadIdx.x % C4;
+    const int r = blockIdx.x * CR + rl;        // row within the tile
     const int row = rt * ROWS_BLK + r;
     const bool ok = r < ROWS_BLK && row < a.rows;
     const float *pg = a.part + (int64_t)gidx * a.nsplit * ROWS_BLK * (DH + 4);
+    auto row_at = [&](int u) { return pg + ((int64_t)u * ROWS_BLK + r) * (DH + 4); };  // o[DH], max, sum
+    auto o_at = [&](int u) { return row_at(u) + 4 * d4; };
 
-    // weights: the C4 lanes of a row (all in one wave) split the partials among them
-    const int rl = threadIdx.x / C4;
+    float4 v[kCombChunk];
+#pragma unroll
+    for (int k = 0; k < kCombChunk; ++k)
+        if (ok && k < ns) v[k] = *reinterpret_cast<const float4 *>(o_at(k));
+
+    // the C4 lanes of a row split its (max, sum) pairs among them
     float mloc = -INFINITY;
-    for (int ss = d4; ss < ns; ss += C4)
-        if (ok) mloc = fmaxf(mloc, pg[((int64_t)ss * ROWS_BLK + r) * (DH + 4) + DH]);
+    for (int ss = d4; ok && ss < ns; ss += C4) mloc = fmaxf(mloc, row_at(ss)[DH]);
 #pragma unroll
     for (int o = C4 / 2; o > 0; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o));
     const float M = mloc;
     float lloc = 0.0f;
-    for (int ss = d4; ss < ns; ss += C4) {
-        float w = 0.0f;
-        if (ok) {
-            const float2 ml = *reinterpret_cast<const float2 *>(pg + ((int64_t)ss * ROWS_BLK + r) * (DH + 4) + DH);
-            w = ml.x == -INFINITY ? 0.0f : exp2f(ml.x - M);
-            lloc += ml.y * w;
-        }
+    for (int ss = d4; ok && ss < ns; ss += C4) {
+        const float2 ml = *reinterpret_cast<const float2 *>(row_at(ss) + DH);
+        const float w = ml.x == -INFINITY ? 0.0f : exp2f(ml.x - M);
         sw[rl][ss] = w;
+        lloc += ml.y * w;
     }
 #pragma unroll
     for (int o = C4 / 2; o > 0; o >>= 1) lloc += __shfl_xor(lloc, o);
     __syncthreads();
     if (!ok) return;
+
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s0 = 0; s0 < ns; s0 += UNROLL) {
-        float4 v[UNROLL];
+    for (int u0 = 0; u0 < ns; u0 += kCombChunk) {
+        if (u0 > 0) {
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u)
-            if (s0 + u < ns) v[u] = *reinterpret_cast<const float4 *>(pg + ((int64_t)(s0 + u) * ROWS_BLK + r) * (DH + 4) + 4 * d4);
+            for (int k = 0; k < kCombChunk; ++k)
+                if (u0 + k < ns) v[k] = *reinterpret_cast<const float4 *>(o_at(u0 + k));
+        }
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            if (s0 + u >= ns) break;
-            const float w = sw[rl][s0 + u];
-            acc.x += v[u].x * w;
-            acc.y += v[u].y * w;
-            acc.z += v[u].z * w;
-            acc.w += v[u].w * w;
+        for (int k = 0; k < kCombChunk; ++k) {
+            if (u0 + k < ns) {
+                const float w = sw[rl][u0 + k];
+                acc.x += v[k].x * w;
+                acc.y += v[k].y * w;
+                acc.z += v[k].z * w;
+                acc.w += v[k].w * w;
+            }
         }
     }
     const float L = lloc;
@@ -621,6 +683,7 @@ static sv_status check_attention(const sv_attn_desc *d)
     if (d->D != 64 && d->D != 128) return SV_ERR_UNSUPPORTED;
     if (d->mask == SV_MASK_TREE && d->n_q > 32768) return SV_ERR_UNSUPPORTED;
     if ((int64_t)d->max_prefix + d->n_q > 0x7fffffffLL) return SV_ERR_UNSUPPORTED;
+    if (d->kv_st > (0x7fffffffLL / 32)) return SV_ERR_UNSUPPORTED;  // in-tile byte offsets are 32-bit
     if (d->dtype == SV_BF16) {
         // 16-byte vector access of q, k, v rows; 8-byte stores of out
         const int64_t s16[] = {d->q_sb, d->q_st, d->q_sh, d->kv_sh, d->kv_st};
@@ -635,12 +698,17 @@ static sv_status check_attention(const sv_attn_desc *d)
 template <int DH, int NWR, int NWK>
 static hipError_t launch_variant(const Plan &p, const AttnArgs &a, hipStream_t s)
 {
-    hipLaunchKernelGGL((attn_bf16_kernel<DH, NWR, NWK>), dim3(p.blocks), dim3(256), 0, s, a);
+    if (NWR == 1)
+        hipLaunchKernelGGL((attn_bf16_kernel<DH, NWR, NWK>), dim3(p.nsplit, a.Hkv, a.B), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((attn_bf16_kernel<DH, NWR, NWK>), dim3(p.blocks), dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.nsplit == 1) return e;
     constexpr int ROWS_BLK = 32 * NWR;
-    constexpr int CR = 256 / (DH / 4);
-    hipLaunchKernelGGL((attn_combine_kernel<DH, ROWS_BLK>), dim3((ROWS_BLK + CR - 1) / CR, p.KG * p.RT), dim3(256), 0,
+    constexpr int CR = kCombThreads / (DH / 4);
+    const int tile_rows = p.rows < ROWS_BLK ? p.rows : ROWS_BLK;
+    hipLaunchKernelGGL((attn_combine_kernel<DH, ROWS_BLK>), dim3((tile_rows + CR - 1) / CR, p.KG * p.RT),
+                       dim3(kCombThreads), 0,
                        s, a);
     return hipGetLastError();
 }

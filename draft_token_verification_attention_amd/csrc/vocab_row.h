@@ -1,10 +1,10 @@
 // vocab_row.h -- block-wide primitives over one chunk of an fp32 logit row
 // (shared by the acceptance and tree-walk kernels).
 //
-// A block of kRowThreads threads owns kChunk consecutive logits of a row.  With
-// vector loads each thread reads float4 at offset 4*t + 1024*k (k = 0..3): every
-// wave instruction is one contiguous 1 KiB segment.  Positions at or beyond V
-// read as -inf and are excluded from every result.
+// A block of kRowThreads threads owns a chunk of consecutive logits of a row.  With
+// vector loads each thread reads float4 at offset 4*t + 1024*k: every wave instruction
+// is one contiguous 1 KiB segment.  Positions at or beyond V read as -inf and are
+// excluded from every result.
 #pragma once
 
 #include "sv_common.h"
@@ -12,10 +12,15 @@
 namespace sv {
 
 constexpr int kRowThreads = 256;
-constexpr int kChunk = 4096;
-constexpr int kPerThread = kChunk / kRowThreads;  // 16
 
-// Index of the k-th logit a thread holds.
+// A block owns kRowThreads * PER consecutive logits of a row (PER per thread).
+template <int PER>
+struct Chunk {
+    static constexpr int kPer = PER;
+    static constexpr int kSize = PER * kRowThreads;
+};
+
+// Index of the k-th logit a thread holds (vector layout: float4 at 4t + 1024*(k/4)).
 template <bool VEC>
 __device__ __forceinline__ int chunk_index(int chunk_base, int k)
 {
@@ -23,12 +28,12 @@ __device__ __forceinline__ int chunk_index(int chunk_base, int k)
     return chunk_base + (int)threadIdx.x + kRowThreads * k;
 }
 
-template <bool VEC>
-__device__ __forceinline__ void load_chunk(const float *__restrict__ row, int chunk_base, int V, float x[kPerThread])
+template <bool VEC, int PER>
+__device__ __forceinline__ void load_chunk(const float *__restrict__ row, int chunk_base, int V, float (&x)[PER])
 {
     if (VEC) {
 #pragma unroll
-        for (int k4 = 0; k4 < kPerThread / 4; ++k4) {
+        for (int k4 = 0; k4 < PER / 4; ++k4) {
             const int e = chunk_base + 4 * (int)threadIdx.x + 1024 * k4;
             if (e + 3 < V) {
                 const float4 f = *reinterpret_cast<const float4 *>(row + e);
@@ -43,7 +48,7 @@ __device__ __forceinline__ void load_chunk(const float *__restrict__ row, int ch
         }
     } else {
 #pragma unroll
-        for (int k = 0; k < kPerThread; ++k) {
+        for (int k = 0; k < PER; ++k) {
             const int e = chunk_base + (int)threadIdx.x + kRowThreads * k;
             x[k] = e < V ? row[e] : -INFINITY;
         }
@@ -121,45 +126,79 @@ __device__ __forceinline__ int block_max_int(int v, int *scratch)
     return r;
 }
 
-// Exclusive prefix sum (fp64) of one value per thread, in thread order.
-__device__ __forceinline__ double block_exclusive_scan(double v, double *scratch /* kRowThreads */)
+// Exclusive prefix sum (fp64) of one value per thread, in thread order: a wave scan,
+// then the wave totals (fixed order, deterministic).
+__device__ __forceinline__ double block_exclusive_scan(double v, double *scratch /* >= waves */)
 {
-    __syncthreads();
-    scratch[threadIdx.x] = v;
-    __syncthreads();
-    // Hillis-Steele over 256 entries: fixed order, deterministic.
-    for (int off = 1; off < kRowThreads; off <<= 1) {
-        const double add = threadIdx.x >= (unsigned)off ? scratch[threadIdx.x - off] : 0.0;
-        __syncthreads();
-        scratch[threadIdx.x] += add;
-        __syncthreads();
+    const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+    double incl = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const double t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
     }
-    return scratch[threadIdx.x] - v;
+    __syncthreads();
+    if (lane == kWave - 1) scratch[w] = incl;
+    __syncthreads();
+    double before = 0.0;
+    for (int i = 0; i < w; ++i) before += scratch[i];
+    return before + incl - v;
 }
 
-// Inverse-CDF search inside one chunk of non-negative weights w(e), in token order.
-// `base` is the cumulative weight before the chunk, `target` = u * Z.  Returns the
-// smallest index e with base + C_e > target, or -1 when the chunk's running sum
-// never passes it.  Each thread scans 16 consecutive positions.
-template <typename WeightFn>
-__device__ __forceinline__ int chunk_inverse_cdf(int chunk_base, int V, double base, double target,
-                                                 WeightFn weight, double *scan_scratch, int *iscratch)
+// Inverse-CDF search inside one chunk, in token order, over weights w(l0[e], l1[e]) of
+// one or two logit rows (l1 may be null: then w gets l0[e] twice).  `base` is the
+// cumulative weight before the chunk, `target` = u * Z.  Returns the smallest e with
+// base + C_e > target, or -1 when the chunk's running sum never passes it.  Two levels:
+// every thread sums PER consecutive weights (16-byte loads when VEC), a block scan finds
+// the segment where the running sum crosses target, and one wave scans that segment.
+template <int PER, bool VEC, typename WeightFn>
+__device__ __forceinline__ int chunk_inverse_cdf(const float *l0, const float *l1, int chunk_base, int V, double base,
+                                                 double target, WeightFn weight, double *scratch, int *iscratch)
 {
-    double w[kPerThread];
+    static_assert(PER <= kWave && PER % 4 == 0, "one wave scans a segment");
+    __shared__ int s_seg;
+    __shared__ double s_c0;
+    const int first = chunk_base + PER * (int)threadIdx.x;
     double local = 0.0;
-    const int first = chunk_base + kPerThread * (int)threadIdx.x;
+    if (VEC && first + PER <= V) {
 #pragma unroll
-    for (int k = 0; k < kPerThread; ++k) {
-        const int e = first + k;
-        w[k] = e < V ? weight(e) : 0.0;
-        local += w[k];
+        for (int k4 = 0; k4 < PER / 4; ++k4) {
+            const float4 a = *reinterpret_cast<const float4 *>(l0 + first + 4 * k4);
+            const float4 c = l1 ? *reinterpret_cast<const float4 *>(l1 + first + 4 * k4) : a;
+            local += weight(a.x, c.x) + weight(a.y, c.y) + weight(a.z, c.z) + weight(a.w, c.w);
+        }
+    } else {
+        for (int k = 0; k < PER; ++k) {
+            const int e = first + k;
+            if (e < V) local += weight(l0[e], l1 ? l1[e] : l0[e]);
+        }
     }
-    double c = base + block_exclusive_scan(local, scan_scratch);
+    const double c0 = base + block_exclusive_scan(local, scratch);
+    const bool crossing = local > 0.0 && c0 <= target && c0 + local > target;
+    const int seg = block_min_int(crossing ? (int)threadIdx.x : 0x7fffffff, iscratch);
+    if (seg == 0x7fffffff) return -1;
+    if ((int)threadIdx.x == seg) {
+        s_seg = seg;
+        s_c0 = c0;
+    }
+    __syncthreads();
     int found = 0x7fffffff;
+    if (threadIdx.x < kWave) {
+        const int lane = threadIdx.x;
+        const int e = chunk_base + PER * s_seg + lane;
+        const double w = (lane < PER && e < V) ? weight(l0[e], l1 ? l1[e] : l0[e]) : 0.0;
+        double incl = w;
 #pragma unroll
-    for (int k = 0; k < kPerThread; ++k) {
-        c += w[k];
-        if (found == 0x7fffffff && w[k] > 0.0 && c > target) found = first + k;
+        for (int o = 1; o < kWave; o <<= 1) {
+            const double t = __shfl_up(incl, o);
+            if (lane >= o) incl += t;
+        }
+        const uint64_t hit = __ballot(w > 0.0 && s_c0 + incl > target);
+        const uint64_t pos = __ballot(w > 0.0);
+        if (hit)
+            found = chunk_base + PER * s_seg + (__ffsll((unsigned long long)hit) - 1);
+        else if (pos)  // rounding: the segment's own sum stops short of target
+            found = chunk_base + PER * s_seg + (63 - __clzll((unsigned long long)pos));
     }
     const int r = block_min_int(found, iscratch);
     return r == 0x7fffffff ? -1 : r;

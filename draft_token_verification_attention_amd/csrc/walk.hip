@@ -18,6 +18,11 @@ namespace {
 
 using namespace sv;
 
+// 4096 logits per block: a level reads one row, so smaller blocks spread it wider.
+using WChunk = Chunk<16>;
+constexpr int kChunk = WChunk::kSize;
+constexpr int kPerThread = WChunk::kPer;
+
 struct WalkPart {
     float m;
     int32_t arg;
@@ -86,7 +91,7 @@ __global__ __launch_bounds__(kRowThreads) void walk_level_kernel(WalkArgs a, Wal
     const float *row = a.logits + ((int64_t)b * a.n + v) * a.V;
     const int base = c * kChunk;
     float x[kPerThread];
-    load_chunk<VEC>(row, base, a.V, x);
+    load_chunk<VEC, kPerThread>(row, base, a.V, x);
 
     WalkPart part;
     if (!SAMPLE) {
@@ -158,12 +163,12 @@ __global__ __launch_bounds__(kRowThreads) void walk_level_kernel(WalkArgs a, Wal
         const int cb = s_chunk * kChunk;
         const float mc = s_mc;
         const double f = s_factor;
-        auto weight = [&](int e) -> double { return (double)exp2f((row[e] - mc) * a.kf) * f; };
-        int y = chunk_inverse_cdf(cb, a.V, s_base, s_target, weight, scan, iscr);
+        auto weight = [&](float l, float) -> double { return (double)exp2f((l - mc) * a.kf) * f; };
+        int y = chunk_inverse_cdf<kPerThread, VEC>(row, nullptr, cb, a.V, s_base, s_target, weight, scan, iscr);
         if (y < 0) {
             int lastpos = -1;
             for (int e = cb + (int)threadIdx.x; e < min(cb + kChunk, a.V); e += kRowThreads)
-                if (weight(e) > 0.0) lastpos = max(lastpos, e);
+                if (weight(row[e], 0.0f) > 0.0) lastpos = max(lastpos, e);
             y = block_max_int(lastpos, iscr);
             if (y < 0) y = cb;
         }

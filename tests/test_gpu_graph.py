@@ -1,0 +1,71 @@
+"""HIP-graph capture of the verify step: a captured attention + acceptance sequence is
+replayed several times, with eager calls on other inputs and host synchronizations in
+between, and every replay must equal the eager result on the same inputs."""
+import ctypes
+import math
+
+import numpy as np
+import pytest
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import draft_token_verification_attention_amd as sv  # noqa: E402
+from svgpu import dev_array  # noqa: E402
+
+
+def _inputs(seed, P):
+    att = synth.attention_inputs(seed, B=2, n_q=6, Hq=32, Hkv=8, D=128, prefix_len=[P, P // 3 + 7], dtype="bf16",
+                                 qkv_scale=1.0)
+    acc = synth.accept_inputs(seed, B=2, gamma=5, V=20000, target_var=3.0, noise_var=1.0, tau=0.8)
+    return att, acc
+
+
+def test_graph_replays_match_eager():
+    att, acc = _inputs(1, 3000)
+    q, k, v = dev_array(att["q"], True), dev_array(att["k"], True), dev_array(att["v"], True)
+    kv_off, pl = dev_array(att["kv_off"]), dev_array(att["prefix_len"])
+    tgt, dr, tok = dev_array(acc["target"]), dev_array(acc["draft"]), dev_array(acc["draft_tokens"])
+    out = torch.empty(q.shape, dtype=q.dtype, device="cuda")
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    alen = torch.empty(2, dtype=torch.int32, device="cuda")
+    otok = torch.empty((2, 6), dtype=torch.int32, device="cuda")
+    ad = sv.attn_desc(q, k, v, kv_off, pl, Hkv=8, max_prefix=3000, scale=1 / math.sqrt(128), kv_sh=att["kv_sh"],
+                      kv_st=att["kv_st"], out=out, lse=lse, split_keys=256)
+    sd = sv.accept_desc(sv.SV_SAMPLE, tgt, dr, tok, 0.8, 99, 3, None, alen, otok, None, None)
+    wa = torch.zeros(sv.lib.sv_verify_attention_workspace(ctypes.byref(ad)) + 256, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(sv.lib.sv_spec_accept_workspace(ctypes.byref(sd)) + 256, dtype=torch.uint8, device="cuda")
+    pa = ctypes.c_void_p(wa.data_ptr() + (-wa.data_ptr()) % 256)
+    ps = ctypes.c_void_p(ws.data_ptr() + (-ws.data_ptr()) % 256)
+
+    def launch(stream):
+        assert sv.lib.sv_verify_attention(ctypes.byref(ad), pa, wa.numel() - 256, stream) == 0
+        assert sv.lib.sv_spec_accept(ctypes.byref(sd), ps, ws.numel() - 256, stream) == 0
+
+    launch(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    ref = (out.clone(), lse.clone(), alen.clone(), otok.clone())
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        launch(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    other_att, other_acc = _inputs(2, 1500)
+    for rep in range(5):
+        out.zero_(), lse.zero_(), alen.zero_(), otok.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1]), rep
+        assert torch.equal(alen, ref[2]) and torch.equal(otok, ref[3]), rep
+        # eager work on other inputs (and the shared binding workspace) between replays
+        sv.sv_verify_attention(dev_array(other_att["q"], True), dev_array(other_att["k"], True),
+                               dev_array(other_att["v"], True), dev_array(other_att["kv_off"]),
+                               dev_array(other_att["prefix_len"]), Hkv=8, max_prefix=1500, scale=0.1,
+                               kv_sh=other_att["kv_sh"], kv_st=other_att["kv_st"], split_keys=128)
+        sv.sv_spec_accept(sv.SV_SAMPLE, dev_array(other_acc["target"]), dev_array(other_acc["draft"]),
+                          dev_array(other_acc["draft_tokens"]), 0.8, 5, rep)
+        torch.cuda.synchronize()
