@@ -8,15 +8,18 @@
 //   "Speculative Decoding: The Art of Guessing Well", section "Speculative sampling".
 //
 // Kernels (one launch each, all decisions on the device):
-//   stats   grid (chunk, row, sequence).  Each block reads 4096 logits of one row once:
-//           GREEDY keeps (max, first argmax); SAMPLE keeps (chunk max m_c, S_c =
-//           sum exp((l - m_c)/T) in fp64).  The last block of a sequence combines the
-//           row statistics, draws the ratio-test uniforms and decides J (and, under
-//           GREEDY, the extra token z_J).
-//   alpha   optional: sum_x min(p_i, q_i) per draft position (one more read of the rows).
-//   sample  SAMPLE only, grid (chunk, sequence): residual mass per chunk of the two rows
-//           at position J; the last block finds the chunk holding u* Z and scans it in
-//           token order for the extra token.
+//   stats    grid (chunk, row, sequence).  Each block reads one chunk of one row once:
+//            GREEDY keeps (max, first argmax); SAMPLE keeps (chunk max m_c, S_c =
+//            sum exp((l - m_c)/T) in fp64) and the logit of the drafted token when the
+//            chunk holds it.  No cross-block hand-off: the kernel boundary publishes.
+//   greedy   GREEDY, one block per sequence: argmax per row from the chunk partials,
+//            the matching prefix J and the extra token z_J.
+//   alpha    optional: sum_x min(p_i, q_i) per draft position (one more read of the rows).
+//   resample SAMPLE, grid (chunk, sequence).  Every block re-derives the row statistics
+//            and the ratio tests from the chunk partials in a fixed order (so all blocks
+//            agree on J), then sums the residual mass of its chunk of the two rows at
+//            position J; the last block finds the chunk holding u* Z and scans it in
+//            token order for the extra token.
 // Exponentials of the bulk run in fp32; every sum, the CDF and the decided p(x), q(x)
 // are fp64.
 #include "vocab_row.h"
@@ -35,27 +38,18 @@ struct RowPart {
     int32_t arg;
     double s;
 };
-struct RowStat {
-    double M;
-    double Z;
-};
-struct SeqState {
-    int32_t J;
-    int32_t pad;
-    double Mp, Zp, Mq, Zq;
-};
 struct ResPart {
     double r;
     double p;
 };
 
 struct AcceptWs {
-    int *cnt;  // [B]: one completion counter per sequence, shared by the call's kernels in turn
-    RowPart *part;      // [B][rows][nchunk]
-    RowStat *rowstat;   // [B][rows]
-    SeqState *seq;      // [B]
-    ResPart *res;       // [B][nchunk]
-    double *apart;      // [B][gamma][nchunk]
+    int *cnt;        // [B]: one completion counter per sequence, shared by the call's kernels in turn
+    RowPart *part;   // [B][rows][nchunk]
+    float *xlog;     // [B][2 gamma]: target then draft logit of each drafted token
+    double *u;       // [B][gamma + 1]: the round's uniforms (ratio tests, then the extra token)
+    ResPart *res;    // [B][nchunk]
+    double *apart;   // [B][gamma][nchunk]
 };
 
 struct AcceptArgs {
@@ -75,7 +69,7 @@ struct AcceptArgs {
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-    size_t cnt, part, rowstat, seq, res, apart, total;
+    size_t cnt, part, xlog, u, res, apart, total;
 };
 
 static WsLayout accept_layout(int B, int gamma, int V)
@@ -88,10 +82,10 @@ static WsLayout accept_layout(int B, int gamma, int V)
     o += kCounterBytes;
     L.part = o;
     o += align256((size_t)B * rows * nchunk * sizeof(RowPart));
-    L.rowstat = o;
-    o += align256((size_t)B * rows * sizeof(RowStat));
-    L.seq = o;
-    o += align256((size_t)B * sizeof(SeqState));
+    L.xlog = o;
+    o += align256((size_t)B * 2 * gamma * sizeof(float));
+    L.u = o;
+    o += align256((size_t)B * (gamma + 1) * sizeof(double));
     L.res = o;
     o += align256((size_t)B * nchunk * sizeof(ResPart));
     L.apart = o;
@@ -99,6 +93,9 @@ static WsLayout accept_layout(int B, int gamma, int V)
     L.total = o;
     return L;
 }
+
+// Row partials staged in LDS by the decide steps (dynamic shared memory, at most this many)
+constexpr int kMaxStaged = 2048;
 
 __device__ __forceinline__ const float *row_ptr(const AcceptArgs &a, int b, int r)
 {
@@ -112,96 +109,75 @@ __device__ __forceinline__ uint64_t stream_of(const AcceptArgs &a, int b)
 }
 
 // ---------------------------------------------------------------------------
-// decide (runs in the last stats block of sequence b)
+// Row statistics from the chunk partials, identical in every block that computes them:
+// the partials of rows [0, nrows) are staged in LDS (one memory round trip), then one
+// wave per row reduces them in a fixed lane order.
 // ---------------------------------------------------------------------------
-__device__ void decide_greedy(const AcceptArgs &a, const AcceptWs &w, int b)
+// Stage the n chunk partials of a sequence in LDS (n <= kMaxStaged).  Every thread
+// issues NT unconditional loads (clamped in-bounds addresses) before any is waited for;
+// `meanwhile` runs between issuing them and using them.
+template <int NT, typename Fn>
+__device__ __forceinline__ void stage_parts_nt(const RowPart *pp, int n, RowPart *stage, Fn meanwhile)
 {
-    __shared__ int z[65];
-    __shared__ int firstbad, bad;
-    const int g = a.gamma;
-    if (threadIdx.x == 0) {
-        firstbad = g;
-        bad = 0;
-    }
-    const int wave = threadIdx.x / kWave, nwaves = blockDim.x / kWave;
-    for (int r = wave; r <= g; r += nwaves) {
-        float v;
-        int idx;
-        wave_combine_argmax(w.part + ((int64_t)b * a.rows + r) * a.nchunk, a.nchunk, v, idx);
-        if (threadIdx.x % kWave == 0) z[r] = idx;
-    }
+    // moved as raw 16-byte vectors (an array of the struct would live in private memory)
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    static_assert(sizeof(RowPart) == sizeof(u32x4), "16-byte partials");
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(pp);
+    u32x4 *dst = reinterpret_cast<u32x4 *>(stage);
+    u32x4 t[NT];
+#pragma unroll
+    for (int u = 0; u < NT; ++u) t[u] = src[min((int)threadIdx.x + u * kRowThreads, n - 1)];
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of `meanwhile`
+    meanwhile();
+    // unconditional stores (the stage has NT * kRowThreads slots): a conditional store
+    // would let the compiler sink its load next to it, one round trip per load
+#pragma unroll
+    for (int u = 0; u < NT; ++u) dst[threadIdx.x + u * kRowThreads] = t[u];
     __syncthreads();
-    for (int i = threadIdx.x; i < g; i += blockDim.x) {
-        const int x = a.tokens[(int64_t)b * g + i];
-        if (x != z[i]) atomicMin(&firstbad, i);
-        if (x < 0 || x >= a.V) bad = 1;
-    }
-    __syncthreads();
-    const int J = firstbad;
-    int32_t *out = a.out_tokens + (int64_t)b * (g + 1);
-    for (int i = threadIdx.x; i <= g; i += blockDim.x)
-        out[i] = i < J ? a.tokens[(int64_t)b * g + i] : (i == J ? z[J] : -1);
-    if (a.alpha)  // alpha is a sampling quantity
-        for (int i = threadIdx.x; i < g; i += blockDim.x) a.alpha[(int64_t)b * g + i] = __int_as_float(0x7fc00000);
-    if (threadIdx.x == 0) {
-        a.accept_len[b] = J;
-        if (a.dev_status) a.dev_status[b] = bad ? 2 : 0;
-    }
 }
 
-__device__ void decide_sample(const AcceptArgs &a, const AcceptWs &w, int b)
+template <typename Fn>
+__device__ __forceinline__ void stage_parts(const RowPart *pp, int n, RowPart *stage, Fn meanwhile)
 {
-    __shared__ double sM[129], sZ[129];
-    __shared__ int firstbad, bad;
-    const int g = a.gamma;
-    if (threadIdx.x == 0) {
-        firstbad = g;
-        bad = 0;
-    }
-    const int wave = threadIdx.x / kWave, nwaves = blockDim.x / kWave;
-    for (int r = wave; r < a.rows; r += nwaves) {
+    static_assert(kMaxStaged <= 8 * kRowThreads, "staging depth");
+    if (n <= kRowThreads)
+        stage_parts_nt<1>(pp, n, stage, meanwhile);
+    else if (n <= 2 * kRowThreads)
+        stage_parts_nt<2>(pp, n, stage, meanwhile);
+    else if (n <= 4 * kRowThreads)
+        stage_parts_nt<4>(pp, n, stage, meanwhile);
+    else
+        stage_parts_nt<8>(pp, n, stage, meanwhile);
+}
+
+template <int LPR>
+__device__ __forceinline__ void row_softmax_stats_lpr(const RowPart *src, int nrows, int nchunk, float kf, double *sM,
+                                                      double *sZ)
+{
+    constexpr int RPP = kRowThreads / LPR;  // rows per block pass
+    const int lane_row = (int)threadIdx.x / LPR;
+    for (int r0 = 0; r0 < nrows; r0 += RPP) {
         float M;
         double Z;
-        wave_combine_softmax(w.part + ((int64_t)b * a.rows + r) * a.nchunk, a.nchunk, a.kd, M, Z);
-        if (threadIdx.x % kWave == 0) {
-            sM[r] = (double)M;
-            sZ[r] = Z;
-            w.rowstat[(int64_t)b * a.rows + r] = RowStat{(double)M, Z};
+        group_combine_softmax<LPR>(src, r0 + lane_row, nrows, nchunk, kf, M, Z);
+        if ((threadIdx.x % LPR) == 0 && r0 + lane_row < nrows) {
+            sM[r0 + lane_row] = (double)M;
+            sZ[r0 + lane_row] = Z;
         }
     }
     __syncthreads();
-    const uint64_t stream = stream_of(a, b);
-    for (int i = threadIdx.x; i < g; i += blockDim.x) {
-        const int x = a.tokens[(int64_t)b * g + i];
-        bool pass = false;
-        if (x >= 0 && x < a.V) {
-            const double lp = (double)a.target[((int64_t)b * (g + 1) + i) * a.V + x];
-            const double lq = (double)a.draft[((int64_t)b * g + i) * a.V + x];
-            const double p = exp((lp - sM[i]) * a.inv_t) / sZ[i];
-            const double q = exp((lq - sM[g + 1 + i]) * a.inv_t) / sZ[g + 1 + i];
-            const double u = philox_uniform(a.seed, (uint64_t)i, a.step, stream, kTagAccept);
-            pass = u * q < p;
-        } else {
-            bad = 1;
-        }
-        if (!pass) atomicMin(&firstbad, i);
-    }
-    __syncthreads();
-    const int J = firstbad;
-    int32_t *out = a.out_tokens + (int64_t)b * (g + 1);
-    for (int i = threadIdx.x; i <= g; i += blockDim.x) out[i] = i < J ? a.tokens[(int64_t)b * g + i] : -1;
-    if (threadIdx.x == 0) {
-        a.accept_len[b] = J;
-        if (a.dev_status) a.dev_status[b] = bad ? 2 : 0;
-        SeqState s;
-        s.J = J;
-        s.pad = 0;
-        s.Mp = sM[J];
-        s.Zp = sZ[J];
-        s.Mq = J < g ? sM[g + 1 + J] : 0.0;
-        s.Zq = J < g ? sZ[g + 1 + J] : 0.0;
-        w.seq[b] = s;
-    }
+}
+
+// (M, Z) of rows [0, nrows): the chunk partials of a row sit on 16, 32 or 64 lanes.
+__device__ __forceinline__ void row_softmax_stats(const RowPart *src, int nrows, int nchunk, float kf, double *sM,
+                                                  double *sZ)
+{
+    if (nchunk <= 16)
+        row_softmax_stats_lpr<16>(src, nrows, nchunk, kf, sM, sZ);
+    else if (nchunk <= 32)
+        row_softmax_stats_lpr<32>(src, nrows, nchunk, kf, sM, sZ);
+    else
+        row_softmax_stats_lpr<64>(src, nrows, nchunk, kf, sM, sZ);
 }
 
 // ---------------------------------------------------------------------------
@@ -213,12 +189,23 @@ __global__ __launch_bounds__(kRowThreads) void accept_stats_kernel(AcceptArgs a,
     __shared__ float fscr[kRowThreads / kWave];
     __shared__ int iscr[kRowThreads / kWave];
     __shared__ double dscr[kRowThreads / kWave];
-    __shared__ int last_flag;
     const int c = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
+    const int g = a.gamma;
+    if (SAMPLE && r == a.rows) {
+        // one extra block per sequence draws the round's uniforms (they depend on no
+        // data), off the critical path of the decide step
+        if (c == 0 && (int)threadIdx.x <= g)
+            w.u[(int64_t)b * (g + 1) + threadIdx.x] =
+                philox_uniform(a.seed, threadIdx.x, a.step, stream_of(a, b), kTagAccept);
+        return;
+    }
     const float *row = row_ptr(a, b, r);
     const int base = c * kChunk;
-    float x[kPerThread];
-    load_chunk<VEC, kPerThread>(row, base, a.V, x);
+    // the drafted token of this row's position (none for the bonus row gamma)
+    const int pos = r <= g ? r : r - g - 1;
+    const int x = (SAMPLE && pos < g) ? a.tokens[(int64_t)b * g + pos] : -1;
+    float xv[kPerThread];
+    load_chunk<VEC, kPerThread>(row, base, a.V, xv);
 
     RowPart part;
     if (!SAMPLE) {
@@ -227,39 +214,84 @@ __global__ __launch_bounds__(kRowThreads) void accept_stats_kernel(AcceptArgs a,
 #pragma unroll
         for (int k = 0; k < kPerThread; ++k) {
             const int e = chunk_index<VEC>(base, k);
-            if (e < a.V) argmax_merge(v, idx, x[k], e);
+            if (e < a.V) argmax_merge(v, idx, xv[k], e);
         }
         block_argmax(v, idx, fscr, iscr);
         part.m = v;
         part.arg = idx;
         part.s = 0.0;
     } else {
+        // the thread holding the drafted token keeps its logit for the ratio test
+        if (x >= base && x < base + kChunk && x < a.V) {
+#pragma unroll
+            for (int k = 0; k < kPerThread; ++k)
+                if (chunk_index<VEC>(base, k) == x)
+                    w.xlog[(int64_t)b * 2 * g + (r <= g ? 0 : g) + pos] = xv[k];
+        }
         // each thread: its own max and its sum relative to it (no barrier); then the block
         // rescales the per-thread sums to the chunk max in fp64
         float mt = -INFINITY;
 #pragma unroll
-        for (int k = 0; k < kPerThread; ++k) mt = fmaxf(mt, x[k]);
+        for (int k = 0; k < kPerThread; ++k) mt = fmaxf(mt, xv[k]);
+        // branch-free: -inf logits (masked, or beyond V) weigh exp2f(-inf) = 0
+        const float mref = mt == -INFINITY ? 0.0f : mt;
         double st = 0.0;
 #pragma unroll
-        for (int k = 0; k < kPerThread; ++k)
-            if (x[k] != -INFINITY) st += (double)exp2f((x[k] - mt) * a.kf);
+        for (int k = 0; k < kPerThread; ++k) st += (double)exp2f((xv[k] - mref) * a.kf);
         const float m = block_max(mt, fscr);
-        const double s = block_sum(st > 0.0 ? st * exp2(((double)mt - (double)m) * a.kd) : 0.0, dscr);
+        const double sm = block_sum(st > 0.0 ? st * (double)exp2f((mt - m) * a.kf) : 0.0, dscr);
         part.m = m;
         part.arg = 0;
-        part.s = s;
+        part.s = sm;
     }
+    if (threadIdx.x == 0) w.part[((int64_t)b * a.rows + r) * a.nchunk + c] = part;
+}
+
+// ---------------------------------------------------------------------------
+// GREEDY decide, one block per sequence: z_i = argmax of target row i, J = the length of
+// the prefix with x_i == z_i, emitted x_0..x_{J-1}, z_J.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kRowThreads) void accept_greedy_kernel(AcceptArgs a, AcceptWs w)
+{
+    extern __shared__ __align__(16) unsigned char dyn_lds[];
+    __shared__ int z[65];
+    __shared__ int firstbad, bad;
+    const int b = blockIdx.x;
+    const int g = a.gamma;
+    const int x = threadIdx.x < g ? a.tokens[(int64_t)b * g + threadIdx.x] : 0;
     if (threadIdx.x == 0) {
-        RowPart *dst = w.part + ((int64_t)b * a.rows + r) * a.nchunk + c;
-        st_coherent(&dst->m, part.m);
-        st_coherent(&dst->arg, part.arg);
-        st_coherent(&dst->s, part.s);
+        firstbad = g;
+        bad = 0;
     }
-    if (!arrive_last(&w.cnt[b], a.rows * a.nchunk, &last_flag)) return;
-    if (SAMPLE)
-        decide_sample(a, w, b);
-    else
-        decide_greedy(a, w, b);
+    const RowPart *pp = w.part + (int64_t)b * a.rows * a.nchunk;
+    RowPart *stage = reinterpret_cast<RowPart *>(dyn_lds);
+    const bool staged = a.rows * a.nchunk <= kMaxStaged;
+    if (staged) stage_parts(pp, a.rows * a.nchunk, stage, [] {});
+    const int wave = threadIdx.x / kWave;
+    for (int r = wave; r <= g; r += kRowThreads / kWave) {
+        float v;
+        int idx;
+        if (staged)
+            wave_combine_argmax(stage + (int64_t)r * a.nchunk, a.nchunk, v, idx);
+        else
+            wave_combine_argmax(pp + (int64_t)r * a.nchunk, a.nchunk, v, idx);
+        if (threadIdx.x % kWave == 0) z[r] = idx;
+    }
+    __syncthreads();
+    if (threadIdx.x < g) {
+        if (x != z[threadIdx.x]) atomicMin(&firstbad, (int)threadIdx.x);
+        if (x < 0 || x >= a.V) bad = 1;
+    }
+    __syncthreads();
+    const int J = firstbad;
+    int32_t *out = a.out_tokens + (int64_t)b * (g + 1);
+    for (int i = threadIdx.x; i <= g; i += blockDim.x) out[i] = i < J ? a.tokens[(int64_t)b * g + i] : (i == J ? z[J] : -1);
+    if (a.alpha)  // alpha is a sampling quantity
+        for (int i = threadIdx.x; i < g; i += blockDim.x) a.alpha[(int64_t)b * g + i] = __int_as_float(0x7fc00000);
+    if (threadIdx.x == 0) {
+        a.accept_len[b] = J;
+        if (a.dev_status) a.dev_status[b] = bad ? 2 : 0;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -269,17 +301,28 @@ __global__ __launch_bounds__(kRowThreads) void accept_alpha_kernel(AcceptArgs a,
     constexpr int kChunk = PER * kRowThreads;
     constexpr int kPerThread = PER;
     __shared__ double dscr[kRowThreads / kWave];
+    __shared__ double sM[2], sZ[2];
     __shared__ int last_flag;
     const int c = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
     const int g = a.gamma;
-    const RowStat sp = w.rowstat[(int64_t)b * a.rows + i];
-    const RowStat sq = w.rowstat[(int64_t)b * a.rows + g + 1 + i];
-    const float Mp = (float)sp.M, Mq = (float)sq.M;
-    const double iZp = 1.0 / sp.Z, iZq = 1.0 / sq.Z;
     float xp[kPerThread], xq[kPerThread];
     const int base = c * kChunk;
-    load_chunk<VEC, kPerThread>(row_ptr(a, b, i), base, a.V, xp);
-    load_chunk<VEC, kPerThread>(row_ptr(a, b, g + 1 + i), base, a.V, xq);
+    load_chunk2<VEC, kPerThread>(row_ptr(a, b, i), row_ptr(a, b, g + 1 + i), base, a.V, xp, xq);
+    // statistics of rows i (target) and gamma+1+i (draft): waves 0 and 1
+    const int wave = threadIdx.x / kWave;
+    if (wave < 2) {
+        float M;
+        double Z;
+        group_combine_softmax<kWave>(w.part + ((int64_t)b * a.rows + (wave == 0 ? i : g + 1 + i)) * a.nchunk, 0, 1,
+                                     a.nchunk, a.kf, M, Z);
+        if (threadIdx.x % kWave == 0) {
+            sM[wave] = (double)M;
+            sZ[wave] = Z;
+        }
+    }
+    __syncthreads();
+    const float Mp = (float)sM[0], Mq = (float)sM[1];
+    const double iZp = 1.0 / sZ[0], iZq = 1.0 / sZ[1];
     double s = 0.0;
 #pragma unroll
     for (int k = 0; k < kPerThread; ++k) {
@@ -299,24 +342,81 @@ __global__ __launch_bounds__(kRowThreads) void accept_alpha_kernel(AcceptArgs a,
 }
 
 // ---------------------------------------------------------------------------
+// SAMPLE decide and residual draw.  Every block of sequence b: row statistics of the
+// 2 gamma + 1 rows, the ratio tests u_i q(x_i) < p(x_i) (all blocks reach the same J),
+// then the residual mass of its chunk of the rows at position J.
+// ---------------------------------------------------------------------------
 template <bool VEC, int PER>
-__global__ __launch_bounds__(kRowThreads) void accept_sample_kernel(AcceptArgs a, AcceptWs w)
+__global__ __launch_bounds__(kRowThreads) void accept_resample_kernel(AcceptArgs a, AcceptWs w)
 {
     constexpr int kChunk = PER * kRowThreads;
     constexpr int kPerThread = PER;
-    __shared__ double dscr[kRowThreads / kWave];
+    extern __shared__ __align__(16) unsigned char dyn_lds[];
+    __shared__ double sM[129], sZ[129];
+    __shared__ double dscr[2 * (kRowThreads / kWave)];
     __shared__ double scan[kRowThreads];
     __shared__ int iscr[kRowThreads / kWave];
-    __shared__ int last_flag, s_chunk, s_usep;
-    __shared__ double s_base, s_target;
+    __shared__ int last_flag, s_chunk, s_usep, firstbad, bad;
+    __shared__ double s_base, s_target, s_uextra;
     const int c = blockIdx.x, b = blockIdx.y;
     const int g = a.gamma;
-    const SeqState st = w.seq[b];
-    const int J = st.J;
+
+    // drafted tokens and their logits (written by the statistics kernel)
+    int x = 0;
+    float lpx = 0.0f, lqx = 0.0f;
+    double u_mine = 0.0;  // thread i < gamma: ratio test i; thread gamma: the extra token
+    if (threadIdx.x < g) {
+        x = a.tokens[(int64_t)b * g + threadIdx.x];
+        lpx = w.xlog[(int64_t)b * 2 * g + threadIdx.x];
+        lqx = w.xlog[(int64_t)b * 2 * g + g + threadIdx.x];
+    }
+    if ((int)threadIdx.x <= g) u_mine = w.u[(int64_t)b * (g + 1) + threadIdx.x];
+    if (threadIdx.x == 0) {
+        firstbad = g;
+        bad = 0;
+    }
+    const RowPart *pp = w.part + (int64_t)b * a.rows * a.nchunk;
+    RowPart *stage = reinterpret_cast<RowPart *>(dyn_lds);
+    auto keep_extra = [&] {
+        if ((int)threadIdx.x == g) s_uextra = u_mine;
+    };
+    if (a.rows * a.nchunk <= kMaxStaged) {
+        stage_parts(pp, a.rows * a.nchunk, stage, keep_extra);
+        row_softmax_stats(stage, a.rows, a.nchunk, a.kf, sM, sZ);
+    } else {
+        keep_extra();
+        __syncthreads();
+        row_softmax_stats(pp, a.rows, a.nchunk, a.kf, sM, sZ);
+    }
+    if (threadIdx.x < g) {
+        const int i = threadIdx.x;
+        bool pass = false;
+        if (x >= 0 && x < a.V) {
+            const double p = exp(((double)lpx - sM[i]) * a.inv_t) / sZ[i];
+            const double q = exp(((double)lqx - sM[g + 1 + i]) * a.inv_t) / sZ[g + 1 + i];
+            pass = u_mine * q < p;
+        } else {
+            bad = 1;
+        }
+        if (!pass) atomicMin(&firstbad, i);
+    }
+    __syncthreads();
+    const int J = firstbad;
+    if (c == 0) {
+        int32_t *out = a.out_tokens + (int64_t)b * (g + 1);
+        for (int i = threadIdx.x; i <= g; i += blockDim.x)
+            if (i != J) out[i] = i < J ? a.tokens[(int64_t)b * g + i] : -1;
+        if (threadIdx.x == 0) {
+            a.accept_len[b] = J;
+            if (a.dev_status) a.dev_status[b] = bad ? 2 : 0;
+        }
+    }
+
     const float *prow = a.target + ((int64_t)b * (g + 1) + J) * a.V;
     const float *qrow = J < g ? a.draft + ((int64_t)b * g + J) * a.V : nullptr;
-    const float Mp = (float)st.Mp, Mq = (float)st.Mq;
-    const double iZp = 1.0 / st.Zp, iZq = J < g ? 1.0 / st.Zq : 0.0;
+    // with no draft row (J == gamma) q is 0: iZq = 0, and Mq = Mp keeps exp2f finite
+    const float Mp = (float)sM[J], Mq = J < g ? (float)sM[g + 1 + J] : Mp;
+    const double iZp = 1.0 / sZ[J], iZq = J < g ? 1.0 / sZ[g + 1 + J] : 0.0;
     const int base = c * kChunk;
 
     // weight of token e: residual (or p when every draft was kept / the residual is empty)
@@ -324,18 +424,16 @@ __global__ __launch_bounds__(kRowThreads) void accept_sample_kernel(AcceptArgs a
     auto q_of = [&](float l) { return (double)exp2f((l - Mq) * a.kf) * iZq; };
 
     float xp[kPerThread], xq[kPerThread];
-    load_chunk<VEC, kPerThread>(prow, base, a.V, xp);
-    if (qrow) load_chunk<VEC>(qrow, base, a.V, xq);
+    load_chunk2<VEC, kPerThread>(prow, qrow ? qrow : prow, base, a.V, xp, xq);
+    // branch-free: a position at or beyond V holds -inf, whose weight exp2f(-inf) = 0
     double rs = 0.0, ps = 0.0;
 #pragma unroll
     for (int k = 0; k < kPerThread; ++k) {
-        if (xp[k] == -INFINITY) continue;
         const double p = p_of(xp[k]);
         ps += p;
-        rs += qrow ? fmax(0.0, p - q_of(xq[k])) : p;
+        rs += fmax(0.0, p - q_of(xq[k]));
     }
-    rs = block_sum(rs, dscr);
-    ps = block_sum(ps, dscr);
+    block_sum2(rs, ps, dscr);
     if (threadIdx.x == 0) {
         st_coherent(&w.res[(int64_t)b * a.nchunk + c].r, rs);
         st_coherent(&w.res[(int64_t)b * a.nchunk + c].p, ps);
@@ -353,8 +451,7 @@ __global__ __launch_bounds__(kRowThreads) void accept_sample_kernel(AcceptArgs a
         zr = wave_sum(zr);
         zp = wave_sum(zp);
         const bool usep = !(zr > 0.0);
-        const double u = philox_uniform(a.seed, (uint64_t)g, a.step, stream_of(a, b), kTagAccept);
-        const double target = u * (usep ? zp : zr);
+        const double target = s_uextra * (usep ? zp : zr);
         int chunk;
         double cbase;
         wave_find_chunk(a.nchunk, target, [&](int cc) { return usep ? rp[cc].p : rp[cc].r; }, chunk, cbase);
@@ -375,21 +472,14 @@ __global__ __launch_bounds__(kRowThreads) void accept_sample_kernel(AcceptArgs a
         return twor ? fmax(0.0, p - q_of(lq)) : p;
     };
     int y = chunk_inverse_cdf<PER, VEC>(prow, twor ? qrow : nullptr, cbase, a.V, s_base, s_target, weight, scan, iscr);
-    if (y < 0) {
-        // rounding left the running sum just short of u* Z: take the last token with mass
-        int lastpos = -1;
-        for (int e = cbase + (int)threadIdx.x; e < min(cbase + kChunk, a.V); e += kRowThreads)
-            if (weight(prow[e], twor ? qrow[e] : prow[e]) > 0.0) lastpos = max(lastpos, e);
-        y = block_max_int(lastpos, iscr);
-        if (y < 0) y = cbase;
-    }
+    if (y < 0) y = cbase;  // no mass in the chunk at all (cannot happen for the chunk found)
     if (threadIdx.x == 0) a.out_tokens[(int64_t)b * (g + 1) + J] = y;
 }
 
 template <typename K>
-static hipError_t launch(K kernel, dim3 grid, hipStream_t s, const AcceptArgs &a, const AcceptWs &w)
+static hipError_t launch(K kernel, dim3 grid, hipStream_t s, const AcceptArgs &a, const AcceptWs &w, size_t lds = 0)
 {
-    hipLaunchKernelGGL(kernel, grid, dim3(kRowThreads), 0, s, a, w);
+    hipLaunchKernelGGL(kernel, grid, dim3(kRowThreads), lds, s, a, w);
     return hipGetLastError();
 }
 
@@ -397,12 +487,21 @@ template <bool VEC, int PER>
 static sv_status run_accept(const AcceptArgs &a, const AcceptWs &w, hipStream_t s, bool sample, bool alpha)
 {
     const dim3 gstats(a.nchunk, a.rows, a.B);
-    if (!sample)
-        return launch(accept_stats_kernel<VEC, false, PER>, gstats, s, a, w) == hipSuccess ? SV_OK : SV_ERR_HIP;
-    if (launch(accept_stats_kernel<VEC, true, PER>, gstats, s, a, w) != hipSuccess) return SV_ERR_HIP;
+    // staging slots: the part count rounded up to 1, 2, 4 or 8 per thread
+    const int staged = a.rows * a.nchunk;
+    int slots = kRowThreads;
+    while (slots < staged) slots *= 2;
+    const size_t lds = staged <= kMaxStaged ? (size_t)slots * sizeof(RowPart) : 0;
+    if (!sample) {
+        if (launch(accept_stats_kernel<VEC, false, PER>, gstats, s, a, w) != hipSuccess) return SV_ERR_HIP;
+        return launch(accept_greedy_kernel, dim3(a.B), s, a, w, lds) == hipSuccess ? SV_OK : SV_ERR_HIP;
+    }
+    if (launch(accept_stats_kernel<VEC, true, PER>, dim3(a.nchunk, a.rows + 1, a.B), s, a, w) != hipSuccess)
+        return SV_ERR_HIP;
     if (alpha && launch(accept_alpha_kernel<VEC, PER>, dim3(a.nchunk, a.gamma, a.B), s, a, w) != hipSuccess)
         return SV_ERR_HIP;
-    return launch(accept_sample_kernel<VEC, PER>, dim3(a.nchunk, a.B), s, a, w) == hipSuccess ? SV_OK : SV_ERR_HIP;
+    return launch(accept_resample_kernel<VEC, PER>, dim3(a.nchunk, a.B), s, a, w, lds) == hipSuccess ? SV_OK
+                                                                                                  : SV_ERR_HIP;
 }
 
 }  // namespace
@@ -432,8 +531,8 @@ extern "C" sv_status sv_spec_accept(const sv_accept_desc *d, void *workspace, si
     AcceptWs w;
     w.cnt = (int *)(ws + L.cnt);
     w.part = (RowPart *)(ws + L.part);
-    w.rowstat = (RowStat *)(ws + L.rowstat);
-    w.seq = (SeqState *)(ws + L.seq);
+    w.xlog = (float *)(ws + L.xlog);
+    w.u = (double *)(ws + L.u);
     w.res = (ResPart *)(ws + L.res);
     w.apart = (double *)(ws + L.apart);
 

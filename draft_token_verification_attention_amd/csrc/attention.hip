@@ -66,6 +66,19 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u)
 // (vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their no-wait maxima).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
+// Combine lane l with lane l ^ 32 (v_permlane32_swap: with both operands x, the two
+// results hold x[l % 32] and x[l % 32 + 32] in every lane l).
+__device__ __forceinline__ float half_swap_max(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ bool node_visible(const AttnArgs &a, const uint32_t *bits_row, int i, int j)
 {
     // j = position among the new tokens (0 <= j < n_q)
@@ -282,15 +295,23 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
         if (!have) continue;
         const int t0 = tile_start(li);
 
-        // S^T (32 keys x 32 rows) = K (keys x d) . Q^T (d x rows)
-        f32x16 sacc;
+        // S^T (32 keys x 32 rows) = K (keys x d) . Q^T (d x rows), as two independent MFMA
+        // chains over the even and odd d chunks (half the dependent-MFMA latency)
+        f32x16 sacc, sacc1;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) sacc[v] = 0.0f;
-#pragma unroll
-        for (int c = 0; c < NKC; ++c) {
-            const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(gK + l32 * KROW + (16 * c + 8 * h) * 2);
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], sacc, 0, 0, 0);
+        for (int v = 0; v < 16; ++v) {
+            sacc[v] = 0.0f;
+            sacc1[v] = 0.0f;
         }
+#pragma unroll
+        for (int c = 0; c < NKC; c += 2) {
+            const bf16x8 kf0 = *reinterpret_cast<const bf16x8 *>(gK + l32 * KROW + (16 * c + 8 * h) * 2);
+            const bf16x8 kf1 = *reinterpret_cast<const bf16x8 *>(gK + l32 * KROW + (16 * c + 16 + 8 * h) * 2);
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0, qf[c], sacc, 0, 0, 0);
+            sacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf1, qf[c + 1], sacc1, 0, 0, 0);
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sacc[v] += sacc1[v];
         // lane (row l32, half h) holds keys 8*(v/4) + 4*h + v%4
         float sv[16];
         const bool need_mask = (t0 + kTileKeys > P);
@@ -308,7 +329,7 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
         float mloc = sv[0];
 #pragma unroll
         for (int v = 1; v < 16; ++v) mloc = fmaxf(mloc, sv[v]);
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+        mloc = half_swap_max(mloc);  // the row's other 16 keys sit in lane l ^ 32
         const float m_new = fmaxf(m_run, mloc);
         float alpha = 1.0f;
         float p[16];
@@ -392,7 +413,7 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
             const float lk = mls[((wr * NWK + k) * 2) * 64 + 64 + lane];
             Lr += (mk == -INFINITY) ? 0.0f : lk * exp2f(mk - M);
         }
-        Lr += __shfl_xor(Lr, 32);  // the other half of the row's keys
+        Lr = half_swap_sum(Lr);  // the other half of the row's keys
         row_m = M;
         row_inv_l = Lr;
         if (NWK > 1) {
@@ -455,22 +476,25 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
 }
 
 // ---------------------------------------------------------------------------
-// Split combine: one thread per output float4 of a row.  Per row: M = max_s m_s,
-// L = sum_s l_s 2^(m_s - M), O = sum_s o_s 2^(m_s - M) / L.  The partials are read in
-// chunks of kCombChunk splits (all of a chunk's loads in flight at once); the first
-// chunk is issued before the (max, sum) pairs, so a combine of up to kCombChunk splits
-// costs one memory round trip.
-// Grid: (row chunk, kv group x row tile); a block covers CR rows x DH/4 float4 columns.
+// Split combine.  Per row: M = max_s m_s, L = sum_s l_s 2^(m_s - M),
+// O = sum_s o_s 2^(m_s - M) / L.  A block covers CR rows; each row is served by NSL
+// split lanes x DH/4 float4 lanes: split lane sl reads splits sl, sl + NSL, ... (all of
+// its loads issued at once, clamped in-bounds and weighted 0 past the row's last split),
+// and the split lanes are summed through LDS in fixed order.
+// Grid: (row chunk, kv group x row tile).
 // ---------------------------------------------------------------------------
 constexpr int kCombThreads = 256;
-constexpr int kCombChunk = 8;
 
-template <int DH, int ROWS_BLK>
+template <int DH, int ROWS_BLK, int NSL>
 __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a)
 {
-    constexpr int C4 = DH / 4;                 // float4 per row (lanes of one row, inside a wave)
-    constexpr int CR = kCombThreads / C4;      // rows per block
-    __shared__ float sw[CR][kMaxSplits + 1];   // per-split weights of this block's rows
+    constexpr int C4 = DH / 4;                    // float4 per row
+    constexpr int RL = NSL * C4;                  // threads per row
+    constexpr int CR = kCombThreads / RL;         // rows per block
+    constexpr int SPT = kMaxSplits / NSL;         // splits per lane at most
+    __shared__ float s_m[kCombThreads];
+    __shared__ float4 s_o[kCombThreads];
+    __shared__ float s_l[kCombThreads];
     const int gidx = blockIdx.y;
     const int kg = gidx / a.RT, rt = gidx % a.RT;
     const int b = kg / a.Hkv, kvh = kg % a.Hkv;
@@ -478,65 +502,76 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a)
     const int T = P + a.n_q;
     const bool overflow = (int64_t)T > (int64_t)a.nsplit * a.split_keys;
     const int ns = overflow ? a.nsplit : (T + a.split_keys - 1) / a.split_keys;
-    const int rl = threadIdx.x / C4;           // row within the block
+    const int rl = threadIdx.x / RL;              // row within the block
+    const int sl = (threadIdx.x / C4) % NSL;      // split lane
     const int d4 = threadIdx.x % C4;
-    const int r = blockIdx.x * CR + rl;        // row within the tile
+    const int r = blockIdx.x * CR + rl;           // row within the tile
     const int row = rt * ROWS_BLK + r;
     const bool ok = r < ROWS_BLK && row < a.rows;
+    const int rr = ok ? r : 0;                    // in-bounds row for the (unused) loads of idle rows
     const float *pg = a.part + (int64_t)gidx * a.nsplit * ROWS_BLK * (DH + 4);
-    auto row_at = [&](int u) { return pg + ((int64_t)u * ROWS_BLK + r) * (DH + 4); };  // o[DH], max, sum
-    auto o_at = [&](int u) { return row_at(u) + 4 * d4; };
+    auto row_at = [&](int u) { return pg + ((int64_t)u * ROWS_BLK + rr) * (DH + 4); };  // o[DH], max, sum
+    const int nmine = ns > sl ? (ns - sl + NSL - 1) / NSL : 0;  // splits this lane owns
 
-    float4 v[kCombChunk];
+    float4 o[SPT];
+    float2 ml[SPT];
 #pragma unroll
-    for (int k = 0; k < kCombChunk; ++k)
-        if (ok && k < ns) v[k] = *reinterpret_cast<const float4 *>(o_at(k));
-
-    // the C4 lanes of a row split its (max, sum) pairs among them
+    for (int k = 0; k < SPT; ++k) {
+        if (k * NSL < ns) {  // uniform over the block
+            const int u = min(sl + k * NSL, ns - 1);
+            o[k] = *reinterpret_cast<const float4 *>(row_at(u) + 4 * d4);
+            ml[k] = *reinterpret_cast<const float2 *>(row_at(u) + DH);
+        }
+    }
     float mloc = -INFINITY;
-    for (int ss = d4; ok && ss < ns; ss += C4) mloc = fmaxf(mloc, row_at(ss)[DH]);
 #pragma unroll
-    for (int o = C4 / 2; o > 0; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o));
-    const float M = mloc;
-    float lloc = 0.0f;
-    for (int ss = d4; ok && ss < ns; ss += C4) {
-        const float2 ml = *reinterpret_cast<const float2 *>(row_at(ss) + DH);
-        const float w = ml.x == -INFINITY ? 0.0f : exp2f(ml.x - M);
-        sw[rl][ss] = w;
-        lloc += ml.y * w;
-    }
-#pragma unroll
-    for (int o = C4 / 2; o > 0; o >>= 1) lloc += __shfl_xor(lloc, o);
+    for (int k = 0; k < SPT; ++k)
+        if (k < nmine) mloc = fmaxf(mloc, ml[k].x);
+    s_m[threadIdx.x] = mloc;
     __syncthreads();
-    if (!ok) return;
-
+    float M = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < NSL; ++q) M = fmaxf(M, s_m[rl * RL + q * C4 + d4]);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int u0 = 0; u0 < ns; u0 += kCombChunk) {
-        if (u0 > 0) {
+    float lsum = 0.0f;
 #pragma unroll
-            for (int k = 0; k < kCombChunk; ++k)
-                if (u0 + k < ns) v[k] = *reinterpret_cast<const float4 *>(o_at(u0 + k));
-        }
-#pragma unroll
-        for (int k = 0; k < kCombChunk; ++k) {
-            if (u0 + k < ns) {
-                const float w = sw[rl][u0 + k];
-                acc.x += v[k].x * w;
-                acc.y += v[k].y * w;
-                acc.z += v[k].z * w;
-                acc.w += v[k].w * w;
-            }
+    for (int k = 0; k < SPT; ++k) {
+        if (k < nmine) {
+            const float w = ml[k].x == -INFINITY ? 0.0f : exp2f(ml[k].x - M);
+            acc.x += o[k].x * w;
+            acc.y += o[k].y * w;
+            acc.z += o[k].z * w;
+            acc.w += o[k].w * w;
+            lsum += ml[k].y * w;
         }
     }
-    const float L = lloc;
+    if (NSL > 1) {
+        s_o[threadIdx.x] = acc;
+        s_l[threadIdx.x] = lsum;
+        __syncthreads();
+        if (sl != 0) return;
+        acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        lsum = 0.0f;
+#pragma unroll
+        for (int q = 0; q < NSL; ++q) {  // fixed order: deterministic
+            const float4 t = s_o[rl * RL + q * C4 + d4];
+            acc.x += t.x;
+            acc.y += t.y;
+            acc.z += t.z;
+            acc.w += t.w;
+            lsum += s_l[rl * RL + q * C4 + d4];
+        }
+    }
+    if (!ok) return;
+    const float L = lsum;
     const float inv = overflow ? __int_as_float(0x7fc00000) : 1.0f / L;
     const int i = row / a.G;
     const int hq = kvh * a.G + row % a.G;
-    uint16_t *o = (uint16_t *)a.out + (int64_t)b * a.o_sb + (int64_t)i * a.o_st + (int64_t)hq * a.o_sh + 4 * d4;
+    uint16_t *out = (uint16_t *)a.out + (int64_t)b * a.o_sb + (int64_t)i * a.o_st + (int64_t)hq * a.o_sh + 4 * d4;
     uint2 pk;
     pk.x = (uint32_t)f32_to_bf16(acc.x * inv) | ((uint32_t)f32_to_bf16(acc.y * inv) << 16);
     pk.y = (uint32_t)f32_to_bf16(acc.z * inv) | ((uint32_t)f32_to_bf16(acc.w * inv) << 16);
-    *reinterpret_cast<uint2 *>(o) = pk;
+    *reinterpret_cast<uint2 *>(out) = pk;
     if (a.lse && d4 == 0)
         a.lse[((int64_t)b * a.n_q + i) * a.Hq + hq] = overflow ? __int_as_float(0x7fc00000) : (M + log2f(L)) * kLn2;
 }
@@ -627,13 +662,13 @@ static bool plan_attention(const sv_attn_desc *d, Plan &p)
     if (d->split_keys > 0) {
         sk = ((int64_t)d->split_keys + unit - 1) / unit * unit;
     } else if (p.variant == 1) {
-        // Few query rows: splitting keys is cheap (a partial is at most 32 rows), so cut
-        // each sequence until the groups fill one wave of blocks on the 256 CUs (two
-        // 4-wave blocks fit per CU), keeping splits between 128 and 4096 keys.
-        const int64_t nsp = (512 + groups - 1) / groups;
-        sk = (Tmax + nsp - 1) / nsp;
+        // Few query rows: splitting keys is cheap (a partial is at most 32 rows).  Aim at
+        // about 4096 splits in all, which balances uneven sequence lengths over the 256 CUs
+        // (two 4-wave blocks per CU), keeping splits between 256 keys (shorter ones cost
+        // more in partials and launch than they gain) and 4096.
+        sk = (Tmax * groups + 4095) / 4096;
         sk = (sk + unit - 1) / unit * unit;
-        if (sk < 128) sk = 128;
+        if (sk < 256) sk = 256;
         if (sk > 4096) sk = 4096;
     } else {
         // Many rows per block: a partial costs as much as the keys it summarizes, so split
@@ -705,11 +740,18 @@ static hipError_t launch_variant(const Plan &p, const AttnArgs &a, hipStream_t s
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.nsplit == 1) return e;
     constexpr int ROWS_BLK = 32 * NWR;
-    constexpr int CR = kCombThreads / (DH / 4);
     const int tile_rows = p.rows < ROWS_BLK ? p.rows : ROWS_BLK;
-    hipLaunchKernelGGL((attn_combine_kernel<DH, ROWS_BLK>), dim3((tile_rows + CR - 1) / CR, p.KG * p.RT),
-                       dim3(kCombThreads), 0,
-                       s, a);
+    // split lanes per row: enough for the splits, at most the block's width
+    const int nsl = p.nsplit <= 1 ? 1 : p.nsplit <= 2 ? 2 : p.nsplit <= 4 ? 4 : 8;
+    const dim3 blk(kCombThreads);
+    const int g = p.KG * p.RT;
+    auto rows_per = [](int nsl_) { return kCombThreads / (nsl_ * (DH / 4)); };
+    switch (nsl) {
+    case 1: hipLaunchKernelGGL((attn_combine_kernel<DH, ROWS_BLK, 1>), dim3((tile_rows + rows_per(1) - 1) / rows_per(1), g), blk, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((attn_combine_kernel<DH, ROWS_BLK, 2>), dim3((tile_rows + rows_per(2) - 1) / rows_per(2), g), blk, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((attn_combine_kernel<DH, ROWS_BLK, 4>), dim3((tile_rows + rows_per(4) - 1) / rows_per(4), g), blk, 0, s, a); break;
+    default: hipLaunchKernelGGL((attn_combine_kernel<DH, ROWS_BLK, 8>), dim3((tile_rows + rows_per(8) - 1) / rows_per(8), g), blk, 0, s, a); break;
+    }
     return hipGetLastError();
 }
 

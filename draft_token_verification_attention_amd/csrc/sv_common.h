@@ -56,22 +56,124 @@ __device__ __forceinline__ double philox_uniform(uint64_t seed, uint64_t index, 
 }
 
 // ---------------------------------------------------------------------------
-// wave64 reductions
+// wave64 cross-lane primitives on DPP lane moves (VALU operand modifiers: no LDS round
+// trip, unlike shuffles, which go through ds_bpermute).  GFX9 DPP controls: row_shr:n
+// moves a value n lanes up inside each row of 16 lanes; row_bcast:15 / row_bcast:31 copy
+// lane 15 of each row / lane 31 into the following rows selected by the row mask.
+// Lanes without a source (or outside the row mask) receive the identity `id`.
 // ---------------------------------------------------------------------------
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t id, uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, CTRL, ROWS, 0xf, false);
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_move(int id, int x)
+{
+    return (int)dpp_u32<CTRL, ROWS>((uint32_t)id, (uint32_t)x);
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_move(float id, float x)
+{
+    return __uint_as_float(dpp_u32<CTRL, ROWS>(__float_as_uint(id), __float_as_uint(x)));
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_move(double id, double x)
+{
+    const uint64_t o = (uint64_t)__double_as_longlong(id), v = (uint64_t)__double_as_longlong(x);
+    const uint32_t lo = dpp_u32<CTRL, ROWS>((uint32_t)o, (uint32_t)v);
+    const uint32_t hi = dpp_u32<CTRL, ROWS>((uint32_t)(o >> 32), (uint32_t)(v >> 32));
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// value of lane l (l uniform across the wave)
+__device__ __forceinline__ int lane_value(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
+__device__ __forceinline__ float lane_value(float x, int l)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+__device__ __forceinline__ double lane_value(double x, int l)
+{
+    const uint64_t v = (uint64_t)__double_as_longlong(x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Inclusive scan over the 64 lanes in lane order for an associative op with identity
+// id: Hillis-Steele inside each 16-lane row, then the row totals.  The combination
+// order is fixed, so the result is deterministic.
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_scan_incl(T x, T id, Op op)
+{
+    x = op(x, dpp_move<kDppRowShr1, 0xf>(id, x));
+    x = op(x, dpp_move<kDppRowShr2, 0xf>(id, x));
+    x = op(x, dpp_move<kDppRowShr4, 0xf>(id, x));
+    x = op(x, dpp_move<kDppRowShr8, 0xf>(id, x));
+    x = op(x, dpp_move<kDppRowBcast15, 0xa>(id, x));
+    x = op(x, dpp_move<kDppRowBcast31, 0xc>(id, x));
+    return x;
+}
+
+struct OpAdd {
+    template <typename T>
+    __device__ T operator()(T a, T b) const { return a + b; }
+};
+struct OpMax {
+    __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
+    __device__ double operator()(double a, double b) const { return fmax(a, b); }
+    __device__ int operator()(int a, int b) const { return max(a, b); }
+};
+struct OpMin {
+    __device__ int operator()(int a, int b) const { return min(a, b); }
+};
+
+// Wave totals (every lane gets the result).
 template <typename T>
 __device__ __forceinline__ T wave_sum(T x)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-    return x;
+    return lane_value(wave_scan_incl(x, (T)0, OpAdd()), kWave - 1);
 }
 
 template <typename T>
 __device__ __forceinline__ T wave_max(T x)
 {
+    return lane_value(wave_scan_incl(x, (T)-INFINITY, OpMax()), kWave - 1);
+}
+
+__device__ __forceinline__ int wave_max_int(int x)
+{
+    return lane_value(wave_scan_incl(x, (int)0x80000000, OpMax()), kWave - 1);
+}
+
+__device__ __forceinline__ int wave_min_int(int x)
+{
+    return lane_value(wave_scan_incl(x, 0x7fffffff, OpMin()), kWave - 1);
+}
+
+// Totals of aligned lane groups of GROUP = 16, 32 or 64 lanes (every lane gets its own
+// group's total).
+template <int GROUP, typename T, typename Op>
+__device__ __forceinline__ T group_total(T x, T id, Op op)
+{
+    static_assert(GROUP == 16 || GROUP == 32 || GROUP == 64, "lane group");
+    x = op(x, dpp_move<kDppRowShr1, 0xf>(id, x));
+    x = op(x, dpp_move<kDppRowShr2, 0xf>(id, x));
+    x = op(x, dpp_move<kDppRowShr4, 0xf>(id, x));
+    x = op(x, dpp_move<kDppRowShr8, 0xf>(id, x));
+    if (GROUP >= 32) x = op(x, dpp_move<kDppRowBcast15, 0xa>(id, x));
+    if (GROUP == 64) x = op(x, dpp_move<kDppRowBcast31, 0xc>(id, x));
+    const int g = (int)(threadIdx.x % kWave) / GROUP;
+    T r = lane_value(x, GROUP - 1);
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x = fmax(x, __shfl_xor(x, o));
-    return x;
+    for (int k = 1; k < kWave / GROUP; ++k) {
+        const T t = lane_value(x, (k + 1) * GROUP - 1);
+        if (g == k) r = t;
+    }
+    return r;
 }
 
 // (value, index) with the larger value winning and ties going to the lower index.
@@ -83,14 +185,24 @@ __device__ __forceinline__ void argmax_merge(float &v, int &i, float v2, int i2)
     }
 }
 
+template <int CTRL, int ROWS>
+__device__ __forceinline__ void argmax_step(float &v, int &i)
+{
+    const float v2 = dpp_move<CTRL, ROWS>(-INFINITY, v);
+    const int i2 = dpp_move<CTRL, ROWS>(0x7fffffff, i);
+    argmax_merge(v, i, v2, i2);
+}
+
 __device__ __forceinline__ void wave_argmax(float &v, int &i)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const float v2 = __shfl_xor(v, o);
-        const int i2 = __shfl_xor(i, o);
-        argmax_merge(v, i, v2, i2);
-    }
+    argmax_step<kDppRowShr1, 0xf>(v, i);
+    argmax_step<kDppRowShr2, 0xf>(v, i);
+    argmax_step<kDppRowShr4, 0xf>(v, i);
+    argmax_step<kDppRowShr8, 0xf>(v, i);
+    argmax_step<kDppRowBcast15, 0xa>(v, i);
+    argmax_step<kDppRowBcast31, 0xc>(v, i);
+    v = lane_value(v, kWave - 1);
+    i = lane_value(i, kWave - 1);
 }
 
 // ---------------------------------------------------------------------------

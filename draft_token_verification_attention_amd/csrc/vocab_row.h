@@ -28,30 +28,64 @@ __device__ __forceinline__ int chunk_index(int chunk_base, int k)
     return chunk_base + (int)threadIdx.x + kRowThreads * k;
 }
 
+// All of a thread's loads are issued before any is waited for: a full chunk (the common
+// case, a uniform branch) uses unconditional vector loads; the last, partial chunk of a row
+// reads clamped in-bounds addresses and masks the positions at or beyond V.
 template <bool VEC, int PER>
 __device__ __forceinline__ void load_chunk(const float *__restrict__ row, int chunk_base, int V, float (&x)[PER])
 {
-    if (VEC) {
+    if (VEC && chunk_base + PER * kRowThreads <= V) {
+#pragma unroll
+        for (int k4 = 0; k4 < PER / 4; ++k4) {
+            const float4 f = *reinterpret_cast<const float4 *>(row + chunk_base + 4 * (int)threadIdx.x + 1024 * k4);
+            x[4 * k4 + 0] = f.x;
+            x[4 * k4 + 1] = f.y;
+            x[4 * k4 + 2] = f.z;
+            x[4 * k4 + 3] = f.w;
+        }
+        return;
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int e = chunk_index<VEC>(chunk_base, k);
+        const float v = row[min(e, V - 1)];
+        x[k] = e < V ? v : -INFINITY;
+    }
+}
+
+// The same chunk of two rows, every load issued before any is waited for (one branch:
+// full chunk or the row's last, partial chunk).
+template <bool VEC, int PER>
+__device__ __forceinline__ void load_chunk2(const float *__restrict__ r0, const float *__restrict__ r1, int chunk_base,
+                                            int V, float (&x0)[PER], float (&x1)[PER])
+{
+    if (VEC && chunk_base + PER * kRowThreads <= V) {
+        float4 f0[PER / 4], f1[PER / 4];
 #pragma unroll
         for (int k4 = 0; k4 < PER / 4; ++k4) {
             const int e = chunk_base + 4 * (int)threadIdx.x + 1024 * k4;
-            if (e + 3 < V) {
-                const float4 f = *reinterpret_cast<const float4 *>(row + e);
-                x[4 * k4 + 0] = f.x;
-                x[4 * k4 + 1] = f.y;
-                x[4 * k4 + 2] = f.z;
-                x[4 * k4 + 3] = f.w;
-            } else {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) x[4 * k4 + j] = (e + j < V) ? row[e + j] : -INFINITY;
-            }
+            f0[k4] = *reinterpret_cast<const float4 *>(r0 + e);
+            f1[k4] = *reinterpret_cast<const float4 *>(r1 + e);
         }
-    } else {
 #pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int e = chunk_base + (int)threadIdx.x + kRowThreads * k;
-            x[k] = e < V ? row[e] : -INFINITY;
+        for (int k4 = 0; k4 < PER / 4; ++k4) {
+            x0[4 * k4 + 0] = f0[k4].x;
+            x0[4 * k4 + 1] = f0[k4].y;
+            x0[4 * k4 + 2] = f0[k4].z;
+            x0[4 * k4 + 3] = f0[k4].w;
+            x1[4 * k4 + 0] = f1[k4].x;
+            x1[4 * k4 + 1] = f1[k4].y;
+            x1[4 * k4 + 2] = f1[k4].z;
+            x1[4 * k4 + 3] = f1[k4].w;
         }
+        return;
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int e = chunk_index<VEC>(chunk_base, k);
+        const float v0 = r0[min(e, V - 1)], v1 = r1[min(e, V - 1)];
+        x0[k] = e < V ? v0 : -INFINITY;
+        x1[k] = e < V ? v1 : -INFINITY;
     }
 }
 
@@ -100,8 +134,7 @@ __device__ __forceinline__ void block_argmax(float &v, int &idx, float *sv, int 
 
 __device__ __forceinline__ int block_min_int(int v, int *scratch)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
+    v = wave_min_int(v);
     const int w = threadIdx.x / kWave;
     __syncthreads();
     if ((threadIdx.x % kWave) == 0) scratch[w] = v;
@@ -114,8 +147,7 @@ __device__ __forceinline__ int block_min_int(int v, int *scratch)
 
 __device__ __forceinline__ int block_max_int(int v, int *scratch)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+    v = wave_max_int(v);
     const int w = threadIdx.x / kWave;
     __syncthreads();
     if ((threadIdx.x % kWave) == 0) scratch[w] = v;
@@ -126,17 +158,34 @@ __device__ __forceinline__ int block_max_int(int v, int *scratch)
     return r;
 }
 
+// Two fp64 block sums at once (one barrier pair for both).
+__device__ __forceinline__ void block_sum2(double &a, double &b, double *scratch /* >= 2 * waves */)
+{
+    a = wave_sum(a);
+    b = wave_sum(b);
+    const int w = threadIdx.x / kWave;
+    constexpr int NW = kRowThreads / kWave;
+    __syncthreads();
+    if ((threadIdx.x % kWave) == 0) {
+        scratch[w] = a;
+        scratch[NW + w] = b;
+    }
+    __syncthreads();
+    a = 0.0;
+    b = 0.0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {  // fixed order: deterministic
+        a += scratch[i];
+        b += scratch[NW + i];
+    }
+}
+
 // Exclusive prefix sum (fp64) of one value per thread, in thread order: a wave scan,
 // then the wave totals (fixed order, deterministic).
 __device__ __forceinline__ double block_exclusive_scan(double v, double *scratch /* >= waves */)
 {
     const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
-    double incl = v;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const double t = __shfl_up(incl, o);
-        if (lane >= o) incl += t;
-    }
+    const double incl = wave_scan_incl(v, 0.0, OpAdd());
     __syncthreads();
     if (lane == kWave - 1) scratch[w] = incl;
     __syncthreads();
@@ -148,60 +197,71 @@ __device__ __forceinline__ double block_exclusive_scan(double v, double *scratch
 // Inverse-CDF search inside one chunk, in token order, over weights w(l0[e], l1[e]) of
 // one or two logit rows (l1 may be null: then w gets l0[e] twice).  `base` is the
 // cumulative weight before the chunk, `target` = u * Z.  Returns the smallest e with
-// base + C_e > target, or -1 when the chunk's running sum never passes it.  Two levels:
-// every thread sums PER consecutive weights (16-byte loads when VEC), a block scan finds
-// the segment where the running sum crosses target, and one wave scans that segment.
+// base + C_e > target; when rounding leaves the chunk's running sum at or below target,
+// the last position with positive weight (-1 if none).  Every thread owns PER
+// consecutive positions (16-byte loads when VEC) and sums their weights in order; a block
+// scan of those sums gives each thread its running sum c0; the one thread with
+// c0 <= target < c0 + its sum scans its own weights, still in registers.
 template <int PER, bool VEC, typename WeightFn>
 __device__ __forceinline__ int chunk_inverse_cdf(const float *l0, const float *l1, int chunk_base, int V, double base,
                                                  double target, WeightFn weight, double *scratch, int *iscratch)
 {
-    static_assert(PER <= kWave && PER % 4 == 0, "one wave scans a segment");
-    __shared__ int s_seg;
-    __shared__ double s_c0;
+    static_assert(PER % 4 == 0, "vector segments");
+    __shared__ int s_found;
     const int first = chunk_base + PER * (int)threadIdx.x;
-    double local = 0.0;
-    if (VEC && first + PER <= V) {
+    const float *l1r = l1 ? l1 : l0;  // the weight ignores its second argument for one row
+    double w[PER];
+    if (VEC && chunk_base + PER * kRowThreads <= V) {  // full chunk: all loads issued up front
+        float4 a[PER / 4], c[PER / 4];
 #pragma unroll
         for (int k4 = 0; k4 < PER / 4; ++k4) {
-            const float4 a = *reinterpret_cast<const float4 *>(l0 + first + 4 * k4);
-            const float4 c = l1 ? *reinterpret_cast<const float4 *>(l1 + first + 4 * k4) : a;
-            local += weight(a.x, c.x) + weight(a.y, c.y) + weight(a.z, c.z) + weight(a.w, c.w);
+            a[k4] = *reinterpret_cast<const float4 *>(l0 + first + 4 * k4);
+            c[k4] = *reinterpret_cast<const float4 *>(l1r + first + 4 * k4);
+        }
+#pragma unroll
+        for (int k4 = 0; k4 < PER / 4; ++k4) {
+            w[4 * k4 + 0] = weight(a[k4].x, c[k4].x);
+            w[4 * k4 + 1] = weight(a[k4].y, c[k4].y);
+            w[4 * k4 + 2] = weight(a[k4].z, c[k4].z);
+            w[4 * k4 + 3] = weight(a[k4].w, c[k4].w);
         }
     } else {
+        float a[PER], c[PER];
+#pragma unroll
         for (int k = 0; k < PER; ++k) {
-            const int e = first + k;
-            if (e < V) local += weight(l0[e], l1 ? l1[e] : l0[e]);
+            const int e = min(first + k, V - 1);
+            a[k] = l0[e];
+            c[k] = l1r[e];
         }
+#pragma unroll
+        for (int k = 0; k < PER; ++k) w[k] = first + k < V ? weight(a[k], c[k]) : 0.0;
     }
-    const double c0 = base + block_exclusive_scan(local, scratch);
-    const bool crossing = local > 0.0 && c0 <= target && c0 + local > target;
-    const int seg = block_min_int(crossing ? (int)threadIdx.x : 0x7fffffff, iscratch);
-    if (seg == 0x7fffffff) return -1;
-    if ((int)threadIdx.x == seg) {
-        s_seg = seg;
-        s_c0 = c0;
+    double local = 0.0;
+    int lastpos = -1;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        local += w[k];
+        if (w[k] > 0.0) lastpos = first + k;
+    }
+    if (threadIdx.x == 0) s_found = 0x7fffffff;
+    const double c0 = base + block_exclusive_scan(local, scratch);  // (its barriers publish s_found)
+    if (c0 <= target) {
+        // first own position whose running sum c0 + w_0 + ... + w_k passes target (the
+        // running sum only grows where w_k > 0, so that position has mass)
+        double pre = c0;
+        int hit = 0x7fffffff;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            pre += w[k];
+            if (hit == 0x7fffffff && pre > target) hit = first + k;
+        }
+        if (hit != 0x7fffffff) atomicMin(&s_found, hit);
     }
     __syncthreads();
-    int found = 0x7fffffff;
-    if (threadIdx.x < kWave) {
-        const int lane = threadIdx.x;
-        const int e = chunk_base + PER * s_seg + lane;
-        const double w = (lane < PER && e < V) ? weight(l0[e], l1 ? l1[e] : l0[e]) : 0.0;
-        double incl = w;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-            const double t = __shfl_up(incl, o);
-            if (lane >= o) incl += t;
-        }
-        const uint64_t hit = __ballot(w > 0.0 && s_c0 + incl > target);
-        const uint64_t pos = __ballot(w > 0.0);
-        if (hit)
-            found = chunk_base + PER * s_seg + (__ffsll((unsigned long long)hit) - 1);
-        else if (pos)  // rounding: the segment's own sum stops short of target
-            found = chunk_base + PER * s_seg + (63 - __clzll((unsigned long long)pos));
-    }
-    const int r = block_min_int(found, iscratch);
-    return r == 0x7fffffff ? -1 : r;
+    const int f = s_found;
+    if (f != 0x7fffffff) return f;
+    const int r = block_max_int(lastpos, iscratch);
+    return r;
 }
 
 // Combine per-chunk row statistics with one wave: lanes stride over the chunks.
@@ -232,6 +292,30 @@ __device__ __forceinline__ void wave_combine_softmax(const Part *pp, int nchunk,
     Z = wave_sum(z);
 }
 
+// Softmax statistics of several rows at once from their chunk partials: rows are laid
+// out over aligned groups of LPR lanes (LPR = 16, 32 or 64; a lane strides over chunks
+// c = lane % LPR + k LPR), so one wave pass covers 64 / LPR rows.  Per row:
+// M = max_c m_c and Z = sum_c S_c 2^((m_c - M) k) with the rescale factor in fp32.  Must
+// be called by a whole wave; `row` is this lane's row (rows >= nrows compute nothing
+// useful), the results are valid in every lane of the row's group.
+template <int LPR, typename Part>
+__device__ __forceinline__ void group_combine_softmax(const Part *pp, int row, int nrows, int nchunk, float kf,
+                                                      float &M, double &Z)
+{
+    const int c0 = (int)(threadIdx.x % LPR);
+    float m = -INFINITY;
+    if (row < nrows)
+        for (int c = c0; c < nchunk; c += LPR) m = fmaxf(m, pp[(int64_t)row * nchunk + c].m);
+    M = group_total<LPR>(m, -INFINITY, OpMax());
+    double z = 0.0;
+    if (row < nrows)
+        for (int c = c0; c < nchunk; c += LPR) {
+            const Part q = pp[(int64_t)row * nchunk + c];
+            if (q.s > 0.0) z += q.s * (double)exp2f((q.m - M) * kf);
+        }
+    Z = group_total<LPR>(z, 0.0, OpAdd());
+}
+
 // Find the first chunk whose running weight passes `target` (one wave; chunk weights
 // come from weight(c)).  Returns the chunk and the running weight before it; when
 // rounding leaves every prefix at or below target, the last chunk with weight.
@@ -247,27 +331,22 @@ __device__ __forceinline__ void wave_find_chunk(int nchunk, double target, WFn w
         const int c = c0 + lane;
         const double w = c < nchunk ? weight(c) : 0.0;
         // inclusive scan across the wave (fixed order)
-        double incl = w;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-            const double t = __shfl_up(incl, o);
-            if (lane >= o) incl += t;
-        }
+        const double incl = wave_scan_incl(w, 0.0, OpAdd());
         const double excl = carry + incl - w;
         const uint64_t pass = __ballot(c < nchunk && w > 0.0 && carry + incl > target);
         const uint64_t pos = __ballot(c < nchunk && w > 0.0);
         if (pos) {
             const int lp = 63 - __clzll((unsigned long long)pos);
             last_pos = c0 + lp;
-            last_base = __shfl(excl, lp);
+            last_base = lane_value(excl, lp);
         }
         if (pass) {
             const int fl = __ffsll((unsigned long long)pass) - 1;
             chunk = c0 + fl;
-            base = __shfl(excl, fl);
+            base = lane_value(excl, fl);
             return;
         }
-        carry += __shfl(incl, kWave - 1);
+        carry += lane_value(incl, kWave - 1);
     }
     chunk = last_pos < 0 ? nchunk - 1 : last_pos;
     base = last_pos < 0 ? 0.0 : last_base;

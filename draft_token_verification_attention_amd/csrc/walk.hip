@@ -165,13 +165,7 @@ __global__ __launch_bounds__(kRowThreads) void walk_level_kernel(WalkArgs a, Wal
         const double f = s_factor;
         auto weight = [&](float l, float) -> double { return (double)exp2f((l - mc) * a.kf) * f; };
         int y = chunk_inverse_cdf<kPerThread, VEC>(row, nullptr, cb, a.V, s_base, s_target, weight, scan, iscr);
-        if (y < 0) {
-            int lastpos = -1;
-            for (int e = cb + (int)threadIdx.x; e < min(cb + kChunk, a.V); e += kRowThreads)
-                if (weight(row[e], 0.0f) > 0.0) lastpos = max(lastpos, e);
-            y = block_max_int(lastpos, iscr);
-            if (y < 0) y = cb;
-        }
+        if (y < 0) y = cb;  // no mass in the chunk at all (cannot happen for the chunk found)
         if (threadIdx.x == 0) s_y = y;
         __syncthreads();
     }
