@@ -173,20 +173,36 @@ def main():
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
-    # kernel durations: HIP events on the launch stream around each call, same K steps
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        launch((args.warmup + i) % R, sh, events[i])
+    # Kernel durations: HIP events on the launch stream, same K steps.  The library's
+    # measurement hook records one more event right after the main attention kernel, so the
+    # attention call splits into its main kernel and the split combine.
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for e in events:
+        e[1].record()  # creates the event the library will record
     torch.cuda.synchronize()
-    att_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
-    acc_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    for i in range(args.steps):
+        sv.lib.sv_set_attention_mark(ctypes.c_void_p(events[i][1].cuda_event))
+        ev = events[i]
+        ev[0].record()
+        st = sv.lib.sv_verify_attention(ctypes.byref(adescs[(args.warmup + i) % R]), pa, ws_a, sh)
+        ev[2].record()
+        st2 = sv.lib.sv_spec_accept(ctypes.byref(sdescs[(args.warmup + i) % R]), ps, ws_s, sh)
+        ev[3].record()
+        if st or st2:
+            raise RuntimeError("launch failed: %d %d" % (st, st2))
+    sv.lib.sv_set_attention_mark(None)
+    torch.cuda.synchronize()
+    main_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    comb_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    att_ms = main_ms + comb_ms
+    acc_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
 
     drafts = B * gamma
     value = drafts / (ms_per_step * 1e-3)
     kv_tokens = int((P.astype(np.int64) + n_q).sum())
     att_bytes = esz * (B * n_q * Hq * D + 2 * kv_tokens * Hkv * D) + esz * B * n_q * Hq * D
     acc_bytes = 4 * V * B * (2 * gamma + 1)
-    att_gbs = att_bytes / (att_ms * 1e-3) / 1e9
+    main_gbs = att_bytes / (main_ms * 1e-3) / 1e9
 
     line = {
         "metric": "draft tokens verified/sec on 1 MI355X; achieved HBM GB/s as % of peak",
@@ -204,10 +220,14 @@ def main():
         "config": {"workload": cfg["name"], "batch": B, "gamma": gamma, "cached_context": int(P.max()),
                    "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "vocab": V, "temperature": tau,
                    "mode": "sample", "rotated_input_copies": R, "launch": "eager" if args.eager else "hip_graph"},
-        "roofline": {"bound": "hbm", "achieved": round(att_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(att_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "attn_bf16_kernel", "kernel_ms": round(att_ms, 5),
+        "roofline": {"bound": "hbm", "achieved": round(main_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(main_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl),
+                     "kernel": "attn_bf16_kernel", "kernel_ms": round(main_ms, 5),
                      "algorithmic_bytes": att_bytes},
+        "kernels_ms": {"attn_bf16_kernel": round(main_ms, 5), "attn_combine_kernel": round(comb_ms, 5),
+                       "sv_spec_accept": round(acc_ms, 5)},
+        "attention": {"kernel_ms": round(att_ms, 5), "algorithmic_bytes": att_bytes,
+                      "achieved_GBs": round(att_bytes / (att_ms * 1e-3) / 1e9, 1)},
         "accept": {"kernel_ms": round(acc_ms, 5), "algorithmic_bytes": acc_bytes,
                    "achieved_GBs": round(acc_bytes / (acc_ms * 1e-3) / 1e9, 1)},
     }
@@ -215,6 +235,25 @@ def main():
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(att, acc, cfg, scale, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+# HBM bytes per launch of attn_bf16_kernel (2 x FETCH_SIZE + WRITE_SIZE, the FETCH_SIZE
+# counter reading half the bytes of a plain copy of known size on this GPU), from the
+# rocprofv3 --pmc runs summarized under profiles/, and the SHA-256 of the attention source
+# they were taken on: a changed kernel reports null until the counters are taken again.
+TRAFFIC = {}
+TRAFFIC_SRC_SHA256 = None
+
+
+def measured_traffic(wl):
+    import hashlib
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "draft_token_verification_attention_amd",
+                       "csrc", "attention.hip")
+    with open(src, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if sha != TRAFFIC_SRC_SHA256 or wl not in TRAFFIC:
+        return None
+    return TRAFFIC[wl]
 
 
 def cpu_baseline(att, acc, cfg, scale, seconds):

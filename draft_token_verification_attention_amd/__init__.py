@@ -4,7 +4,7 @@ Argument marshalling only: every step of the path runs in the library's kernels.
 PyTorch supplies device memory and the current HIP stream.  The names mirror the
 C entry points declared in include/specverify.h.
 
-The library must be built in-tree (``python -m draft_token_verification_attention_amd._build``);
+The library must be built in-tree (``python draft_token_verification_attention_amd/_build.py``);
 importing this package without it raises ImportError -- there is no fallback.
 """
 from __future__ import annotations
@@ -54,13 +54,13 @@ class sv_walk_desc(ctypes.Structure):
 
 EXPORTS = ("sv_build_tree_mask", "sv_verify_attention_workspace", "sv_verify_attention",
            "sv_spec_accept_workspace", "sv_spec_accept", "sv_tree_walk_workspace", "sv_tree_walk",
-           "sv_status_string")
+           "sv_set_attention_mark", "sv_status_string")
 
 
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError("libspecverify.so is not built: run "
-                          "`python -m draft_token_verification_attention_amd._build` (%s)" % LIB_PATH)
+                          "`python draft_token_verification_attention_amd/_build.py` (%s)" % LIB_PATH)
     L = ctypes.CDLL(LIB_PATH)
     L.sv_build_tree_mask.argtypes = [_P, _i32, _i32, _P, _P, _P, _P, _P]
     L.sv_build_tree_mask.restype = ctypes.c_int
@@ -76,6 +76,8 @@ def _load():
     L.sv_tree_walk_workspace.restype = ctypes.c_size_t
     L.sv_tree_walk.argtypes = [ctypes.POINTER(sv_walk_desc), _P, ctypes.c_size_t, _P]
     L.sv_tree_walk.restype = ctypes.c_int
+    L.sv_set_attention_mark.argtypes = [_P]
+    L.sv_set_attention_mark.restype = ctypes.c_int
     L.sv_status_string.argtypes = [ctypes.c_int]
     L.sv_status_string.restype = ctypes.c_char_p
     return L

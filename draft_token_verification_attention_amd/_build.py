@@ -1,6 +1,8 @@
 """Build libspecverify.so (HIP for gfx950) in-tree with hipcc.
 
-    python -m draft_token_verification_attention_amd._build
+    python draft_token_verification_attention_amd/_build.py
+
+(run by path: importing the package needs the library this builds)
 """
 from __future__ import annotations
 

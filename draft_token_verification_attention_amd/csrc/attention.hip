@@ -730,6 +730,8 @@ static sv_status check_attention(const sv_attn_desc *d)
     return SV_OK;
 }
 
+static void *g_mark_event = nullptr;  // sv_set_attention_mark
+
 template <int DH, int NWR, int NWK>
 static hipError_t launch_variant(const Plan &p, const AttnArgs &a, hipStream_t s)
 {
@@ -738,6 +740,7 @@ static hipError_t launch_variant(const Plan &p, const AttnArgs &a, hipStream_t s
     else
         hipLaunchKernelGGL((attn_bf16_kernel<DH, NWR, NWK>), dim3(p.blocks), dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
+    if (e == hipSuccess && g_mark_event) e = hipEventRecord((hipEvent_t)g_mark_event, s);
     if (e != hipSuccess || p.nsplit == 1) return e;
     constexpr int ROWS_BLK = 32 * NWR;
     const int tile_rows = p.rows < ROWS_BLK ? p.rows : ROWS_BLK;
@@ -831,4 +834,10 @@ extern "C" sv_status sv_verify_attention(const sv_attn_desc *d, void *workspace,
         e = d->D == 128 ? launch_bf16<128>(p, a, s) : launch_bf16<64>(p, a, s);
     }
     return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+extern "C" sv_status sv_set_attention_mark(void *event)
+{
+    g_mark_event = event;
+    return SV_OK;
 }

@@ -231,6 +231,14 @@ SV_API size_t sv_tree_walk_workspace(const sv_walk_desc *desc);
 SV_API sv_status sv_tree_walk(const sv_walk_desc *desc, void *workspace, size_t workspace_bytes,
                        void *stream);
 
+/* Measurement hook for benchmarks.  When `event` (a hipEvent_t) is not NULL, every later */
+/* sv_verify_attention call also records it on its stream right after its main attention */
+/* kernel and before the split combine (if the call has one), so a caller's own events   */
+/* around the call split its time between the two kernels.  NULL turns the hook off.     */
+/* Process-wide setting without synchronization: set it from the launching thread.       */
+/* Always returns SV_OK; a failed record shows up as SV_ERR_HIP from the call.          */
+SV_API sv_status sv_set_attention_mark(void *event);
+
 /* Human-readable name of a status code (static storage). */
 SV_API const char *sv_status_string(sv_status status);
 
