@@ -49,11 +49,13 @@ struct AcceptWs {
     float *xlog;     // [B][2 gamma]: target then draft logit of each drafted token
     double *u;       // [B][gamma + 1]: the round's uniforms (ratio tests, then the extra token)
     ResPart *res;    // [B][nchunk]
+    double *seg;     // [B][nchunk][PER]: residual mass of each 256-token segment of a chunk
     double *apart;   // [B][gamma][nchunk]
 };
 
 struct AcceptArgs {
     int B, gamma, V, rows, nchunk;
+    int max_blocks;    // resident-block budget of a looping kernel
     int sample;
     float kf;          // log2(e) / T in fp32, for the bulk exponentials
     double inv_t;      // 1 / T in fp64, for decided probabilities
@@ -69,7 +71,7 @@ struct AcceptArgs {
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-    size_t cnt, part, xlog, u, res, apart, total;
+    size_t cnt, part, xlog, u, res, seg, apart, total;
 };
 
 static WsLayout accept_layout(int B, int gamma, int V)
@@ -88,6 +90,8 @@ static WsLayout accept_layout(int B, int gamma, int V)
     o += align256((size_t)B * (gamma + 1) * sizeof(double));
     L.res = o;
     o += align256((size_t)B * nchunk * sizeof(ResPart));
+    L.seg = o;  // 256-token segments: enough for either chunk size
+    o += align256((size_t)B * (nchunk + 3) * 16 * sizeof(double));
     L.apart = o;
     o += align256((size_t)B * gamma * nchunk * sizeof(double));
     L.total = o;
@@ -189,62 +193,67 @@ __global__ __launch_bounds__(kRowThreads) void accept_stats_kernel(AcceptArgs a,
     __shared__ float fscr[kRowThreads / kWave];
     __shared__ int iscr[kRowThreads / kWave];
     __shared__ double dscr[kRowThreads / kWave];
-    const int c = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
     const int g = a.gamma;
-    if (SAMPLE && r == a.rows) {
-        // one extra block per sequence draws the round's uniforms (they depend on no
-        // data), off the critical path of the decide step
-        if (c == 0 && (int)threadIdx.x <= g)
-            w.u[(int64_t)b * (g + 1) + threadIdx.x] =
-                philox_uniform(a.seed, threadIdx.x, a.step, stream_of(a, b), kTagAccept);
-        return;
-    }
-    const float *row = row_ptr(a, b, r);
-    const int base = c * kChunk;
-    // the drafted token of this row's position (none for the bonus row gamma)
-    const int pos = r <= g ? r : r - g - 1;
-    const int x = (SAMPLE && pos < g) ? a.tokens[(int64_t)b * g + pos] : -1;
-    float xv[kPerThread];
-    load_chunk<VEC, kPerThread>(row, base, a.V, xv);
+    // Tasks (chunk, row, sequence), chunk fastest; SAMPLE adds one row of tasks per
+    // sequence that draws the round's uniforms.  A grid smaller than the task count loops
+    // over them (blocks stay resident instead of being dispatched one per task).
+    const int rows_t = a.rows + (SAMPLE ? 1 : 0);
+    const int ntask = a.nchunk * rows_t * a.B;
+    for (int t = blockIdx.x; t < ntask; t += gridDim.x) {
+        const int c = t % a.nchunk;
+        const int r = (t / a.nchunk) % rows_t;
+        const int b = t / (a.nchunk * rows_t);
+        if (SAMPLE && r == a.rows) {
+            // the uniforms depend on no data: drawn off the decide step's critical path
+            if (c == 0 && (int)threadIdx.x <= g)
+                w.u[(int64_t)b * (g + 1) + threadIdx.x] =
+                    philox_uniform(a.seed, threadIdx.x, a.step, stream_of(a, b), kTagAccept);
+            continue;
+        }
+        const float *row = row_ptr(a, b, r);
+        const int base = c * kChunk;
+        // the drafted token of this row's position (none for the bonus row gamma)
+        const int pos = r <= g ? r : r - g - 1;
+        const int x = (SAMPLE && pos < g) ? a.tokens[(int64_t)b * g + pos] : -1;
+        float xv[kPerThread];
+        load_chunk<VEC, kPerThread>(row, base, a.V, xv);
 
-    RowPart part;
-    if (!SAMPLE) {
-        float v = -INFINITY;
-        int idx = 0x7fffffff;
+        RowPart part;
+        if (!SAMPLE) {
+            float v = -INFINITY;
+            int idx = 0x7fffffff;
 #pragma unroll
-        for (int k = 0; k < kPerThread; ++k) {
-            const int e = chunk_index<VEC>(base, k);
-            if (e < a.V) argmax_merge(v, idx, xv[k], e);
+            for (int k = 0; k < kPerThread; ++k) argmax_merge(v, idx, xv[k], chunk_index<VEC>(base, k));
+            block_argmax(v, idx, fscr, iscr);  // positions beyond V hold -inf and never win
+            part.m = v;
+            part.arg = idx;
+            part.s = 0.0;
+        } else {
+            // the thread holding the drafted token keeps its logit for the ratio test
+            if (x >= base && x < base + kChunk && x < a.V) {
+#pragma unroll
+                for (int k = 0; k < kPerThread; ++k)
+                    if (chunk_index<VEC>(base, k) == x)
+                        w.xlog[(int64_t)b * 2 * g + (r <= g ? 0 : g) + pos] = xv[k];
+            }
+            // each thread: its own max and its sum relative to it (no barrier); then the
+            // block rescales the per-thread sums to the chunk max in fp64
+            float mt = -INFINITY;
+#pragma unroll
+            for (int k = 0; k < kPerThread; ++k) mt = fmaxf(mt, xv[k]);
+            // branch-free: -inf logits (masked, or beyond V) weigh exp2f(-inf) = 0
+            const float mref = mt == -INFINITY ? 0.0f : mt;
+            double st = 0.0;
+#pragma unroll
+            for (int k = 0; k < kPerThread; ++k) st += (double)exp2f((xv[k] - mref) * a.kf);
+            const float m = block_max(mt, fscr);
+            const double sm = block_sum(st > 0.0 ? st * (double)exp2f((mt - m) * a.kf) : 0.0, dscr);
+            part.m = m;
+            part.arg = 0;
+            part.s = sm;
         }
-        block_argmax(v, idx, fscr, iscr);
-        part.m = v;
-        part.arg = idx;
-        part.s = 0.0;
-    } else {
-        // the thread holding the drafted token keeps its logit for the ratio test
-        if (x >= base && x < base + kChunk && x < a.V) {
-#pragma unroll
-            for (int k = 0; k < kPerThread; ++k)
-                if (chunk_index<VEC>(base, k) == x)
-                    w.xlog[(int64_t)b * 2 * g + (r <= g ? 0 : g) + pos] = xv[k];
-        }
-        // each thread: its own max and its sum relative to it (no barrier); then the block
-        // rescales the per-thread sums to the chunk max in fp64
-        float mt = -INFINITY;
-#pragma unroll
-        for (int k = 0; k < kPerThread; ++k) mt = fmaxf(mt, xv[k]);
-        // branch-free: -inf logits (masked, or beyond V) weigh exp2f(-inf) = 0
-        const float mref = mt == -INFINITY ? 0.0f : mt;
-        double st = 0.0;
-#pragma unroll
-        for (int k = 0; k < kPerThread; ++k) st += (double)exp2f((xv[k] - mref) * a.kf);
-        const float m = block_max(mt, fscr);
-        const double sm = block_sum(st > 0.0 ? st * (double)exp2f((mt - m) * a.kf) : 0.0, dscr);
-        part.m = m;
-        part.arg = 0;
-        part.s = sm;
+        if (threadIdx.x == 0) w.part[((int64_t)b * a.rows + r) * a.nchunk + c] = part;
     }
-    if (threadIdx.x == 0) w.part[((int64_t)b * a.rows + r) * a.nchunk + c] = part;
 }
 
 // ---------------------------------------------------------------------------
@@ -426,12 +435,29 @@ __global__ __launch_bounds__(kRowThreads) void accept_resample_kernel(AcceptArgs
     float xp[kPerThread], xq[kPerThread];
     load_chunk2<VEC, kPerThread>(prow, qrow ? qrow : prow, base, a.V, xp, xq);
     // branch-free: a position at or beyond V holds -inf, whose weight exp2f(-inf) = 0
+    // per thread, the residual mass of each float4 group (VEC layout: group k4 of wave w
+    // is part of the chunk's 256-token segment 4 k4 + w, in token order)
     double rs = 0.0, ps = 0.0;
+    double r4[kPerThread / 4];
 #pragma unroll
-    for (int k = 0; k < kPerThread; ++k) {
-        const double p = p_of(xp[k]);
-        ps += p;
-        rs += fmax(0.0, p - q_of(xq[k]));
+    for (int k4 = 0; k4 < kPerThread / 4; ++k4) {
+        r4[k4] = 0.0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const double p = p_of(xp[4 * k4 + j]);
+            ps += p;
+            r4[k4] += fmax(0.0, p - q_of(xq[4 * k4 + j]));
+        }
+        rs += r4[k4];
+    }
+    if (VEC) {
+        const int wv = threadIdx.x / kWave;
+        double *sg = w.seg + ((int64_t)b * a.nchunk + c) * kPerThread;
+#pragma unroll
+        for (int k4 = 0; k4 < kPerThread / 4; ++k4) {
+            const double t = wave_sum(r4[k4]);
+            if (threadIdx.x % kWave == 0) st_coherent(&sg[4 * k4 + wv], t);
+        }
     }
     block_sum2(rs, ps, dscr);
     if (threadIdx.x == 0) {
@@ -466,6 +492,58 @@ __global__ __launch_bounds__(kRowThreads) void accept_resample_kernel(AcceptArgs
     const int cs = s_chunk;
     const bool usep = s_usep != 0;
     const int cbase = cs * kChunk;
+    if (VEC && !(usep && qrow)) {
+        // The residual (or p, with no draft row) has its 256-token segment sums stored:
+        // wave 0 finds the segment holding u* Z, then the token inside it.
+        if (threadIdx.x < kWave) {
+            const int lane = threadIdx.x;
+            const double target = s_target;
+            const double *sg = w.seg + ((int64_t)b * a.nchunk + cs) * kPerThread;
+            const double v = lane < kPerThread ? sg[lane] : 0.0;
+            const double incl = wave_scan_incl(v, 0.0, OpAdd());
+            const double excl = s_base + incl - v;
+            const uint64_t pass = __ballot(v > 0.0 && s_base + incl > target);
+            const uint64_t posm = __ballot(v > 0.0);
+            // rounding can leave every running sum at or below target: the last segment with mass
+            const int sseg = pass ? __ffsll((unsigned long long)pass) - 1
+                                  : (posm ? 63 - __clzll((unsigned long long)posm) : 0);
+            const double sbase = lane_value(excl, sseg);
+            const int e0 = cbase + 256 * sseg + 4 * lane;  // this lane's four tokens
+            const int ec = min(e0, a.V - 4);
+            const float4 fp = *reinterpret_cast<const float4 *>(prow + ec);
+            const float4 fq = *reinterpret_cast<const float4 *>((qrow ? qrow : prow) + ec);
+            const bool in = e0 < a.V;
+            double wt[4];
+            wt[0] = in ? fmax(0.0, p_of(fp.x) - q_of(fq.x)) : 0.0;
+            wt[1] = in ? fmax(0.0, p_of(fp.y) - q_of(fq.y)) : 0.0;
+            wt[2] = in ? fmax(0.0, p_of(fp.z) - q_of(fq.z)) : 0.0;
+            wt[3] = in ? fmax(0.0, p_of(fp.w) - q_of(fq.w)) : 0.0;
+            const double lsum = ((wt[0] + wt[1]) + wt[2]) + wt[3];
+            const double c0 = sbase + wave_scan_incl(lsum, 0.0, OpAdd()) - lsum;
+            int hit = -1, lastpos = -1;
+            double pre = c0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                pre += wt[j];
+                if (hit < 0 && pre > target && wt[j] > 0.0) hit = j;
+                if (wt[j] > 0.0) lastpos = j;
+            }
+            const uint64_t hm = __ballot(c0 <= target && hit >= 0);
+            const uint64_t lm = __ballot(lastpos >= 0);
+            int y;
+            if (hm) {
+                const int hl = __ffsll((unsigned long long)hm) - 1;
+                y = cbase + 256 * sseg + 4 * hl + lane_value(hit, hl);
+            } else if (lm) {  // rounding: the segment's running sum stops short of target
+                const int ll = 63 - __clzll((unsigned long long)lm);
+                y = cbase + 256 * sseg + 4 * ll + lane_value(lastpos, ll);
+            } else {
+                y = cbase;  // no mass in the segment at all (cannot happen for the segment found)
+            }
+            if (lane == 0) a.out_tokens[(int64_t)b * (g + 1) + J] = y;
+        }
+        return;
+    }
     const bool twor = !usep && qrow;
     auto weight = [&](float lp, float lq) -> double {
         const double p = p_of(lp);
@@ -486,18 +564,18 @@ static hipError_t launch(K kernel, dim3 grid, hipStream_t s, const AcceptArgs &a
 template <bool VEC, int PER>
 static sv_status run_accept(const AcceptArgs &a, const AcceptWs &w, hipStream_t s, bool sample, bool alpha)
 {
-    const dim3 gstats(a.nchunk, a.rows, a.B);
     // staging slots: the part count rounded up to 1, 2, 4 or 8 per thread
     const int staged = a.rows * a.nchunk;
     int slots = kRowThreads;
     while (slots < staged) slots *= 2;
     const size_t lds = staged <= kMaxStaged ? (size_t)slots * sizeof(RowPart) : 0;
+    const int64_t ntask = (int64_t)a.nchunk * (a.rows + (sample ? 1 : 0)) * a.B;
+    const dim3 gstats((unsigned)(ntask < a.max_blocks ? ntask : a.max_blocks));
     if (!sample) {
         if (launch(accept_stats_kernel<VEC, false, PER>, gstats, s, a, w) != hipSuccess) return SV_ERR_HIP;
         return launch(accept_greedy_kernel, dim3(a.B), s, a, w, lds) == hipSuccess ? SV_OK : SV_ERR_HIP;
     }
-    if (launch(accept_stats_kernel<VEC, true, PER>, dim3(a.nchunk, a.rows + 1, a.B), s, a, w) != hipSuccess)
-        return SV_ERR_HIP;
+    if (launch(accept_stats_kernel<VEC, true, PER>, gstats, s, a, w) != hipSuccess) return SV_ERR_HIP;
     if (alpha && launch(accept_alpha_kernel<VEC, PER>, dim3(a.nchunk, a.gamma, a.B), s, a, w) != hipSuccess)
         return SV_ERR_HIP;
     return launch(accept_resample_kernel<VEC, PER>, dim3(a.nchunk, a.B), s, a, w, lds) == hipSuccess ? SV_OK
@@ -534,6 +612,7 @@ extern "C" sv_status sv_spec_accept(const sv_accept_desc *d, void *workspace, si
     w.xlog = (float *)(ws + L.xlog);
     w.u = (double *)(ws + L.u);
     w.res = (ResPart *)(ws + L.res);
+    w.seg = (double *)(ws + L.seg);
     w.apart = (double *)(ws + L.apart);
 
     AcceptArgs a;
@@ -562,6 +641,7 @@ extern "C" sv_status sv_spec_accept(const sv_accept_desc *d, void *workspace, si
     const int big_chunks = (d->V + 4 * kMinChunk - 1) / (4 * kMinChunk);
     const bool wide = (int64_t)a.B * a.rows * big_chunks >= 1024;
     a.nchunk = wide ? big_chunks : (d->V + kMinChunk - 1) / kMinChunk;
+    a.max_blocks = 4 * device_cu_count();
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
     return wide ? (vec ? run_accept<true, 64>(a, w, s, sample, d->alpha != nullptr)

@@ -477,103 +477,119 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
 
 // ---------------------------------------------------------------------------
 // Split combine.  Per row: M = max_s m_s, L = sum_s l_s 2^(m_s - M),
-// O = sum_s o_s 2^(m_s - M) / L.  A block covers CR rows; each row is served by NSL
-// split lanes x DH/4 float4 lanes: split lane sl reads splits sl, sl + NSL, ... (all of
-// its loads issued at once, clamped in-bounds and weighted 0 past the row's last split),
-// and the split lanes are summed through LDS in fixed order.
-// Grid: (row chunk, kv group x row tile).
+// O = sum_s o_s 2^(m_s - M) / L.  A row is served by NSL split lanes x DH/16 column lanes
+// (each column lane owns 4 float4 of the row); split lane sl reads splits sl, sl + NSL, ...,
+// SPT of them at most, all loads issued at once (clamped in-bounds, weighted 0 past the
+// row's last split).  The split lanes are summed through LDS in fixed order.
+// Tasks (row chunk, kv group x row tile); a grid smaller than the task count loops.
 // ---------------------------------------------------------------------------
 constexpr int kCombThreads = 256;
+constexpr int kCombVec = 4;  // float4 per thread and split
 
-template <int DH, int ROWS_BLK, int NSL>
-__global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a)
+template <int DH, int ROWS_BLK, int NSL, int SPT>
+__global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a, int nrc, int ntask)
 {
-    constexpr int C4 = DH / 4;                    // float4 per row
-    constexpr int RL = NSL * C4;                  // threads per row
+    constexpr int L4 = DH / 4 / kCombVec;         // column lanes per row
+    constexpr int RL = NSL * L4;                  // threads per row
     constexpr int CR = kCombThreads / RL;         // rows per block
-    constexpr int SPT = kMaxSplits / NSL;         // splits per lane at most
+    static_assert(CR >= 1 && kCombThreads % RL == 0, "combine layout");
     __shared__ float s_m[kCombThreads];
-    __shared__ float4 s_o[kCombThreads];
+    __shared__ float4 s_o[kCombVec][kCombThreads];
     __shared__ float s_l[kCombThreads];
-    const int gidx = blockIdx.y;
-    const int kg = gidx / a.RT, rt = gidx % a.RT;
-    const int b = kg / a.Hkv, kvh = kg % a.Hkv;
-    const int P = a.prefix_len[b];
-    const int T = P + a.n_q;
-    const bool overflow = (int64_t)T > (int64_t)a.nsplit * a.split_keys;
-    const int ns = overflow ? a.nsplit : (T + a.split_keys - 1) / a.split_keys;
     const int rl = threadIdx.x / RL;              // row within the block
-    const int sl = (threadIdx.x / C4) % NSL;      // split lane
-    const int d4 = threadIdx.x % C4;
-    const int r = blockIdx.x * CR + rl;           // row within the tile
-    const int row = rt * ROWS_BLK + r;
-    const bool ok = r < ROWS_BLK && row < a.rows;
-    const int rr = ok ? r : 0;                    // in-bounds row for the (unused) loads of idle rows
-    const float *pg = a.part + (int64_t)gidx * a.nsplit * ROWS_BLK * (DH + 4);
-    auto row_at = [&](int u) { return pg + ((int64_t)u * ROWS_BLK + rr) * (DH + 4); };  // o[DH], max, sum
-    const int nmine = ns > sl ? (ns - sl + NSL - 1) / NSL : 0;  // splits this lane owns
+    const int sl = (threadIdx.x / L4) % NSL;      // split lane
+    const int cl = threadIdx.x % L4;              // column lane: float4 columns cl + L4 * v
+    for (int t = blockIdx.x; t < ntask; t += gridDim.x) {
+        if (t != (int)blockIdx.x) __syncthreads();  // the previous task's LDS reads are done
+        const int gidx = t / nrc;
+        const int kg = gidx / a.RT, rt = gidx % a.RT;
+        const int b = kg / a.Hkv, kvh = kg % a.Hkv;
+        const int P = a.prefix_len[b];
+        const int T = P + a.n_q;
+        const bool overflow = (int64_t)T > (int64_t)a.nsplit * a.split_keys;
+        const int ns = overflow ? a.nsplit : (T + a.split_keys - 1) / a.split_keys;
+        const int r = (t % nrc) * CR + rl;        // row within the tile
+        const int row = rt * ROWS_BLK + r;
+        const bool ok = r < ROWS_BLK && row < a.rows;
+        const int rr = ok ? r : 0;                // in-bounds row for the (unused) loads of idle rows
+        const float *pg = a.part + (int64_t)gidx * a.nsplit * ROWS_BLK * (DH + 4);
+        auto row_at = [&](int u) { return pg + ((int64_t)u * ROWS_BLK + rr) * (DH + 4); };  // o[DH], max, sum
+        const int nmine = ns > sl ? (ns - sl + NSL - 1) / NSL : 0;  // splits this lane owns
 
-    float4 o[SPT];
-    float2 ml[SPT];
+        float4 o[SPT][kCombVec];
+        float2 ml[SPT];
 #pragma unroll
-    for (int k = 0; k < SPT; ++k) {
-        if (k * NSL < ns) {  // uniform over the block
-            const int u = min(sl + k * NSL, ns - 1);
-            o[k] = *reinterpret_cast<const float4 *>(row_at(u) + 4 * d4);
-            ml[k] = *reinterpret_cast<const float2 *>(row_at(u) + DH);
+        for (int k = 0; k < SPT; ++k) {
+            const float *rp = row_at(min(sl + k * NSL, ns - 1));
+#pragma unroll
+            for (int v = 0; v < kCombVec; ++v) o[k][v] = *reinterpret_cast<const float4 *>(rp + 4 * (cl + L4 * v));
+            ml[k] = *reinterpret_cast<const float2 *>(rp + DH);
         }
-    }
-    float mloc = -INFINITY;
+        float mloc = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < SPT; ++k)
-        if (k < nmine) mloc = fmaxf(mloc, ml[k].x);
-    s_m[threadIdx.x] = mloc;
-    __syncthreads();
-    float M = -INFINITY;
+        for (int k = 0; k < SPT; ++k)
+            if (k < nmine) mloc = fmaxf(mloc, ml[k].x);
+        s_m[threadIdx.x] = mloc;
+        __syncthreads();
+        float M = -INFINITY;
 #pragma unroll
-    for (int q = 0; q < NSL; ++q) M = fmaxf(M, s_m[rl * RL + q * C4 + d4]);
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    float lsum = 0.0f;
+        for (int q = 0; q < NSL; ++q) M = fmaxf(M, s_m[rl * RL + q * L4 + cl]);
+        float4 acc[kCombVec];
 #pragma unroll
-    for (int k = 0; k < SPT; ++k) {
-        if (k < nmine) {
-            const float w = ml[k].x == -INFINITY ? 0.0f : exp2f(ml[k].x - M);
-            acc.x += o[k].x * w;
-            acc.y += o[k].y * w;
-            acc.z += o[k].z * w;
-            acc.w += o[k].w * w;
+        for (int v = 0; v < kCombVec; ++v) acc[v] = make_float4(0.f, 0.f, 0.f, 0.f);
+        float lsum = 0.0f;
+#pragma unroll
+        for (int k = 0; k < SPT; ++k) {
+            const float w = (k < nmine && ml[k].x != -INFINITY) ? exp2f(ml[k].x - M) : 0.0f;
+#pragma unroll
+            for (int v = 0; v < kCombVec; ++v) {
+                acc[v].x += o[k][v].x * w;
+                acc[v].y += o[k][v].y * w;
+                acc[v].z += o[k][v].z * w;
+                acc[v].w += o[k][v].w * w;
+            }
             lsum += ml[k].y * w;
         }
-    }
-    if (NSL > 1) {
-        s_o[threadIdx.x] = acc;
-        s_l[threadIdx.x] = lsum;
-        __syncthreads();
-        if (sl != 0) return;
-        acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        lsum = 0.0f;
+        if (NSL > 1) {
 #pragma unroll
-        for (int q = 0; q < NSL; ++q) {  // fixed order: deterministic
-            const float4 t = s_o[rl * RL + q * C4 + d4];
-            acc.x += t.x;
-            acc.y += t.y;
-            acc.z += t.z;
-            acc.w += t.w;
-            lsum += s_l[rl * RL + q * C4 + d4];
+            for (int v = 0; v < kCombVec; ++v) s_o[v][threadIdx.x] = acc[v];
+            s_l[threadIdx.x] = lsum;
+            __syncthreads();
+            lsum = 0.0f;
+#pragma unroll
+            for (int v = 0; v < kCombVec; ++v) acc[v] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int q = 0; q < NSL; ++q) {  // fixed order: deterministic
+                const int src = rl * RL + q * L4 + cl;
+#pragma unroll
+                for (int v = 0; v < kCombVec; ++v) {
+                    const float4 tq = s_o[v][src];
+                    acc[v].x += tq.x;
+                    acc[v].y += tq.y;
+                    acc[v].z += tq.z;
+                    acc[v].w += tq.w;
+                }
+                lsum += s_l[src];
+            }
+        }
+        if (ok && sl == 0) {
+            const float L = lsum;
+            const float inv = overflow ? __int_as_float(0x7fc00000) : 1.0f / L;
+            const int i = row / a.G;
+            const int hq = kvh * a.G + row % a.G;
+            uint16_t *out = (uint16_t *)a.out + (int64_t)b * a.o_sb + (int64_t)i * a.o_st + (int64_t)hq * a.o_sh;
+#pragma unroll
+            for (int v = 0; v < kCombVec; ++v) {
+                uint2 pk;
+                pk.x = (uint32_t)f32_to_bf16(acc[v].x * inv) | ((uint32_t)f32_to_bf16(acc[v].y * inv) << 16);
+                pk.y = (uint32_t)f32_to_bf16(acc[v].z * inv) | ((uint32_t)f32_to_bf16(acc[v].w * inv) << 16);
+                *reinterpret_cast<uint2 *>(out + 4 * (cl + L4 * v)) = pk;
+            }
+            if (a.lse && cl == 0)
+                a.lse[((int64_t)b * a.n_q + i) * a.Hq + hq] =
+                    overflow ? __int_as_float(0x7fc00000) : (M + log2f(L)) * kLn2;
         }
     }
-    if (!ok) return;
-    const float L = lsum;
-    const float inv = overflow ? __int_as_float(0x7fc00000) : 1.0f / L;
-    const int i = row / a.G;
-    const int hq = kvh * a.G + row % a.G;
-    uint16_t *out = (uint16_t *)a.out + (int64_t)b * a.o_sb + (int64_t)i * a.o_st + (int64_t)hq * a.o_sh + 4 * d4;
-    uint2 pk;
-    pk.x = (uint32_t)f32_to_bf16(acc.x * inv) | ((uint32_t)f32_to_bf16(acc.y * inv) << 16);
-    pk.y = (uint32_t)f32_to_bf16(acc.z * inv) | ((uint32_t)f32_to_bf16(acc.w * inv) << 16);
-    *reinterpret_cast<uint2 *>(out) = pk;
-    if (a.lse && d4 == 0)
-        a.lse[((int64_t)b * a.n_q + i) * a.Hq + hq] = overflow ? __int_as_float(0x7fc00000) : (M + log2f(L)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -630,6 +646,7 @@ struct Plan {
     int NWR, NWK, rows, RT, KG, nsplit, split_keys, kg_pad;
     size_t part_bytes, cnt_bytes, total;
     unsigned blocks;
+    int max_blocks;  // resident-block budget of the looping combine (set at launch)
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -666,10 +683,11 @@ static bool plan_attention(const sv_attn_desc *d, Plan &p)
         // about 4096 splits in all, which balances uneven sequence lengths over the 256 CUs
         // (two 4-wave blocks per CU), keeping splits between 256 keys (shorter ones cost
         // more in partials and launch than they gain) and 4096.
-        sk = (Tmax * groups + 4095) / 4096;
-        sk = (sk + unit - 1) / unit * unit;
-        if (sk < 256) sk = 256;
-        if (sk > 4096) sk = 4096;
+        // Splits are a power of two long (measured: 1024-key splits stream a 64-sequence
+        // batch a third faster than 1056-key ones).
+        const int64_t want = (Tmax * groups + 4095) / 4096;
+        sk = 256;
+        while (sk * 2 <= want && sk < 4096) sk *= 2;
     } else {
         // Many rows per block: a partial costs as much as the keys it summarizes, so split
         // only when there are too few row tiles to occupy the chip.
@@ -744,17 +762,24 @@ static hipError_t launch_variant(const Plan &p, const AttnArgs &a, hipStream_t s
     if (e != hipSuccess || p.nsplit == 1) return e;
     constexpr int ROWS_BLK = 32 * NWR;
     const int tile_rows = p.rows < ROWS_BLK ? p.rows : ROWS_BLK;
-    // split lanes per row: enough for the splits, at most the block's width
+    // split lanes per row: one per split up to 8; beyond, each lane takes SPT splits
     const int nsl = p.nsplit <= 1 ? 1 : p.nsplit <= 2 ? 2 : p.nsplit <= 4 ? 4 : 8;
-    const dim3 blk(kCombThreads);
-    const int g = p.KG * p.RT;
-    auto rows_per = [](int nsl_) { return kCombThreads / (nsl_ * (DH / 4)); };
-    switch (nsl) {
-    case 1: hipLaunchKernelGGL((attn_combine_kernel<DH, ROWS_BLK, 1>), dim3((tile_rows + rows_per(1) - 1) / rows_per(1), g), blk, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((attn_combine_kernel<DH, ROWS_BLK, 2>), dim3((tile_rows + rows_per(2) - 1) / rows_per(2), g), blk, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((attn_combine_kernel<DH, ROWS_BLK, 4>), dim3((tile_rows + rows_per(4) - 1) / rows_per(4), g), blk, 0, s, a); break;
-    default: hipLaunchKernelGGL((attn_combine_kernel<DH, ROWS_BLK, 8>), dim3((tile_rows + rows_per(8) - 1) / rows_per(8), g), blk, 0, s, a); break;
-    }
+    const int need = (p.nsplit + nsl - 1) / nsl;
+    const int spt = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
+    const int cr = kCombThreads / (nsl * (DH / 4 / kCombVec));  // rows per block
+    const int nrc = (tile_rows + cr - 1) / cr;                  // row chunks per tile
+    const int ntask = nrc * p.KG * p.RT;
+    const int grid = ntask < p.max_blocks ? ntask : p.max_blocks;
+    const dim3 g(grid), blk(kCombThreads);
+#define SV_COMBINE(NSL_, SPT_) hipLaunchKernelGGL((attn_combine_kernel<DH, ROWS_BLK, NSL_, SPT_>), g, blk, 0, s, a, nrc, ntask)
+    if (nsl == 1) SV_COMBINE(1, 1);
+    else if (nsl == 2) SV_COMBINE(2, 1);
+    else if (nsl == 4) SV_COMBINE(4, 1);
+    else if (spt == 1) SV_COMBINE(8, 1);
+    else if (spt == 2) SV_COMBINE(8, 2);
+    else if (spt == 4) SV_COMBINE(8, 4);
+    else SV_COMBINE(8, 8);
+#undef SV_COMBINE
     return hipGetLastError();
 }
 
@@ -831,6 +856,7 @@ extern "C" sv_status sv_verify_attention(const sv_attn_desc *d, void *workspace,
         hipLaunchKernelGGL(attn_f32_kernel, dim3((unsigned)nrows), dim3(64), 0, s, a, d->D);
         e = hipGetLastError();
     } else {
+        p.max_blocks = 16 * device_cu_count();
         e = d->D == 128 ? launch_bf16<128>(p, a, s) : launch_bf16<64>(p, a, s);
     }
     return e == hipSuccess ? SV_OK : SV_ERR_HIP;

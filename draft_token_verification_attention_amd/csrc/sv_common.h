@@ -19,6 +19,21 @@ constexpr int kMaxCounters = (int)(kCounterBytes / sizeof(int));
 constexpr uint64_t kTagAccept = 0x53560001ULL;
 constexpr uint64_t kTagWalk = 0x53560002ULL;
 
+// Compute units of the current device (host side; cached per device).  Looping kernels
+// size their grids from it.
+static inline int device_cu_count()
+{
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 // ---------------------------------------------------------------------------
 // Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy
 // as 1, 2, 3", SC'11).  Each round multiplies counter words 0 and 2 by two fixed

@@ -45,6 +45,19 @@ __device__ __forceinline__ void load_chunk(const float *__restrict__ row, int ch
         }
         return;
     }
+    if (VEC) {  // V % 4 == 0: a float4 is wholly inside or wholly beyond the row
+#pragma unroll
+        for (int k4 = 0; k4 < PER / 4; ++k4) {
+            const int e = chunk_base + 4 * (int)threadIdx.x + 1024 * k4;
+            const float4 f = *reinterpret_cast<const float4 *>(row + min(e, V - 4));
+            const bool in = e < V;
+            x[4 * k4 + 0] = in ? f.x : -INFINITY;
+            x[4 * k4 + 1] = in ? f.y : -INFINITY;
+            x[4 * k4 + 2] = in ? f.z : -INFINITY;
+            x[4 * k4 + 3] = in ? f.w : -INFINITY;
+        }
+        return;
+    }
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
         const int e = chunk_index<VEC>(chunk_base, k);
@@ -77,6 +90,28 @@ __device__ __forceinline__ void load_chunk2(const float *__restrict__ r0, const 
             x1[4 * k4 + 1] = f1[k4].y;
             x1[4 * k4 + 2] = f1[k4].z;
             x1[4 * k4 + 3] = f1[k4].w;
+        }
+        return;
+    }
+    if (VEC) {  // V % 4 == 0: a float4 is wholly inside or wholly beyond the row
+        float4 f0[PER / 4], f1[PER / 4];
+#pragma unroll
+        for (int k4 = 0; k4 < PER / 4; ++k4) {
+            const int e = min(chunk_base + 4 * (int)threadIdx.x + 1024 * k4, V - 4);
+            f0[k4] = *reinterpret_cast<const float4 *>(r0 + e);
+            f1[k4] = *reinterpret_cast<const float4 *>(r1 + e);
+        }
+#pragma unroll
+        for (int k4 = 0; k4 < PER / 4; ++k4) {
+            const bool in = chunk_base + 4 * (int)threadIdx.x + 1024 * k4 < V;
+            x0[4 * k4 + 0] = in ? f0[k4].x : -INFINITY;
+            x0[4 * k4 + 1] = in ? f0[k4].y : -INFINITY;
+            x0[4 * k4 + 2] = in ? f0[k4].z : -INFINITY;
+            x0[4 * k4 + 3] = in ? f0[k4].w : -INFINITY;
+            x1[4 * k4 + 0] = in ? f1[k4].x : -INFINITY;
+            x1[4 * k4 + 1] = in ? f1[k4].y : -INFINITY;
+            x1[4 * k4 + 2] = in ? f1[k4].z : -INFINITY;
+            x1[4 * k4 + 3] = in ? f1[k4].w : -INFINITY;
         }
         return;
     }
