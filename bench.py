@@ -79,8 +79,7 @@ def main():
     cfg = synth.WORKLOADS[args.workload]
     wl = args.workload
     if cfg["kind"] != "chain":
-        print("tree workloads are measured by bench_tree (not yet wired)", file=sys.stderr)
-        sys.exit(2)
+        return bench_tree(args, cfg, wl, dev)
 
     # ---------------- inputs (host, seeded) ----------------
     B, gamma = cfg["B"], cfg["gamma"]
@@ -148,30 +147,7 @@ def main():
         launch(i % R, sh)
     torch.cuda.synchronize()
 
-    # One HIP graph per input copy: a step is one graph replay (the attention kernels and the
-    # acceptance kernels, captured on torch's capture stream; no memset nodes).
-    graphs = []
-    if not args.eager:
-        for r in range(R):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                launch(r, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
-            graphs.append(g)
-        for i in range(args.warmup):
-            graphs[i % R].replay()
-        torch.cuda.synchronize()
-
-    # timed region: exactly K steps
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        if graphs:
-            graphs[(args.warmup + i) % R].replay()
-        else:
-            launch((args.warmup + i) % R, sh)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    ms_per_step = timed_steps(launch, R, args, sh)
 
     # Kernel durations: HIP events on the launch stream, same K steps.  The library's
     # measurement hook records one more event right after the main attention kernel, so the
@@ -235,6 +211,214 @@ def main():
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(att, acc, cfg, scale, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def timed_steps(launch, R, args, sh):
+    """Warm up, then time exactly args.steps steps (wall clock between two device
+    synchronizations); step i reads input copy i mod R.  Unless --eager, the steps are
+    replayed from HIP graphs that each hold S consecutive steps (S the largest divisor of
+    the step count up to 10), so the host's per-replay cost is spread over S steps; the
+    kernels and their arguments are exactly those of the eager launches."""
+    import ctypes
+    import torch
+    K = args.steps
+    if args.eager:
+        for i in range(args.warmup):
+            launch(i % R, sh)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            launch((args.warmup + i) % R, sh)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / K
+    S = max(d for d in range(1, min(10, K) + 1) if K % d == 0)
+    graphs = []
+    for r in range(R):  # graph r: the S steps starting at copy r
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cs = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            for k in range(S):
+                launch((r + k) % R, cs)
+        graphs.append(g)
+    for m in range(max(1, args.warmup // S)):
+        graphs[(m * S) % R].replay()
+    torch.cuda.synchronize()
+    first = args.warmup
+    t0 = time.perf_counter()
+    for m in range(K // S):
+        graphs[(first + m * S) % R].replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / K
+
+
+def bench_tree(args, cfg, wl, dev):
+    """A tree round: the mask build from the parent array, the tree attention over the
+    cache + node tokens, and the tree walk (sampling, the workload's temperature) over
+    the per-node target logits.  Draft tokens verified per step = drafted nodes."""
+    import ctypes
+    import torch
+    import draft_token_verification_attention_amd as sv
+    import synth
+
+    parents, paths = synth.build_tree(cfg)
+    n = len(parents)
+    Hq, Hkv, D, V, tau, P = cfg["Hq"], cfg["Hkv"], cfg["D"], cfg["V"], cfg["tau"], cfg["P"]
+    att = synth.attention_inputs(wl, B=1, n_q=n, Hq=Hq, Hkv=Hkv, D=D, prefix_len=[P], dtype="bf16",
+                                 qkv_scale=cfg["qkv_scale"])
+    lg = synth.tree_logits(wl, 1, n, V, cfg["target_var"])
+    toks = synth.node_tokens(wl, lg, parents, synth.path_ranks(paths))
+    depth = np.zeros(n, dtype=np.int64)
+    for i in range(1, n):
+        depth[i] = depth[parents[i]] + 1
+    max_depth = int(depth.max())
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    base = dict(q=bf(att["q"]), k=bf(att["k"]), v=bf(att["v"]), logits=torch.from_numpy(lg).to(dev))
+    del lg
+    set_bytes = sum(t.numel() * t.element_size() for t in base.values())
+    R = max(1, int(math.ceil(args.rotate_bytes / set_bytes)))
+    copies = [base] + [{k: t.clone() for k, t in base.items()} for _ in range(R - 1)]
+    par_d = torch.from_numpy(parents.astype(np.int32)).to(dev)
+    toks_d = torch.from_numpy(toks.astype(np.int32)).to(dev)
+    kv_off = torch.from_numpy(att["kv_off"].astype(np.int64)).to(dev)
+    prefix = torch.tensor([P], dtype=torch.int32, device=dev)
+    words = (n + 31) // 32
+    bits = torch.empty((n, words), dtype=torch.int32, device=dev)
+    dep_d = torch.empty(n, dtype=torch.int32, device=dev)
+    pos_d = torch.empty(n, dtype=torch.int64, device=dev)
+    mstat = torch.empty(1, dtype=torch.int32, device=dev)
+    out = torch.empty((1, n, Hq, D), dtype=torch.bfloat16, device=dev)
+    acc_len = torch.empty(1, dtype=torch.int32, device=dev)
+    path = torch.empty((1, max_depth + 1), dtype=torch.int32, device=dev)
+    out_tok = torch.empty((1, max_depth + 1), dtype=torch.int32, device=dev)
+    wstat = torch.empty(1, dtype=torch.int32, device=dev)
+    scale = 1.0 / math.sqrt(D)
+    adescs = [sv.attn_desc(c["q"], c["k"], c["v"], kv_off, prefix, Hkv=Hkv, max_prefix=P, scale=scale,
+                           kv_sh=att["kv_sh"], kv_st=att["kv_st"], out=out, tree_bits=bits, tree_sb=0,
+                           split_keys=args.split_keys) for c in copies]
+    wdescs = [sv.walk_desc(sv.SV_SAMPLE, c["logits"], toks_d, par_d, max_depth, tau, 1000 + wl, 0, None,
+                           acc_len, path, out_tok, wstat) for c in copies]
+    ws_a = sv.lib.sv_verify_attention_workspace(ctypes.byref(adescs[0]))
+    ws_w = sv.lib.sv_tree_walk_workspace(ctypes.byref(wdescs[0]))
+    ws_att = torch.zeros(ws_a + 256, dtype=torch.uint8, device=dev)
+    ws_wlk = torch.zeros(ws_w + 256, dtype=torch.uint8, device=dev)
+    pa = ctypes.c_void_p(ws_att.data_ptr() + (-ws_att.data_ptr()) % 256)
+    pw = ctypes.c_void_p(ws_wlk.data_ptr() + (-ws_wlk.data_ptr()) % 256)
+    sh = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+    def launch(r, sh, ev=None):
+        if ev is not None:
+            ev[0].record()
+        st0 = sv.lib.sv_build_tree_mask(ctypes.c_void_p(par_d.data_ptr()), n, P, ctypes.c_void_p(bits.data_ptr()),
+                                        ctypes.c_void_p(dep_d.data_ptr()), ctypes.c_void_p(pos_d.data_ptr()),
+                                        ctypes.c_void_p(mstat.data_ptr()), sh)
+        if ev is not None:
+            ev[1].record()
+        st1 = sv.lib.sv_verify_attention(ctypes.byref(adescs[r]), pa, ws_a, sh)
+        if ev is not None:
+            ev[3].record()
+        st2 = sv.lib.sv_tree_walk(ctypes.byref(wdescs[r]), pw, ws_w, sh)
+        if ev is not None:
+            ev[4].record()
+        if st0 or st1 or st2:
+            raise RuntimeError("launch failed: %d %d %d" % (st0, st1, st2))
+
+    for i in range(args.warmup):
+        launch(i % R, sh)
+    torch.cuda.synchronize()
+    ms_per_step = timed_steps(launch, R, args, sh)
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for e in events:
+        e[2].record()
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        sv.lib.sv_set_attention_mark(ctypes.c_void_p(events[i][2].cuda_event))
+        launch((args.warmup + i) % R, sh, events[i])
+    sv.lib.sv_set_attention_mark(None)
+    torch.cuda.synchronize()
+    mask_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    main_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    comb_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
+    walk_ms = float(np.mean([e[3].elapsed_time(e[4]) for e in events]))
+
+    drafted = n - 1
+    value = drafted / (ms_per_step * 1e-3)
+    anc = int((depth + 1).sum())  # sum over nodes of the ancestor-or-self count
+    att_flops = 4.0 * D * Hq * (n * P + anc)
+    att_bytes = 2 * (n * Hq * D + 2 * (P + n) * Hkv * D) + 2 * n * Hq * D + 4 * n * words
+    main_tflops = att_flops / (main_ms * 1e-3) / 1e12
+    main_gbs = att_bytes / (main_ms * 1e-3) / 1e9
+    walk_rows = int(to_host_int(acc_len)) + 1
+    mfma = {"bound": "mfma", "achieved": round(main_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(main_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": measured_traffic(wl),
+            "kernel": "attn_bf16_kernel", "kernel_ms": round(main_ms, 5), "algorithmic_flops": att_flops}
+    hbm = {"bound": "hbm", "achieved": round(main_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": round(main_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl),
+           "kernel": "attn_bf16_kernel", "kernel_ms": round(main_ms, 5), "algorithmic_bytes": att_bytes}
+    line = {
+        "metric": "draft tokens verified/sec on 1 MI355X; achieved HBM GB/s as % of peak",
+        "value": round(value, 1), "unit": "draft tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg["name"], "batch": 1, "tree_nodes": drafted, "cached_context": P,
+                   "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "vocab": V, "temperature": tau,
+                   "mode": "sample", "rotated_input_copies": R, "launch": "eager" if args.eager else "hip_graph"},
+        "roofline": mfma if wl == 5 else hbm,
+        "roofline_other": hbm if wl == 5 else mfma,
+        "kernels_ms": {"tree_mask_kernel": round(mask_ms, 5), "attn_bf16_kernel": round(main_ms, 5),
+                       "attn_combine_kernel": round(comb_ms, 5), "sv_tree_walk": round(walk_ms, 5)},
+        "walk": {"kernel_ms": round(walk_ms, 5), "rows_visited": walk_rows,
+                 "algorithmic_bytes": 4 * V * walk_rows},
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline_tree(att, cfg, wl, parents, toks, scale, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+def to_host_int(t):
+    return int(t.cpu().numpy().ravel()[0])
+
+
+def cpu_baseline_tree(att, cfg, wl, parents, toks, scale, seconds):
+    """The oracle on a bounded sample: the mask, the fp64 attention of a seeded sample of
+    rows (timed, then scaled to every row) and the tree walk, repeated for ~`seconds`."""
+    import oracle
+    import synth
+    threads = os.cpu_count() or 1
+    oracle.set_threads(threads)
+    n, Hq = len(parents), cfg["Hq"]
+    total_rows = n * Hq
+    r = np.random.default_rng(wl)
+    nsample = min(total_rows, 4096)
+    pick = r.choice(total_rows, size=nsample, replace=False)
+    rows = np.stack([np.zeros(nsample, np.int64), pick // Hq, pick % Hq], 1).astype(np.int32)
+    lg = synth.tree_logits(wl, 1, n, cfg["V"], cfg["target_var"]) if n <= 128 else None
+    t_mask = t_att = t_walk = 0.0
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        ta = time.perf_counter()
+        bits = oracle.tree_mask(parents, cfg["P"])[0]
+        tb = time.perf_counter()
+        oracle.attention(att, scale=scale, tree_bits=bits, tree_sb=0, rows=rows)
+        tc = time.perf_counter()
+        if lg is not None:
+            oracle.tree_walk(oracle.SAMPLE, lg, toks, parents, cfg["tau"], seed=1000 + wl, step=reps)
+        td = time.perf_counter()
+        t_mask += tb - ta
+        t_att += tc - tb
+        t_walk += td - tc
+        reps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    step_s = (t_mask + t_att * total_rows / nsample + t_walk) / reps
+    return {"value": round((n - 1) / step_s, 3), "unit": "draft tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d reps of: mask, fp64 attention of %d of %d rows (time scaled to all rows)%s"
+                      % (reps, nsample, total_rows, ", tree walk" if lg is not None else
+                         "; walk not sampled (its 2.4 GB logits stay off the host leg)")}
 
 
 # HBM bytes per launch of attn_bf16_kernel (2 x FETCH_SIZE + WRITE_SIZE, the FETCH_SIZE

@@ -33,14 +33,19 @@ def sources():
 
 def build(verbose: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    objs = []
+    from concurrent.futures import ThreadPoolExecutor
+    jobs = []
     for src in sources():
         obj = os.path.join(CSRC, os.path.basename(src) + ".o")
-        cmd = [hipcc, *HIPCC_FLAGS, "-c", src, "-o", obj]
-        if verbose:
+        jobs.append(([hipcc, *HIPCC_FLAGS, "-c", src, "-o", obj], obj))
+    if verbose:
+        for cmd, _ in jobs:
             print(" ".join(cmd), flush=True)
-        subprocess.check_call(cmd)
-        objs.append(obj)
+    workers = max(1, min(len(jobs), os.cpu_count() or 1, 8))
+    with ThreadPoolExecutor(workers) as ex:  # one hipcc per source file
+        for f in [ex.submit(subprocess.check_call, cmd) for cmd, _ in jobs]:
+            f.result()
+    objs = [obj for _, obj in jobs]
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [hipcc, "-shared", "--offload-arch=" + ARCH, "-fPIC", "-o", tmp, *objs]
     if verbose:

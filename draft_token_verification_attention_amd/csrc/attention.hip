@@ -477,16 +477,16 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
 
 // ---------------------------------------------------------------------------
 // Split combine.  Per row: M = max_s m_s, L = sum_s l_s 2^(m_s - M),
-// O = sum_s o_s 2^(m_s - M) / L.  A row is served by NSL split lanes x DH/16 column lanes
-// (each column lane owns 4 float4 of the row); split lane sl reads splits sl, sl + NSL, ...,
+// O = sum_s o_s 2^(m_s - M) / L.  A row is served by NSL split lanes x column lanes, each
+// column lane owning kCombVec float4 of the row (1 for small grids, latency first; 4 for
+// large ones, fewer blocks); split lane sl reads splits sl, sl + NSL, ...,
 // SPT of them at most, all loads issued at once (clamped in-bounds, weighted 0 past the
 // row's last split).  The split lanes are summed through LDS in fixed order.
 // Tasks (row chunk, kv group x row tile); a grid smaller than the task count loops.
 // ---------------------------------------------------------------------------
 constexpr int kCombThreads = 256;
-constexpr int kCombVec = 4;  // float4 per thread and split
 
-template <int DH, int ROWS_BLK, int NSL, int SPT>
+template <int DH, int ROWS_BLK, int NSL, int SPT, int kCombVec>
 __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a, int nrc, int ntask)
 {
     constexpr int L4 = DH / 4 / kCombVec;         // column lanes per row
@@ -766,12 +766,18 @@ static hipError_t launch_variant(const Plan &p, const AttnArgs &a, hipStream_t s
     const int nsl = p.nsplit <= 1 ? 1 : p.nsplit <= 2 ? 2 : p.nsplit <= 4 ? 4 : 8;
     const int need = (p.nsplit + nsl - 1) / nsl;
     const int spt = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
-    const int cr = kCombThreads / (nsl * (DH / 4 / kCombVec));  // rows per block
+    // one float4 per thread while the grid stays small, else four
+    const int nrc1 = (tile_rows + kCombThreads / (nsl * (DH / 4)) - 1) / (kCombThreads / (nsl * (DH / 4)));
+    const int vpt = (int64_t)nrc1 * p.KG * p.RT > 4 * (p.max_blocks / 16) ? 4 : 1;
+    const int cr = kCombThreads / (nsl * (DH / 4 / vpt));      // rows per block
     const int nrc = (tile_rows + cr - 1) / cr;                  // row chunks per tile
     const int ntask = nrc * p.KG * p.RT;
     const int grid = ntask < p.max_blocks ? ntask : p.max_blocks;
     const dim3 g(grid), blk(kCombThreads);
-#define SV_COMBINE(NSL_, SPT_) hipLaunchKernelGGL((attn_combine_kernel<DH, ROWS_BLK, NSL_, SPT_>), g, blk, 0, s, a, nrc, ntask)
+#define SV_COMBINE2(NSL_, SPT_, V_) \
+    hipLaunchKernelGGL((attn_combine_kernel<DH, ROWS_BLK, NSL_, SPT_, V_>), g, blk, 0, s, a, nrc, ntask)
+#define SV_COMBINE(NSL_, SPT_) \
+    do { if (vpt == 1) SV_COMBINE2(NSL_, SPT_, 1); else SV_COMBINE2(NSL_, SPT_, 4); } while (0)
     if (nsl == 1) SV_COMBINE(1, 1);
     else if (nsl == 2) SV_COMBINE(2, 1);
     else if (nsl == 4) SV_COMBINE(4, 1);
@@ -780,6 +786,7 @@ static hipError_t launch_variant(const Plan &p, const AttnArgs &a, hipStream_t s
     else if (spt == 4) SV_COMBINE(8, 4);
     else SV_COMBINE(8, 8);
 #undef SV_COMBINE
+#undef SV_COMBINE2
     return hipGetLastError();
 }
 
