@@ -66,6 +66,17 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u)
 // (vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their no-wait maxima).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, source lane r supplies the address of
+// four consecutive 16-bit values M[r][0..3]; destination lane r receives
+// (M[r / 4][r % 4], M[4 + r / 4][r % 4], M[8 + r / 4][r % 4], M[12 + r / 4][r % 4]).
+__device__ __forceinline__ v4s lds_read_tr16(const char *p)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(p));
+}
+
 // Combine lane l with lane l ^ 32 (v_permlane32_swap: with both operands x, the two
 // results hold x[l % 32] and x[l % 32 + 32] in every lane l).
 __device__ __forceinline__ float half_swap_max(float x)
@@ -362,23 +373,20 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
 #pragma unroll
             for (int j = 0; j < 8; ++j) pb[c][j] = (__bf16)p[8 * c + j];
 
-        // O^T (d x rows) += V^T (d x keys) . P^T (keys x rows)
-        const uint16_t *vt = reinterpret_cast<const uint16_t *>(gV);
+        // O^T (d x rows) += V^T (d x keys) . P^T (keys x rows).  Lane (d, h) needs V at
+        // column d for keys 16c + 4h + 0..3 and 16c + 8 + 4h + 0..3: two LDS transpose reads
+        // (within each 16-lane group, source lane r addresses key row r / 4 of the group's
+        // four and the four columns starting at 4 (r % 4); destination lane r gets column
+        // r of those four rows).
+        const int g16 = lane >> 4, r16 = lane & 15;
+        const char *vsrc = gV + (4 * (g16 >> 1) + (r16 >> 2)) * KROW + 2 * (16 * (g16 & 1) + 4 * (r16 & 3));
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
-                uint32_t wv[4];
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int j0 = 2 * jj, j1 = 2 * jj + 1;
-                    const int key0 = 16 * c + 8 * (j0 >> 2) + 4 * h + (j0 & 3);
-                    const int key1 = 16 * c + 8 * (j1 >> 2) + 4 * h + (j1 & 3);
-                    const uint32_t lo = vt[(key0 * KROW) / 2 + 32 * db + l32];
-                    const uint32_t hi = vt[(key1 * KROW) / 2 + 32 * db + l32];
-                    wv[jj] = lo | (hi << 16);
-                }
-                const bf16x8 vf = as_bf16x8(make_uint4(wv[0], wv[1], wv[2], wv[3]));
+                const char *p0 = vsrc + 16 * c * KROW + 64 * db;
+                const v4s lo = lds_read_tr16(p0), hi = lds_read_tr16(p0 + 8 * KROW);
+                const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[c], oacc[db], 0, 0, 0);
             }
         }
