@@ -8,10 +8,10 @@
 //   "Speculative Decoding: The Art of Guessing Well", section "Speculative sampling".
 //
 // Kernels (one launch each, all decisions on the device):
-//   stats    grid (chunk, row, sequence).  Each block reads one chunk of one row once:
-//            GREEDY keeps (max, first argmax); SAMPLE keeps (chunk max m_c, S_c =
-//            sum exp((l - m_c)/T) in fp64) and the logit of the drafted token when the
-//            chunk holds it.  No cross-block hand-off: the kernel boundary publishes.
+//   stats    tasks (chunk, row, sequence), looping grid.  A task reads one chunk of one
+//            row once; each wave keeps, for its quarter of the chunk, GREEDY (max, first
+//            argmax) or SAMPLE (max m, S = sum exp((l - m)/T) in fp64).  No barrier per
+//            task, no cross-block hand-off: the kernel boundary publishes.
 //   greedy   GREEDY, one block per sequence: argmax per row from the chunk partials,
 //            the matching prefix J and the extra token z_J.
 //   alpha    optional: sum_x min(p_i, q_i) per draft position (one more read of the rows).
@@ -32,6 +32,12 @@ using namespace sv;
 // before any reduction: the larger chunk when the call has blocks to spare (big batches),
 // the smaller one when latency matters (a single sequence).
 constexpr int kMinChunk = 16 * kRowThreads;
+// Row partials per chunk: with the large chunks (big calls) every wave keeps its own (no
+// block barrier per task, for bandwidth); with the small ones (latency) the block reduces to
+// one, which keeps the decide step's staging small.
+template <int PER>
+constexpr int parts_per_chunk() { return PER >= 64 ? kRowThreads / kWave : 1; }
+constexpr int kMaxPartsPerChunk = kRowThreads / kWave;
 
 struct RowPart {
     float m;
@@ -45,8 +51,7 @@ struct ResPart {
 
 struct AcceptWs {
     int *cnt;        // [B]: one completion counter per sequence, shared by the call's kernels in turn
-    RowPart *part;   // [B][rows][nchunk]
-    float *xlog;     // [B][2 gamma]: target then draft logit of each drafted token
+    RowPart *part;   // [B][rows][npart]: one partial per (chunk, wave)
     double *u;       // [B][gamma + 1]: the round's uniforms (ratio tests, then the extra token)
     ResPart *res;    // [B][nchunk]
     double *seg;     // [B][nchunk][PER]: residual mass of each 256-token segment of a chunk
@@ -55,7 +60,7 @@ struct AcceptWs {
 
 struct AcceptArgs {
     int B, gamma, V, rows, nchunk;
-    int max_blocks;    // resident-block budget of a looping kernel
+    int npart;         // row partials: nchunk x waves per block
     int sample;
     float kf;          // log2(e) / T in fp32, for the bulk exponentials
     double inv_t;      // 1 / T in fp64, for decided probabilities
@@ -71,7 +76,7 @@ struct AcceptArgs {
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-    size_t cnt, part, xlog, u, res, seg, apart, total;
+    size_t cnt, part, u, res, seg, apart, total;
 };
 
 static WsLayout accept_layout(int B, int gamma, int V)
@@ -83,9 +88,7 @@ static WsLayout accept_layout(int B, int gamma, int V)
     L.cnt = o;
     o += kCounterBytes;
     L.part = o;
-    o += align256((size_t)B * rows * nchunk * sizeof(RowPart));
-    L.xlog = o;
-    o += align256((size_t)B * 2 * gamma * sizeof(float));
+    o += align256((size_t)B * rows * nchunk * kMaxPartsPerChunk * sizeof(RowPart));
     L.u = o;
     o += align256((size_t)B * (gamma + 1) * sizeof(double));
     L.res = o;
@@ -212,30 +215,25 @@ __global__ __launch_bounds__(kRowThreads) void accept_stats_kernel(AcceptArgs a,
         }
         const float *row = row_ptr(a, b, r);
         const int base = c * kChunk;
-        // the drafted token of this row's position (none for the bonus row gamma)
-        const int pos = r <= g ? r : r - g - 1;
-        const int x = (SAMPLE && pos < g) ? a.tokens[(int64_t)b * g + pos] : -1;
         float xv[kPerThread];
         load_chunk<VEC, kPerThread>(row, base, a.V, xv);
 
+        constexpr int kParts = parts_per_chunk<PER>();
         RowPart part;
         if (!SAMPLE) {
             float v = -INFINITY;
             int idx = 0x7fffffff;
 #pragma unroll
             for (int k = 0; k < kPerThread; ++k) argmax_merge(v, idx, xv[k], chunk_index<VEC>(base, k));
-            block_argmax(v, idx, fscr, iscr);  // positions beyond V hold -inf and never win
+            // positions beyond V hold -inf and never win
+            if (kParts > 1)
+                wave_argmax(v, idx);
+            else
+                block_argmax(v, idx, fscr, iscr);
             part.m = v;
             part.arg = idx;
             part.s = 0.0;
         } else {
-            // the thread holding the drafted token keeps its logit for the ratio test
-            if (x >= base && x < base + kChunk && x < a.V) {
-#pragma unroll
-                for (int k = 0; k < kPerThread; ++k)
-                    if (chunk_index<VEC>(base, k) == x)
-                        w.xlog[(int64_t)b * 2 * g + (r <= g ? 0 : g) + pos] = xv[k];
-            }
             // each thread: its own max and its sum relative to it (no barrier); then the
             // block rescales the per-thread sums to the chunk max in fp64
             float mt = -INFINITY;
@@ -246,13 +244,15 @@ __global__ __launch_bounds__(kRowThreads) void accept_stats_kernel(AcceptArgs a,
             double st = 0.0;
 #pragma unroll
             for (int k = 0; k < kPerThread; ++k) st += (double)exp2f((xv[k] - mref) * a.kf);
-            const float m = block_max(mt, fscr);
-            const double sm = block_sum(st > 0.0 ? st * (double)exp2f((mt - m) * a.kf) : 0.0, dscr);
+            const float m = kParts > 1 ? wave_max(mt) : block_max(mt, fscr);
+            const double z = st > 0.0 ? st * (double)exp2f((mt - m) * a.kf) : 0.0;
+            const double sm = kParts > 1 ? wave_sum(z) : block_sum(z, dscr);
             part.m = m;
             part.arg = 0;
             part.s = sm;
         }
-        if (threadIdx.x == 0) w.part[((int64_t)b * a.rows + r) * a.nchunk + c] = part;
+        if ((kParts > 1 && threadIdx.x % kWave == 0) || threadIdx.x == 0)
+            w.part[((int64_t)b * a.rows + r) * a.npart + c * kParts + threadIdx.x / kWave] = part;
     }
 }
 
@@ -272,18 +272,18 @@ __global__ __launch_bounds__(kRowThreads) void accept_greedy_kernel(AcceptArgs a
         firstbad = g;
         bad = 0;
     }
-    const RowPart *pp = w.part + (int64_t)b * a.rows * a.nchunk;
+    const RowPart *pp = w.part + (int64_t)b * a.rows * a.npart;
     RowPart *stage = reinterpret_cast<RowPart *>(dyn_lds);
-    const bool staged = a.rows * a.nchunk <= kMaxStaged;
-    if (staged) stage_parts(pp, a.rows * a.nchunk, stage, [] {});
+    const bool staged = a.rows * a.npart <= kMaxStaged;
+    if (staged) stage_parts(pp, a.rows * a.npart, stage, [] {});
     const int wave = threadIdx.x / kWave;
     for (int r = wave; r <= g; r += kRowThreads / kWave) {
         float v;
         int idx;
         if (staged)
-            wave_combine_argmax(stage + (int64_t)r * a.nchunk, a.nchunk, v, idx);
+            wave_combine_argmax(stage + (int64_t)r * a.npart, a.npart, v, idx);
         else
-            wave_combine_argmax(pp + (int64_t)r * a.nchunk, a.nchunk, v, idx);
+            wave_combine_argmax(pp + (int64_t)r * a.npart, a.npart, v, idx);
         if (threadIdx.x % kWave == 0) z[r] = idx;
     }
     __syncthreads();
@@ -322,8 +322,8 @@ __global__ __launch_bounds__(kRowThreads) void accept_alpha_kernel(AcceptArgs a,
     if (wave < 2) {
         float M;
         double Z;
-        group_combine_softmax<kWave>(w.part + ((int64_t)b * a.rows + (wave == 0 ? i : g + 1 + i)) * a.nchunk, 0, 1,
-                                     a.nchunk, a.kf, M, Z);
+        group_combine_softmax<kWave>(w.part + ((int64_t)b * a.rows + (wave == 0 ? i : g + 1 + i)) * a.npart, 0, 1,
+                                     a.npart, a.kf, M, Z);
         if (threadIdx.x % kWave == 0) {
             sM[wave] = (double)M;
             sZ[wave] = Z;
@@ -370,32 +370,34 @@ __global__ __launch_bounds__(kRowThreads) void accept_resample_kernel(AcceptArgs
     const int c = blockIdx.x, b = blockIdx.y;
     const int g = a.gamma;
 
-    // drafted tokens and their logits (written by the statistics kernel)
+    // drafted tokens and their logits (two dependent loads, hidden behind the staging of
+    // the row partials and the row statistics)
     int x = 0;
     float lpx = 0.0f, lqx = 0.0f;
     double u_mine = 0.0;  // thread i < gamma: ratio test i; thread gamma: the extra token
     if (threadIdx.x < g) {
         x = a.tokens[(int64_t)b * g + threadIdx.x];
-        lpx = w.xlog[(int64_t)b * 2 * g + threadIdx.x];
-        lqx = w.xlog[(int64_t)b * 2 * g + g + threadIdx.x];
+        const int xc = min(max(x, 0), a.V - 1);  // a bad token is flagged below, its logit unused
+        lpx = a.target[((int64_t)b * (g + 1) + threadIdx.x) * a.V + xc];
+        lqx = a.draft[((int64_t)b * g + threadIdx.x) * a.V + xc];
     }
     if ((int)threadIdx.x <= g) u_mine = w.u[(int64_t)b * (g + 1) + threadIdx.x];
     if (threadIdx.x == 0) {
         firstbad = g;
         bad = 0;
     }
-    const RowPart *pp = w.part + (int64_t)b * a.rows * a.nchunk;
+    const RowPart *pp = w.part + (int64_t)b * a.rows * a.npart;
     RowPart *stage = reinterpret_cast<RowPart *>(dyn_lds);
     auto keep_extra = [&] {
         if ((int)threadIdx.x == g) s_uextra = u_mine;
     };
-    if (a.rows * a.nchunk <= kMaxStaged) {
-        stage_parts(pp, a.rows * a.nchunk, stage, keep_extra);
-        row_softmax_stats(stage, a.rows, a.nchunk, a.kf, sM, sZ);
+    if (a.rows * a.npart <= kMaxStaged) {
+        stage_parts(pp, a.rows * a.npart, stage, keep_extra);
+        row_softmax_stats(stage, a.rows, a.npart, a.kf, sM, sZ);
     } else {
         keep_extra();
         __syncthreads();
-        row_softmax_stats(pp, a.rows, a.nchunk, a.kf, sM, sZ);
+        row_softmax_stats(pp, a.rows, a.npart, a.kf, sM, sZ);
     }
     if (threadIdx.x < g) {
         const int i = threadIdx.x;
@@ -561,16 +563,37 @@ static hipError_t launch(K kernel, dim3 grid, hipStream_t s, const AcceptArgs &a
     return hipGetLastError();
 }
 
+// Blocks of a looping kernel that are resident at once on the current device (occupancy
+// x compute units), cached per kernel and device: a larger grid would leave the last blocks
+// waiting for a second round.
+template <bool VEC, bool SAMPLE, int PER>
+static int stats_resident_blocks()
+{
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (cached[dev] == 0) {
+        int per_cu = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, accept_stats_kernel<VEC, SAMPLE, PER>, kRowThreads,
+                                                          0) != hipSuccess ||
+            per_cu < 1)
+            per_cu = 2;
+        cached[dev] = per_cu * device_cu_count();
+    }
+    return cached[dev];
+}
+
 template <bool VEC, int PER>
 static sv_status run_accept(const AcceptArgs &a, const AcceptWs &w, hipStream_t s, bool sample, bool alpha)
 {
     // staging slots: the part count rounded up to 1, 2, 4 or 8 per thread
-    const int staged = a.rows * a.nchunk;
+    const int staged = a.rows * a.npart;
     int slots = kRowThreads;
     while (slots < staged) slots *= 2;
     const size_t lds = staged <= kMaxStaged ? (size_t)slots * sizeof(RowPart) : 0;
     const int64_t ntask = (int64_t)a.nchunk * (a.rows + (sample ? 1 : 0)) * a.B;
-    const dim3 gstats((unsigned)(ntask < a.max_blocks ? ntask : a.max_blocks));
+    const int64_t resident = sample ? stats_resident_blocks<VEC, true, PER>() : stats_resident_blocks<VEC, false, PER>();
+    const dim3 gstats((unsigned)(ntask < resident ? ntask : resident));
     if (!sample) {
         if (launch(accept_stats_kernel<VEC, false, PER>, gstats, s, a, w) != hipSuccess) return SV_ERR_HIP;
         return launch(accept_greedy_kernel, dim3(a.B), s, a, w, lds) == hipSuccess ? SV_OK : SV_ERR_HIP;
@@ -609,7 +632,6 @@ extern "C" sv_status sv_spec_accept(const sv_accept_desc *d, void *workspace, si
     AcceptWs w;
     w.cnt = (int *)(ws + L.cnt);
     w.part = (RowPart *)(ws + L.part);
-    w.xlog = (float *)(ws + L.xlog);
     w.u = (double *)(ws + L.u);
     w.res = (ResPart *)(ws + L.res);
     w.seg = (double *)(ws + L.seg);
@@ -641,7 +663,7 @@ extern "C" sv_status sv_spec_accept(const sv_accept_desc *d, void *workspace, si
     const int big_chunks = (d->V + 4 * kMinChunk - 1) / (4 * kMinChunk);
     const bool wide = (int64_t)a.B * a.rows * big_chunks >= 1024;
     a.nchunk = wide ? big_chunks : (d->V + kMinChunk - 1) / kMinChunk;
-    a.max_blocks = 4 * device_cu_count();
+    a.npart = a.nchunk * (wide ? parts_per_chunk<64>() : parts_per_chunk<16>());
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
     return wide ? (vec ? run_accept<true, 64>(a, w, s, sample, d->alpha != nullptr)

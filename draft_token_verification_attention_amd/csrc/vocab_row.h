@@ -28,33 +28,25 @@ __device__ __forceinline__ int chunk_index(int chunk_base, int k)
     return chunk_base + (int)threadIdx.x + kRowThreads * k;
 }
 
-// All of a thread's loads are issued before any is waited for: a full chunk (the common
-// case, a uniform branch) uses unconditional vector loads; the last, partial chunk of a row
-// reads clamped in-bounds addresses and masks the positions at or beyond V.
+// All of a thread's loads are issued before any is waited for, with no branch (a load
+// under a branch lets the compiler wait for earlier loads at the join): vector rows read
+// clamped in-bounds float4s and mask the positions at or beyond V (V % 4 == 0, so a float4
+// is wholly inside or wholly beyond the row).
 template <bool VEC, int PER>
 __device__ __forceinline__ void load_chunk(const float *__restrict__ row, int chunk_base, int V, float (&x)[PER])
 {
-    if (VEC && chunk_base + PER * kRowThreads <= V) {
+    if (VEC) {
+        float4 f[PER / 4];
+#pragma unroll
+        for (int k4 = 0; k4 < PER / 4; ++k4)
+            f[k4] = *reinterpret_cast<const float4 *>(row + min(chunk_base + 4 * (int)threadIdx.x + 1024 * k4, V - 4));
 #pragma unroll
         for (int k4 = 0; k4 < PER / 4; ++k4) {
-            const float4 f = *reinterpret_cast<const float4 *>(row + chunk_base + 4 * (int)threadIdx.x + 1024 * k4);
-            x[4 * k4 + 0] = f.x;
-            x[4 * k4 + 1] = f.y;
-            x[4 * k4 + 2] = f.z;
-            x[4 * k4 + 3] = f.w;
-        }
-        return;
-    }
-    if (VEC) {  // V % 4 == 0: a float4 is wholly inside or wholly beyond the row
-#pragma unroll
-        for (int k4 = 0; k4 < PER / 4; ++k4) {
-            const int e = chunk_base + 4 * (int)threadIdx.x + 1024 * k4;
-            const float4 f = *reinterpret_cast<const float4 *>(row + min(e, V - 4));
-            const bool in = e < V;
-            x[4 * k4 + 0] = in ? f.x : -INFINITY;
-            x[4 * k4 + 1] = in ? f.y : -INFINITY;
-            x[4 * k4 + 2] = in ? f.z : -INFINITY;
-            x[4 * k4 + 3] = in ? f.w : -INFINITY;
+            const bool in = chunk_base + 4 * (int)threadIdx.x + 1024 * k4 < V;
+            x[4 * k4 + 0] = in ? f[k4].x : -INFINITY;
+            x[4 * k4 + 1] = in ? f[k4].y : -INFINITY;
+            x[4 * k4 + 2] = in ? f[k4].z : -INFINITY;
+            x[4 * k4 + 3] = in ? f[k4].w : -INFINITY;
         }
         return;
     }
@@ -72,28 +64,7 @@ template <bool VEC, int PER>
 __device__ __forceinline__ void load_chunk2(const float *__restrict__ r0, const float *__restrict__ r1, int chunk_base,
                                             int V, float (&x0)[PER], float (&x1)[PER])
 {
-    if (VEC && chunk_base + PER * kRowThreads <= V) {
-        float4 f0[PER / 4], f1[PER / 4];
-#pragma unroll
-        for (int k4 = 0; k4 < PER / 4; ++k4) {
-            const int e = chunk_base + 4 * (int)threadIdx.x + 1024 * k4;
-            f0[k4] = *reinterpret_cast<const float4 *>(r0 + e);
-            f1[k4] = *reinterpret_cast<const float4 *>(r1 + e);
-        }
-#pragma unroll
-        for (int k4 = 0; k4 < PER / 4; ++k4) {
-            x0[4 * k4 + 0] = f0[k4].x;
-            x0[4 * k4 + 1] = f0[k4].y;
-            x0[4 * k4 + 2] = f0[k4].z;
-            x0[4 * k4 + 3] = f0[k4].w;
-            x1[4 * k4 + 0] = f1[k4].x;
-            x1[4 * k4 + 1] = f1[k4].y;
-            x1[4 * k4 + 2] = f1[k4].z;
-            x1[4 * k4 + 3] = f1[k4].w;
-        }
-        return;
-    }
-    if (VEC) {  // V % 4 == 0: a float4 is wholly inside or wholly beyond the row
+    if (VEC) {  // clamped float4s, masked (no branch: see load_chunk)
         float4 f0[PER / 4], f1[PER / 4];
 #pragma unroll
         for (int k4 = 0; k4 < PER / 4; ++k4) {
