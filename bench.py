@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--split-keys", type=int, default=0)
+    ap.add_argument("--kv-cache", choices=["auto", "ragged"], default="auto",
+                    help="auto: dense cache for one sequence, ragged (kv_off) for a batch")
     ap.add_argument("--rotate-bytes", type=float, default=1.1e9)
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of replaying HIP graphs")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -100,7 +102,11 @@ def main():
 
     base = dict(q=to_dev(att["q"], bf), k=to_dev(att["k"], bf), v=to_dev(att["v"], bf),
                 target=to_dev(acc["target"]), draft=to_dev(acc["draft"]))
-    kv_off = to_dev(att["kv_off"].astype(np.int64))
+    # One sequence: a dense cache (kv_off NULL; the sequence owns max_prefix + n_q token
+    # slots, which is what the packed buffer holds).  A batch: the packed ragged cache.
+    dense = B == 1 and int(P[0]) == max_prefix and args.kv_cache != "ragged"
+    kv_off = None if dense else to_dev(att["kv_off"].astype(np.int64))
+    kv_sb = (max_prefix + n_q) * Hkv * D if dense else 0
     prefix = to_dev(P.astype(np.int32))
     toks = to_dev(acc["draft_tokens"].astype(np.int32))
     set_bytes = sum(t.numel() * t.element_size() for t in base.values())
@@ -119,7 +125,7 @@ def main():
     for c in copies:
         adescs.append(sv.attn_desc(c["q"], c["k"], c["v"], kv_off, prefix, Hkv=Hkv, max_prefix=max_prefix,
                                    scale=scale, kv_sh=att["kv_sh"], kv_st=att["kv_st"], out=out,
-                                   split_keys=args.split_keys))
+                                   split_keys=args.split_keys, kv_sb=kv_sb))
         sdescs.append(sv.accept_desc(sv.SV_SAMPLE, c["target"], c["draft"], toks, tau, 1000 + wl, 0, None,
                                      acc_len, out_tok, None, status))
     ws_a = sv.lib.sv_verify_attention_workspace(ctypes.byref(adescs[0]))
@@ -195,7 +201,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg["name"], "batch": B, "gamma": gamma, "cached_context": int(P.max()),
                    "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "vocab": V, "temperature": tau,
-                   "mode": "sample", "rotated_input_copies": R, "launch": "eager" if args.eager else "hip_graph"},
+                   "mode": "sample", "kv_cache": "dense" if dense else "ragged (kv_off)",
+                   "rotated_input_copies": R, "launch": "eager" if args.eager else "hip_graph"},
         "roofline": {"bound": "hbm", "achieved": round(main_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(main_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl),
                      "kernel": "attn_bf16_kernel", "kernel_ms": round(main_ms, 5),

@@ -36,7 +36,7 @@ class sv_attn_desc(ctypes.Structure):
                 ("max_prefix", _i32), ("split_keys", _i32), ("scale", _f32),
                 ("q", _P), ("q_sb", _i64), ("q_st", _i64), ("q_sh", _i64),
                 ("k", _P), ("v", _P), ("kv_off", _P), ("kv_sh", _i64), ("kv_st", _i64),
-                ("prefix_len", _P), ("tree_bits", _P), ("tree_sb", _i64),
+                ("kv_sb", _i64), ("prefix_len", _P), ("tree_bits", _P), ("tree_sb", _i64),
                 ("out", _P), ("o_sb", _i64), ("o_st", _i64), ("o_sh", _i64), ("lse", _P)]
 
 
@@ -145,7 +145,7 @@ def sv_build_tree_mask(parents: torch.Tensor, prefix_len: int):
 
 def attn_desc(q, k, v, kv_off, prefix_len, *, Hkv: int, max_prefix: int, scale: float,
               kv_sh: int, kv_st: int, out, lse=None, tree_bits=None, tree_sb: int = 0,
-              split_keys: int = 0) -> sv_attn_desc:
+              split_keys: int = 0, kv_sb: int = 0) -> sv_attn_desc:
     B, n_q, Hq, D = q.shape
     d = sv_attn_desc()
     d.dtype = SV_BF16 if q.dtype == torch.bfloat16 else SV_F32
@@ -155,8 +155,8 @@ def attn_desc(q, k, v, kv_off, prefix_len, *, Hkv: int, max_prefix: int, scale: 
     d.q = q.data_ptr()
     d.q_sb, d.q_st, d.q_sh = q.stride(0), q.stride(1), q.stride(2)
     d.k, d.v = k.data_ptr(), v.data_ptr()
-    d.kv_off = kv_off.data_ptr()
-    d.kv_sh, d.kv_st = int(kv_sh), int(kv_st)
+    d.kv_off = None if kv_off is None else kv_off.data_ptr()
+    d.kv_sh, d.kv_st, d.kv_sb = int(kv_sh), int(kv_st), int(kv_sb)
     d.prefix_len = prefix_len.data_ptr()
     d.tree_bits = None if tree_bits is None else tree_bits.data_ptr()
     d.tree_sb = int(tree_sb)
@@ -168,10 +168,12 @@ def attn_desc(q, k, v, kv_off, prefix_len, *, Hkv: int, max_prefix: int, scale: 
 
 def sv_verify_attention(q, k, v, kv_off, prefix_len, *, Hkv: int, max_prefix: int, scale: float,
                         kv_sh: int, kv_st: int, tree_bits=None, tree_sb: int = 0, out=None,
-                        want_lse: bool = False, split_keys: int = 0):
+                        want_lse: bool = False, split_keys: int = 0, kv_sb: int = 0):
     """q [B][n_q][Hq][D] (bf16 or fp32, D contiguous); k, v flat caches of the same dtype;
-    kv_off int64 [B]; prefix_len int32 [B]; tree_bits int32 rows from sv_build_tree_mask
-    (TREE) or None (CAUSAL).  Returns (out [B][n_q][Hq][D], lse fp32 [B][n_q][Hq] or None)."""
+    kv_off int64 [B], or None for a dense cache whose sequence b starts at element b*kv_sb
+    (each sequence then owns max_prefix + n_q token slots); prefix_len int32 [B]; tree_bits
+    int32 rows from sv_build_tree_mask (TREE) or None (CAUSAL).
+    Returns (out [B][n_q][Hq][D], lse fp32 [B][n_q][Hq] or None)."""
     _need_cuda(q, k, v, kv_off, prefix_len, tree_bits)
     if q.stride(-1) != 1:
         raise ValueError("q must have a contiguous head dimension")
@@ -179,7 +181,8 @@ def sv_verify_attention(q, k, v, kv_off, prefix_len, *, Hkv: int, max_prefix: in
         out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if want_lse else None
     d = attn_desc(q, k, v, kv_off, prefix_len, Hkv=Hkv, max_prefix=max_prefix, scale=scale, kv_sh=kv_sh,
-                  kv_st=kv_st, out=out, lse=lse, tree_bits=tree_bits, tree_sb=tree_sb, split_keys=split_keys)
+                  kv_st=kv_st, out=out, lse=lse, tree_bits=tree_bits, tree_sb=tree_sb, split_keys=split_keys,
+                  kv_sb=kv_sb)
     nb = lib.sv_verify_attention_workspace(ctypes.byref(d))
     ws = workspace(nb, q.device)
     _check(lib.sv_verify_attention(ctypes.byref(d), _ptr(ws), nb, _stream(q.device)), "sv_verify_attention")

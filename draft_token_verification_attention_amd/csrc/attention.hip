@@ -42,9 +42,10 @@ struct AttnArgs {
     const void *q;
     int64_t q_sb, q_st, q_sh;
     const void *k, *v;
-    const int64_t *kv_off;
-    int64_t kv_sh, kv_st;
+    const int64_t *kv_off;  // or NULL: sequence b starts at element b * kv_sb
+    int64_t kv_sh, kv_st, kv_sb;
     const int32_t *prefix_len;
+    int max_prefix, tmax;   // tmax = max_prefix + n_q
     const uint32_t *tree_bits;
     int64_t tree_sb;
     int words, tree;
@@ -109,7 +110,9 @@ __device__ __forceinline__ bool node_visible(const AttnArgs &a, const uint32_t *
 }
 
 // ---------------------------------------------------------------------------
-template <int DH, int NWR, int NWK>
+// SPEC (one-row-wave variant, kv_off NULL): each wave issues its first tile's loads before
+// the sequence length is known.
+template <int DH, int NWR, int NWK, bool SPEC>
 __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a)
 {
     constexpr int ROWS_BLK = 32 * NWR;
@@ -126,6 +129,7 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
     constexpr int KPW = kTileKeys / NWR;                // key rows loaded per wave
     constexpr int NI = KPW / KPI;                       // load instructions per wave and tensor
     static_assert(NI >= 1 && KPW % KPI == 0, "tile split");
+    static_assert(!SPEC || NWR == 1, "speculative first tile: one-row-wave variant");
 
     __shared__ __align__(16) char smem[SMEM];
     __shared__ uint16_t tile_list[kMaxTiles];
@@ -179,19 +183,38 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
             qf[c] = as_bf16x8(u);
         }
     }
+    const int SK = a.split_keys;
+    const int64_t seq_off = SPEC ? (int64_t)b * a.kv_sb : (a.kv_off ? a.kv_off[b] : (int64_t)b * a.kv_sb);
+    const uint16_t *kbase = (const uint16_t *)a.k + seq_off + (int64_t)kvh * a.kv_sh;
+    const uint16_t *vbase = (const uint16_t *)a.v + seq_off + (int64_t)kvh * a.kv_sh;
+
+    // ---- staging registers for this wave's share of a K/V tile ----
+    u32x4 kreg[NI], vreg[NI];
+    const int ld_key0 = wr * KPW + lane / LPR;
+    const int ld_dc = lane % LPR;
+    if constexpr (SPEC) {
+        // The first tile of this wave (tile wk of the split), loaded while the sequence
+        // length is still in flight.  Every sequence's slot holds tmax tokens, so rows are
+        // clamped below tmax; rows at or past the sequence's end are zeroed before use.
+        const int t0 = s * SK + wk * kTileKeys;
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const int64_t o = (int64_t)min(t0 + ld_key0 + j * KPI, a.tmax - 1) * a.kv_st + 8 * ld_dc;
+            kreg[j] = load_kv16<true>(reinterpret_cast<const char *>(kbase + o));
+            vreg[j] = load_kv16<true>(reinterpret_cast<const char *>(vbase + o));
+        }
+    }
     const int P = a.prefix_len[b];
     const int T = P + a.n_q;
-    const int SK = a.split_keys;
-    const bool overflow = (int64_t)T > (int64_t)a.nsplit * SK;
+    // a sequence longer than max_prefix reads nothing and reports NaN rows
+    const bool overflow = P > a.max_prefix;
     const int ns = overflow ? a.nsplit : (T + SK - 1) / SK;
     if (s >= ns) return;
     const int kstart = s * SK;
-    const int kend = min(kstart + SK, T);
+    const int kend = overflow ? kstart : min(kstart + SK, T);
     const int row_hi = min(rowbase + ROWS_BLK, a.rows) - 1;
     const int i_lo = rowbase / a.G, i_hi = row_hi / a.G;
 
-    const uint16_t *kbase = (const uint16_t *)a.k + a.kv_off[b] + (int64_t)kvh * a.kv_sh;
-    const uint16_t *vbase = (const uint16_t *)a.v + a.kv_off[b] + (int64_t)kvh * a.kv_sh;
     const uint32_t *bits_b = a.tree ? a.tree_bits + (int64_t)b * a.tree_sb : nullptr;
 
     // ---- the tiles some row of this block can see ----
@@ -251,10 +274,6 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
 
     const uint32_t *my_bits = a.tree ? bits_b + (int64_t)my_i * a.words : nullptr;
 
-    // ---- staging registers for this wave's share of a K/V tile ----
-    u32x4 kreg[NI], vreg[NI];
-    const int ld_key0 = wr * KPW + lane / LPR;
-    const int ld_dc = lane % LPR;
     // Tile loads address a uniform tile base (scalar registers) plus per-lane byte offsets
     // that are the same for every full tile.  In the last, partial tile, key rows past the
     // end of the cache re-read the last valid row (in bounds); the mask hides those keys,
@@ -297,9 +316,11 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
     // Wait for Q here, before the first tile's loads are issued (it was issued first and has
     // mostly landed by now).  Left to the compiler, the wait for Q merges into the first MFMA
     // of every tile as a wait for all outstanding loads, which defeats the prefetch.
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    if (niter > 0) issue_loads(0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(SPEC ? 2 * NI : 0));
+    if (!SPEC && niter > 0) issue_loads(0);
     const int my_iters = kDecode ? (count - wk + NWK - 1) / NWK : niter;
+    // rows of the speculative first tile at or past the end of the sequence (zeroed)
+    const int spec_lim = T - (kstart + wk * kTileKeys);
     for (int it = 0; it < my_iters; ++it) {
         const int li = it * NWK + wk;
         const bool have = li < count;
@@ -308,8 +329,13 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
 #pragma unroll
             for (int j = 0; j < NI; ++j) {
                 const int key = ld_key0 + j * KPI;
-                *reinterpret_cast<u32x4 *>(gK + key * KROW + 16 * ld_dc) = kreg[j];
-                *reinterpret_cast<u32x4 *>(gV + key * KROW + 16 * ld_dc) = vreg[j];
+                u32x4 kv = kreg[j], vv = vreg[j];
+                if (SPEC && it == 0 && key >= spec_lim) {
+                    kv = u32x4{0u, 0u, 0u, 0u};
+                    vv = u32x4{0u, 0u, 0u, 0u};
+                }
+                *reinterpret_cast<u32x4 *>(gK + key * KROW + 16 * ld_dc) = kv;
+                *reinterpret_cast<u32x4 *>(gV + key * KROW + 16 * ld_dc) = vv;
             }
         }
         if (!kDecode) __syncthreads();
@@ -525,7 +551,7 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a, 
         const int b = kg / a.Hkv, kvh = kg % a.Hkv;
         const int P = a.prefix_len[b];
         const int T = P + a.n_q;
-        const bool overflow = (int64_t)T > (int64_t)a.nsplit * a.split_keys;
+        const bool overflow = P > a.max_prefix;
         const int ns = overflow ? a.nsplit : (T + a.split_keys - 1) / a.split_keys;
         const int r = (t % nrc) * CR + rl;        // row within the tile
         const int row = rt * ROWS_BLK + r;
@@ -623,10 +649,12 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a, int D)
     const int lane = threadIdx.x;
     const int kvh = h / a.G;
     const int P = a.prefix_len[b];
-    const int T = P + a.n_q;
+    const bool overflow = P > a.max_prefix;  // reads nothing, reports NaN
+    const int T = overflow ? 0 : P + a.n_q;
     const float *q = (const float *)a.q + (int64_t)b * a.q_sb + (int64_t)i * a.q_st + (int64_t)h * a.q_sh;
-    const float *kb = (const float *)a.k + a.kv_off[b] + (int64_t)kvh * a.kv_sh;
-    const float *vb = (const float *)a.v + a.kv_off[b] + (int64_t)kvh * a.kv_sh;
+    const int64_t seq_off = a.kv_off ? a.kv_off[b] : (int64_t)b * a.kv_sb;
+    const float *kb = (const float *)a.k + seq_off + (int64_t)kvh * a.kv_sh;
+    const float *vb = (const float *)a.v + seq_off + (int64_t)kvh * a.kv_sh;
     const uint32_t *bits = a.tree ? a.tree_bits + (int64_t)b * a.tree_sb + (int64_t)i * a.words : nullptr;
     const bool two = D > 64;
     const float q0 = q[lane];
@@ -652,9 +680,11 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a, int D)
         m = mn;
     }
     float *o = (float *)a.out + (int64_t)b * a.o_sb + (int64_t)i * a.o_st + (int64_t)h * a.o_sh;
-    o[lane] = o0 / l;
-    if (two) o[lane + 64] = o1 / l;
-    if (a.lse && lane == 0) a.lse[((int64_t)b * a.n_q + i) * a.Hq + h] = (m + log2f(l)) * kLn2;
+    const float qnan = __int_as_float(0x7fc00000);
+    o[lane] = overflow ? qnan : o0 / l;
+    if (two) o[lane + 64] = overflow ? qnan : o1 / l;
+    if (a.lse && lane == 0)
+        a.lse[((int64_t)b * a.n_q + i) * a.Hq + h] = overflow ? qnan : (m + log2f(l)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -666,6 +696,7 @@ struct Plan {
     size_t part_bytes, cnt_bytes, total;
     unsigned blocks;
     int max_blocks;  // resident-block budget of the looping combine (set at launch)
+    bool spec;       // speculative first tile (set at launch)
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -731,8 +762,7 @@ static bool plan_attention(const sv_attn_desc *d, Plan &p)
     const size_t D = (size_t)d->D;
     if ((int64_t)p.KG * p.RT > kMaxCounters) return false;
     p.cnt_bytes = kCounterBytes;
-    // partials exist even for one split: a sequence longer than max_prefix still merges
-    // through them (to report NaN rows)
+    // (with one split the kernel stores its output directly; the partial area stays unused)
     p.part_bytes = align256((size_t)p.KG * p.RT * p.nsplit * rows_blk * (D + 4) * sizeof(float));
     p.total = p.cnt_bytes + p.part_bytes;
     return true;
@@ -747,7 +777,8 @@ static sv_status check_attention(const sv_attn_desc *d)
     if (d->Hq % d->Hkv != 0) return SV_ERR_INVALID_ARG;
     if (!(d->scale == d->scale)) return SV_ERR_INVALID_ARG;
     if (d->split_keys < 0) return SV_ERR_INVALID_ARG;
-    if (!d->q || !d->k || !d->v || !d->kv_off || !d->prefix_len || !d->out) return SV_ERR_INVALID_ARG;
+    if (!d->q || !d->k || !d->v || !d->prefix_len || !d->out) return SV_ERR_INVALID_ARG;
+    if (!d->kv_off && d->kv_sb < 0) return SV_ERR_INVALID_ARG;
     if (d->mask == SV_MASK_TREE && !d->tree_bits) return SV_ERR_INVALID_ARG;
     if (d->q_sb < 0 || d->q_st < 0 || d->q_sh < 0 || d->kv_sh < 0 || d->kv_st < 0 || d->o_sb < 0 || d->o_st < 0 ||
         d->o_sh < 0 || d->tree_sb < 0)
@@ -758,7 +789,7 @@ static sv_status check_attention(const sv_attn_desc *d)
     if (d->kv_st > (0x7fffffffLL / 32)) return SV_ERR_UNSUPPORTED;  // in-tile byte offsets are 32-bit
     if (d->dtype == SV_BF16) {
         // 16-byte vector access of q, k, v rows; 8-byte stores of out
-        const int64_t s16[] = {d->q_sb, d->q_st, d->q_sh, d->kv_sh, d->kv_st};
+        const int64_t s16[] = {d->q_sb, d->q_st, d->q_sh, d->kv_sh, d->kv_st, d->kv_off ? 0 : d->kv_sb};
         for (int64_t x : s16)
             if (x % 8) return SV_ERR_UNSUPPORTED;
         if (((uintptr_t)d->q | (uintptr_t)d->k | (uintptr_t)d->v) & 15) return SV_ERR_UNSUPPORTED;
@@ -772,10 +803,12 @@ static void *g_mark_event = nullptr;  // sv_set_attention_mark
 template <int DH, int NWR, int NWK>
 static hipError_t launch_variant(const Plan &p, const AttnArgs &a, hipStream_t s)
 {
-    if (NWR == 1)
-        hipLaunchKernelGGL((attn_bf16_kernel<DH, NWR, NWK>), dim3(p.nsplit, a.Hkv, a.B), dim3(256), 0, s, a);
+    if (NWR == 1 && p.spec)
+        hipLaunchKernelGGL((attn_bf16_kernel<DH, 1, NWK, true>), dim3(p.nsplit, a.Hkv, a.B), dim3(64 * NWK), 0, s, a);
+    else if (NWR == 1)
+        hipLaunchKernelGGL((attn_bf16_kernel<DH, 1, NWK, false>), dim3(p.nsplit, a.Hkv, a.B), dim3(64 * NWK), 0, s, a);
     else
-        hipLaunchKernelGGL((attn_bf16_kernel<DH, NWR, NWK>), dim3(p.blocks), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((attn_bf16_kernel<DH, NWR, NWK, false>), dim3(p.blocks), dim3(64 * NWR * NWK), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && g_mark_event) e = hipEventRecord((hipEvent_t)g_mark_event, s);
     if (e != hipSuccess || p.nsplit == 1) return e;
@@ -849,7 +882,10 @@ extern "C" sv_status sv_verify_attention(const sv_attn_desc *d, void *workspace,
     a.kv_off = d->kv_off;
     a.kv_sh = d->kv_sh;
     a.kv_st = d->kv_st;
+    a.kv_sb = d->kv_sb;
     a.prefix_len = d->prefix_len;
+    a.max_prefix = d->max_prefix;
+    a.tmax = d->max_prefix + d->n_q;
     a.tree_bits = d->tree_bits;
     a.tree_sb = d->tree_sb;
     a.words = (d->n_q + 31) / 32;
@@ -883,6 +919,10 @@ extern "C" sv_status sv_verify_attention(const sv_attn_desc *d, void *workspace,
         e = hipGetLastError();
     } else {
         p.max_blocks = 16 * device_cu_count();
+        // A grid of at most one block per CU is latency-bound: with a dense cache layout
+        // (no kv_off) the first tiles are loaded while the sequence lengths are in flight.
+        // Larger grids skip it (their empty splits would load tiles for nothing).
+        p.spec = p.variant == 1 && !d->kv_off && p.blocks <= (unsigned)device_cu_count();
         e = d->D == 128 ? launch_bf16<128>(p, a, s) : launch_bf16<64>(p, a, s);
     }
     return e == hipSuccess ? SV_OK : SV_ERR_HIP;

@@ -107,6 +107,9 @@ SV_API sv_status sv_build_tree_mask(const int32_t *parents, int32_t n, int32_t p
 /*   k, v cache of sequence b starts at element kv_off[b] (device int64 [B]); token t of */
 /*        KV head g is at kv_off[b] + g*kv_sh + t*kv_st.  The cache must hold P + n_q     */
 /*        tokens: the keys/values of the n_q new tokens are written before this call.    */
+/*        kv_off may be NULL (a dense cache): sequence b then starts at element b*kv_sb,  */
+/*        and every sequence must own max_prefix + n_q token slots, since the kernel may */
+/*        read any of them (rows past P + n_q are read but never used).                  */
 /*   prefix_len  device int32 [B];  max_prefix (host) must bound every prefix_len[b]:    */
 /*        it sizes the launch; a sequence whose P exceeds it gets NaN output rows.        */
 /*   tree_bits   TREE only: device uint32 rows as produced by sv_build_tree_mask, for    */
@@ -117,8 +120,8 @@ SV_API sv_status sv_build_tree_mask(const int32_t *parents, int32_t n, int32_t p
 /* split_keys: keys per work split (a tuning knob, rounded up to the kernel's tile        */
 /*        granularity); 0 picks a split that fills the GPU.                              */
 /* Supported: D in {64, 128}; Hq % Hkv == 0; n_q >= 1.  bf16 also needs 16-byte aligned  */
-/* q, k, v, strides and kv_off[b] that are multiples of 8 elements, and out and its      */
-/* strides aligned to 4 elements (else SV_ERR_UNSUPPORTED; kv_off is not checked).       */
+/* q, k, v, strides, kv_sb and kv_off[b] that are multiples of 8 elements, and out and  */
+/* its strides aligned to 4 elements (else SV_ERR_UNSUPPORTED; kv_off is not checked).   */
 /* ---------------------------------------------------------------------------------- */
 typedef struct sv_attn_desc {
     sv_dtype dtype;
@@ -133,6 +136,7 @@ typedef struct sv_attn_desc {
     const void *v;
     const int64_t *kv_off;
     int64_t kv_sh, kv_st;
+    int64_t kv_sb;
     const int32_t *prefix_len;
     const uint32_t *tree_bits;
     int64_t tree_sb;

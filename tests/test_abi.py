@@ -63,6 +63,9 @@ def _attn(**kw):
     (dict(q=FAKE + 8), sv.SV_ERR_UNSUPPORTED),                   # misaligned
     (dict(max_prefix=-1), sv.SV_ERR_INVALID_ARG),
     (dict(dtype=7), sv.SV_ERR_INVALID_ARG),
+    (dict(kv_off=None, kv_sb=-8), sv.SV_ERR_INVALID_ARG),        # dense cache, negative stride
+    (dict(kv_off=None, kv_sb=1001), sv.SV_ERR_UNSUPPORTED),      # dense cache, unaligned stride
+    (dict(kv_off=None, kv_sb=4102 * 1024), sv.SV_ERR_WORKSPACE), # dense cache: valid
     ({}, sv.SV_ERR_WORKSPACE),                                   # valid, but no workspace
 ])
 def test_attention_argument_checks(change, status):

@@ -24,12 +24,12 @@ from svgpu import attention_on_gpu, rows_of  # noqa: E402
 BF16_TOL, F32_TOL = 2e-2, 1e-4
 
 
-def _compare(inp, scale, tree_bits=None, tree_sb=0, rows=None, split_keys=0, max_prefix=None):
+def _compare(inp, scale, tree_bits=None, tree_sb=0, rows=None, split_keys=0, max_prefix=None, dense=False):
     tol = BF16_TOL if inp["dtype"] == "bf16" else F32_TOL
     ltol = 1e-3 if inp["dtype"] == "bf16" else 1e-5
     ref, ref_lse, rows = oracle.attention(inp, scale=scale, tree_bits=tree_bits, tree_sb=tree_sb, rows=rows)
     out, lse = attention_on_gpu(inp, scale, tree_bits=tree_bits, tree_sb=tree_sb, split_keys=split_keys,
-                                max_prefix=max_prefix)
+                                max_prefix=max_prefix, dense=dense)
     got = rows_of(out, rows)
     got_lse = rows_of(lse, rows)
     err = np.abs(got - ref).max()
@@ -158,6 +158,51 @@ def test_workload_cartesian_tree_sampled_rows():
     nodes = np.concatenate([np.arange(10), r.integers(0, n, 150), np.arange(n - 10, n)])
     rows = np.stack([np.zeros_like(nodes), nodes, r.integers(0, cfg["Hq"], len(nodes))], 1)
     _compare(inp, 1 / math.sqrt(cfg["D"]), tree_bits=bits, rows=rows)
+
+
+DENSE_SHAPES = [
+    # B, n_q, Hq, Hkv, D, prefix lengths, max_prefix (token slots per sequence = max_prefix + n_q)
+    (1, 6, 32, 8, 128, [4096], 4096),     # the 8B chain: first tiles loaded before the length
+    (1, 6, 32, 8, 128, [4000], 4100),     # slots past the sequence hold NaN and are read
+    (3, 5, 32, 8, 128, [64, 65, 1000], 1100),
+    (2, 8, 8, 1, 64, [31, 2047], 2047),
+    (40, 4, 32, 8, 128, [int(x) for x in np.linspace(3, 700, 40)], 720),  # grid beyond one block per CU
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", DENSE_SHAPES, ids=lambda s: "B%d_nq%d_D%d_mp%d" % (s[0], s[1], s[4], s[6]))
+def test_dense_layout_parity(dtype, shape):
+    """kv_off NULL: sequence b at b*kv_sb; every unused token slot of the cache is NaN."""
+    B, n_q, Hq, Hkv, D, P, mp = shape
+    inp = synth.attention_inputs(21, B=B, n_q=n_q, Hq=Hq, Hkv=Hkv, D=D, prefix_len=P, dtype=dtype, qkv_scale=1.0)
+    rows = None if B * n_q * Hq <= 2048 else rows_of_sample(inp, 400)
+    _compare(inp, 1 / math.sqrt(D), rows=rows, max_prefix=mp, dense=True)
+
+
+@pytest.mark.parametrize("split_keys", [0, 64])
+def test_dense_layout_tree(split_keys):
+    n = 7
+    parents = np.array([-1, 0, 0, 1, 1, 2, 5], dtype=np.int32)
+    bits, _, _ = oracle.tree_mask(parents, 700)
+    inp = synth.attention_inputs(22, B=1, n_q=n, Hq=8, Hkv=2, D=128, prefix_len=[700], dtype="bf16", qkv_scale=1.0)
+    _compare(inp, 1 / math.sqrt(128), tree_bits=bits, max_prefix=760, split_keys=split_keys, dense=True)
+
+
+def rows_of_sample(inp, n):
+    r = np.random.default_rng(5)
+    return np.stack([r.integers(0, inp["B"], n), r.integers(0, inp["n_q"], n), r.integers(0, inp["Hq"], n)], 1)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dense", [False, True])
+def test_prefix_just_beyond_bound_gives_nan(dtype, dense):
+    """P = max_prefix + 1 still fits the launch's one 128-key split, yet its rows are NaN
+    (and with a dense cache nothing past the sequence's max_prefix + n_q slots is read)."""
+    inp = synth.attention_inputs(7, B=2, n_q=4, Hq=8, Hkv=2, D=128, prefix_len=[100, 101], dtype=dtype)
+    out, lse = attention_on_gpu(inp, 0.1, max_prefix=100, split_keys=128, dense=dense)
+    assert np.isfinite(out[0]).all() and np.isfinite(lse[0]).all()
+    assert np.isnan(out[1]).all() and np.isnan(lse[1]).all()
 
 
 def test_prefix_beyond_bound_gives_nan():
