@@ -432,8 +432,8 @@ def cpu_baseline_tree(att, cfg, wl, parents, toks, scale, seconds):
 # counter reading half the bytes of a plain copy of known size on this GPU), from the
 # rocprofv3 --pmc runs summarized under profiles/, and the SHA-256 of the attention source
 # they were taken on: a changed kernel reports null until the counters are taken again.
-TRAFFIC = {2: 19184474, 4: 1128595583}
-TRAFFIC_SRC_SHA256 = "feddf9da971373ac9862f47a7ecddd282c880e8a9988f6dd24097bc1577af88c"
+TRAFFIC = {2: 19161806, 4: 1129431006}
+TRAFFIC_SRC_SHA256 = "f0daa90844936fc4b7ea0432fd6311720bdfdc8cee6f8e942d96aa6797a143f1"
 
 
 def measured_traffic(wl):
