@@ -212,6 +212,27 @@ def test_prefix_beyond_bound_gives_nan():
     assert np.isnan(out[1]).all() and np.isnan(lse[1]).all()
 
 
+def test_batch_split_edges():
+    """A batch of many 256-key splits: sequences that end exactly on a split boundary, empty
+    prefixes, sequences beyond max_prefix (NaN rows), and repeated calls on one workspace."""
+    n_q, Hq, Hkv, D, sk = 5, 32, 8, 128, 256
+    r = np.random.default_rng(3)
+    P = list(r.integers(0, 2000, 40)) + [0, 251, 507, 1019, 2000, 2001, 2600, 1, 763]
+    inp = synth.attention_inputs(23, B=len(P), n_q=n_q, Hq=Hq, Hkv=Hkv, D=D, prefix_len=P, dtype="bf16",
+                                 qkv_scale=1.0)
+    ok = [b for b in range(len(P)) if P[b] <= 2000]
+    rows = rows_of_sample(dict(inp, B=len(ok)), 500)
+    rows[:, 0] = np.array(ok)[rows[:, 0]]
+    rows = np.concatenate([rows, np.array([[b, n_q - 1, Hq - 1] for b in ok])])
+    _compare(inp, 1 / math.sqrt(D), rows=rows, max_prefix=2000, split_keys=sk)
+    first, fl = attention_on_gpu(inp, 0.09, max_prefix=2000, split_keys=sk)
+    for b in range(len(P)):
+        assert np.isnan(first[b]).all() == (P[b] > 2000), b
+    again, al = attention_on_gpu(inp, 0.09, max_prefix=2000, split_keys=sk)
+    assert np.array_equal(np.nan_to_num(again, nan=7.0), np.nan_to_num(first, nan=7.0))
+    assert np.array_equal(np.nan_to_num(al, nan=7.0), np.nan_to_num(fl, nan=7.0))
+
+
 def test_deterministic_repeats():
     inp = synth.attention_inputs(8, B=1, n_q=6, Hq=32, Hkv=8, D=128, prefix_len=[4096], dtype="bf16")
     first, fl = attention_on_gpu(inp, 0.088)
