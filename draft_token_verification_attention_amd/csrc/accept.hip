@@ -239,13 +239,13 @@ __global__ __launch_bounds__(kRowThreads) void accept_stats_kernel(AcceptArgs a,
             float mt = -INFINITY;
 #pragma unroll
             for (int k = 0; k < kPerThread; ++k) mt = fmaxf(mt, xv[k]);
-            // branch-free: -inf logits (masked, or beyond V) weigh exp2f(-inf) = 0
+            // branch-free: -inf logits (masked, or beyond V) weigh exp2_fast(-inf) = 0
             const float mref = mt == -INFINITY ? 0.0f : mt;
             double st = 0.0;
 #pragma unroll
-            for (int k = 0; k < kPerThread; ++k) st += (double)exp2f((xv[k] - mref) * a.kf);
+            for (int k = 0; k < kPerThread; ++k) st += (double)exp2_fast((xv[k] - mref) * a.kf);
             const float m = kParts > 1 ? wave_max(mt) : block_max(mt, fscr);
-            const double z = st > 0.0 ? st * (double)exp2f((mt - m) * a.kf) : 0.0;
+            const double z = st > 0.0 ? st * (double)exp2_fast((mt - m) * a.kf) : 0.0;
             const double sm = kParts > 1 ? wave_sum(z) : block_sum(z, dscr);
             part.m = m;
             part.arg = 0;
@@ -336,8 +336,8 @@ __global__ __launch_bounds__(kRowThreads) void accept_alpha_kernel(AcceptArgs a,
 #pragma unroll
     for (int k = 0; k < kPerThread; ++k) {
         if (xp[k] == -INFINITY && xq[k] == -INFINITY) continue;
-        const double p = (double)exp2f((xp[k] - Mp) * a.kf) * iZp;
-        const double q = (double)exp2f((xq[k] - Mq) * a.kf) * iZq;
+        const double p = (double)exp2_fast((xp[k] - Mp) * a.kf) * iZp;
+        const double q = (double)exp2_fast((xq[k] - Mq) * a.kf) * iZq;
         s += fmin(p, q);
     }
     s = block_sum(s, dscr);
@@ -431,12 +431,12 @@ __global__ __launch_bounds__(kRowThreads) void accept_resample_kernel(AcceptArgs
     const int base = c * kChunk;
 
     // weight of token e: residual (or p when every draft was kept / the residual is empty)
-    auto p_of = [&](float l) { return (double)exp2f((l - Mp) * a.kf) * iZp; };
-    auto q_of = [&](float l) { return (double)exp2f((l - Mq) * a.kf) * iZq; };
+    auto p_of = [&](float l) { return (double)exp2_fast((l - Mp) * a.kf) * iZp; };
+    auto q_of = [&](float l) { return (double)exp2_fast((l - Mq) * a.kf) * iZq; };
 
     float xp[kPerThread], xq[kPerThread];
     load_chunk2<VEC, kPerThread>(prow, qrow ? qrow : prow, base, a.V, xp, xq);
-    // branch-free: a position at or beyond V holds -inf, whose weight exp2f(-inf) = 0
+    // branch-free: a position at or beyond V holds -inf, whose weight exp2_fast(-inf) = 0
     // per thread, the residual mass of each float4 group (VEC layout: group k4 of wave w
     // is part of the chunk's 256-token segment 4 k4 + w, in token order)
     double rs = 0.0, ps = 0.0;

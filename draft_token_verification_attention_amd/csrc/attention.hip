@@ -116,9 +116,13 @@ template <int DH, int NWR, int NWK, bool SPEC>
 __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a)
 {
     constexpr int ROWS_BLK = 32 * NWR;
-    constexpr int KROW = DH * 2 + 16;                   // LDS bytes per key row (16 B pad)
+    // LDS row pitches: K rows padded by 16 B (the 16-byte A-operand reads of 32 rows hit
+    // distinct banks), V rows by 64 B (the transpose reads of 4 rows x 4 column groups per
+    // 16 lanes hit distinct banks; with a 16 B pad they conflict 4-way)
+    constexpr int KROW = DH * 2 + 16;
+    constexpr int VROW = DH * 2 + 64;
     constexpr int TILE_BYTES = kTileKeys * KROW;
-    constexpr int GROUP_BYTES = 2 * TILE_BYTES;         // K then V
+    constexpr int GROUP_BYTES = kTileKeys * (KROW + VROW);  // K then V
     constexpr int TILES_LDS = NWK * GROUP_BYTES;
     constexpr int NDB = DH / 32;                        // 32-wide d blocks of O^T
     constexpr int NKC = DH / 16;                        // 16-deep d chunks of S^T
@@ -335,7 +339,7 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
                     vv = u32x4{0u, 0u, 0u, 0u};
                 }
                 *reinterpret_cast<u32x4 *>(gK + key * KROW + 16 * ld_dc) = kv;
-                *reinterpret_cast<u32x4 *>(gV + key * KROW + 16 * ld_dc) = vv;
+                *reinterpret_cast<u32x4 *>(gV + key * VROW + 16 * ld_dc) = vv;
             }
         }
         if (!kDecode) __syncthreads();
@@ -385,9 +389,9 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
 #pragma unroll
             for (int v = 0; v < 16; ++v) p[v] = 0.0f;
         } else {
-            alpha = exp2f(m_run - m_new);  // m_run == -inf gives 0
+            alpha = exp2_fast(m_run - m_new);  // m_run == -inf gives 0
 #pragma unroll
-            for (int v = 0; v < 16; ++v) p[v] = exp2f(sv[v] - m_new);
+            for (int v = 0; v < 16; ++v) p[v] = exp2_fast(sv[v] - m_new);
         }
         float psum = 0.0f;
 #pragma unroll
@@ -416,13 +420,13 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
         // four and the four columns starting at 4 (r % 4); destination lane r gets column
         // r of those four rows).
         const int g16 = lane >> 4, r16 = lane & 15;
-        const char *vsrc = gV + (4 * (g16 >> 1) + (r16 >> 2)) * KROW + 2 * (16 * (g16 & 1) + 4 * (r16 & 3));
+        const char *vsrc = gV + (4 * (g16 >> 1) + (r16 >> 2)) * VROW + 2 * (16 * (g16 & 1) + 4 * (r16 & 3));
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
-                const char *p0 = vsrc + 16 * c * KROW + 64 * db;
-                const v4s lo = lds_read_tr16(p0), hi = lds_read_tr16(p0 + 8 * KROW);
+                const char *p0 = vsrc + 16 * c * VROW + 64 * db;
+                const v4s lo = lds_read_tr16(p0), hi = lds_read_tr16(p0 + 8 * VROW);
                 const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[c], oacc[db], 0, 0, 0);
             }
@@ -456,13 +460,13 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
         for (int k = 0; k < NWK; ++k) {
             const float mk = mls[((wr * NWK + k) * 2) * 64 + lane];
             const float lk = mls[((wr * NWK + k) * 2) * 64 + 64 + lane];
-            Lr += (mk == -INFINITY) ? 0.0f : lk * exp2f(mk - M);
+            Lr += (mk == -INFINITY) ? 0.0f : lk * exp2_fast(mk - M);
         }
         Lr = half_swap_sum(Lr);  // the other half of the row's keys
         row_m = M;
         row_inv_l = Lr;
         if (NWK > 1) {
-            const float f = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - M);
+            const float f = (m_run == -INFINITY) ? 0.0f : exp2_fast(m_run - M);
             float *my_acc = accs + ((wr * NWK + wk) * NE) * 64;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
@@ -585,7 +589,7 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a, 
         float lsum = 0.0f;
 #pragma unroll
         for (int k = 0; k < SPT; ++k) {
-            const float w = (k < nmine && ml[k].x != -INFINITY) ? exp2f(ml[k].x - M) : 0.0f;
+            const float w = (k < nmine && ml[k].x != -INFINITY) ? exp2_fast(ml[k].x - M) : 0.0f;
 #pragma unroll
             for (int v = 0; v < kCombVec; ++v) {
                 acc[v].x += o[k][v].x * w;
@@ -671,8 +675,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a, int D)
         if (two) part += q1 * kr[lane + 64];
         const float sc = wave_sum(part) * a.scale_log2;
         const float mn = fmaxf(m, sc);
-        const float f = exp2f(m - mn);
-        const float pw = exp2f(sc - mn);
+        const float f = exp2_fast(m - mn);
+        const float pw = exp2_fast(sc - mn);
         const float *vr = vb + (int64_t)t * a.kv_st;
         l = l * f + pw;
         o0 = o0 * f + pw * vr[lane];
@@ -803,12 +807,14 @@ static void *g_mark_event = nullptr;  // sv_set_attention_mark
 template <int DH, int NWR, int NWK>
 static hipError_t launch_variant(const Plan &p, const AttnArgs &a, hipStream_t s)
 {
-    if (NWR == 1 && p.spec)
-        hipLaunchKernelGGL((attn_bf16_kernel<DH, 1, NWK, true>), dim3(p.nsplit, a.Hkv, a.B), dim3(64 * NWK), 0, s, a);
-    else if (NWR == 1)
-        hipLaunchKernelGGL((attn_bf16_kernel<DH, 1, NWK, false>), dim3(p.nsplit, a.Hkv, a.B), dim3(64 * NWK), 0, s, a);
-    else
+    if constexpr (NWR == 1) {
+        if (p.spec)
+            hipLaunchKernelGGL((attn_bf16_kernel<DH, 1, NWK, true>), dim3(p.nsplit, a.Hkv, a.B), dim3(64 * NWK), 0, s, a);
+        else
+            hipLaunchKernelGGL((attn_bf16_kernel<DH, 1, NWK, false>), dim3(p.nsplit, a.Hkv, a.B), dim3(64 * NWK), 0, s, a);
+    } else {
         hipLaunchKernelGGL((attn_bf16_kernel<DH, NWR, NWK, false>), dim3(p.blocks), dim3(64 * NWR * NWK), 0, s, a);
+    }
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && g_mark_event) e = hipEventRecord((hipEvent_t)g_mark_event, s);
     if (e != hipSuccess || p.nsplit == 1) return e;

@@ -10,6 +10,12 @@ namespace sv {
 
 constexpr int kWave = 64;
 
+// 2^x as one v_exp_f32.  For x >= -126 this is exactly exp2f (whose library form adds a
+// range test and a rescale around the same instruction, seven instructions in all); below,
+// where exp2f returns a denormal, it may return 0.  Softmax weights that small vanish next to
+// the maximum's weight of 1.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Every workspace starts with this fixed region of completion counters.  It must be zero
 // when a workspace is first used; every call leaves it zero again.  Partial results live
 // after it, so calls of any entry point and any shape can share one workspace (if they do

@@ -317,7 +317,7 @@ __device__ __forceinline__ void group_combine_softmax(const Part *pp, int row, i
     if (row < nrows)
         for (int c = c0; c < nchunk; c += LPR) {
             const Part q = pp[(int64_t)row * nchunk + c];
-            if (q.s > 0.0) z += q.s * (double)exp2f((q.m - M) * kf);
+            if (q.s > 0.0) z += q.s * (double)exp2_fast((q.m - M) * kf);
         }
     Z = group_total<LPR>(z, 0.0, OpAdd());
 }

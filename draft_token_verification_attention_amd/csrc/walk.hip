@@ -114,7 +114,7 @@ __global__ __launch_bounds__(kRowThreads) void walk_level_kernel(WalkArgs a, Wal
         double s = 0.0;
 #pragma unroll
         for (int k = 0; k < kPerThread; ++k)
-            if (x[k] != -INFINITY) s += (double)exp2f((x[k] - m) * a.kf);
+            if (x[k] != -INFINITY) s += (double)exp2_fast((x[k] - m) * a.kf);
         s = block_sum(s, dscr);
         part.m = m;
         part.arg = 0;
@@ -163,7 +163,7 @@ __global__ __launch_bounds__(kRowThreads) void walk_level_kernel(WalkArgs a, Wal
         const int cb = s_chunk * kChunk;
         const float mc = s_mc;
         const double f = s_factor;
-        auto weight = [&](float l, float) -> double { return (double)exp2f((l - mc) * a.kf) * f; };
+        auto weight = [&](float l, float) -> double { return (double)exp2_fast((l - mc) * a.kf) * f; };
         int y = chunk_inverse_cdf<kPerThread, VEC>(row, nullptr, cb, a.V, s_base, s_target, weight, scan, iscr);
         if (y < 0) y = cb;  // no mass in the chunk at all (cannot happen for the chunk found)
         if (threadIdx.x == 0) s_y = y;
