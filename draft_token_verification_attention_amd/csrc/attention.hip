@@ -347,8 +347,11 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
         if (!have) continue;
         const int t0 = tile_start(li);
 
-        // S^T (32 keys x 32 rows) = K (keys x d) . Q^T (d x rows), as two independent MFMA
-        // chains over the even and odd d chunks (half the dependent-MFMA latency)
+        // S^T (32 keys x 32 rows) = K (keys x d) . Q^T (d x rows).  One row wave: two
+        // independent MFMA chains over the even and odd d chunks (half the dependent-MFMA
+        // latency on a latency-bound path); several: one chain (other waves hide its latency,
+        // and the 16 adds that join two chains are VALU time the MFMA-bound path lacks)
+        constexpr bool kTwoChains = kDecode;
         f32x16 sacc, sacc1;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -360,16 +363,22 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
             const bf16x8 kf0 = *reinterpret_cast<const bf16x8 *>(gK + l32 * KROW + (16 * c + 8 * h) * 2);
             const bf16x8 kf1 = *reinterpret_cast<const bf16x8 *>(gK + l32 * KROW + (16 * c + 16 + 8 * h) * 2);
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0, qf[c], sacc, 0, 0, 0);
-            sacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf1, qf[c + 1], sacc1, 0, 0, 0);
+            if constexpr (kTwoChains)
+                sacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf1, qf[c + 1], sacc1, 0, 0, 0);
+            else
+                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf1, qf[c + 1], sacc, 0, 0, 0);
         }
+        if constexpr (kTwoChains) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) sacc[v] += sacc1[v];
-        // lane (row l32, half h) holds keys 8*(v/4) + 4*h + v%4
+            for (int v = 0; v < 16; ++v) sacc[v] += sacc1[v];
+        }
+        // lane (row l32, half h) holds keys 8*(v/4) + 4*h + v%4.  The row max is taken on the
+        // raw scores (scale > 0) and the scale is folded into the exponent's FMA.
         float sv[16];
         const bool need_mask = (t0 + kTileKeys > P);
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            float x = sacc[v] * a.scale_log2;
+            float x = sacc[v];
             if (need_mask) {
                 const int t = t0 + 8 * (v >> 2) + 4 * h + (v & 3);
                 bool vis = t < T;
@@ -382,7 +391,7 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
 #pragma unroll
         for (int v = 1; v < 16; ++v) mloc = fmaxf(mloc, sv[v]);
         mloc = half_swap_max(mloc);  // the row's other 16 keys sit in lane l ^ 32
-        const float m_new = fmaxf(m_run, mloc);
+        const float m_new = fmaxf(m_run, mloc * a.scale_log2);
         float alpha = 1.0f;
         float p[16];
         if (m_new == -INFINITY) {
@@ -391,7 +400,7 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
         } else {
             alpha = exp2_fast(m_run - m_new);  // m_run == -inf gives 0
 #pragma unroll
-            for (int v = 0; v < 16; ++v) p[v] = exp2_fast(sv[v] - m_new);
+            for (int v = 0; v < 16; ++v) p[v] = exp2_fast(fmaf(sv[v], a.scale_log2, -m_new));
         }
         float psum = 0.0f;
 #pragma unroll
@@ -779,7 +788,7 @@ static sv_status check_attention(const sv_attn_desc *d)
     if (d->mask != SV_MASK_CAUSAL && d->mask != SV_MASK_TREE) return SV_ERR_INVALID_ARG;
     if (d->B < 0 || d->n_q < 1 || d->Hq < 1 || d->Hkv < 1 || d->D < 1 || d->max_prefix < 0) return SV_ERR_INVALID_ARG;
     if (d->Hq % d->Hkv != 0) return SV_ERR_INVALID_ARG;
-    if (!(d->scale == d->scale)) return SV_ERR_INVALID_ARG;
+    if (!(d->scale > 0.0f)) return SV_ERR_INVALID_ARG;  // also NaN
     if (d->split_keys < 0) return SV_ERR_INVALID_ARG;
     if (!d->q || !d->k || !d->v || !d->prefix_len || !d->out) return SV_ERR_INVALID_ARG;
     if (!d->kv_off && d->kv_sb < 0) return SV_ERR_INVALID_ARG;

@@ -62,6 +62,9 @@ def _attn(**kw):
     (dict(kv_st=1001), sv.SV_ERR_UNSUPPORTED),                   # not a multiple of 8 elements
     (dict(q=FAKE + 8), sv.SV_ERR_UNSUPPORTED),                   # misaligned
     (dict(max_prefix=-1), sv.SV_ERR_INVALID_ARG),
+    (dict(scale=0.0), sv.SV_ERR_INVALID_ARG),
+    (dict(scale=-0.088), sv.SV_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), sv.SV_ERR_INVALID_ARG),
     (dict(dtype=7), sv.SV_ERR_INVALID_ARG),
     (dict(kv_off=None, kv_sb=-8), sv.SV_ERR_INVALID_ARG),        # dense cache, negative stride
     (dict(kv_off=None, kv_sb=1001), sv.SV_ERR_UNSUPPORTED),      # dense cache, unaligned stride
