@@ -432,8 +432,8 @@ def cpu_baseline_tree(att, cfg, wl, parents, toks, scale, seconds):
 # counter reading half the bytes of a plain copy of known size on this GPU), from the
 # rocprofv3 --pmc runs summarized under profiles/, and the SHA-256 of the attention source
 # they were taken on: a changed kernel reports null until the counters are taken again.
-TRAFFIC = {2: 19161806, 4: 1129431006}
-TRAFFIC_SRC_SHA256 = "f0daa90844936fc4b7ea0432fd6311720bdfdc8cee6f8e942d96aa6797a143f1"
+TRAFFIC = {2: 19146683, 4: 1129418171}
+TRAFFIC_SRC_SHA256 = "a1a3a0fc31ac86b8bd90c9c58f842fd7a41917f8fb1f3bb4599268a4826a6b6c"
 
 
 def measured_traffic(wl):
