@@ -37,6 +37,7 @@ constexpr int kMaxTiles = 1024;  // tiles per split (split_keys <= 32768)
 constexpr int kMaxSplits = 64;   // key splits per sequence
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLazyLog2 = 8.0f;  // online softmax: largest unrescaled weight is 2^8
 
 struct AttnArgs {
     const void *q;
@@ -391,7 +392,11 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
 #pragma unroll
         for (int v = 1; v < 16; ++v) mloc = fmaxf(mloc, sv[v]);
         mloc = half_swap_max(mloc);  // the row's other 16 keys sit in lane l ^ 32
-        const float m_new = fmaxf(m_run, mloc * a.scale_log2);
+        // Lazy reference: the running max m_run (log2 units) moves only when a tile's row max
+        // passes it by more than kLazyLog2, so most tiles skip the accumulator rescale; weights
+        // against the stale reference stay below 2^kLazyLog2 (exact in the final l and O).
+        const float m_tile = mloc * a.scale_log2;
+        const float m_new = (m_tile <= m_run + kLazyLog2) ? m_run : m_tile;
         float alpha = 1.0f;
         float p[16];
         if (m_new == -INFINITY) {
