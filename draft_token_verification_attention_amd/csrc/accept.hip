@@ -175,13 +175,15 @@ __device__ __forceinline__ void row_softmax_stats_lpr(const RowPart *src, int nr
     __syncthreads();
 }
 
-// (M, Z) of rows [0, nrows): the chunk partials of a row sit on 16, 32 or 64 lanes.
+// (M, Z) of rows [0, nrows): the chunk partials of a row sit on 16, 32 or 64 lanes -- the
+// fewest lanes that hold a part each, but more lanes per row only while every row still
+// fits in one pass of the block (a second pass costs more than a lane reading two parts)
 __device__ __forceinline__ void row_softmax_stats(const RowPart *src, int nrows, int nchunk, float kf, double *sM,
                                                   double *sZ)
 {
-    if (nchunk <= 16)
+    if (nchunk <= 16 || nrows > kRowThreads / 32)
         row_softmax_stats_lpr<16>(src, nrows, nchunk, kf, sM, sZ);
-    else if (nchunk <= 32)
+    else if (nchunk <= 32 || nrows > kRowThreads / 64)
         row_softmax_stats_lpr<32>(src, nrows, nchunk, kf, sM, sZ);
     else
         row_softmax_stats_lpr<64>(src, nrows, nchunk, kf, sM, sZ);
