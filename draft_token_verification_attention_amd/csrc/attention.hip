@@ -757,16 +757,19 @@ static bool plan_attention(const sv_attn_desc *d, Plan &p)
         sk = 256;
         while (sk * 2 <= want && sk < 4096) sk *= 2;
     } else {
-        // Many rows per block: a partial costs as much as the keys it summarizes, so split
-        // only when there are too few row tiles to occupy the chip.
-        if (groups >= 512) {
+        // Many rows per block: a partial (32 NWR rows x (D + 4) fp32, written and read back)
+        // costs about as much as the K/V of 130 keys, so split only until every CU has a
+        // block, and never below 256 keys (measured on the 64-node Medusa tree, 2048-key
+        // cache: 128-key splits 54 us per round, 256-key 45 us, 512-key 47 us).
+        const int64_t cus = device_cu_count();
+        if (groups >= cus) {
             sk = Tmax;
         } else {
-            const int64_t nsp = (512 + groups - 1) / groups;
+            const int64_t nsp = (cus + groups - 1) / groups;
             sk = (Tmax + nsp - 1) / nsp;
         }
         sk = (sk + unit - 1) / unit * unit;
-        if (sk < unit) sk = unit;
+        if (sk < 256) sk = 256;
     }
     if ((Tmax + sk - 1) / sk > kMaxSplits) sk = ((Tmax + kMaxSplits - 1) / kMaxSplits + unit - 1) / unit * unit;
     if (sk > (int64_t)kMaxTiles * kTileKeys) return false;
