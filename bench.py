@@ -432,8 +432,8 @@ def cpu_baseline_tree(att, cfg, wl, parents, toks, scale, seconds):
 # counter reading half the bytes of a plain copy of known size on this GPU), from the
 # rocprofv3 --pmc runs summarized under profiles/, and the SHA-256 of the attention source
 # they were taken on: a changed kernel reports null until the counters are taken again.
-TRAFFIC = {2: 19146683, 4: 1129418171}
-TRAFFIC_SRC_SHA256 = "a1a3a0fc31ac86b8bd90c9c58f842fd7a41917f8fb1f3bb4599268a4826a6b6c"
+TRAFFIC = {2: 19146696, 4: 1129419806}
+TRAFFIC_SRC_SHA256 = "c84a41ddd235549e33f78c1ee980c2d020d5ed94decd4296bce37ee82c24e87b"
 
 
 def measured_traffic(wl):
