@@ -27,10 +27,16 @@ def _mask_on_gpu(parents, P):
     return bits.cpu().numpy().view(np.uint32), depth.cpu().numpy(), pos.cpu().numpy(), int(st.cpu()[0])
 
 
-@pytest.mark.parametrize("case", ["page", "chain1", "chain70", "random513", "forest", "medusa", "cartesian"])
+@pytest.mark.parametrize("case", ["page", "chain1", "chain70", "random513", "forest", "medusa", "cartesian",
+                                  "chain2500", "random9000"])
 def test_tree_mask_parity(case):
+    """random9000 exceeds the kernel's LDS staging of the parent array (read from global memory)."""
     P = 17
-    if case == "page":
+    if case == "chain2500":
+        parents = np.arange(2500) - 1
+    elif case == "random9000":
+        parents = synth.random_tree(5, 9000, branch_p=0.9)
+    elif case == "page":
         parents = np.array([-1, -1, 0, 0, 1, 2])
     elif case == "chain1":
         parents = np.array([-1])
