@@ -433,7 +433,7 @@ def cpu_baseline_tree(att, cfg, wl, parents, toks, scale, seconds):
 # rocprofv3 --pmc runs summarized under profiles/, and the SHA-256 of the attention source
 # they were taken on: a changed kernel reports null until the counters are taken again.
 TRAFFIC = {2: 19146696, 4: 1129419806}
-TRAFFIC_SRC_SHA256 = "c84a41ddd235549e33f78c1ee980c2d020d5ed94decd4296bce37ee82c24e87b"
+TRAFFIC_SRC_SHA256 = "2fe5220deb4513d4563d7dc67095f05fb0a5a12daddf2dfa96248add086d4536"
 
 
 def measured_traffic(wl):

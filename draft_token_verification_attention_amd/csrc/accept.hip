@@ -9,17 +9,18 @@
 //
 // Kernels (one launch each, all decisions on the device):
 //   stats    tasks (chunk, row, sequence), looping grid.  A task reads one chunk of one
-//            row once; each wave keeps, for its quarter of the chunk, GREEDY (max, first
-//            argmax) or SAMPLE (max m, S = sum exp((l - m)/T) in fp64).  No barrier per
-//            task, no cross-block hand-off: the kernel boundary publishes.
+//            row once and keeps, per block (4096-logit chunks) or per wave (16384-logit
+//            chunks, no block-wide reduction), GREEDY (max, first argmax) or SAMPLE (max m,
+//            S = sum exp((l - m)/T) in fp64).  No cross-block hand-off: the kernel
+//            boundary publishes.
 //   greedy   GREEDY, one block per sequence: argmax per row from the chunk partials,
 //            the matching prefix J and the extra token z_J.
 //   alpha    optional: sum_x min(p_i, q_i) per draft position (one more read of the rows).
 //   resample SAMPLE, grid (chunk, sequence).  Every block re-derives the row statistics
 //            and the ratio tests from the chunk partials in a fixed order (so all blocks
 //            agree on J), then sums the residual mass of its chunk of the two rows at
-//            position J; the last block finds the chunk holding u* Z and scans it in
-//            token order for the extra token.
+//            position J and its 256-token segment sums; the last block finds the chunk
+//            holding u* Z, then the segment, then (one wave, token order) the extra token.
 // Exponentials of the bulk run in fp32; every sum, the CDF and the decided p(x), q(x)
 // are fp64.
 #include "vocab_row.h"

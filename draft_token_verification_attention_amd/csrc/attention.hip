@@ -12,14 +12,18 @@
 //     packing, row n = i * G + g), so every K/V tile is read once for all of them.
 //   * A block owns (sequence, KV head, row tile of 32*NWR rows, key split).  Its waves
 //     form NWK key groups x NWR row waves: a key group stages 32-key tiles of K and V
-//     through LDS (coalesced 16-byte loads, register double buffering), and each row
-//     wave of the group computes S^T = K Q^T and O^T += V^T P^T for its 32 rows on MFMA.
-//   * Online softmax in registers (log2 domain).  Key groups merge through LDS; key
-//     splits merge through a workspace by the last-arriving block (log-sum-exp combine).
+//     through LDS (coalesced 16-byte loads, the next tile in registers while the current
+//     one is computed), and each row wave of the group computes S^T = K Q^T and
+//     O^T += V^T P^T for its 32 rows on MFMA.
+//   * Online softmax in registers (log2 domain, lazily moved reference max).  Key groups
+//     merge through LDS; key splits are merged by attn_combine_kernel (log-sum-exp).
 //   * Tiles the mask hides from every row of the block are never loaded (tree nodes of
 //     other branches; chain positions after the block's last row).
-//   * Blocks are numbered so that all blocks of one (sequence, KV head) run on the same
-//     XCD (workgroup id mod 8), keeping its partial results and K/V reuse in one L2.
+//   * One row wave (decode): a plain (split, KV head, sequence) grid, K/V streamed with
+//     nontemporal loads; with a dense cache and a grid of at most one block per CU, each
+//     wave loads its first tile before the sequence length arrives.  Several row waves:
+//     all blocks of one KV head are numbered onto one XCD (workgroup id mod 8), so the row
+//     tiles that re-read its K/V share that XCD's L2.
 // fp32 path: one wave per query row, lanes across the head dimension (VALU).
 #include "sv_common.h"
 
