@@ -16,11 +16,15 @@
 //   greedy   GREEDY, one block per sequence: argmax per row from the chunk partials,
 //            the matching prefix J and the extra token z_J.
 //   alpha    optional: sum_x min(p_i, q_i) per draft position (one more read of the rows).
-//   resample SAMPLE, grid (chunk, sequence).  Every block re-derives the row statistics
-//            and the ratio tests from the chunk partials in a fixed order (so all blocks
-//            agree on J), then sums the residual mass of its chunk of the two rows at
-//            position J and its 256-token segment sums; the last block finds the chunk
-//            holding u* Z, then the segment, then (one wave, token order) the extra token.
+//   resample SAMPLE, grid (chunk, sequence); small calls in the vector layout take
+//            2048-logit chunks of their own (half the bytes per block to wait for once J
+//            is known).  Every block re-derives the row statistics and the ratio tests from
+//            the chunk partials in a fixed order (so all blocks agree on J), then sums the
+//            residual mass of its chunk of the two rows at position J and its 256-token
+//            segment sums; the last block reads every segment sum at once and finds the
+//            segment holding u* Z (block-wide scan), then (one wave, token order) the extra
+//            token.  When the residual has no mass, or the layout is not the vector one, it
+//            finds the chunk first, then the token inside it.
 // Exponentials of the bulk run in fp32; every sum, the CDF and the decided p(x), q(x)
 // are fp64.
 #include "vocab_row.h"
@@ -39,6 +43,10 @@ constexpr int kMinChunk = 16 * kRowThreads;
 template <int PER>
 constexpr int parts_per_chunk() { return PER >= 64 ? kRowThreads / kWave : 1; }
 constexpr int kMaxPartsPerChunk = kRowThreads / kWave;
+// The residual draw of a small call (vector layout) takes 2048-logit chunks: twice the
+// blocks of the stats chunks, half the bytes each block waits for once J is known.
+constexpr int kResPer = 8;
+constexpr int kResChunk = kResPer * kRowThreads;
 
 struct RowPart {
     float m;
@@ -61,6 +69,7 @@ struct AcceptWs {
 
 struct AcceptArgs {
     int B, gamma, V, rows, nchunk;
+    int rnchunk;       // chunks of the residual draw (its own chunk size)
     int npart;         // row partials: nchunk x waves per block
     int sample;
     float kf;          // log2(e) / T in fp32, for the bulk exponentials
@@ -92,8 +101,8 @@ static WsLayout accept_layout(int B, int gamma, int V)
     o += align256((size_t)B * rows * nchunk * kMaxPartsPerChunk * sizeof(RowPart));
     L.u = o;
     o += align256((size_t)B * (gamma + 1) * sizeof(double));
-    L.res = o;
-    o += align256((size_t)B * nchunk * sizeof(ResPart));
+    L.res = o;  // per resample chunk: the smallest chunks are kResChunk tokens
+    o += align256((size_t)B * (((size_t)V + kResChunk - 1) / kResChunk) * sizeof(ResPart));
     L.seg = o;  // 256-token segments: enough for either chunk size
     o += align256((size_t)B * (nchunk + 3) * 16 * sizeof(double));
     L.apart = o;
@@ -101,6 +110,10 @@ static WsLayout accept_layout(int B, int gamma, int V)
     L.total = o;
     return L;
 }
+
+// Segment sums a thread of the resample's last block reads at once (sequences of up to
+// 256 x 4 segments of 256 tokens take the one-pass segment search)
+constexpr int kSegPerThread = 4;
 
 // Row partials staged in LDS by the decide steps (dynamic shared memory, at most this many)
 constexpr int kMaxStaged = 2048;
@@ -370,23 +383,23 @@ __global__ __launch_bounds__(kRowThreads, 2) void accept_resample_kernel(AcceptA
     __shared__ double dscr[2 * (kRowThreads / kWave)];
     __shared__ double scan[kRowThreads];
     __shared__ int iscr[kRowThreads / kWave];
-    __shared__ int last_flag, s_chunk, s_usep, firstbad, bad;
+    __shared__ int last_flag, s_chunk, s_usep, s_seg0, firstbad, bad;
+    __shared__ int s_whit[kRowThreads / kWave], s_wlast[kRowThreads / kWave];
     __shared__ double s_base, s_target, s_uextra;
     const int c = blockIdx.x, b = blockIdx.y;
     const int g = a.gamma;
 
-    // drafted tokens and their logits (two dependent loads, hidden behind the staging of
-    // the row partials and the row statistics)
-    int x = 0;
-    float lpx = 0.0f, lqx = 0.0f;
-    double u_mine = 0.0;  // thread i < gamma: ratio test i; thread gamma: the extra token
-    if (threadIdx.x < g) {
-        x = a.tokens[(int64_t)b * g + threadIdx.x];
-        const int xc = min(max(x, 0), a.V - 1);  // a bad token is flagged below, its logit unused
-        lpx = a.target[((int64_t)b * (g + 1) + threadIdx.x) * a.V + xc];
-        lqx = a.draft[((int64_t)b * g + threadIdx.x) * a.V + xc];
-    }
-    if ((int)threadIdx.x <= g) u_mine = w.u[(int64_t)b * (g + 1) + threadIdx.x];
+    // drafted tokens and their logits (two dependent loads, hidden behind the staging of the
+    // row partials and the row statistics; a bad token is flagged below, its logit unused),
+    // and the uniforms: thread i < gamma ratio test i, thread gamma the extra token.
+    // Unconditional loads from clamped slots: a load under a branch would be waited for at
+    // the branch, before the partials are asked for.
+    const int ti = min((int)threadIdx.x, g - 1);
+    const int x = a.tokens[(int64_t)b * g + ti];
+    const int xc = min(max(x, 0), a.V - 1);
+    const float lpx = a.target[((int64_t)b * (g + 1) + ti) * a.V + xc];
+    const float lqx = a.draft[((int64_t)b * g + ti) * a.V + xc];
+    const double u_mine = w.u[(int64_t)b * (g + 1) + min((int)threadIdx.x, g)];
     if (threadIdx.x == 0) {
         firstbad = g;
         bad = 0;
@@ -459,7 +472,7 @@ __global__ __launch_bounds__(kRowThreads, 2) void accept_resample_kernel(AcceptA
     }
     if (VEC) {
         const int wv = threadIdx.x / kWave;
-        double *sg = w.seg + ((int64_t)b * a.nchunk + c) * kPerThread;
+        double *sg = w.seg + ((int64_t)b * a.rnchunk + c) * kPerThread;
 #pragma unroll
         for (int k4 = 0; k4 < kPerThread / 4; ++k4) {
             const double t = wave_sum(r4[k4]);
@@ -468,16 +481,130 @@ __global__ __launch_bounds__(kRowThreads, 2) void accept_resample_kernel(AcceptA
     }
     block_sum2(rs, ps, dscr);
     if (threadIdx.x == 0) {
-        st_coherent(&w.res[(int64_t)b * a.nchunk + c].r, rs);
-        st_coherent(&w.res[(int64_t)b * a.nchunk + c].p, ps);
+        st_coherent(&w.res[(int64_t)b * a.rnchunk + c].r, rs);
+        st_coherent(&w.res[(int64_t)b * a.rnchunk + c].p, ps);
     }
-    if (!arrive_last(&w.cnt[b], a.nchunk, &last_flag)) return;
+    if (!arrive_last(&w.cnt[b], a.rnchunk, &last_flag)) return;
 
-    // last block: locate the chunk holding u* Z (wave 0), then scan it in token order
+    // wave 0, the residual's 256-token segment starting at token seg0 holding u* Z, whose
+    // mass before it is sbase: the token inside it (every lane returns it)
+    auto token_in_segment = [&](int seg0, double sbase, double target) -> int {
+        const int lane = threadIdx.x;
+        const int e0 = seg0 + 4 * lane;  // this lane's four tokens
+        const int ec = min(e0, a.V - 4);
+        const float4 fp = *reinterpret_cast<const float4 *>(prow + ec);
+        const float4 fq = *reinterpret_cast<const float4 *>((qrow ? qrow : prow) + ec);
+        const bool in = e0 < a.V;
+        double wt[4];
+        wt[0] = in ? fmax(0.0, p_of(fp.x) - q_of(fq.x)) : 0.0;
+        wt[1] = in ? fmax(0.0, p_of(fp.y) - q_of(fq.y)) : 0.0;
+        wt[2] = in ? fmax(0.0, p_of(fp.z) - q_of(fq.z)) : 0.0;
+        wt[3] = in ? fmax(0.0, p_of(fp.w) - q_of(fq.w)) : 0.0;
+        const double lsum = ((wt[0] + wt[1]) + wt[2]) + wt[3];
+        const double c0 = sbase + wave_scan_incl(lsum, 0.0, OpAdd()) - lsum;
+        int hit = -1, lastpos = -1;
+        double pre = c0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            pre += wt[j];
+            if (hit < 0 && pre > target && wt[j] > 0.0) hit = j;
+            if (wt[j] > 0.0) lastpos = j;
+        }
+        const uint64_t hm = __ballot(c0 <= target && hit >= 0);
+        const uint64_t lm = __ballot(lastpos >= 0);
+        int y;
+        if (hm) {
+            const int hl = __ffsll((unsigned long long)hm) - 1;
+            y = seg0 + 4 * hl + lane_value(hit, hl);
+        } else if (lm) {  // rounding: the segment's running sum stops short of target
+            const int ll = 63 - __clzll((unsigned long long)lm);
+            y = seg0 + 4 * ll + lane_value(lastpos, ll);
+        } else {
+            y = seg0;  // no mass in the segment at all (cannot happen for the segment found)
+        }
+        return y;
+    };
+
+    // last block, residual with mass (the common case): the block reads every 256-token
+    // segment sum of the sequence at once (kSegPerThread consecutive ones per thread, so in
+    // token order, coalesced), scans them, finds the segment holding u* Z_r with Z_r their
+    // total, and wave 0 finds the token inside it: two memory round trips
+    if (VEC && a.rnchunk * kPerThread <= kRowThreads * kSegPerThread) {
+        static_assert(kSegPerThread == 4 && kPerThread % kSegPerThread == 0, "whole threads of segments");
+        const int t = threadIdx.x, lane = t % kWave, wv = t / kWave;
+        const int nseg = a.rnchunk * kPerThread;
+        const bool live = t * kSegPerThread < nseg;
+        // two unconditional 16-byte loads from a clamped thread, zeroed past the end
+        const double2 *sg = reinterpret_cast<const double2 *>(
+            w.seg + (int64_t)b * nseg + (int64_t)min(t, nseg / kSegPerThread - 1) * kSegPerThread);
+        const double2 h0 = sg[0], h1 = sg[1];
+        const double v[kSegPerThread] = {live ? h0.x : 0.0, live ? h0.y : 0.0, live ? h1.x : 0.0, live ? h1.y : 0.0};
+        const double ts = ((v[0] + v[1]) + v[2]) + v[3];
+        const double incl_w = wave_scan_incl(ts, 0.0, OpAdd());
+        if (lane == kWave - 1) dscr[wv] = incl_w;
+        __syncthreads();
+        double wbase = 0.0, zr = 0.0;
+#pragma unroll
+        for (int k = 0; k < kRowThreads / kWave; ++k) {
+            if (k < wv) wbase += dscr[k];
+            zr += dscr[k];
+        }
+        if (zr > 0.0) {  // the same in every thread
+            const double incl = wbase + incl_w;
+            const double target = s_uextra * zr;
+            const uint64_t hit = __ballot(ts > 0.0 && incl > target);
+            const uint64_t pos = __ballot(ts > 0.0);
+            if (lane == 0) {
+                s_whit[wv] = hit ? wv * kWave + __ffsll((unsigned long long)hit) - 1 : kRowThreads;
+                s_wlast[wv] = pos ? wv * kWave + 63 - __clzll((unsigned long long)pos) : -1;
+            }
+            __syncthreads();
+            int th = kRowThreads, tl = -1;
+#pragma unroll
+            for (int k = 0; k < kRowThreads / kWave; ++k) {
+                th = min(th, s_whit[k]);
+                tl = max(tl, s_wlast[k]);
+            }
+            // rounding can leave every running sum at or below target: the last thread with mass
+            if (t == (th < kRowThreads ? th : tl)) {
+                double cum = incl - ts;
+                int sj = -1, lastj = 0;
+                double sbase = cum, lastbase = cum;
+#pragma unroll
+                for (int j = 0; j < kSegPerThread; ++j) {
+                    if (v[j] > 0.0) {
+                        if (sj < 0 && cum + v[j] > target) {
+                            sj = j;
+                            sbase = cum;
+                        }
+                        lastj = j;
+                        lastbase = cum;
+                    }
+                    cum += v[j];
+                }
+                if (sj < 0) {
+                    sj = lastj;
+                    sbase = lastbase;
+                }
+                s_seg0 = 256 * (t * kSegPerThread + sj);
+                s_base = sbase;
+                s_target = target;
+            }
+            __syncthreads();
+            if (t < kWave) {
+                const int y = token_in_segment(s_seg0, s_base, s_target);
+                if (lane == 0) a.out_tokens[(int64_t)b * (g + 1) + J] = y;
+            }
+            return;
+        }
+        __syncthreads();  // no residual mass: the chunk path below, with p
+    }
+
+    // otherwise: locate the chunk holding u* Z (wave 0), then scan it in token order
     if (threadIdx.x < kWave) {
-        const ResPart *rp = w.res + (int64_t)b * a.nchunk;
+        const ResPart *rp = w.res + (int64_t)b * a.rnchunk;
         double zr = 0.0, zp = 0.0;
-        for (int cc = threadIdx.x; cc < a.nchunk; cc += kWave) {
+        for (int cc = threadIdx.x; cc < a.rnchunk; cc += kWave) {
             zr += rp[cc].r;
             zp += rp[cc].p;
         }
@@ -487,7 +614,7 @@ __global__ __launch_bounds__(kRowThreads, 2) void accept_resample_kernel(AcceptA
         const double target = s_uextra * (usep ? zp : zr);
         int chunk;
         double cbase;
-        wave_find_chunk(a.nchunk, target, [&](int cc) { return usep ? rp[cc].p : rp[cc].r; }, chunk, cbase);
+        wave_find_chunk(a.rnchunk, target, [&](int cc) { return usep ? rp[cc].p : rp[cc].r; }, chunk, cbase);
         if (threadIdx.x == 0) {
             s_chunk = chunk;
             s_base = cbase;
@@ -505,7 +632,7 @@ __global__ __launch_bounds__(kRowThreads, 2) void accept_resample_kernel(AcceptA
         if (threadIdx.x < kWave) {
             const int lane = threadIdx.x;
             const double target = s_target;
-            const double *sg = w.seg + ((int64_t)b * a.nchunk + cs) * kPerThread;
+            const double *sg = w.seg + ((int64_t)b * a.rnchunk + cs) * kPerThread;
             const double v = lane < kPerThread ? sg[lane] : 0.0;
             const double incl = wave_scan_incl(v, 0.0, OpAdd());
             const double excl = s_base + incl - v;
@@ -514,39 +641,7 @@ __global__ __launch_bounds__(kRowThreads, 2) void accept_resample_kernel(AcceptA
             // rounding can leave every running sum at or below target: the last segment with mass
             const int sseg = pass ? __ffsll((unsigned long long)pass) - 1
                                   : (posm ? 63 - __clzll((unsigned long long)posm) : 0);
-            const double sbase = lane_value(excl, sseg);
-            const int e0 = cbase + 256 * sseg + 4 * lane;  // this lane's four tokens
-            const int ec = min(e0, a.V - 4);
-            const float4 fp = *reinterpret_cast<const float4 *>(prow + ec);
-            const float4 fq = *reinterpret_cast<const float4 *>((qrow ? qrow : prow) + ec);
-            const bool in = e0 < a.V;
-            double wt[4];
-            wt[0] = in ? fmax(0.0, p_of(fp.x) - q_of(fq.x)) : 0.0;
-            wt[1] = in ? fmax(0.0, p_of(fp.y) - q_of(fq.y)) : 0.0;
-            wt[2] = in ? fmax(0.0, p_of(fp.z) - q_of(fq.z)) : 0.0;
-            wt[3] = in ? fmax(0.0, p_of(fp.w) - q_of(fq.w)) : 0.0;
-            const double lsum = ((wt[0] + wt[1]) + wt[2]) + wt[3];
-            const double c0 = sbase + wave_scan_incl(lsum, 0.0, OpAdd()) - lsum;
-            int hit = -1, lastpos = -1;
-            double pre = c0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                pre += wt[j];
-                if (hit < 0 && pre > target && wt[j] > 0.0) hit = j;
-                if (wt[j] > 0.0) lastpos = j;
-            }
-            const uint64_t hm = __ballot(c0 <= target && hit >= 0);
-            const uint64_t lm = __ballot(lastpos >= 0);
-            int y;
-            if (hm) {
-                const int hl = __ffsll((unsigned long long)hm) - 1;
-                y = cbase + 256 * sseg + 4 * hl + lane_value(hit, hl);
-            } else if (lm) {  // rounding: the segment's running sum stops short of target
-                const int ll = 63 - __clzll((unsigned long long)lm);
-                y = cbase + 256 * sseg + 4 * ll + lane_value(lastpos, ll);
-            } else {
-                y = cbase;  // no mass in the segment at all (cannot happen for the segment found)
-            }
+            const int y = token_in_segment(cbase + 256 * sseg, lane_value(excl, sseg), target);
             if (lane == 0) a.out_tokens[(int64_t)b * (g + 1) + J] = y;
         }
         return;
@@ -588,6 +683,21 @@ static int stats_resident_blocks()
     return cached[dev];
 }
 
+// The residual draw: small calls in the vector layout on kResChunk chunks, others on the
+// stats chunks.
+template <bool VEC, int PER>
+static hipError_t launch_resample(const AcceptArgs &a0, const AcceptWs &w, hipStream_t s, size_t lds)
+{
+    AcceptArgs a = a0;
+    if constexpr (VEC && PER == 16) {
+        a.rnchunk = (a.V + kResChunk - 1) / kResChunk;
+        return launch(accept_resample_kernel<true, kResPer>, dim3(a.rnchunk, a.B), s, a, w, lds);
+    } else {
+        a.rnchunk = a.nchunk;
+        return launch(accept_resample_kernel<VEC, PER>, dim3(a.rnchunk, a.B), s, a, w, lds);
+    }
+}
+
 template <bool VEC, int PER>
 static sv_status run_accept(const AcceptArgs &a, const AcceptWs &w, hipStream_t s, bool sample, bool alpha)
 {
@@ -606,8 +716,7 @@ static sv_status run_accept(const AcceptArgs &a, const AcceptWs &w, hipStream_t 
     if (launch(accept_stats_kernel<VEC, true, PER>, gstats, s, a, w) != hipSuccess) return SV_ERR_HIP;
     if (alpha && launch(accept_alpha_kernel<VEC, PER>, dim3(a.nchunk, a.gamma, a.B), s, a, w) != hipSuccess)
         return SV_ERR_HIP;
-    return launch(accept_resample_kernel<VEC, PER>, dim3(a.nchunk, a.B), s, a, w, lds) == hipSuccess ? SV_OK
-                                                                                                  : SV_ERR_HIP;
+    return launch_resample<VEC, PER>(a, w, s, lds) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
 }  // namespace
@@ -669,6 +778,7 @@ extern "C" sv_status sv_spec_accept(const sv_accept_desc *d, void *workspace, si
     const bool wide = (int64_t)a.B * a.rows * big_chunks >= 1024;
     a.nchunk = wide ? big_chunks : (d->V + kMinChunk - 1) / kMinChunk;
     a.npart = a.nchunk * (wide ? parts_per_chunk<64>() : parts_per_chunk<16>());
+    a.rnchunk = a.nchunk;
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
     return wide ? (vec ? run_accept<true, 64>(a, w, s, sample, d->alpha != nullptr)
