@@ -401,16 +401,14 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
         // against the stale reference stay below 2^kLazyLog2 (exact in the final l and O).
         const float m_tile = mloc * a.scale_log2;
         const float m_new = (m_tile <= m_run + kLazyLog2) ? m_run : m_tile;
-        float alpha = 1.0f;
+        // Branch-free: a row with no visible key yet (m_new = -inf) subtracts 0 instead, so
+        // its weights are exp2(-inf) = 0 and its alpha 0 (l and O are still zero there); a
+        // branch made the compiler zero all 16 weights ahead of it on every tile.
+        const float m_sub = (m_new == -INFINITY) ? 0.0f : m_new;
+        const float alpha = exp2_fast(m_run - m_sub);  // m_run == -inf gives 0
         float p[16];
-        if (m_new == -INFINITY) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) p[v] = 0.0f;
-        } else {
-            alpha = exp2_fast(m_run - m_new);  // m_run == -inf gives 0
-#pragma unroll
-            for (int v = 0; v < 16; ++v) p[v] = exp2_fast(fmaf(sv[v], a.scale_log2, -m_new));
-        }
+        for (int v = 0; v < 16; ++v) p[v] = exp2_fast(fmaf(sv[v], a.scale_log2, -m_sub));
         float psum = 0.0f;
 #pragma unroll
         for (int v = 0; v < 16; ++v) psum += p[v];

@@ -45,7 +45,7 @@ def _assert_parity(ref, got, label=""):
     assert np.all(got["status"] == 0)
 
 
-@pytest.mark.parametrize("V", [1, 2, 7, 1000, 1023, 4096, 4097, 12289])
+@pytest.mark.parametrize("V", [1, 2, 7, 1000, 1023, 4096, 4097, 5000, 12289])
 @pytest.mark.parametrize("gamma", [1, 5, 16])
 def test_sample_parity_shapes(V, gamma):
     B = 64
