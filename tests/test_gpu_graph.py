@@ -69,3 +69,71 @@ def test_graph_replays_match_eager():
         sv.sv_spec_accept(sv.SV_SAMPLE, dev_array(other_acc["target"]), dev_array(other_acc["draft"]),
                           dev_array(other_acc["draft_tokens"]), 0.8, 5, rep)
         torch.cuda.synchronize()
+
+
+def test_tree_round_graph_replays_match_eager():
+    """Mask build, tree attention and the sampled level-by-level walk (one launch per
+    depth, completion counters in a shared workspace) captured once and replayed."""
+    parents = synth.random_tree(3, 150, branch_p=0.8)
+    n = len(parents)
+    depth = np.zeros(n, np.int64)
+    for i in range(1, n):
+        depth[i] = depth[parents[i]] + 1 if parents[i] >= 0 else 0
+    md = int(depth.max())
+    P = 700
+    att = synth.attention_inputs(4, B=1, n_q=n, Hq=16, Hkv=4, D=128, prefix_len=[P], dtype="bf16", qkv_scale=1.0)
+    lg = synth.tree_logits(4, 1, n, 9000, 3.0)
+    toks = synth.node_tokens(4, lg, parents)
+    par = dev_array(np.asarray(parents, np.int32))
+    q, k, v = dev_array(att["q"], True), dev_array(att["k"], True), dev_array(att["v"], True)
+    kv_off, pl = dev_array(att["kv_off"]), dev_array(att["prefix_len"])
+    lgd, tkd = dev_array(lg), dev_array(toks.astype(np.int32))
+    words = (n + 31) // 32
+    bits = torch.empty((n, words), dtype=torch.int32, device="cuda")
+    dep = torch.empty(n, dtype=torch.int32, device="cuda")
+    pos = torch.empty(n, dtype=torch.int64, device="cuda")
+    mst = torch.empty(1, dtype=torch.int32, device="cuda")
+    out = torch.empty(q.shape, dtype=q.dtype, device="cuda")
+    alen = torch.empty(1, dtype=torch.int32, device="cuda")
+    path = torch.empty((1, md + 1), dtype=torch.int32, device="cuda")
+    otok = torch.empty((1, md + 1), dtype=torch.int32, device="cuda")
+    wst = torch.empty(1, dtype=torch.int32, device="cuda")
+    ad = sv.attn_desc(q, k, v, kv_off, pl, Hkv=4, max_prefix=P, scale=1 / math.sqrt(128), kv_sh=att["kv_sh"],
+                      kv_st=att["kv_st"], out=out, tree_bits=bits)
+    wd = sv.walk_desc(sv.SV_SAMPLE, lgd, tkd, par, md, 0.7, 17, 2, None, alen, path, otok, wst)
+    wa = torch.zeros(sv.lib.sv_verify_attention_workspace(ctypes.byref(ad)) + 256, dtype=torch.uint8, device="cuda")
+    ww = torch.zeros(sv.lib.sv_tree_walk_workspace(ctypes.byref(wd)) + 256, dtype=torch.uint8, device="cuda")
+    pa = ctypes.c_void_p(wa.data_ptr() + (-wa.data_ptr()) % 256)
+    pw = ctypes.c_void_p(ww.data_ptr() + (-ww.data_ptr()) % 256)
+
+    def launch(stream):
+        assert sv.lib.sv_build_tree_mask(ctypes.c_void_p(par.data_ptr()), n, P, ctypes.c_void_p(bits.data_ptr()),
+                                         ctypes.c_void_p(dep.data_ptr()), ctypes.c_void_p(pos.data_ptr()),
+                                         ctypes.c_void_p(mst.data_ptr()), stream) == 0
+        assert sv.lib.sv_verify_attention(ctypes.byref(ad), pa, wa.numel() - 256, stream) == 0
+        assert sv.lib.sv_tree_walk(ctypes.byref(wd), pw, ww.numel() - 256, stream) == 0
+
+    launch(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    outs = (bits, dep, pos, out, alen, path, otok, wst)
+    ref = tuple(t.clone() for t in outs)
+    assert int(mst.cpu()[0]) == 0 and int(wst.cpu()[0]) == 0
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        launch(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    other = synth.tree_logits(5, 2, 40, 3000, 3.0)
+    other_par = synth.random_tree(6, 40, branch_p=0.7)
+    other_tok = synth.node_tokens(6, other, other_par)
+    for rep in range(5):
+        for t in outs:
+            t.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for j, (t, r) in enumerate(zip(outs, ref)):
+            assert torch.equal(t, r), (rep, j)
+        # eager walks and masks on other inputs (the binding's own workspace) between replays
+        sv.sv_tree_walk(sv.SV_SAMPLE, dev_array(other), dev_array(other_tok.astype(np.int32)),
+                        dev_array(np.asarray(other_par, np.int32)), 6, 0.9, rep, 0)
+        sv.sv_build_tree_mask(dev_array(np.asarray(other_par, np.int32)), 11)
+        torch.cuda.synchronize()
