@@ -66,8 +66,8 @@ def main():
         copy_calibration()
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (see DESIGN.md on sharding); "
-              "run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the library runs on one device per process and has no "
+              "multi-GPU path; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
     import draft_token_verification_attention_amd as sv
