@@ -45,7 +45,7 @@ extern "C" {
 typedef enum sv_status {
     SV_OK = 0,
     SV_ERR_INVALID_ARG = 1,  /* a null pointer, a negative size, inconsistent shapes      */
-    SV_ERR_UNSUPPORTED = 2,  /* a valid request this build does not implement (e.g. D=96) */
+    SV_ERR_UNSUPPORTED = 2,  /* a valid request the library does not implement (e.g. D=96) */
     SV_ERR_WORKSPACE = 3,    /* workspace pointer null or smaller than *_workspace()     */
     SV_ERR_HIP = 4           /* a HIP launch failed                                       */
 } sv_status;
