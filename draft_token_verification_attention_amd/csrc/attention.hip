@@ -750,12 +750,14 @@ static bool plan_attention(const sv_attn_desc *d, Plan &p)
         sk = ((int64_t)d->split_keys + unit - 1) / unit * unit;
     } else if (p.variant == 1) {
         // Few query rows: splitting keys is cheap (a partial is at most 32 rows).  Aim at
-        // about 4096 splits in all, which balances uneven sequence lengths over the 256 CUs
+        // about 2048 splits in all, which balances uneven sequence lengths over the 256 CUs
         // (two 4-wave blocks per CU), keeping splits between 256 keys (shorter ones cost
         // more in partials and launch than they gain) and 4096.
         // Splits are a power of two long (measured: 1024-key splits stream a 64-sequence
-        // batch a third faster than 1056-key ones).
-        const int64_t want = (Tmax * groups + 4095) / 4096;
+        // batch a third faster than 1056-key ones).  On that batch (8197-key bound):
+        // 2048-key splits 198.6 + 12.9 us (main + combine), 1024-key 200.0 + 14.6, 4096-key
+        // 224.6 + 9.3, 512-key 212.4 + 18.3.
+        const int64_t want = (Tmax * groups + 2047) / 2048;
         sk = 256;
         while (sk * 2 <= want && sk < 4096) sk *= 2;
     } else {
