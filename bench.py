@@ -10,7 +10,9 @@ the tree workloads, the mask build and the tree walk).  The default workload is 
 Inputs are resident in HBM before the timed region.  Each step reads a different one of
 R device copies of the inputs (R * working set >= 1 GiB), so the 256 MB Infinity Cache
 cannot serve repeated reads.  Kernel durations come from HIP events recorded on the
-stream the library launches on.
+stream the library launches on; the main attention kernel's (the roofline's) from events
+that hipExtLaunchKernel sets to the kernel's own start and end, the span a kernel trace
+reports.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--no-cpu]
 """
@@ -27,6 +29,8 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+# how the roofline's kernel duration is taken
+KERNEL_SPAN = "kernel start to end: hipExtLaunchKernel events on the launch stream, separate eager pass"
 
 
 def parse():
@@ -156,27 +160,41 @@ def main():
     ms_per_step = timed_steps(launch, R, args, sh)
 
     # Kernel durations: HIP events on the launch stream, same K steps.  The library's
-    # measurement hook records one more event right after the main attention kernel, so the
-    # attention call splits into its main kernel and the split combine.
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # measurement hooks record one more event right after the main attention kernel (the
+    # attention call splits into its main kernel and the split combine) and give the main
+    # kernel's own start and end (hipExtLaunchKernel events: the span a kernel trace reports,
+    # without the dispatch ahead of the kernel).
+    # Two passes over the same K steps: the first with plain launches (call and combine
+    # intervals), the second with the kernel-span events (whose launch path adds host work
+    # between the events around the call).
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     for e in events:
-        e[1].record()  # creates the event the library will record
+        for k in (1, 4, 5):
+            e[k].record()  # creates the events the library records
     torch.cuda.synchronize()
-    for i in range(args.steps):
-        sv.lib.sv_set_attention_mark(ctypes.c_void_p(events[i][1].cuda_event))
-        ev = events[i]
-        ev[0].record()
-        st = sv.lib.sv_verify_attention(ctypes.byref(adescs[(args.warmup + i) % R]), pa, ws_a, sh)
-        ev[2].record()
-        st2 = sv.lib.sv_spec_accept(ctypes.byref(sdescs[(args.warmup + i) % R]), ps, ws_s, sh)
-        ev[3].record()
-        if st or st2:
-            raise RuntimeError("launch failed: %d %d" % (st, st2))
-    sv.lib.sv_set_attention_mark(None)
-    torch.cuda.synchronize()
-    main_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    for span in (False, True):
+        for i in range(args.steps):
+            ev = events[i]
+            if span:
+                sv.lib.sv_set_attention_timing(ctypes.c_void_p(ev[4].cuda_event), ctypes.c_void_p(ev[5].cuda_event))
+            else:
+                sv.lib.sv_set_attention_mark(ctypes.c_void_p(ev[1].cuda_event))
+                ev[0].record()
+            st = sv.lib.sv_verify_attention(ctypes.byref(adescs[(args.warmup + i) % R]), pa, ws_a, sh)
+            if not span:
+                ev[2].record()
+            st2 = sv.lib.sv_spec_accept(ctypes.byref(sdescs[(args.warmup + i) % R]), ps, ws_s, sh)
+            if not span:
+                ev[3].record()
+            if st or st2:
+                raise RuntimeError("launch failed: %d %d" % (st, st2))
+        sv.lib.sv_set_attention_mark(None)
+        sv.lib.sv_set_attention_timing(None, None)
+        torch.cuda.synchronize()
+    main_ms = float(np.mean([e[4].elapsed_time(e[5]) for e in events]))
+    main_call_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
     comb_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
-    att_ms = main_ms + comb_ms
+    att_ms = float(np.mean([e[0].elapsed_time(e[2]) for e in events]))
     acc_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
 
     drafts = B * gamma
@@ -206,9 +224,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(main_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(main_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl),
                      "kernel": "attn_bf16_kernel", "kernel_ms": round(main_ms, 5),
-                     "algorithmic_bytes": att_bytes},
-        "kernels_ms": {"attn_bf16_kernel": round(main_ms, 5), "attn_combine_kernel": round(comb_ms, 5),
-                       "sv_spec_accept": round(acc_ms, 5)},
+                     "timing": KERNEL_SPAN, "algorithmic_bytes": att_bytes},
+        "kernels_ms": {"attn_bf16_kernel": round(main_ms, 5), "attn_bf16_kernel_with_dispatch": round(main_call_ms, 5),
+                       "attn_combine_kernel": round(comb_ms, 5), "sv_spec_accept": round(acc_ms, 5)},
         "attention": {"kernel_ms": round(att_ms, 5), "algorithmic_bytes": att_bytes,
                       "achieved_GBs": round(att_bytes / (att_ms * 1e-3) / 1e9, 1)},
         "accept": {"kernel_ms": round(acc_ms, 5), "algorithmic_bytes": acc_bytes,
@@ -337,17 +355,26 @@ def bench_tree(args, cfg, wl, dev):
     torch.cuda.synchronize()
     ms_per_step = timed_steps(launch, R, args, sh)
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
     for e in events:
-        e[2].record()
+        for k in (2, 5, 6):
+            e[k].record()  # creates the events the library records
     torch.cuda.synchronize()
+    # two passes, as for the chain workloads: plain launches, then the kernel-span events
     for i in range(args.steps):
         sv.lib.sv_set_attention_mark(ctypes.c_void_p(events[i][2].cuda_event))
         launch((args.warmup + i) % R, sh, events[i])
     sv.lib.sv_set_attention_mark(None)
     torch.cuda.synchronize()
+    for i in range(args.steps):
+        sv.lib.sv_set_attention_timing(ctypes.c_void_p(events[i][5].cuda_event),
+                                       ctypes.c_void_p(events[i][6].cuda_event))
+        launch((args.warmup + i) % R, sh)
+    sv.lib.sv_set_attention_timing(None, None)
+    torch.cuda.synchronize()
     mask_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
-    main_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    main_ms = float(np.mean([e[5].elapsed_time(e[6]) for e in events]))
+    main_call_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
     comb_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
     walk_ms = float(np.mean([e[3].elapsed_time(e[4]) for e in events]))
 
@@ -361,10 +388,12 @@ def bench_tree(args, cfg, wl, dev):
     walk_rows = int(to_host_int(acc_len)) + 1
     mfma = {"bound": "mfma", "achieved": round(main_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(main_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": measured_traffic(wl),
-            "kernel": "attn_bf16_kernel", "kernel_ms": round(main_ms, 5), "algorithmic_flops": att_flops}
+            "kernel": "attn_bf16_kernel", "kernel_ms": round(main_ms, 5), "timing": KERNEL_SPAN,
+            "algorithmic_flops": att_flops}
     hbm = {"bound": "hbm", "achieved": round(main_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
            "frac": round(main_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl),
-           "kernel": "attn_bf16_kernel", "kernel_ms": round(main_ms, 5), "algorithmic_bytes": att_bytes}
+           "kernel": "attn_bf16_kernel", "kernel_ms": round(main_ms, 5), "timing": KERNEL_SPAN,
+           "algorithmic_bytes": att_bytes}
     line = {
         "metric": "draft tokens verified/sec on 1 MI355X; achieved HBM GB/s as % of peak",
         "value": round(value, 1), "unit": "draft tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -376,6 +405,7 @@ def bench_tree(args, cfg, wl, dev):
         "roofline": mfma if wl == 5 else hbm,
         "roofline_other": hbm if wl == 5 else mfma,
         "kernels_ms": {"tree_mask_kernel": round(mask_ms, 5), "attn_bf16_kernel": round(main_ms, 5),
+                       "attn_bf16_kernel_with_dispatch": round(main_call_ms, 5),
                        "attn_combine_kernel": round(comb_ms, 5), "sv_tree_walk": round(walk_ms, 5)},
         "walk": {"kernel_ms": round(walk_ms, 5), "rows_visited": walk_rows,
                  "algorithmic_bytes": 4 * V * walk_rows},
@@ -432,8 +462,8 @@ def cpu_baseline_tree(att, cfg, wl, parents, toks, scale, seconds):
 # counter reading half the bytes of a plain copy of known size on this GPU), from the
 # rocprofv3 --pmc runs summarized under profiles/, and the SHA-256 of the attention source
 # they were taken on: a changed kernel reports null until the counters are taken again.
-TRAFFIC = {2: 19146691, 4: 1110649685}
-TRAFFIC_SRC_SHA256 = "41343a964f64d4810dbe1726ce9f183c60ae66ba25737a8aeae8715f433c35c3"
+TRAFFIC = {2: 19146466, 4: 1110643185}
+TRAFFIC_SRC_SHA256 = "a3fbfc017d9e28f113e062b109e7c4e44c72da9319b949d8abe0daeaf2fe09e8"
 
 
 def measured_traffic(wl):

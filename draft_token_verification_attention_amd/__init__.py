@@ -54,7 +54,7 @@ class sv_walk_desc(ctypes.Structure):
 
 EXPORTS = ("sv_build_tree_mask", "sv_verify_attention_workspace", "sv_verify_attention",
            "sv_spec_accept_workspace", "sv_spec_accept", "sv_tree_walk_workspace", "sv_tree_walk",
-           "sv_set_attention_mark", "sv_status_string")
+           "sv_set_attention_mark", "sv_set_attention_timing", "sv_status_string")
 
 
 def _load():
@@ -78,6 +78,8 @@ def _load():
     L.sv_tree_walk.restype = ctypes.c_int
     L.sv_set_attention_mark.argtypes = [_P]
     L.sv_set_attention_mark.restype = ctypes.c_int
+    L.sv_set_attention_timing.argtypes = [_P, _P]
+    L.sv_set_attention_timing.restype = ctypes.c_int
     L.sv_status_string.argtypes = [ctypes.c_int]
     L.sv_status_string.restype = ctypes.c_char_p
     return L

@@ -25,6 +25,8 @@
 //     all blocks of one KV head are numbered onto one XCD (workgroup id mod 8), so the row
 //     tiles that re-read its K/V share that XCD's L2.
 // fp32 path: one wave per query row, lanes across the head dimension (VALU).
+#include <hip/hip_ext.h>
+
 #include "sv_common.h"
 
 namespace {
@@ -824,17 +826,30 @@ static sv_status check_attention(const sv_attn_desc *d)
 }
 
 static void *g_mark_event = nullptr;  // sv_set_attention_mark
+static void *g_time_start = nullptr;  // sv_set_attention_timing
+static void *g_time_stop = nullptr;
+
+// The main attention kernel's launch; with the timing hook set, through hipExtLaunchKernel,
+// whose events take the kernel's own start and end (the times a kernel trace reports).
+template <typename K>
+static void launch_main(K kernel, dim3 grid, dim3 block, hipStream_t s, const AttnArgs &a)
+{
+    if (g_time_start || g_time_stop)
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, s, (hipEvent_t)g_time_start, (hipEvent_t)g_time_stop, 0, a);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, 0, s, a);
+}
 
 template <int DH, int NWR, int NWK>
 static hipError_t launch_variant(const Plan &p, const AttnArgs &a, hipStream_t s)
 {
     if constexpr (NWR == 1) {
         if (p.spec)
-            hipLaunchKernelGGL((attn_bf16_kernel<DH, 1, NWK, true>), dim3(p.nsplit, a.Hkv, a.B), dim3(64 * NWK), 0, s, a);
+            launch_main(attn_bf16_kernel<DH, 1, NWK, true>, dim3(p.nsplit, a.Hkv, a.B), dim3(64 * NWK), s, a);
         else
-            hipLaunchKernelGGL((attn_bf16_kernel<DH, 1, NWK, false>), dim3(p.nsplit, a.Hkv, a.B), dim3(64 * NWK), 0, s, a);
+            launch_main(attn_bf16_kernel<DH, 1, NWK, false>, dim3(p.nsplit, a.Hkv, a.B), dim3(64 * NWK), s, a);
     } else {
-        hipLaunchKernelGGL((attn_bf16_kernel<DH, NWR, NWK, false>), dim3(p.blocks), dim3(64 * NWR * NWK), 0, s, a);
+        launch_main(attn_bf16_kernel<DH, NWR, NWK, false>, dim3(p.blocks), dim3(64 * NWR * NWK), s, a);
     }
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && g_mark_event) e = hipEventRecord((hipEvent_t)g_mark_event, s);
@@ -958,5 +973,12 @@ extern "C" sv_status sv_verify_attention(const sv_attn_desc *d, void *workspace,
 extern "C" sv_status sv_set_attention_mark(void *event)
 {
     g_mark_event = event;
+    return SV_OK;
+}
+
+extern "C" sv_status sv_set_attention_timing(void *start_event, void *stop_event)
+{
+    g_time_start = start_event;
+    g_time_stop = stop_event;
     return SV_OK;
 }

@@ -244,6 +244,14 @@ SV_API sv_status sv_tree_walk(const sv_walk_desc *desc, void *workspace, size_t 
 /* Always returns SV_OK; a failed record shows up as SV_ERR_HIP from the call.          */
 SV_API sv_status sv_set_attention_mark(void *event);
 
+/* Measurement hook for benchmarks.  When either event (a hipEvent_t) is not NULL, every     */
+/* later sv_verify_attention call launches its main attention kernel so that `start_event`  */
+/* takes the kernel's start time and `stop_event` its end time (the span a kernel trace     */
+/* reports, without the dispatch ahead of the kernel).  Either may be NULL; both NULL turn  */
+/* the hook off.  Process-wide setting without synchronization: set it from the launching   */
+/* thread.  Always returns SV_OK; a failed launch shows up as SV_ERR_HIP from the call.      */
+SV_API sv_status sv_set_attention_timing(void *start_event, void *stop_event);
+
 /* Human-readable name of a status code (static storage). */
 SV_API const char *sv_status_string(sv_status status);
 

@@ -20,15 +20,16 @@ def declared_symbols():
 
 def test_library_exports_every_declared_symbol():
     names = declared_symbols()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     for n in names:
         assert hasattr(sv.lib, n), n
     assert set(names) == set(sv.EXPORTS)
 
 
 def test_attention_mark_hook_is_host_only():
-    # setting or clearing the measurement hook touches no device
+    # setting or clearing the measurement hooks touches no device
     assert sv.lib.sv_set_attention_mark(None) == 0
+    assert sv.lib.sv_set_attention_timing(None, None) == 0
 
 
 def test_status_strings():
