@@ -98,6 +98,20 @@ def test_walk_parity_random_trees(mode, seed, n, V, br):
 
 
 @pytest.mark.parametrize("mode", [GREEDY, SAMPLE])
+@pytest.mark.parametrize("fan", [100, 300])
+def test_walk_wide_fanout(mode, fan):
+    """A root with more children than the walk gathers in LDS (300) and with fewer (100),
+    each child with one grandchild: the child lookup takes both of its forms."""
+    parents = np.array([-1] + [0] * fan + list(range(1, fan + 1)), dtype=np.int64)
+    B = 16
+    lg = synth.tree_logits(fan, B, len(parents), 700, 3.0)
+    toks = synth.node_tokens(fan, lg, parents)
+    for step in range(2):
+        ref, got = _walk_both(mode, lg, toks, parents, 0.8, seed=9, step=step)
+        _assert_walk_parity(ref, got, "fan %d step %d" % (fan, step))
+
+
+@pytest.mark.parametrize("mode", [GREEDY, SAMPLE])
 def test_walk_workload_medusa(mode):
     cfg = synth.WORKLOADS[3]
     parents, paths = synth.build_tree(cfg)
