@@ -733,9 +733,13 @@ static bool plan_attention(const sv_attn_desc *d, Plan &p)
     }
     const int G = d->Hq / d->Hkv;
     p.rows = d->n_q * G;
+    // Up to 512 rows, 64-row blocks also serve whenever they pad fewer rows than 128-row
+    // ones (measured, 4 query heads per KV head, 2048-key cache: 260 rows 24.7 -> 22.8 us,
+    // 132 rows 19.8 -> 18.0 us; 16384 keys: 260 rows 74.4 -> 70.0 us, 132 rows 46.3 -> 47.4 us).
+    const int pad64 = (p.rows + 63) / 64 * 64 - p.rows, pad128 = (p.rows + 127) / 128 * 128 - p.rows;
     if (p.rows <= 32) {
         p.variant = 1; p.NWR = 1; p.NWK = 4;
-    } else if (p.rows <= 64) {
+    } else if (p.rows <= 64 || (p.rows <= 512 && pad64 < pad128)) {
         p.variant = 2; p.NWR = 2; p.NWK = 2;
     } else {
         p.variant = 3; p.NWR = 4; p.NWK = 1;
