@@ -462,8 +462,8 @@ def cpu_baseline_tree(att, cfg, wl, parents, toks, scale, seconds):
 # counter reading half the bytes of a plain copy of known size on this GPU), from the
 # rocprofv3 --pmc runs summarized under profiles/, and the SHA-256 of the attention source
 # they were taken on: a changed kernel reports null until the counters are taken again.
-TRAFFIC = {2: 19146475, 4: 1110645339}
-TRAFFIC_SRC_SHA256 = "babf6530c4637bfbf4fdfb1c74a65e9fa4fb4c3bc379027abf757f8f7cfa4ea9"
+TRAFFIC = {2: 19146477, 4: 1110644912}
+TRAFFIC_SRC_SHA256 = "b8eb2f65936caab8ae51137e71cbd4b04890d738471eb81e06f327b1645abe21"
 
 
 def measured_traffic(wl):

@@ -733,13 +733,18 @@ static bool plan_attention(const sv_attn_desc *d, Plan &p)
     }
     const int G = d->Hq / d->Hkv;
     p.rows = d->n_q * G;
-    // Up to 512 rows, 64-row blocks also serve whenever they pad fewer rows than 128-row
-    // ones (measured, 4 query heads per KV head, 2048-key cache: 260 rows 24.7 -> 22.8 us,
-    // 132 rows 19.8 -> 18.0 us; 16384 keys: 260 rows 74.4 -> 70.0 us, 132 rows 46.3 -> 47.4 us).
+    // 64-row blocks (two key waves each: half the tiles per wave, twice the row tiles) beat
+    // 128-row ones while the cache is short, and for a few hundred rows when they pad fewer
+    // rows.  Measured, random trees with 4 query heads per KV head (128-row -> 64-row us):
+    //   2048-key cache: 516 rows 37.3 -> 28.0, 1028 rows 51.4 -> 46.3, 4100 rows 153.5 -> 114.3;
+    //   4096: 516 rows 47.4 -> 39.2, 1028 rows 66.7 -> 68.7, 4100 rows 223.0 -> 202.0;
+    //   8192: 1028 rows 98.8 -> 115.6, 4100 rows 356.0 -> 372.8;
+    //   16384: 260 rows 74.4 -> 70.0, 516 rows 106.1 -> 110.2, 4100 rows 658.9 -> 703.6.
     const int pad64 = (p.rows + 63) / 64 * 64 - p.rows, pad128 = (p.rows + 127) / 128 * 128 - p.rows;
+    const bool short_cache = (int64_t)d->max_prefix + d->n_q <= 6144;
     if (p.rows <= 32) {
         p.variant = 1; p.NWR = 1; p.NWK = 4;
-    } else if (p.rows <= 64 || (p.rows <= 512 && pad64 < pad128)) {
+    } else if (p.rows <= 64 || (p.rows <= 8192 && short_cache) || (p.rows <= 320 && pad64 < pad128)) {
         p.variant = 2; p.NWR = 2; p.NWK = 2;
     } else {
         p.variant = 3; p.NWR = 4; p.NWK = 1;
