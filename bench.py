@@ -462,8 +462,8 @@ def cpu_baseline_tree(att, cfg, wl, parents, toks, scale, seconds):
 # counter reading half the bytes of a plain copy of known size on this GPU), from the
 # rocprofv3 --pmc runs summarized under profiles/, and the SHA-256 of the attention source
 # they were taken on: a changed kernel reports null until the counters are taken again.
-TRAFFIC = {2: 19146477, 4: 1110644912}
-TRAFFIC_SRC_SHA256 = "b8eb2f65936caab8ae51137e71cbd4b04890d738471eb81e06f327b1645abe21"
+TRAFFIC = {2: 19146497, 4: 1110646812}
+TRAFFIC_SRC_SHA256 = "3398e7dc8c32dedb2dfd4c930e773e685664d3d34f6f1cbbd09753005442452b"
 
 
 def measured_traffic(wl):

@@ -773,18 +773,27 @@ static bool plan_attention(const sv_attn_desc *d, Plan &p)
         while (sk * 2 <= want && sk < 4096) sk *= 2;
     } else {
         // Many rows per block: a partial (32 NWR rows x (D + 4) fp32, written and read back)
-        // costs about as much as the K/V of 130 keys, so split only until every CU has a
-        // block, and never below 256 keys (measured on the 64-node Medusa tree, 2048-key
-        // cache: 128-key splits 54 us per round, 256-key 45 us, 512-key 47 us).
+        // costs about as much as the K/V of 130 keys, so a short cache splits only until
+        // every CU has a block, and never below 256 keys (measured on the 64-node Medusa
+        // tree, 2048-key cache: 128-key splits 54 us per round, 256-key 45 us, 512-key 47 us).
+        // Long caches split further, to about four blocks per CU with splits of at least
+        // 1024 keys (their blocks otherwise walk thousands of tiles one after another).
+        // Measured on random trees with a 16384-key cache, 516 / 1028 / 2052 / 4100 rows:
+        // 106.2 / 180.0 / 344.4 / 656.5 us with the short-cache rule, 77.9 / 136.8 / 237.4 /
+        // 452.2 us with this one; on a 2048-key cache the short-cache rule stays ahead
+        // (516 rows: 27.9 vs 31.6 us).
         const int64_t cus = device_cu_count();
-        if (groups >= cus) {
+        const bool long_cache = Tmax > 6144;
+        const int64_t target = long_cache ? 4 * cus : cus;
+        if (groups >= target) {
             sk = Tmax;
         } else {
-            const int64_t nsp = (cus + groups - 1) / groups;
+            const int64_t nsp = (target + groups - 1) / groups;
             sk = (Tmax + nsp - 1) / nsp;
         }
         sk = (sk + unit - 1) / unit * unit;
-        if (sk < 256) sk = 256;
+        const int64_t min_sk = long_cache ? 1024 : 256;
+        if (sk < min_sk) sk = min_sk;
     }
     if ((Tmax + sk - 1) / sk > kMaxSplits) sk = ((Tmax + kMaxSplits - 1) / kMaxSplits + unit - 1) / unit * unit;
     if (sk > (int64_t)kMaxTiles * kTileKeys) return false;
