@@ -462,8 +462,8 @@ def cpu_baseline_tree(att, cfg, wl, parents, toks, scale, seconds):
 # counter reading half the bytes of a plain copy of known size on this GPU), from the
 # rocprofv3 --pmc runs summarized under profiles/, and the SHA-256 of the attention source
 # they were taken on: a changed kernel reports null until the counters are taken again.
-TRAFFIC = {2: 19146497, 4: 1110646812}
-TRAFFIC_SRC_SHA256 = "3398e7dc8c32dedb2dfd4c930e773e685664d3d34f6f1cbbd09753005442452b"
+TRAFFIC = {2: 19146478, 4: 1110645633}
+TRAFFIC_SRC_SHA256 = "0d52f469f7adb75d24c70fd2a545eee0cdce1203f64ebe2d81b0adc902cb8db5"
 
 
 def measured_traffic(wl):
