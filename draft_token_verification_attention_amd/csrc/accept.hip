@@ -778,7 +778,9 @@ extern "C" sv_status sv_spec_accept(const sv_accept_desc *d, void *workspace, si
     const bool vec = (d->V % 4 == 0) && (((uintptr_t)d->target_logits & 15) == 0) &&
                      (!sample || ((uintptr_t)d->draft_logits & 15) == 0);
     const int big_chunks = (d->V + 4 * kMinChunk - 1) / (4 * kMinChunk);
-    const bool wide = (int64_t)a.B * a.rows * big_chunks >= 1024;
+    // (threshold measured: calls of 704 and 896 big chunks ran 9-21% faster on the large
+    // chunks, calls of 544 up to 15% slower)
+    const bool wide = (int64_t)a.B * a.rows * big_chunks >= 640;
     a.nchunk = wide ? big_chunks : (d->V + kMinChunk - 1) / kMinChunk;
     a.npart = a.nchunk * (wide ? parts_per_chunk<64>() : parts_per_chunk<16>());
     a.rnchunk = a.nchunk;
