@@ -160,6 +160,28 @@ def test_workload_cartesian_tree_sampled_rows():
     _compare(inp, 1 / math.sqrt(cfg["D"]), tree_bits=bits, rows=rows)
 
 
+@pytest.mark.parametrize("n,P", [(129, 2048), (129, 9000), (33, 9000)], ids=["short-64row", "long-128row", "long-pad64"])
+def test_tree_default_plans(n, P):
+    """Default plans of the many-row forms: 64-row blocks on a short cache, 128-row blocks
+    split to several blocks per CU on a long one, 64-row blocks padding fewer rows there."""
+    parents = synth.random_tree(n + P, n, branch_p=0.6)
+    bits, _, _ = oracle.tree_mask(parents, P)
+    inp = synth.attention_inputs(n + 1, B=1, n_q=n, Hq=32, Hkv=8, D=128, prefix_len=[P], dtype="bf16", qkv_scale=1.0)
+    r = np.random.default_rng(2)
+    nodes = np.concatenate([np.arange(4), r.integers(0, n, 60), np.arange(n - 4, n)])
+    rows = np.stack([np.zeros_like(nodes), nodes, r.integers(0, 32, len(nodes))], 1)
+    _compare(inp, 1 / math.sqrt(128), tree_bits=bits, rows=rows)
+
+
+@pytest.mark.parametrize("B,P", [(16, 1000), (8, 3000), (4, 5000)], ids=["no-split", "1024-split-B8", "1024-split-B4"])
+def test_chain_batch_default_plans(B, P):
+    """Default plans of the one-row-wave form for batches: one split per sequence on a short
+    cache, at least 1024-key splits on longer ones."""
+    inp = synth.attention_inputs(B * 7 + P, B=B, n_q=6, Hq=32, Hkv=8, D=128, prefix_len=[P - 3 * b for b in range(B)],
+                                 dtype="bf16", qkv_scale=1.0)
+    _compare(inp, 1 / math.sqrt(128), rows=rows_of_sample(inp, 120))
+
+
 DENSE_SHAPES = [
     # B, n_q, Hq, Hkv, D, prefix lengths, max_prefix (token slots per sequence = max_prefix + n_q)
     (1, 6, 32, 8, 128, [4096], 4096),     # the 8B chain: first tiles loaded before the length
