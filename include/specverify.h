@@ -23,7 +23,9 @@
  *     every call leaves them zero again (partial results live after them).  So one
  *     workspace, zero-filled once, may serve any sequence of calls of any entry point and
  *     shape, provided the calls do not overlap in time (e.g. they share one stream).
- *   - The library allocates no memory and keeps no global state.
+ *   - The library allocates no memory.  Its only global state is the two benchmark
+ *     hooks at the end of this header (event handles, off by default); no result
+ *     depends on them.
  *   - No C++ exception crosses this interface.
  */
 #ifndef SPECVERIFY_H
