@@ -140,6 +140,21 @@ def test_output_law_chi_square_on_gpu():
     assert abs(J.mean() - np.cumprod(alpha).sum()) < 4 * J.std() / math.sqrt(N)
 
 
+@pytest.mark.parametrize("B,gamma,V", [(1, 5, 128256), (4, 3, 5000), (16, 2, 1000), (1, 64, 4097), (64, 1, 7)])
+def test_alpha_pass_changes_no_decision(B, gamma, V):
+    """Asking for alpha adds its own pass over the rows between the statistics and the
+    residual draw; the accepted lengths and tokens stay the same, bit for bit, over several
+    rounds."""
+    a = synth.accept_inputs(70 + B, B=B, gamma=gamma, V=V, target_var=3.0, noise_var=1.0, tau=0.8)
+    for step in range(4):
+        args = (SAMPLE, dev_array(a["target"]), dev_array(a["draft"]), dev_array(a["draft_tokens"]), 0.8, 9, step)
+        one = to_host(sv.sv_spec_accept(*args))
+        two = to_host(sv.sv_spec_accept(*args, want_alpha=True))
+        assert np.array_equal(one["accept_len"], two["accept_len"])
+        assert np.array_equal(one["out_tokens"], two["out_tokens"])
+        assert np.all(one["status"] == 0) and np.all(two["status"] == 0)
+
+
 def test_deterministic_repeats():
     a = synth.accept_inputs(2, B=1, gamma=5, V=128256, target_var=3.0, noise_var=1.5, tau=0.8)
     args = (SAMPLE, dev_array(a["target"]), dev_array(a["draft"]), dev_array(a["draft_tokens"]), 0.8, 7)
