@@ -462,8 +462,8 @@ def cpu_baseline_tree(att, cfg, wl, parents, toks, scale, seconds):
 # counter reading half the bytes of a plain copy of known size on this GPU), from the
 # rocprofv3 --pmc runs summarized under profiles/, and the SHA-256 of the attention source
 # they were taken on: a changed kernel reports null until the counters are taken again.
-TRAFFIC = {2: 19146478, 4: 1110645633}
-TRAFFIC_SRC_SHA256 = "0d52f469f7adb75d24c70fd2a545eee0cdce1203f64ebe2d81b0adc902cb8db5"
+TRAFFIC = {2: 19146491, 4: 1110644725}
+TRAFFIC_SRC_SHA256 = "f0181d9ba00dab5aead0be6b439625055d682b4177dd223d0d4fe6d7c20343a0"
 
 
 def measured_traffic(wl):

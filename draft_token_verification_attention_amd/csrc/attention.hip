@@ -62,7 +62,6 @@ struct AttnArgs {
     int B, n_q, Hq, Hkv, G, rows, RT, KG, nsplit, split_keys;
     float scale_log2;
     float *part;  // [KG*RT][nsplit][32*NWR][D + 4]: o[D], max, sum, pad (16-byte rows)
-    int *cnt;     // [KG*RT]
 };
 
 // 16-byte K/V load.  NT: with the nontemporal hint, for tiles that no other block re-reads
@@ -814,7 +813,9 @@ static bool plan_attention(const sv_attn_desc *d, Plan &p)
     if (blocks > 0x7fffffff) return false;
     p.blocks = (unsigned)blocks;
     const size_t D = (size_t)d->D;
-    if ((int64_t)p.KG * p.RT > kMaxCounters) return false;
+    // (the one-row-wave grid puts sequences on its third dimension)
+    if (p.variant == 1 && d->B > 65535) return false;
+    // the counter area every call's workspace starts with (unused here)
     p.cnt_bytes = kCounterBytes;
     // (with one split the kernel stores its output directly; the partial area stays unused)
     p.part_bytes = align256((size_t)p.KG * p.RT * p.nsplit * rows_blk * (D + 4) * sizeof(float));
@@ -975,7 +976,6 @@ extern "C" sv_status sv_verify_attention(const sv_attn_desc *d, void *workspace,
     a.nsplit = p.nsplit;
     a.split_keys = p.split_keys;
     a.scale_log2 = d->scale * kLog2e;
-    a.cnt = p.total ? (int *)workspace : nullptr;
     a.part = p.part_bytes ? (float *)((char *)workspace + p.cnt_bytes) : nullptr;
 
     hipStream_t s = (hipStream_t)stream;

@@ -125,6 +125,7 @@ SV_API sv_status sv_build_tree_mask(const int32_t *parents, int32_t n, int32_t p
 /* Supported: D in {64, 128}; Hq % Hkv == 0; n_q >= 1.  bf16 also needs 16-byte aligned  */
 /* q, k, v, strides, kv_sb and kv_off[b] that are multiples of 8 elements, and out and  */
 /* its strides aligned to 4 elements (else SV_ERR_UNSUPPORTED; kv_off is not checked).   */
+/* bf16 calls with at most 32 query rows per KV head (n_q x Hq/Hkv) take B <= 65535.     */
 /* ---------------------------------------------------------------------------------- */
 typedef struct sv_attn_desc {
     sv_dtype dtype;

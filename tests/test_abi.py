@@ -71,6 +71,7 @@ def _attn(**kw):
     (dict(kv_off=None, kv_sb=1001), sv.SV_ERR_UNSUPPORTED),      # dense cache, unaligned stride
     (dict(kv_off=None, kv_sb=4102 * 1024), sv.SV_ERR_WORKSPACE), # dense cache: valid
     ({}, sv.SV_ERR_WORKSPACE),                                   # valid, but no workspace
+    (dict(B=70000), sv.SV_ERR_UNSUPPORTED),                      # few rows per KV head: grid's sequence limit
 ])
 def test_attention_argument_checks(change, status):
     d = _attn(**change)
