@@ -193,7 +193,7 @@ def spec_accept(mode: int, target, draft, draft_tokens, temperature: float, seed
 
 
 def tree_walk(mode: int, logits, tokens, parents, temperature: float, seed: int, step: int = 0,
-              stream_ids=None, max_depth=None):
+              stream_ids=None, max_depth=None, handle=None, allow_too_deep: bool = False):
     """-> dict(accept_len [B], path [B][max_depth+1], out_tokens [B][max_depth+1], flags [B])."""
     lg = _c(logits, np.float32)
     B, n, V = lg.shape
@@ -207,8 +207,9 @@ def tree_walk(mode: int, logits, tokens, parents, temperature: float, seed: int,
     path = np.zeros((B, max_depth + 1), dtype=np.int32)
     out = np.zeros((B, max_depth + 1), dtype=np.int32)
     flags = np.zeros(B, dtype=np.int32)
-    st = lib().orc_tree_walk(int(mode), B, n, V, int(max_depth), float(temperature), _p(lg), _p(tk), _p(par),
-                             int(seed), int(step), _p(sid), _p(acc), _p(path), _p(out), _p(flags))
-    if st != 0:
+    st = (handle or lib()).orc_tree_walk(int(mode), B, n, V, int(max_depth), float(temperature), _p(lg), _p(tk),
+                                         _p(par), int(seed), int(step), _p(sid), _p(acc), _p(path), _p(out),
+                                         _p(flags))
+    if st != 0 and not (st == 3 and allow_too_deep):
         raise ValueError("orc_tree_walk status %d" % st)
-    return dict(accept_len=acc, path=path, out_tokens=out, flags=flags)
+    return dict(accept_len=acc, path=path, out_tokens=out, flags=flags, status=st)

@@ -74,7 +74,14 @@ ORC_EXPORT double orc_uniform(uint64_t seed, uint64_t c0, uint64_t step, uint64_
 
 #define ORC_TAG_ACCEPT 0x53560001ULL
 #define ORC_TAG_WALK   0x53560002ULL
-#define ORC_NEAR       1e-6
+/* Near-threshold windows.  A ratio test is near when |u - p/q| < 1e-6 (the tolerance
+ * of accept decisions).  A draw u*Z from weights in units of probability mass
+ * (p, or the residual (p - q)+ with p, q normalized) is near when it lies within 1e-10 of
+ * either cumulative sum that brackets the chosen token: the fp64 sums over a 128K-token row
+ * are exact to about 1e-11, so a draw farther away than this is decided by the arithmetic
+ * alone.  (A window of 1e-6 Z flagged a sixth of all draws at 128K tokens.)              */
+#define ORC_NEAR_RATIO 1e-6
+#define ORC_NEAR_DRAW  1e-10
 
 /* ------------------------------------------------------------------------- */
 /* Token tree -> ancestor-or-self mask, depth and position ids.               */
@@ -209,7 +216,7 @@ static int32_t argmax_row(const float *logits, int32_t V)
 
 /* Inverse CDF in ascending token-id order: the smallest y with C_y > u * Z,
  * C the running sum of w, Z the total.  *near is set when u*Z lies within
- * 1e-6*Z of C_{y-1} or C_y (a draw whose token could flip under rounding).
+ * ORC_NEAR_DRAW of C_{y-1} or C_y (a draw whose token could flip under rounding).
  * Returns -1 when Z is not positive.                                          */
 static int32_t inverse_cdf(const double *w, int32_t V, double u, int32_t *near)
 {
@@ -228,7 +235,7 @@ static int32_t inverse_cdf(const double *w, int32_t V, double u, int32_t *near)
         for (int32_t x = V - 1; x >= 0; --x) if (w[x] > 0.0) { y = x; break; }
         prev = c;
     }
-    if (near) *near = (fabs(target - prev) < ORC_NEAR * z) || (fabs(c - target) < ORC_NEAR * z);
+    if (near) *near = (fabs(target - prev) < ORC_NEAR_DRAW) || (fabs(c - target) < ORC_NEAR_DRAW);
     return y;
 }
 
@@ -258,7 +265,7 @@ static int32_t inverse_cdf(const double *w, int32_t V, double u, int32_t *near)
 /* Outputs: accept_len[B]; out_tokens[B][gamma+1] (J drafts, the extra token,  */
 /* then -1); alpha[B][gamma] = sum_x min(p_i, q_i) when non-null (SAMPLE);     */
 /* flags[B]: bit0 = an evaluated ratio test had |u - p/q| < 1e-6,              */
-/* bit1 = the extra draw lay within 1e-6*Z of a CDF boundary.                  */
+/* bit1 = the extra draw lay within 1e-10 of a CDF boundary.                   */
 /* ------------------------------------------------------------------------- */
 ORC_EXPORT int32_t orc_spec_accept(int32_t mode, int32_t B, int32_t gamma, int32_t V, float temperature,
                                    const float *target, const float *draft, const int32_t *draft_tokens,
@@ -311,7 +318,7 @@ ORC_EXPORT int32_t orc_spec_accept(int32_t mode, int32_t B, int32_t gamma, int32
             const int32_t x = xb[J];
             const double u = orc_uniform(seed, (uint64_t)J, step, stream, ORC_TAG_ACCEPT);
             const double px = p[x], qx = q[x];
-            if (qx > 0.0 && fabs(u - px / qx) < ORC_NEAR) fl |= 1;
+            if (qx > 0.0 && fabs(u - px / qx) < ORC_NEAR_RATIO) fl |= 1;
             if (!(u * qx < px)) break;
         }
         /* the extra token */
@@ -351,8 +358,9 @@ ORC_EXPORT int32_t orc_spec_accept(int32_t mode, int32_t B, int32_t gamma, int32
 /* go down level by level until no child matches.                              */
 /* Outputs: accept_len[B] = J; path[B][max_depth+1] = (0, n_1, ..., n_J, -1..);*/
 /* out_tokens[B][max_depth+1] = (tokens of n_1..n_J, y, -1..); flags[B] bit1   */
-/* = some draw lay within 1e-6*Z of a CDF boundary.                            */
-/* Returns 0; 3 if a walk would pass max_depth; 2 on a bad token/parent.       */
+/* = some draw lay within 1e-10 of a CDF boundary.                             */
+/* Returns 0; 3 if a walk would pass max_depth (that walk stops at the node  */
+/* at depth max_depth and emits its choice y); 2 on a bad token/parent.       */
 /* ------------------------------------------------------------------------- */
 ORC_EXPORT int32_t orc_tree_walk(int32_t mode, int32_t B, int32_t n, int32_t V, int32_t max_depth,
                                  float temperature, const float *logits, const int32_t *tokens,
@@ -391,9 +399,10 @@ ORC_EXPORT int32_t orc_tree_walk(int32_t mode, int32_t B, int32_t n, int32_t V, 
             for (int32_t c = v + 1; c < n; ++c)
                 if (parents[c] == v && tk[c] == y) { child = c; break; }
             if (child < 0) { ob[d] = y; break; }
-            if (d + 1 > max_depth) {
+            if (d + 1 > max_depth) {   /* no room below: the choice at v is emitted */
 #pragma omp atomic write
                 status = 3;
+                ob[d] = y;
                 break;
             }
             ob[d] = tk[child];

@@ -9,17 +9,7 @@ import pytest
 
 import oracle
 from conftest import read_golden
-
-
-def _numpy_block(counter, key):
-    """NumPy's Philox advances its counter before producing a block, so block(c)
-    comes from a generator whose counter is c - 1 (256-bit little-endian decrement)."""
-    c = [int(x) for x in counter]
-    val = sum(w << (64 * i) for i, w in enumerate(c))
-    val = (val - 1) % (1 << 256)
-    prev = np.array([(val >> (64 * i)) & ((1 << 64) - 1) for i in range(4)], dtype=np.uint64)
-    g = np.random.Philox(counter=prev, key=np.array(key, dtype=np.uint64))
-    return g.random_raw(4).astype(np.uint64)
+from np_philox import block as _numpy_block
 
 
 def test_known_answer():
