@@ -4,21 +4,30 @@
 A step is one pass of the whole hot path over one batch of synthetic input: the verify
 attention over every sequence's KV cache, then acceptance over the vocabulary (and, for
 the tree workloads, the mask build and the tree walk).  The default workload is the
-8B-like chain: batch 1, gamma = 5 drafts, 4096 cached tokens, 32 query / 8 KV heads of
-128, bf16; vocabulary 128256 with fp32 logits, temperature 0.8, speculative sampling.
+batched chain: 64 sequences, gamma = 4 drafts each, cached contexts uniform in
+[512, 8192], 32 query / 8 KV heads of 128, bf16; vocabulary 128256 with fp32 logits,
+temperature 1.0, speculative sampling with a Philox stream per sequence.
 
 Inputs are resident in HBM before the timed region.  Each step reads a different one of
-R device copies of the inputs (R * working set >= 1 GiB), so the 256 MB Infinity Cache
-cannot serve repeated reads.  Kernel durations come from HIP events recorded on the
-stream the library launches on; the main attention kernel's (the roofline's) from events
-that hipExtLaunchKernel sets to the kernel's own start and end, the span a kernel trace
-reports.
+R device copies of the inputs (R * working set >= 1.1 GB), so the 256 MB Infinity Cache
+cannot serve repeated reads.  The timed steps replay HIP graphs of consecutive steps.
+Kernel durations come from HIP events on the stream the library launches on: the
+attention call takes events in its descriptor that hipExtLaunchKernel sets to its
+kernels' own start and end (the span a kernel trace reports).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--no-cpu]
+The line also carries: the roofline of the attention pass (main kernel + split combine,
+the dominant cost), the CPU oracle timed on the host (all cores and one thread, on a
+bounded sample) with a parity verdict of the GPU step against it (decisions bit-exact
+except near-threshold draws, which are counted; attention max-abs error), and, unless
+--no-extra, short runs of the 8B-like chain and the full Cartesian tree (its MFMA
+utilisation against the bf16 dense peak).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4] [--no-cpu] [--no-extra]
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import math
 import os
@@ -29,8 +38,8 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
-# how the roofline's kernel duration is taken
-KERNEL_SPAN = "kernel start to end: hipExtLaunchKernel events on the launch stream, separate eager pass"
+KERNEL_SPAN = ("kernel start to end: hipExtLaunchKernel events on the launch stream, "
+               "separate eager pass over the same steps")
 
 
 def parse():
@@ -38,8 +47,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
+    ap.add_argument("--no-extra", action="store_true", help="skip the short runs of the other workloads")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--split-keys", type=int, default=0)
     ap.add_argument("--kv-cache", choices=["auto", "ragged"], default="auto",
@@ -64,6 +74,26 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": 4 * n, "launches": 5}))
 
 
+def host_threads() -> int:
+    """Host threads this process may use: its CPU affinity, capped by OMP_NUM_THREADS."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
+
+
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -74,186 +104,101 @@ def main():
               "multi-GPU path; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
-    import draft_token_verification_attention_amd as sv
-    import synth
+    import draft_token_verification_attention_amd  # noqa: F401  (fails loudly without the library)
 
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    cfg = synth.WORKLOADS[args.workload]
-    wl = args.workload
-    if cfg["kind"] != "chain":
-        return bench_tree(args, cfg, wl, dev)
-
-    # ---------------- inputs (host, seeded) ----------------
-    B, gamma = cfg["B"], cfg["gamma"]
-    n_q = gamma + 1
-    Hq, Hkv, D, V, tau = cfg["Hq"], cfg["Hkv"], cfg["D"], cfg["V"], cfg["tau"]
-    P = synth.prefix_lengths(wl, cfg)
-    max_prefix = int(cfg.get("P_hi", int(P.max())))
-    att = synth.attention_inputs(wl, B=B, n_q=n_q, Hq=Hq, Hkv=Hkv, D=D, prefix_len=P, dtype=cfg["dtype"],
-                                 qkv_scale=cfg["qkv_scale"])
-    acc = synth.accept_inputs(wl, B=B, gamma=gamma, V=V, target_var=cfg["target_var"],
-                              noise_var=cfg["noise_var"], tau=tau)
-    bf = cfg["dtype"] == "bf16"
-
-    def to_dev(a, bf16=False):
-        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16) if bf16 else np.ascontiguousarray(a))
-        t = t.view(torch.bfloat16) if bf16 else t
-        return t.to(dev)
-
-    base = dict(q=to_dev(att["q"], bf), k=to_dev(att["k"], bf), v=to_dev(att["v"], bf),
-                target=to_dev(acc["target"]), draft=to_dev(acc["draft"]))
-    # One sequence: a dense cache (kv_off NULL; the sequence owns max_prefix + n_q token
-    # slots, which is what the packed buffer holds).  A batch: the packed ragged cache.
-    dense = B == 1 and int(P[0]) == max_prefix and args.kv_cache != "ragged"
-    kv_off = None if dense else to_dev(att["kv_off"].astype(np.int64))
-    kv_sb = (max_prefix + n_q) * Hkv * D if dense else 0
-    prefix = to_dev(P.astype(np.int32))
-    toks = to_dev(acc["draft_tokens"].astype(np.int32))
-    set_bytes = sum(t.numel() * t.element_size() for t in base.values())
-    R = max(1, int(math.ceil(args.rotate_bytes / set_bytes)))
-    copies = [base] + [{k: t.clone() for k, t in base.items()} for _ in range(R - 1)]
-    scale = 1.0 / math.sqrt(D)
-    esz = 2 if bf else 4
-
-    # outputs and descriptors prepared once: the timed loop only launches
-    out = torch.empty((B, n_q, Hq, D), dtype=base["q"].dtype, device=dev)
-    acc_len = torch.empty(B, dtype=torch.int32, device=dev)
-    out_tok = torch.empty((B, n_q), dtype=torch.int32, device=dev)
-    status = torch.empty(B, dtype=torch.int32, device=dev)
-    import ctypes
-    adescs, sdescs = [], []
-    for c in copies:
-        adescs.append(sv.attn_desc(c["q"], c["k"], c["v"], kv_off, prefix, Hkv=Hkv, max_prefix=max_prefix,
-                                   scale=scale, kv_sh=att["kv_sh"], kv_st=att["kv_st"], out=out,
-                                   split_keys=args.split_keys, kv_sb=kv_sb))
-        sdescs.append(sv.accept_desc(sv.SV_SAMPLE, c["target"], c["draft"], toks, tau, 1000 + wl, 0, None,
-                                     acc_len, out_tok, None, status))
-    ws_a = sv.lib.sv_verify_attention_workspace(ctypes.byref(adescs[0]))
-    ws_s = sv.lib.sv_spec_accept_workspace(ctypes.byref(sdescs[0]))
-    ws_att = torch.zeros(ws_a + 256, dtype=torch.uint8, device=dev)
-    ws_acc = torch.zeros(ws_s + 256, dtype=torch.uint8, device=dev)
-    pa = ctypes.c_void_p(ws_att.data_ptr() + (-ws_att.data_ptr()) % 256)
-    ps = ctypes.c_void_p(ws_acc.data_ptr() + (-ws_acc.data_ptr()) % 256)
-    stream = torch.cuda.current_stream(dev)
-    sh = ctypes.c_void_p(stream.cuda_stream)
-
-    def launch(r, sh, ev=None):
-        if ev is not None:
-            ev[0].record()
-        st = sv.lib.sv_verify_attention(ctypes.byref(adescs[r]), pa, ws_a, sh)
-        if ev is not None:
-            ev[1].record()
-        st2 = sv.lib.sv_spec_accept(ctypes.byref(sdescs[r]), ps, ws_s, sh)
-        if ev is not None:
-            ev[2].record()
-        if st or st2:
-            raise RuntimeError("launch failed: %d %d" % (st, st2))
-
-    for i in range(args.warmup):
-        launch(i % R, sh)
-    torch.cuda.synchronize()
-
-    ms_per_step = timed_steps(launch, R, args, sh)
-
-    # Kernel durations: HIP events on the launch stream, same K steps.  The library's
-    # measurement hooks record one more event right after the main attention kernel (the
-    # attention call splits into its main kernel and the split combine) and give the main
-    # kernel's own start and end (hipExtLaunchKernel events: the span a kernel trace reports,
-    # without the dispatch ahead of the kernel).
-    # Two passes over the same K steps: the first with plain launches (call and combine
-    # intervals), the second with the kernel-span events (whose launch path adds host work
-    # between the events around the call).
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
-    for e in events:
-        for k in (1, 4, 5):
-            e[k].record()  # creates the events the library records
-    torch.cuda.synchronize()
-    for span in (False, True):
-        for i in range(args.steps):
-            ev = events[i]
-            if span:
-                sv.lib.sv_set_attention_timing(ctypes.c_void_p(ev[4].cuda_event), ctypes.c_void_p(ev[5].cuda_event))
-            else:
-                sv.lib.sv_set_attention_mark(ctypes.c_void_p(ev[1].cuda_event))
-                ev[0].record()
-            st = sv.lib.sv_verify_attention(ctypes.byref(adescs[(args.warmup + i) % R]), pa, ws_a, sh)
-            if not span:
-                ev[2].record()
-            st2 = sv.lib.sv_spec_accept(ctypes.byref(sdescs[(args.warmup + i) % R]), ps, ws_s, sh)
-            if not span:
-                ev[3].record()
-            if st or st2:
-                raise RuntimeError("launch failed: %d %d" % (st, st2))
-        sv.lib.sv_set_attention_mark(None)
-        sv.lib.sv_set_attention_timing(None, None)
-        torch.cuda.synchronize()
-    main_ms = float(np.mean([e[4].elapsed_time(e[5]) for e in events]))
-    main_call_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
-    comb_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
-    att_ms = float(np.mean([e[0].elapsed_time(e[2]) for e in events]))
-    acc_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
-
-    drafts = B * gamma
-    value = drafts / (ms_per_step * 1e-3)
-    kv_tokens = int((P.astype(np.int64) + n_q).sum())
-    att_bytes = esz * (B * n_q * Hq * D + 2 * kv_tokens * Hkv * D) + esz * B * n_q * Hq * D
-    acc_bytes = 4 * V * B * (2 * gamma + 1)
-    main_gbs = att_bytes / (main_ms * 1e-3) / 1e9
-
-    line = {
-        "metric": "draft tokens verified/sec on 1 MI355X; achieved HBM GB/s as % of peak",
-        "value": round(value, 1),
-        "unit": "draft tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": cfg["dtype"],
-        "data": "synthetic",
-        "config": {"workload": cfg["name"], "batch": B, "gamma": gamma, "cached_context": int(P.max()),
-                   "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "vocab": V, "temperature": tau,
-                   "mode": "sample", "kv_cache": "dense" if dense else "ragged (kv_off)",
-                   "rotated_input_copies": R, "launch": "eager" if args.eager else "hip_graph"},
-        "roofline": {"bound": "hbm", "achieved": round(main_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(main_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl),
-                     "kernel": "attn_bf16_kernel", "kernel_ms": round(main_ms, 5),
-                     "timing": KERNEL_SPAN, "algorithmic_bytes": att_bytes},
-        "kernels_ms": {"attn_bf16_kernel": round(main_ms, 5), "attn_bf16_kernel_with_dispatch": round(main_call_ms, 5),
-                       "attn_combine_kernel": round(comb_ms, 5), "sv_spec_accept": round(acc_ms, 5)},
-        "attention": {"kernel_ms": round(att_ms, 5), "algorithmic_bytes": att_bytes,
-                      "achieved_GBs": round(att_bytes / (att_ms * 1e-3) / 1e9, 1)},
-        "accept": {"kernel_ms": round(acc_ms, 5), "algorithmic_bytes": acc_bytes,
-                   "achieved_GBs": round(acc_bytes / (acc_ms * 1e-3) / 1e9, 1)},
-    }
-
-    if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(att, acc, cfg, scale, args.cpu_seconds)
+    line = run_workload(args.workload, args, dev, args.steps, args.warmup, cpu=not args.no_cpu, headline=True)
+    if not args.no_extra:
+        extra = {}
+        for wl in (2, 5):
+            if wl == args.workload:
+                continue
+            r = run_workload(wl, args, dev, 50, 5, cpu=False, headline=False)
+            extra[r["config"]["workload"]] = {k: r[k] for k in ("value", "unit", "ms_per_step", "roofline",
+                                                                 "roofline_other", "kernels_ms") if k in r}
+        line["other_workloads"] = extra
     print(json.dumps(line), flush=True)
 
 
-def timed_steps(launch, R, args, sh):
-    """Warm up, then time exactly args.steps steps (wall clock between two device
-    synchronizations); step i reads input copy i mod R.  Unless --eager, the steps are
+def run_workload(wl, args, dev, steps, warmup, cpu, headline):
+    import synth
+    cfg = synth.WORKLOADS[wl]
+    if cfg["kind"] == "chain":
+        return bench_chain(args, cfg, wl, dev, steps, warmup, cpu)
+    return bench_tree(args, cfg, wl, dev, steps, warmup, cpu)
+
+
+def _bf16_dev(a, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def _f32_dev(a, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def _aligned(buf):
+    return ctypes.c_void_p(buf.data_ptr() + (-buf.data_ptr()) % 256)
+
+
+def _ev(e):
+    return ctypes.c_void_p(e.cuda_event)
+
+
+def attention_timing(sv, adescs, ws, R, first, steps, run_rest, sh):
+    """Per-kernel durations over the same steps the timed region ran, in two eager passes:
+    events around the calls (dispatch included), then the descriptor's kernel-span events
+    (main kernel start/end, end of the call's last kernel).  ws = (workspace, bytes) of the
+    attention call; run_rest(r) launches the rest of the step after it.  Medians."""
+    import torch
+    n_ev = 8
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(steps)]
+    for e in events:
+        for k in (4, 5, 6):
+            e[k].record()  # creates the events the library records
+    torch.cuda.synchronize()
+    for span in (False, True):
+        for i in range(steps):
+            ev = events[i]
+            d = adescs[(first + i) % R]
+            if span:
+                d.ev_kernel_start, d.ev_kernel_stop, d.ev_call_stop = _ev(ev[4]), _ev(ev[5]), _ev(ev[6])
+            else:
+                ev[0].record()
+            st = sv.lib.sv_verify_attention(ctypes.byref(d), ws[0], ws[1], sh)
+            d.ev_kernel_start = d.ev_kernel_stop = d.ev_call_stop = None
+            if not span:
+                ev[1].record()
+            run_rest((first + i) % R)
+            if not span:
+                ev[2].record()
+            if st:
+                raise RuntimeError("attention launch failed: %d" % st)
+        torch.cuda.synchronize()
+    t = lambda a, b: float(np.median([e[a].elapsed_time(e[b]) for e in events]))  # noqa: E731
+    return dict(main=t(4, 5), attn_span=t(4, 6), combine=t(5, 6), attn_call=t(0, 1), rest=t(1, 2))
+
+
+def timed_steps(launch, R, steps, warmup, eager, sh):
+    """Warm up, then time exactly `steps` steps (wall clock between two device
+    synchronizations); step i reads input copy i mod R.  Unless eager, the steps are
     replayed from HIP graphs that each hold S consecutive steps (S the largest divisor of
     the step count up to 10), so the host's per-replay cost is spread over S steps; the
     kernels and their arguments are exactly those of the eager launches."""
-    import ctypes
     import torch
-    K = args.steps
-    if args.eager:
-        for i in range(args.warmup):
+    K = steps
+    if eager:
+        for i in range(warmup):
             launch(i % R, sh)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(K):
-            launch((args.warmup + i) % R, sh)
+            launch((warmup + i) % R, sh)
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) * 1e3 / K
     S = max(d for d in range(1, min(10, K) + 1) if K % d == 0)
@@ -265,22 +210,142 @@ def timed_steps(launch, R, args, sh):
             for k in range(S):
                 launch((r + k) % R, cs)
         graphs.append(g)
-    for m in range(max(1, args.warmup // S)):
+    for m in range(max(1, warmup // S)):
         graphs[(m * S) % R].replay()
     torch.cuda.synchronize()
-    first = args.warmup
     t0 = time.perf_counter()
     for m in range(K // S):
-        graphs[(first + m * S) % R].replay()
+        graphs[(warmup + m * S) % R].replay()
     torch.cuda.synchronize()
     return (time.perf_counter() - t0) * 1e3 / K
 
 
-def bench_tree(args, cfg, wl, dev):
+# --------------------------------------------------------------------------- #
+def bench_chain(args, cfg, wl, dev, steps, warmup, cpu):
+    import torch
+    import draft_token_verification_attention_amd as sv
+    import synth
+
+    B, gamma = cfg["B"], cfg["gamma"]
+    n_q = gamma + 1
+    Hq, Hkv, D, V, tau = cfg["Hq"], cfg["Hkv"], cfg["D"], cfg["V"], cfg["tau"]
+    P = synth.prefix_lengths(wl, cfg)
+    max_prefix = int(cfg.get("P_hi", int(P.max())))
+    att = synth.attention_inputs(wl, B=B, n_q=n_q, Hq=Hq, Hkv=Hkv, D=D, prefix_len=P, dtype=cfg["dtype"],
+                                 qkv_scale=cfg["qkv_scale"])
+    acc = synth.accept_inputs(wl, B=B, gamma=gamma, V=V, target_var=cfg["target_var"],
+                              noise_var=cfg["noise_var"], tau=tau)
+    bf = cfg["dtype"] == "bf16"
+    todev = (lambda a: _bf16_dev(a, dev)) if bf else (lambda a: _f32_dev(a, dev))
+    base = dict(q=todev(att["q"]), k=todev(att["k"]), v=todev(att["v"]),
+                target=_f32_dev(acc["target"], dev), draft=_f32_dev(acc["draft"], dev))
+    # One sequence: a dense cache (kv_off NULL; the sequence owns max_prefix + n_q token
+    # slots, which is what the packed buffer holds).  A batch: the packed ragged cache.
+    dense = B == 1 and int(P[0]) == max_prefix and args.kv_cache != "ragged"
+    kv_off = None if dense else _f32_dev(att["kv_off"].astype(np.int64), dev)
+    kv_sb = (max_prefix + n_q) * Hkv * D if dense else 0
+    prefix = _f32_dev(P.astype(np.int32), dev)
+    toks = _f32_dev(acc["draft_tokens"].astype(np.int32), dev)
+    set_bytes = sum(t.numel() * t.element_size() for t in base.values())
+    R = max(1, int(math.ceil(args.rotate_bytes / set_bytes)))
+    copies = [base] + [{k: t.clone() for k, t in base.items()} for _ in range(R - 1)]
+    scale = 1.0 / math.sqrt(D)
+    esz = 2 if bf else 4
+    seed = 1000 + wl
+
+    # outputs and descriptors prepared once: the timed loop only launches
+    out = torch.empty((B, n_q, Hq, D), dtype=base["q"].dtype, device=dev)
+    acc_len = torch.empty(B, dtype=torch.int32, device=dev)
+    out_tok = torch.empty((B, n_q), dtype=torch.int32, device=dev)
+    status = torch.empty(B, dtype=torch.int32, device=dev)
+    adescs, sdescs = [], []
+    for c in copies:
+        adescs.append(sv.attn_desc(c["q"], c["k"], c["v"], kv_off, prefix, Hkv=Hkv, max_prefix=max_prefix,
+                                   scale=scale, kv_sh=att["kv_sh"], kv_st=att["kv_st"], out=out,
+                                   split_keys=args.split_keys, kv_sb=kv_sb))
+        sdescs.append(sv.accept_desc(sv.SV_SAMPLE, c["target"], c["draft"], toks, tau, seed, 0, None,
+                                     acc_len, out_tok, None, status))
+    ws_a = sv.lib.sv_verify_attention_workspace(ctypes.byref(adescs[0]))
+    ws_s = sv.lib.sv_spec_accept_workspace(ctypes.byref(sdescs[0]))
+    ws_att = torch.zeros(ws_a + 256, dtype=torch.uint8, device=dev)
+    ws_acc = torch.zeros(ws_s + 256, dtype=torch.uint8, device=dev)
+    pa, ps = _aligned(ws_att), _aligned(ws_acc)
+    sh = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+    def launch(r, sh):
+        st = sv.lib.sv_verify_attention(ctypes.byref(adescs[r]), pa, ws_a, sh)
+        st2 = sv.lib.sv_spec_accept(ctypes.byref(sdescs[r]), ps, ws_s, sh)
+        if st or st2:
+            raise RuntimeError("launch failed: %d %d" % (st, st2))
+
+    for i in range(warmup):
+        launch(i % R, sh)
+    torch.cuda.synchronize()
+    ms_per_step = timed_steps(launch, R, steps, warmup, args.eager, sh)
+
+    def rest(r):
+        if sv.lib.sv_spec_accept(ctypes.byref(sdescs[r]), ps, ws_s, sh):
+            raise RuntimeError("acceptance launch failed")
+    t = attention_timing(sv, adescs, (pa, ws_a), R, warmup, steps, rest, sh)
+
+    drafts = B * gamma
+    value = drafts / (ms_per_step * 1e-3)
+    kv_tokens = int((P.astype(np.int64) + n_q).sum())
+    att_bytes = esz * (B * n_q * Hq * D + 2 * kv_tokens * Hkv * D) + esz * B * n_q * Hq * D
+    acc_bytes = 4 * V * B * (2 * gamma + 1)
+    gbs = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9  # noqa: E731
+    traffic = measured_traffic(wl)
+    line = {
+        "metric": "draft tokens verified/sec on 1 MI355X; achieved HBM GB/s as % of peak",
+        "value": round(value, 1),
+        "unit": "draft tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg["dtype"],
+        "data": "synthetic",
+        "config": {"workload": cfg["name"], "batch": B, "gamma": gamma,
+                   "cached_context": ("uniform [%d, %d]" % (cfg["P_lo"], cfg["P_hi"])) if "P_lo" in cfg
+                   else int(P.max()),
+                   "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "vocab": V, "temperature": tau,
+                   "mode": "sample", "kv_cache": "dense" if dense else "ragged (kv_off)",
+                   "rotated_input_copies": R, "launch": "eager" if args.eager else "hip_graph"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs(att_bytes, t["attn_span"]), 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs(att_bytes, t["attn_span"]) / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else traffic["attention"],
+                     "kernel": "attention pass: attn_bf16_kernel + attn_combine_kernel" if bf else "attn_f32_kernel",
+                     "kernel_ms": round(t["attn_span"], 5), "timing": KERNEL_SPAN + "; main kernel start to "
+                     "the end of the call's last kernel, median over the steps", "algorithmic_bytes": att_bytes,
+                     "main_kernel_only": {"kernel_ms": round(t["main"], 5),
+                                          "achieved": round(gbs(att_bytes, t["main"]), 1),
+                                          "frac": round(gbs(att_bytes, t["main"]) / HBM_PEAK_GBS, 4),
+                                          "traffic": None if traffic is None else traffic["main"]}},
+        "kernels_ms": {"attn_bf16_kernel": round(t["main"], 5), "attn_combine_kernel": round(t["combine"], 5),
+                       "attention_call_with_dispatch": round(t["attn_call"], 5),
+                       "sv_spec_accept": round(t["rest"], 5)},
+        "attention": {"kernel_ms": round(t["attn_span"], 5), "algorithmic_bytes": att_bytes,
+                      "achieved_GBs": round(gbs(att_bytes, t["attn_span"]), 1)},
+        "accept": {"kernel_ms": round(t["rest"], 5), "algorithmic_bytes": acc_bytes,
+                   "achieved_GBs": round(gbs(acc_bytes, t["rest"]), 1)},
+    }
+    if cpu:
+        # the GPU's own outputs for the step on copy 0 (seed, step 0), for the parity verdict
+        launch(0, sh)
+        torch.cuda.synchronize()
+        gpu = dict(out=out.float().cpu().numpy(), accept_len=acc_len.cpu().numpy(),
+                   out_tokens=out_tok.cpu().numpy(), status=status.cpu().numpy())
+        line["cpu_baseline"] = cpu_baseline_chain(att, acc, cfg, scale, seed, gpu, args.cpu_seconds)
+    return line
+
+
+def bench_tree(args, cfg, wl, dev, steps, warmup, cpu):
     """A tree round: the mask build from the parent array, the tree attention over the
     cache + node tokens, and the tree walk (sampling, the workload's temperature) over
     the per-node target logits.  Draft tokens verified per step = drafted nodes."""
-    import ctypes
     import torch
     import draft_token_verification_attention_amd as sv
     import synth
@@ -297,17 +362,16 @@ def bench_tree(args, cfg, wl, dev):
         depth[i] = depth[parents[i]] + 1
     max_depth = int(depth.max())
 
-    def bf(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
-
-    base = dict(q=bf(att["q"]), k=bf(att["k"]), v=bf(att["v"]), logits=torch.from_numpy(lg).to(dev))
+    base = dict(q=_bf16_dev(att["q"], dev), k=_bf16_dev(att["k"], dev), v=_bf16_dev(att["v"], dev),
+                logits=_f32_dev(lg, dev))
+    lg_host = lg if cpu and n <= 128 else None
     del lg
     set_bytes = sum(t.numel() * t.element_size() for t in base.values())
     R = max(1, int(math.ceil(args.rotate_bytes / set_bytes)))
     copies = [base] + [{k: t.clone() for k, t in base.items()} for _ in range(R - 1)]
-    par_d = torch.from_numpy(parents.astype(np.int32)).to(dev)
-    toks_d = torch.from_numpy(toks.astype(np.int32)).to(dev)
-    kv_off = torch.from_numpy(att["kv_off"].astype(np.int64)).to(dev)
+    par_d = _f32_dev(parents.astype(np.int32), dev)
+    toks_d = _f32_dev(toks.astype(np.int32), dev)
+    kv_off = _f32_dev(att["kv_off"].astype(np.int64), dev)
     prefix = torch.tensor([P], dtype=torch.int32, device=dev)
     words = (n + 31) // 32
     bits = torch.empty((n, words), dtype=torch.int32, device=dev)
@@ -320,150 +384,101 @@ def bench_tree(args, cfg, wl, dev):
     out_tok = torch.empty((1, max_depth + 1), dtype=torch.int32, device=dev)
     wstat = torch.empty(1, dtype=torch.int32, device=dev)
     scale = 1.0 / math.sqrt(D)
+    seed = 1000 + wl
     adescs = [sv.attn_desc(c["q"], c["k"], c["v"], kv_off, prefix, Hkv=Hkv, max_prefix=P, scale=scale,
                            kv_sh=att["kv_sh"], kv_st=att["kv_st"], out=out, tree_bits=bits, tree_sb=0,
                            split_keys=args.split_keys) for c in copies]
-    wdescs = [sv.walk_desc(sv.SV_SAMPLE, c["logits"], toks_d, par_d, max_depth, tau, 1000 + wl, 0, None,
+    wdescs = [sv.walk_desc(sv.SV_SAMPLE, c["logits"], toks_d, par_d, max_depth, tau, seed, 0, None,
                            acc_len, path, out_tok, wstat) for c in copies]
     ws_a = sv.lib.sv_verify_attention_workspace(ctypes.byref(adescs[0]))
     ws_w = sv.lib.sv_tree_walk_workspace(ctypes.byref(wdescs[0]))
     ws_att = torch.zeros(ws_a + 256, dtype=torch.uint8, device=dev)
     ws_wlk = torch.zeros(ws_w + 256, dtype=torch.uint8, device=dev)
-    pa = ctypes.c_void_p(ws_att.data_ptr() + (-ws_att.data_ptr()) % 256)
-    pw = ctypes.c_void_p(ws_wlk.data_ptr() + (-ws_wlk.data_ptr()) % 256)
+    pa, pw = _aligned(ws_att), _aligned(ws_wlk)
     sh = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    vp = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
 
-    def launch(r, sh, ev=None):
-        if ev is not None:
-            ev[0].record()
-        st0 = sv.lib.sv_build_tree_mask(ctypes.c_void_p(par_d.data_ptr()), n, P, ctypes.c_void_p(bits.data_ptr()),
-                                        ctypes.c_void_p(dep_d.data_ptr()), ctypes.c_void_p(pos_d.data_ptr()),
-                                        ctypes.c_void_p(mstat.data_ptr()), sh)
-        if ev is not None:
-            ev[1].record()
+    def mask(sh):
+        return sv.lib.sv_build_tree_mask(vp(par_d), n, P, vp(bits), vp(dep_d), vp(pos_d), vp(mstat), sh)
+
+    def launch(r, sh):
+        st0 = mask(sh)
         st1 = sv.lib.sv_verify_attention(ctypes.byref(adescs[r]), pa, ws_a, sh)
-        if ev is not None:
-            ev[3].record()
         st2 = sv.lib.sv_tree_walk(ctypes.byref(wdescs[r]), pw, ws_w, sh)
-        if ev is not None:
-            ev[4].record()
         if st0 or st1 or st2:
             raise RuntimeError("launch failed: %d %d %d" % (st0, st1, st2))
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         launch(i % R, sh)
     torch.cuda.synchronize()
-    ms_per_step = timed_steps(launch, R, args, sh)
+    ms_per_step = timed_steps(launch, R, steps, warmup, args.eager, sh)
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
-    for e in events:
-        for k in (2, 5, 6):
-            e[k].record()  # creates the events the library records
+    def rest(r):
+        if sv.lib.sv_tree_walk(ctypes.byref(wdescs[r]), pw, ws_w, sh):
+            raise RuntimeError("walk launch failed")
+    t = attention_timing(sv, adescs, (pa, ws_a), R, warmup, steps, rest, sh)
+    # the mask build alone
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
+    for i in range(steps):
+        ev[2 * i].record()
+        mask(sh)
+        ev[2 * i + 1].record()
     torch.cuda.synchronize()
-    # two passes, as for the chain workloads: plain launches, then the kernel-span events
-    for i in range(args.steps):
-        sv.lib.sv_set_attention_mark(ctypes.c_void_p(events[i][2].cuda_event))
-        launch((args.warmup + i) % R, sh, events[i])
-    sv.lib.sv_set_attention_mark(None)
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        sv.lib.sv_set_attention_timing(ctypes.c_void_p(events[i][5].cuda_event),
-                                       ctypes.c_void_p(events[i][6].cuda_event))
-        launch((args.warmup + i) % R, sh)
-    sv.lib.sv_set_attention_timing(None, None)
-    torch.cuda.synchronize()
-    mask_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
-    main_ms = float(np.mean([e[5].elapsed_time(e[6]) for e in events]))
-    main_call_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
-    comb_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
-    walk_ms = float(np.mean([e[3].elapsed_time(e[4]) for e in events]))
+    mask_ms = float(np.median([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps)]))
 
     drafted = n - 1
     value = drafted / (ms_per_step * 1e-3)
     anc = int((depth + 1).sum())  # sum over nodes of the ancestor-or-self count
     att_flops = 4.0 * D * Hq * (n * P + anc)
     att_bytes = 2 * (n * Hq * D + 2 * (P + n) * Hkv * D) + 2 * n * Hq * D + 4 * n * words
-    main_tflops = att_flops / (main_ms * 1e-3) / 1e12
-    main_gbs = att_bytes / (main_ms * 1e-3) / 1e9
-    walk_rows = int(to_host_int(acc_len)) + 1
-    mfma = {"bound": "mfma", "achieved": round(main_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(main_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": measured_traffic(wl),
-            "kernel": "attn_bf16_kernel", "kernel_ms": round(main_ms, 5), "timing": KERNEL_SPAN,
-            "algorithmic_flops": att_flops}
-    hbm = {"bound": "hbm", "achieved": round(main_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-           "frac": round(main_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl),
-           "kernel": "attn_bf16_kernel", "kernel_ms": round(main_ms, 5), "timing": KERNEL_SPAN,
-           "algorithmic_bytes": att_bytes}
+    traffic = measured_traffic(wl)
+    tr_attn = None if traffic is None else traffic["attention"]
+    span = t["attn_span"]
+    mfma = {"bound": "mfma", "achieved": round(att_flops / (span * 1e-3) / 1e12, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(att_flops / (span * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": tr_attn, "kernel": "attention pass: attn_bf16_kernel + attn_combine_kernel",
+            "kernel_ms": round(span, 5), "timing": KERNEL_SPAN, "algorithmic_flops": att_flops,
+            "main_kernel_only": {"kernel_ms": round(t["main"], 5),
+                                 "frac": round(att_flops / (t["main"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}}
+    hbm = {"bound": "hbm", "achieved": round(att_bytes / (span * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+           "unit": "GB/s", "frac": round(att_bytes / (span * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": tr_attn,
+           "kernel": "attention pass: attn_bf16_kernel + attn_combine_kernel", "kernel_ms": round(span, 5),
+           "timing": KERNEL_SPAN, "algorithmic_bytes": att_bytes,
+           "main_kernel_only": {"kernel_ms": round(t["main"], 5),
+                                "frac": round(att_bytes / (t["main"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
+    walk_rows = int(acc_len.cpu().numpy()[0]) + 1
     line = {
         "metric": "draft tokens verified/sec on 1 MI355X; achieved HBM GB/s as % of peak",
-        "value": round(value, 1), "unit": "draft tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "value": round(value, 1), "unit": "draft tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": cfg["name"], "batch": 1, "tree_nodes": drafted, "cached_context": P,
                    "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "vocab": V, "temperature": tau,
                    "mode": "sample", "rotated_input_copies": R, "launch": "eager" if args.eager else "hip_graph"},
         "roofline": mfma if wl == 5 else hbm,
         "roofline_other": hbm if wl == 5 else mfma,
-        "kernels_ms": {"tree_mask_kernel": round(mask_ms, 5), "attn_bf16_kernel": round(main_ms, 5),
-                       "attn_bf16_kernel_with_dispatch": round(main_call_ms, 5),
-                       "attn_combine_kernel": round(comb_ms, 5), "sv_tree_walk": round(walk_ms, 5)},
-        "walk": {"kernel_ms": round(walk_ms, 5), "rows_visited": walk_rows,
-                 "algorithmic_bytes": 4 * V * walk_rows},
+        "kernels_ms": {"tree_mask_kernel": round(mask_ms, 5), "attn_bf16_kernel": round(t["main"], 5),
+                       "attn_combine_kernel": round(t["combine"], 5),
+                       "attention_call_with_dispatch": round(t["attn_call"], 5), "sv_tree_walk": round(t["rest"], 5)},
+        "walk": {"kernel_ms": round(t["rest"], 5), "rows_visited": walk_rows, "algorithmic_bytes": 4 * V * walk_rows},
     }
-    if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline_tree(att, cfg, wl, parents, toks, scale, args.cpu_seconds)
-    print(json.dumps(line), flush=True)
+    if cpu:
+        launch(0, sh)
+        torch.cuda.synchronize()
+        gpu = dict(out=out.float().cpu().numpy(), path=path.cpu().numpy(), accept_len=acc_len.cpu().numpy(),
+                   out_tokens=out_tok.cpu().numpy())
+        line["cpu_baseline"] = cpu_baseline_tree(att, cfg, wl, parents, toks, lg_host, scale, seed, gpu,
+                                                 args.cpu_seconds)
+    return line
 
 
-def to_host_int(t):
-    return int(t.cpu().numpy().ravel()[0])
-
-
-def cpu_baseline_tree(att, cfg, wl, parents, toks, scale, seconds):
-    """The oracle on a bounded sample: the mask, the fp64 attention of a seeded sample of
-    rows (timed, then scaled to every row) and the tree walk, repeated for ~`seconds`."""
-    import oracle
-    import synth
-    threads = os.cpu_count() or 1
-    oracle.set_threads(threads)
-    n, Hq = len(parents), cfg["Hq"]
-    total_rows = n * Hq
-    r = np.random.default_rng(wl)
-    nsample = min(total_rows, 4096)
-    pick = r.choice(total_rows, size=nsample, replace=False)
-    rows = np.stack([np.zeros(nsample, np.int64), pick // Hq, pick % Hq], 1).astype(np.int32)
-    lg = synth.tree_logits(wl, 1, n, cfg["V"], cfg["target_var"]) if n <= 128 else None
-    t_mask = t_att = t_walk = 0.0
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        ta = time.perf_counter()
-        bits = oracle.tree_mask(parents, cfg["P"])[0]
-        tb = time.perf_counter()
-        oracle.attention(att, scale=scale, tree_bits=bits, tree_sb=0, rows=rows)
-        tc = time.perf_counter()
-        if lg is not None:
-            oracle.tree_walk(oracle.SAMPLE, lg, toks, parents, cfg["tau"], seed=1000 + wl, step=reps)
-        td = time.perf_counter()
-        t_mask += tb - ta
-        t_att += tc - tb
-        t_walk += td - tc
-        reps += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    step_s = (t_mask + t_att * total_rows / nsample + t_walk) / reps
-    return {"value": round((n - 1) / step_s, 3), "unit": "draft tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "%d reps of: mask, fp64 attention of %d of %d rows (time scaled to all rows)%s"
-                      % (reps, nsample, total_rows, ", tree walk" if lg is not None else
-                         "; walk not sampled (its 2.4 GB logits stay off the host leg)")}
-
-
-# HBM bytes per launch of attn_bf16_kernel (2 x FETCH_SIZE + WRITE_SIZE, the FETCH_SIZE
-# counter reading half the bytes of a plain copy of known size on this GPU), from the
-# rocprofv3 --pmc runs summarized under profiles/, and the SHA-256 of the attention source
-# they were taken on: a changed kernel reports null until the counters are taken again.
-TRAFFIC = {2: 19146491, 4: 1110644725}
-TRAFFIC_SRC_SHA256 = "f0181d9ba00dab5aead0be6b439625055d682b4177dd223d0d4fe6d7c20343a0"
+# --------------------------------------------------------------------------- #
+# HBM bytes per launch (2 x FETCH_SIZE + WRITE_SIZE, the FETCH_SIZE counter reading half the
+# bytes of a plain copy of known size on this GPU) from the rocprofv3 --pmc runs summarized
+# under profiles/, with the SHA-256 of the attention source they were taken on: a changed
+# kernel reports null until the counters are taken again.  "attention" = main + combine.
+TRAFFIC = {}
+TRAFFIC_SRC_SHA256 = None
 
 
 def measured_traffic(wl):
@@ -477,24 +492,127 @@ def measured_traffic(wl):
     return TRAFFIC[wl]
 
 
-def cpu_baseline(att, acc, cfg, scale, seconds):
-    """The fp64 oracle, as it stands, on the host cores: whole steps of the same workload
-    (attention over every row, then sampling acceptance), repeated for ~`seconds`."""
+def _parity_accept(ref, gpu):
+    flagged = ref["flags"] != 0
+    same = (ref["accept_len"] == gpu["accept_len"]) & np.all(ref["out_tokens"] == gpu["out_tokens"], axis=1)
+    return {"sequences": int(len(same)), "bit_exact": int(same.sum()), "near_threshold": int(flagged.sum()),
+            "mismatched_near_threshold": int((~same & flagged).sum()),
+            "mismatched_other": int((~same & ~flagged).sum())}
+
+
+def cpu_baseline_chain(att, acc, cfg, scale, seed, gpu, seconds):
+    """The fp64 oracle, as it stands, on the host: whole steps of the same workload on all
+    host threads (attention of every row, then sampling acceptance), repeated for about
+    `seconds`; then one thread on a bounded sample (the attention rows and acceptance of
+    the first sequences, scaled to the whole step).  The first all-threads step runs on
+    the inputs, seed and step of the GPU step whose outputs `gpu` holds: its results give
+    the parity verdict."""
     import oracle
-    threads = os.cpu_count() or 1
+    threads = host_threads()
     oracle.set_threads(threads)
-    gamma, tau = cfg["gamma"], cfg["tau"]
+    B, gamma, tau = cfg["B"], cfg["gamma"], cfg["tau"]
     n = 0
+    parity = None
     t0 = time.perf_counter()
     while True:
-        oracle.attention(att, scale=scale)
-        oracle.spec_accept(oracle.SAMPLE, acc["target"], acc["draft"], acc["draft_tokens"], tau, seed=1000, step=n)
+        o, _, rows = oracle.attention(att, scale=scale)
+        r = oracle.spec_accept(oracle.SAMPLE, acc["target"], acc["draft"], acc["draft_tokens"], tau, seed=seed,
+                               step=n)
+        if n == 0:
+            got = gpu["out"][rows[:, 0], rows[:, 1], rows[:, 2]]
+            parity = {"accept": _parity_accept(r, gpu), "gpu_status_nonzero": int((gpu["status"] != 0).sum()),
+                      "attention_rows": int(len(rows)), "attention_max_abs": float(np.abs(got - o).max()),
+                      "attention_max_abs_over_max_out": float(np.abs(got - o).max() / np.abs(o).max()),
+                      "attention_bound": 2e-2 if att["dtype"] == "bf16" else 1e-4}
+            parity["verdict"] = bool(parity["accept"]["mismatched_other"] == 0 and parity["gpu_status_nonzero"] == 0
+                                     and parity["attention_max_abs"] <= parity["attention_bound"])
         n += 1
         if time.perf_counter() - t0 >= seconds:
             break
-    dt = (time.perf_counter() - t0) / n
-    return {"value": round(cfg["B"] * gamma / dt, 2), "unit": "draft tokens/s", "cores": threads,
-            "kind": "oracle", "sample": "%d whole steps of the same workload (all attention rows + acceptance)" % n}
+    dt_all = (time.perf_counter() - t0) / n
+    # one thread: the first k sequences, attention rows and acceptance timed apart and
+    # scaled to the whole step by their share of the cached keys and of the sequences
+    oracle.set_threads(1)
+    k = max(1, min(B, 2))
+    rows = np.array([(b, i, h) for b in range(k) for i in range(att["n_q"]) for h in range(att["Hq"])], np.int32)
+    keys_all = float((att["prefix_len"].astype(np.int64) + att["n_q"]).sum())
+    keys_k = float((att["prefix_len"][:k].astype(np.int64) + att["n_q"]).sum())
+    m, ta, tc = 0, 0.0, 0.0
+    t1 = time.perf_counter()
+    while True:
+        t2 = time.perf_counter()
+        oracle.attention(att, scale=scale, rows=rows)
+        t3 = time.perf_counter()
+        oracle.spec_accept(oracle.SAMPLE, acc["target"][:k], acc["draft"][:k], acc["draft_tokens"][:k], tau,
+                           seed=seed, step=m)
+        tc += time.perf_counter() - t3
+        ta += t3 - t2
+        m += 1
+        if time.perf_counter() - t1 >= seconds:
+            break
+    dt_one = (ta * keys_all / keys_k + tc * B / k) / m
+    oracle.set_threads(threads)
+    return {"value": round(B * gamma / dt_all, 3), "unit": "draft tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d whole steps of the same workload (every attention row + acceptance of every sequence)"
+                      % n,
+            "single_thread": {"value": round(B * gamma / dt_one, 3), "cores": 1,
+                              "sample": "%d reps of the attention rows and the acceptance of the first %d of %d "
+                                        "sequences, timed apart and scaled by their share of the cached keys "
+                                        "(x%.2f) and of the sequences (x%.1f)"
+                                        % (m, k, B, keys_all / keys_k, B / k)},
+            "host_cpu": host_cpu_model(), "parity": parity}
+
+
+def cpu_baseline_tree(att, cfg, wl, parents, toks, lg, scale, seed, gpu, seconds):
+    """The oracle on a bounded sample: the mask, the fp64 attention of a seeded sample of
+    rows (timed, then scaled to every row) and the tree walk, repeated for ~`seconds`;
+    the first repetition's rows and walk (seed and step of the GPU step whose outputs
+    `gpu` holds) give the parity verdict."""
+    import oracle
+    threads = host_threads()
+    oracle.set_threads(threads)
+    n, Hq = len(parents), cfg["Hq"]
+    total_rows = n * Hq
+    r = np.random.default_rng(wl)
+    nsample = min(total_rows, 4096)
+    pick = np.sort(r.choice(total_rows, size=nsample, replace=False))
+    rows = np.stack([np.zeros(nsample, np.int64), pick // Hq, pick % Hq], 1).astype(np.int32)
+    t_mask = t_att = t_walk = 0.0
+    reps = 0
+    parity = None
+    t0 = time.perf_counter()
+    while True:
+        ta = time.perf_counter()
+        bits = oracle.tree_mask(parents, cfg["P"])[0]
+        tb = time.perf_counter()
+        o, _, _ = oracle.attention(att, scale=scale, tree_bits=bits, tree_sb=0, rows=rows)
+        tc = time.perf_counter()
+        w = None
+        if lg is not None:
+            w = oracle.tree_walk(oracle.SAMPLE, lg, toks, parents, cfg["tau"], seed=seed, step=reps)
+        td = time.perf_counter()
+        if reps == 0:
+            got = gpu["out"][rows[:, 0], rows[:, 1], rows[:, 2]]
+            parity = {"attention_rows": int(nsample), "attention_max_abs": float(np.abs(got - o).max()),
+                      "attention_bound": 2e-2}
+            ok = parity["attention_max_abs"] <= 2e-2
+            if w is not None:
+                same = bool(np.array_equal(w["path"], gpu["path"]) and np.array_equal(w["out_tokens"], gpu["out_tokens"]))
+                parity["walk"] = {"bit_exact": same, "near_threshold": int((w["flags"] != 0).sum())}
+                ok = ok and (same or bool(w["flags"][0]))
+            parity["verdict"] = bool(ok)
+        t_mask += tb - ta
+        t_att += tc - tb
+        t_walk += td - tc
+        reps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    step_s = (t_mask + t_att * total_rows / nsample + t_walk) / reps
+    return {"value": round((n - 1) / step_s, 3), "unit": "draft tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d reps of: mask, fp64 attention of %d of %d rows (time scaled to all rows)%s"
+                      % (reps, nsample, total_rows, ", tree walk" if lg is not None else
+                         "; walk not sampled (its 2.4 GB logits stay off the host leg)"),
+            "host_cpu": host_cpu_model(), "parity": parity}
 
 
 if __name__ == "__main__":

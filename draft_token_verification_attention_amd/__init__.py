@@ -37,7 +37,8 @@ class sv_attn_desc(ctypes.Structure):
                 ("q", _P), ("q_sb", _i64), ("q_st", _i64), ("q_sh", _i64),
                 ("k", _P), ("v", _P), ("kv_off", _P), ("kv_sh", _i64), ("kv_st", _i64),
                 ("kv_sb", _i64), ("prefix_len", _P), ("tree_bits", _P), ("tree_sb", _i64),
-                ("out", _P), ("o_sb", _i64), ("o_st", _i64), ("o_sh", _i64), ("lse", _P)]
+                ("out", _P), ("o_sb", _i64), ("o_st", _i64), ("o_sh", _i64), ("lse", _P),
+                ("ev_kernel_start", _P), ("ev_kernel_stop", _P), ("ev_call_stop", _P)]
 
 
 class sv_accept_desc(ctypes.Structure):
@@ -54,7 +55,7 @@ class sv_walk_desc(ctypes.Structure):
 
 EXPORTS = ("sv_build_tree_mask", "sv_verify_attention_workspace", "sv_verify_attention",
            "sv_spec_accept_workspace", "sv_spec_accept", "sv_tree_walk_workspace", "sv_tree_walk",
-           "sv_set_attention_mark", "sv_set_attention_timing", "sv_status_string")
+           "sv_status_string")
 
 
 def _load():
@@ -76,10 +77,6 @@ def _load():
     L.sv_tree_walk_workspace.restype = ctypes.c_size_t
     L.sv_tree_walk.argtypes = [ctypes.POINTER(sv_walk_desc), _P, ctypes.c_size_t, _P]
     L.sv_tree_walk.restype = ctypes.c_int
-    L.sv_set_attention_mark.argtypes = [_P]
-    L.sv_set_attention_mark.restype = ctypes.c_int
-    L.sv_set_attention_timing.argtypes = [_P, _P]
-    L.sv_set_attention_timing.restype = ctypes.c_int
     L.sv_status_string.argtypes = [ctypes.c_int]
     L.sv_status_string.restype = ctypes.c_char_p
     return L

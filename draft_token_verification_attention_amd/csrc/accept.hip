@@ -25,8 +25,9 @@
 //            segment holding u* Z (block-wide scan), then (one wave, token order) the extra
 //            token.  When the residual has no mass, or the layout is not the vector one, it
 //            finds the chunk first, then the token inside it.
-// Exponentials of the bulk run in fp32; every sum, the CDF and the decided p(x), q(x)
-// are fp64.
+// Every exponential a sampling decision depends on -- the softmax sums of the statistics
+// pass, the residual and CDF weights, the decided p(x), q(x) -- is fp64 (exp2_acc / exp),
+// and so is every sum; the optional alpha pass keeps fp32 exponentials.
 #include "vocab_row.h"
 
 namespace {
@@ -172,15 +173,15 @@ __device__ __forceinline__ void stage_parts(const RowPart *pp, int n, RowPart *s
 }
 
 template <int LPR>
-__device__ __forceinline__ void row_softmax_stats_lpr(const RowPart *src, int nrows, int nchunk, float kf, double *sM,
-                                                      double *sZ)
+__device__ __forceinline__ void row_softmax_stats_lpr(const RowPart *src, int nrows, int nchunk, double kd,
+                                                      double *sM, double *sZ)
 {
     constexpr int RPP = kRowThreads / LPR;  // rows per block pass
     const int lane_row = (int)threadIdx.x / LPR;
     for (int r0 = 0; r0 < nrows; r0 += RPP) {
         float M;
         double Z;
-        group_combine_softmax<LPR>(src, r0 + lane_row, nrows, nchunk, kf, M, Z);
+        group_combine_softmax<LPR>(src, r0 + lane_row, nrows, nchunk, kd, M, Z);
         if ((threadIdx.x % LPR) == 0 && r0 + lane_row < nrows) {
             sM[r0 + lane_row] = (double)M;
             sZ[r0 + lane_row] = Z;
@@ -192,15 +193,15 @@ __device__ __forceinline__ void row_softmax_stats_lpr(const RowPart *src, int nr
 // (M, Z) of rows [0, nrows): the chunk partials of a row sit on 16, 32 or 64 lanes -- the
 // fewest lanes that hold a part each, but more lanes per row only while every row still
 // fits in one pass of the block (a second pass costs more than a lane reading two parts)
-__device__ __forceinline__ void row_softmax_stats(const RowPart *src, int nrows, int nchunk, float kf, double *sM,
+__device__ __forceinline__ void row_softmax_stats(const RowPart *src, int nrows, int nchunk, double kd, double *sM,
                                                   double *sZ)
 {
     if (nchunk <= 16 || nrows > kRowThreads / 32)
-        row_softmax_stats_lpr<16>(src, nrows, nchunk, kf, sM, sZ);
+        row_softmax_stats_lpr<16>(src, nrows, nchunk, kd, sM, sZ);
     else if (nchunk <= 32 || nrows > kRowThreads / 64)
-        row_softmax_stats_lpr<32>(src, nrows, nchunk, kf, sM, sZ);
+        row_softmax_stats_lpr<32>(src, nrows, nchunk, kd, sM, sZ);
     else
-        row_softmax_stats_lpr<64>(src, nrows, nchunk, kf, sM, sZ);
+        row_softmax_stats_lpr<64>(src, nrows, nchunk, kd, sM, sZ);
 }
 
 // ---------------------------------------------------------------------------
@@ -251,17 +252,18 @@ __global__ __launch_bounds__(kRowThreads) void accept_stats_kernel(AcceptArgs a,
             part.s = 0.0;
         } else {
             // each thread: its own max and its sum relative to it (no barrier); then the
-            // block rescales the per-thread sums to the chunk max in fp64
+            // block rescales the per-thread sums to the chunk max.  Weights and rescale in
+            // fp64 (exp2_acc): the decisions downstream depend on these sums.
             float mt = -INFINITY;
 #pragma unroll
             for (int k = 0; k < kPerThread; ++k) mt = fmaxf(mt, xv[k]);
-            // branch-free: -inf logits (masked, or beyond V) weigh exp2_fast(-inf) = 0
-            const float mref = mt == -INFINITY ? 0.0f : mt;
+            // branch-free: -inf logits (masked, or beyond V) weigh exp2_acc(-inf) = 0
+            const double mref = mt == -INFINITY ? 0.0 : (double)mt;
             double st = 0.0;
 #pragma unroll
-            for (int k = 0; k < kPerThread; ++k) st += (double)exp2_fast((xv[k] - mref) * a.kf);
+            for (int k = 0; k < kPerThread; ++k) st += exp2_acc(((double)xv[k] - mref) * a.kd);
             const float m = kParts > 1 ? wave_max(mt) : block_max(mt, fscr);
-            const double z = st > 0.0 ? st * (double)exp2_fast((mt - m) * a.kf) : 0.0;
+            const double z = st > 0.0 ? st * exp2_acc(((double)mt - (double)m) * a.kd) : 0.0;
             const double sm = kParts > 1 ? wave_sum(z) : block_sum(z, dscr);
             part.m = m;
             part.arg = 0;
@@ -339,7 +341,7 @@ __global__ __launch_bounds__(kRowThreads) void accept_alpha_kernel(AcceptArgs a,
         float M;
         double Z;
         group_combine_softmax<kWave>(w.part + ((int64_t)b * a.rows + (wave == 0 ? i : g + 1 + i)) * a.npart, 0, 1,
-                                     a.npart, a.kf, M, Z);
+                                     a.npart, a.kd, M, Z);
         if (threadIdx.x % kWave == 0) {
             sM[wave] = (double)M;
             sZ[wave] = Z;
@@ -411,11 +413,11 @@ __global__ __launch_bounds__(kRowThreads, 2) void accept_resample_kernel(AcceptA
     };
     if (a.rows * a.npart <= kMaxStaged) {
         stage_parts(pp, a.rows * a.npart, stage, keep_extra);
-        row_softmax_stats(stage, a.rows, a.npart, a.kf, sM, sZ);
+        row_softmax_stats(stage, a.rows, a.npart, a.kd, sM, sZ);
     } else {
         keep_extra();
         __syncthreads();
-        row_softmax_stats(pp, a.rows, a.npart, a.kf, sM, sZ);
+        row_softmax_stats(pp, a.rows, a.npart, a.kd, sM, sZ);
     }
     if (threadIdx.x < g) {
         const int i = threadIdx.x;
@@ -443,14 +445,15 @@ __global__ __launch_bounds__(kRowThreads, 2) void accept_resample_kernel(AcceptA
 
     const float *prow = a.target + ((int64_t)b * (g + 1) + J) * a.V;
     const float *qrow = J < g ? a.draft + ((int64_t)b * g + J) * a.V : nullptr;
-    // with no draft row (J == gamma) q is 0: iZq = 0, and Mq = Mp keeps exp2f finite
-    const float Mp = (float)sM[J], Mq = J < g ? (float)sM[g + 1 + J] : Mp;
+    // with no draft row (J == gamma) q is 0: iZq = 0, and Mq = Mp keeps the exponent finite
+    const double Mp = sM[J], Mq = J < g ? sM[g + 1 + J] : Mp;
     const double iZp = 1.0 / sZ[J], iZq = J < g ? 1.0 / sZ[g + 1 + J] : 0.0;
     const int base = c * kChunk;
 
-    // weight of token e: residual (or p when every draft was kept / the residual is empty)
-    auto p_of = [&](float l) { return (double)exp2_fast((l - Mp) * a.kf) * iZp; };
-    auto q_of = [&](float l) { return (double)exp2_fast((l - Mq) * a.kf) * iZq; };
+    // weight of token e: residual (or p when every draft was kept / the residual is empty),
+    // every weight in fp64 (exp2_acc)
+    auto p_of = [&](float l) { return exp2_acc(((double)l - Mp) * a.kd) * iZp; };
+    auto q_of = [&](float l) { return exp2_acc(((double)l - Mq) * a.kd) * iZq; };
 
     float xp[kPerThread], xq[kPerThread];
     load_chunk2<VEC, kPerThread>(prow, qrow ? qrow : prow, base, a.V, xp, xq);
@@ -664,22 +667,16 @@ static hipError_t launch(K kernel, dim3 grid, hipStream_t s, const AcceptArgs &a
 }
 
 // Blocks of a looping kernel that are resident at once on the current device (occupancy
-// x compute units), cached per kernel and device.
+// x compute units), asked of the runtime on every call.
 template <bool VEC, bool SAMPLE, int PER>
 static int stats_resident_blocks()
 {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    if (cached[dev] == 0) {
-        int per_cu = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, accept_stats_kernel<VEC, SAMPLE, PER>, kRowThreads,
-                                                          0) != hipSuccess ||
-            per_cu < 1)
-            per_cu = 2;
-        cached[dev] = per_cu * device_cu_count();
-    }
-    return cached[dev];
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, accept_stats_kernel<VEC, SAMPLE, PER>, kRowThreads, 0) !=
+            hipSuccess ||
+        per_cu < 1)
+        per_cu = 2;
+    return per_cu * device_cu_count();
 }
 
 // The residual draw: small calls in the vector layout on kResChunk chunks, others on the

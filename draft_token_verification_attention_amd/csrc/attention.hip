@@ -216,8 +216,9 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
     }
     const int P = a.prefix_len[b];
     const int T = P + a.n_q;
-    // a sequence longer than max_prefix reads nothing and reports NaN rows
-    const bool overflow = P > a.max_prefix;
+    // a sequence whose prefix is negative or longer than max_prefix reads nothing and
+    // reports NaN rows
+    const bool overflow = P > a.max_prefix || P < 0;
     const int ns = overflow ? a.nsplit : (T + SK - 1) / SK;
     if (s >= ns) return;
     const int kstart = s * SK;
@@ -572,7 +573,7 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a, 
         const int b = kg / a.Hkv, kvh = kg % a.Hkv;
         const int P = a.prefix_len[b];
         const int T = P + a.n_q;
-        const bool overflow = P > a.max_prefix;
+        const bool overflow = P > a.max_prefix || P < 0;
         const int ns = overflow ? a.nsplit : (T + a.split_keys - 1) / a.split_keys;
         const int r = (t % nrc) * CR + rl;        // row within the tile
         const int row = rt * ROWS_BLK + r;
@@ -670,7 +671,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a, int D)
     const int lane = threadIdx.x;
     const int kvh = h / a.G;
     const int P = a.prefix_len[b];
-    const bool overflow = P > a.max_prefix;  // reads nothing, reports NaN
+    const bool overflow = P > a.max_prefix || P < 0;  // reads nothing, reports NaN
     const int T = overflow ? 0 : P + a.n_q;
     const float *q = (const float *)a.q + (int64_t)b * a.q_sb + (int64_t)i * a.q_st + (int64_t)h * a.q_sh;
     const int64_t seq_off = a.kv_off ? a.kv_off[b] : (int64_t)b * a.kv_sb;
@@ -722,7 +723,7 @@ struct Plan {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-static bool plan_attention(const sv_attn_desc *d, Plan &p)
+static bool plan_attention(const sv_attn_desc *d, int cu_count, Plan &p)
 {
     p = Plan{};
     if (d->dtype == SV_F32) {
@@ -790,7 +791,7 @@ static bool plan_attention(const sv_attn_desc *d, Plan &p)
         // 106.2 / 180.0 / 344.4 / 656.5 us with the short-cache rule, 77.9 / 136.8 / 237.4 /
         // 452.2 us with this one; on a 2048-key cache the short-cache rule stays ahead
         // (516 rows: 27.9 vs 31.6 us).
-        const int64_t cus = device_cu_count();
+        const int64_t cus = cu_count;
         const bool long_cache = Tmax > 6144;
         const int64_t target = long_cache ? 4 * cus : cus;
         if (groups >= target) {
@@ -853,34 +854,42 @@ static sv_status check_attention(const sv_attn_desc *d)
     return SV_OK;
 }
 
-static void *g_mark_event = nullptr;  // sv_set_attention_mark
-static void *g_time_start = nullptr;  // sv_set_attention_timing
-static void *g_time_stop = nullptr;
+// Optional measurement events of a call (from the descriptor; NULL when unused).
+struct Events {
+    hipEvent_t start, stop, call_stop;
+};
 
-// The main attention kernel's launch; with the timing hook set, through hipExtLaunchKernel,
-// whose events take the kernel's own start and end (the times a kernel trace reports).
-template <typename K>
-static void launch_main(K kernel, dim3 grid, dim3 block, hipStream_t s, const AttnArgs &a)
+// A launch of the call; with a start or stop event, through hipExtLaunchKernel, whose events
+// take the kernel's own start and end (the times a kernel trace reports).
+template <typename K, typename... Args>
+static void launch_timed(K kernel, dim3 grid, dim3 block, hipStream_t s, hipEvent_t start, hipEvent_t stop,
+                         Args... args)
 {
-    if (g_time_start || g_time_stop)
-        hipExtLaunchKernelGGL(kernel, grid, block, 0, s, (hipEvent_t)g_time_start, (hipEvent_t)g_time_stop, 0, a);
+    if (start || stop)
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, s, start, stop, 0, args...);
     else
-        hipLaunchKernelGGL(kernel, grid, block, 0, s, a);
+        hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+}
+
+template <typename K>
+static void launch_main(K kernel, dim3 grid, dim3 block, hipStream_t s, const Events &ev, const AttnArgs &a)
+{
+    launch_timed(kernel, grid, block, s, ev.start, ev.stop, a);
 }
 
 template <int DH, int NWR, int NWK>
-static hipError_t launch_variant(const Plan &p, const AttnArgs &a, hipStream_t s)
+static hipError_t launch_variant(const Plan &p, const AttnArgs &a, hipStream_t s, const Events &ev)
 {
     if constexpr (NWR == 1) {
         if (p.spec)
-            launch_main(attn_bf16_kernel<DH, 1, NWK, true>, dim3(p.nsplit, a.Hkv, a.B), dim3(64 * NWK), s, a);
+            launch_main(attn_bf16_kernel<DH, 1, NWK, true>, dim3(p.nsplit, a.Hkv, a.B), dim3(64 * NWK), s, ev, a);
         else
-            launch_main(attn_bf16_kernel<DH, 1, NWK, false>, dim3(p.nsplit, a.Hkv, a.B), dim3(64 * NWK), s, a);
+            launch_main(attn_bf16_kernel<DH, 1, NWK, false>, dim3(p.nsplit, a.Hkv, a.B), dim3(64 * NWK), s, ev, a);
     } else {
-        launch_main(attn_bf16_kernel<DH, NWR, NWK, false>, dim3(p.blocks), dim3(64 * NWR * NWK), s, a);
+        launch_main(attn_bf16_kernel<DH, NWR, NWK, false>, dim3(p.blocks), dim3(64 * NWR * NWK), s, ev, a);
     }
     hipError_t e = hipGetLastError();
-    if (e == hipSuccess && g_mark_event) e = hipEventRecord((hipEvent_t)g_mark_event, s);
+    if (e == hipSuccess && p.nsplit == 1 && ev.call_stop) e = hipEventRecord(ev.call_stop, s);
     if (e != hipSuccess || p.nsplit == 1) return e;
     constexpr int ROWS_BLK = 32 * NWR;
     const int tile_rows = p.rows < ROWS_BLK ? p.rows : ROWS_BLK;
@@ -897,7 +906,7 @@ static hipError_t launch_variant(const Plan &p, const AttnArgs &a, hipStream_t s
     const int grid = ntask < p.max_blocks ? ntask : p.max_blocks;
     const dim3 g(grid), blk(kCombThreads);
 #define SV_COMBINE2(NSL_, SPT_, V_) \
-    hipLaunchKernelGGL((attn_combine_kernel<DH, ROWS_BLK, NSL_, SPT_, V_>), g, blk, 0, s, a, nrc, ntask)
+    launch_timed(attn_combine_kernel<DH, ROWS_BLK, NSL_, SPT_, V_>, g, blk, s, nullptr, ev.call_stop, a, nrc, ntask)
 #define SV_COMBINE(NSL_, SPT_) \
     do { if (vpt == 1) SV_COMBINE2(NSL_, SPT_, 1); else SV_COMBINE2(NSL_, SPT_, 4); } while (0)
     if (nsl == 1) SV_COMBINE(1, 1);
@@ -913,12 +922,12 @@ static hipError_t launch_variant(const Plan &p, const AttnArgs &a, hipStream_t s
 }
 
 template <int DH>
-static hipError_t launch_bf16(const Plan &p, const AttnArgs &a, hipStream_t s)
+static hipError_t launch_bf16(const Plan &p, const AttnArgs &a, hipStream_t s, const Events &ev)
 {
     switch (p.variant) {
-    case 1: return launch_variant<DH, 1, 4>(p, a, s);
-    case 2: return launch_variant<DH, 2, 2>(p, a, s);
-    default: return launch_variant<DH, 4, 1>(p, a, s);
+    case 1: return launch_variant<DH, 1, 4>(p, a, s, ev);
+    case 2: return launch_variant<DH, 2, 2>(p, a, s, ev);
+    default: return launch_variant<DH, 4, 1>(p, a, s, ev);
     }
 }
 
@@ -928,7 +937,7 @@ extern "C" size_t sv_verify_attention_workspace(const sv_attn_desc *d)
 {
     if (check_attention(d) != SV_OK) return 0;
     Plan p;
-    if (!plan_attention(d, p)) return 0;
+    if (!plan_attention(d, device_cu_count(), p)) return 0;
     return p.total;
 }
 
@@ -937,8 +946,9 @@ extern "C" sv_status sv_verify_attention(const sv_attn_desc *d, void *workspace,
     const sv_status st = check_attention(d);
     if (st != SV_OK) return st;
     if (d->B == 0) return SV_OK;
+    const int cus = device_cu_count();
     Plan p;
-    if (!plan_attention(d, p)) return SV_ERR_UNSUPPORTED;
+    if (!plan_attention(d, cus, p)) return SV_ERR_UNSUPPORTED;
     if (p.total > 0 && (!workspace || workspace_bytes < p.total || ((uintptr_t)workspace & 255)))
         return SV_ERR_WORKSPACE;
 
@@ -987,25 +997,13 @@ extern "C" sv_status sv_verify_attention(const sv_attn_desc *d, void *workspace,
         hipLaunchKernelGGL(attn_f32_kernel, dim3((unsigned)nrows), dim3(64), 0, s, a, d->D);
         e = hipGetLastError();
     } else {
-        p.max_blocks = 16 * device_cu_count();
+        p.max_blocks = 16 * cus;
         // A grid of at most one block per CU is latency-bound: with a dense cache layout
         // (no kv_off) the first tiles are loaded while the sequence lengths are in flight.
         // Larger grids skip it (their empty splits would load tiles for nothing).
-        p.spec = p.variant == 1 && !d->kv_off && p.blocks <= (unsigned)device_cu_count();
-        e = d->D == 128 ? launch_bf16<128>(p, a, s) : launch_bf16<64>(p, a, s);
+        p.spec = p.variant == 1 && !d->kv_off && p.blocks <= (unsigned)cus;
+        const Events ev{(hipEvent_t)d->ev_kernel_start, (hipEvent_t)d->ev_kernel_stop, (hipEvent_t)d->ev_call_stop};
+        e = d->D == 128 ? launch_bf16<128>(p, a, s, ev) : launch_bf16<64>(p, a, s, ev);
     }
     return e == hipSuccess ? SV_OK : SV_ERR_HIP;
-}
-
-extern "C" sv_status sv_set_attention_mark(void *event)
-{
-    g_mark_event = event;
-    return SV_OK;
-}
-
-extern "C" sv_status sv_set_attention_timing(void *start_event, void *stop_event)
-{
-    g_time_start = start_event;
-    g_time_stop = stop_event;
-    return SV_OK;
 }

@@ -16,6 +16,36 @@ constexpr int kWave = 64;
 // the maximum's weight of 1.
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 2^e in fp64, to about 1e-14 relative, for every weight a sampling decision depends on
+// (softmax sums, residual masses, CDF weights).  e = n + f with n = rint(e) and |f| <= 1/2;
+// 2^f = exp(f ln 2) by its Taylor series to degree 11 (|f ln 2| <= 0.347, so the first
+// omitted term is below 7e-15 of the sum), then 2^f is scaled by 2^n.  e = -inf gives 0.
+// (fp32 v_exp_f32 weights carry ~1e-7 relative error each, which moves a 128K-token CDF by
+// ~1e-9: far more than the fp64 arithmetic of the decisions themselves.)
+struct Exp2Taylor {
+    double c[12];
+    constexpr Exp2Taylor() : c{}
+    {
+        const double ln2 = 0.6931471805599453094;
+        double t = 1.0;
+        for (int k = 0; k < 12; ++k) {
+            c[k] = t;  // ln2^k / k!
+            t = t * ln2 / (double)(k + 1);
+        }
+    }
+};
+__device__ __forceinline__ double exp2_acc(double e)
+{
+    constexpr Exp2Taylor T;
+    e = fmax(e, -1100.0);  // below 2^-1074 the result is 0 (and -inf stays finite here)
+    const double n = rint(e);
+    const double f = e - n;  // exact
+    double p = T.c[11];
+#pragma unroll
+    for (int k = 10; k >= 0; --k) p = fma(p, f, T.c[k]);
+    return ldexp(p, (int)n);
+}
+
 // Every workspace starts with this fixed region of completion counters.  It must be zero
 // when a workspace is first used; every call leaves it zero again.  Partial results live
 // after it, so calls of any entry point and any shape can share one workspace (if they do
@@ -25,19 +55,15 @@ constexpr int kMaxCounters = (int)(kCounterBytes / sizeof(int));
 constexpr uint64_t kTagAccept = 0x53560001ULL;
 constexpr uint64_t kTagWalk = 0x53560002ULL;
 
-// Compute units of the current device (host side; cached per device).  Looping kernels
-// size their grids from it.
+// Compute units of the current device (host side, asked of the runtime on every call:
+// the library keeps no state between calls).  Looping kernels size their grids from it.
 static inline int device_cu_count()
 {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = 256;
+    return n;
 }
 
 // ---------------------------------------------------------------------------

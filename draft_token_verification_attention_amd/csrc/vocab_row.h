@@ -293,7 +293,7 @@ __device__ __forceinline__ void wave_combine_softmax(const Part *pp, int nchunk,
     M = wave_max(m);
     double z = 0.0;
     for (int c = lane; c < nchunk; c += kWave)
-        if (pp[c].s > 0.0) z += pp[c].s * exp2(((double)pp[c].m - (double)M) * kd);
+        if (pp[c].s > 0.0) z += pp[c].s * exp2_acc(((double)pp[c].m - (double)M) * kd);
     // fixed-order reduction: deterministic
     Z = wave_sum(z);
 }
@@ -301,11 +301,11 @@ __device__ __forceinline__ void wave_combine_softmax(const Part *pp, int nchunk,
 // Softmax statistics of several rows at once from their chunk partials: rows are laid
 // out over aligned groups of LPR lanes (LPR = 16, 32 or 64; a lane strides over chunks
 // c = lane % LPR + k LPR), so one wave pass covers 64 / LPR rows.  Per row:
-// M = max_c m_c and Z = sum_c S_c 2^((m_c - M) k) with the rescale factor in fp32.  Must
-// be called by a whole wave; `row` is this lane's row (rows >= nrows compute nothing
+// M = max_c m_c and Z = sum_c S_c 2^((m_c - M) k), the rescale factor in fp64 (exp2_acc).
+// Must be called by a whole wave; `row` is this lane's row (rows >= nrows compute nothing
 // useful), the results are valid in every lane of the row's group.
 template <int LPR, typename Part>
-__device__ __forceinline__ void group_combine_softmax(const Part *pp, int row, int nrows, int nchunk, float kf,
+__device__ __forceinline__ void group_combine_softmax(const Part *pp, int row, int nrows, int nchunk, double kd,
                                                       float &M, double &Z)
 {
     const int c0 = (int)(threadIdx.x % LPR);
@@ -317,7 +317,7 @@ __device__ __forceinline__ void group_combine_softmax(const Part *pp, int row, i
     if (row < nrows)
         for (int c = c0; c < nchunk; c += LPR) {
             const Part q = pp[(int64_t)row * nchunk + c];
-            if (q.s > 0.0) z += q.s * (double)exp2_fast((q.m - M) * kf);
+            if (q.s > 0.0) z += q.s * exp2_acc(((double)q.m - (double)M) * kd);
         }
     Z = group_total<LPR>(z, 0.0, OpAdd());
 }

@@ -118,10 +118,10 @@ __global__ __launch_bounds__(kRowThreads) void walk_level_kernel(WalkArgs a, Wal
 #pragma unroll
         for (int k = 0; k < kPerThread; ++k) m = fmaxf(m, x[k]);
         m = block_max(m, fscr);
+        // weights in fp64 (exp2_acc; -inf logits weigh 0): the draw depends on these sums
         double s = 0.0;
 #pragma unroll
-        for (int k = 0; k < kPerThread; ++k)
-            if (x[k] != -INFINITY) s += (double)exp2_fast((x[k] - m) * a.kf);
+        for (int k = 0; k < kPerThread; ++k) s += exp2_acc(((double)x[k] - (double)m) * a.kd);
         s = block_sum(s, dscr);
         part.m = m;
         part.arg = 0;
@@ -184,13 +184,13 @@ __global__ __launch_bounds__(kRowThreads) void walk_level_kernel(WalkArgs a, Wal
             int found;
             double cum;
             wave_find_chunk(a.nchunk, target,
-                            [&](int cc) { return pp[cc].s * exp2(((double)pp[cc].m - (double)M) * a.kd); }, found,
+                            [&](int cc) { return pp[cc].s * exp2_acc(((double)pp[cc].m - (double)M) * a.kd); }, found,
                             cum);
             if (threadIdx.x == 0) {
                 s_chunk = found;
                 s_base = cum;
                 s_target = target;
-                s_factor = exp2(((double)pp[found].m - (double)M) * a.kd);
+                s_factor = exp2_acc(((double)pp[found].m - (double)M) * a.kd);
                 s_mc = pp[found].m;
             }
         }
@@ -198,7 +198,7 @@ __global__ __launch_bounds__(kRowThreads) void walk_level_kernel(WalkArgs a, Wal
         const int cb = s_chunk * kChunk;
         const float mc = s_mc;
         const double f = s_factor;
-        auto weight = [&](float l, float) -> double { return (double)exp2_fast((l - mc) * a.kf) * f; };
+        auto weight = [&](float l, float) -> double { return exp2_acc(((double)l - (double)mc) * a.kd) * f; };
         int y = chunk_inverse_cdf<kPerThread, VEC>(row, nullptr, cb, a.V, s_base, s_target, weight, scan, iscr);
         if (y < 0) y = cb;  // no mass in the chunk at all (cannot happen for the chunk found)
         if (threadIdx.x == 0) s_y = y;

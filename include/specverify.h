@@ -23,9 +23,11 @@
  *     every call leaves them zero again (partial results live after them).  So one
  *     workspace, zero-filled once, may serve any sequence of calls of any entry point and
  *     shape, provided the calls do not overlap in time (e.g. they share one stream).
- *   - The library allocates no memory.  Its only global state is the two benchmark
- *     hooks at the end of this header (event handles, off by default); no result
- *     depends on them.
+ *   - The library allocates no memory and keeps no state between calls: whatever a call
+ *     needs (device attributes, occupancy) it asks the runtime for during the call.
+ *     Completion counters return to zero at the end of every kernel that uses them, and
+ *     a launch that fails never runs, so a call that returns SV_ERR_HIP leaves its
+ *     workspace's counter region zero as well.
  *   - No C++ exception crosses this interface.
  */
 #ifndef SPECVERIFY_H
@@ -113,7 +115,8 @@ SV_API sv_status sv_build_tree_mask(const int32_t *parents, int32_t n, int32_t p
 /*        and every sequence must own max_prefix + n_q token slots, since the kernel may */
 /*        read any of them (rows past P + n_q are read but never used).                  */
 /*   prefix_len  device int32 [B];  max_prefix (host) must bound every prefix_len[b]:    */
-/*        it sizes the launch; a sequence whose P exceeds it gets NaN output rows.        */
+/*        it sizes the launch; a sequence whose P exceeds it, or is negative, reads       */
+/*        nothing and gets NaN output rows (and NaN lse).                                */
 /*   tree_bits   TREE only: device uint32 rows as produced by sv_build_tree_mask, for    */
 /*        n_q nodes; sequence b uses tree_bits + b*tree_sb (tree_sb = 0: one shared tree).*/
 /*   out  [B][n_q][Hq][D] of `dtype` at out + b*o_sb + i*o_st + h*o_sh                   */
@@ -126,6 +129,13 @@ SV_API sv_status sv_build_tree_mask(const int32_t *parents, int32_t n, int32_t p
 /* q, k, v, strides, kv_sb and kv_off[b] that are multiples of 8 elements, and out and  */
 /* its strides aligned to 4 elements (else SV_ERR_UNSUPPORTED; kv_off is not checked).   */
 /* bf16 calls with at most 32 query rows per KV head (n_q x Hq/Hkv) take B <= 65535.     */
+/* Measurement events (optional, hipEvent_t, NULL when unused; no result depends on them):*/
+/*   ev_kernel_start / ev_kernel_stop: the bf16 main attention kernel is launched so that  */
+/*        they take its own start and end times (the span a kernel trace reports,         */
+/*        without the dispatch ahead of it);                                            */
+/*   ev_call_stop: the end time of the call's last kernel -- the split combine's own end  */
+/*        when the call has one (launched the same way), else the main kernel's end.      */
+/*        ev_kernel_start to ev_call_stop spans the whole attention pass on the GPU.      */
 /* ---------------------------------------------------------------------------------- */
 typedef struct sv_attn_desc {
     sv_dtype dtype;
@@ -147,6 +157,9 @@ typedef struct sv_attn_desc {
     void *out;
     int64_t o_sb, o_st, o_sh;
     float *lse;
+    void *ev_kernel_start;
+    void *ev_kernel_stop;
+    void *ev_call_stop;
 } sv_attn_desc;
 
 SV_API size_t sv_verify_attention_workspace(const sv_attn_desc *desc);
@@ -218,7 +231,9 @@ SV_API sv_status sv_spec_accept(const sv_accept_desc *desc, void *workspace, siz
 /*   out_tokens device int32 [B][max_depth+1] = (tokens of n_1..n_J, the choice at n_J,  */
 /*              -1, ...)                                                                 */
 /*   dev_status optional device int32 [B]: 0, or 3 when the walk would go below         */
-/*              max_depth (outputs then stop at max_depth)                               */
+/*              max_depth: it then stops at its node at depth max_depth and emits the    */
+/*              choice there as the extra token (accept_len = max_depth; still a draw    */
+/*              from the target at that node)                                            */
 /* Supported: 1 <= n, 0 <= max_depth <= 63, 1 <= V, B <= 32768.                          */
 /* ---------------------------------------------------------------------------------- */
 typedef struct sv_walk_desc {
@@ -238,22 +253,6 @@ typedef struct sv_walk_desc {
 SV_API size_t sv_tree_walk_workspace(const sv_walk_desc *desc);
 SV_API sv_status sv_tree_walk(const sv_walk_desc *desc, void *workspace, size_t workspace_bytes,
                        void *stream);
-
-/* Measurement hook for benchmarks.  When `event` (a hipEvent_t) is not NULL, every later */
-/* sv_verify_attention call also records it on its stream right after its main attention */
-/* kernel and before the split combine (if the call has one), so a caller's own events   */
-/* around the call split its time between the two kernels.  NULL turns the hook off.     */
-/* Process-wide setting without synchronization: set it from the launching thread.       */
-/* Always returns SV_OK; a failed record shows up as SV_ERR_HIP from the call.          */
-SV_API sv_status sv_set_attention_mark(void *event);
-
-/* Measurement hook for benchmarks.  When either event (a hipEvent_t) is not NULL, every     */
-/* later sv_verify_attention call launches its main attention kernel so that `start_event`  */
-/* takes the kernel's start time and `stop_event` its end time (the span a kernel trace     */
-/* reports, without the dispatch ahead of the kernel).  Either may be NULL; both NULL turn  */
-/* the hook off.  Process-wide setting without synchronization: set it from the launching   */
-/* thread.  Always returns SV_OK; a failed launch shows up as SV_ERR_HIP from the call.      */
-SV_API sv_status sv_set_attention_timing(void *start_event, void *stop_event);
 
 /* Human-readable name of a status code (static storage). */
 SV_API const char *sv_status_string(sv_status status);

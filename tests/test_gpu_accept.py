@@ -3,7 +3,8 @@ GPU's own draws.
 
 Bar: accepted lengths and emitted tokens bit-exact on the same Philox uniforms, except in
 sequences the oracle flags as near-threshold (a ratio-test uniform within 1e-6 of p/q, or
-the extra draw within 1e-6*Z of a CDF boundary); those are counted and reported.
+the extra draw within 1e-10 of probability mass of a CDF boundary); those are counted,
+reported, and bounded: at most 2 per call below 1000 sequences, else 1e-3 of them.
 """
 import math
 
@@ -35,13 +36,22 @@ def _run_both(mode, target, draft, toks, tau, seed, step=0, stream_ids=None, wan
     return ref, got
 
 
-def _assert_parity(ref, got, label=""):
+def near_threshold_limit(n):
+    """Flagged sequences a parity check may excuse: at most 2 below 1000 compared, else
+    1e-3 of them (a uniform within 1e-6 of its threshold has probability about 2e-6 per
+    decision, so a flag that fires more often than this is broken, not unlucky)."""
+    return 2 if n < 1000 else int(1e-3 * n)
+
+
+def _assert_parity(ref, got, label="", excused_ok=None):
     flagged = ref["flags"] != 0
     same = (ref["accept_len"] == got["accept_len"]) & np.all(ref["out_tokens"] == got["out_tokens"], axis=1)
     bad = ~same & ~flagged
     print("%s sequences=%d near-threshold=%d mismatched(near)=%d mismatched(other)=%d"
           % (label, len(same), flagged.sum(), (~same & flagged).sum(), bad.sum()))
     assert not bad.any(), np.nonzero(bad)[0][:10]
+    limit = near_threshold_limit(len(same)) if excused_ok is None else excused_ok
+    assert flagged.sum() <= limit, (flagged.sum(), limit)
     assert np.all(got["status"] == 0)
 
 
@@ -192,3 +202,19 @@ def test_shared_workspace_across_entry_points_and_shapes():
         from svgpu import attention_on_gpu, rows_of
         out, _ = attention_on_gpu(inp, 0.09, split_keys=128)
         assert np.abs(rows_of(out, rows) - ref_o).max() <= 2e-2
+
+
+def test_crafted_near_threshold_decisions():
+    """Ratio tests placed 1e-7 ... 1e-5 from p/q and extra draws placed 1e-11 ... 1e-9 from a
+    CDF boundary (inputs built from NumPy's own Philox): every decision outside its window
+    (1e-6 for a ratio test, 1e-10 of probability mass for a draw) must match the oracle bit
+    for bit, which bounds the GPU's error in p/q and in the CDF; the sequences the oracle
+    flags are exactly the crafted ones inside the window."""
+    from test_oracle_flags import DELTAS, DRAW_DELTAS, STEPS, crafted_draw_inputs, crafted_ratio_inputs, _streams
+    st = _streams(48)
+    near = np.array([abs(STEPS[b % len(STEPS)]) < 1.0 for b in range(len(st))])
+    for make, deltas, seed, step in ((crafted_ratio_inputs, DELTAS, 101, 3), (crafted_draw_inputs, DRAW_DELTAS, 102, 5)):
+        tgt, dr, toks = make(seed, step, st, deltas)
+        ref, got = _run_both(SAMPLE, tgt, dr, toks, 1.0, seed=seed, step=step, stream_ids=st.astype(np.int64))
+        assert np.array_equal(ref["flags"] != 0, near)
+        _assert_parity(ref, got, make.__name__, excused_ok=int(near.sum()))

@@ -234,6 +234,24 @@ def test_prefix_beyond_bound_gives_nan():
     assert np.isnan(out[1]).all() and np.isnan(lse[1]).all()
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("split_keys", [0, 64])
+def test_negative_prefix_gives_nan(dtype, split_keys):
+    """A negative prefix length reads nothing and gives NaN rows, like one beyond max_prefix
+    (with 64-key splits the call also runs the split combine); the other sequences match
+    the oracle."""
+    inp = synth.attention_inputs(8, B=3, n_q=4, Hq=8, Hkv=2, D=128, prefix_len=[100, 100, 37], dtype=dtype)
+    ref, ref_lse, rows = oracle.attention(inp, scale=0.1)
+    bad = dict(inp)
+    bad["prefix_len"] = np.array([100, -3, 37], np.int32)
+    out, lse = attention_on_gpu(bad, 0.1, max_prefix=100, split_keys=split_keys)
+    assert np.isnan(out[1]).all() and np.isnan(lse[1]).all()
+    keep = rows[:, 0] != 1
+    tol = 2e-2 if dtype == "bf16" else 1e-4
+    assert np.abs(rows_of(out, rows[keep]) - ref[keep]).max() <= tol
+    assert np.isfinite(out[[0, 2]]).all()
+
+
 def test_batch_split_edges():
     """A batch of many 256-key splits: sequences that end exactly on a split boundary, empty
     prefixes, sequences beyond max_prefix (NaN rows), and repeated calls on one workspace."""
