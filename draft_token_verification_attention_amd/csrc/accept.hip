@@ -25,9 +25,10 @@
 //            segment holding u* Z (block-wide scan), then (one wave, token order) the extra
 //            token.  When the residual has no mass, or the layout is not the vector one, it
 //            finds the chunk first, then the token inside it.
-// Every exponential a sampling decision depends on -- the softmax sums of the statistics
-// pass, the residual and CDF weights, the decided p(x), q(x) -- is fp64 (exp2_acc / exp),
-// and so is every sum; the optional alpha pass keeps fp32 exponentials.
+// Exponentials of the statistics pass (and of the optional alpha pass) run in fp32: their
+// normalizers are good to about 1e-9, ample for the ratio tests.  The decided p(x), q(x),
+// the residual and CDF weights, and the normalizers the draw uses are fp64 (exp, exp2_acc),
+// and so is every sum.
 #include "vocab_row.h"
 
 namespace {
@@ -54,9 +55,9 @@ struct RowPart {
     int32_t arg;
     double s;
 };
-struct ResPart {
-    double r;
-    double p;
+struct ResPart {   // per residual chunk: sums of wp and wq over the tokens with residual
+    double a, b;    // mass (estimated), and of wp and wq over every token of the chunk
+    double wp, wq;
 };
 
 struct AcceptWs {
@@ -64,7 +65,7 @@ struct AcceptWs {
     RowPart *part;   // [B][rows][npart]: one partial per (chunk, wave)
     double *u;       // [B][gamma + 1]: the round's uniforms (ratio tests, then the extra token)
     ResPart *res;    // [B][nchunk]
-    double *seg;     // [B][nchunk][PER]: residual mass of each 256-token segment of a chunk
+    double *seg;     // [B][nchunk][PER][2]: (A, B) of each 256-token segment of a chunk
     double *apart;   // [B][gamma][nchunk]
 };
 
@@ -104,8 +105,8 @@ static WsLayout accept_layout(int B, int gamma, int V)
     o += align256((size_t)B * (gamma + 1) * sizeof(double));
     L.res = o;  // per resample chunk: the smallest chunks are kResChunk tokens
     o += align256((size_t)B * (((size_t)V + kResChunk - 1) / kResChunk) * sizeof(ResPart));
-    L.seg = o;  // 256-token segments: enough for either chunk size
-    o += align256((size_t)B * (nchunk + 3) * 16 * sizeof(double));
+    L.seg = o;  // (A, B) of every 256-token segment: enough for either chunk size
+    o += align256((size_t)B * (nchunk + 3) * 16 * 2 * sizeof(double));
     L.apart = o;
     o += align256((size_t)B * gamma * nchunk * sizeof(double));
     L.total = o;
@@ -252,18 +253,20 @@ __global__ __launch_bounds__(kRowThreads) void accept_stats_kernel(AcceptArgs a,
             part.s = 0.0;
         } else {
             // each thread: its own max and its sum relative to it (no barrier); then the
-            // block rescales the per-thread sums to the chunk max.  Weights and rescale in
-            // fp64 (exp2_acc): the decisions downstream depend on these sums.
+            // block rescales the per-thread sums to the chunk max.  fp32 exponentials: these
+            // normalizers (good to about 1e-9) serve the ratio tests, whose tolerance is
+            // 1e-6, and tell the residual draw which tokens carry residual mass; the draw
+            // itself weighs that mass with exact normalizers of its own.
             float mt = -INFINITY;
 #pragma unroll
             for (int k = 0; k < kPerThread; ++k) mt = fmaxf(mt, xv[k]);
-            // branch-free: -inf logits (masked, or beyond V) weigh exp2_acc(-inf) = 0
-            const double mref = mt == -INFINITY ? 0.0 : (double)mt;
+            // branch-free: -inf logits (masked, or beyond V) weigh exp2_fast(-inf) = 0
+            const float mref = mt == -INFINITY ? 0.0f : mt;
             double st = 0.0;
 #pragma unroll
-            for (int k = 0; k < kPerThread; ++k) st += exp2_acc(((double)xv[k] - mref) * a.kd);
+            for (int k = 0; k < kPerThread; ++k) st += (double)exp2_fast((xv[k] - mref) * a.kf);
             const float m = kParts > 1 ? wave_max(mt) : block_max(mt, fscr);
-            const double z = st > 0.0 ? st * exp2_acc(((double)mt - (double)m) * a.kd) : 0.0;
+            const double z = st > 0.0 ? st * (double)exp2_fast((mt - m) * a.kf) : 0.0;
             const double sm = kParts > 1 ? wave_sum(z) : block_sum(z, dscr);
             part.m = m;
             part.arg = 0;
@@ -445,52 +448,82 @@ __global__ __launch_bounds__(kRowThreads, 2) void accept_resample_kernel(AcceptA
 
     const float *prow = a.target + ((int64_t)b * (g + 1) + J) * a.V;
     const float *qrow = J < g ? a.draft + ((int64_t)b * g + J) * a.V : nullptr;
-    // with no draft row (J == gamma) q is 0: iZq = 0, and Mq = Mp keeps the exponent finite
-    const double Mp = sM[J], Mq = J < g ? sM[g + 1 + J] : Mp;
-    const double iZp = 1.0 / sZ[J], iZq = J < g ? 1.0 / sZ[g + 1 + J] : 0.0;
     const int base = c * kChunk;
 
-    // weight of token e: residual (or p when every draft was kept / the residual is empty),
-    // every weight in fp64 (exp2_acc)
-    auto p_of = [&](float l) { return exp2_acc(((double)l - Mp) * a.kd) * iZp; };
-    auto q_of = [&](float l) { return exp2_acc(((double)l - Mq) * a.kd) * iZq; };
+    // Weights of token e relative to the rows' maxima, in fp64 (exp2_acc):
+    // wp = 2^((l_p(e) - Mp) k), wq likewise (0 with no draft row, J == gamma).  The residual is
+    // r(e) = max(0, wp/Zp - wq/Zq) with the normalizers Zp = sum wp, Zq = sum wq, which only
+    // the last block knows exactly (every block sums its chunk of both rows).  The statistics
+    // pass gives them to about 1e-9 (fp32 exponentials): enough to tell which tokens carry
+    // residual mass (wp/Zp' > wq/Zq'), not to weigh it.  So every block stores, per 256-token
+    // segment and per chunk, the sums A = sum wp and B = sum wq over those tokens, and the
+    // chunk's totals of wp and wq; the last block weighs a segment as A/Zp - B/Zq with the
+    // exact normalizers.  (A token misjudged by the estimate holds a residual smaller than the
+    // estimate's error: the segment masses are off by its square.)
+    const double Mp = sM[J], Mq = J < g ? sM[g + 1 + J] : Mp;
+    const double iZp_est = 1.0 / sZ[J], iZq_est = J < g ? 1.0 / sZ[g + 1 + J] : 0.0;
+    const double qmask = J < g ? 1.0 : 0.0;
+    auto wp_of = [&](float l) { return exp2_acc(((double)l - Mp) * a.kd); };
+    auto wq_of = [&](float l) { return exp2_acc(((double)l - Mq) * a.kd) * qmask; };
 
     float xp[kPerThread], xq[kPerThread];
     load_chunk2<VEC, kPerThread>(prow, qrow ? qrow : prow, base, a.V, xp, xq);
-    // branch-free: a position at or beyond V holds -inf, whose weight exp2_fast(-inf) = 0
-    // per thread, the residual mass of each float4 group (VEC layout: group k4 of wave w
-    // is part of the chunk's 256-token segment 4 k4 + w, in token order)
-    double rs = 0.0, ps = 0.0;
-    double r4[kPerThread / 4];
+    // branch-free: a position at or beyond V holds -inf, whose weight is 0.  Per thread, the
+    // sums of each float4 group (VEC layout: group k4 of wave w is part of the chunk's
+    // 256-token segment 4 k4 + w, in token order)
+    double ta = 0.0, tb = 0.0, tp = 0.0, tq = 0.0;
+    double a4[kPerThread / 4], b4[kPerThread / 4];
 #pragma unroll
     for (int k4 = 0; k4 < kPerThread / 4; ++k4) {
-        r4[k4] = 0.0;
+        a4[k4] = 0.0;
+        b4[k4] = 0.0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const double p = p_of(xp[4 * k4 + j]);
-            ps += p;
-            r4[k4] += fmax(0.0, p - q_of(xq[4 * k4 + j]));
+            const double wp = wp_of(xp[4 * k4 + j]), wq = wq_of(xq[4 * k4 + j]);
+            tp += wp;
+            tq += wq;
+            const bool in = wp * iZp_est > wq * iZq_est;
+            a4[k4] += in ? wp : 0.0;
+            b4[k4] += in ? wq : 0.0;
         }
-        rs += r4[k4];
+        ta += a4[k4];
+        tb += b4[k4];
     }
     if (VEC) {
         const int wv = threadIdx.x / kWave;
-        double *sg = w.seg + ((int64_t)b * a.rnchunk + c) * kPerThread;
+        double *sg = w.seg + 2 * (((int64_t)b * a.rnchunk + c) * kPerThread);
 #pragma unroll
         for (int k4 = 0; k4 < kPerThread / 4; ++k4) {
-            const double t = wave_sum(r4[k4]);
-            if (threadIdx.x % kWave == 0) st_coherent(&sg[4 * k4 + wv], t);
+            const double sa = wave_sum(a4[k4]), sb = wave_sum(b4[k4]);
+            if (threadIdx.x % kWave == 0) {
+                st_coherent(&sg[2 * (4 * k4 + wv)], sa);
+                st_coherent(&sg[2 * (4 * k4 + wv) + 1], sb);
+            }
         }
     }
-    block_sum2(rs, ps, dscr);
+    block_sum2(ta, tb, dscr);
+    block_sum2(tp, tq, dscr);
     if (threadIdx.x == 0) {
-        st_coherent(&w.res[(int64_t)b * a.rnchunk + c].r, rs);
-        st_coherent(&w.res[(int64_t)b * a.rnchunk + c].p, ps);
+        ResPart *rp = &w.res[(int64_t)b * a.rnchunk + c];
+        st_coherent(&rp->a, ta);
+        st_coherent(&rp->b, tb);
+        st_coherent(&rp->wp, tp);
+        st_coherent(&rp->wq, tq);
     }
     if (!arrive_last(&w.cnt[b], a.rnchunk, &last_flag)) return;
 
+    // ---- last block: the exact normalizers, then the extra token ----
+    const ResPart *rp = w.res + (int64_t)b * a.rnchunk;
+    // (every thread's share of the chunk totals, loaded first: their sum gates all the rest)
+    double zp = 0.0, zq = 0.0;
+    for (int cc = threadIdx.x; cc < a.rnchunk; cc += kRowThreads) {
+        zp += rp[cc].wp;
+        zq += rp[cc].wq;
+    }
     // wave 0, the residual's 256-token segment starting at token seg0 holding u* Z, whose
     // mass before it is sbase: the token inside it (every lane returns it)
+    double iZp = 0.0, iZq = 0.0;
+    auto r_of = [&](float lp, float lq) { return fmax(0.0, wp_of(lp) * iZp - wq_of(lq) * iZq); };
     auto token_in_segment = [&](int seg0, double sbase, double target) -> int {
         const int lane = threadIdx.x;
         const int e0 = seg0 + 4 * lane;  // this lane's four tokens
@@ -499,10 +532,10 @@ __global__ __launch_bounds__(kRowThreads, 2) void accept_resample_kernel(AcceptA
         const float4 fq = *reinterpret_cast<const float4 *>((qrow ? qrow : prow) + ec);
         const bool in = e0 < a.V;
         double wt[4];
-        wt[0] = in ? fmax(0.0, p_of(fp.x) - q_of(fq.x)) : 0.0;
-        wt[1] = in ? fmax(0.0, p_of(fp.y) - q_of(fq.y)) : 0.0;
-        wt[2] = in ? fmax(0.0, p_of(fp.z) - q_of(fq.z)) : 0.0;
-        wt[3] = in ? fmax(0.0, p_of(fp.w) - q_of(fq.w)) : 0.0;
+        wt[0] = in ? r_of(fp.x, fq.x) : 0.0;
+        wt[1] = in ? r_of(fp.y, fq.y) : 0.0;
+        wt[2] = in ? r_of(fp.z, fq.z) : 0.0;
+        wt[3] = in ? r_of(fp.w, fq.w) : 0.0;
         const double lsum = ((wt[0] + wt[1]) + wt[2]) + wt[3];
         const double c0 = sbase + wave_scan_incl(lsum, 0.0, OpAdd()) - lsum;
         int hit = -1, lastpos = -1;
@@ -529,21 +562,29 @@ __global__ __launch_bounds__(kRowThreads, 2) void accept_resample_kernel(AcceptA
     };
 
     // last block, residual with mass (the common case): the block reads every 256-token
-    // segment sum of the sequence at once (kSegPerThread consecutive ones per thread, so in
-    // token order, coalesced), scans them, finds the segment holding u* Z_r with Z_r their
-    // total, and wave 0 finds the token inside it: two memory round trips
+    // segment's (A, B) of the sequence at once (kSegPerThread consecutive segments per
+    // thread, so in token order, coalesced), weighs them with the exact normalizers, scans
+    // them, finds the segment holding u* Z_r with Z_r their total, and wave 0 finds the token
+    // inside it
     if (VEC && a.rnchunk * kPerThread <= kRowThreads * kSegPerThread) {
         static_assert(kSegPerThread == 4 && kPerThread % kSegPerThread == 0, "whole threads of segments");
         const int t = threadIdx.x, lane = t % kWave, wv = t / kWave;
         const int nseg = a.rnchunk * kPerThread;
         const bool live = t * kSegPerThread < nseg;
-        // two unconditional 16-byte loads from a clamped thread, zeroed past the end
+        // four unconditional 16-byte loads (A, B of four segments) from a clamped thread
         const double2 *sg = reinterpret_cast<const double2 *>(
-            w.seg + (int64_t)b * nseg + (int64_t)min(t, nseg / kSegPerThread - 1) * kSegPerThread);
-        const double2 h0 = sg[0], h1 = sg[1];
-        const double v[kSegPerThread] = {live ? h0.x : 0.0, live ? h0.y : 0.0, live ? h1.x : 0.0, live ? h1.y : 0.0};
+            w.seg + 2 * ((int64_t)b * nseg + (int64_t)min(t, nseg / kSegPerThread - 1) * kSegPerThread));
+        const double2 h0 = sg[0], h1 = sg[1], h2 = sg[2], h3 = sg[3];
+        block_sum2(zp, zq, dscr);
+        iZp = 1.0 / zp;
+        iZq = qrow ? 1.0 / zq : 0.0;
+        const double2 hs[kSegPerThread] = {h0, h1, h2, h3};
+        double v[kSegPerThread];
+#pragma unroll
+        for (int j = 0; j < kSegPerThread; ++j) v[j] = live ? fmax(0.0, hs[j].x * iZp - hs[j].y * iZq) : 0.0;
         const double ts = ((v[0] + v[1]) + v[2]) + v[3];
         const double incl_w = wave_scan_incl(ts, 0.0, OpAdd());
+        __syncthreads();  // dscr is reused below
         if (lane == kWave - 1) dscr[wv] = incl_w;
         __syncthreads();
         double wbase = 0.0, zr = 0.0;
@@ -601,23 +642,24 @@ __global__ __launch_bounds__(kRowThreads, 2) void accept_resample_kernel(AcceptA
             return;
         }
         __syncthreads();  // no residual mass: the chunk path below, with p
+    } else {
+        block_sum2(zp, zq, dscr);
+        iZp = 1.0 / zp;
+        iZq = qrow ? 1.0 / zq : 0.0;
     }
 
     // otherwise: locate the chunk holding u* Z (wave 0), then scan it in token order
     if (threadIdx.x < kWave) {
-        const ResPart *rp = w.res + (int64_t)b * a.rnchunk;
-        double zr = 0.0, zp = 0.0;
-        for (int cc = threadIdx.x; cc < a.rnchunk; cc += kWave) {
-            zr += rp[cc].r;
-            zp += rp[cc].p;
-        }
+        double zr = 0.0;
+        for (int cc = threadIdx.x; cc < a.rnchunk; cc += kWave) zr += fmax(0.0, rp[cc].a * iZp - rp[cc].b * iZq);
         zr = wave_sum(zr);
-        zp = wave_sum(zp);
         const bool usep = !(zr > 0.0);
-        const double target = s_uextra * (usep ? zp : zr);
+        const double target = s_uextra * (usep ? 1.0 : zr);
         int chunk;
         double cbase;
-        wave_find_chunk(a.rnchunk, target, [&](int cc) { return usep ? rp[cc].p : rp[cc].r; }, chunk, cbase);
+        wave_find_chunk(a.rnchunk, target,
+                        [&](int cc) { return usep ? rp[cc].wp * iZp : fmax(0.0, rp[cc].a * iZp - rp[cc].b * iZq); },
+                        chunk, cbase);
         if (threadIdx.x == 0) {
             s_chunk = chunk;
             s_base = cbase;
@@ -630,13 +672,13 @@ __global__ __launch_bounds__(kRowThreads, 2) void accept_resample_kernel(AcceptA
     const bool usep = s_usep != 0;
     const int cbase = cs * kChunk;
     if (VEC && !(usep && qrow)) {
-        // The residual (or p, with no draft row) has its 256-token segment sums stored:
-        // wave 0 finds the segment holding u* Z, then the token inside it.
+        // The residual (or p, with no draft row) has its segment sums stored: wave 0 finds the
+        // segment holding u* Z, then the token inside it.
         if (threadIdx.x < kWave) {
             const int lane = threadIdx.x;
             const double target = s_target;
-            const double *sg = w.seg + ((int64_t)b * a.rnchunk + cs) * kPerThread;
-            const double v = lane < kPerThread ? sg[lane] : 0.0;
+            const double *sg = w.seg + 2 * (((int64_t)b * a.rnchunk + cs) * kPerThread);
+            const double v = lane < kPerThread ? fmax(0.0, sg[2 * lane] * iZp - sg[2 * lane + 1] * iZq) : 0.0;
             const double incl = wave_scan_incl(v, 0.0, OpAdd());
             const double excl = s_base + incl - v;
             const uint64_t pass = __ballot(v > 0.0 && s_base + incl > target);
@@ -650,10 +692,7 @@ __global__ __launch_bounds__(kRowThreads, 2) void accept_resample_kernel(AcceptA
         return;
     }
     const bool twor = !usep && qrow;
-    auto weight = [&](float lp, float lq) -> double {
-        const double p = p_of(lp);
-        return twor ? fmax(0.0, p - q_of(lq)) : p;
-    };
+    auto weight = [&](float lp, float lq) -> double { return twor ? r_of(lp, lq) : wp_of(lp) * iZp; };
     int y = chunk_inverse_cdf<PER, VEC>(prow, twor ? qrow : nullptr, cbase, a.V, s_base, s_target, weight, scan, iscr);
     if (y < 0) y = cbase;  // no mass in the chunk at all (cannot happen for the chunk found)
     if (threadIdx.x == 0) a.out_tokens[(int64_t)b * (g + 1) + J] = y;
@@ -679,19 +718,17 @@ static int stats_resident_blocks()
     return per_cu * device_cu_count();
 }
 
-// The residual draw: small calls in the vector layout on kResChunk chunks, others on the
-// stats chunks.
+// The residual draw runs on chunks of its own: kResChunk (2048) tokens for small calls in
+// the vector layout, 4096 otherwise.  Each of its tokens takes two fp64 exponentials, so
+// the statistics pass's 16384-token chunks would hold 128 logits per thread (256 registers
+// and spills, 50 us on the 64-sequence batch).
 template <bool VEC, int PER>
 static hipError_t launch_resample(const AcceptArgs &a0, const AcceptWs &w, hipStream_t s, size_t lds)
 {
     AcceptArgs a = a0;
-    if constexpr (VEC && PER == 16) {
-        a.rnchunk = (a.V + kResChunk - 1) / kResChunk;
-        return launch(accept_resample_kernel<true, kResPer>, dim3(a.rnchunk, a.B), s, a, w, lds);
-    } else {
-        a.rnchunk = a.nchunk;
-        return launch(accept_resample_kernel<VEC, PER>, dim3(a.rnchunk, a.B), s, a, w, lds);
-    }
+    constexpr int RP = (VEC && PER == 16) ? kResPer : 16;
+    a.rnchunk = (a.V + RP * kRowThreads - 1) / (RP * kRowThreads);
+    return launch(accept_resample_kernel<VEC, RP>, dim3(a.rnchunk, a.B), s, a, w, lds);
 }
 
 template <bool VEC, int PER>
