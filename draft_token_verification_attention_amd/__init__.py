@@ -18,6 +18,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libspecverify.so")
 
 SV_OK, SV_ERR_INVALID_ARG, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_HIP = range(5)
+SV_STATIC_SCRATCH_BYTES = 16 << 20
 SV_F32, SV_BF16 = 0, 1
 SV_GREEDY, SV_SAMPLE = 0, 1
 SV_MASK_CAUSAL, SV_MASK_TREE = 0, 1
@@ -54,8 +55,8 @@ class sv_walk_desc(ctypes.Structure):
 
 
 EXPORTS = ("sv_build_tree_mask", "sv_verify_attention_workspace", "sv_verify_attention",
-           "sv_spec_accept_workspace", "sv_spec_accept", "sv_tree_walk_workspace", "sv_tree_walk",
-           "sv_status_string")
+           "sv_spec_accept_workspace", "sv_spec_accept", "sv_spec_accept_static", "sv_tree_walk_workspace",
+           "sv_tree_walk", "sv_status_string")
 
 
 def _load():
@@ -73,6 +74,8 @@ def _load():
     L.sv_spec_accept_workspace.restype = ctypes.c_size_t
     L.sv_spec_accept.argtypes = [ctypes.POINTER(sv_accept_desc), _P, ctypes.c_size_t, _P]
     L.sv_spec_accept.restype = ctypes.c_int
+    L.sv_spec_accept_static.argtypes = [ctypes.POINTER(sv_accept_desc), _P]
+    L.sv_spec_accept_static.restype = ctypes.c_int
     L.sv_tree_walk_workspace.argtypes = [ctypes.POINTER(sv_walk_desc)]
     L.sv_tree_walk_workspace.restype = ctypes.c_size_t
     L.sv_tree_walk.argtypes = [ctypes.POINTER(sv_walk_desc), _P, ctypes.c_size_t, _P]
@@ -223,6 +226,25 @@ def sv_spec_accept(mode: int, target, draft, draft_tokens, temperature: float, s
     ws = workspace(nb, dev)
     _check(lib.sv_spec_accept(ctypes.byref(d), _ptr(ws), nb, _stream(dev)), "sv_spec_accept")
     return dict(accept_len=acc, out_tokens=out, alpha=alpha, status=status)
+
+
+def sv_spec_accept_static(mode: int, target, draft, draft_tokens, temperature: float, seed: int, step: int = 0,
+                          stream_ids=None, want_alpha: bool = False, out=None):
+    """sv_spec_accept on the library's fixed device scratch (no workspace argument).  The
+    output tensors can be passed in (``out`` = a dict like the one returned) so that the
+    call itself allocates nothing.  Returns that dict."""
+    _need_cuda(target, draft, draft_tokens, stream_ids)
+    B, g1, V = target.shape
+    dev = target.device
+    if out is None:
+        out = dict(accept_len=torch.empty(B, dtype=torch.int32, device=dev),
+                   out_tokens=torch.empty((B, g1), dtype=torch.int32, device=dev),
+                   alpha=torch.empty((B, g1 - 1), dtype=torch.float32, device=dev) if want_alpha else None,
+                   status=torch.empty(B, dtype=torch.int32, device=dev))
+    d = accept_desc(mode, target, draft, draft_tokens, temperature, seed, step, stream_ids, out["accept_len"],
+                    out["out_tokens"], out.get("alpha"), out["status"])
+    _check(lib.sv_spec_accept_static(ctypes.byref(d), _stream(dev)), "sv_spec_accept_static")
+    return out
 
 
 def walk_desc(mode, logits, tokens, parents, max_depth, temperature, seed, step, stream_ids,

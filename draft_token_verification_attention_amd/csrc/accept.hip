@@ -29,6 +29,8 @@
 // normalizers are good to about 1e-9, ample for the ratio tests.  The decided p(x), q(x),
 // the residual and CDF weights, and the normalizers the draw uses are fp64 (exp, exp2_acc),
 // and so is every sum.
+#include <mutex>
+
 #include "vocab_row.h"
 
 namespace {
@@ -220,6 +222,10 @@ __global__ __launch_bounds__(kRowThreads) void accept_stats_kernel(AcceptArgs a,
     // over them (blocks stay resident instead of being dispatched one per task).
     const int rows_t = a.rows + (SAMPLE ? 1 : 0);
     const int ntask = a.nchunk * rows_t * a.B;
+    // Block 0 also zeroes the call's completion counters, which only the later kernels of
+    // the call use: a workspace is then ready whatever an earlier call left in it.
+    if (blockIdx.x == 0)
+        for (int b = threadIdx.x; b < a.B; b += kRowThreads) w.cnt[b] = 0;
     for (int t = blockIdx.x; t < ntask; t += gridDim.x) {
         const int c = t % a.nchunk;
         const int r = (t / a.nchunk) % rows_t;
@@ -825,3 +831,46 @@ extern "C" sv_status sv_spec_accept(const sv_accept_desc *d, void *workspace, si
                 : (vec ? run_accept<true, 16>(a, w, s, sample, d->alpha != nullptr)
                        : run_accept<false, 16>(a, w, s, sample, d->alpha != nullptr));
 }
+
+// ---------------------------------------------------------------------------
+// Allocation-free variant: the workspace is `scratch`, a fixed device array of this file
+// (one copy per GPU, held until the process ends).  In host code `scratch` names only a
+// host-side stand-in, so its device address is asked of the runtime once per device (with
+// that device current) and kept; kernels get that address, never the array's name.
+// ---------------------------------------------------------------------------
+constexpr size_t kStaticScratchBytes = (size_t)SV_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device, once looked up
+}  // namespace
+
+static sv_status scratch_address(void **ptr)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return SV_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return SV_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SV_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return SV_OK;
+}
+
+extern "C" sv_status sv_spec_accept_static(const sv_accept_desc *d, void *stream)
+{
+    // the size check reads only B, gamma and V, and comes before any runtime call
+    if (d && sv_spec_accept_workspace(d) > kStaticScratchBytes) return SV_ERR_WORKSPACE;
+    void *ws = nullptr;
+    const sv_status st = scratch_address(&ws);
+    if (st != SV_OK) return st;
+    // the kernels clear the counters they use (accept_stats_kernel), so whatever an earlier
+    // call left in the array does no harm; calls that overlap in time on one GPU race
+    return sv_spec_accept(d, ws, kStaticScratchBytes, stream);
+}
+

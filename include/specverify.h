@@ -24,7 +24,9 @@
  *     workspace, zero-filled once, may serve any sequence of calls of any entry point and
  *     shape, provided the calls do not overlap in time (e.g. they share one stream).
  *   - The library allocates no memory and keeps no state between calls: whatever a call
- *     needs (device attributes, occupancy) it asks the runtime for during the call.
+ *     needs (device attributes, occupancy) it asks the runtime for during the call.  The
+ *     one exception is sv_spec_accept_static's fixed device array and the per-device
+ *     record of its address.
  *     Completion counters return to zero at the end of every kernel that uses them, and
  *     a launch that fails never runs, so a call that returns SV_ERR_HIP leaves its
  *     workspace's counter region zero as well.
@@ -210,6 +212,22 @@ typedef struct sv_accept_desc {
 SV_API size_t sv_spec_accept_workspace(const sv_accept_desc *desc);
 SV_API sv_status sv_spec_accept(const sv_accept_desc *desc, void *workspace, size_t workspace_bytes,
                          void *stream);
+
+/* ---------------------------------------------------------------------------------- */
+/* sv_spec_accept_static -- sv_spec_accept for callers that cannot allocate device       */
+/* memory (code under HIP graph capture, tight serving loops, harnesses that forbid      */
+/* allocation): the same kernels and results, with the workspace taken from a fixed      */
+/* device array inside the library of SV_STATIC_SCRATCH_BYTES per GPU (held from the      */
+/* first call on that GPU until the process ends; its address is looked up on that first */
+/* call, which should therefore not itself be under graph capture).  The calling thread's*/
+/* current device must be the stream's.  Inputs and outputs as in sv_spec_accept.        */
+/* Errors: as sv_spec_accept; SV_ERR_WORKSPACE when sv_spec_accept_workspace(desc)       */
+/* exceeds SV_STATIC_SCRATCH_BYTES (checked on the host before anything else).  Every    */
+/* call on one GPU shares the array: calls that overlap in time on one GPU race (issue   */
+/* them on one stream, or order them).  The call allocates nothing.                      */
+/* ---------------------------------------------------------------------------------- */
+#define SV_STATIC_SCRATCH_BYTES (16u << 20)
+SV_API sv_status sv_spec_accept_static(const sv_accept_desc *desc, void *stream);
 
 /* ---------------------------------------------------------------------------------- */
 /* sv_tree_walk -- verification of a token tree by a walk from the root.                 */

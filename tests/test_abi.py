@@ -27,13 +27,16 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_library_keeps_no_mutable_state():
-    """The only data symbols of the built library are the kernels' host-side handles and
-    the toolchain's own registration and runtime symbols: no file-scope or function-local
-    static variable carries state from one call to the next."""
+    """The only data symbols of the built library are the kernels' host-side handles, the
+    toolchain's own registration and runtime symbols, and sv_spec_accept_static's fixed
+    device array with the per-device record of its address: no other file-scope or
+    function-local static variable carries state from one call to the next."""
     import subprocess
     out = subprocess.run(["nm", "-C", sv.LIB_PATH], check=True, capture_output=True, text=True).stdout
     data = [ln.split(" ", 2)[2] for ln in out.splitlines() if re.match(r"^[0-9a-f]+ [bBdD] ", ln)]
-    allowed = re.compile(r"^(_DYNAMIC|_GLOBAL_OFFSET_TABLE_|__\w+(\.\w+)?|.*_kernel(<.*>)?\(.*\))$")
+    allowed = re.compile(r"^(_DYNAMIC|_GLOBAL_OFFSET_TABLE_|__\w+(\.\w+)?|DW\.ref\.__\w+|.*_kernel(<.*>)?\(.*\)|"
+                         # sv_spec_accept_static's fixed device array and the record of its address
+                         r"scratch|\(anonymous namespace\)::g_scratch_(ptr|mutex))$")
     stray = [d for d in data if not allowed.match(d)]
     assert not stray, stray
 
@@ -168,3 +171,13 @@ def test_oracle_and_library_share_nothing():
             txt = open(os.path.join(ROOT, "oracle", f)).read()
             assert "import draft_token_verification_attention_amd" not in txt
             assert "specverify.h" not in txt and "sv_common" not in txt
+
+
+def test_static_accept_rejects_calls_beyond_its_scratch():
+    """The size check of sv_spec_accept_static runs on the host before any runtime call."""
+    d = sv.sv_accept_desc()
+    d.mode, d.B, d.gamma, d.V, d.temperature = 1, 4096, 4, 128256, 1.0
+    assert sv.lib.sv_spec_accept_workspace(ctypes.byref(d)) > sv.SV_STATIC_SCRATCH_BYTES
+    assert sv.lib.sv_spec_accept_static(ctypes.byref(d), None) == sv.SV_ERR_WORKSPACE
+    d.B = 64
+    assert sv.lib.sv_spec_accept_workspace(ctypes.byref(d)) <= sv.SV_STATIC_SCRATCH_BYTES
