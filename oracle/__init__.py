@@ -11,7 +11,12 @@ the Medusa page; attention against torch's float64 scaled_dot_product_attention
 on CPU and against per-path brute force; acceptance against the three-token
 worked example, alpha = 1 - TV, the special cases, chi-square of the output law
 and E[J] = sum_i prod_{j<=i} alpha_j; the tree walk against brute force and the
-closed-form node-acceptance probabilities.
+closed-form node-acceptance probabilities; the near-threshold flags against an
+independent NumPy recomputation on crafted inputs; the KV commit against a
+simulated chain pass and attention through torch's SDPA; block verification
+against the printed 11/9 and the two-token law; Gumbel coupling against NumPy's
+Philox, the Gumbel-max law and the printed match-probability formula; recursive
+rejection against the output law p and the printed acceptance formula.
 """
 from __future__ import annotations
 
@@ -27,6 +32,8 @@ _SO = os.path.join(_HERE, "liboracle.so")
 
 TAG_ACCEPT = 0x53560001
 TAG_WALK = 0x53560002
+TAG_GUMBEL = 0x53560003
+TAG_RRS = 0x53560004
 GREEDY, SAMPLE = 0, 1
 
 _lib = None
@@ -67,6 +74,16 @@ def _typed(L):
     L.orc_spec_accept.restype = i32
     L.orc_tree_walk.argtypes = [i32, i32, i32, i32, i32, f32, P, P, P, u64, u64, P, P, P, P, P]
     L.orc_tree_walk.restype = i32
+    L.orc_kv_commit.argtypes = [i32, i32, i32, i32, i32, P, P, P, i64, i64, P, P, P, i32, P]
+    L.orc_kv_commit.restype = i32
+    L.orc_block_accept.argtypes = [i32, i32, i32, f32, P, P, P, u64, u64, P, P, P, P, P]
+    L.orc_block_accept.restype = i32
+    L.orc_gumbel_argmax.argtypes = [i32, i32, i32, f32, P, u64, u64, P, P, P]
+    L.orc_gumbel_argmax.restype = i32
+    L.orc_gumbel_accept.argtypes = [i32, i32, i32, f32, P, P, u64, u64, P, P, P, P]
+    L.orc_gumbel_accept.restype = i32
+    L.orc_tree_rrs.argtypes = [i32, i32, i32, i32, f32, i32, P, P, P, P, u64, u64, P, P, P, P, P]
+    L.orc_tree_rrs.restype = i32
     return L
 
 
@@ -212,4 +229,97 @@ def tree_walk(mode: int, logits, tokens, parents, temperature: float, seed: int,
                                          _p(flags))
     if st != 0 and not (st == 3 and allow_too_deep):
         raise ValueError("orc_tree_walk status %d" % st)
+    return dict(accept_len=acc, path=path, out_tokens=out, flags=flags, status=st)
+
+
+# --------------------------------------------------------------------------- #
+def kv_commit(k, v, kv_off, prefix_len, accept_len, *, n_q: int, Hkv: int, D: int, kv_sh: int, kv_st: int,
+              path=None):
+    """Commit in place on copies of the flat caches k, v (numpy; float32 or bf16 bit patterns).
+    Returns (k, v, new_len, status) -- status 0, or 1 + the first bad sequence."""
+    k = np.array(k, copy=True, order="C")
+    v = np.array(v, copy=True, order="C")
+    B = len(prefix_len)
+    pl = _c(prefix_len, np.int32)
+    acc = _c(accept_len, np.int32)
+    pth = None if path is None else _c(path, np.int32).reshape(B, -1)
+    new_len = np.zeros(B, dtype=np.int32)
+    st = lib().orc_kv_commit(B, int(n_q), int(Hkv), int(D), k.itemsize, _p(k), _p(v), _p(_c(kv_off, np.int64)),
+                             int(kv_sh), int(kv_st), _p(pl), _p(acc), _p(pth), 0 if pth is None else pth.shape[1],
+                             _p(new_len))
+    return k, v, new_len, st
+
+
+def block_accept(target, draft, draft_tokens, temperature: float, seed: int, step: int = 0, stream_ids=None,
+                 handle=None):
+    """Block verification -> dict(accept_len, out_tokens, weights [B][gamma+1], flags)."""
+    tgt = _c(target, np.float32)
+    B, g1, V = tgt.shape
+    gamma = g1 - 1
+    dr = _c(draft, np.float32)
+    toks = _c(draft_tokens, np.int32).reshape(B, gamma)
+    sid = None if stream_ids is None else _c(stream_ids, np.uint64)
+    acc = np.zeros(B, dtype=np.int32)
+    out = np.zeros((B, g1), dtype=np.int32)
+    w = np.zeros((B, g1), dtype=np.float64)
+    flags = np.zeros(B, dtype=np.int32)
+    st = (handle or lib()).orc_block_accept(B, gamma, V, float(temperature), _p(tgt), _p(dr), _p(toks), int(seed),
+                                            int(step), _p(sid), _p(acc), _p(out), _p(w), _p(flags))
+    if st != 0:
+        raise ValueError("orc_block_accept status %d" % st)
+    return dict(accept_len=acc, out_tokens=out, weights=w, flags=flags)
+
+
+def gumbel_argmax(logits, temperature: float, seed: int, step: int = 0, stream_ids=None):
+    """argmax(logits/T + shared Gumbel noise) of every row [B][rows][V] (row i = position i)
+    -> (tokens [B][rows], gap [B][rows])."""
+    lg = _c(logits, np.float32)
+    B, rows, V = lg.shape
+    sid = None if stream_ids is None else _c(stream_ids, np.uint64)
+    out = np.zeros((B, rows), dtype=np.int32)
+    gap = np.zeros((B, rows), dtype=np.float64)
+    st = lib().orc_gumbel_argmax(B, rows, V, float(temperature), _p(lg), int(seed), int(step), _p(sid), _p(out),
+                                 _p(gap))
+    if st != 0:
+        raise ValueError("orc_gumbel_argmax status %d" % st)
+    return out, gap
+
+
+def gumbel_accept(target, draft_tokens, temperature: float, seed: int, step: int = 0, stream_ids=None):
+    """Gumbel-coupled verification -> dict(accept_len, out_tokens, flags)."""
+    tgt = _c(target, np.float32)
+    B, g1, V = tgt.shape
+    toks = _c(draft_tokens, np.int32).reshape(B, g1 - 1)
+    sid = None if stream_ids is None else _c(stream_ids, np.uint64)
+    acc = np.zeros(B, dtype=np.int32)
+    out = np.zeros((B, g1), dtype=np.int32)
+    flags = np.zeros(B, dtype=np.int32)
+    st = lib().orc_gumbel_accept(B, g1 - 1, V, float(temperature), _p(tgt), _p(toks), int(seed), int(step), _p(sid),
+                                 _p(acc), _p(out), _p(flags))
+    if st != 0:
+        raise ValueError("orc_gumbel_accept status %d" % st)
+    return dict(accept_len=acc, out_tokens=out, flags=flags)
+
+
+def tree_rrs(target, draft, tokens, parents, temperature: float, seed: int, step: int = 0, stream_ids=None,
+             max_depth=None, without_replacement: bool = False, handle=None, allow_too_deep: bool = False):
+    """Recursive rejection over a token tree -> dict(accept_len, path, out_tokens, flags, status)."""
+    tgt = _c(target, np.float32)
+    B, n, V = tgt.shape
+    dr = _c(draft, np.float32)
+    tk = _c(tokens, np.int32).reshape(B, n)
+    par = _c(parents, np.int32)
+    if max_depth is None:
+        _, depth, _ = tree_mask(par, 0)
+        max_depth = int(depth.max())
+    sid = None if stream_ids is None else _c(stream_ids, np.uint64)
+    acc = np.zeros(B, dtype=np.int32)
+    path = np.zeros((B, max_depth + 1), dtype=np.int32)
+    out = np.zeros((B, max_depth + 1), dtype=np.int32)
+    flags = np.zeros(B, dtype=np.int32)
+    st = (handle or lib()).orc_tree_rrs(B, n, V, int(max_depth), float(temperature), int(bool(without_replacement)),
+                                        _p(tgt), _p(dr), _p(tk), _p(par), int(seed), int(step), _p(sid), _p(acc),
+                                        _p(path), _p(out), _p(flags))
+    if st != 0 and not (st == 3 and allow_too_deep):
+        raise ValueError("orc_tree_rrs status %d" % st)
     return dict(accept_len=acc, path=path, out_tokens=out, flags=flags, status=st)

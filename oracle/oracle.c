@@ -416,3 +416,347 @@ ORC_EXPORT int32_t orc_tree_walk(int32_t mode, int32_t B, int32_t n, int32_t V, 
     }
     return status;
 }
+
+/* ========================================================================= */
+/* Beyond the verify step proper: the cache commit after a round, and three   */
+/* other verification rules the pages give.                                  */
+/* ========================================================================= */
+
+#define ORC_TAG_GUMBEL 0x53560003ULL
+#define ORC_TAG_RRS    0x53560004ULL
+#define ORC_NEAR_GUMBEL 1e-12
+
+/* ------------------------------------------------------------------------- */
+/* KV-cache commit.  [TB] section "Keeping the caches consistent after a      */
+/* rejection": after J acceptances the entries of the accepted drafts are      */
+/* right and those of the rejected ones are discarded; the correction or bonus */
+/* token has no entry yet.  A contiguous cache rolls back by moving its length */
+/* pointer; a tree needs one more step, gathering the accepted branch's        */
+/* entries (scattered among discarded siblings) into consecutive slots.  [AG]  */
+/* section "Verification bottlenecks" (KV cache bookkeeping) says the same.    */
+/* The pass wrote node j (chain row j) of sequence b at position P_b + j, node */
+/* 0 being the last committed token.  Afterwards position P_b + k holds the    */
+/* entry of path node k, k = 1..J, and the length is P_b + 1 + J.  Element    */
+/* (t, g, d) of a cache is at kv_off[b] + g kv_sh + t kv_st + d, esize bytes.  */
+/* path == NULL: a chain, only the length moves.  Returns 0, or 1 + the first  */
+/* sequence with J or a path node out of range (that sequence is untouched).   */
+/* ------------------------------------------------------------------------- */
+ORC_EXPORT int32_t orc_kv_commit(int32_t B, int32_t n_q, int32_t Hkv, int32_t D, int32_t esize,
+                                 void *k, void *v, const int64_t *kv_off, int64_t kv_sh, int64_t kv_st,
+                                 const int32_t *prefix_len, const int32_t *accept_len,
+                                 const int32_t *path, int32_t path_stride, int32_t *new_len)
+{
+    int32_t bad = 0;
+    for (int32_t b = 0; b < B; ++b) {
+        const int64_t P = prefix_len[b];
+        const int32_t J = accept_len[b];
+        new_len[b] = prefix_len[b];
+        int ok = (J >= 0 && J < n_q);
+        if (ok && path)
+            for (int32_t kk = 1; kk <= J; ++kk) {
+                const int32_t node = path[(int64_t)b * path_stride + kk];
+                if (node < kk || node >= n_q) ok = 0;
+            }
+        if (!ok) {
+            if (!bad) bad = b + 1;
+            continue;
+        }
+        if (path) {
+            for (int32_t kk = 1; kk <= J; ++kk) {       /* in path order: a slot is written */
+                const int32_t node = path[(int64_t)b * path_stride + kk];  /* after it was read */
+                if (node == kk) continue;
+                for (int32_t g = 0; g < Hkv; ++g) {
+                    const int64_t src = kv_off[b] + g * kv_sh + (P + node) * kv_st;
+                    const int64_t dst = kv_off[b] + g * kv_sh + (P + kk) * kv_st;
+                    memcpy((char *)k + dst * esize, (char *)k + src * esize, (size_t)D * esize);
+                    memcpy((char *)v + dst * esize, (char *)v + src * esize, (size_t)D * esize);
+                }
+            }
+        }
+        new_len[b] = (int32_t)(P + 1 + J);
+    }
+    return bad;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Block verification.  [AG] section "Block verification": with p_k, q_k the  */
+/* target's and drafter's distributions at draft position k (target row k-1,  */
+/* draft row k-1 here) and x_k the k-th draft, the running weight             */
+/*   w_0 = 1,  w_k = min(1, w_{k-1} p_k(x_k) / q_k(x_k));                      */
+/* prefix k survives with probability                                         */
+/*   h_k = m_k / (m_k + 1 - w_k) (1 when w_k = 1),                             */
+/*   m_k = sum_x (w_k p_{k+1}(x) - q_{k+1}(x))+,  q_{gamma+1} = 0 (m_gamma = w_gamma);*/
+/* the longest surviving prefix n is kept and the next token is drawn from    */
+/* (w_n p_{n+1} - q_{n+1})+ normalized.  Uniforms: survival of prefix k uses  */
+/* index k-1, the draw index gamma (tag ACCEPT, as speculative sampling: with */
+/* gamma = 1 the two rules take the same decisions).  A drafted token with    */
+/* q = 0 sets w_k = 1 if p > 0 (and w_{k-1} > 0), else 0.  A zero residual     */
+/* falls back to p_{n+1}.  p, q = softmax(logits / T).                         */
+/* Outputs as orc_spec_accept; weights[B][gamma+1] = w_0..w_gamma (optional);  */
+/* flags bit0 = some |u - h_k| < 1e-6, bit1 = the draw within 1e-10 of a      */
+/* CDF boundary.                                                              */
+/* ------------------------------------------------------------------------- */
+ORC_EXPORT int32_t orc_block_accept(int32_t B, int32_t gamma, int32_t V, float temperature,
+                                    const float *target, const float *draft, const int32_t *draft_tokens,
+                                    uint64_t seed, uint64_t step, const uint64_t *stream_ids,
+                                    int32_t *accept_len, int32_t *out_tokens, double *weights, int32_t *flags)
+{
+    if (B < 0 || gamma < 1 || V <= 0 || !(temperature > 0.0f)) return 1;
+    const double tau = (double)temperature;
+    int32_t bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int32_t b = 0; b < B; ++b) {
+        const float *tb = target + (int64_t)b * (gamma + 1) * V;
+        const float *db = draft + (int64_t)b * gamma * V;
+        const int32_t *xb = draft_tokens + (int64_t)b * gamma;
+        int32_t *ob = out_tokens + (int64_t)b * (gamma + 1);
+        const uint64_t stream = stream_ids ? stream_ids[b] : (uint64_t)b;
+        double *p = (double *)malloc(sizeof(double) * (size_t)V);
+        double *q = (double *)malloc(sizeof(double) * (size_t)V);
+        double *w = (double *)malloc(sizeof(double) * (size_t)(gamma + 1));
+        int32_t fl = 0, n = 0;
+        for (int32_t i = 0; i <= gamma; ++i) ob[i] = -1;
+        for (int32_t i = 0; i < gamma; ++i)
+            if (xb[i] < 0 || xb[i] >= V) {
+#pragma omp atomic write
+                bad = 1;
+            }
+        w[0] = 1.0;
+        for (int32_t kk = 1; kk <= gamma; ++kk) {
+            const int32_t x = xb[kk - 1];
+            softmax_row(tb + (int64_t)(kk - 1) * V, V, tau, p);
+            softmax_row(db + (int64_t)(kk - 1) * V, V, tau, q);
+            if (q[x] > 0.0) w[kk] = fmin(1.0, w[kk - 1] * p[x] / q[x]);
+            else w[kk] = (w[kk - 1] > 0.0 && p[x] > 0.0) ? 1.0 : 0.0;
+        }
+        for (int32_t kk = 1; kk <= gamma; ++kk) {
+            double m;
+            if (kk < gamma) {
+                softmax_row(tb + (int64_t)kk * V, V, tau, p);
+                softmax_row(db + (int64_t)kk * V, V, tau, q);
+                m = 0.0;
+                for (int32_t x = 0; x < V; ++x) m += fmax(0.0, w[kk] * p[x] - q[x]);
+            } else {
+                m = w[gamma];
+            }
+            const double h = w[kk] < 1.0 ? m / (m + 1.0 - w[kk]) : 1.0;
+            const double u = orc_uniform(seed, (uint64_t)(kk - 1), step, stream, ORC_TAG_ACCEPT);
+            if (fabs(u - h) < ORC_NEAR_RATIO) fl |= 1;
+            if (u <= h) n = kk;
+        }
+        /* the next token, from (w_n p_{n+1} - q_{n+1})+ */
+        softmax_row(tb + (int64_t)n * V, V, tau, p);
+        if (n < gamma) {
+            softmax_row(db + (int64_t)n * V, V, tau, q);
+            for (int32_t x = 0; x < V; ++x) q[x] = fmax(0.0, w[n] * p[x] - q[x]);
+        } else {
+            for (int32_t x = 0; x < V; ++x) q[x] = w[gamma] * p[x];
+        }
+        const double ustar = orc_uniform(seed, (uint64_t)gamma, step, stream, ORC_TAG_ACCEPT);
+        int32_t near = 0;
+        int32_t y = inverse_cdf(q, V, ustar, &near);
+        if (y < 0) y = inverse_cdf(p, V, ustar, &near);
+        if (near) fl |= 2;
+        for (int32_t i = 0; i < n; ++i) ob[i] = xb[i];
+        ob[n] = y;
+        accept_len[b] = n;
+        if (weights)
+            for (int32_t i = 0; i <= gamma; ++i) weights[(int64_t)b * (gamma + 1) + i] = w[i];
+        if (flags) flags[b] = fl;
+        free(p);
+        free(q);
+        free(w);
+    }
+    return bad ? 2 : 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Gumbel-max with shared noise.  [AG] section "Sampling with shared noise":  */
+/* sampling from softmax(l) is argmax_x (l(x) + g_x), g_x = -log(-log u_x);   */
+/* drafter and target share the noise vector g_i of draft position i.         */
+/* Here l = logits / T, and u_x of position i is word (x mod 4) of the Philox */
+/* block with counter (x div 4, step, stream, TAG_GUMBEL + 2^32 i), mapped to */
+/* (0,1) like every uniform.  T = 0: the plain argmax (no noise).  Ties go to */
+/* the lowest token.  gap = best score - second best (+inf when V = 1).        */
+/* ------------------------------------------------------------------------- */
+static int32_t gumbel_argmax_row(const float *logits, int32_t V, double tau, uint64_t seed, uint64_t step,
+                                 uint64_t stream, uint64_t pos, double *gap)
+{
+    double best = -INFINITY, second = -INFINITY;
+    int32_t arg = 0;
+    uint64_t words[4] = {0, 0, 0, 0};
+    for (int32_t x = 0; x < V; ++x) {
+        double s;
+        if (tau == 0.0) {
+            s = (double)logits[x];
+        } else {
+            if ((x & 3) == 0) {
+                uint64_t ctr[4] = {(uint64_t)x >> 2, step, stream, ORC_TAG_GUMBEL + (pos << 32)};
+                uint64_t key[2] = {seed, 0};
+                orc_philox4x64_10(ctr, key, words);
+            }
+            const double u = (double)(2 * (words[x & 3] >> 12) + 1) * 0x1p-53;
+            s = (double)logits[x] / tau + (-log(-log(u)));
+        }
+        if (s > best) {
+            second = best;
+            best = s;
+            arg = x;
+        } else if (s > second) {
+            second = s;
+        }
+    }
+    if (gap) *gap = best - second;
+    return arg;
+}
+
+/* argmax_x (l_{b,i}(x) / T + g_{i,x}) for every row i of `rows` rows per sequence    */
+/* (position i): the target's own samples, or the drafter's proposals when given   */
+/* the drafter's logits.  out [B][rows]; gap [B][rows] optional.                    */
+ORC_EXPORT int32_t orc_gumbel_argmax(int32_t B, int32_t rows, int32_t V, float temperature, const float *logits,
+                                     uint64_t seed, uint64_t step, const uint64_t *stream_ids, int32_t *out,
+                                     double *gap)
+{
+    if (B < 0 || rows < 0 || V <= 0 || !(temperature >= 0.0f)) return 1;
+    const double tau = (double)temperature;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int32_t b = 0; b < B; ++b) {
+        const uint64_t stream = stream_ids ? stream_ids[b] : (uint64_t)b;
+        for (int32_t i = 0; i < rows; ++i)
+            out[(int64_t)b * rows + i] = gumbel_argmax_row(logits + ((int64_t)b * rows + i) * V, V, tau, seed,
+                                                           step, stream, (uint64_t)i,
+                                                           gap ? gap + (int64_t)b * rows + i : NULL);
+    }
+    return 0;
+}
+
+/* Gumbel-coupled verification ([AG], same section): the target's sample y_i  */
+/* at every position, the longest prefix with x_i == y_i is kept (J), and y_J */
+/* is appended -- exact matching, as under greedy decoding; the output is what */
+/* the target samples with that noise on its own.  Outputs as orc_spec_accept; */
+/* flags bit0 = an evaluated position's best two scores within 1e-12.          */
+ORC_EXPORT int32_t orc_gumbel_accept(int32_t B, int32_t gamma, int32_t V, float temperature, const float *target,
+                                     const int32_t *draft_tokens, uint64_t seed, uint64_t step,
+                                     const uint64_t *stream_ids, int32_t *accept_len, int32_t *out_tokens,
+                                     int32_t *flags)
+{
+    if (B < 0 || gamma < 1 || V <= 0 || !(temperature >= 0.0f)) return 1;
+    const double tau = (double)temperature;
+    int32_t bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int32_t b = 0; b < B; ++b) {
+        const float *tb = target + (int64_t)b * (gamma + 1) * V;
+        const int32_t *xb = draft_tokens + (int64_t)b * gamma;
+        int32_t *ob = out_tokens + (int64_t)b * (gamma + 1);
+        const uint64_t stream = stream_ids ? stream_ids[b] : (uint64_t)b;
+        int32_t fl = 0, J = 0, y = -1;
+        for (int32_t i = 0; i <= gamma; ++i) ob[i] = -1;
+        for (int32_t i = 0; i < gamma; ++i)
+            if (xb[i] < 0 || xb[i] >= V) {
+#pragma omp atomic write
+                bad = 1;
+            }
+        for (;;) {
+            double gap;
+            y = gumbel_argmax_row(tb + (int64_t)J * V, V, tau, seed, step, stream, (uint64_t)J, &gap);
+            if (gap < ORC_NEAR_GUMBEL) fl |= 1;
+            if (J == gamma || xb[J] != y) break;
+            ob[J] = y;
+            ++J;
+        }
+        ob[J] = y;
+        accept_len[b] = J;
+        if (flags) flags[b] = fl;
+    }
+    return bad ? 2 : 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Tree verification by recursive rejection.  [TB] box "Recursive rejection   */
+/* at a node with several children": the children s_1..s_k of a node (node    */
+/* order) were drawn from the drafter's q at that node; with R_1 = p, try     */
+/* s_i: accept with probability min(1, R_i(s_i)/q(s_i)) and move to that      */
+/* child; on rejection R_{i+1} = (R_i - q)+ normalized.  If every child is    */
+/* rejected (or the node is a leaf), the extra token is drawn from R_{k+1}.    */
+/* without_replacement: the children were drawn without replacement (the     */
+/* Sequoia variant the same section describes): after a rejection the        */
+/* rejected token is also zeroed in q and q renormalized.                     */
+/* p, q = softmax(target / T), softmax(draft / T) of the node's rows (row v   */
+/* of the drafter's logits is the distribution it drew v's children from).   */
+/* Uniforms (tag RRS): try i at depth d uses index 2^16 d + i, the draw       */
+/* 2^16 d + 0xffff.  Accept test u q(s) < R(s) (as u < R/q; q(s) = 0 passes   */
+/* iff R(s) > 0).  A zero (R - q)+ (rounding only) keeps R.  At max_depth an   */
+/* accepted child's token is emitted as the extra token (status 3).           */
+/* Outputs as orc_tree_walk; flags bit0 = a test with |u - R/q| < 1e-6, bit1 = */
+/* the draw within 1e-10 of a CDF boundary.                                   */
+/* ------------------------------------------------------------------------- */
+ORC_EXPORT int32_t orc_tree_rrs(int32_t B, int32_t n, int32_t V, int32_t max_depth, float temperature,
+                                int32_t without_replacement, const float *target, const float *draft,
+                                const int32_t *tokens, const int32_t *parents, uint64_t seed, uint64_t step,
+                                const uint64_t *stream_ids, int32_t *accept_len, int32_t *path,
+                                int32_t *out_tokens, int32_t *flags)
+{
+    if (B < 0 || n <= 0 || V <= 0 || max_depth < 0 || !(temperature > 0.0f)) return 1;
+    if (parents[0] != -1) return 2;
+    for (int32_t i = 1; i < n; ++i) if (parents[i] < -1 || parents[i] >= i) return 2;
+    const double tau = (double)temperature;
+    int32_t status = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int32_t b = 0; b < B; ++b) {
+        const float *tb = target + (int64_t)b * n * V;
+        const float *db = draft + (int64_t)b * n * V;
+        const int32_t *tk = tokens + (int64_t)b * n;
+        int32_t *pb = path + (int64_t)b * (max_depth + 1);
+        int32_t *ob = out_tokens + (int64_t)b * (max_depth + 1);
+        const uint64_t stream = stream_ids ? stream_ids[b] : (uint64_t)b;
+        double *R = (double *)malloc(sizeof(double) * (size_t)V);
+        double *q = (double *)malloc(sizeof(double) * (size_t)V);
+        for (int32_t d = 0; d <= max_depth; ++d) { pb[d] = -1; ob[d] = -1; }
+        int32_t fl = 0, v = 0, d = 0;
+        pb[0] = 0;
+        for (;;) {
+            softmax_row(tb + (int64_t)v * V, V, tau, R);
+            softmax_row(db + (int64_t)v * V, V, tau, q);
+            int32_t accepted = -1, tries = 0;
+            for (int32_t c = v + 1; c < n; ++c) {
+                if (parents[c] != v) continue;
+                const int32_t s = tk[c];
+                const double u = orc_uniform(seed, ((uint64_t)d << 16) | (uint64_t)tries, step, stream, ORC_TAG_RRS);
+                if (q[s] > 0.0 && fabs(u - R[s] / q[s]) < ORC_NEAR_RATIO) fl |= 1;
+                if (u * q[s] < R[s]) { accepted = c; break; }
+                double z = 0.0;
+                for (int32_t x = 0; x < V; ++x) z += fmax(0.0, R[x] - q[x]);
+                if (z > 0.0)
+                    for (int32_t x = 0; x < V; ++x) R[x] = fmax(0.0, R[x] - q[x]) / z;
+                if (without_replacement) {
+                    q[s] = 0.0;
+                    double zq = 0.0;
+                    for (int32_t x = 0; x < V; ++x) zq += q[x];
+                    if (zq > 0.0) for (int32_t x = 0; x < V; ++x) q[x] /= zq;
+                }
+                ++tries;
+            }
+            if (accepted < 0) {
+                int32_t near = 0;
+                const double u = orc_uniform(seed, ((uint64_t)d << 16) | 0xffffULL, step, stream, ORC_TAG_RRS);
+                ob[d] = inverse_cdf(R, V, u, &near);
+                if (near) fl |= 2;
+                break;
+            }
+            ob[d] = tk[accepted];
+            if (d + 1 > max_depth) {
+#pragma omp atomic write
+                status = 3;
+                break;
+            }
+            v = accepted;
+            ++d;
+            pb[d] = v;
+        }
+        accept_len[b] = d;
+        if (flags) flags[b] = fl;
+        free(R);
+        free(q);
+    }
+    return status;
+}
