@@ -54,9 +54,16 @@ class sv_walk_desc(ctypes.Structure):
                 ("accept_len", _P), ("path", _P), ("out_tokens", _P), ("dev_status", _P)]
 
 
+class sv_commit_desc(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int), ("B", _i32), ("n_q", _i32), ("Hkv", _i32), ("D", _i32),
+                ("k", _P), ("v", _P), ("kv_off", _P), ("kv_sb", _i64), ("kv_sh", _i64), ("kv_st", _i64),
+                ("prefix_len", _P), ("accept_len", _P), ("path", _P), ("path_stride", _i32),
+                ("new_len", _P), ("dev_status", _P)]
+
+
 EXPORTS = ("sv_build_tree_mask", "sv_verify_attention_workspace", "sv_verify_attention",
            "sv_spec_accept_workspace", "sv_spec_accept", "sv_spec_accept_static", "sv_tree_walk_workspace",
-           "sv_tree_walk", "sv_status_string")
+           "sv_tree_walk", "sv_kv_commit", "sv_status_string")
 
 
 def _load():
@@ -80,6 +87,8 @@ def _load():
     L.sv_tree_walk_workspace.restype = ctypes.c_size_t
     L.sv_tree_walk.argtypes = [ctypes.POINTER(sv_walk_desc), _P, ctypes.c_size_t, _P]
     L.sv_tree_walk.restype = ctypes.c_int
+    L.sv_kv_commit.argtypes = [ctypes.POINTER(sv_commit_desc), _P]
+    L.sv_kv_commit.restype = ctypes.c_int
     L.sv_status_string.argtypes = [ctypes.c_int]
     L.sv_status_string.restype = ctypes.c_char_p
     return L
@@ -279,3 +288,35 @@ def sv_tree_walk(mode: int, logits, tokens, parents, max_depth: int, temperature
     ws = workspace(nb, dev)
     _check(lib.sv_tree_walk(ctypes.byref(d), _ptr(ws), nb, _stream(dev)), "sv_tree_walk")
     return dict(accept_len=acc, path=path, out_tokens=out, status=status)
+
+
+def commit_desc(k, v, kv_off, prefix_len, accept_len, *, n_q: int, Hkv: int, D: int, kv_sh: int, kv_st: int,
+                kv_sb: int = 0, path=None, new_len=None, dev_status=None) -> sv_commit_desc:
+    d = sv_commit_desc()
+    d.dtype = SV_BF16 if k.dtype == torch.bfloat16 else SV_F32
+    d.B, d.n_q, d.Hkv, d.D = prefix_len.numel(), int(n_q), int(Hkv), int(D)
+    d.k, d.v = k.data_ptr(), v.data_ptr()
+    d.kv_off = None if kv_off is None else kv_off.data_ptr()
+    d.kv_sb, d.kv_sh, d.kv_st = int(kv_sb), int(kv_sh), int(kv_st)
+    d.prefix_len, d.accept_len = prefix_len.data_ptr(), accept_len.data_ptr()
+    d.path = None if path is None else path.data_ptr()
+    d.path_stride = 0 if path is None else path.shape[-1]
+    d.new_len = (prefix_len if new_len is None else new_len).data_ptr()
+    d.dev_status = None if dev_status is None else dev_status.data_ptr()
+    return d
+
+
+def sv_kv_commit(k, v, kv_off, prefix_len, accept_len, *, n_q: int, Hkv: int, D: int, kv_sh: int, kv_st: int,
+                 kv_sb: int = 0, path=None, in_place: bool = False):
+    """Commit a round in the caches k, v (moved in place).  Returns (new_len int32 [B], status
+    int32 [B]); with in_place the new lengths are written into prefix_len as well (and it is
+    returned)."""
+    _need_cuda(k, v, kv_off, prefix_len, accept_len, path)
+    B = prefix_len.numel()
+    new_len = prefix_len if in_place else torch.empty(B, dtype=torch.int32, device=k.device)
+    status = torch.empty(B, dtype=torch.int32, device=k.device)
+    d = commit_desc(k, v, kv_off, prefix_len, accept_len, n_q=n_q, Hkv=Hkv, D=D, kv_sh=kv_sh, kv_st=kv_st,
+                    kv_sb=kv_sb, path=None if path is None else path.contiguous(), new_len=new_len,
+                    dev_status=status)
+    _check(lib.sv_kv_commit(ctypes.byref(d), _stream(k.device)), "sv_kv_commit")
+    return new_len, status

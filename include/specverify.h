@@ -272,6 +272,46 @@ SV_API size_t sv_tree_walk_workspace(const sv_walk_desc *desc);
 SV_API sv_status sv_tree_walk(const sv_walk_desc *desc, void *workspace, size_t workspace_bytes,
                        void *stream);
 
+/* ---------------------------------------------------------------------------------- */
+/* sv_kv_commit -- the KV-cache commit after a round.  [TB] section "Keeping the caches   */
+/* consistent after a rejection": after J acceptances the entries of the accepted drafts */
+/* are kept and the rejected ones discarded; the correction or bonus token has no entry  */
+/* yet.  A chain rolls back by moving its length; a tree also gathers the accepted       */
+/* branch's entries, scattered among discarded siblings, into consecutive slots ([AG]    */
+/* "Verification bottlenecks": KV cache bookkeeping).                                    */
+/* The verification pass wrote node (or chain row) j of sequence b at position P_b + j,  */
+/* node 0 being the last committed token.  Afterwards position P_b + k holds the entry of */
+/* path node k (k = 1..J_b) and new_len[b] = P_b + 1 + J_b.                              */
+/*   k, v       the caches, layout as sv_verify_attention (kv_off or dense kv_sb; token t */
+/*              of KV head g at kv_off[b] + g*kv_sh + t*kv_st, D contiguous elements of   */
+/*              `dtype`); rows are moved in place                                        */
+/*   prefix_len device int32 [B]: P_b;  accept_len device int32 [B]: J_b (from           */
+/*              sv_spec_accept or sv_tree_walk)                                           */
+/*   path       device int32 [B][path_stride]: sv_tree_walk's path (node 0 first), or    */
+/*              NULL for chains (only the length moves)                                  */
+/*   new_len    device int32 [B]: P_b + 1 + J_b; may be prefix_len itself (in place)     */
+/*   dev_status optional device int32 [B]: 0, or 4 when J_b is outside [0, n_q) or a     */
+/*              path node k is outside [k, n_q) (that sequence is left untouched)         */
+/* Supported: path_stride <= 65 (a walk's max_depth <= 63); D * element size and the     */
+/* strides multiples of 16 bytes, k and v 16-byte aligned (else SV_ERR_UNSUPPORTED).      */
+/* ---------------------------------------------------------------------------------- */
+typedef struct sv_commit_desc {
+    sv_dtype dtype;
+    int32_t B, n_q, Hkv, D;
+    void *k;
+    void *v;
+    const int64_t *kv_off;
+    int64_t kv_sb, kv_sh, kv_st;
+    const int32_t *prefix_len;
+    const int32_t *accept_len;
+    const int32_t *path;
+    int32_t path_stride;
+    int32_t *new_len;
+    int32_t *dev_status;
+} sv_commit_desc;
+
+SV_API sv_status sv_kv_commit(const sv_commit_desc *desc, void *stream);
+
 /* Human-readable name of a status code (static storage). */
 SV_API const char *sv_status_string(sv_status status);
 
