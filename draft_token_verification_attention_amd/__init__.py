@@ -21,6 +21,7 @@ SV_OK, SV_ERR_INVALID_ARG, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_HIP = ra
 SV_STATIC_SCRATCH_BYTES = 16 << 20
 SV_F32, SV_BF16 = 0, 1
 SV_GREEDY, SV_SAMPLE = 0, 1
+SV_RULE_TOKEN, SV_RULE_BLOCK, SV_RULE_GUMBEL = 0, 1, 2
 SV_MASK_CAUSAL, SV_MASK_TREE = 0, 1
 
 _P = ctypes.c_void_p
@@ -45,7 +46,8 @@ class sv_attn_desc(ctypes.Structure):
 class sv_accept_desc(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int), ("B", _i32), ("gamma", _i32), ("V", _i32), ("temperature", _f32),
                 ("target_logits", _P), ("draft_logits", _P), ("draft_tokens", _P), ("rng", sv_philox),
-                ("accept_len", _P), ("out_tokens", _P), ("alpha", _P), ("dev_status", _P)]
+                ("accept_len", _P), ("out_tokens", _P), ("alpha", _P), ("dev_status", _P),
+                ("rule", ctypes.c_int)]
 
 
 class sv_walk_desc(ctypes.Structure):
@@ -201,7 +203,7 @@ def sv_verify_attention(q, k, v, kv_off, prefix_len, *, Hkv: int, max_prefix: in
 
 
 def accept_desc(mode, target, draft, draft_tokens, temperature, seed, step, stream_ids,
-                accept_len, out_tokens, alpha, dev_status) -> sv_accept_desc:
+                accept_len, out_tokens, alpha, dev_status, rule: int = SV_RULE_TOKEN) -> sv_accept_desc:
     B, g1, V = target.shape
     d = sv_accept_desc()
     d.mode, d.B, d.gamma, d.V, d.temperature = int(mode), B, g1 - 1, V, float(temperature)
@@ -212,11 +214,12 @@ def accept_desc(mode, target, draft, draft_tokens, temperature, seed, step, stre
     d.accept_len, d.out_tokens = accept_len.data_ptr(), out_tokens.data_ptr()
     d.alpha = None if alpha is None else alpha.data_ptr()
     d.dev_status = None if dev_status is None else dev_status.data_ptr()
+    d.rule = int(rule)
     return d
 
 
 def sv_spec_accept(mode: int, target, draft, draft_tokens, temperature: float, seed: int, step: int = 0,
-                   stream_ids=None, want_alpha: bool = False):
+                   stream_ids=None, want_alpha: bool = False, rule: int = SV_RULE_TOKEN):
     """target fp32 [B][gamma+1][V]; draft fp32 [B][gamma][V] (SAMPLE); draft_tokens int32 [B][gamma].
     Returns dict(accept_len, out_tokens, alpha or None, status) as device tensors."""
     _need_cuda(target, draft, draft_tokens, stream_ids)
@@ -230,7 +233,7 @@ def sv_spec_accept(mode: int, target, draft, draft_tokens, temperature: float, s
     alpha = torch.empty((B, g1 - 1), dtype=torch.float32, device=dev) if want_alpha else None
     status = torch.empty(B, dtype=torch.int32, device=dev)
     sid = None if stream_ids is None else stream_ids.to(torch.int64).contiguous()
-    d = accept_desc(mode, target, draft, draft_tokens, temperature, seed, step, sid, acc, out, alpha, status)
+    d = accept_desc(mode, target, draft, draft_tokens, temperature, seed, step, sid, acc, out, alpha, status, rule)
     nb = lib.sv_spec_accept_workspace(ctypes.byref(d))
     ws = workspace(nb, dev)
     _check(lib.sv_spec_accept(ctypes.byref(d), _ptr(ws), nb, _stream(dev)), "sv_spec_accept")

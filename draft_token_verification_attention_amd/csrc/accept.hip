@@ -62,6 +62,18 @@ struct ResPart {   // per residual chunk: sums of wp and wq over the tokens with
     double wp, wq;
 };
 
+struct BlockChunk {   // block verification, per (sequence, candidate, 4096-token chunk)
+    double a, b;      // sums of wp and wq over the tokens with (estimated) residual mass
+    double wp, wq;    // sums of wp and wq over every token
+};
+struct GumbelPart {   // Gumbel-coupled verification, per (sequence, position, chunk)
+    double s;         // the chunk's best score l/T + g
+    int32_t arg;      // its token (the lowest among equal scores)
+    int32_t pad;
+};
+constexpr int kBlockPer = 16;  // block verification and Gumbel passes: 4096-token chunks
+constexpr int kBlockChunk = kBlockPer * kRowThreads;
+
 struct AcceptWs {
     int *cnt;        // [B]: one completion counter per sequence, shared by the call's kernels in turn
     RowPart *part;   // [B][rows][npart]: one partial per (chunk, wave)
@@ -69,6 +81,9 @@ struct AcceptWs {
     ResPart *res;    // [B][nchunk]
     double *seg;     // [B][nchunk][PER][2]: (A, B) of each 256-token segment of a chunk
     double *apart;   // [B][gamma][nchunk]
+    BlockChunk *bchunk;  // block verification: [B][gamma + 1][4096-token chunks]
+    double *bseg;        // block verification: [B][gamma + 1][chunks][16][2] (A, B per segment)
+    GumbelPart *gpart;   // Gumbel coupling: [B][gamma + 1][4096-token chunks]
 };
 
 struct AcceptArgs {
@@ -79,6 +94,8 @@ struct AcceptArgs {
     float kf;          // log2(e) / T in fp32, for the bulk exponentials
     double inv_t;      // 1 / T in fp64, for decided probabilities
     double kd;         // log2(e) / T in fp64, for chunk rescaling
+    double tau;        // T in fp64 (Gumbel scores l / T)
+    int rule;          // sv_rule
     const float *target, *draft;
     const int32_t *tokens;
     uint64_t seed, step;
@@ -90,10 +107,10 @@ struct AcceptArgs {
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-    size_t cnt, part, u, res, seg, apart, total;
+    size_t cnt, part, u, res, seg, apart, bchunk, bseg, gchunk, total;
 };
 
-static WsLayout accept_layout(int B, int gamma, int V)
+static WsLayout accept_layout(int B, int gamma, int V, int rule = SV_RULE_TOKEN)
 {
     const size_t rows = 2 * (size_t)gamma + 1;
     const size_t nchunk = ((size_t)V + kMinChunk - 1) / kMinChunk;  // the larger of the two chunk counts
@@ -111,6 +128,13 @@ static WsLayout accept_layout(int B, int gamma, int V)
     o += align256((size_t)B * (nchunk + 3) * 16 * 2 * sizeof(double));
     L.apart = o;
     o += align256((size_t)B * gamma * nchunk * sizeof(double));
+    const size_t bnchunk = ((size_t)V + kBlockChunk - 1) / kBlockChunk;
+    L.bchunk = o;
+    if (rule == SV_RULE_BLOCK) o += align256((size_t)B * (gamma + 1) * bnchunk * sizeof(BlockChunk));
+    L.bseg = o;
+    if (rule == SV_RULE_BLOCK) o += align256((size_t)B * (gamma + 1) * bnchunk * kBlockPer * 2 * sizeof(double));
+    L.gchunk = o;
+    if (rule == SV_RULE_GUMBEL) o += align256((size_t)B * (gamma + 1) * bnchunk * sizeof(GumbelPart));
     L.total = o;
     return L;
 }
@@ -704,6 +728,510 @@ __global__ __launch_bounds__(kRowThreads, 2) void accept_resample_kernel(AcceptA
     if (threadIdx.x == 0) a.out_tokens[(int64_t)b * (g + 1) + J] = y;
 }
 
+// ---------------------------------------------------------------------------
+// Block verification ("Speculative Decoding: The Art of Guessing Well", section "Block
+// verification"), after the statistics pass:
+//   block pass  grid (4096-token chunk, candidate k = 0..gamma, sequence).  Candidate k
+//               keeps k drafts; its residual (w_k p_{k+1} - q_{k+1})+ lives on target row
+//               k and draft row k (none for k = gamma).  Every block weighs its chunk of
+//               both rows in fp64 (exp2_acc) and stores the sums of wp and wq over every
+//               token, and (A, B) = the sums over the tokens whose residual is positive by
+//               the statistics pass's estimates (normalizers and w_k), per chunk and per
+//               256-token segment.
+//   decide      one block per sequence: exact normalizers (sums of the chunk totals), exact
+//               p_k(x_k), q_k(x_k) and running weights w_k, masses m_k = sum over chunks of
+//               max(0, w_k A/Zp - B/Zq) (m_gamma = w_gamma), survival h_k =
+//               m_k / (m_k + 1 - w_k), n = the longest prefix with u_{k-1} <= h_k, then the
+//               draw from candidate n's segments as in the residual draw.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ double next_weight(double w, double p, double q)
+{
+    return q > 0.0 ? fmin(1.0, w * p / q) : ((w > 0.0 && p > 0.0) ? 1.0 : 0.0);
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kRowThreads, 2) void accept_block_pass_kernel(AcceptArgs a, AcceptWs w)
+{
+    constexpr int PER = kBlockPer;
+    extern __shared__ __align__(16) unsigned char dyn_lds[];
+    __shared__ double sM[129], sZ[129];
+    __shared__ double dscr[2 * (kRowThreads / kWave)];
+    __shared__ double s_p[64], s_q[64];
+    __shared__ double s_w;
+    const int c = blockIdx.x, kc = blockIdx.y, b = blockIdx.z;
+    const int g = a.gamma;
+    const int nch = gridDim.x;
+    // the drafted tokens' logits (estimates of p_j(x_j), q_j(x_j) for j < kc)
+    const int ti = min((int)threadIdx.x, g - 1);
+    const int x = a.tokens[(int64_t)b * g + ti];
+    const int xc = min(max(x, 0), a.V - 1);
+    const float lpx = a.target[((int64_t)b * (g + 1) + ti) * a.V + xc];
+    const float lqx = a.draft[((int64_t)b * g + ti) * a.V + xc];
+    const RowPart *pp = w.part + (int64_t)b * a.rows * a.npart;
+    RowPart *stage = reinterpret_cast<RowPart *>(dyn_lds);
+    if (a.rows * a.npart <= kMaxStaged) {
+        stage_parts(pp, a.rows * a.npart, stage, [] {});
+        row_softmax_stats(stage, a.rows, a.npart, a.kd, sM, sZ);
+    } else {
+        row_softmax_stats(pp, a.rows, a.npart, a.kd, sM, sZ);
+    }
+    if ((int)threadIdx.x < kc) {
+        const int j = threadIdx.x;
+        s_p[j] = exp(((double)lpx - sM[j]) * a.inv_t) / sZ[j];
+        s_q[j] = exp(((double)lqx - sM[g + 1 + j]) * a.inv_t) / sZ[g + 1 + j];
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double wk = 1.0;
+        for (int j = 0; j < kc; ++j) wk = next_weight(wk, s_p[j], s_q[j]);
+        s_w = wk;
+    }
+    __syncthreads();
+    const double wk = s_w;
+    const float *prow = a.target + ((int64_t)b * (g + 1) + kc) * a.V;
+    const float *qrow = kc < g ? a.draft + ((int64_t)b * g + kc) * a.V : prow;
+    const double Mp = sM[kc], Mq = kc < g ? sM[g + 1 + kc] : Mp;
+    const double iZp_est = 1.0 / sZ[kc], iZq_est = kc < g ? 1.0 / sZ[g + 1 + kc] : 0.0;
+    const double qmask = kc < g ? 1.0 : 0.0;
+    float xp[PER], xq[PER];
+    load_chunk2<VEC, PER>(prow, qrow, c * kBlockChunk, a.V, xp, xq);
+    double ta = 0.0, tb = 0.0, tp = 0.0, tq = 0.0;
+    double a4[PER / 4], b4[PER / 4];
+#pragma unroll
+    for (int k4 = 0; k4 < PER / 4; ++k4) {
+        a4[k4] = 0.0;
+        b4[k4] = 0.0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const double wp = exp2_acc(((double)xp[4 * k4 + j] - Mp) * a.kd);
+            const double wq = exp2_acc(((double)xq[4 * k4 + j] - Mq) * a.kd) * qmask;
+            tp += wp;
+            tq += wq;
+            const bool in = wk * wp * iZp_est > wq * iZq_est;
+            a4[k4] += in ? wp : 0.0;
+            b4[k4] += in ? wq : 0.0;
+        }
+        ta += a4[k4];
+        tb += b4[k4];
+    }
+    const int64_t slot = ((int64_t)b * (g + 1) + kc) * nch + c;
+    if (VEC) {
+        const int wv = threadIdx.x / kWave;
+        double *sg = w.bseg + slot * PER * 2;
+#pragma unroll
+        for (int k4 = 0; k4 < PER / 4; ++k4) {
+            const double sa = wave_sum(a4[k4]), sb = wave_sum(b4[k4]);
+            if (threadIdx.x % kWave == 0) {
+                sg[2 * (4 * k4 + wv)] = sa;
+                sg[2 * (4 * k4 + wv) + 1] = sb;
+            }
+        }
+    }
+    block_sum2(ta, tb, dscr);
+    block_sum2(tp, tq, dscr);
+    if (threadIdx.x == 0) w.bchunk[slot] = BlockChunk{ta, tb, tp, tq};
+}
+
+// One-pass draw over per-segment masses held kSegPerThread to a thread, in token order:
+// finds the segment whose running mass passes target = u * (the total); when rounding
+// leaves every running sum at or below target, the last segment with mass.  Returns
+// false (in every thread) when the total is not positive; else s_seg, s_base (the mass
+// before the segment) and s_target are set for the whole block.
+__device__ bool draw_segment(const double (&v)[kSegPerThread], double u, double *dscr, int *s_whit, int *s_wlast,
+                             int *s_seg, double *s_base, double *s_target)
+{
+    const int t = threadIdx.x, lane = t % kWave, wv = t / kWave;
+    const double ts = ((v[0] + v[1]) + v[2]) + v[3];
+    const double incl_w = wave_scan_incl(ts, 0.0, OpAdd());
+    __syncthreads();
+    if (lane == kWave - 1) dscr[wv] = incl_w;
+    __syncthreads();
+    double wbase = 0.0, zr = 0.0;
+#pragma unroll
+    for (int k = 0; k < kRowThreads / kWave; ++k) {
+        if (k < wv) wbase += dscr[k];
+        zr += dscr[k];
+    }
+    if (!(zr > 0.0)) return false;
+    const double incl = wbase + incl_w;
+    const double target = u * zr;
+    const uint64_t hit = __ballot(ts > 0.0 && incl > target);
+    const uint64_t pos = __ballot(ts > 0.0);
+    if (lane == 0) {
+        s_whit[wv] = hit ? wv * kWave + __ffsll((unsigned long long)hit) - 1 : kRowThreads;
+        s_wlast[wv] = pos ? wv * kWave + 63 - __clzll((unsigned long long)pos) : -1;
+    }
+    __syncthreads();
+    int th = kRowThreads, tl = -1;
+#pragma unroll
+    for (int k = 0; k < kRowThreads / kWave; ++k) {
+        th = min(th, s_whit[k]);
+        tl = max(tl, s_wlast[k]);
+    }
+    if (t == (th < kRowThreads ? th : tl)) {
+        double cum = incl - ts;
+        int sj = -1, lastj = 0;
+        double sbase = cum, lastbase = cum;
+#pragma unroll
+        for (int j = 0; j < kSegPerThread; ++j) {
+            if (v[j] > 0.0) {
+                if (sj < 0 && cum + v[j] > target) {
+                    sj = j;
+                    sbase = cum;
+                }
+                lastj = j;
+                lastbase = cum;
+            }
+            cum += v[j];
+        }
+        if (sj < 0) {
+            sj = lastj;
+            sbase = lastbase;
+        }
+        *s_seg = t * kSegPerThread + sj;
+        *s_base = sbase;
+        *s_target = target;
+    }
+    __syncthreads();
+    return true;
+}
+
+// One wave: the token of the 256-token segment starting at seg0 whose running weight, from
+// sbase, passes target (weights r(l_p, l_q) of four tokens per lane); the last token with
+// weight when rounding stops short.  Every lane returns it.
+template <typename W>
+__device__ int wave_token_in_segment(const float *prow, const float *qrow, int V, int seg0, double sbase,
+                                     double target, W r)
+{
+    const int lane = threadIdx.x % kWave;
+    const int e0 = seg0 + 4 * lane;
+    double wt[4];
+    if (V % 4 == 0) {
+        const int ec = min(e0, V - 4);
+        const float4 fp = *reinterpret_cast<const float4 *>(prow + ec);
+        const float4 fq = *reinterpret_cast<const float4 *>(qrow + ec);
+        const bool in = e0 < V;
+        wt[0] = in ? r(fp.x, fq.x) : 0.0;
+        wt[1] = in ? r(fp.y, fq.y) : 0.0;
+        wt[2] = in ? r(fp.z, fq.z) : 0.0;
+        wt[3] = in ? r(fp.w, fq.w) : 0.0;
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = min(e0 + j, V - 1);
+            wt[j] = e0 + j < V ? r(prow[e], qrow[e]) : 0.0;
+        }
+    }
+    const double lsum = ((wt[0] + wt[1]) + wt[2]) + wt[3];
+    const double c0 = sbase + wave_scan_incl(lsum, 0.0, OpAdd()) - lsum;
+    int hit = -1, lastpos = -1;
+    double pre = c0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        pre += wt[j];
+        if (hit < 0 && pre > target && wt[j] > 0.0) hit = j;
+        if (wt[j] > 0.0) lastpos = j;
+    }
+    const uint64_t hm = __ballot(c0 <= target && hit >= 0);
+    const uint64_t lm = __ballot(lastpos >= 0);
+    if (hm) {
+        const int hl = __ffsll((unsigned long long)hm) - 1;
+        return seg0 + 4 * hl + lane_value(hit, hl);
+    }
+    if (lm) {
+        const int ll = 63 - __clzll((unsigned long long)lm);
+        return seg0 + 4 * ll + lane_value(lastpos, ll);
+    }
+    return seg0;
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kRowThreads) void accept_block_decide_kernel(AcceptArgs a, AcceptWs w, int nch)
+{
+    extern __shared__ __align__(16) unsigned char dyn_lds[];
+    __shared__ double sM[129], sZ[129];
+    __shared__ double dscr[2 * (kRowThreads / kWave)];
+    __shared__ double s_zp[65], s_zq[65], s_m[65], s_wt[65], s_p[64], s_q[64];
+    __shared__ double s_base, s_target, s_ustar;
+    __shared__ int s_n, s_seg, s_chunk, s_usep, bad;
+    __shared__ int s_whit[kRowThreads / kWave], s_wlast[kRowThreads / kWave];
+    __shared__ double scan[kRowThreads];
+    __shared__ int iscr[kRowThreads / kWave];
+    const int b = blockIdx.x;
+    const int g = a.gamma;
+    const int ti = min((int)threadIdx.x, g - 1);
+    const int x = a.tokens[(int64_t)b * g + ti];
+    const int xc = min(max(x, 0), a.V - 1);
+    const float lpx = a.target[((int64_t)b * (g + 1) + ti) * a.V + xc];
+    const float lqx = a.draft[((int64_t)b * g + ti) * a.V + xc];
+    const double u_mine = w.u[(int64_t)b * (g + 1) + min((int)threadIdx.x, g)];
+    if (threadIdx.x == 0) bad = 0;
+    const RowPart *pp = w.part + (int64_t)b * a.rows * a.npart;
+    RowPart *stage = reinterpret_cast<RowPart *>(dyn_lds);
+    if (a.rows * a.npart <= kMaxStaged) {
+        stage_parts(pp, a.rows * a.npart, stage, [] {});
+        row_softmax_stats(stage, a.rows, a.npart, a.kd, sM, sZ);
+    } else {
+        row_softmax_stats(pp, a.rows, a.npart, a.kd, sM, sZ);
+    }
+    // exact normalizers of every candidate's rows, and the masses' (A, B) sums: one wave per
+    // candidate, lanes over the chunks, fixed order
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const BlockChunk *bc = w.bchunk + (int64_t)b * (g + 1) * nch;
+    for (int kc = wave; kc <= g; kc += kRowThreads / kWave) {
+        double zp = 0.0, zq = 0.0;
+        for (int c = lane; c < nch; c += kWave) {
+            zp += bc[(int64_t)kc * nch + c].wp;
+            zq += bc[(int64_t)kc * nch + c].wq;
+        }
+        zp = wave_sum(zp);
+        zq = wave_sum(zq);
+        if (lane == 0) {
+            s_zp[kc] = zp;
+            s_zq[kc] = zq;
+        }
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < g) {
+        const int j = threadIdx.x;
+        s_p[j] = exp2_acc(((double)lpx - sM[j]) * a.kd) / s_zp[j];
+        s_q[j] = exp2_acc(((double)lqx - sM[g + 1 + j]) * a.kd) / s_zq[j];
+        if (x < 0 || x >= a.V) bad = 1;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        s_wt[0] = 1.0;
+        for (int k = 1; k <= g; ++k) s_wt[k] = next_weight(s_wt[k - 1], s_p[k - 1], s_q[k - 1]);
+    }
+    __syncthreads();
+    for (int kc = wave; kc <= g; kc += kRowThreads / kWave) {
+        const double wk = s_wt[kc], ip = 1.0 / s_zp[kc], iq = kc < g ? 1.0 / s_zq[kc] : 0.0;
+        double m = 0.0;
+        for (int c = lane; c < nch; c += kWave) {
+            const BlockChunk q = bc[(int64_t)kc * nch + c];
+            m += fmax(0.0, wk * q.a * ip - q.b * iq);
+        }
+        m = wave_sum(m);
+        if (lane == 0) s_m[kc] = kc < g ? m : s_wt[g];
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int n = 0;
+        for (int k = 1; k <= g; ++k) {
+            const double wk = s_wt[k], mk = s_m[k];
+            const double h = wk < 1.0 ? mk / (mk + 1.0 - wk) : 1.0;
+            // the survival uniforms are w.u[b][0..gamma-1], the draw's w.u[b][gamma]
+            if (w.u[(int64_t)b * (g + 1) + k - 1] <= h) n = k;
+        }
+        s_n = n;
+    }
+    __syncthreads();
+    const int n = s_n;
+    int32_t *out = a.out_tokens + (int64_t)b * (g + 1);
+    for (int i = threadIdx.x; i <= g; i += kRowThreads)
+        if (i != n) out[i] = i < n ? a.tokens[(int64_t)b * g + i] : -1;
+    if (threadIdx.x == 0) {
+        a.accept_len[b] = n;
+        if (a.dev_status) a.dev_status[b] = bad ? 2 : 0;
+    }
+    // the draw from (w_n p_{n+1} - q_{n+1})+ (candidate n), with the uniform thread gamma holds
+    if ((int)threadIdx.x == g) s_ustar = u_mine;
+    __syncthreads();
+    const double us = s_ustar;
+    const float *prow = a.target + ((int64_t)b * (g + 1) + n) * a.V;
+    const float *qrow = n < g ? a.draft + ((int64_t)b * g + n) * a.V : prow;
+    const double Mp = sM[n], Mq = n < g ? sM[g + 1 + n] : Mp;
+    const double wn = s_wt[n], ip = 1.0 / s_zp[n], iq = n < g ? 1.0 / s_zq[n] : 0.0;
+    const double qmask = n < g ? 1.0 : 0.0;
+    auto r_of = [&](float lp, float lq) {
+        return fmax(0.0, wn * exp2_acc(((double)lp - Mp) * a.kd) * ip -
+                             exp2_acc(((double)lq - Mq) * a.kd) * qmask * iq);
+    };
+    const int nseg = nch * kBlockPer;
+    if (VEC && nseg <= kRowThreads * kSegPerThread) {
+        const int t = threadIdx.x;
+        const bool live = t * kSegPerThread < nseg;
+        const double2 *sg = reinterpret_cast<const double2 *>(
+            w.bseg + (((int64_t)b * (g + 1) + n) * nch) * kBlockPer * 2 +
+            (int64_t)min(t, nseg / kSegPerThread - 1) * kSegPerThread * 2);
+        double v[kSegPerThread];
+#pragma unroll
+        for (int j = 0; j < kSegPerThread; ++j) {
+            const double2 h = sg[j];
+            v[j] = live ? fmax(0.0, wn * h.x * ip - h.y * iq) : 0.0;
+        }
+        if (draw_segment(v, us, dscr, s_whit, s_wlast, &s_seg, &s_base, &s_target)) {
+            if (threadIdx.x < kWave) {
+                const int y = wave_token_in_segment(prow, qrow, a.V, 256 * s_seg, s_base, s_target, r_of);
+                if (lane == 0) out[n] = y;
+            }
+            return;
+        }
+    }
+    // chunk path: the chunk holding u* Z (wave 0), then the token inside it (the block); a
+    // residual without mass draws from p_{n+1}
+    if (threadIdx.x < kWave) {
+        const BlockChunk *q = bc + (int64_t)n * nch;
+        double zr = 0.0;
+        for (int c = lane; c < nch; c += kWave) zr += fmax(0.0, wn * q[c].a * ip - q[c].b * iq);
+        zr = wave_sum(zr);
+        const bool usep = !(zr > 0.0);
+        const double target = us * (usep ? 1.0 : zr);
+        int chunk;
+        double cbase;
+        wave_find_chunk(nch, target,
+                        [&](int c) { return usep ? q[c].wp * ip : fmax(0.0, wn * q[c].a * ip - q[c].b * iq); },
+                        chunk, cbase);
+        if (lane == 0) {
+            s_chunk = chunk;
+            s_base = cbase;
+            s_target = target;
+            s_usep = usep;
+        }
+    }
+    __syncthreads();
+    const bool usep = s_usep != 0;
+    auto weight = [&](float lp, float lq) -> double {
+        return usep ? exp2_acc(((double)lp - Mp) * a.kd) * ip : r_of(lp, lq);
+    };
+    int y = chunk_inverse_cdf<kBlockPer, VEC>(prow, qrow, s_chunk * kBlockChunk, a.V, s_base, s_target, weight,
+                                              scan, iscr);
+    if (y < 0) y = s_chunk * kBlockChunk;
+    if (threadIdx.x == 0) out[n] = y;
+}
+
+// ---------------------------------------------------------------------------
+// Gumbel-coupled verification ("Speculative Decoding: The Art of Guessing Well", section
+// "Sampling with shared noise"):
+//   gumbel pass  grid (4096-token chunk, position i = 0..gamma, sequence): the chunk's best
+//                score l/T - log(-log u) in fp64 (ties to the lowest token).  Every thread
+//                holds four groups of four consecutive tokens, so each group takes one
+//                Philox block (counter (x div 4, step, stream, tag + 2^32 i)).
+//   decide       one block per sequence: y_i = the best over the chunks, J = the first
+//                mismatch of the drafts, outputs.
+// ---------------------------------------------------------------------------
+template <bool VEC>
+__global__ __launch_bounds__(kRowThreads) void accept_gumbel_pass_kernel(AcceptArgs a, AcceptWs w)
+{
+    __shared__ double s_s[kRowThreads / kWave];
+    __shared__ int s_i[kRowThreads / kWave];
+    const int c = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
+    const int nch = gridDim.x;
+    const float *row = a.target + ((int64_t)b * (a.gamma + 1) + i) * a.V;
+    const int base = c * kBlockChunk;
+    const uint64_t stream = stream_of(a, b);
+    const uint64_t tag = kTagGumbel + ((uint64_t)i << 32);
+    double best = -INFINITY;
+    int arg = 0x7fffffff;
+    float lg[kBlockPer];
+#pragma unroll
+    for (int k4 = 0; k4 < kBlockPer / 4; ++k4) {
+        const int e = base + 4 * (int)threadIdx.x + 1024 * k4;
+        if (VEC) {
+            const float4 f = *reinterpret_cast<const float4 *>(row + min(e, a.V - 4));
+            lg[4 * k4 + 0] = f.x;
+            lg[4 * k4 + 1] = f.y;
+            lg[4 * k4 + 2] = f.z;
+            lg[4 * k4 + 3] = f.w;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) lg[4 * k4 + j] = row[min(e + j, a.V - 1)];
+        }
+    }
+#pragma unroll
+    for (int k4 = 0; k4 < kBlockPer / 4; ++k4) {
+        const int e = base + 4 * (int)threadIdx.x + 1024 * k4;
+        if (e >= a.V) continue;
+        uint64_t ctr[4] = {(uint64_t)e >> 2, a.step, stream, tag};
+        philox4x64_10(ctr, a.seed, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (e + j >= a.V) continue;
+            const double u = (double)(2 * (ctr[j] >> 12) + 1) * 0x1p-53;
+            const double sc = (double)lg[4 * k4 + j] / a.tau + (-log(-log(u)));
+            if (sc > best) {  // tokens are visited in increasing order: ties keep the first
+                best = sc;
+                arg = e + j;
+            }
+        }
+    }
+    // block argmax (larger score, then lower token)
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const double ob = __shfl_xor(best, off, kWave);
+        const int oa = __shfl_xor(arg, off, kWave);
+        if (ob > best || (ob == best && oa < arg)) {
+            best = ob;
+            arg = oa;
+        }
+    }
+    const int wv = threadIdx.x / kWave;
+    if (threadIdx.x % kWave == 0) {
+        s_s[wv] = best;
+        s_i[wv] = arg;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int k = 1; k < kRowThreads / kWave; ++k)
+            if (s_s[k] > best || (s_s[k] == best && s_i[k] < arg)) {
+                best = s_s[k];
+                arg = s_i[k];
+            }
+        w.gpart[((int64_t)b * (a.gamma + 1) + i) * nch + c] = GumbelPart{best, arg, 0};
+    }
+}
+
+__global__ __launch_bounds__(kRowThreads) void accept_gumbel_decide_kernel(AcceptArgs a, AcceptWs w, int nch)
+{
+    __shared__ int y[65];
+    __shared__ int firstbad, bad;
+    const int b = blockIdx.x;
+    const int g = a.gamma;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    if (threadIdx.x == 0) {
+        firstbad = g;
+        bad = 0;
+    }
+    const GumbelPart *gp = w.gpart + (int64_t)b * (g + 1) * nch;
+    for (int i = wave; i <= g; i += kRowThreads / kWave) {
+        double best = -INFINITY;
+        int arg = 0x7fffffff;
+        for (int c = lane; c < nch; c += kWave) {
+            const GumbelPart q = gp[(int64_t)i * nch + c];
+            if (q.s > best || (q.s == best && q.arg < arg)) {
+                best = q.s;
+                arg = q.arg;
+            }
+        }
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const double ob = __shfl_xor(best, off, kWave);
+            const int oa = __shfl_xor(arg, off, kWave);
+            if (ob > best || (ob == best && oa < arg)) {
+                best = ob;
+                arg = oa;
+            }
+        }
+        if (lane == 0) y[i] = arg;
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < g) {
+        const int x = a.tokens[(int64_t)b * g + threadIdx.x];
+        if (x != y[threadIdx.x]) atomicMin(&firstbad, (int)threadIdx.x);
+        if (x < 0 || x >= a.V) bad = 1;
+    }
+    __syncthreads();
+    const int J = firstbad;
+    int32_t *out = a.out_tokens + (int64_t)b * (g + 1);
+    for (int i = threadIdx.x; i <= g; i += kRowThreads) out[i] = i < J ? a.tokens[(int64_t)b * g + i] : (i == J ? y[J] : -1);
+    if (a.alpha)
+        for (int i = threadIdx.x; i < g; i += kRowThreads) a.alpha[(int64_t)b * g + i] = __int_as_float(0x7fc00000);
+    if (threadIdx.x == 0) {
+        a.accept_len[b] = J;
+        if (a.dev_status) a.dev_status[b] = bad ? 2 : 0;
+    }
+}
+
 template <typename K>
 static hipError_t launch(K kernel, dim3 grid, hipStream_t s, const AcceptArgs &a, const AcceptWs &w, size_t lds = 0)
 {
@@ -756,9 +1284,22 @@ static sv_status run_accept(const AcceptArgs &a, const AcceptWs &w, hipStream_t 
         if (launch(accept_stats_kernel<VEC, false, PER>, gstats, s, a, w) != hipSuccess) return SV_ERR_HIP;
         return launch(accept_greedy_kernel, dim3(a.B), s, a, w, lds) == hipSuccess ? SV_OK : SV_ERR_HIP;
     }
+    const int bnch = (a.V + kBlockChunk - 1) / kBlockChunk;
+    if (a.rule == SV_RULE_GUMBEL) {  // no statistics: Gumbel scores need no normalizer
+        if (launch(accept_gumbel_pass_kernel<VEC>, dim3(bnch, a.gamma + 1, a.B), s, a, w) != hipSuccess)
+            return SV_ERR_HIP;
+        hipLaunchKernelGGL(accept_gumbel_decide_kernel, dim3(a.B), dim3(kRowThreads), 0, s, a, w, bnch);
+        return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
+    }
     if (launch(accept_stats_kernel<VEC, true, PER>, gstats, s, a, w) != hipSuccess) return SV_ERR_HIP;
     if (alpha && launch(accept_alpha_kernel<VEC, PER>, dim3(a.nchunk, a.gamma, a.B), s, a, w) != hipSuccess)
         return SV_ERR_HIP;
+    if (a.rule == SV_RULE_BLOCK) {
+        if (launch(accept_block_pass_kernel<VEC>, dim3(bnch, a.gamma + 1, a.B), s, a, w, lds) != hipSuccess)
+            return SV_ERR_HIP;
+        hipLaunchKernelGGL(accept_block_decide_kernel<VEC>, dim3(a.B), dim3(kRowThreads), lds, s, a, w, bnch);
+        return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
+    }
     return launch_resample<VEC, PER>(a, w, s, lds) == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
@@ -767,7 +1308,8 @@ static sv_status run_accept(const AcceptArgs &a, const AcceptWs &w, hipStream_t 
 extern "C" size_t sv_spec_accept_workspace(const sv_accept_desc *d)
 {
     if (!d || d->B < 0 || d->gamma < 1 || d->V < 1) return 0;
-    return accept_layout(d->B, d->gamma, d->V).total;
+    if (d->rule != SV_RULE_TOKEN && d->rule != SV_RULE_BLOCK && d->rule != SV_RULE_GUMBEL) return 0;
+    return accept_layout(d->B, d->gamma, d->V, d->rule).total;
 }
 
 extern "C" sv_status sv_spec_accept(const sv_accept_desc *d, void *workspace, size_t workspace_bytes, void *stream)
@@ -777,12 +1319,13 @@ extern "C" sv_status sv_spec_accept(const sv_accept_desc *d, void *workspace, si
     if (d->mode != SV_GREEDY && d->mode != SV_SAMPLE) return SV_ERR_INVALID_ARG;
     if (!(d->temperature >= 0.0f) || d->temperature == INFINITY) return SV_ERR_INVALID_ARG;
     if (d->gamma > 64) return SV_ERR_UNSUPPORTED;
+    if (d->rule != SV_RULE_TOKEN && d->rule != SV_RULE_BLOCK && d->rule != SV_RULE_GUMBEL) return SV_ERR_INVALID_ARG;
     const bool sample = d->mode == SV_SAMPLE && d->temperature > 0.0f;
     if (!d->target_logits || !d->draft_tokens || !d->accept_len || !d->out_tokens) return SV_ERR_INVALID_ARG;
-    if (sample && !d->draft_logits) return SV_ERR_INVALID_ARG;
+    if (sample && d->rule != SV_RULE_GUMBEL && !d->draft_logits) return SV_ERR_INVALID_ARG;
     if (d->B == 0) return SV_OK;
     if (d->B > kMaxCounters) return SV_ERR_UNSUPPORTED;
-    const WsLayout L = accept_layout(d->B, d->gamma, d->V);
+    const WsLayout L = accept_layout(d->B, d->gamma, d->V, d->rule);
     if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace & 255)) return SV_ERR_WORKSPACE;
 
     char *ws = (char *)workspace;
@@ -793,6 +1336,9 @@ extern "C" sv_status sv_spec_accept(const sv_accept_desc *d, void *workspace, si
     w.res = (ResPart *)(ws + L.res);
     w.seg = (double *)(ws + L.seg);
     w.apart = (double *)(ws + L.apart);
+    w.bchunk = (BlockChunk *)(ws + L.bchunk);
+    w.bseg = (double *)(ws + L.bseg);
+    w.gpart = (GumbelPart *)(ws + L.gchunk);
 
     AcceptArgs a;
     a.B = d->B;
@@ -804,6 +1350,8 @@ extern "C" sv_status sv_spec_accept(const sv_accept_desc *d, void *workspace, si
     a.kd = 1.4426950408889634 / T;
     a.kf = (float)a.kd;
     a.inv_t = 1.0 / T;
+    a.tau = T;
+    a.rule = d->rule;
     a.target = d->target_logits;
     a.draft = d->draft_logits;
     a.tokens = d->draft_tokens;

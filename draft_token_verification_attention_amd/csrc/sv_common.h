@@ -54,6 +54,8 @@ constexpr size_t kCounterBytes = 128 * 1024;
 constexpr int kMaxCounters = (int)(kCounterBytes / sizeof(int));
 constexpr uint64_t kTagAccept = 0x53560001ULL;
 constexpr uint64_t kTagWalk = 0x53560002ULL;
+constexpr uint64_t kTagGumbel = 0x53560003ULL;
+constexpr uint64_t kTagRRS = 0x53560004ULL;
 
 // Compute units of the current device (host side, asked of the runtime on every call:
 // the library keeps no state between calls).  Looping kernels size their grids from it.

@@ -63,6 +63,16 @@ typedef enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
  * as the temperature goes to 0 both models approach their argmax).                      */
 typedef enum sv_mode { SV_GREEDY = 0, SV_SAMPLE = 1 } sv_mode;
 
+/* Verification rule of sv_spec_accept in SAMPLE mode (GREEDY mode is greedy matching   */
+/* under every rule: each reduces to it when both models are one-hot).                    */
+/*   TOKEN:  speculative sampling, token by token ([TB] "The speculative sampling rule").  */
+/*   BLOCK:  block verification ([AG] "Block verification"): the drafted prefix is kept    */
+/*           jointly, by running weights w_k = min(1, w_{k-1} p_k(x_k)/q_k(x_k)).          */
+/*   GUMBEL: Gumbel-coupled verification ([AG] "Sampling with shared noise"): the target    */
+/*           samples every position by Gumbel-max with noise it shares with the drafter,  */
+/*           and the longest prefix where the drafts equal those samples is kept.          */
+typedef enum sv_rule { SV_RULE_TOKEN = 0, SV_RULE_BLOCK = 1, SV_RULE_GUMBEL = 2 } sv_rule;
+
 /* CAUSAL: bottom-right-aligned causal mask of a chain ([TB] "Checking several tokens costs
  * about as much as writing one").  TREE: ancestor-or-self mask of a token tree ([TB] box
  * "Token tree and tree attention"; [MED] "Attention Tree").                              */
@@ -193,6 +203,20 @@ SV_API sv_status sv_verify_attention(const sv_attn_desc *desc, void *workspace, 
 /*                 skips its extra pass over the rows                                    */
 /*   dev_status    optional device int32 [B]: 0, or 2 when a draft token is outside      */
 /*                 [0, V) (that sequence's outputs are then unspecified)                 */
+/*   rule          SV_RULE_TOKEN (the above), SV_RULE_BLOCK or SV_RULE_GUMBEL (SAMPLE     */
+/*                 mode; see below).  The workspace size depends on it.                   */
+/* BLOCK ([AG] "Block verification"): with p_k, q_k the target rows and draft rows of     */
+/*   position k (row k-1) and w_0 = 1, w_k = min(1, w_{k-1} p_k(x_k)/q_k(x_k)) (a drafted  */
+/*   token with q = 0 gives 1 if p > 0, else 0), prefix k survives when its uniform       */
+/*   (index k-1) is <= h_k = m_k / (m_k + 1 - w_k) (1 when w_k = 1), m_k =                 */
+/*   sum_x (w_k p_{k+1}(x) - q_{k+1}(x))+ and m_gamma = w_gamma; J = the longest surviving */
+/*   prefix, and the extra token is an inverse-CDF draw (index gamma) from                */
+/*   (w_J p_{J+1} - q_{J+1})+ (q_{gamma+1} = 0; a zero residual falls back to p_{J+1}).    */
+/* GUMBEL ([AG] "Sampling with shared noise"): y_i = argmax_x (l_i(x)/T + g_i(x)),         */
+/*   g = -log(-log u), u of token x at position i the word x mod 4 of the Philox block    */
+/*   with counter (x div 4, step, stream, 0x53560003 + 2^32 i); J = the first i < gamma    */
+/*   with x_i != y_i (else gamma); emits x_0..x_{J-1}, y_J.  Draft logits are not read    */
+/*   (the drafter used the same noise); scores in fp64, ties to the lowest token.          */
 /* Supported: 1 <= gamma <= 64, 1 <= V, B <= 32768.                                      */
 /* ---------------------------------------------------------------------------------- */
 typedef struct sv_accept_desc {
@@ -207,6 +231,7 @@ typedef struct sv_accept_desc {
     int32_t *out_tokens;
     float *alpha;
     int32_t *dev_status;
+    sv_rule rule;
 } sv_accept_desc;
 
 SV_API size_t sv_spec_accept_workspace(const sv_accept_desc *desc);
