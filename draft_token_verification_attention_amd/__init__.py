@@ -22,6 +22,7 @@ SV_STATIC_SCRATCH_BYTES = 16 << 20
 SV_F32, SV_BF16 = 0, 1
 SV_GREEDY, SV_SAMPLE = 0, 1
 SV_RULE_TOKEN, SV_RULE_BLOCK, SV_RULE_GUMBEL = 0, 1, 2
+SV_WALK_MATCH, SV_WALK_RRS, SV_WALK_RRS_WOR = 0, 1, 2
 SV_MASK_CAUSAL, SV_MASK_TREE = 0, 1
 
 _P = ctypes.c_void_p
@@ -53,7 +54,8 @@ class sv_accept_desc(ctypes.Structure):
 class sv_walk_desc(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int), ("B", _i32), ("n", _i32), ("V", _i32), ("max_depth", _i32),
                 ("temperature", _f32), ("logits", _P), ("tokens", _P), ("parents", _P), ("rng", sv_philox),
-                ("accept_len", _P), ("path", _P), ("out_tokens", _P), ("dev_status", _P)]
+                ("accept_len", _P), ("path", _P), ("out_tokens", _P), ("dev_status", _P),
+                ("rule", ctypes.c_int), ("draft_logits", _P), ("max_children", _i32)]
 
 
 class sv_commit_desc(ctypes.Structure):
@@ -260,7 +262,8 @@ def sv_spec_accept_static(mode: int, target, draft, draft_tokens, temperature: f
 
 
 def walk_desc(mode, logits, tokens, parents, max_depth, temperature, seed, step, stream_ids,
-              accept_len, path, out_tokens, dev_status) -> sv_walk_desc:
+              accept_len, path, out_tokens, dev_status, rule: int = SV_WALK_MATCH, draft_logits=None,
+              max_children: int = 0) -> sv_walk_desc:
     B, n, V = logits.shape
     d = sv_walk_desc()
     d.mode, d.B, d.n, d.V, d.max_depth, d.temperature = int(mode), B, n, V, int(max_depth), float(temperature)
@@ -268,11 +271,15 @@ def walk_desc(mode, logits, tokens, parents, max_depth, temperature, seed, step,
     d.rng = sv_philox(int(seed), int(step), None if stream_ids is None else stream_ids.data_ptr())
     d.accept_len, d.path, d.out_tokens = accept_len.data_ptr(), path.data_ptr(), out_tokens.data_ptr()
     d.dev_status = None if dev_status is None else dev_status.data_ptr()
+    d.rule = int(rule)
+    d.draft_logits = None if draft_logits is None else draft_logits.data_ptr()
+    d.max_children = int(max_children)
     return d
 
 
 def sv_tree_walk(mode: int, logits, tokens, parents, max_depth: int, temperature: float, seed: int,
-                 step: int = 0, stream_ids=None):
+                 step: int = 0, stream_ids=None, rule: int = SV_WALK_MATCH, draft_logits=None,
+                 max_children: int = 0):
     """logits fp32 [B][n][V]; tokens int32 [B][n]; parents int32 [n].
     Returns dict(accept_len, path, out_tokens, status) as device tensors."""
     _need_cuda(logits, tokens, parents, stream_ids)
@@ -286,7 +293,10 @@ def sv_tree_walk(mode: int, logits, tokens, parents, max_depth: int, temperature
     out = torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev)
     status = torch.empty(B, dtype=torch.int32, device=dev)
     sid = None if stream_ids is None else stream_ids.to(torch.int64).contiguous()
-    d = walk_desc(mode, logits, tokens, parents, max_depth, temperature, seed, step, sid, acc, path, out, status)
+    _need_cuda(draft_logits)
+    draft_logits = None if draft_logits is None else draft_logits.contiguous()
+    d = walk_desc(mode, logits, tokens, parents, max_depth, temperature, seed, step, sid, acc, path, out, status,
+                  rule, draft_logits, max_children)
     nb = lib.sv_tree_walk_workspace(ctypes.byref(d))
     ws = workspace(nb, dev)
     _check(lib.sv_tree_walk(ctypes.byref(d), _ptr(ws), nb, _stream(dev)), "sv_tree_walk")

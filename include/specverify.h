@@ -273,12 +273,30 @@ SV_API sv_status sv_spec_accept_static(const sv_accept_desc *desc, void *stream)
 /*   path       device int32 [B][max_depth+1] = (0, n_1, ..., n_J, -1, ...)              */
 /*   out_tokens device int32 [B][max_depth+1] = (tokens of n_1..n_J, the choice at n_J,  */
 /*              -1, ...)                                                                 */
-/*   dev_status optional device int32 [B]: 0, or 3 when the walk would go below         */
+/*   dev_status optional device int32 [B]: 0, 5 (RRS, see below), or 3 when the walk    */
+/*              would go below                                                           */
 /*              max_depth: it then stops at its node at depth max_depth and emits the    */
 /*              choice there as the extra token (accept_len = max_depth; still a draw    */
 /*              from the target at that node)                                            */
+/*   rule       SV_WALK_MATCH: the walk above.  SAMPLE mode only (GREEDY is the greedy     */
+/*              walk under every rule): SV_WALK_RRS, recursive rejection ([TB] box         */
+/*              "Recursive rejection at a node with several children"): the children      */
+/*              s_1..s_k of node v (node order) were drawn i.i.d. from the drafter's q_v   */
+/*              = softmax(draft_logits[v] / T); with R_1 = p_v, child i is accepted when   */
+/*              u q(s_i) < R_i(s_i), R_{i+1} = (R_i - q)+ normalized, and if every child   */
+/*              is rejected (or v is a leaf) the extra token is drawn from R_{k+1};        */
+/*              SV_WALK_RRS_WOR, the same for children drawn without replacement (same    */
+/*              section): a rejected token is also removed from q, which is renormalized. */
+/*              Uniforms: tag 0x53560004, index 2^16 d + i for try i at depth d, 2^16 d +  */
+/*              0xffff for the draw.  An accepted child at max_depth is emitted as the    */
+/*              extra token (status 3).                                                   */
+/*   draft_logits  RRS: device fp32 [B][n][V], row v = the drafter's logits at node v       */
+/*   max_children  RRS: a bound on the children of any node (1..64; it sets the number of  */
+/*              passes per level); a node with more sets status 5 and ends its walk       */
 /* Supported: 1 <= n, 0 <= max_depth <= 63, 1 <= V, B <= 32768.                          */
 /* ---------------------------------------------------------------------------------- */
+typedef enum sv_walk_rule { SV_WALK_MATCH = 0, SV_WALK_RRS = 1, SV_WALK_RRS_WOR = 2 } sv_walk_rule;
+
 typedef struct sv_walk_desc {
     sv_mode mode;
     int32_t B, n, V, max_depth;
@@ -291,6 +309,9 @@ typedef struct sv_walk_desc {
     int32_t *path;
     int32_t *out_tokens;
     int32_t *dev_status;
+    sv_walk_rule rule;
+    const float *draft_logits;
+    int32_t max_children;
 } sv_walk_desc;
 
 SV_API size_t sv_tree_walk_workspace(const sv_walk_desc *desc);
