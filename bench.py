@@ -114,12 +114,13 @@ def main():
     line = run_workload(args.workload, args, dev, args.steps, args.warmup, cpu=not args.no_cpu, headline=True)
     if not args.no_extra:
         extra = {}
-        for wl in (2, 5):
+        for wl in (2, 3, 5):
             if wl == args.workload:
                 continue
             r = run_workload(wl, args, dev, 50, 5, cpu=False, headline=False)
             extra[r["config"]["workload"]] = {k: r[k] for k in ("value", "unit", "ms_per_step", "roofline",
-                                                                 "roofline_other", "kernels_ms") if k in r}
+                                                                 "roofline_other", "kernels_ms", "next_rows")
+                                              if k in r}
         line["other_workloads"] = extra
     print(json.dumps(line), flush=True)
 
@@ -182,6 +183,76 @@ def attention_timing(sv, adescs, ws, R, first, steps, run_rest, sh):
         torch.cuda.synchronize()
     t = lambda a, b: float(np.median([e[a].elapsed_time(e[b]) for e in events]))  # noqa: E731
     return dict(main=t(4, 5), attn_span=t(4, 6), combine=t(5, 6), attn_call=t(0, 1), rest=t(1, 2))
+
+
+def median_event_ms(call, steps, sh):
+    """Median over `steps` eager calls of the time between events recorded on the launch
+    stream right before and right after each call (dispatch included)."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(3):
+        call(i)
+    torch.cuda.synchronize()
+    for i, (e0, e1) in enumerate(ev):
+        e0.record()
+        call(i)
+        e1.record()
+    torch.cuda.synchronize()
+    return float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
+
+
+def time_accept_rule(sv, copies, toks, tau, seed, rule, shape, steps, sh, dev):
+    """sv_spec_accept under another rule on the same inputs (the GPU's own inputs, rotated)."""
+    import torch
+    B, gamma, V = shape
+    R = len(copies)
+    acc_len = torch.empty(B, dtype=torch.int32, device=dev)
+    out_tok = torch.empty((B, gamma + 1), dtype=torch.int32, device=dev)
+    status = torch.empty(B, dtype=torch.int32, device=dev)
+    descs = [sv.accept_desc(sv.SV_SAMPLE, c["target"], c["draft"], toks, tau, seed, 0, None, acc_len, out_tok, None,
+                            status, rule) for c in copies]
+    nb = sv.lib.sv_spec_accept_workspace(ctypes.byref(descs[0]))
+    ws = torch.zeros(nb + 256, dtype=torch.uint8, device=dev)
+    pw = _aligned(ws)
+
+    def call(i):
+        if sv.lib.sv_spec_accept(ctypes.byref(descs[i % R]), pw, nb, sh):
+            raise RuntimeError("acceptance launch failed")
+    ms = median_event_ms(call, steps, sh)
+    rows = (2 * gamma + 1) if rule != sv.SV_RULE_GUMBEL else (gamma + 1)
+    nbytes = 4 * V * B * rows
+    out = {"kernel_ms": round(ms, 5), "value": round(B * gamma / (ms * 1e-3), 1), "unit": "draft tokens/s (acceptance alone)",
+           "algorithmic_bytes": nbytes, "achieved_GBs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+           "mean_accepted": float(acc_len.float().mean().item())}
+    if rule == sv.SV_RULE_GUMBEL:
+        out["note"] = ("ALU-bound: a Philox4x64-10 block per four tokens and two fp64 logarithms per token; "
+                       "drafts from the workload's own sampler (independent noise), which changes no cost")
+    return out
+
+
+def time_commit(sv, k, v, kv_off, prefix, acc_len, path, n_q, Hkv, D, kv_sh, kv_st, kv_sb, esize, steps, sh, dev):
+    """sv_kv_commit on the given caches (new lengths to a separate buffer, so every call
+    moves the same rows).  Algorithmic bytes: the moved K and V rows, read and written."""
+    import torch
+    B = prefix.numel()
+    new_len = torch.empty(B, dtype=torch.int32, device=dev)
+    status = torch.empty(B, dtype=torch.int32, device=dev)
+    d = sv.commit_desc(k, v, kv_off, prefix, acc_len, n_q=n_q, Hkv=Hkv, D=D, kv_sh=kv_sh, kv_st=kv_st, kv_sb=kv_sb,
+                       path=path, new_len=new_len, dev_status=status)
+
+    def call(i):
+        if sv.lib.sv_kv_commit(ctypes.byref(d), sh):
+            raise RuntimeError("commit launch failed")
+    ms = median_event_ms(call, steps, sh)
+    moved = 0
+    if path is not None:
+        J = acc_len.cpu().numpy()
+        pth = path.cpu().numpy()
+        moved = int(sum(int((pth[b, 1:J[b] + 1] != np.arange(1, J[b] + 1)).sum()) for b in range(B)))
+    nbytes = moved * Hkv * D * esize * 2 * 2
+    return {"kernel_ms": round(ms, 5), "rows_moved": moved, "algorithmic_bytes": nbytes,
+            "achieved_GBs": round(nbytes / (ms * 1e-3) / 1e9, 3) if nbytes else 0.0,
+            "bound": "latency (one block per sequence; a few KB to move)"}
 
 
 def timed_steps(launch, R, steps, warmup, eager, sh):
@@ -332,6 +403,15 @@ def bench_chain(args, cfg, wl, dev, steps, warmup, cpu):
         "accept": {"kernel_ms": round(t["rest"], 5), "algorithmic_bytes": acc_bytes,
                    "achieved_GBs": round(gbs(acc_bytes, t["rest"]), 1)},
     }
+    if bf:
+        line["next_rows"] = {
+            "block_verification": time_accept_rule(sv, copies, toks, tau, seed, sv.SV_RULE_BLOCK, (B, gamma, V),
+                                                   steps, sh, dev),
+            "gumbel_verification": time_accept_rule(sv, copies, toks, tau, seed, sv.SV_RULE_GUMBEL, (B, gamma, V),
+                                                    steps, sh, dev),
+            "kv_commit_chain": time_commit(sv, base["k"], base["v"], kv_off, prefix, acc_len, None, n_q, Hkv, D,
+                                           att["kv_sh"], att["kv_st"], kv_sb, esz, steps, sh, dev),
+        }
     if cpu:
         # the GPU's own outputs for the step on copy 0 (seed, step 0), for the parity verdict
         launch(0, sh)
@@ -447,6 +527,46 @@ def bench_tree(args, cfg, wl, dev, steps, warmup, cpu):
            "main_kernel_only": {"kernel_ms": round(t["main"], 5),
                                 "frac": round(att_bytes / (t["main"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
     walk_rows = int(acc_len.cpu().numpy()[0]) + 1
+    # next rows: the KV commit of the walked branch (on a copy of the caches), and for the
+    # small tree the walk by recursive rejection (draft logits = target + N(0, 1) noise)
+    # the commit gathers the tree's deepest branch (the longest the walk can accept; a sampled
+    # walk of one step often accepts few nodes)
+    leaf = int(np.argmax(depth))
+    branch = []
+    while leaf >= 0:
+        branch.append(leaf)
+        leaf = int(parents[leaf])
+    branch = branch[::-1]
+    cpath = torch.full((1, max_depth + 1), -1, dtype=torch.int32)
+    cpath[0, :len(branch)] = torch.tensor(branch, dtype=torch.int32)
+    cacc = torch.tensor([len(branch) - 1], dtype=torch.int32, device=dev)
+    kc, vc = base["k"].clone(), base["v"].clone()
+    nxt = {"kv_commit_tree": time_commit(sv, kc, vc, kv_off, prefix, cacc, cpath.to(dev), n, Hkv, D, att["kv_sh"],
+                                         att["kv_st"], 0, 2, steps, sh, dev)}
+    nxt["kv_commit_tree"]["branch"] = branch
+    del kc, vc
+    if n <= 128:
+        lg_d = base["logits"]
+        noise = torch.from_numpy(synth.normal(wl, "draft_noise", (1, n, V))).to(dev)
+        dr_d = lg_d + noise
+        kids = np.bincount(parents[1:], minlength=n)
+        mk = int(kids.max())
+        rdesc = sv.walk_desc(sv.SV_SAMPLE, lg_d, toks_d, par_d, max_depth, tau, seed, 0, None, acc_len, path, out_tok,
+                             wstat, sv.SV_WALK_RRS, dr_d, mk)
+        nb = sv.lib.sv_tree_walk_workspace(ctypes.byref(rdesc))
+        wsr = torch.zeros(nb + 256, dtype=torch.uint8, device=dev)
+        pr = _aligned(wsr)
+
+        def rcall(i):
+            rdesc.rng.step = i
+            if sv.lib.sv_tree_walk(ctypes.byref(rdesc), pr, nb, sh):
+                raise RuntimeError("rrs walk failed")
+        ms = median_event_ms(rcall, steps, sh)
+        nxt["rrs_walk"] = {"kernel_ms": round(ms, 5), "max_children": mk,
+                           "launches": (max_depth + 1) * (1 + mk),
+                           "note": "node tokens of the workload's drafter; draft logits = target + N(0,1)",
+                           "bound": "latency (launches per level: one node pass and max_children try passes)"}
+        del noise, dr_d
     line = {
         "metric": "draft tokens verified/sec on 1 MI355X; achieved HBM GB/s as % of peak",
         "value": round(value, 1), "unit": "draft tokens/s", "n_gpus": 1, "steps": steps,
@@ -461,6 +581,7 @@ def bench_tree(args, cfg, wl, dev, steps, warmup, cpu):
                        "attn_combine_kernel": round(t["combine"], 5),
                        "attention_call_with_dispatch": round(t["attn_call"], 5), "sv_tree_walk": round(t["rest"], 5)},
         "walk": {"kernel_ms": round(t["rest"], 5), "rows_visited": walk_rows, "algorithmic_bytes": 4 * V * walk_rows},
+        "next_rows": nxt,
     }
     if cpu:
         launch(0, sh)
