@@ -225,7 +225,7 @@ def time_accept_rule(sv, copies, toks, tau, seed, rule, shape, steps, sh, dev):
            "algorithmic_bytes": nbytes, "achieved_GBs": round(nbytes / (ms * 1e-3) / 1e9, 1),
            "mean_accepted": float(acc_len.float().mean().item())}
     if rule == sv.SV_RULE_GUMBEL:
-        out["note"] = ("ALU-bound: a Philox4x64-10 block per four tokens and two fp64 logarithms per token; "
+        out["note"] = ("ALU-bound: a Philox4x64-10 block per four tokens and two fp32 logarithms per token (fp64 scores only for the few tokens near each chunk's best); "
                        "drafts from the workload's own sampler (independent noise), which changes no cost")
     return out
 

@@ -1106,23 +1106,43 @@ __global__ __launch_bounds__(kRowThreads) void accept_block_decide_kernel(Accept
 //   gumbel pass  grid (4096-token chunk, position i = 0..gamma, sequence): the chunk's best
 //                score l/T - log(-log u) in fp64 (ties to the lowest token).  Every thread
 //                holds four groups of four consecutive tokens, so each group takes one
-//                Philox block (counter (x div 4, step, stream, tag + 2^32 i)).
+//                Philox block (counter (x div 4, step, stream, tag + 2^32 i)).  Scores are
+//                first estimated in fp32 (hardware log2); only tokens whose estimate lies
+//                within a margin of the chunk's best estimate -- far wider than the
+//                estimate's error, so the fp64 winner is always among them -- get the fp64
+//                score, which alone decides.
 //   decide       one block per sequence: y_i = the best over the chunks, J = the first
 //                mismatch of the drafts, outputs.
 // ---------------------------------------------------------------------------
+// fp32 estimate of -log(u) for the uniform u = (2 (w >> 12) + 1) 2^-53 of Philox word w,
+// relative error under 1e-5: log2 of u itself when u < 1/2; otherwise -log(1 - r) of
+// r = 1 - u, which is formed exactly from the integer, through a short series for r <= 1/64
+// (log2 of a number near 1 would lose the relative precision there).
+__device__ __forceinline__ float neg_log_uniform_f32(uint64_t w)
+{
+    constexpr float kLn2f = 0.69314718055994530942f;
+    const uint64_t n = 2 * (w >> 12) + 1;          // u = n 2^-53
+    const bool low = n < (1ull << 52);             // u < 1/2
+    const uint64_t k = low ? n : (1ull << 53) - n; // 2^53 u, or 2^53 (1 - u)
+    const float x = fmaf((float)(uint32_t)(k >> 32), 0x1p32f, (float)(uint32_t)k) * 0x1p-53f;
+    if (low) return -__builtin_amdgcn_logf(x) * kLn2f;
+    if (x <= 0x1p-6f) return x * (1.f + x * (0.5f + x * (1.f / 3.f + x * 0.25f)));
+    return -__builtin_amdgcn_logf(1.f - x) * kLn2f;
+}
+
 template <bool VEC>
 __global__ __launch_bounds__(kRowThreads) void accept_gumbel_pass_kernel(AcceptArgs a, AcceptWs w)
 {
+    constexpr float kLn2f = 0.69314718055994530942f;
     __shared__ double s_s[kRowThreads / kWave];
     __shared__ int s_i[kRowThreads / kWave];
+    __shared__ float s_m[kRowThreads / kWave];
     const int c = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
     const int nch = gridDim.x;
     const float *row = a.target + ((int64_t)b * (a.gamma + 1) + i) * a.V;
     const int base = c * kBlockChunk;
     const uint64_t stream = stream_of(a, b);
     const uint64_t tag = kTagGumbel + ((uint64_t)i << 32);
-    double best = -INFINITY;
-    int arg = 0x7fffffff;
     float lg[kBlockPer];
 #pragma unroll
     for (int k4 = 0; k4 < kBlockPer / 4; ++k4) {
@@ -1138,21 +1158,59 @@ __global__ __launch_bounds__(kRowThreads) void accept_gumbel_pass_kernel(AcceptA
             for (int j = 0; j < 4; ++j) lg[4 * k4 + j] = row[min(e + j, a.V - 1)];
         }
     }
+    // fp32 estimates: |error| < 1e-5 (1 + |l/T| + |g|) with |g| < 37, g the Gumbel term
+    const float itau = (float)(1.0 / a.tau);
+    float est[kBlockPer];
+    float m = -INFINITY;
 #pragma unroll
     for (int k4 = 0; k4 < kBlockPer / 4; ++k4) {
         const int e = base + 4 * (int)threadIdx.x + 1024 * k4;
-        if (e >= a.V) continue;
         uint64_t ctr[4] = {(uint64_t)e >> 2, a.step, stream, tag};
-        philox4x64_10(ctr, a.seed, 0);
+        if (e < a.V) philox4x64_10(ctr, a.seed, 0);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            if (e + j >= a.V) continue;
-            const double u = (double)(2 * (ctr[j] >> 12) + 1) * 0x1p-53;
-            const double sc = (double)lg[4 * k4 + j] / a.tau + (-log(-log(u)));
-            if (sc > best) {  // tokens are visited in increasing order: ties keep the first
-                best = sc;
-                arg = e + j;
-            }
+            est[4 * k4 + j] = e + j < a.V
+                                  ? lg[4 * k4 + j] * itau - __builtin_amdgcn_logf(neg_log_uniform_f32(ctr[j])) * kLn2f
+                                  : -INFINITY;
+            m = fmaxf(m, est[4 * k4 + j]);
+        }
+    }
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+    if (threadIdx.x % kWave == 0) s_m[threadIdx.x / kWave] = m;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kRowThreads / kWave; ++k) m = fmaxf(m, s_m[k]);
+    // candidates: estimates within 1e-2 + 1e-3 |best| of the best estimate (a margin
+    // hundreds of times the estimates' error).  When no estimate is above -inf, every
+    // finite logit is a candidate (l/T can overflow fp32 while fp64 holds it).
+    const float thr = m == INFINITY ? INFINITY : m - (1e-2f + 1e-3f * fabsf(m));
+    const bool none = m == -INFINITY;
+    unsigned cand = 0;
+#pragma unroll
+    for (int k4 = 0; k4 < kBlockPer / 4; ++k4) {
+        const int e = base + 4 * (int)threadIdx.x + 1024 * k4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bool in = none ? (e + j < a.V && lg[4 * k4 + j] > -INFINITY) : est[4 * k4 + j] >= thr;
+            cand |= (unsigned)in << (4 * k4 + j);
+        }
+    }
+    // exact fp64 scores of the candidates, in increasing token order (ties keep the first)
+    double best = -INFINITY;
+    int arg = 0x7fffffff;
+    while (cand) {
+        const int j = __builtin_ctz(cand);
+        cand &= cand - 1;
+        const int e = base + 4 * (int)threadIdx.x + 1024 * (j >> 2) + (j & 3);
+        uint64_t ctr[4] = {(uint64_t)e >> 2, a.step, stream, tag};
+        philox4x64_10(ctr, a.seed, 0);
+        const uint64_t wj = (j & 3) == 0 ? ctr[0] : (j & 3) == 1 ? ctr[1] : (j & 3) == 2 ? ctr[2] : ctr[3];
+        const double u = (double)(2 * (wj >> 12) + 1) * 0x1p-53;
+        const double sc = (double)row[e] / a.tau + (-log(-log(u)));
+        if (sc > best) {
+            best = sc;
+            arg = e;
         }
     }
     // block argmax (larger score, then lower token)

@@ -115,3 +115,48 @@ def test_gumbel_draws_follow_the_target_law_on_gpu():
     p = special.softmax(lg[0].astype(np.float64) / float(np.float32(0.7)))
     assert stats.chisquare(counts, p * N).pvalue > 1e-4
     assert np.all(got["accept_len"] == 0) and np.all(got["status"] == 2)
+
+
+@pytest.mark.parametrize("same_chunk", [True, False])
+def test_gumbel_near_ties_below_fp32_resolution(same_chunk):
+    """Two contenders per row whose fp64 Gumbel scores l/T + g differ by less than an fp32
+    ulp of the score (the second logit is the fp32 value nearest to a tie), far above the
+    oracle's 1e-12 tie window: the GPU's winner is the fp64 one, at both positions, with
+    the contenders in one 4096-token chunk or in two."""
+    from np_philox import block as np_block, word_to_uniform
+    B, V, seed, step = 128, 5000, 23, 4
+    tau = float(np.float32(0.9))
+    sid = np.arange(B, dtype=np.uint64) * 11 + 5
+    r = np.random.default_rng(9 + same_chunk)
+
+    def g(tok, b, pos):
+        w = np_block([tok >> 2, step, int(sid[b]), oracle.TAG_GUMBEL + (pos << 32)], [seed, 0])[tok & 3]
+        return -math.log(-math.log(word_to_uniform(w)))
+
+    tgt = np.full((B, 2, V), -40.0, np.float32)
+    toks = np.zeros((B, 1), np.int32)
+    win = np.zeros((B, 2), np.int64)
+    gaps = []
+    for b in range(B):
+        for pos in range(2):
+            ta = int(r.integers(0, 2000))
+            tb = int(r.integers(2100, 4000)) if same_chunk else int(r.integers(4096, V))
+            la = np.float32(r.uniform(5.0, 12.0))
+            lb = np.float32(float(la) + tau * (g(ta, b, pos) - g(tb, b, pos)))
+            tgt[b, pos, ta], tgt[b, pos, tb] = la, lb
+            gap = (float(la) / tau + g(ta, b, pos)) - (float(lb) / tau + g(tb, b, pos))
+            gaps.append(abs(gap))
+            win[b, pos] = ta if gap > 0 else tb
+            if pos == 0:
+                toks[b, 0] = ta if r.random() < 0.5 else tb
+    gaps = np.array(gaps)
+    assert gaps.max() < 2e-6 and gaps.min() > 1e-11, (gaps.min(), gaps.max())
+    got = to_host(sv.sv_spec_accept(SAMPLE, dev_array(tgt), None, dev_array(toks), tau, seed, step,
+                                    dev_array(sid.astype(np.int64)), rule=sv.SV_RULE_GUMBEL))
+    ref = oracle.gumbel_accept(tgt, toks, tau, seed=seed, step=step, stream_ids=sid)
+    _assert_parity(ref, got, "gumbel near ties same_chunk=%s" % same_chunk, excused_ok=0)
+    J = (toks[:, 0] == win[:, 0]).astype(np.int64)
+    assert np.array_equal(got["accept_len"], J)
+    assert np.array_equal(got["out_tokens"][np.arange(B), J], win[np.arange(B), J])
+    first = win[:, 0] == np.array([int(np.nonzero(tgt[b, 0] > -40)[0][0]) for b in range(B)])
+    assert 0.2 < first.mean() < 0.8, first.mean()     # both contenders win often
