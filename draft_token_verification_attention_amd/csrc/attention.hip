@@ -719,6 +719,7 @@ struct Plan {
     unsigned blocks;
     int max_blocks;  // resident-block budget of the looping combine (set at launch)
     bool spec;       // speculative first tile (set at launch)
+    int gsplit;      // split extent of the one-row-wave grid (odd when nsplit > 1)
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -810,6 +811,14 @@ static bool plan_attention(const sv_attn_desc *d, int cu_count, Plan &p)
     const int64_t nsplit = (Tmax + sk - 1) / sk;
     if (nsplit > kMaxSplits) return false;
     p.nsplit = (int)(nsplit < 1 ? 1 : nsplit);
+    // The one-row-wave grid is (split, KV head, sequence), split fastest, and the hardware
+    // deals workgroup i to XCD i mod 8.  An even split count lines the splits up with the
+    // XCDs (with 8 splits, XCD 0 gets every sequence's first split and XCD 7 only the
+    // longest sequences' last ones).  An odd grid width gives each XCD one KV head of every
+    // (sequence, split); the extra split index is empty and its blocks return at once.
+    // Measured on the 64-sequence batch (contexts 512..8192, 1024-key splits): 8 splits
+    // 284 us, 9 splits 197 us.
+    p.gsplit = (p.variant == 1 && p.nsplit % 2 == 0) ? p.nsplit + 1 : p.nsplit;
     const int64_t blocks = (int64_t)p.kg_pad * p.RT * p.nsplit;
     if (blocks > 0x7fffffff) return false;
     p.blocks = (unsigned)blocks;
@@ -882,9 +891,9 @@ static hipError_t launch_variant(const Plan &p, const AttnArgs &a, hipStream_t s
 {
     if constexpr (NWR == 1) {
         if (p.spec)
-            launch_main(attn_bf16_kernel<DH, 1, NWK, true>, dim3(p.nsplit, a.Hkv, a.B), dim3(64 * NWK), s, ev, a);
+            launch_main(attn_bf16_kernel<DH, 1, NWK, true>, dim3(p.gsplit, a.Hkv, a.B), dim3(64 * NWK), s, ev, a);
         else
-            launch_main(attn_bf16_kernel<DH, 1, NWK, false>, dim3(p.nsplit, a.Hkv, a.B), dim3(64 * NWK), s, ev, a);
+            launch_main(attn_bf16_kernel<DH, 1, NWK, false>, dim3(p.gsplit, a.Hkv, a.B), dim3(64 * NWK), s, ev, a);
     } else {
         launch_main(attn_bf16_kernel<DH, NWR, NWK, false>, dim3(p.blocks), dim3(64 * NWR * NWK), s, ev, a);
     }
@@ -1001,7 +1010,7 @@ extern "C" sv_status sv_verify_attention(const sv_attn_desc *d, void *workspace,
         // A grid of at most one block per CU is latency-bound: with a dense cache layout
         // (no kv_off) the first tiles are loaded while the sequence lengths are in flight.
         // Larger grids skip it (their empty splits would load tiles for nothing).
-        p.spec = p.variant == 1 && !d->kv_off && p.blocks <= (unsigned)cus;
+        p.spec = p.variant == 1 && !d->kv_off && (int64_t)p.gsplit * d->Hkv * d->B <= cus;
         const Events ev{(hipEvent_t)d->ev_kernel_start, (hipEvent_t)d->ev_kernel_stop, (hipEvent_t)d->ev_call_stop};
         e = d->D == 128 ? launch_bf16<128>(p, a, s, ev) : launch_bf16<64>(p, a, s, ev);
     }

@@ -212,6 +212,15 @@ def test_dense_layout_parity(dtype, shape):
     _compare(inp, 1 / math.sqrt(D), rows=rows, max_prefix=mp, dense=True)
 
 
+@pytest.mark.parametrize("split_keys", [128, 256])
+def test_dense_even_split_count(split_keys):
+    """8 or 4 key splits: the grid gets one more, empty, split index (an odd width spreads
+    the splits over the XCDs); its blocks issue their clamped first-tile loads and return."""
+    inp = synth.attention_inputs(24, B=2, n_q=5, Hq=32, Hkv=8, D=128, prefix_len=[100, 1000], dtype="bf16",
+                                 qkv_scale=1.0)
+    _compare(inp, 1 / math.sqrt(128), max_prefix=1000, split_keys=split_keys, dense=True)
+
+
 @pytest.mark.parametrize("split_keys", [0, 64])
 def test_dense_layout_tree(split_keys):
     n = 7
