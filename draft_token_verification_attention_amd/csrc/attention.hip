@@ -61,7 +61,8 @@ struct AttnArgs {
     float *lse;
     int B, n_q, Hq, Hkv, G, rows, RT, KG, nsplit, split_keys;
     float scale_log2;
-    float *part;  // [KG*RT][nsplit][32*NWR][D + 4]: o[D], max, sum, pad (16-byte rows)
+    float *part;  // [KG*RT][nsplit][32*NWR][D]: unnormalized o of each split
+    float2 *pml;  // [KG*RT][nsplit][32*NWR]: (max in log2 units, sum) of each split
 };
 
 // 16-byte K/V load.  NT: with the nontemporal hint, for tiles that no other block re-reads
@@ -188,8 +189,7 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
                                (int64_t)(kvh * a.G + (row_ok ? my_row % a.G : 0)) * a.q_sh;
 #pragma unroll
         for (int c = 0; c < NKC; ++c) {
-            uint4 u = make_uint4(0, 0, 0, 0);
-            if (row_ok) u = *reinterpret_cast<const uint4 *>(qrow + 16 * c + 8 * h);
+            const uint4 u = *reinterpret_cast<const uint4 *>(qrow + 16 * c + 8 * h);
             qf[c] = as_bf16x8(u);
         }
     }
@@ -324,11 +324,45 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
     // One row wave: each wave streams its own tiles through its own LDS buffers, so the
     // loop needs no block barrier (a wave's LDS accesses complete in issue order).
     // Several row waves share a tile: barriers around the LDS writes.
-    // Wait for Q here, before the first tile's loads are issued (it was issued first and has
-    // mostly landed by now).  Left to the compiler, the wait for Q merges into the first MFMA
-    // of every tile as a wait for all outstanding loads, which defeats the prefetch.
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(SPEC ? 2 * NI : 0));
-    if (!SPEC && niter > 0) issue_loads(0);
+    // Q must have landed before the first MFMA.  Left to the compiler, that wait merges into
+    // the first MFMA of every tile as a wait for all outstanding loads, which defeats the
+    // prefetch; so the wait is explicit, here.  One row wave: the first tile's loads go out
+    // first, and the wait covers Q alone (issued before them), leaving the tile in flight
+    // (1-2% on the 64-sequence batch).  Every wave issues that tile without a branch (a
+    // branch there makes the compiler copy registers that are still loading): a wave past
+    // the split's last tile re-reads that tile, a block with no tile reads its own first Q
+    // row.  Q itself is loaded by every lane (padding rows read the block's first row; their
+    // results are never stored), again without a branch.
+    if constexpr (kDecode && !SPEC) {
+        const bool any = count > 0;
+        const int t0 = kstart + (any ? min(wk, count - 1) : 0) * kTileKeys;
+        const char *qsafe = reinterpret_cast<const char *>((const uint16_t *)a.q + (int64_t)b * a.q_sb +
+                                                           (int64_t)(kvh * a.G) * a.q_sh);
+        const char *kb = any ? reinterpret_cast<const char *>(kbase + (int64_t)t0 * a.kv_st) : qsafe;
+        const char *vb = any ? reinterpret_cast<const char *>(vbase + (int64_t)t0 * a.kv_st) : qsafe;
+        const int lim = T - 1 - t0;
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const uint32_t o = !any ? 0u
+                               : (t0 + kTileKeys <= T)
+                                   ? voff[j]
+                                   : 2u * ((uint32_t)min(ld_key0 + j * KPI, lim) * (uint32_t)a.kv_st + 8u * ld_dc);
+            kreg[j] = load_kv16<true>(kb + o);
+            vreg[j] = load_kv16<true>(vb + o);
+        }
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NI));
+    } else {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(SPEC ? 2 * NI : 0));
+        if (!SPEC && niter > 0) issue_loads(0);
+    }
+    // Q is complete here: hand it on as a fresh value, so that no wait for it (which would
+    // also wait for the tile in flight) lands in the loop
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) {
+        u32x4 t = __builtin_bit_cast(u32x4, qf[c]);
+        asm volatile("" : "+v"(t));
+        qf[c] = __builtin_bit_cast(bf16x8, t);
+    }
     const int my_iters = kDecode ? (count - wk + NWK - 1) / NWK : niter;
     // rows of the speculative first tile at or past the end of the sequence (zeroed)
     const int spec_lim = T - (kstart + wk * kTileKeys);
@@ -530,16 +564,23 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
     }
 
     // several splits: store this split's partial -- unnormalized o, max (log2 units), sum --
-    // for the combine kernel, which runs after this kernel completes
+    // for the combine kernel, which runs after this kernel completes.  o rows are D floats
+    // (whole 128-byte lines, each written by one wave's consecutive stores); the (max, sum)
+    // pairs sit in an array of their own.  These writes reach HBM while other blocks are
+    // still streaming K/V, and there they cost far more than their size: on the 64-sequence
+    // batch the partials are 2% of the bytes and 15% of the time (a plain streaming read
+    // with the same writes added slows from 6.7 to 5.6 TB/s; writes that stay in L2 cost
+    // nothing).
     const int gidx = kg * a.RT + rt;
-    float *pr = a.part + (((int64_t)gidx * a.nsplit + s) * ROWS_BLK + wr * 32 + l32) * (DH + 4);
+    const int64_t prow = ((int64_t)gidx * a.nsplit + s) * ROWS_BLK + wr * 32 + l32;
+    float *pr = a.part + prow * DH;
 #pragma unroll
     for (int j = 0; j < ne; j += 4) {
         const int e = e0 + j;
         const int d = 32 * (e / 16) + 8 * ((e % 16) / 4) + 4 * h;
         *reinterpret_cast<float4 *>(pr + d) = make_float4(elem(j), elem(j + 1), elem(j + 2), elem(j + 3));
     }
-    if (h == 0 && wk == 0) *reinterpret_cast<float2 *>(pr + DH) = make_float2(row_m, l_row);
+    if (h == 0 && wk == 0) a.pml[prow] = make_float2(row_m, l_row);
 }
 
 // ---------------------------------------------------------------------------
@@ -579,18 +620,19 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a, 
         const int row = rt * ROWS_BLK + r;
         const bool ok = r < ROWS_BLK && row < a.rows;
         const int rr = ok ? r : 0;                // in-bounds row for the (unused) loads of idle rows
-        const float *pg = a.part + (int64_t)gidx * a.nsplit * ROWS_BLK * (DH + 4);
-        auto row_at = [&](int u) { return pg + ((int64_t)u * ROWS_BLK + rr) * (DH + 4); };  // o[DH], max, sum
+        const int64_t pg = (int64_t)gidx * a.nsplit * ROWS_BLK;
+        auto row_of = [&](int u) { return pg + (int64_t)u * ROWS_BLK + rr; };  // partial row of split u
         const int nmine = ns > sl ? (ns - sl + NSL - 1) / NSL : 0;  // splits this lane owns
 
         float4 o[SPT][kCombVec];
         float2 ml[SPT];
 #pragma unroll
         for (int k = 0; k < SPT; ++k) {
-            const float *rp = row_at(min(sl + k * NSL, ns - 1));
+            const int64_t pr = row_of(min(sl + k * NSL, ns - 1));
+            const float *rp = a.part + pr * DH;
 #pragma unroll
             for (int v = 0; v < kCombVec; ++v) o[k][v] = *reinterpret_cast<const float4 *>(rp + 4 * (cl + L4 * v));
-            ml[k] = *reinterpret_cast<const float2 *>(rp + DH);
+            ml[k] = a.pml[pr];
         }
         float mloc = -INFINITY;
 #pragma unroll
@@ -715,7 +757,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a, int D)
 struct Plan {
     int variant;  // 0: fp32, 1: (NWR=1, NWK=4), 2: (NWR=2, NWK=2), 3: (NWR=4, NWK=1)
     int NWR, NWK, rows, RT, KG, nsplit, split_keys, kg_pad;
-    size_t part_bytes, cnt_bytes, total;
+    size_t part_bytes, o_bytes, cnt_bytes, total;  // part_bytes = o partials + (max, sum) pairs
     unsigned blocks;
     int max_blocks;  // resident-block budget of the looping combine (set at launch)
     bool spec;       // speculative first tile (set at launch)
@@ -782,7 +824,7 @@ static bool plan_attention(const sv_attn_desc *d, int cu_count, Plan &p)
         if ((groups >= 64 && Tmax > 2048) || (groups >= 32 && Tmax >= 4096)) sk = sk < 1024 ? 1024 : sk;
         if (groups >= 64 && Tmax <= 2048) sk = (Tmax + unit - 1) / unit * unit;
     } else {
-        // Many rows per block: a partial (32 NWR rows x (D + 4) fp32, written and read back)
+        // Many rows per block: a partial (32 NWR rows x D fp32 and a (max, sum) pair per row, written and read back)
         // costs about as much as the K/V of 130 keys, so a short cache splits only until
         // every CU has a block, and never below 256 keys (measured on the 64-node Medusa
         // tree, 2048-key cache: 128-key splits 54 us per round, 256-key 45 us, 512-key 47 us).
@@ -828,7 +870,9 @@ static bool plan_attention(const sv_attn_desc *d, int cu_count, Plan &p)
     // the counter area every call's workspace starts with (unused here)
     p.cnt_bytes = kCounterBytes;
     // (with one split the kernel stores its output directly; the partial area stays unused)
-    p.part_bytes = align256((size_t)p.KG * p.RT * p.nsplit * rows_blk * (D + 4) * sizeof(float));
+    const size_t prows = (size_t)p.KG * p.RT * p.nsplit * rows_blk;
+    p.o_bytes = align256(prows * D * sizeof(float));
+    p.part_bytes = p.o_bytes + align256(prows * 2 * sizeof(float));
     p.total = p.cnt_bytes + p.part_bytes;
     return true;
 }
@@ -996,6 +1040,7 @@ extern "C" sv_status sv_verify_attention(const sv_attn_desc *d, void *workspace,
     a.split_keys = p.split_keys;
     a.scale_log2 = d->scale * kLog2e;
     a.part = p.part_bytes ? (float *)((char *)workspace + p.cnt_bytes) : nullptr;
+    a.pml = p.part_bytes ? (float2 *)((char *)workspace + p.cnt_bytes + p.o_bytes) : nullptr;
 
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
