@@ -61,7 +61,7 @@ struct AttnArgs {
     float *lse;
     int B, n_q, Hq, Hkv, G, rows, RT, KG, nsplit, split_keys;
     float scale_log2;
-    float *part;  // [KG*RT][nsplit][32*NWR][D]: unnormalized o of each split
+    float *part;  // [KG*RT][nsplit][32*NWR][D] bf16: o / sum of each split
     float2 *pml;  // [KG*RT][nsplit][32*NWR]: (max in log2 units, sum) of each split
 };
 
@@ -563,22 +563,27 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
         return;
     }
 
-    // several splits: store this split's partial -- unnormalized o, max (log2 units), sum --
-    // for the combine kernel, which runs after this kernel completes.  o rows are D floats
-    // (whole 128-byte lines, each written by one wave's consecutive stores); the (max, sum)
-    // pairs sit in an array of their own.  These writes reach HBM while other blocks are
-    // still streaming K/V, and there they cost far more than their size: on the 64-sequence
-    // batch the partials are 2% of the bytes and 15% of the time (a plain streaming read
-    // with the same writes added slows from 6.7 to 5.6 TB/s; writes that stay in L2 cost
-    // nothing).
+    // several splits: store this split's partial -- o / sum in bf16, (max in log2 units, sum)
+    // in fp32 -- for the combine kernel, which runs after this kernel completes.  These
+    // writes reach HBM while other blocks are still streaming K/V, and there they cost far
+    // more than their size (a plain streaming read with fp32 partials' worth of writes added
+    // slows from 6.7 to 5.6 TB/s; writes that stay in L2 cost nothing), so the partial o is
+    // stored normalized and in bf16: half the bytes, 197.6 -> 186.6 us on the 64-sequence
+    // batch.  o / sum is a convex combination of V rows, so its rounding error is at most
+    // 2^-9 of the largest |V| element it averages, and the combined output (again a convex
+    // combination) carries at most that on top of its own bf16 rounding.
     const int gidx = kg * a.RT + rt;
     const int64_t prow = ((int64_t)gidx * a.nsplit + s) * ROWS_BLK + wr * 32 + l32;
-    float *pr = a.part + prow * DH;
+    uint16_t *pr = reinterpret_cast<uint16_t *>(a.part) + prow * DH;
+    const float pinv = l_row > 0.0f ? 1.0f / l_row : 0.0f;
 #pragma unroll
     for (int j = 0; j < ne; j += 4) {
         const int e = e0 + j;
         const int d = 32 * (e / 16) + 8 * ((e % 16) / 4) + 4 * h;
-        *reinterpret_cast<float4 *>(pr + d) = make_float4(elem(j), elem(j + 1), elem(j + 2), elem(j + 3));
+        uint2 pk;
+        pk.x = (uint32_t)f32_to_bf16(elem(j) * pinv) | ((uint32_t)f32_to_bf16(elem(j + 1) * pinv) << 16);
+        pk.y = (uint32_t)f32_to_bf16(elem(j + 2) * pinv) | ((uint32_t)f32_to_bf16(elem(j + 3) * pinv) << 16);
+        *reinterpret_cast<uint2 *>(pr + d) = pk;
     }
     if (h == 0 && wk == 0) a.pml[prow] = make_float2(row_m, l_row);
 }
@@ -629,9 +634,13 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a, 
 #pragma unroll
         for (int k = 0; k < SPT; ++k) {
             const int64_t pr = row_of(min(sl + k * NSL, ns - 1));
-            const float *rp = a.part + pr * DH;
+            const uint16_t *rp = reinterpret_cast<const uint16_t *>(a.part) + pr * DH;
 #pragma unroll
-            for (int v = 0; v < kCombVec; ++v) o[k][v] = *reinterpret_cast<const float4 *>(rp + 4 * (cl + L4 * v));
+            for (int v = 0; v < kCombVec; ++v) {
+                const uint2 u = *reinterpret_cast<const uint2 *>(rp + 4 * (cl + L4 * v));
+                o[k][v] = make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                                      __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+            }
             ml[k] = a.pml[pr];
         }
         float mloc = -INFINITY;
@@ -649,7 +658,7 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a, 
         float lsum = 0.0f;
 #pragma unroll
         for (int k = 0; k < SPT; ++k) {
-            const float w = (k < nmine && ml[k].x != -INFINITY) ? exp2_fast(ml[k].x - M) : 0.0f;
+            const float w = (k < nmine && ml[k].x != -INFINITY) ? ml[k].y * exp2_fast(ml[k].x - M) : 0.0f;
 #pragma unroll
             for (int v = 0; v < kCombVec; ++v) {
                 acc[v].x += o[k][v].x * w;
@@ -657,7 +666,7 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs a, 
                 acc[v].z += o[k][v].z * w;
                 acc[v].w += o[k][v].w * w;
             }
-            lsum += ml[k].y * w;
+            lsum += w;
         }
         if (NSL > 1) {
 #pragma unroll
@@ -824,8 +833,8 @@ static bool plan_attention(const sv_attn_desc *d, int cu_count, Plan &p)
         if ((groups >= 64 && Tmax > 2048) || (groups >= 32 && Tmax >= 4096)) sk = sk < 1024 ? 1024 : sk;
         if (groups >= 64 && Tmax <= 2048) sk = (Tmax + unit - 1) / unit * unit;
     } else {
-        // Many rows per block: a partial (32 NWR rows x D fp32 and a (max, sum) pair per row, written and read back)
-        // costs about as much as the K/V of 130 keys, so a short cache splits only until
+        // Many rows per block: a partial (32 NWR rows x D, and a (max, sum) pair per row, written and read back)
+        // cost about as much as the K/V of 130 keys in fp32, so a short cache splits only until
         // every CU has a block, and never below 256 keys (measured on the 64-node Medusa
         // tree, 2048-key cache: 128-key splits 54 us per round, 256-key 45 us, 512-key 47 us).
         // Long caches split further, to about four blocks per CU with splits of at least
@@ -871,7 +880,7 @@ static bool plan_attention(const sv_attn_desc *d, int cu_count, Plan &p)
     p.cnt_bytes = kCounterBytes;
     // (with one split the kernel stores its output directly; the partial area stays unused)
     const size_t prows = (size_t)p.KG * p.RT * p.nsplit * rows_blk;
-    p.o_bytes = align256(prows * D * sizeof(float));
+    p.o_bytes = align256(prows * D * sizeof(uint16_t));
     p.part_bytes = p.o_bytes + align256(prows * 2 * sizeof(float));
     p.total = p.cnt_bytes + p.part_bytes;
     return true;
