@@ -292,6 +292,18 @@ def test_batch_split_edges():
     assert np.array_equal(np.nan_to_num(al, nan=7.0), np.nan_to_num(fl, nan=7.0))
 
 
+@pytest.mark.parametrize("split_keys", [64, 128, 256])
+def test_batch_many_splits_combine(split_keys):
+    """A batch whose combine grid is large: four split lanes per row, each merging 2, 4 or 8
+    splits (32, 16 and 8 splits of up to 2000 + 5 keys)."""
+    n_q, Hq, Hkv, D = 5, 32, 8, 128
+    P = list(np.random.default_rng(5).integers(0, 2001, 40))
+    inp = synth.attention_inputs(25, B=len(P), n_q=n_q, Hq=Hq, Hkv=Hkv, D=D, prefix_len=P, dtype="bf16",
+                                 qkv_scale=1.0)
+    rows = rows_of_sample(inp, 600)
+    _compare(inp, 1 / math.sqrt(D), rows=rows, max_prefix=2000, split_keys=split_keys)
+
+
 def test_deterministic_repeats():
     inp = synth.attention_inputs(8, B=1, n_q=6, Hq=32, Hkv=8, D=128, prefix_len=[4096], dtype="bf16")
     first, fl = attention_on_gpu(inp, 0.088)
