@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of replaying HIP graphs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy 5 times (reference for the HBM byte counters)")
+    ap.add_argument("--latency-floor", action="store_true",
+                    help="only time plain device operations of the 8B chain's attention size (16.9 MB): a copy, "
+                         "a one-pass reduction, and a 4-byte copy (the launch floor)")
     return ap.parse_args()
 
 
@@ -72,6 +75,37 @@ def copy_calibration():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes": 4 * n, "launches": 5}))
+
+
+def latency_floor(reps=200):
+    """What one sequence's attention is measured against: plain device operations over the
+    8B chain's attention bytes (16,900,096: Q, K/V of 4102 keys x 8 KV heads x 128, O), each
+    launched back to back `reps` times, median of HIP event intervals (the kernel trace of the
+    same run gives the kernels' own spans)."""
+    import torch
+    n = 16900096 // 2
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    tiny_s = torch.ones(2, dtype=torch.bfloat16, device="cuda")
+    tiny_d = torch.empty_like(tiny_s)
+    out = torch.empty((), dtype=torch.float32, device="cuda")
+    ops = {"copy_16.9MB": lambda: dst.copy_(src),
+           "sum_16.9MB": lambda: torch.sum(src, dim=0, dtype=torch.float32, out=out),
+           "copy_4B": lambda: tiny_d.copy_(tiny_s)}
+    res = {}
+    for name, op in ops.items():
+        for _ in range(20):
+            op()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        torch.cuda.synchronize()
+        for e0, e1 in evs:
+            e0.record()
+            op()
+            e1.record()
+        torch.cuda.synchronize()
+        t = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+        res[name + "_us"] = round(1e3 * t[len(t) // 2], 2)
+    print(json.dumps({"latency_floor": res, "bytes": 16900096, "reps": reps}))
 
 
 def host_threads() -> int:
@@ -98,6 +132,9 @@ def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.latency_floor:
+        latency_floor()
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: the library runs on one device per process and has no "
