@@ -635,8 +635,9 @@ def bench_tree(args, cfg, wl, dev, steps, warmup, cpu):
 # bytes of a plain copy of known size on this GPU) from the rocprofv3 --pmc runs summarized
 # under profiles/, with the SHA-256 of the attention source they were taken on: a changed
 # kernel reports null until the counters are taken again.  "attention" = main + combine.
-TRAFFIC = {4: {"main": 1103942803, "attention": 1114156418}, 2: {"main": 18302160, "attention": 19533072}}
-TRAFFIC_SRC_SHA256 = "8e920b5137f36c73782e6dc3e2faa3f7529e3c9e7f921525afde512304df4bc6"
+TRAFFIC = {4: {"main": 1103942215, "attention": 1114320685}, 2: {"main": 18289044, "attention": 19519958},
+           3: {"main": 13266282, "attention": 17991613}, 5: {"main": 779117719, "attention": 779117719}}
+TRAFFIC_SRC_SHA256 = "b781ff54a5bedc1838dda041d566183f866cf24a951f570b44b6966150dc731d"
 
 
 def measured_traffic(wl):
