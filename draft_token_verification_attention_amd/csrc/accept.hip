@@ -493,8 +493,11 @@ __global__ __launch_bounds__(kRowThreads, 2) void accept_resample_kernel(AcceptA
     const double Mp = sM[J], Mq = J < g ? sM[g + 1 + J] : Mp;
     const double iZp_est = 1.0 / sZ[J], iZq_est = J < g ? 1.0 / sZ[g + 1 + J] : 0.0;
     const double qmask = J < g ? 1.0 : 0.0;
-    auto wp_of = [&](float l) { return exp2_acc(((double)l - Mp) * a.kd); };
-    auto wq_of = [&](float l) { return exp2_acc(((double)l - Mq) * a.kd) * qmask; };
+    // (l - M) kd as one multiply-add on the precomputed -M kd: 1e-16 |M kd| more error in
+    // the exponent, ~1e-14 of a weight at logits of 100, one instruction less per weight
+    const double nMpk = -Mp * a.kd, nMqk = -Mq * a.kd;
+    auto wp_of = [&](float l) { return exp2_acc(fma((double)l, a.kd, nMpk)); };
+    auto wq_of = [&](float l) { return exp2_acc(fma((double)l, a.kd, nMqk)) * qmask; };
 
     float xp[kPerThread], xq[kPerThread];
     load_chunk2<VEC, kPerThread>(prow, qrow ? qrow : prow, base, a.V, xp, xq);
@@ -791,6 +794,7 @@ __global__ __launch_bounds__(kRowThreads, 2) void accept_block_pass_kernel(Accep
     const float *prow = a.target + ((int64_t)b * (g + 1) + kc) * a.V;
     const float *qrow = kc < g ? a.draft + ((int64_t)b * g + kc) * a.V : prow;
     const double Mp = sM[kc], Mq = kc < g ? sM[g + 1 + kc] : Mp;
+    const double nMpk = -Mp * a.kd, nMqk = -Mq * a.kd;  // exponents as one multiply-add each
     const double iZp_est = 1.0 / sZ[kc], iZq_est = kc < g ? 1.0 / sZ[g + 1 + kc] : 0.0;
     const double qmask = kc < g ? 1.0 : 0.0;
     float xp[PER], xq[PER];
@@ -803,8 +807,8 @@ __global__ __launch_bounds__(kRowThreads, 2) void accept_block_pass_kernel(Accep
         b4[k4] = 0.0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const double wp = exp2_acc(((double)xp[4 * k4 + j] - Mp) * a.kd);
-            const double wq = exp2_acc(((double)xq[4 * k4 + j] - Mq) * a.kd) * qmask;
+            const double wp = exp2_acc(fma((double)xp[4 * k4 + j], a.kd, nMpk));
+            const double wq = exp2_acc(fma((double)xq[4 * k4 + j], a.kd, nMqk)) * qmask;
             tp += wp;
             tq += wq;
             const bool in = wk * wp * iZp_est > wq * iZq_est;
