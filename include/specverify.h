@@ -133,7 +133,10 @@ SV_API sv_status sv_build_tree_mask(const int32_t *parents, int32_t n, int32_t p
 /*        n_q nodes; sequence b uses tree_bits + b*tree_sb (tree_sb = 0: one shared tree).*/
 /*   out  [B][n_q][Hq][D] of `dtype` at out + b*o_sb + i*o_st + h*o_sh                   */
 /*   lse  optional fp32 [B][n_q][Hq] contiguous, or NULL                                 */
-/* dtype: SV_BF16 (bf16 in and out, fp32 accumulation, MFMA) or SV_F32 (fp32 throughout).*/
+/* dtype: SV_BF16 (bf16 in and out, fp32 accumulation, MFMA; key splits hand their       */
+/*        partial outputs to the merge as o / sum rounded to bf16 -- a convex combination  */
+/*        of V rows, so at most one more bf16 rounding of the output) or SV_F32 (fp32     */
+/*        throughout).                                                                   */
 /* scale > 0 (else SV_ERR_INVALID_ARG).                                                  */
 /* split_keys: keys per work split (a tuning knob, rounded up to the kernel's tile        */
 /*        granularity); 0 picks a split that fills the GPU.                              */
