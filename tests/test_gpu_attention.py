@@ -183,6 +183,42 @@ def test_tree_default_plans(n, P):
     _compare(inp, 1 / math.sqrt(128), tree_bits=bits, rows=rows)
 
 
+MANY_ROW_CASES = [
+    # name, seed, B, n_q, prefix lengths, Hq, Hkv, D, tree, split_keys, dense (max_prefix), q_scale
+    ("tree-P7001-splits", 31, 1, 300, [7001], 32, 8, 128, True, 0, None, 1.0),
+    ("tree-P7001-nosplit-sharp", 32, 1, 300, [7001], 32, 8, 128, True, 32768, None, 3.0),
+    ("chain-nq48-B2", 33, 2, 48, [6500, 7003], 64, 8, 128, False, 0, None, 1.0),
+    ("tree-D64", 34, 1, 150, [6300], 16, 2, 64, True, 0, None, 1.0),
+    ("tree-dense-B2-sharp", 35, 2, 100, [6200, 6900], 64, 8, 128, True, 2048, 6950, 3.0),
+]
+
+
+def _tile_rows(inp, b, kvh, rt):
+    """The (sequence, token, query head) triples of one 128-row tile of KV head kvh (rows are
+    packed as token * G + g over the query heads of that KV head)."""
+    G = inp["Hq"] // inp["Hkv"]
+    r = np.arange(128 * rt, min(128 * (rt + 1), inp["n_q"] * G))
+    return np.stack([np.full(r.size, b), r // G, kvh * G + r % G], 1)
+
+
+@pytest.mark.parametrize("case", MANY_ROW_CASES, ids=lambda c: c[0])
+def test_many_row_blocks(case):
+    """128-row blocks on long caches (the software-pipelined kernel): tile masks from tree
+    bits or the causal rule, a prefix that ends inside a tile, key splits and none, D = 64,
+    the dense layout, and a sharp softmax that moves the running max."""
+    name, seed, B, n, P, Hq, Hkv, D, tree, sk, mp, qs = case
+    bits = None
+    if tree:
+        parents = synth.random_tree(seed, n, branch_p=0.6)
+        parents[n // 3] = -1                      # a forest
+        bits, _, _ = oracle.tree_mask(parents, P[0])
+    inp = synth.attention_inputs(seed, B=B, n_q=n, Hq=Hq, Hkv=Hkv, D=D, prefix_len=P, dtype="bf16",
+                                 qkv_scale=1.0, q_scale=qs)
+    rows = np.concatenate([rows_of_sample(inp, 300), _tile_rows(inp, B - 1, Hkv - 1, 1),
+                           _tile_rows(inp, 0, 0, (n * Hq // Hkv - 1) // 128)])
+    _compare(inp, 1 / math.sqrt(D), tree_bits=bits, rows=rows, split_keys=sk, max_prefix=mp, dense=mp is not None)
+
+
 @pytest.mark.parametrize("B,P", [(16, 1000), (8, 3000), (4, 5000)], ids=["no-split", "1024-split-B8", "1024-split-B4"])
 def test_chain_batch_default_plans(B, P):
     """Default plans of the one-row-wave form for batches: one split per sequence on a short
