@@ -48,7 +48,7 @@ class sv_accept_desc(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int), ("B", _i32), ("gamma", _i32), ("V", _i32), ("temperature", _f32),
                 ("target_logits", _P), ("draft_logits", _P), ("draft_tokens", _P), ("rng", sv_philox),
                 ("accept_len", _P), ("out_tokens", _P), ("alpha", _P), ("dev_status", _P),
-                ("rule", ctypes.c_int)]
+                ("rule", ctypes.c_int), ("draft_len", _P)]
 
 
 class sv_walk_desc(ctypes.Structure):
@@ -205,7 +205,8 @@ def sv_verify_attention(q, k, v, kv_off, prefix_len, *, Hkv: int, max_prefix: in
 
 
 def accept_desc(mode, target, draft, draft_tokens, temperature, seed, step, stream_ids,
-                accept_len, out_tokens, alpha, dev_status, rule: int = SV_RULE_TOKEN) -> sv_accept_desc:
+                accept_len, out_tokens, alpha, dev_status, rule: int = SV_RULE_TOKEN,
+                draft_len=None) -> sv_accept_desc:
     B, g1, V = target.shape
     d = sv_accept_desc()
     d.mode, d.B, d.gamma, d.V, d.temperature = int(mode), B, g1 - 1, V, float(temperature)
@@ -217,14 +218,16 @@ def accept_desc(mode, target, draft, draft_tokens, temperature, seed, step, stre
     d.alpha = None if alpha is None else alpha.data_ptr()
     d.dev_status = None if dev_status is None else dev_status.data_ptr()
     d.rule = int(rule)
+    d.draft_len = None if draft_len is None else draft_len.data_ptr()
     return d
 
 
 def sv_spec_accept(mode: int, target, draft, draft_tokens, temperature: float, seed: int, step: int = 0,
-                   stream_ids=None, want_alpha: bool = False, rule: int = SV_RULE_TOKEN):
-    """target fp32 [B][gamma+1][V]; draft fp32 [B][gamma][V] (SAMPLE); draft_tokens int32 [B][gamma].
+                   stream_ids=None, want_alpha: bool = False, rule: int = SV_RULE_TOKEN, draft_len=None):
+    """target fp32 [B][gamma+1][V]; draft fp32 [B][gamma][V] (SAMPLE); draft_tokens int32 [B][gamma];
+    draft_len optional int32 [B] (drafts each sequence verifies, 0..gamma).
     Returns dict(accept_len, out_tokens, alpha or None, status) as device tensors."""
-    _need_cuda(target, draft, draft_tokens, stream_ids)
+    _need_cuda(target, draft, draft_tokens, stream_ids, draft_len)
     target = target.contiguous()
     draft = None if draft is None else draft.contiguous()
     draft_tokens = draft_tokens.to(torch.int32).contiguous()
@@ -235,7 +238,9 @@ def sv_spec_accept(mode: int, target, draft, draft_tokens, temperature: float, s
     alpha = torch.empty((B, g1 - 1), dtype=torch.float32, device=dev) if want_alpha else None
     status = torch.empty(B, dtype=torch.int32, device=dev)
     sid = None if stream_ids is None else stream_ids.to(torch.int64).contiguous()
-    d = accept_desc(mode, target, draft, draft_tokens, temperature, seed, step, sid, acc, out, alpha, status, rule)
+    dl = None if draft_len is None else draft_len.to(torch.int32).contiguous()
+    d = accept_desc(mode, target, draft, draft_tokens, temperature, seed, step, sid, acc, out, alpha, status, rule,
+                    dl)
     nb = lib.sv_spec_accept_workspace(ctypes.byref(d))
     ws = workspace(nb, dev)
     _check(lib.sv_spec_accept(ctypes.byref(d), _ptr(ws), nb, _stream(dev)), "sv_spec_accept")
@@ -243,7 +248,7 @@ def sv_spec_accept(mode: int, target, draft, draft_tokens, temperature: float, s
 
 
 def sv_spec_accept_static(mode: int, target, draft, draft_tokens, temperature: float, seed: int, step: int = 0,
-                          stream_ids=None, want_alpha: bool = False, out=None):
+                          stream_ids=None, want_alpha: bool = False, out=None, draft_len=None):
     """sv_spec_accept on the library's fixed device scratch (no workspace argument).  The
     output tensors can be passed in (``out`` = a dict like the one returned) so that the
     call itself allocates nothing.  Returns that dict."""
@@ -256,7 +261,7 @@ def sv_spec_accept_static(mode: int, target, draft, draft_tokens, temperature: f
                    alpha=torch.empty((B, g1 - 1), dtype=torch.float32, device=dev) if want_alpha else None,
                    status=torch.empty(B, dtype=torch.int32, device=dev))
     d = accept_desc(mode, target, draft, draft_tokens, temperature, seed, step, stream_ids, out["accept_len"],
-                    out["out_tokens"], out.get("alpha"), out["status"])
+                    out["out_tokens"], out.get("alpha"), out["status"], draft_len=draft_len)
     _check(lib.sv_spec_accept_static(ctypes.byref(d), _stream(dev)), "sv_spec_accept_static")
     return out
 

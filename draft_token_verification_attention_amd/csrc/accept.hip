@@ -102,6 +102,7 @@ struct AcceptArgs {
     const uint64_t *stream_ids;
     int32_t *accept_len, *out_tokens, *dev_status;
     float *alpha;
+    const int32_t *draft_len;  // or NULL: every sequence verifies gamma drafts
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -155,6 +156,22 @@ __device__ __forceinline__ const float *row_ptr(const AcceptArgs &a, int b, int 
 __device__ __forceinline__ uint64_t stream_of(const AcceptArgs &a, int b)
 {
     return a.stream_ids ? a.stream_ids[b] : (uint64_t)b;
+}
+
+// The drafts sequence b verifies (its own gamma): draft_len[b], taken into [0, gamma] (a
+// length outside it is reported by the decide step), or gamma without per-sequence lengths.
+// Sequence b then gets exactly the round the rule gives with gamma = its length, on its
+// first rows; rows past them are neither read nor needed.
+__device__ __forceinline__ int gamma_of(const AcceptArgs &a, int b)
+{
+    return a.draft_len ? min(max(a.draft_len[b], 0), a.gamma) : a.gamma;
+}
+// dev_status of sequence b: 3 for a length outside [0, gamma], else 2 for a verified draft
+// token outside [0, V), else 0
+__device__ __forceinline__ int32_t status_of(const AcceptArgs &a, int b, bool bad_token)
+{
+    if (a.draft_len && (a.draft_len[b] < 0 || a.draft_len[b] > a.gamma)) return 3;
+    return bad_token ? 2 : 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -261,6 +278,11 @@ __global__ __launch_bounds__(kRowThreads) void accept_stats_kernel(AcceptArgs a,
                     philox_uniform(a.seed, threadIdx.x, a.step, stream_of(a, b), kTagAccept);
             continue;
         }
+        // rows past the sequence's own length are not needed (target row gb is its last)
+        if (a.draft_len) {
+            const int gb = gamma_of(a, b);
+            if (r <= g ? r > gb : r - g - 1 >= gb) continue;
+        }
         const float *row = row_ptr(a, b, r);
         const int base = c * kChunk;
         float xv[kPerThread];
@@ -318,9 +340,10 @@ __global__ __launch_bounds__(kRowThreads) void accept_greedy_kernel(AcceptArgs a
     __shared__ int firstbad, bad;
     const int b = blockIdx.x;
     const int g = a.gamma;
+    const int gb = gamma_of(a, b);
     const int x = threadIdx.x < g ? a.tokens[(int64_t)b * g + threadIdx.x] : 0;
     if (threadIdx.x == 0) {
-        firstbad = g;
+        firstbad = gb;
         bad = 0;
     }
     const RowPart *pp = w.part + (int64_t)b * a.rows * a.npart;
@@ -328,7 +351,7 @@ __global__ __launch_bounds__(kRowThreads) void accept_greedy_kernel(AcceptArgs a
     const bool staged = a.rows * a.npart <= kMaxStaged;
     if (staged) stage_parts(pp, a.rows * a.npart, stage, [] {});
     const int wave = threadIdx.x / kWave;
-    for (int r = wave; r <= g; r += kRowThreads / kWave) {
+    for (int r = wave; r <= gb; r += kRowThreads / kWave) {
         float v;
         int idx;
         if (staged)
@@ -338,7 +361,7 @@ __global__ __launch_bounds__(kRowThreads) void accept_greedy_kernel(AcceptArgs a
         if (threadIdx.x % kWave == 0) z[r] = idx;
     }
     __syncthreads();
-    if (threadIdx.x < g) {
+    if ((int)threadIdx.x < gb) {
         if (x != z[threadIdx.x]) atomicMin(&firstbad, (int)threadIdx.x);
         if (x < 0 || x >= a.V) bad = 1;
     }
@@ -350,7 +373,7 @@ __global__ __launch_bounds__(kRowThreads) void accept_greedy_kernel(AcceptArgs a
         for (int i = threadIdx.x; i < g; i += blockDim.x) a.alpha[(int64_t)b * g + i] = __int_as_float(0x7fc00000);
     if (threadIdx.x == 0) {
         a.accept_len[b] = J;
-        if (a.dev_status) a.dev_status[b] = bad ? 2 : 0;
+        if (a.dev_status) a.dev_status[b] = status_of(a, b, bad);
     }
 }
 
@@ -365,15 +388,20 @@ __global__ __launch_bounds__(kRowThreads) void accept_alpha_kernel(AcceptArgs a,
     __shared__ int last_flag;
     const int c = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
     const int g = a.gamma;
+    const int gb = gamma_of(a, b);
+    // a position past the sequence's length is not verified: it adds nothing and its alpha
+    // is NaN (its block still arrives at the counter)
+    const bool live = i < gb;
     float xp[kPerThread], xq[kPerThread];
     const int base = c * kChunk;
-    load_chunk2<VEC, kPerThread>(row_ptr(a, b, i), row_ptr(a, b, g + 1 + i), base, a.V, xp, xq);
+    const int ir = live ? i : 0;
+    load_chunk2<VEC, kPerThread>(row_ptr(a, b, ir), row_ptr(a, b, g + 1 + ir), base, a.V, xp, xq);
     // statistics of rows i (target) and gamma+1+i (draft): waves 0 and 1
     const int wave = threadIdx.x / kWave;
     if (wave < 2) {
         float M;
         double Z;
-        group_combine_softmax<kWave>(w.part + ((int64_t)b * a.rows + (wave == 0 ? i : g + 1 + i)) * a.npart, 0, 1,
+        group_combine_softmax<kWave>(w.part + ((int64_t)b * a.rows + (wave == 0 ? ir : g + 1 + ir)) * a.npart, 0, 1,
                                      a.npart, a.kd, M, Z);
         if (threadIdx.x % kWave == 0) {
             sM[wave] = (double)M;
@@ -392,12 +420,12 @@ __global__ __launch_bounds__(kRowThreads) void accept_alpha_kernel(AcceptArgs a,
         s += fmin(p, q);
     }
     s = block_sum(s, dscr);
-    if (threadIdx.x == 0) st_coherent(&w.apart[((int64_t)b * g + i) * a.nchunk + c], s);
+    if (threadIdx.x == 0) st_coherent(&w.apart[((int64_t)b * g + i) * a.nchunk + c], live ? s : 0.0);
     if (!arrive_last(&w.cnt[b], g * a.nchunk, &last_flag)) return;
     for (int j = threadIdx.x; j < g; j += blockDim.x) {
         double t = 0.0;
         for (int cc = 0; cc < a.nchunk; ++cc) t += w.apart[((int64_t)b * g + j) * a.nchunk + cc];
-        a.alpha[(int64_t)b * g + j] = (float)t;
+        a.alpha[(int64_t)b * g + j] = j < gb ? (float)t : __int_as_float(0x7fc00000);
     }
 }
 
@@ -423,6 +451,7 @@ __global__ __launch_bounds__(kRowThreads, 2) void accept_resample_kernel(AcceptA
     __shared__ double s_base, s_target, s_uextra;
     const int c = blockIdx.x, b = blockIdx.y;
     const int g = a.gamma;
+    const int gb = gamma_of(a, b);  // this sequence's drafts (rows past them are not read)
 
     // drafted tokens and their logits (two dependent loads, hidden behind the staging of the
     // row partials and the row statistics; a bad token is flagged below, its logit unused),
@@ -436,13 +465,13 @@ __global__ __launch_bounds__(kRowThreads, 2) void accept_resample_kernel(AcceptA
     const float lqx = a.draft[((int64_t)b * g + ti) * a.V + xc];
     const double u_mine = w.u[(int64_t)b * (g + 1) + min((int)threadIdx.x, g)];
     if (threadIdx.x == 0) {
-        firstbad = g;
+        firstbad = gb;
         bad = 0;
     }
     const RowPart *pp = w.part + (int64_t)b * a.rows * a.npart;
     RowPart *stage = reinterpret_cast<RowPart *>(dyn_lds);
     auto keep_extra = [&] {
-        if ((int)threadIdx.x == g) s_uextra = u_mine;
+        if ((int)threadIdx.x == gb) s_uextra = u_mine;
     };
     if (a.rows * a.npart <= kMaxStaged) {
         stage_parts(pp, a.rows * a.npart, stage, keep_extra);
@@ -452,7 +481,7 @@ __global__ __launch_bounds__(kRowThreads, 2) void accept_resample_kernel(AcceptA
         __syncthreads();
         row_softmax_stats(pp, a.rows, a.npart, a.kd, sM, sZ);
     }
-    if (threadIdx.x < g) {
+    if ((int)threadIdx.x < gb) {
         const int i = threadIdx.x;
         bool pass = false;
         if (x >= 0 && x < a.V) {
@@ -472,12 +501,12 @@ __global__ __launch_bounds__(kRowThreads, 2) void accept_resample_kernel(AcceptA
             if (i != J) out[i] = i < J ? a.tokens[(int64_t)b * g + i] : -1;
         if (threadIdx.x == 0) {
             a.accept_len[b] = J;
-            if (a.dev_status) a.dev_status[b] = bad ? 2 : 0;
+            if (a.dev_status) a.dev_status[b] = status_of(a, b, bad);
         }
     }
 
     const float *prow = a.target + ((int64_t)b * (g + 1) + J) * a.V;
-    const float *qrow = J < g ? a.draft + ((int64_t)b * g + J) * a.V : nullptr;
+    const float *qrow = J < gb ? a.draft + ((int64_t)b * g + J) * a.V : nullptr;
     const int base = c * kChunk;
 
     // Weights of token e relative to the rows' maxima, in fp64 (exp2_acc):
@@ -490,9 +519,9 @@ __global__ __launch_bounds__(kRowThreads, 2) void accept_resample_kernel(AcceptA
     // chunk's totals of wp and wq; the last block weighs a segment as A/Zp - B/Zq with the
     // exact normalizers.  (A token misjudged by the estimate holds a residual smaller than the
     // estimate's error: the segment masses are off by its square.)
-    const double Mp = sM[J], Mq = J < g ? sM[g + 1 + J] : Mp;
-    const double iZp_est = 1.0 / sZ[J], iZq_est = J < g ? 1.0 / sZ[g + 1 + J] : 0.0;
-    const double qmask = J < g ? 1.0 : 0.0;
+    const double Mp = sM[J], Mq = J < gb ? sM[g + 1 + J] : Mp;
+    const double iZp_est = 1.0 / sZ[J], iZq_est = J < gb ? 1.0 / sZ[g + 1 + J] : 0.0;
+    const double qmask = J < gb ? 1.0 : 0.0;
     // (l - M) kd as one multiply-add on the precomputed -M kd: 1e-16 |M kd| more error in
     // the exponent, ~1e-14 of a weight at logits of 100, one instruction less per weight
     const double nMpk = -Mp * a.kd, nMqk = -Mq * a.kd;
@@ -763,6 +792,8 @@ __global__ __launch_bounds__(kRowThreads, 2) void accept_block_pass_kernel(Accep
     __shared__ double s_w;
     const int c = blockIdx.x, kc = blockIdx.y, b = blockIdx.z;
     const int g = a.gamma;
+    const int gb = gamma_of(a, b);
+    if (kc > gb) return;  // a candidate past the sequence's length
     const int nch = gridDim.x;
     // the drafted tokens' logits (estimates of p_j(x_j), q_j(x_j) for j < kc)
     const int ti = min((int)threadIdx.x, g - 1);
@@ -792,11 +823,11 @@ __global__ __launch_bounds__(kRowThreads, 2) void accept_block_pass_kernel(Accep
     __syncthreads();
     const double wk = s_w;
     const float *prow = a.target + ((int64_t)b * (g + 1) + kc) * a.V;
-    const float *qrow = kc < g ? a.draft + ((int64_t)b * g + kc) * a.V : prow;
-    const double Mp = sM[kc], Mq = kc < g ? sM[g + 1 + kc] : Mp;
+    const float *qrow = kc < gb ? a.draft + ((int64_t)b * g + kc) * a.V : prow;
+    const double Mp = sM[kc], Mq = kc < gb ? sM[g + 1 + kc] : Mp;
     const double nMpk = -Mp * a.kd, nMqk = -Mq * a.kd;  // exponents as one multiply-add each
-    const double iZp_est = 1.0 / sZ[kc], iZq_est = kc < g ? 1.0 / sZ[g + 1 + kc] : 0.0;
-    const double qmask = kc < g ? 1.0 : 0.0;
+    const double iZp_est = 1.0 / sZ[kc], iZq_est = kc < gb ? 1.0 / sZ[g + 1 + kc] : 0.0;
+    const double qmask = kc < gb ? 1.0 : 0.0;
     float xp[PER], xq[PER];
     load_chunk2<VEC, PER>(prow, qrow, c * kBlockChunk, a.V, xp, xq);
     double ta = 0.0, tb = 0.0, tp = 0.0, tq = 0.0;
@@ -963,6 +994,7 @@ __global__ __launch_bounds__(kRowThreads) void accept_block_decide_kernel(Accept
     __shared__ int iscr[kRowThreads / kWave];
     const int b = blockIdx.x;
     const int g = a.gamma;
+    const int gb = gamma_of(a, b);  // this sequence's drafts: candidates 0..gb
     const int ti = min((int)threadIdx.x, g - 1);
     const int x = a.tokens[(int64_t)b * g + ti];
     const int xc = min(max(x, 0), a.V - 1);
@@ -982,7 +1014,7 @@ __global__ __launch_bounds__(kRowThreads) void accept_block_decide_kernel(Accept
     // candidate, lanes over the chunks, fixed order
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const BlockChunk *bc = w.bchunk + (int64_t)b * (g + 1) * nch;
-    for (int kc = wave; kc <= g; kc += kRowThreads / kWave) {
+    for (int kc = wave; kc <= gb; kc += kRowThreads / kWave) {
         double zp = 0.0, zq = 0.0;
         for (int c = lane; c < nch; c += kWave) {
             zp += bc[(int64_t)kc * nch + c].wp;
@@ -996,7 +1028,7 @@ __global__ __launch_bounds__(kRowThreads) void accept_block_decide_kernel(Accept
         }
     }
     __syncthreads();
-    if ((int)threadIdx.x < g) {
+    if ((int)threadIdx.x < gb) {
         const int j = threadIdx.x;
         s_p[j] = exp2_acc(((double)lpx - sM[j]) * a.kd) / s_zp[j];
         s_q[j] = exp2_acc(((double)lqx - sM[g + 1 + j]) * a.kd) / s_zq[j];
@@ -1005,26 +1037,26 @@ __global__ __launch_bounds__(kRowThreads) void accept_block_decide_kernel(Accept
     __syncthreads();
     if (threadIdx.x == 0) {
         s_wt[0] = 1.0;
-        for (int k = 1; k <= g; ++k) s_wt[k] = next_weight(s_wt[k - 1], s_p[k - 1], s_q[k - 1]);
+        for (int k = 1; k <= gb; ++k) s_wt[k] = next_weight(s_wt[k - 1], s_p[k - 1], s_q[k - 1]);
     }
     __syncthreads();
-    for (int kc = wave; kc <= g; kc += kRowThreads / kWave) {
-        const double wk = s_wt[kc], ip = 1.0 / s_zp[kc], iq = kc < g ? 1.0 / s_zq[kc] : 0.0;
+    for (int kc = wave; kc <= gb; kc += kRowThreads / kWave) {
+        const double wk = s_wt[kc], ip = 1.0 / s_zp[kc], iq = kc < gb ? 1.0 / s_zq[kc] : 0.0;
         double m = 0.0;
         for (int c = lane; c < nch; c += kWave) {
             const BlockChunk q = bc[(int64_t)kc * nch + c];
             m += fmax(0.0, wk * q.a * ip - q.b * iq);
         }
         m = wave_sum(m);
-        if (lane == 0) s_m[kc] = kc < g ? m : s_wt[g];
+        if (lane == 0) s_m[kc] = kc < gb ? m : s_wt[gb];
     }
     __syncthreads();
     if (threadIdx.x == 0) {
         int n = 0;
-        for (int k = 1; k <= g; ++k) {
+        for (int k = 1; k <= gb; ++k) {
             const double wk = s_wt[k], mk = s_m[k];
             const double h = wk < 1.0 ? mk / (mk + 1.0 - wk) : 1.0;
-            // the survival uniforms are w.u[b][0..gamma-1], the draw's w.u[b][gamma]
+            // the survival uniforms are w.u[b][0..gb-1], the draw's w.u[b][gb]
             if (w.u[(int64_t)b * (g + 1) + k - 1] <= h) n = k;
         }
         s_n = n;
@@ -1036,17 +1068,17 @@ __global__ __launch_bounds__(kRowThreads) void accept_block_decide_kernel(Accept
         if (i != n) out[i] = i < n ? a.tokens[(int64_t)b * g + i] : -1;
     if (threadIdx.x == 0) {
         a.accept_len[b] = n;
-        if (a.dev_status) a.dev_status[b] = bad ? 2 : 0;
+        if (a.dev_status) a.dev_status[b] = status_of(a, b, bad);
     }
-    // the draw from (w_n p_{n+1} - q_{n+1})+ (candidate n), with the uniform thread gamma holds
-    if ((int)threadIdx.x == g) s_ustar = u_mine;
+    // the draw from (w_n p_{n+1} - q_{n+1})+ (candidate n), with the uniform thread gb holds
+    if ((int)threadIdx.x == gb) s_ustar = u_mine;
     __syncthreads();
     const double us = s_ustar;
     const float *prow = a.target + ((int64_t)b * (g + 1) + n) * a.V;
-    const float *qrow = n < g ? a.draft + ((int64_t)b * g + n) * a.V : prow;
-    const double Mp = sM[n], Mq = n < g ? sM[g + 1 + n] : Mp;
-    const double wn = s_wt[n], ip = 1.0 / s_zp[n], iq = n < g ? 1.0 / s_zq[n] : 0.0;
-    const double qmask = n < g ? 1.0 : 0.0;
+    const float *qrow = n < gb ? a.draft + ((int64_t)b * g + n) * a.V : prow;
+    const double Mp = sM[n], Mq = n < gb ? sM[g + 1 + n] : Mp;
+    const double wn = s_wt[n], ip = 1.0 / s_zp[n], iq = n < gb ? 1.0 / s_zq[n] : 0.0;
+    const double qmask = n < gb ? 1.0 : 0.0;
     auto r_of = [&](float lp, float lq) {
         return fmax(0.0, wn * exp2_acc(((double)lp - Mp) * a.kd) * ip -
                              exp2_acc(((double)lq - Mq) * a.kd) * qmask * iq);
@@ -1142,6 +1174,7 @@ __global__ __launch_bounds__(kRowThreads) void accept_gumbel_pass_kernel(AcceptA
     __shared__ int s_i[kRowThreads / kWave];
     __shared__ float s_m[kRowThreads / kWave];
     const int c = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
+    if (i > gamma_of(a, b)) return;  // a position past the sequence's length
     const int nch = gridDim.x;
     const float *row = a.target + ((int64_t)b * (a.gamma + 1) + i) * a.V;
     const int base = c * kBlockChunk;
@@ -1249,13 +1282,14 @@ __global__ __launch_bounds__(kRowThreads) void accept_gumbel_decide_kernel(Accep
     __shared__ int firstbad, bad;
     const int b = blockIdx.x;
     const int g = a.gamma;
+    const int gb = gamma_of(a, b);
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     if (threadIdx.x == 0) {
-        firstbad = g;
+        firstbad = gb;
         bad = 0;
     }
     const GumbelPart *gp = w.gpart + (int64_t)b * (g + 1) * nch;
-    for (int i = wave; i <= g; i += kRowThreads / kWave) {
+    for (int i = wave; i <= gb; i += kRowThreads / kWave) {
         double best = -INFINITY;
         int arg = 0x7fffffff;
         for (int c = lane; c < nch; c += kWave) {
@@ -1277,7 +1311,7 @@ __global__ __launch_bounds__(kRowThreads) void accept_gumbel_decide_kernel(Accep
         if (lane == 0) y[i] = arg;
     }
     __syncthreads();
-    if ((int)threadIdx.x < g) {
+    if ((int)threadIdx.x < gb) {
         const int x = a.tokens[(int64_t)b * g + threadIdx.x];
         if (x != y[threadIdx.x]) atomicMin(&firstbad, (int)threadIdx.x);
         if (x < 0 || x >= a.V) bad = 1;
@@ -1290,7 +1324,7 @@ __global__ __launch_bounds__(kRowThreads) void accept_gumbel_decide_kernel(Accep
         for (int i = threadIdx.x; i < g; i += kRowThreads) a.alpha[(int64_t)b * g + i] = __int_as_float(0x7fc00000);
     if (threadIdx.x == 0) {
         a.accept_len[b] = J;
-        if (a.dev_status) a.dev_status[b] = bad ? 2 : 0;
+        if (a.dev_status) a.dev_status[b] = status_of(a, b, bad);
     }
 }
 
@@ -1424,6 +1458,7 @@ extern "C" sv_status sv_spec_accept(const sv_accept_desc *d, void *workspace, si
     a.out_tokens = d->out_tokens;
     a.dev_status = d->dev_status;
     a.alpha = d->alpha;
+    a.draft_len = d->draft_len;
 
     const bool vec = (d->V % 4 == 0) && (((uintptr_t)d->target_logits & 15) == 0) &&
                      (!sample || ((uintptr_t)d->draft_logits & 15) == 0);

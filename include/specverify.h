@@ -220,6 +220,21 @@ SV_API sv_status sv_verify_attention(const sv_attn_desc *desc, void *workspace, 
 /*   with counter (x div 4, step, stream, 0x53560003 + 2^32 i); J = the first i < gamma    */
 /*   with x_i != y_i (else gamma); emits x_0..x_{J-1}, y_J.  Draft logits are not read    */
 /*   (the drafter used the same noise); scores in fp64, ties to the lowest token.          */
+/* RAGGED LENGTHS ([TB] section "Choosing how much to verify at every step": a step      */
+/*   verifies its own number of drafts per request):                                     */
+/*   draft_len     optional device int32 [B]; sequence b verifies only its first          */
+/*                 L_b = draft_len[b] drafts, 0 <= L_b <= gamma.  Its results are exactly  */
+/*                 those of the same call with gamma = L_b on its first L_b + 1 target     */
+/*                 rows, L_b draft rows and tokens (so the extra token takes the uniform   */
+/*                 of index L_b, and L_b = 0 is one draw from target row 0); rows past     */
+/*                 them are neither read nor needed.  accept_len <= L_b; out_tokens as     */
+/*                 above, then -1 to gamma + 1 entries; alpha NaN past L_b.  NULL: every   */
+/*                 sequence verifies gamma drafts.  The layouts keep their gamma strides.  */
+/*                 The result is exact only when L_b does not depend on the drafted tokens  */
+/*                 themselves (the section's warning box "Trimming a draft can break       */
+/*                 exactness"): the caller's choice, which the library cannot check.        */
+/*   dev_status    3 when draft_len[b] is outside [0, gamma] (the sequence is then taken   */
+/*                 with L_b clamped into it; its outputs are unspecified)                  */
 /* Supported: 1 <= gamma <= 64, 1 <= V, B <= 32768.                                      */
 /* ---------------------------------------------------------------------------------- */
 typedef struct sv_accept_desc {
@@ -235,6 +250,7 @@ typedef struct sv_accept_desc {
     float *alpha;
     int32_t *dev_status;
     sv_rule rule;
+    const int32_t *draft_len;
 } sv_accept_desc;
 
 SV_API size_t sv_spec_accept_workspace(const sv_accept_desc *desc);

@@ -301,6 +301,56 @@ def gumbel_accept(target, draft_tokens, temperature: float, seed: int, step: int
     return dict(accept_len=acc, out_tokens=out, flags=flags)
 
 
+RULE_TOKEN, RULE_BLOCK, RULE_GUMBEL = 0, 1, 2
+
+
+def accept_ragged(rule: int, mode: int, target, draft, draft_tokens, draft_len, temperature: float, seed: int,
+                  step: int = 0, stream_ids=None, want_alpha: bool = False):
+    """One round where sequence b verifies only its first L_b = draft_len[b] drafts.
+
+    "Speculative decoding" (Zero to Frontier), section "Choosing how much to verify at every
+    step": a step that verifies l_r drafts of request r runs the target over 1 + l_r tokens of
+    it, so the round of sequence b is the ordinary round with gamma = L_b on its first L_b + 1
+    target rows, L_b draft rows and tokens, with its own stream of uniforms.  This calls the
+    fixed-gamma functions above once per distinct length (rule 0: spec_accept, 1: block_accept,
+    2: gumbel_accept) and lays the results out at the full gamma: out_tokens [B][gamma+1]
+    padded with -1, alpha [B][gamma] NaN past L_b.  L_b = 0 is one draw from target row 0.
+    """
+    tgt = _c(target, np.float32)
+    B, g1, V = tgt.shape
+    gamma = g1 - 1
+    dr = None if draft is None else _c(draft, np.float32)
+    toks = _c(draft_tokens, np.int32).reshape(B, gamma)
+    L = np.asarray(draft_len, dtype=np.int64).reshape(B)
+    if (L < 0).any() or (L > gamma).any():
+        raise ValueError("draft lengths must lie in [0, gamma]")
+    sid = np.arange(B, dtype=np.uint64) if stream_ids is None else _c(stream_ids, np.uint64).reshape(B)
+    acc = np.zeros(B, dtype=np.int32)
+    out = np.full((B, g1), -1, dtype=np.int32)
+    alpha = np.full((B, gamma), np.nan) if want_alpha else None
+    flags = np.zeros(B, dtype=np.int32)
+    for lb in np.unique(L):
+        lb = int(lb)
+        idx = np.nonzero(L == lb)[0]
+        t = np.ascontiguousarray(tgt[idx, :lb + 1])
+        x = np.ascontiguousarray(toks[idx, :lb])
+        d = None if dr is None else np.ascontiguousarray(dr[idx, :lb])
+        s = np.ascontiguousarray(sid[idx])
+        sampled = not (mode == GREEDY or temperature == 0.0)  # else every rule is the greedy one
+        if sampled and rule == RULE_GUMBEL:
+            r = gumbel_accept(t, x, temperature, seed, step, stream_ids=s)
+        elif sampled and rule == RULE_BLOCK:
+            r = block_accept(t, d, x, temperature, seed, step, stream_ids=s)
+        else:
+            r = spec_accept(mode, t, d, x, temperature, seed, step, stream_ids=s, want_alpha=want_alpha)
+            if want_alpha and lb > 0:
+                alpha[idx, :lb] = r["alpha"]
+        acc[idx] = r["accept_len"]
+        out[idx, :lb + 1] = r["out_tokens"]
+        flags[idx] = r["flags"]
+    return dict(accept_len=acc, out_tokens=out, alpha=alpha, flags=flags)
+
+
 def tree_rrs(target, draft, tokens, parents, temperature: float, seed: int, step: int = 0, stream_ids=None,
              max_depth=None, without_replacement: bool = False, handle=None, allow_too_deep: bool = False):
     """Recursive rejection over a token tree -> dict(accept_len, path, out_tokens, flags, status)."""

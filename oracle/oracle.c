@@ -492,6 +492,8 @@ ORC_EXPORT int32_t orc_kv_commit(int32_t B, int32_t n_q, int32_t Hkv, int32_t D,
 /* gamma = 1 the two rules take the same decisions).  A drafted token with    */
 /* q = 0 sets w_k = 1 if p > 0 (and w_{k-1} > 0), else 0.  A zero residual     */
 /* falls back to p_{n+1}.  p, q = softmax(logits / T).                         */
+/* gamma = 0 (no draft verified): one draw from p_1 with the uniform of index */
+/* 0, as in orc_spec_accept.                                                  */
 /* Outputs as orc_spec_accept; weights[B][gamma+1] = w_0..w_gamma (optional);  */
 /* flags bit0 = some |u - h_k| < 1e-6, bit1 = the draw within 1e-10 of a      */
 /* CDF boundary.                                                              */
@@ -501,7 +503,7 @@ ORC_EXPORT int32_t orc_block_accept(int32_t B, int32_t gamma, int32_t V, float t
                                     uint64_t seed, uint64_t step, const uint64_t *stream_ids,
                                     int32_t *accept_len, int32_t *out_tokens, double *weights, int32_t *flags)
 {
-    if (B < 0 || gamma < 1 || V <= 0 || !(temperature > 0.0f)) return 1;
+    if (B < 0 || gamma < 0 || V <= 0 || !(temperature > 0.0f)) return 1;
     const double tau = (double)temperature;
     int32_t bad = 0;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -633,14 +635,15 @@ ORC_EXPORT int32_t orc_gumbel_argmax(int32_t B, int32_t rows, int32_t V, float t
 /* Gumbel-coupled verification ([AG], same section): the target's sample y_i  */
 /* at every position, the longest prefix with x_i == y_i is kept (J), and y_J */
 /* is appended -- exact matching, as under greedy decoding; the output is what */
-/* the target samples with that noise on its own.  Outputs as orc_spec_accept; */
+/* the target samples with that noise on its own (gamma = 0: just y_0).      */
+/* Outputs as orc_spec_accept;                                                 */
 /* flags bit0 = an evaluated position's best two scores within 1e-12.          */
 ORC_EXPORT int32_t orc_gumbel_accept(int32_t B, int32_t gamma, int32_t V, float temperature, const float *target,
                                      const int32_t *draft_tokens, uint64_t seed, uint64_t step,
                                      const uint64_t *stream_ids, int32_t *accept_len, int32_t *out_tokens,
                                      int32_t *flags)
 {
-    if (B < 0 || gamma < 1 || V <= 0 || !(temperature >= 0.0f)) return 1;
+    if (B < 0 || gamma < 0 || V <= 0 || !(temperature >= 0.0f)) return 1;
     const double tau = (double)temperature;
     int32_t bad = 0;
 #pragma omp parallel for schedule(dynamic, 1)

@@ -181,3 +181,32 @@ def test_static_accept_rejects_calls_beyond_its_scratch():
     assert sv.lib.sv_spec_accept_static(ctypes.byref(d), None) == sv.SV_ERR_WORKSPACE
     d.B = 64
     assert sv.lib.sv_spec_accept_workspace(ctypes.byref(d)) <= sv.SV_STATIC_SCRATCH_BYTES
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    """Every descriptor the binding declares has the C header's field offsets and size (a
+    small C program built against include/specverify.h prints them)."""
+    import shutil
+    import subprocess
+    if not shutil.which("gcc"):
+        pytest.skip("no C compiler")
+    structs = {"sv_philox": sv.sv_philox, "sv_attn_desc": sv.sv_attn_desc, "sv_accept_desc": sv.sv_accept_desc,
+               "sv_walk_desc": sv.sv_walk_desc, "sv_commit_desc": sv.sv_commit_desc}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "specverify.h"', "int main(void) {"]
+    for name, cls in structs.items():
+        lines.append('printf("%s sizeof %%zu\\n", sizeof(%s));' % (name, name))
+        for field, _ in cls._fields_:
+            lines.append('printf("%s %s %%zu\\n", offsetof(%s, %s));' % (name, field, name, field))
+    lines += ["return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = {}
+    for ln in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.splitlines():
+        s, f, v = ln.split()
+        got[(s, f)] = int(v)
+    for name, cls in structs.items():
+        assert got[(name, "sizeof")] == ctypes.sizeof(cls), name
+        for field, _ in cls._fields_:
+            assert got[(name, field)] == getattr(cls, field).offset, (name, field)
