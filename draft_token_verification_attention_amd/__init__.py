@@ -65,9 +65,14 @@ class sv_commit_desc(ctypes.Structure):
                 ("new_len", _P), ("dev_status", _P)]
 
 
+class sv_trunc_desc(ctypes.Structure):
+    _fields_ = [("R", _i32), ("V", _i32), ("temperature", _f32), ("top_k", _i32), ("top_p", _f32),
+                ("top_k_rows", _P), ("top_p_rows", _P), ("logits", _P), ("out", _P), ("kept", _P)]
+
+
 EXPORTS = ("sv_build_tree_mask", "sv_verify_attention_workspace", "sv_verify_attention",
            "sv_spec_accept_workspace", "sv_spec_accept", "sv_spec_accept_static", "sv_tree_walk_workspace",
-           "sv_tree_walk", "sv_kv_commit", "sv_status_string")
+           "sv_tree_walk", "sv_kv_commit", "sv_truncate", "sv_status_string")
 
 
 def _load():
@@ -93,6 +98,8 @@ def _load():
     L.sv_tree_walk.restype = ctypes.c_int
     L.sv_kv_commit.argtypes = [ctypes.POINTER(sv_commit_desc), _P]
     L.sv_kv_commit.restype = ctypes.c_int
+    L.sv_truncate.argtypes = [ctypes.POINTER(sv_trunc_desc), _P]
+    L.sv_truncate.restype = ctypes.c_int
     L.sv_status_string.argtypes = [ctypes.c_int]
     L.sv_status_string.restype = ctypes.c_char_p
     return L
@@ -338,3 +345,41 @@ def sv_kv_commit(k, v, kv_off, prefix_len, accept_len, *, n_q: int, Hkv: int, D:
                     dev_status=status)
     _check(lib.sv_kv_commit(ctypes.byref(d), _stream(k.device)), "sv_kv_commit")
     return new_len, status
+
+
+# --------------------------------------------------------------------------- #
+def trunc_desc(logits, out, *, temperature: float, top_k: int = 0, top_p: float = 1.0, top_k_rows=None,
+               top_p_rows=None, kept=None) -> sv_trunc_desc:
+    d = sv_trunc_desc()
+    d.R, d.V = logits.shape[0], logits.shape[1]
+    d.temperature, d.top_k, d.top_p = float(temperature), int(top_k), float(top_p)
+    d.top_k_rows = None if top_k_rows is None else top_k_rows.data_ptr()
+    d.top_p_rows = None if top_p_rows is None else top_p_rows.data_ptr()
+    d.logits, d.out = logits.data_ptr(), out.data_ptr()
+    d.kept = None if kept is None else kept.data_ptr()
+    return d
+
+
+def sv_truncate(logits, *, temperature: float, top_k: int = 0, top_p: float = 1.0, top_k_rows=None,
+                top_p_rows=None, in_place: bool = False):
+    """Top-k then top-p truncation of fp32 logit rows [R][V] (any leading shape is flattened
+    into R).  Returns (out, kept int32 [R]): out holds the kept tokens' logits and -inf
+    elsewhere; with in_place it is `logits` itself (which must then be contiguous fp32)."""
+    _need_cuda(logits, top_k_rows, top_p_rows)
+    if logits.dtype != torch.float32:
+        raise ValueError("sv_truncate takes fp32 logits")
+    V = logits.shape[-1]
+    if in_place and not logits.is_contiguous():
+        raise ValueError("sv_truncate in place needs contiguous logits")
+    R = 1
+    for n in logits.shape[:-1]:
+        R *= n
+    x = logits.reshape(R, V) if in_place else logits.contiguous().reshape(R, V)
+    out = x if in_place else torch.empty_like(x)
+    kept = torch.empty(R, dtype=torch.int32, device=x.device)
+    kr = None if top_k_rows is None else top_k_rows.to(torch.int32).contiguous().reshape(R)
+    pr = None if top_p_rows is None else top_p_rows.to(torch.float32).contiguous().reshape(R)
+    d = trunc_desc(x, out, temperature=temperature, top_k=top_k, top_p=top_p, top_k_rows=kr, top_p_rows=pr,
+                   kept=kept)
+    _check(lib.sv_truncate(ctypes.byref(d), _stream(x.device)), "sv_truncate")
+    return out.reshape(logits.shape), kept

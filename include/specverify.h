@@ -377,6 +377,51 @@ typedef struct sv_commit_desc {
 
 SV_API sv_status sv_kv_commit(const sv_commit_desc *desc, void *stream);
 
+/* ---------------------------------------------------------------------------------- */
+/* sv_truncate -- top-k and top-p (nucleus) truncation of logit rows, the processing     */
+/* that makes p and q the distributions the two models really sample from ([TB] section  */
+/* "When the target samples, keep a guess with probability p over q", and box "The       */
+/* speculative sampling rule", case "A processed target": temperature and top-p are     */
+/* applied to the target with the drafted prefix as context).  The draft's rows must go  */
+/* through the same processing before they enter the ratio: the box "Four ways to lose   */
+/* exactness without noticing" names the draft's logits before its top-p cut as a wrong */
+/* q.  Feed the output rows to sv_spec_accept (or sv_tree_walk) with the same T.          */
+/* Tokens of a row are ordered by logit, highest first, equal logits by token id, lowest */
+/* first.  top-k keeps the first k of them (off when k <= 0 or k >= V).  top-p then keeps  */
+/* the shortest prefix of what top-k kept whose mass under softmax(l / T), taken over    */
+/* that kept set, reaches top_p times the set's total mass, and never fewer than one     */
+/* token (off when top_p >= 1 or NaN; top_p <= 0 keeps one token).  A row whose logits    */
+/* are all -inf is left as it is by top-p.                                                 */
+/*   logits      device fp32 [R][V]                                                        */
+/*   out         device fp32 [R][V]: the logit of each kept token, -inf elsewhere; may be */
+/*               `logits` itself (in place)                                                */
+/*   kept        optional device int32 [R]: the number of kept tokens of each row          */
+/*   top_k_rows  optional device int32 [R]: per-row k, replaces top_k                     */
+/*   top_p_rows  optional device fp32 [R]: per-row top_p, replaces top_p                  */
+/*   temperature T > 0 and finite (weights of top-p; read even when top-p is off)         */
+/* Top-p weights are 2^((l - max) log2(e) / T) in fp64 (to about 2e-14 relative), summed */
+/* exactly as integers in units of 2^-62 of the largest one, so the kept set does not     */
+/* depend on the order of the sums, and it can differ from the exact one only where the  */
+/* cut lies within about 1e-13 of the set's mass, relative.  NaN or +inf logits: results */
+/* unspecified.                                                                           */
+/* Errors: R < 0, V < 1, T not in (0, inf), NaN top_p, or (R > 0) a null logits or out  */
+/*   -> SV_ERR_INVALID_ARG.  R == 0 launches nothing.                                     */
+/* Supported: 1 <= V <= 2^24 (else SV_ERR_UNSUPPORTED), R <= 2^31 - 1.                    */
+/* ---------------------------------------------------------------------------------- */
+typedef struct sv_trunc_desc {
+    int32_t R, V;
+    float temperature;
+    int32_t top_k;
+    float top_p;
+    const int32_t *top_k_rows;
+    const float *top_p_rows;
+    const float *logits;
+    float *out;
+    int32_t *kept;
+} sv_trunc_desc;
+
+SV_API sv_status sv_truncate(const sv_trunc_desc *desc, void *stream);
+
 /* Human-readable name of a status code (static storage). */
 SV_API const char *sv_status_string(sv_status status);
 

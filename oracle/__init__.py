@@ -84,6 +84,8 @@ def _typed(L):
     L.orc_gumbel_accept.restype = i32
     L.orc_tree_rrs.argtypes = [i32, i32, i32, i32, f32, i32, P, P, P, P, u64, u64, P, P, P, P, P]
     L.orc_tree_rrs.restype = i32
+    L.orc_truncate.argtypes = [i32, i32, f32, i32, f32, P, P, P, P, P, P]
+    L.orc_truncate.restype = i32
     return L
 
 
@@ -299,6 +301,27 @@ def gumbel_accept(target, draft_tokens, temperature: float, seed: int, step: int
     if st != 0:
         raise ValueError("orc_gumbel_accept status %d" % st)
     return dict(accept_len=acc, out_tokens=out, flags=flags)
+
+
+def truncate(logits, temperature: float, top_k: int = 0, top_p: float = 1.0, top_k_rows=None, top_p_rows=None,
+             handle=None):
+    """Top-k, then top-p truncation of every row of logits [..., V] (oracle.c orc_truncate)
+    -> dict(out (same shape, -inf off the kept set), kept [rows], flags [rows])."""
+    lg = _c(logits, np.float32)
+    shape = lg.shape
+    V = shape[-1]
+    rows = lg.reshape(-1, V)
+    R = rows.shape[0]
+    out = np.empty_like(rows)
+    kept = np.zeros(R, dtype=np.int32)
+    flags = np.zeros(R, dtype=np.int32)
+    kr = None if top_k_rows is None else _c(top_k_rows, np.int32).reshape(R)
+    pr = None if top_p_rows is None else _c(top_p_rows, np.float32).reshape(R)
+    st = (handle or lib()).orc_truncate(R, V, float(temperature), int(top_k), float(top_p), _p(kr), _p(pr),
+                                        _p(rows), _p(out), _p(kept), _p(flags))
+    if st != 0:
+        raise ValueError("orc_truncate status %d" % st)
+    return dict(out=out.reshape(shape), kept=kept, flags=flags)
 
 
 RULE_TOKEN, RULE_BLOCK, RULE_GUMBEL = 0, 1, 2

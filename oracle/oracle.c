@@ -763,3 +763,85 @@ ORC_EXPORT int32_t orc_tree_rrs(int32_t B, int32_t n, int32_t V, int32_t max_dep
     }
     return status;
 }
+
+/* ------------------------------------------------------------------------- */
+/* Truncated sampling distributions.  "Speculative decoding" (Zero to        */
+/* Frontier), section "When the target samples, keep a guess with           */
+/* probability p over q": p and q are the distributions each model really   */
+/* samples from, after temperature and truncation such as top-p; the box     */
+/* "The speculative sampling rule", special case "A processed target"; box   */
+/* "Four ways to lose exactness without noticing": the q of the ratio must   */
+/* be the draft's own truncated distribution.                                */
+/*   Row r of logits l: tokens in the order (l descending, token id          */
+/*   ascending).  top-k keeps the first k (k <= 0 or k >= V: all); then      */
+/*   top-p keeps the shortest prefix of those whose mass under               */
+/*   softmax(l / T), renormalized over them, reaches top_p (top_p >= 1: all; */
+/*   at least one token).  out = l on kept tokens, -inf elsewhere, so that   */
+/*   softmax(out / T) is the truncated, renormalized distribution.           */
+/*   kept[r] = tokens kept; flags[r] bit0: the top-p prefix mass at the       */
+/*   chosen boundary lay within 1e-10 of the target, relative to the set's   */
+/*   mass: there weights rounded otherwise (fp64 to ~1e-14 each, summed in    */
+/*   another order) could move the boundary by one token.                    */
+/*   Per-row k and top_p (top_k_rows, top_p_rows) override the scalars.      */
+/* ------------------------------------------------------------------------- */
+#define ORC_NEAR_NUCLEUS 1e-10
+
+typedef struct {
+    float l;
+    int32_t id;
+} orc_tok;
+
+static int orc_tok_cmp(const void *a, const void *b)
+{
+    const orc_tok *x = (const orc_tok *)a, *y = (const orc_tok *)b;
+    if (x->l > y->l) return -1;
+    if (x->l < y->l) return 1;
+    return (x->id > y->id) - (x->id < y->id);
+}
+
+ORC_EXPORT int32_t orc_truncate(int32_t R, int32_t V, float temperature, int32_t top_k, float top_p,
+                                const int32_t *top_k_rows, const float *top_p_rows, const float *logits, float *out,
+                                int32_t *kept, int32_t *flags)
+{
+    if (R < 0 || V <= 0) return 1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int32_t r = 0; r < R; ++r) {
+        const float *l = logits + (int64_t)r * V;
+        float *o = out + (int64_t)r * V;
+        const int32_t k = top_k_rows ? top_k_rows[r] : top_k;
+        const double pp = (double)(top_p_rows ? top_p_rows[r] : top_p);
+        orc_tok *t = (orc_tok *)malloc(sizeof(orc_tok) * (size_t)V);
+        for (int32_t x = 0; x < V; ++x) t[x] = (orc_tok){l[x], x};
+        qsort(t, (size_t)V, sizeof(orc_tok), orc_tok_cmp);
+        int32_t n = (k > 0 && k < V) ? k : V;
+        int32_t fl = 0;
+        if (pp < 1.0) {
+            const double T = (double)temperature, M = (double)t[0].l;
+            double z = 0.0;
+            for (int32_t i = 0; i < n; ++i) z += exp(((double)t[i].l - M) / T);
+            const double target = pp * z;
+            double c = 0.0;
+            int32_t m = 0;
+            while (m < n) {
+                const double before = c;
+                c += exp(((double)t[m].l - M) / T);
+                ++m;
+                if (c >= target) {
+                    /* the cut could move by one token: later if c barely reaches the target,
+                     * earlier if the prefix before it barely misses (never below one token) */
+                    if (fabs(c - target) < ORC_NEAR_NUCLEUS * z ||
+                        (m > 1 && fabs(before - target) < ORC_NEAR_NUCLEUS * z))
+                        fl |= 1;
+                    break;
+                }
+            }
+            n = m > 0 ? m : 1;
+        }
+        for (int32_t x = 0; x < V; ++x) o[x] = -INFINITY;
+        for (int32_t i = 0; i < n; ++i) o[t[i].id] = t[i].l;
+        if (kept) kept[r] = n;
+        if (flags) flags[r] = fl;
+        free(t);
+    }
+    return 0;
+}

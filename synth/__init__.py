@@ -28,7 +28,7 @@ import numpy as np
 _STREAM = {
     "prefix": 1, "q": 2, "k": 3, "v": 4, "target": 5, "draft_noise": 6,
     "draft_gumbel": 7, "node_noise": 8, "tree_logits": 9, "root_token": 10,
-    "misc": 11,
+    "misc": 11, "logit_rows": 12,
 }
 
 
@@ -275,3 +275,12 @@ def node_tokens(seed: int, logits: np.ndarray, parents: np.ndarray, ranks=None) 
 def path_ranks(paths: list) -> np.ndarray:
     """Last rank of each node's rank path (0 for the root)."""
     return np.array([p[-1] if p else 0 for p in paths], dtype=np.int32)
+
+
+def logit_rows(seed: int, R: int, V: int, variance: float, grid: float = 0.0) -> np.ndarray:
+    """fp32 logit rows [R][V] ~ N(0, variance); with grid > 0 every logit is rounded to a
+    multiple of grid, so that rows hold many exactly equal logits (ties)."""
+    a = normal(seed, "logit_rows", (R, V), variance)
+    if grid > 0:
+        a = (np.round(a / np.float32(grid)) * np.float32(grid)).astype(np.float32)
+    return a
