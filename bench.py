@@ -267,6 +267,32 @@ def time_accept_rule(sv, copies, toks, tau, seed, rule, shape, steps, sh, dev):
     return out
 
 
+def time_truncate(sv, copies, tau, top_k, top_p, steps, sh, dev):
+    """sv_truncate on both models' rows of the round (target [B][gamma+1][V] and draft
+    [B][gamma][V]; two calls per step, into separate output buffers so the inputs stay as they
+    are).  Algorithmic bytes: every logit read once and written once."""
+    import torch
+    R = len(copies)
+    outs = {k: torch.empty_like(copies[0][k]) for k in ("target", "draft")}
+    kept = {k: torch.empty(copies[0][k].numel() // copies[0][k].shape[-1], dtype=torch.int32, device=dev)
+            for k in ("target", "draft")}
+    V = copies[0]["target"].shape[-1]
+    descs = [[sv.trunc_desc(c[k].reshape(-1, V), outs[k].reshape(-1, V), temperature=tau, top_k=top_k,
+                            top_p=top_p, kept=kept[k]) for k in ("target", "draft")] for c in copies]
+
+    def call(i):
+        for d in descs[i % R]:
+            if sv.lib.sv_truncate(ctypes.byref(d), sh):
+                raise RuntimeError("truncate launch failed")
+    ms = median_event_ms(call, steps, sh)
+    rows = sum(kept[k].numel() for k in kept)
+    nbytes = 8 * V * rows
+    return {"kernel_ms": round(ms, 5), "rows": rows, "top_k": top_k, "top_p": top_p,
+            "algorithmic_bytes": nbytes, "achieved_GBs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "mean_kept": round(float(torch.cat([kept["target"], kept["draft"]]).float().mean().item()), 1),
+            "bound": "hbm (the row is read 2 to 3 times: selection passes, then a gather pass that writes)"}
+
+
 def time_commit(sv, k, v, kv_off, prefix, acc_len, path, n_q, Hkv, D, kv_sh, kv_st, kv_sb, esize, steps, sh, dev):
     """sv_kv_commit on the given caches (new lengths to a separate buffer, so every call
     moves the same rows).  Algorithmic bytes: the moved K and V rows, read and written."""
@@ -448,6 +474,8 @@ def bench_chain(args, cfg, wl, dev, steps, warmup, cpu):
                                                     steps, sh, dev),
             "kv_commit_chain": time_commit(sv, base["k"], base["v"], kv_off, prefix, acc_len, None, n_q, Hkv, D,
                                            att["kv_sh"], att["kv_st"], kv_sb, esz, steps, sh, dev),
+            "truncate_top_k_top_p": time_truncate(sv, copies, tau, 50, 0.9, steps, sh, dev),
+            "truncate_top_p": time_truncate(sv, copies, tau, 0, 0.9, steps, sh, dev),
         }
     if cpu:
         # the GPU's own outputs for the step on copy 0 (seed, step 0), for the parity verdict

@@ -7,15 +7,22 @@
 // ways to lose exactness without noticing" (the q of the ratio must be the draft's own
 // truncated distribution, not its logits before truncation).
 //
-// One block per row.  Tokens are ordered by (logit descending, token id ascending); a
-// selection keeps the tokens up to a threshold (key*, id*) in that order, key an
-// order-preserving 32-bit image of the logit.  key* comes from a radix select over the row
-// (three passes: 11, 11 and 10 bits of the key, histograms in LDS), id* from one pass in
-// token order when only some of the tokens tied at key* are kept.  Top-p weighs token x by
-// w = 2^((l_x - M) log2(e) / T) (M the row's largest logit), in fp64 to about 2e-14, and sums
-// the weights as integers in units of 2^-62: every sum is exact and independent of the
-// order of the LDS atomics, so the kept set is deterministic, and the cut is the exact one
-// for those weights.  A last pass writes the logits of kept tokens and -inf elsewhere.
+// One block per row.  Tokens are ordered by (logit descending, token id ascending), i.e. by a
+// unique 56-bit composite C = (order-preserving key of the logit) << 24 | (2^24 - 1 - id),
+// descending.  Both cuts keep a prefix of that order, so the kept set is {C >= C*} for one
+// threshold token C*, found by a radix select: LDS histograms of one digit of C at a time
+// (11, 11, 10, 8, 8, 8 bits for counts, 10, 10, 10, 10, 8, 8 for masses), each walked from
+// the top to the bin where the running count (top-k) or mass (top-p) reaches its target.  Levels run over the row until the tokens left
+// in the crossing bin number at most kCap; one more pass gathers them into LDS (and writes
+// every other token's output), and the remaining levels run on that list.  Top-p's first
+// levels bin tokens by their weight instead (16 bins per factor of two, then 1024 sub-bins
+// of each), which spreads them over many more bins than the logit's leading bits do.  LDS stays under 48 KB, so three rows
+// run on each compute unit at once.
+//
+// Top-p weighs token x by w = 2^((l_x - M) log2(e) / T) (M the row's largest logit), in fp64
+// to about 2e-14, and sums the weights as integers in units of 2^-62: every sum is exact and
+// independent of the order of the LDS atomics, so the kept set is deterministic, and the cut
+// is the exact one for those weights.
 #include "vocab_row.h"
 
 namespace {
@@ -24,13 +31,30 @@ using namespace sv;
 typedef unsigned __int128 u128;
 
 constexpr int kTrThreads = kRowThreads;   // 256
-constexpr int kTrBins = 2048;             // radix digits of 11, 11 and 10 bits
+constexpr int kBins = 2048;               // count histogram bins (digits of at most 11 bits)
+constexpr int kMassBins = 1024;           // mass histogram bins (digits of at most 10 bits)
+constexpr int kCap = 2048;                // candidates gathered into LDS
+constexpr int kUnroll = 8;                // float4 loads in flight per thread
 constexpr int kFixBits = 62;              // a weight w in [0, 1] is floor(w 2^62)
 constexpr int kLoBits = 30;               // ... added to a bin as its high and low parts
+constexpr int kLevels = 6;
+constexpr int kIdBits = 24;               // token ids < 2^24
+constexpr uint64_t kIdMask = (1ull << kIdBits) - 1;
+constexpr float kFinePerUnit = 16384.0f;  // fine weight bins per unit of log2(weight)
+constexpr int kFineBits = 20;             // fine weight bins: 2^20, over 64 units
+
+// digits of C, top first: for counts, and for masses (whose histograms have fewer bins)
+__device__ __constant__ const int kShiftC[kLevels] = {45, 34, 24, 16, 8, 0};
+__device__ __constant__ const int kWidthC[kLevels] = {11, 11, 10, 8, 8, 8};
+__device__ __constant__ const int kShiftM[kLevels] = {46, 36, 26, 16, 8, 0};
+__device__ __constant__ const int kWidthM[kLevels] = {10, 10, 10, 10, 8, 8};
+template <bool MASS> __device__ __forceinline__ int dshift(int l) { return MASS ? kShiftM[l] : kShiftC[l]; }
+template <bool MASS> __device__ __forceinline__ int dwidth(int l) { return MASS ? kWidthM[l] : kWidthC[l]; }
 
 struct TruncArgs {
     int R, V;
     double kd;     // log2(e) / T, for the top-p weights
+    float kb;      // kFinePerUnit log2(e) / T, for the weight bins
     int top_k;
     float top_p;
     const int32_t *k_rows;
@@ -38,7 +62,7 @@ struct TruncArgs {
     const float *in;
     float *out;
     int32_t *kept;
-    int vec;       // 16-byte aligned rows with V % 4 == 0: float4 loads
+    int vec;       // 16-byte aligned rows with V % 4 == 0: float4 loads and stores
 };
 
 // Ascending with the float value (-0 taken as +0; rows hold no NaN).
@@ -53,6 +77,15 @@ __device__ __forceinline__ float key_value(uint32_t k)
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
+__device__ __forceinline__ uint64_t composite(float v, int e)
+{
+    return ((uint64_t)order_key(v) << kIdBits) | (kIdMask - (uint64_t)e);
+}
+
+__device__ __forceinline__ int comp_id(uint64_t c) { return (int)(kIdMask - (c & kIdMask)); }
+
+__device__ __forceinline__ float comp_value(uint64_t c) { return key_value((uint32_t)(c >> kIdBits)); }
+
 // floor(2^((v - M) kd) 2^62) for v <= M; 0 for v = -inf.
 __device__ __forceinline__ uint64_t fix_weight(float v, float M, double kd)
 {
@@ -60,31 +93,98 @@ __device__ __forceinline__ uint64_t fix_weight(float v, float M, double kd)
     return (uint64_t)ldexp(fmin(w, 1.0), kFixBits);
 }
 
-// f(value, token) over the row; round r covers tokens [1024 r, 1024 r + 1024), thread t its
-// tokens 1024 r + 4t .. 4t + 3, so a round is in token order across the threads.
+// Fine weight bin of v: about 16384 bins per unit of -log2(w), 2^20 - 1 for w below about
+// 2^-64 (and -inf); larger v, smaller (or equal) bin.  Its top 10 bits are the first weight
+// level, its low 10 bits the second.  Only its monotonicity matters (the bins split the
+// order; masses come from fix_weight), so it is one fp32 product.
+__device__ __forceinline__ int weight_fine(float v, float M, float kb)
+{
+    constexpr int kTop = (1 << kFineBits) - 1;
+    const float x = (M - v) * kb;
+    return x < (float)kTop ? (int)x : kTop;
+}
+
+// f(value, token) over the row: each thread takes 4 consecutive tokens of every 1024, and
+// issues kUnroll 16-byte loads before using them.
 template <typename F>
 __device__ __forceinline__ void for_row(const float *row, int V, bool vec, F f)
 {
+    constexpr int kStep = 4 * kTrThreads;
+    const int t4 = 4 * (int)threadIdx.x;
     if (vec) {
-        for (int e = 4 * (int)threadIdx.x; e < V; e += 4 * kTrThreads) {
-            const float4 v = *reinterpret_cast<const float4 *>(row + e);
-            f(v.x, e);
-            f(v.y, e + 1);
-            f(v.z, e + 2);
-            f(v.w, e + 3);
+        int e0 = 0;
+        for (; e0 + kUnroll * kStep <= V; e0 += kUnroll * kStep) {
+            float4 x[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) x[u] = *reinterpret_cast<const float4 *>(row + e0 + u * kStep + t4);
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int e = e0 + u * kStep + t4;
+                f(x[u].x, e);
+                f(x[u].y, e + 1);
+                f(x[u].z, e + 2);
+                f(x[u].w, e + 3);
+            }
+        }
+        for (int e = e0 + t4; e < V; e += kStep) {
+            const float4 x = *reinterpret_cast<const float4 *>(row + e);
+            f(x.x, e);
+            f(x.y, e + 1);
+            f(x.z, e + 2);
+            f(x.w, e + 3);
         }
     } else {
-        for (int e0 = 4 * (int)threadIdx.x; e0 < V; e0 += 4 * kTrThreads)
+        for (int e0 = t4; e0 < V; e0 += kStep)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 if (e0 + j < V) f(row[e0 + j], e0 + j);
     }
 }
 
+// out[e] = g(in[e], e) over the row, with the loads of for_row and 16-byte stores.
+template <typename G>
+__device__ __forceinline__ void map_row(const float *row, float *orow, int V, bool vec, G g)
+{
+    constexpr int kStep = 4 * kTrThreads;
+    const int t4 = 4 * (int)threadIdx.x;
+    if (vec) {
+        int e0 = 0;
+        for (; e0 + kUnroll * kStep <= V; e0 += kUnroll * kStep) {
+            float4 x[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) x[u] = *reinterpret_cast<const float4 *>(row + e0 + u * kStep + t4);
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int e = e0 + u * kStep + t4;
+                float4 y;
+                y.x = g(x[u].x, e);
+                y.y = g(x[u].y, e + 1);
+                y.z = g(x[u].z, e + 2);
+                y.w = g(x[u].w, e + 3);
+                *reinterpret_cast<float4 *>(orow + e) = y;
+            }
+        }
+        for (int e = e0 + t4; e < V; e += kStep) {
+            const float4 x = *reinterpret_cast<const float4 *>(row + e);
+            float4 y;
+            y.x = g(x.x, e);
+            y.y = g(x.y, e + 1);
+            y.z = g(x.z, e + 2);
+            y.w = g(x.w, e + 3);
+            *reinterpret_cast<float4 *>(orow + e) = y;
+        }
+    } else {
+        for (int e0 = t4; e0 < V; e0 += kStep)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (e0 + j < V) orow[e0 + j] = g(row[e0 + j], e0 + j);
+    }
+}
+
 // Inclusive scan of one value per thread over the block, in thread order (Hillis-Steele in
 // LDS, exact for integers).  *total gets the block's total.
 template <typename T>
-__device__ T block_scan(T x, T *s, T *total)
+__device__ __forceinline__ T block_scan(T x, T *s, T *total)
 {
     const int t = threadIdx.x;
     __syncthreads();
@@ -102,24 +202,17 @@ __device__ T block_scan(T x, T *s, T *total)
     return r;
 }
 
-// A selection: of the tokens it was restricted to, those with key > key, and those with
-// key == key and token <= id, are kept.
-struct Sel {
-    uint32_t key;
-    int id;
-    uint64_t n_kept;
-};
-
 struct TrShared {
-    uint32_t hc[kTrBins];         // tokens per bin
-    uint64_t hw_hi[kTrBins];      // sum of (floor(w 2^62) >> 30) per bin (top-p)
-    uint64_t hw_lo[kTrBins];      // sum of the low 30 bits
+    uint32_t hc[kBins];         // tokens per bin
+    uint64_t hw_hi[kMassBins];  // sum of (floor(w 2^62) >> 30) per bin (top-p)
+    uint64_t hw_lo[kMassBins];  // sum of the low 30 bits
+    uint64_t list[kCap];        // composites of the gathered tokens
     u128 scan[kTrThreads];
-    uint32_t s_bin;
-    u128 s_above;                 // the walked quantity of the bins before the crossing one
+    uint32_t s_bin, s_n;
+    u128 s_above;               // the walked quantity of the bins before the crossing one
     uint64_t s_cnt_above;
-    int s_id;
-    uint64_t s_run;
+    uint64_t s_found;
+    float s_max[kTrThreads / kWave];
 };
 
 __device__ __forceinline__ u128 bin_mass(const TrShared &sh, int bin)
@@ -128,7 +221,7 @@ __device__ __forceinline__ u128 bin_mass(const TrShared &sh, int bin)
 }
 
 // ceil(pp W) for 0 <= pp < 1 (pp exactly m 2^-s with m < 2^24): the top-p target.
-__device__ u128 mass_target(float pp, u128 W)
+__device__ __forceinline__ u128 mass_target(float pp, u128 W)
 {
     if (!(pp > 0.0f)) return 0;
     int e;
@@ -140,188 +233,322 @@ __device__ u128 mass_target(float pp, u128 W)
     return (P + (((u128)1 << sft) - 1)) >> sft;
 }
 
-// The threshold of the tokens that pass `in`, walked in the order (key descending): the key
-// at which the running count reaches k (top-k), or the running mass reaches top_p times the
-// mass of those tokens (top-p, MASS).  Then id* among the tokens tied at that key, in token
-// order.  Every quantity is an exact integer.
-template <bool MASS, typename In>
-__device__ Sel radix_select(const float *row, const TruncArgs &a, float M, In in, int k, float pp, TrShared &sh)
+// The range of tokens a selection still has to split: those passing its filter whose fine
+// weight bin agrees with wf on its top 10 bits (wl = 1) or all 20 (wl = 2), and whose
+// composite agrees with `prefix` on the bits of `pmask` (the digits fixed so far, top bits
+// first).  The walked quantity (count, or mass) of the tokens before the range in the order
+// is `above`.
+struct Range {
+    int wl, wf;
+    uint64_t prefix, pmask;
+    int level;                 // next composite digit
+    u128 above, target;
+    uint64_t cnt_above;
+    uint32_t n;                // tokens in the range
+};
+
+__device__ __forceinline__ int wfix(const Range &rg, int fine)
 {
-    const int t = threadIdx.x;
-    uint32_t prefix = 0, pmask = 0;
-    uint64_t cnt_above = 0;   // tokens before the current key range
-    u128 above = 0;           // the walked quantity (count or mass) before it
-    u128 target = 0;
-    uint32_t tie_cnt = 0;
-    for (int lev = 0; lev < 3; ++lev) {
-        const int shift = lev == 0 ? 21 : lev == 1 ? 10 : 0;
-        const int nb = lev == 2 ? 1024 : 2048;
-        for (int i = t; i < nb; i += kTrThreads) {
-            sh.hc[i] = 0;
-            if (MASS) {
-                sh.hw_hi[i] = 0;
-                sh.hw_lo[i] = 0;
-            }
-        }
-        if (t == 0) {  // overwritten by the thread that holds the crossing
-            sh.s_bin = 0;
-            sh.s_above = 0;
-            sh.s_cnt_above = 0;
-        }
-        __syncthreads();
-        for_row(row, a.V, a.vec, [&](float v, int e) {
-            const uint32_t key = order_key(v);
-            if ((key & pmask) == prefix && in(key, e)) {
-                const int bin = (int)((key >> shift) & (uint32_t)(nb - 1));
-                atomicAdd(&sh.hc[bin], 1u);
-                if (MASS) {
-                    const uint64_t f = fix_weight(v, M, a.kd);
-                    atomicAdd((unsigned long long *)&sh.hw_hi[bin], (unsigned long long)(f >> kLoBits));
-                    atomicAdd((unsigned long long *)&sh.hw_lo[bin],
-                              (unsigned long long)(f & ((1ull << kLoBits) - 1)));
-                }
-            }
-        });
-        __syncthreads();
-        // this thread's bins, in descending key order: nb - 1 - G t - j
-        const int G = nb / kTrThreads;
-        uint64_t c_loc = 0;
-        u128 w_loc = 0;
-        for (int j = 0; j < G; ++j) {
-            const int bin = nb - 1 - G * t - j;
-            c_loc += sh.hc[bin];
-            w_loc += MASS ? bin_mass(sh, bin) : (u128)sh.hc[bin];
-        }
-        u128 w_tot;
-        const u128 w_pre = block_scan<u128>(w_loc, sh.scan, &w_tot) - w_loc;
-        u128 c_tot128;
-        const uint64_t c_pre = MASS ? (uint64_t)(block_scan<u128>(c_loc, sh.scan, &c_tot128) - c_loc)
-                                    : (uint64_t)w_pre;
-        if (lev == 0) {
-            target = MASS ? mass_target(pp, w_tot) : (u128)k;
-            if (target < 1) target = 1;   // at least one token
-        }
-        // what this level's tokens still have to cover (at most all of them)
-        u128 need = target - above;
-        if (need > w_tot) need = w_tot;
-        // the thread whose bins hold the crossing, and its first bin that reaches it
-        if (w_pre < need && need <= w_pre + w_loc) {
-            u128 c = w_pre;
-            uint64_t cc = c_pre;
-            for (int j = 0; j < G; ++j) {
-                const int bin = nb - 1 - G * t - j;
-                const u128 w = MASS ? bin_mass(sh, bin) : (u128)sh.hc[bin];
-                if (sh.hc[bin] > 0 && c + w >= need) {
-                    sh.s_bin = (uint32_t)bin;
-                    sh.s_above = c;
-                    sh.s_cnt_above = cc;
-                    break;
-                }
-                c += w;
-                cc += sh.hc[bin];
-            }
-        }
-        __syncthreads();
-        const uint32_t bsel = sh.s_bin;
-        above += sh.s_above;
-        cnt_above += sh.s_cnt_above;
-        prefix |= bsel << shift;
-        pmask |= (uint32_t)(nb - 1) << shift;
-        if (lev == 2) tie_cnt = sh.hc[bsel];
-        __syncthreads();
-    }
-    // tokens tied at key*: keep the first `keep` of them in token order
-    uint64_t keep;
-    const u128 rest = target > above ? target - above : 0;
-    if (MASS) {
-        const uint64_t f1 = fix_weight(key_value(prefix), M, a.kd);   // every tied token's weight
-        if (f1 == 0) {
-            keep = tie_cnt;
-        } else {  // ceil(rest / f1): an estimate, then exact corrections
-            keep = (uint64_t)((double)rest / (double)f1);
-            if (keep > tie_cnt) keep = tie_cnt;
-            while (keep < tie_cnt && (u128)keep * f1 < rest) ++keep;
-            while (keep > 1 && (u128)(keep - 1) * f1 >= rest) --keep;
-        }
-    } else {
-        keep = (uint64_t)rest;
-    }
-    if (keep < 1) keep = 1;
-    if (keep > tie_cnt) keep = tie_cnt;
-    Sel r;
-    r.key = prefix;
-    r.n_kept = cnt_above + keep;
-    r.id = 0x7fffffff;
-    if (keep < tie_cnt) {
-        // token order: rounds of 4 x 256 tokens, a block scan of each round's matches
-        if (t == 0) {
-            sh.s_id = -1;
-            sh.s_run = 0;
-        }
-        __syncthreads();
-        for (int e0 = 0; e0 < a.V; e0 += 4 * kTrThreads) {
-            int m[4];
-            uint64_t n = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int e = e0 + 4 * t + j;
-                m[j] = 0;
-                if (e < a.V) {
-                    const uint32_t key = order_key(row[e]);
-                    m[j] = (key == prefix && in(key, e)) ? 1 : 0;
-                }
-                n += m[j];
-            }
-            u128 tot;
-            const uint64_t before = sh.s_run + (uint64_t)(block_scan<u128>(n, sh.scan, &tot) - n);
-            if (before < keep && keep <= before + n) {
-                uint64_t c = before;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    c += m[j];
-                    if (m[j] && c == keep) sh.s_id = e0 + 4 * t + j;
-                }
-            }
-            __syncthreads();
-            if (t == 0) sh.s_run += (uint64_t)tot;
-            __syncthreads();
-            if (sh.s_id >= 0) break;
-        }
-        r.id = sh.s_id;
-        __syncthreads();
-    }
-    return r;
+    return rg.wl == 2 ? fine : rg.wl == 1 ? fine >> 10 : 0;
 }
 
-__global__ __launch_bounds__(kTrThreads) void truncate_kernel(TruncArgs a)
+__device__ __forceinline__ bool in_range(const Range &rg, uint64_t c, int fine)
+{
+    return wfix(rg, fine) == rg.wf && (c & rg.pmask) == rg.prefix;
+}
+
+// Before the range in the order (for tokens that pass the filter).
+__device__ __forceinline__ bool before_range(const Range &rg, uint64_t c, int fine)
+{
+    const int w = wfix(rg, fine);
+    if (w != rg.wf) return w < rg.wf;
+    return (c & rg.pmask) > rg.prefix;
+}
+
+__device__ __forceinline__ void clear_hist(TrShared &sh, int nb, bool mass)
+{
+    for (int i = threadIdx.x; i < nb; i += kTrThreads) {
+        sh.hc[i] = 0;
+        if (mass) {
+            sh.hw_hi[i] = 0;
+            sh.hw_lo[i] = 0;
+        }
+    }
+    if (threadIdx.x == 0) {  // overwritten by the thread that holds the crossing
+        sh.s_bin = 0;
+        sh.s_above = 0;
+        sh.s_cnt_above = 0;
+    }
+}
+
+__device__ __forceinline__ void add_token(TrShared &sh, int bin, bool mass, uint64_t f)
+{
+    atomicAdd(&sh.hc[bin], 1u);
+    if (mass) {
+        atomicAdd((unsigned long long *)&sh.hw_hi[bin], (unsigned long long)(f >> kLoBits));
+        atomicAdd((unsigned long long *)&sh.hw_lo[bin], (unsigned long long)(f & ((1ull << kLoBits) - 1)));
+    }
+}
+
+// Walk the histogram (bins nb-1 down to 0 = the order): the bin where the running quantity
+// reaches the target.  Sets the range's target on the first walk, moves `above` and
+// `cnt_above` past the bins before it, and returns it (rg.n = its tokens).
+template <bool MASS>
+__device__ __forceinline__ int walk(Range &rg, int nb, bool first, int k, float pp, TrShared &sh)
+{
+    const int t = threadIdx.x;
+    const int G = nb / kTrThreads;
+    uint64_t c_loc = 0;
+    u128 w_loc = 0;
+    for (int j = 0; j < G; ++j) {
+        const int bin = nb - 1 - G * t - j;
+        c_loc += sh.hc[bin];
+        w_loc += MASS ? bin_mass(sh, bin) : (u128)sh.hc[bin];
+    }
+    u128 w_tot;
+    const u128 w_pre = block_scan<u128>(w_loc, sh.scan, &w_tot) - w_loc;
+    u128 c_tot;
+    const uint64_t c_pre = MASS ? (uint64_t)(block_scan<u128>(c_loc, sh.scan, &c_tot) - c_loc) : (uint64_t)w_pre;
+    if (first) {
+        rg.target = MASS ? mass_target(pp, w_tot) : (u128)k;
+        if (rg.target < 1) rg.target = 1;   // at least one token
+    }
+    // what this range still has to cover (at most all of it)
+    u128 need = rg.target - rg.above;
+    if (need > w_tot) need = w_tot;
+    if (w_pre < need && need <= w_pre + w_loc) {
+        u128 c = w_pre;
+        uint64_t cc = c_pre;
+        for (int j = 0; j < G; ++j) {
+            const int bin = nb - 1 - G * t - j;
+            const u128 w = MASS ? bin_mass(sh, bin) : (u128)sh.hc[bin];
+            if (sh.hc[bin] > 0 && c + w >= need) {
+                sh.s_bin = (uint32_t)bin;
+                sh.s_above = c;
+                sh.s_cnt_above = cc;
+                break;
+            }
+            c += w;
+            cc += sh.hc[bin];
+        }
+    }
+    __syncthreads();
+    const int bin = (int)sh.s_bin;
+    rg.above += sh.s_above;
+    rg.cnt_above += sh.s_cnt_above;
+    rg.n = sh.hc[bin];
+    __syncthreads();
+    return bin;
+}
+
+template <bool MASS>
+__device__ __forceinline__ void fix_digit(Range &rg, int bin)
+{
+    const int s = dshift<MASS>(rg.level), w = dwidth<MASS>(rg.level);
+    rg.prefix |= (uint64_t)bin << s;
+    rg.pmask |= ((1ull << w) - 1) << s;
+    ++rg.level;
+}
+
+// Finish a selection on the gathered list (sh.list[0 .. sh.s_n), a superset of the range):
+// composite digits until one token is left.  Returns its composite.
+template <bool MASS, typename Filt>
+__device__ __forceinline__ uint64_t finish_in_lds(Range &rg, bool first, int k, float pp, float M, double kd, Filt filt,
+                                  TrShared &sh)
+{
+    const int n = min((int)sh.s_n, kCap);
+    while ((first || rg.n > 1) && rg.level < kLevels) {
+        const int nb = 1 << dwidth<MASS>(rg.level);
+        clear_hist(sh, nb, MASS);
+        __syncthreads();
+        const int s = dshift<MASS>(rg.level);
+        for (int i = threadIdx.x; i < n; i += kTrThreads) {
+            const uint64_t c = sh.list[i];
+            if (filt(c) && (c & rg.pmask) == rg.prefix)
+                add_token(sh, (int)((c >> s) & (uint64_t)(nb - 1)), MASS, MASS ? fix_weight(comp_value(c), M, kd) : 0);
+        }
+        __syncthreads();
+        fix_digit<MASS>(rg, walk<MASS>(rg, nb, first, k, pp, sh));
+        first = false;
+        if (rg.level == kLevels) break;   // every digit fixed: rg.prefix is the token
+    }
+    // the one token of the range
+    if (threadIdx.x == 0) sh.s_found = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += kTrThreads) {
+        const uint64_t c = sh.list[i];
+        if (filt(c) && (c & rg.pmask) == rg.prefix) sh.s_found = c;
+    }
+    __syncthreads();
+    const uint64_t found = sh.s_found;
+    __syncthreads();
+    return found;
+}
+
+__global__ __launch_bounds__(kTrThreads, 3) void truncate_kernel(TruncArgs a)
 {
     __shared__ TrShared sh;
-    __shared__ float fscr[kTrThreads / kWave];
     const int r = blockIdx.x;
+    const int t = threadIdx.x;
     const float *row = a.in + (int64_t)r * a.V;
     float *orow = a.out + (int64_t)r * a.V;
+    const int V = a.V;
+    const bool vec = a.vec != 0;
     const int k = a.k_rows ? a.k_rows[r] : a.top_k;
     const float pp = a.p_rows ? a.p_rows[r] : a.top_p;
-    const bool use_k = k > 0 && k < a.V, want_p = pp < 1.0f;
+    const bool use_k = k > 0 && k < V, want_p = pp < 1.0f;
 
-    float mt = -INFINITY;
-    if (want_p) for_row(row, a.V, a.vec, [&](float v, int) { mt = fmaxf(mt, v); });
-    const float M = want_p ? block_max(mt, fscr) : 0.0f;
+    if (!use_k && !want_p) {  // nothing to cut
+        if (orow != row) map_row(row, orow, V, vec, [](float v, int) { return v; });
+        if (a.kept && t == 0) a.kept[r] = V;
+        return;
+    }
+
+    auto none = [](uint64_t) { return true; };
+    float M = -INFINITY;
+    Range rk{0, 0, 0, 0, 0, 0, 0, 0, (uint32_t)V};
+
+    // ---- top-k: count histogram of the first digit over the row (and the row max) ----
+    if (use_k) {
+        clear_hist(sh, kBins, false);
+        __syncthreads();
+        float mt = -INFINITY;
+        for_row(row, V, vec, [&](float v, int e) __attribute__((always_inline)) {
+            if (want_p) mt = fmaxf(mt, v);
+            atomicAdd(&sh.hc[(int)(composite(v, e) >> kShiftC[0])], 1u);
+        });
+        if (want_p) M = block_max(mt, sh.s_max);
+        __syncthreads();
+        fix_digit<false>(rk, walk<false>(rk, kBins, true, k, 0.0f, sh));
+    } else {
+        float mt = -INFINITY;
+        for_row(row, V, vec, [&](float v, int) __attribute__((always_inline)) { mt = fmaxf(mt, v); });
+        M = block_max(mt, sh.s_max);
+    }
     // a row of -inf logits has no distribution to truncate: top-p leaves it as it is
     const bool use_p = want_p && M != -INFINITY;
+    const double kd = a.kd;
+    const float kb = a.kb;
+    if (!use_k && !use_p) {
+        if (orow != row) map_row(row, orow, V, vec, [](float v, int) { return v; });
+        if (a.kept && t == 0) a.kept[r] = V;
+        return;
+    }
 
-    Sel sk{0u, 0x7fffffff, (uint64_t)a.V};
-    if (use_k) sk = radix_select<false>(row, a, M, [](uint32_t, int) { return true; }, k, 0.0f, sh);
-    auto in_k = [&](uint32_t key, int e) { return !use_k || key > sk.key || (key == sk.key && e <= sk.id); };
-    Sel s = sk;
-    if (use_p) s = radix_select<true>(row, a, M, in_k, 0, pp, sh);
-    const bool cut = use_k || use_p;
-    for_row(row, a.V, a.vec, [&](float v, int e) {
-        const uint32_t key = order_key(v);
-        const bool keep = !cut || (in_k(key, e) && (!use_p || key > s.key || (key == s.key && e <= s.id)));
-        orow[e] = keep ? v : -INFINITY;
-    });
-    if (a.kept && threadIdx.x == 0) a.kept[r] = (int32_t)s.n_kept;
+    uint64_t ck = 0;   // top-k threshold (use_k)
+    bool lds_k = false;
+    if (use_k) {
+        // whole top-k set in LDS (then top-p runs there too), or only the range
+        const bool all = use_p && rk.cnt_above + rk.n <= (uint64_t)kCap;
+        while (!all && rk.n > (uint32_t)kCap && rk.level < kLevels) {  // one more digit over the row
+            const int nb = 1 << dwidth<false>(rk.level);
+            clear_hist(sh, nb, false);
+            __syncthreads();
+            const int s = dshift<false>(rk.level);
+            for_row(row, V, vec, [&](float v, int e) __attribute__((always_inline)) {
+                const uint64_t c = composite(v, e);
+                if ((c & rk.pmask) == rk.prefix) atomicAdd(&sh.hc[(int)((c >> s) & (uint64_t)(nb - 1))], 1u);
+            });
+            __syncthreads();
+            fix_digit<false>(rk, walk<false>(rk, nb, false, k, 0.0f, sh));
+        }
+        // gather; when top-k is the last cut (or the whole set is gathered) also write the
+        // output of every token outside the list
+        if (t == 0) sh.s_n = 0;
+        __syncthreads();
+        const bool write = !use_p || all;
+        auto gather = [&](float v, int e) __attribute__((always_inline)) {
+            const uint64_t c = composite(v, e);
+            const bool take = all ? (c & rk.pmask) >= rk.prefix : (c & rk.pmask) == rk.prefix;
+            if (take) {
+                const uint32_t slot = atomicAdd(&sh.s_n, 1u);
+                if (slot < (uint32_t)kCap) sh.list[slot] = c;
+                return v;   // decided after the selection
+            }
+            return (!use_p && (c & rk.pmask) > rk.prefix) ? v : -INFINITY;
+        };
+        if (write)
+            map_row(row, orow, V, vec, gather);
+        else
+            for_row(row, V, vec, [&](float v, int e) __attribute__((always_inline)) { (void)gather(v, e); });
+        __syncthreads();
+        ck = finish_in_lds<false>(rk, false, k, 0.0f, 0.0f, 0.0, none, sh);
+        lds_k = all;
+    }
+    auto in_k = [&](uint64_t c) { return !use_k || c >= ck; };
+
+    uint64_t cstar = ck;
+    uint64_t n_kept = use_k ? (uint64_t)k : (uint64_t)V;
+    if (use_p) {
+        Range rp{0, 0, 0, 0, 0, 0, 0, 0, 0};
+        if (lds_k) {
+            // the whole top-k set is in the list: top-p there, from the first digit
+            cstar = finish_in_lds<true>(rp, true, 0, pp, M, kd, in_k, sh);
+        } else {
+            // first level over the row: weight bins
+            clear_hist(sh, kMassBins, true);
+            __syncthreads();
+            for_row(row, V, vec, [&](float v, int e) __attribute__((always_inline)) {
+                if (in_k(composite(v, e)))
+                    add_token(sh, kMassBins - 1 - (weight_fine(v, M, kb) >> 10), true, fix_weight(v, M, kd));
+            });
+            __syncthreads();
+            rp.wf = kMassBins - 1 - walk<true>(rp, kMassBins, true, 0, pp, sh);
+            rp.wl = 1;
+            if (rp.n > (uint32_t)kCap) {  // second level: the weight bin's 1024 sub-bins
+                clear_hist(sh, kMassBins, true);
+                __syncthreads();
+                for_row(row, V, vec, [&](float v, int e) __attribute__((always_inline)) {
+                    const int fine = weight_fine(v, M, kb);
+                    if ((fine >> 10) == rp.wf && in_k(composite(v, e)))
+                        add_token(sh, kMassBins - 1 - (fine & 1023), true, fix_weight(v, M, kd));
+                });
+                __syncthreads();
+                rp.wf = (rp.wf << 10) | (kMassBins - 1 - walk<true>(rp, kMassBins, false, 0, pp, sh));
+                rp.wl = 2;
+            }
+            while (rp.n > (uint32_t)kCap && rp.level < kLevels) {  // composite digits over the row, inside the weight bin
+                const int nb = 1 << dwidth<true>(rp.level);
+                clear_hist(sh, nb, true);
+                __syncthreads();
+                const int s = dshift<true>(rp.level);
+                for_row(row, V, vec, [&](float v, int e) __attribute__((always_inline)) {
+                    const uint64_t c = composite(v, e);
+                    if (in_k(c) && in_range(rp, c, weight_fine(v, M, kb)))
+                        add_token(sh, (int)((c >> s) & (uint64_t)(nb - 1)), true, fix_weight(v, M, kd));
+                });
+                __syncthreads();
+                fix_digit<true>(rp, walk<true>(rp, nb, false, 0, pp, sh));
+            }
+            // gather the range; write every other token's output
+            if (t == 0) sh.s_n = 0;
+            __syncthreads();
+            map_row(row, orow, V, vec, [&](float v, int e) __attribute__((always_inline)) {
+                const uint64_t c = composite(v, e);
+                if (!in_k(c)) return -INFINITY;
+                const int wb = weight_fine(v, M, kb);
+                if (in_range(rp, c, wb)) {
+                    const uint32_t slot = atomicAdd(&sh.s_n, 1u);
+                    if (slot < (uint32_t)kCap) sh.list[slot] = c;
+                    return v;   // decided after the selection
+                }
+                return before_range(rp, c, wb) ? v : -INFINITY;
+            });
+            __syncthreads();
+            // the range's remaining digits (the weight bin no longer matters inside the list)
+            cstar = finish_in_lds<true>(rp, false, 0, pp, M, kd, in_k, sh);
+        }
+        n_kept = rp.cnt_above + 1;
+    }
+
+    // the gathered tokens: kept iff C >= C*
+    const int n = min((int)sh.s_n, kCap);
+    for (int i = t; i < n; i += kTrThreads) {
+        const uint64_t c = sh.list[i];
+        const int id = comp_id(c);
+        orow[id] = c >= cstar ? row[id] : -INFINITY;
+    }
+    if (a.kept && t == 0) a.kept[r] = (int32_t)n_kept;
 }
 
 }  // namespace
@@ -332,13 +559,14 @@ extern "C" sv_status sv_truncate(const sv_trunc_desc *d, void *stream)
     if (d->R < 0 || d->V < 1) return SV_ERR_INVALID_ARG;
     if (!(d->temperature > 0.0f) || d->temperature == INFINITY) return SV_ERR_INVALID_ARG;
     if (d->top_p != d->top_p) return SV_ERR_INVALID_ARG;  // NaN
-    if (d->V > (1 << 24)) return SV_ERR_UNSUPPORTED;  // row masses stay below 2^86 units
+    if (d->V > (1 << kIdBits)) return SV_ERR_UNSUPPORTED;  // ids in 24 bits; masses below 2^86 units
     if (d->R == 0) return SV_OK;
     if (!d->logits || !d->out) return SV_ERR_INVALID_ARG;
     TruncArgs a;
     a.R = d->R;
     a.V = d->V;
     a.kd = 1.4426950408889634 / (double)d->temperature;
+    a.kb = (float)(kFinePerUnit * a.kd);
     a.top_k = d->top_k;
     a.top_p = d->top_p;
     a.k_rows = d->top_k_rows;

@@ -52,7 +52,7 @@ def _assert_trunc(lg, T, ref, out, kept, label):
 
 SHAPES = [(1, 64), (7, 64), (1000, 64), (1023, 64), (4096, 48), (5000, 48), (32000, 32), (50257, 16),
           (128256, 16)]
-SETTINGS = [(0, 0.9), (50, 1.0), (50, 0.9), (1, 1.0), (-1, 0.95), (0, 0.5), (0, 0.99), (1000, 0.8)]
+SETTINGS = [(0, 0.9), (50, 1.0), (50, 0.9), (1, 1.0), (-1, 0.95), (0, 0.5), (0, 0.99), (1000, 0.8), (3000, 0.9)]
 
 
 @pytest.mark.parametrize("V,R", SHAPES)
@@ -64,6 +64,18 @@ def test_truncate_parity(V, R, k, p):
         ref = oracle.truncate(lg, T, top_k=kk, top_p=p)
         out, kept = _gpu(lg, T, kk, p)
         _assert_trunc(lg, T, ref, out, kept, "V=%d k=%d p=%g T=%g" % (V, kk, p, T))
+
+
+@pytest.mark.parametrize("var", [0.01, 0.25, 1.0])
+def test_flat_rows(var):
+    """Nearly flat rows over 128256 tokens: the top-p cut lands where thousands of tokens
+    share a weight bin, so the selection takes its finer row levels before gathering."""
+    V, R = 128256, 16
+    lg = synth.logit_rows(11, R, V, var)
+    for k, p in [(0, 0.5), (0, 0.9), (0, 0.99), (20000, 0.9), (2040, 0.999)]:
+        ref = oracle.truncate(lg, 1.0, top_k=k, top_p=p)
+        out, kept = _gpu(lg, 1.0, k, p)
+        _assert_trunc(lg, 1.0, ref, out, kept, "flat var=%g k=%d p=%g" % (var, k, p))
 
 
 @pytest.mark.parametrize("V", [10, 1000, 4099, 128256])
