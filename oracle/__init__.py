@@ -86,6 +86,8 @@ def _typed(L):
     L.orc_tree_rrs.restype = i32
     L.orc_truncate.argtypes = [i32, i32, f32, i32, f32, P, P, P, P, P, P]
     L.orc_truncate.restype = i32
+    L.orc_penalize.argtypes = [i32, i32, i32, P, P, P, P, i32, P, i32, f32, f32, f32]
+    L.orc_penalize.restype = i32
     return L
 
 
@@ -322,6 +324,26 @@ def truncate(logits, temperature: float, top_k: int = 0, top_p: float = 1.0, top
     if st != 0:
         raise ValueError("orc_truncate status %d" % st)
     return dict(out=out.reshape(shape), kept=kept, flags=flags)
+
+
+def penalize(logits, history=None, hist_len=None, drafts=None, repetition: float = 1.0, frequency: float = 0.0,
+             presence: float = 0.0, handle=None):
+    """Repetition / frequency / presence penalties on logits [B][n_rows][V], row i's context
+    being the history then drafts[:, :i] (oracle.c orc_penalize) -> penalized copy."""
+    lg = _c(logits, np.float32)
+    B, n_rows, V = lg.shape
+    out = np.empty_like(lg)
+    hs = None if history is None else _c(history, np.int32).reshape(B, -1)
+    hl = None if hist_len is None else _c(hist_len, np.int32).reshape(B)
+    if hs is not None and hl is None:
+        hl = np.full(B, hs.shape[1], np.int32)
+    dr = None if drafts is None else _c(drafts, np.int32).reshape(B, -1)
+    st = (handle or lib()).orc_penalize(B, n_rows, V, _p(lg), _p(out), _p(hs), _p(hl),
+                                        0 if hs is None else hs.shape[1], _p(dr), 0 if dr is None else dr.shape[1],
+                                        float(repetition), float(frequency), float(presence))
+    if st != 0:
+        raise ValueError("orc_penalize status %d" % st)
+    return out
 
 
 RULE_TOKEN, RULE_BLOCK, RULE_GUMBEL = 0, 1, 2

@@ -845,3 +845,58 @@ ORC_EXPORT int32_t orc_truncate(int32_t R, int32_t V, float temperature, int32_t
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------- */
+/* Penalties on the logits, with the drafted prefix as context ([TB]        */
+/* section "When the target samples, keep a guess with probability p over   */
+/* q": p and q are after temperature, truncation and penalties; box "The    */
+/* speculative sampling rule", case "A processed target": they are applied  */
+/* with the drafted prefix as context).  The pages name penalties without   */
+/* defining them; the usual three are taken:                                */
+/*   Row i of sequence b (logits l, [B][n_rows][V]) has the context C =     */
+/*   history[b][0 .. hist_len[b]) followed by drafts[b][0 .. min(i,         */
+/*   n_drafts)) (drafts NULL: none).  Entries outside [0, V) are skipped,   */
+/*   hist_len is clamped into [0, hist_stride].  For every token t with     */
+/*   c = (occurrences of t in C) > 0, in fp64 and rounded once to fp32:     */
+/*     r = l_t > 0 ? l_t / theta : l_t * theta     (repetition, theta)      */
+/*     l_t <- (r - c * freq) - pres                 (frequency, presence)   */
+/*   Other tokens keep their logit.  out may be logits itself.              */
+/* ------------------------------------------------------------------------- */
+ORC_EXPORT int32_t orc_penalize(int32_t B, int32_t n_rows, int32_t V, const float *logits, float *out,
+                                const int32_t *history, const int32_t *hist_len, int32_t hist_stride,
+                                const int32_t *drafts, int32_t n_drafts, float repetition, float frequency,
+                                float presence)
+{
+    if (B < 0 || n_rows < 0 || V <= 0 || hist_stride < 0 || n_drafts < 0) return 1;
+    const double theta = (double)repetition, fr = (double)frequency, pr = (double)presence;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t row = 0; row < (int64_t)B * n_rows; ++row) {
+        const int32_t b = (int32_t)(row / n_rows), i = (int32_t)(row % n_rows);
+        const float *l = logits + row * V;
+        float *o = out + row * V;
+        int32_t *count = (int32_t *)calloc((size_t)V, sizeof(int32_t));
+        int32_t h = hist_len ? hist_len[b] : 0;
+        h = h < 0 ? 0 : (h > hist_stride ? hist_stride : h);
+        for (int32_t j = 0; j < h; ++j) {
+            const int32_t t = history[(int64_t)b * hist_stride + j];
+            if (t >= 0 && t < V) count[t] += 1;
+        }
+        const int32_t nd = drafts ? (i < n_drafts ? i : n_drafts) : 0;
+        for (int32_t j = 0; j < nd; ++j) {
+            const int32_t t = drafts[(int64_t)b * n_drafts + j];
+            if (t >= 0 && t < V) count[t] += 1;
+        }
+        for (int32_t t = 0; t < V; ++t) {
+            if (count[t] == 0) {
+                o[t] = l[t];
+                continue;
+            }
+            const double x = (double)l[t];
+            const double r = x > 0.0 ? x / theta : x * theta;
+            const double cf = (double)count[t] * fr;
+            o[t] = (float)((r - cf) - pr);
+        }
+        free(count);
+    }
+    return 0;
+}
