@@ -293,6 +293,33 @@ def time_truncate(sv, copies, tau, top_k, top_p, steps, sh, dev):
             "bound": "hbm (the row is read 2 to 3 times: selection passes, then a gather pass that writes)"}
 
 
+def time_penalize(sv, base, toks, hist_tokens, steps, sh, dev):
+    """sv_penalize on both models' rows of the round (two calls per step), each sequence with a
+    history of hist_tokens random tokens and its drafts as the rows' prefixes.  It runs in
+    place on a scratch copy of the rows (repeated calls compound the penalty, which changes
+    no cost).  Work is per history entry, not per logit."""
+    import torch
+    B = toks.shape[0]
+    V = base["target"].shape[-1]
+    rows = {k: base[k].clone() for k in ("target", "draft")}
+    g = torch.Generator(device="cpu").manual_seed(17)
+    hist = torch.randint(0, V, (B, hist_tokens), generator=g, dtype=torch.int32).to(dev)
+    descs = [sv.penalty_desc(rows[k], history=hist, draft_tokens=toks, repetition=1.2, frequency=0.3, presence=0.2)
+             for k in ("target", "draft")]
+    nb = max(sv.lib.sv_penalize_workspace(ctypes.byref(d)) for d in descs)
+    ws = torch.zeros(nb + 256, dtype=torch.uint8, device=dev)
+    pw = _aligned(ws)
+
+    def call(i):
+        for d in descs:
+            if sv.lib.sv_penalize(ctypes.byref(d), pw, nb, sh):
+                raise RuntimeError("penalize launch failed")
+    ms = median_event_ms(call, steps, sh)
+    nrows = sum(r.shape[0] * r.shape[1] for r in rows.values())
+    return {"kernel_ms": round(ms, 5), "rows": nrows, "history_tokens": hist_tokens, "launches": 6,
+            "bound": "latency (three dependent launches per call; reads history entries and a few KB of logits)"}
+
+
 def time_commit(sv, k, v, kv_off, prefix, acc_len, path, n_q, Hkv, D, kv_sh, kv_st, kv_sb, esize, steps, sh, dev):
     """sv_kv_commit on the given caches (new lengths to a separate buffer, so every call
     moves the same rows).  Algorithmic bytes: the moved K and V rows, read and written."""
@@ -476,6 +503,7 @@ def bench_chain(args, cfg, wl, dev, steps, warmup, cpu):
                                            att["kv_sh"], att["kv_st"], kv_sb, esz, steps, sh, dev),
             "truncate_top_k_top_p": time_truncate(sv, copies, tau, 50, 0.9, steps, sh, dev),
             "truncate_top_p": time_truncate(sv, copies, tau, 0, 0.9, steps, sh, dev),
+            "penalize_history_4096": time_penalize(sv, base, toks, 4096, steps, sh, dev),
         }
     if cpu:
         # the GPU's own outputs for the step on copy 0 (seed, step 0), for the parity verdict

@@ -70,9 +70,16 @@ class sv_trunc_desc(ctypes.Structure):
                 ("top_k_rows", _P), ("top_p_rows", _P), ("logits", _P), ("out", _P), ("kept", _P)]
 
 
+class sv_penalty_desc(ctypes.Structure):
+    _fields_ = [("B", _i32), ("n_rows", _i32), ("V", _i32), ("logits", _P), ("history", _P), ("hist_len", _P),
+                ("hist_stride", _i32), ("draft_tokens", _P), ("n_drafts", _i32), ("repetition", _f32),
+                ("frequency", _f32), ("presence", _f32)]
+
+
 EXPORTS = ("sv_build_tree_mask", "sv_verify_attention_workspace", "sv_verify_attention",
            "sv_spec_accept_workspace", "sv_spec_accept", "sv_spec_accept_static", "sv_tree_walk_workspace",
-           "sv_tree_walk", "sv_kv_commit", "sv_truncate", "sv_status_string")
+           "sv_tree_walk", "sv_kv_commit", "sv_truncate", "sv_penalize_workspace", "sv_penalize",
+           "sv_status_string")
 
 
 def _load():
@@ -100,6 +107,10 @@ def _load():
     L.sv_kv_commit.restype = ctypes.c_int
     L.sv_truncate.argtypes = [ctypes.POINTER(sv_trunc_desc), _P]
     L.sv_truncate.restype = ctypes.c_int
+    L.sv_penalize_workspace.argtypes = [ctypes.POINTER(sv_penalty_desc)]
+    L.sv_penalize_workspace.restype = ctypes.c_size_t
+    L.sv_penalize.argtypes = [ctypes.POINTER(sv_penalty_desc), _P, ctypes.c_size_t, _P]
+    L.sv_penalize.restype = ctypes.c_int
     L.sv_status_string.argtypes = [ctypes.c_int]
     L.sv_status_string.restype = ctypes.c_char_p
     return L
@@ -383,3 +394,37 @@ def sv_truncate(logits, *, temperature: float, top_k: int = 0, top_p: float = 1.
                    kept=kept)
     _check(lib.sv_truncate(ctypes.byref(d), _stream(x.device)), "sv_truncate")
     return out.reshape(logits.shape), kept
+
+
+# --------------------------------------------------------------------------- #
+def penalty_desc(logits, *, history=None, hist_len=None, draft_tokens=None, repetition: float = 1.0,
+                 frequency: float = 0.0, presence: float = 0.0) -> sv_penalty_desc:
+    d = sv_penalty_desc()
+    d.B, d.n_rows, d.V = logits.shape
+    d.logits = logits.data_ptr()
+    d.history = None if history is None else history.data_ptr()
+    d.hist_len = None if hist_len is None else hist_len.data_ptr()
+    d.hist_stride = 0 if history is None else history.shape[-1]
+    d.draft_tokens = None if draft_tokens is None else draft_tokens.data_ptr()
+    d.n_drafts = 0 if draft_tokens is None else draft_tokens.shape[-1]
+    d.repetition, d.frequency, d.presence = float(repetition), float(frequency), float(presence)
+    return d
+
+
+def sv_penalize(logits, *, history=None, hist_len=None, draft_tokens=None, repetition: float = 1.0,
+                frequency: float = 0.0, presence: float = 0.0):
+    """Penalties on fp32 logits [B][n_rows][V] in place (which must be contiguous): row i of
+    sequence b counts history[b][:hist_len[b]] and draft_tokens[b][:i].  Returns logits."""
+    _need_cuda(logits, history, hist_len, draft_tokens)
+    if logits.dtype != torch.float32 or logits.dim() != 3 or not logits.is_contiguous():
+        raise ValueError("sv_penalize takes contiguous fp32 logits [B][n_rows][V]")
+    B = logits.shape[0]
+    hs = None if history is None else history.to(torch.int32).contiguous().reshape(B, -1)
+    hl = None if hist_len is None else hist_len.to(torch.int32).contiguous().reshape(B)
+    dr = None if draft_tokens is None else draft_tokens.to(torch.int32).contiguous().reshape(B, -1)
+    d = penalty_desc(logits, history=hs, hist_len=hl, draft_tokens=dr, repetition=repetition, frequency=frequency,
+                     presence=presence)
+    nb = lib.sv_penalize_workspace(ctypes.byref(d))
+    ws = workspace(nb, logits.device)
+    _check(lib.sv_penalize(ctypes.byref(d), _ptr(ws), nb, _stream(logits.device)), "sv_penalize")
+    return logits

@@ -1,0 +1,184 @@
+// penalty.hip -- repetition, frequency and presence penalties on logit rows, with the drafted
+// prefix as context.
+//
+// Sources: "Speculative decoding" (Zero to Frontier textbook, ch. 20, section 20.5), section
+// "When the target samples, keep a guess with probability p over q" (p and q are the
+// distributions each model really samples from, after temperature, truncation and
+// penalties); box "The speculative sampling rule", special case "A processed target" (the
+// target's penalties are applied with the drafted prefix as context).  The pages do not
+// define the penalties; the usual three are taken: a token seen c > 0 times in the context
+// has its logit l replaced by (r - c * frequency) - presence, r = l / theta if l > 0 else
+// l * theta, in fp64 and rounded once to fp32.  Row i of a sequence has as context its
+// history followed by its first i drafted tokens.
+//
+// Three launches.  The history is counted once per sequence into a per-sequence array over
+// the vocabulary (workspace), and each sequence's distinct tokens are listed (the entry whose
+// increment finds the count at zero appends its token).  Then one block per (sequence, chunk
+// of that list) takes each listed token's count once and penalizes the token in every row
+// of the sequence, adding row by row the drafts before it; drafted tokens absent from the
+// history are penalized by the sequence's first block.  Every token of a row is written by
+// exactly one thread.  A last launch clears the counts the history set, the lists and their
+// lengths, leaving the workspace zero.  Work is proportional to the distinct tokens of the
+// history times the rows, not to the vocabulary.
+#include "sv_common.h"
+
+namespace {
+
+using namespace sv;
+
+constexpr int kPenThreads = 256;
+constexpr int kPenChunk = 4 * kPenThreads;   // history entries per block
+constexpr int kMaxPenDrafts = 64;
+
+struct PenArgs {
+    int B, n_rows, V;
+    float *logits;
+    const int32_t *hist;
+    const int32_t *hist_len;
+    int hist_stride;
+    const int32_t *drafts;
+    int n_drafts;
+    double theta, fr, pr;
+    int32_t *count;   // [B][V]
+    int32_t *list;    // [B][hist_stride]: the sequence's distinct tokens, nlist[b] of them
+    int32_t *nlist;   // [B] (in the counter region)
+};
+
+__device__ __forceinline__ int hist_len_of(const PenArgs &a, int b)
+{
+    const int h = a.hist_len ? a.hist_len[b] : a.hist_stride;
+    return min(max(h, 0), a.hist_stride);
+}
+
+// The penalized logit: these fp64 operations in this order, none fused.
+__device__ __forceinline__ float penalized(float l, int c, const PenArgs &a)
+{
+#pragma clang fp contract(off)
+    const double x = (double)l;
+    const double r = x > 0.0 ? x / a.theta : x * a.theta;
+    const double cf = (double)c * a.fr;
+    return (float)((r - cf) - a.pr);
+}
+
+__global__ __launch_bounds__(kPenThreads) void pen_count_kernel(PenArgs a)
+{
+    const int b = blockIdx.x;
+    const int h = hist_len_of(a, b);
+    const int64_t off = (int64_t)b * a.V;
+    for (int j = blockIdx.y * kPenChunk + threadIdx.x; j < min(h, (int)(blockIdx.y + 1) * kPenChunk);
+         j += kPenThreads) {
+        const int t = a.hist[(int64_t)b * a.hist_stride + j];
+        if (t < 0 || t >= a.V) continue;
+        if (atomicAdd(&a.count[off + t], 1) == 0) a.list[(int64_t)b * a.hist_stride + atomicAdd(&a.nlist[b], 1)] = t;
+    }
+}
+
+__global__ __launch_bounds__(kPenThreads) void pen_apply_kernel(PenArgs a)
+{
+    __shared__ int sx[kMaxPenDrafts];
+    const int b = blockIdx.x;
+    const int nd = a.drafts ? a.n_drafts : 0;
+    if ((int)threadIdx.x < nd) sx[threadIdx.x] = a.drafts[(int64_t)b * a.n_drafts + threadIdx.x];
+    __syncthreads();
+    float *l0 = a.logits + (int64_t)b * a.n_rows * a.V;
+    const int64_t off = (int64_t)b * a.V;
+    // token t with history count c0 in every row: row i adds the drafts before it
+    auto apply = [&](int t, int c0) {
+        int c = c0;
+        for (int i = 0; i < a.n_rows; ++i) {
+            if (c > 0) l0[(int64_t)i * a.V + t] = penalized(l0[(int64_t)i * a.V + t], c, a);
+            if (i < nd) c += sx[i] == t;
+        }
+    };
+    const int n = a.nlist ? a.nlist[b] : 0;
+    for (int j = blockIdx.y * kPenChunk + threadIdx.x; j < min(n, (int)(blockIdx.y + 1) * kPenChunk);
+         j += kPenThreads) {
+        const int t = a.list[(int64_t)b * a.hist_stride + j];
+        apply(t, a.count[off + t]);
+    }
+    if (blockIdx.y == 0 && (int)threadIdx.x < nd) {
+        const int j = threadIdx.x;
+        const int t = sx[j];
+        bool first = t >= 0 && t < a.V;
+        for (int k = 0; k < j && first; ++k) first = sx[k] != t;
+        if (first && a.count[off + t] == 0) apply(t, 0);
+    }
+}
+
+__global__ __launch_bounds__(kPenThreads) void pen_clear_kernel(PenArgs a)
+{
+    const int b = blockIdx.x;
+    const int h = hist_len_of(a, b);
+    const int64_t off = (int64_t)b * a.V;
+    for (int j = blockIdx.y * kPenChunk + threadIdx.x; j < min(h, (int)(blockIdx.y + 1) * kPenChunk);
+         j += kPenThreads) {
+        a.list[(int64_t)b * a.hist_stride + j] = 0;   // (the list has at most h entries)
+        const int t = a.hist[(int64_t)b * a.hist_stride + j];
+        if (t < 0 || t >= a.V) continue;
+        a.count[off + t] = 0;
+    }
+    if (blockIdx.y == 0 && threadIdx.x == 0) a.nlist[b] = 0;
+}
+
+bool pen_shape_ok(const sv_penalty_desc *d)
+{
+    if (!d || d->B < 0 || d->n_rows < 0 || d->V < 1 || d->hist_stride < 0 || d->n_drafts < 0) return false;
+    if (!(d->repetition > 0.0f) || d->repetition == INFINITY) return false;
+    if (!(d->frequency == d->frequency) || d->frequency == INFINITY || d->frequency == -INFINITY) return false;
+    if (!(d->presence == d->presence) || d->presence == INFINITY || d->presence == -INFINITY) return false;
+    return true;
+}
+
+size_t pen_count_bytes(const sv_penalty_desc *d)
+{
+    return ((size_t)d->B * (size_t)d->V * sizeof(int32_t) + 255) & ~(size_t)255;
+}
+
+size_t pen_bytes(const sv_penalty_desc *d)
+{
+    return kCounterBytes + pen_count_bytes(d) + (size_t)d->B * (size_t)d->hist_stride * sizeof(int32_t);
+}
+
+}  // namespace
+
+extern "C" size_t sv_penalize_workspace(const sv_penalty_desc *d)
+{
+    if (!pen_shape_ok(d) || d->n_drafts > kMaxPenDrafts) return 0;
+    return pen_bytes(d);
+}
+
+extern "C" sv_status sv_penalize(const sv_penalty_desc *d, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!pen_shape_ok(d)) return SV_ERR_INVALID_ARG;
+    if (d->n_drafts > kMaxPenDrafts) return SV_ERR_UNSUPPORTED;
+    if ((int64_t)d->B * d->n_rows > 0x7fffffff || d->B > kMaxCounters) return SV_ERR_UNSUPPORTED;
+    if ((int64_t)d->B * d->n_rows == 0) return SV_OK;
+    if (!d->logits) return SV_ERR_INVALID_ARG;
+    const bool hist = d->history && d->hist_stride > 0;
+    if (!workspace || workspace_bytes < pen_bytes(d)) return SV_ERR_WORKSPACE;
+    PenArgs a;
+    a.B = d->B;
+    a.n_rows = d->n_rows;
+    a.V = d->V;
+    a.logits = d->logits;
+    a.hist = d->history;
+    a.hist_len = d->hist_len;
+    a.hist_stride = hist ? d->hist_stride : 0;
+    a.drafts = d->draft_tokens;
+    a.n_drafts = d->draft_tokens ? d->n_drafts : 0;
+    a.theta = (double)d->repetition;
+    a.fr = (double)d->frequency;
+    a.pr = (double)d->presence;
+    char *ws = static_cast<char *>(workspace);
+    a.nlist = hist ? reinterpret_cast<int32_t *>(ws) : nullptr;
+    a.count = reinterpret_cast<int32_t *>(ws + kCounterBytes);
+    a.list = reinterpret_cast<int32_t *>(ws + kCounterBytes + pen_count_bytes(d));
+    hipStream_t s = (hipStream_t)stream;
+    const unsigned nchunk = hist ? (unsigned)((d->hist_stride + kPenChunk - 1) / kPenChunk) : 1u;
+    if (nchunk > 65535) return SV_ERR_UNSUPPORTED;
+    (void)hipGetLastError();
+    if (hist) hipLaunchKernelGGL(pen_count_kernel, dim3((unsigned)d->B, nchunk), dim3(kPenThreads), 0, s, a);
+    hipLaunchKernelGGL(pen_apply_kernel, dim3((unsigned)d->B, nchunk), dim3(kPenThreads), 0, s, a);
+    if (hist) hipLaunchKernelGGL(pen_clear_kernel, dim3((unsigned)d->B, nchunk), dim3(kPenThreads), 0, s, a);
+    return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
+}

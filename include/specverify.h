@@ -422,6 +422,47 @@ typedef struct sv_trunc_desc {
 
 SV_API sv_status sv_truncate(const sv_trunc_desc *desc, void *stream);
 
+/* ---------------------------------------------------------------------------------- */
+/* sv_penalize -- repetition, frequency and presence penalties on logit rows, in place,   */
+/* with the drafted prefix as context ([TB] section "When the target samples, keep a     */
+/* guess with probability p over q": p and q are after temperature, truncation and       */
+/* penalties; box "The speculative sampling rule", case "A processed target": they are   */
+/* applied with the drafted prefix as context).  The pages do not define the penalties;  */
+/* the usual three are taken.  Row i of sequence b has the context C = history[b][0 ..   */
+/* hist_len[b]) followed by draft_tokens[b][0 .. min(i, n_drafts)).  For every token t   */
+/* seen c > 0 times in C, with l its logit, in fp64 (no fused operations) and rounded    */
+/* once to fp32:                                                                          */
+/*     r = l > 0 ? l / repetition : l * repetition;   l <- (r - c * frequency) - presence  */
+/* Other logits are not touched.  Use it on the target rows (n_rows = gamma + 1) and the  */
+/* draft rows (n_rows = gamma) with the same drafts, before temperature and sv_truncate. */
+/*   logits       device fp32 [B][n_rows][V], penalized in place                         */
+/*   history      optional device int32 [B][hist_stride]: each sequence's tokens so far  */
+/*   hist_len     optional device int32 [B]: valid entries (clamped into [0, hist_stride]);*/
+/*                NULL: hist_stride each                                                   */
+/*   draft_tokens optional device int32 [B][n_drafts]                                     */
+/*   Entries outside [0, V) are skipped.  repetition 1, frequency 0, presence 0: no change. */
+/* Work is proportional to the history's distinct tokens times the rows, not to V (the   */
+/* workspace holds, after the counter region, a count over the vocabulary and a list of  */
+/* distinct tokens per sequence: 4 V + 4 hist_stride bytes each).                        */
+/* Errors: B, n_rows or hist_stride negative, V < 1, repetition not in (0, inf),          */
+/*   frequency or presence not finite, or (rows > 0) a null logits -> SV_ERR_INVALID_ARG; */
+/*   n_drafts > 64, B > 32768 or more than 65535 chunks of 1024 history entries ->        */
+/*   SV_ERR_UNSUPPORTED.  After SV_ERR_HIP zero the workspace again before reusing it.    */
+/* ---------------------------------------------------------------------------------- */
+typedef struct sv_penalty_desc {
+    int32_t B, n_rows, V;
+    float *logits;
+    const int32_t *history;
+    const int32_t *hist_len;
+    int32_t hist_stride;
+    const int32_t *draft_tokens;
+    int32_t n_drafts;
+    float repetition, frequency, presence;
+} sv_penalty_desc;
+
+SV_API size_t sv_penalize_workspace(const sv_penalty_desc *desc);
+SV_API sv_status sv_penalize(const sv_penalty_desc *desc, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Human-readable name of a status code (static storage). */
 SV_API const char *sv_status_string(sv_status status);
 

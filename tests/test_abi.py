@@ -192,7 +192,7 @@ def test_struct_layouts_match_the_header(tmp_path):
         pytest.skip("no C compiler")
     structs = {"sv_philox": sv.sv_philox, "sv_attn_desc": sv.sv_attn_desc, "sv_accept_desc": sv.sv_accept_desc,
                "sv_walk_desc": sv.sv_walk_desc, "sv_commit_desc": sv.sv_commit_desc,
-               "sv_trunc_desc": sv.sv_trunc_desc}
+               "sv_trunc_desc": sv.sv_trunc_desc, "sv_penalty_desc": sv.sv_penalty_desc}
     lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "specverify.h"', "int main(void) {"]
     for name, cls in structs.items():
         lines.append('printf("%s sizeof %%zu\\n", sizeof(%s));' % (name, name))
