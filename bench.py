@@ -316,8 +316,9 @@ def time_penalize(sv, base, toks, hist_tokens, steps, sh, dev):
                 raise RuntimeError("penalize launch failed")
     ms = median_event_ms(call, steps, sh)
     nrows = sum(r.shape[0] * r.shape[1] for r in rows.values())
-    return {"kernel_ms": round(ms, 5), "rows": nrows, "history_tokens": hist_tokens, "launches": 6,
-            "bound": "latency (three dependent launches per call; reads history entries and a few KB of logits)"}
+    return {"kernel_ms": round(ms, 5), "rows": nrows, "history_tokens": hist_tokens, "launches": 8,
+            "bound": "scattered logits (four dependent launches per call; about one read and write of a "
+                     "logit per distinct history token per row)"}
 
 
 def time_commit(sv, k, v, kv_off, prefix, acc_len, path, n_q, Hkv, D, kv_sh, kv_st, kv_sb, esize, steps, sh, dev):

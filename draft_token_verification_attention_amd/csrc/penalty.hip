@@ -11,15 +11,17 @@
 // l * theta, in fp64 and rounded once to fp32.  Row i of a sequence has as context its
 // history followed by its first i drafted tokens.
 //
-// Three launches.  The history is counted once per sequence into a per-sequence array over
-// the vocabulary (workspace), and each sequence's distinct tokens are listed (the entry whose
-// increment finds the count at zero appends its token).  Then one block per (sequence, chunk
-// of that list) takes each listed token's count once and penalizes the token in every row
-// of the sequence, adding row by row the drafts before it; drafted tokens absent from the
-// history are penalized by the sequence's first block.  Every token of a row is written by
-// exactly one thread.  A last launch clears the counts the history set, the lists and their
-// lengths, leaving the workspace zero.  Work is proportional to the distinct tokens of the
-// history times the rows, not to the vocabulary.
+// Four launches.  The workspace after its counter region may hold anything (other entry
+// points keep partial results there), so the first launch zeroes the count of every token
+// the call will read (history and drafts).  The second counts the history into that
+// per-sequence array over the vocabulary and lists each sequence's distinct tokens (the
+// entry whose increment finds the count at zero appends its token; the list length lives in
+// the counter region).  Then one block per (sequence, chunk of that list) takes each listed
+// token's count once and penalizes the token in every row of the sequence, adding row by row
+// the drafts before it; drafted tokens absent from the history are penalized by the
+// sequence's first block.  Every token of a row is written by exactly one thread.  The last
+// launch returns the list lengths to zero.  Work is proportional to the distinct tokens of
+// the history times the rows, not to the vocabulary.
 #include "sv_common.h"
 
 namespace {
@@ -58,6 +60,22 @@ __device__ __forceinline__ float penalized(float l, int c, const PenArgs &a)
     const double r = x > 0.0 ? x / a.theta : x * a.theta;
     const double cf = (double)c * a.fr;
     return (float)((r - cf) - a.pr);
+}
+
+__global__ __launch_bounds__(kPenThreads) void pen_zero_kernel(PenArgs a)
+{
+    const int b = blockIdx.x;
+    const int h = hist_len_of(a, b);
+    const int64_t off = (int64_t)b * a.V;
+    for (int j = blockIdx.y * kPenChunk + threadIdx.x; j < min(h, (int)(blockIdx.y + 1) * kPenChunk);
+         j += kPenThreads) {
+        const int t = a.hist[(int64_t)b * a.hist_stride + j];
+        if (t >= 0 && t < a.V) a.count[off + t] = 0;
+    }
+    if (blockIdx.y == 0 && a.drafts && (int)threadIdx.x < a.n_drafts) {
+        const int t = a.drafts[(int64_t)b * a.n_drafts + threadIdx.x];
+        if (t >= 0 && t < a.V) a.count[off + t] = 0;
+    }
 }
 
 __global__ __launch_bounds__(kPenThreads) void pen_count_kernel(PenArgs a)
@@ -105,19 +123,10 @@ __global__ __launch_bounds__(kPenThreads) void pen_apply_kernel(PenArgs a)
     }
 }
 
-__global__ __launch_bounds__(kPenThreads) void pen_clear_kernel(PenArgs a)
+__global__ void pen_clear_kernel(PenArgs a)
 {
-    const int b = blockIdx.x;
-    const int h = hist_len_of(a, b);
-    const int64_t off = (int64_t)b * a.V;
-    for (int j = blockIdx.y * kPenChunk + threadIdx.x; j < min(h, (int)(blockIdx.y + 1) * kPenChunk);
-         j += kPenThreads) {
-        a.list[(int64_t)b * a.hist_stride + j] = 0;   // (the list has at most h entries)
-        const int t = a.hist[(int64_t)b * a.hist_stride + j];
-        if (t < 0 || t >= a.V) continue;
-        a.count[off + t] = 0;
-    }
-    if (blockIdx.y == 0 && threadIdx.x == 0) a.nlist[b] = 0;
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b < a.B) a.nlist[b] = 0;
 }
 
 bool pen_shape_ok(const sv_penalty_desc *d)
@@ -177,8 +186,9 @@ extern "C" sv_status sv_penalize(const sv_penalty_desc *d, void *workspace, size
     const unsigned nchunk = hist ? (unsigned)((d->hist_stride + kPenChunk - 1) / kPenChunk) : 1u;
     if (nchunk > 65535) return SV_ERR_UNSUPPORTED;
     (void)hipGetLastError();
+    hipLaunchKernelGGL(pen_zero_kernel, dim3((unsigned)d->B, nchunk), dim3(kPenThreads), 0, s, a);
     if (hist) hipLaunchKernelGGL(pen_count_kernel, dim3((unsigned)d->B, nchunk), dim3(kPenThreads), 0, s, a);
     hipLaunchKernelGGL(pen_apply_kernel, dim3((unsigned)d->B, nchunk), dim3(kPenThreads), 0, s, a);
-    if (hist) hipLaunchKernelGGL(pen_clear_kernel, dim3((unsigned)d->B, nchunk), dim3(kPenThreads), 0, s, a);
+    if (hist) hipLaunchKernelGGL(pen_clear_kernel, dim3((unsigned)((d->B + 255) / 256)), dim3(256), 0, s, a);
     return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
 }

@@ -69,13 +69,16 @@ def test_history_lengths_and_draft_rows():
 
 
 def test_one_workspace_across_calls():
-    """sv_penalize leaves its whole workspace zero: calls of other shapes on one explicit
-    workspace match the oracle, and the workspace reads zero after each."""
+    """The workspace contract: whatever lies after the counter region (other entry points
+    leave partial results there; here, garbage written before every call) does not change
+    the result, and the counter region reads zero after each call.  Calls of other shapes
+    share one explicit workspace."""
     import ctypes
     pen = dict(repetition=1.4, frequency=0.2, presence=0.1)
     ws = torch.zeros(8 << 20, dtype=torch.uint8, device="cuda")
     for seed, B, V, H in [(1, 5, 4000, 800), (2, 5, 4000, 3000), (3, 3, 9000, 2500), (4, 7, 1500, 0),
                           (5, 2, 20000, 5000), (6, 5, 4000, 2048)]:
+        ws[128 * 1024:].random_(0, 256)
         lg, hist, drafts = _inputs(seed, B, 4, V, H, 3, spread=V)
         ref = oracle.penalize(lg, history=hist, drafts=drafts, **pen)
         x = dev_array(lg)
@@ -88,7 +91,7 @@ def test_one_workspace_across_calls():
         assert st == 0
         torch.cuda.synchronize()
         assert np.array_equal(x.cpu().numpy().view(np.uint32), ref.view(np.uint32)), seed
-        assert int(torch.count_nonzero(ws).item()) == 0, seed
+        assert int(torch.count_nonzero(ws[:128 * 1024]).item()) == 0, seed
 
 
 def test_off_and_empty():
