@@ -30,7 +30,11 @@ namespace {
 using namespace sv;
 typedef unsigned __int128 u128;
 
-constexpr int kTrThreads = kRowThreads;   // 256
+// Threads per block: 1024 while there are at most as many rows as compute units (a row then
+// has a compute unit to itself), else 256 (three rows per compute unit).  Measured on rows of
+// 128256 logits, top-p 0.9: one row 203 -> 121 us, 256 rows 232 -> 152 us; 320 rows 280 us
+// either way, and top-k 50 then top-p 0.9 on 320 rows 135 us with 256 threads, 164 with 1024.
+constexpr int kTrThreadsMany = 256, kTrThreadsFew = 1024;
 constexpr int kBins = 2048;               // count histogram bins (digits of at most 11 bits)
 constexpr int kMassBins = 1024;           // mass histogram bins (digits of at most 10 bits)
 constexpr int kCap = 2048;                // candidates gathered into LDS
@@ -106,10 +110,10 @@ __device__ __forceinline__ int weight_fine(float v, float M, float kb)
 
 // f(value, token) over the row: each thread takes 4 consecutive tokens of every 1024, and
 // issues kUnroll 16-byte loads before using them.
-template <typename F>
+template <int NT, typename F>
 __device__ __forceinline__ void for_row(const float *row, int V, bool vec, F f)
 {
-    constexpr int kStep = 4 * kTrThreads;
+    constexpr int kStep = 4 * NT;
     const int t4 = 4 * (int)threadIdx.x;
     if (vec) {
         int e0 = 0;
@@ -142,10 +146,10 @@ __device__ __forceinline__ void for_row(const float *row, int V, bool vec, F f)
 }
 
 // out[e] = g(in[e], e) over the row, with the loads of for_row and 16-byte stores.
-template <typename G>
+template <int NT, typename G>
 __device__ __forceinline__ void map_row(const float *row, float *orow, int V, bool vec, G g)
 {
-    constexpr int kStep = 4 * kTrThreads;
+    constexpr int kStep = 4 * NT;
     const int t4 = 4 * (int)threadIdx.x;
     if (vec) {
         int e0 = 0;
@@ -183,39 +187,41 @@ __device__ __forceinline__ void map_row(const float *row, float *orow, int V, bo
 
 // Inclusive scan of one value per thread over the block, in thread order (Hillis-Steele in
 // LDS, exact for integers).  *total gets the block's total.
-template <typename T>
+template <typename T, int NT>
 __device__ __forceinline__ T block_scan(T x, T *s, T *total)
 {
     const int t = threadIdx.x;
     __syncthreads();
     s[t] = x;
     __syncthreads();
-    for (int off = 1; off < kTrThreads; off <<= 1) {
+    for (int off = 1; off < NT; off <<= 1) {
         const T v = t >= off ? s[t - off] : (T)0;
         __syncthreads();
         s[t] += v;
         __syncthreads();
     }
     const T r = s[t];
-    *total = s[kTrThreads - 1];
+    *total = s[NT - 1];
     __syncthreads();
     return r;
 }
 
+template <int NT>
 struct TrShared {
     uint32_t hc[kBins];         // tokens per bin
     uint64_t hw_hi[kMassBins];  // sum of (floor(w 2^62) >> 30) per bin (top-p)
     uint64_t hw_lo[kMassBins];  // sum of the low 30 bits
     uint64_t list[kCap];        // composites of the gathered tokens
-    u128 scan[kTrThreads];
+    u128 scan[NT];
     uint32_t s_bin, s_n;
     u128 s_above;               // the walked quantity of the bins before the crossing one
     uint64_t s_cnt_above;
     uint64_t s_found;
-    float s_max[kTrThreads / kWave];
+    float s_max[NT / kWave];
 };
 
-__device__ __forceinline__ u128 bin_mass(const TrShared &sh, int bin)
+template <int NT>
+__device__ __forceinline__ u128 bin_mass(const TrShared<NT> &sh, int bin)
 {
     return ((u128)sh.hw_hi[bin] << kLoBits) + sh.hw_lo[bin];
 }
@@ -265,9 +271,10 @@ __device__ __forceinline__ bool before_range(const Range &rg, uint64_t c, int fi
     return (c & rg.pmask) > rg.prefix;
 }
 
-__device__ __forceinline__ void clear_hist(TrShared &sh, int nb, bool mass)
+template <int NT>
+__device__ __forceinline__ void clear_hist(TrShared<NT> &sh, int nb, bool mass)
 {
-    for (int i = threadIdx.x; i < nb; i += kTrThreads) {
+    for (int i = threadIdx.x; i < nb; i += NT) {
         sh.hc[i] = 0;
         if (mass) {
             sh.hw_hi[i] = 0;
@@ -281,7 +288,8 @@ __device__ __forceinline__ void clear_hist(TrShared &sh, int nb, bool mass)
     }
 }
 
-__device__ __forceinline__ void add_token(TrShared &sh, int bin, bool mass, uint64_t f)
+template <int NT>
+__device__ __forceinline__ void add_token(TrShared<NT> &sh, int bin, bool mass, uint64_t f)
 {
     atomicAdd(&sh.hc[bin], 1u);
     if (mass) {
@@ -293,22 +301,23 @@ __device__ __forceinline__ void add_token(TrShared &sh, int bin, bool mass, uint
 // Walk the histogram (bins nb-1 down to 0 = the order): the bin where the running quantity
 // reaches the target.  Sets the range's target on the first walk, moves `above` and
 // `cnt_above` past the bins before it, and returns it (rg.n = its tokens).
-template <bool MASS>
-__device__ __forceinline__ int walk(Range &rg, int nb, bool first, int k, float pp, TrShared &sh)
+template <bool MASS, int NT>
+__device__ __forceinline__ int walk(Range &rg, int nb, bool first, int k, float pp, TrShared<NT> &sh)
 {
     const int t = threadIdx.x;
-    const int G = nb / kTrThreads;
+    const int G = (nb + NT - 1) / NT;   // bins per thread (threads past the bins own none)
     uint64_t c_loc = 0;
     u128 w_loc = 0;
     for (int j = 0; j < G; ++j) {
         const int bin = nb - 1 - G * t - j;
+        if (bin < 0) break;
         c_loc += sh.hc[bin];
         w_loc += MASS ? bin_mass(sh, bin) : (u128)sh.hc[bin];
     }
     u128 w_tot;
-    const u128 w_pre = block_scan<u128>(w_loc, sh.scan, &w_tot) - w_loc;
+    const u128 w_pre = block_scan<u128, NT>(w_loc, sh.scan, &w_tot) - w_loc;
     u128 c_tot;
-    const uint64_t c_pre = MASS ? (uint64_t)(block_scan<u128>(c_loc, sh.scan, &c_tot) - c_loc) : (uint64_t)w_pre;
+    const uint64_t c_pre = MASS ? (uint64_t)(block_scan<u128, NT>(c_loc, sh.scan, &c_tot) - c_loc) : (uint64_t)w_pre;
     if (first) {
         rg.target = MASS ? mass_target(pp, w_tot) : (u128)k;
         if (rg.target < 1) rg.target = 1;   // at least one token
@@ -321,6 +330,7 @@ __device__ __forceinline__ int walk(Range &rg, int nb, bool first, int k, float 
         uint64_t cc = c_pre;
         for (int j = 0; j < G; ++j) {
             const int bin = nb - 1 - G * t - j;
+            if (bin < 0) break;
             const u128 w = MASS ? bin_mass(sh, bin) : (u128)sh.hc[bin];
             if (sh.hc[bin] > 0 && c + w >= need) {
                 sh.s_bin = (uint32_t)bin;
@@ -352,30 +362,30 @@ __device__ __forceinline__ void fix_digit(Range &rg, int bin)
 
 // Finish a selection on the gathered list (sh.list[0 .. sh.s_n), a superset of the range):
 // composite digits until one token is left.  Returns its composite.
-template <bool MASS, typename Filt>
+template <bool MASS, int NT, typename Filt>
 __device__ __forceinline__ uint64_t finish_in_lds(Range &rg, bool first, int k, float pp, float M, double kd, Filt filt,
-                                  TrShared &sh)
+                                  TrShared<NT> &sh)
 {
     const int n = min((int)sh.s_n, kCap);
     while ((first || rg.n > 1) && rg.level < kLevels) {
         const int nb = 1 << dwidth<MASS>(rg.level);
-        clear_hist(sh, nb, MASS);
+        clear_hist<NT>(sh, nb, MASS);
         __syncthreads();
         const int s = dshift<MASS>(rg.level);
-        for (int i = threadIdx.x; i < n; i += kTrThreads) {
+        for (int i = threadIdx.x; i < n; i += NT) {
             const uint64_t c = sh.list[i];
             if (filt(c) && (c & rg.pmask) == rg.prefix)
                 add_token(sh, (int)((c >> s) & (uint64_t)(nb - 1)), MASS, MASS ? fix_weight(comp_value(c), M, kd) : 0);
         }
         __syncthreads();
-        fix_digit<MASS>(rg, walk<MASS>(rg, nb, first, k, pp, sh));
+        fix_digit<MASS>(rg, walk<MASS, NT>(rg, nb, first, k, pp, sh));
         first = false;
         if (rg.level == kLevels) break;   // every digit fixed: rg.prefix is the token
     }
     // the one token of the range
     if (threadIdx.x == 0) sh.s_found = 0;
     __syncthreads();
-    for (int i = threadIdx.x; i < n; i += kTrThreads) {
+    for (int i = threadIdx.x; i < n; i += NT) {
         const uint64_t c = sh.list[i];
         if (filt(c) && (c & rg.pmask) == rg.prefix) sh.s_found = c;
     }
@@ -385,9 +395,24 @@ __device__ __forceinline__ uint64_t finish_in_lds(Range &rg, bool first, int k, 
     return found;
 }
 
-__global__ __launch_bounds__(kTrThreads, 3) void truncate_kernel(TruncArgs a)
+// Largest value over the block.
+template <int NT>
+__device__ __forceinline__ float blk_max(float v, float *scratch)
 {
-    __shared__ TrShared sh;
+    v = wave_max(v);
+    __syncthreads();
+    if ((threadIdx.x % kWave) == 0) scratch[threadIdx.x / kWave] = v;
+    __syncthreads();
+    float r = scratch[0];
+#pragma unroll
+    for (int i = 1; i < NT / kWave; ++i) r = fmaxf(r, scratch[i]);
+    return r;
+}
+
+template <int NT>
+__global__ __launch_bounds__(NT, NT == kTrThreadsMany ? 3 : 4) void truncate_kernel(TruncArgs a)
+{
+    __shared__ TrShared<NT> sh;
     const int r = blockIdx.x;
     const int t = threadIdx.x;
     const float *row = a.in + (int64_t)r * a.V;
@@ -399,7 +424,7 @@ __global__ __launch_bounds__(kTrThreads, 3) void truncate_kernel(TruncArgs a)
     const bool use_k = k > 0 && k < V, want_p = pp < 1.0f;
 
     if (!use_k && !want_p) {  // nothing to cut
-        if (orow != row) map_row(row, orow, V, vec, [](float v, int) { return v; });
+        if (orow != row) map_row<NT>(row, orow, V, vec, [](float v, int) { return v; });
         if (a.kept && t == 0) a.kept[r] = V;
         return;
     }
@@ -410,27 +435,27 @@ __global__ __launch_bounds__(kTrThreads, 3) void truncate_kernel(TruncArgs a)
 
     // ---- top-k: count histogram of the first digit over the row (and the row max) ----
     if (use_k) {
-        clear_hist(sh, kBins, false);
+        clear_hist<NT>(sh, kBins, false);
         __syncthreads();
         float mt = -INFINITY;
-        for_row(row, V, vec, [&](float v, int e) __attribute__((always_inline)) {
+        for_row<NT>(row, V, vec, [&](float v, int e) __attribute__((always_inline)) {
             if (want_p) mt = fmaxf(mt, v);
             atomicAdd(&sh.hc[(int)(composite(v, e) >> kShiftC[0])], 1u);
         });
-        if (want_p) M = block_max(mt, sh.s_max);
+        if (want_p) M = blk_max<NT>(mt, sh.s_max);
         __syncthreads();
-        fix_digit<false>(rk, walk<false>(rk, kBins, true, k, 0.0f, sh));
+        fix_digit<false>(rk, walk<false, NT>(rk, kBins, true, k, 0.0f, sh));
     } else {
         float mt = -INFINITY;
-        for_row(row, V, vec, [&](float v, int) __attribute__((always_inline)) { mt = fmaxf(mt, v); });
-        M = block_max(mt, sh.s_max);
+        for_row<NT>(row, V, vec, [&](float v, int) __attribute__((always_inline)) { mt = fmaxf(mt, v); });
+        M = blk_max<NT>(mt, sh.s_max);
     }
     // a row of -inf logits has no distribution to truncate: top-p leaves it as it is
     const bool use_p = want_p && M != -INFINITY;
     const double kd = a.kd;
     const float kb = a.kb;
     if (!use_k && !use_p) {
-        if (orow != row) map_row(row, orow, V, vec, [](float v, int) { return v; });
+        if (orow != row) map_row<NT>(row, orow, V, vec, [](float v, int) { return v; });
         if (a.kept && t == 0) a.kept[r] = V;
         return;
     }
@@ -442,15 +467,15 @@ __global__ __launch_bounds__(kTrThreads, 3) void truncate_kernel(TruncArgs a)
         const bool all = use_p && rk.cnt_above + rk.n <= (uint64_t)kCap;
         while (!all && rk.n > (uint32_t)kCap && rk.level < kLevels) {  // one more digit over the row
             const int nb = 1 << dwidth<false>(rk.level);
-            clear_hist(sh, nb, false);
+            clear_hist<NT>(sh, nb, false);
             __syncthreads();
             const int s = dshift<false>(rk.level);
-            for_row(row, V, vec, [&](float v, int e) __attribute__((always_inline)) {
+            for_row<NT>(row, V, vec, [&](float v, int e) __attribute__((always_inline)) {
                 const uint64_t c = composite(v, e);
                 if ((c & rk.pmask) == rk.prefix) atomicAdd(&sh.hc[(int)((c >> s) & (uint64_t)(nb - 1))], 1u);
             });
             __syncthreads();
-            fix_digit<false>(rk, walk<false>(rk, nb, false, k, 0.0f, sh));
+            fix_digit<false>(rk, walk<false, NT>(rk, nb, false, k, 0.0f, sh));
         }
         // gather; when top-k is the last cut (or the whole set is gathered) also write the
         // output of every token outside the list
@@ -468,11 +493,11 @@ __global__ __launch_bounds__(kTrThreads, 3) void truncate_kernel(TruncArgs a)
             return (!use_p && (c & rk.pmask) > rk.prefix) ? v : -INFINITY;
         };
         if (write)
-            map_row(row, orow, V, vec, gather);
+            map_row<NT>(row, orow, V, vec, gather);
         else
-            for_row(row, V, vec, [&](float v, int e) __attribute__((always_inline)) { (void)gather(v, e); });
+            for_row<NT>(row, V, vec, [&](float v, int e) __attribute__((always_inline)) { (void)gather(v, e); });
         __syncthreads();
-        ck = finish_in_lds<false>(rk, false, k, 0.0f, 0.0f, 0.0, none, sh);
+        ck = finish_in_lds<false, NT>(rk, false, k, 0.0f, 0.0f, 0.0, none, sh);
         lds_k = all;
     }
     auto in_k = [&](uint64_t c) { return !use_k || c >= ck; };
@@ -483,47 +508,47 @@ __global__ __launch_bounds__(kTrThreads, 3) void truncate_kernel(TruncArgs a)
         Range rp{0, 0, 0, 0, 0, 0, 0, 0, 0};
         if (lds_k) {
             // the whole top-k set is in the list: top-p there, from the first digit
-            cstar = finish_in_lds<true>(rp, true, 0, pp, M, kd, in_k, sh);
+            cstar = finish_in_lds<true, NT>(rp, true, 0, pp, M, kd, in_k, sh);
         } else {
             // first level over the row: weight bins
-            clear_hist(sh, kMassBins, true);
+            clear_hist<NT>(sh, kMassBins, true);
             __syncthreads();
-            for_row(row, V, vec, [&](float v, int e) __attribute__((always_inline)) {
+            for_row<NT>(row, V, vec, [&](float v, int e) __attribute__((always_inline)) {
                 if (in_k(composite(v, e)))
                     add_token(sh, kMassBins - 1 - (weight_fine(v, M, kb) >> 10), true, fix_weight(v, M, kd));
             });
             __syncthreads();
-            rp.wf = kMassBins - 1 - walk<true>(rp, kMassBins, true, 0, pp, sh);
+            rp.wf = kMassBins - 1 - walk<true, NT>(rp, kMassBins, true, 0, pp, sh);
             rp.wl = 1;
             if (rp.n > (uint32_t)kCap) {  // second level: the weight bin's 1024 sub-bins
-                clear_hist(sh, kMassBins, true);
+                clear_hist<NT>(sh, kMassBins, true);
                 __syncthreads();
-                for_row(row, V, vec, [&](float v, int e) __attribute__((always_inline)) {
+                for_row<NT>(row, V, vec, [&](float v, int e) __attribute__((always_inline)) {
                     const int fine = weight_fine(v, M, kb);
                     if ((fine >> 10) == rp.wf && in_k(composite(v, e)))
                         add_token(sh, kMassBins - 1 - (fine & 1023), true, fix_weight(v, M, kd));
                 });
                 __syncthreads();
-                rp.wf = (rp.wf << 10) | (kMassBins - 1 - walk<true>(rp, kMassBins, false, 0, pp, sh));
+                rp.wf = (rp.wf << 10) | (kMassBins - 1 - walk<true, NT>(rp, kMassBins, false, 0, pp, sh));
                 rp.wl = 2;
             }
             while (rp.n > (uint32_t)kCap && rp.level < kLevels) {  // composite digits over the row, inside the weight bin
                 const int nb = 1 << dwidth<true>(rp.level);
-                clear_hist(sh, nb, true);
+                clear_hist<NT>(sh, nb, true);
                 __syncthreads();
                 const int s = dshift<true>(rp.level);
-                for_row(row, V, vec, [&](float v, int e) __attribute__((always_inline)) {
+                for_row<NT>(row, V, vec, [&](float v, int e) __attribute__((always_inline)) {
                     const uint64_t c = composite(v, e);
                     if (in_k(c) && in_range(rp, c, weight_fine(v, M, kb)))
                         add_token(sh, (int)((c >> s) & (uint64_t)(nb - 1)), true, fix_weight(v, M, kd));
                 });
                 __syncthreads();
-                fix_digit<true>(rp, walk<true>(rp, nb, false, 0, pp, sh));
+                fix_digit<true>(rp, walk<true, NT>(rp, nb, false, 0, pp, sh));
             }
             // gather the range; write every other token's output
             if (t == 0) sh.s_n = 0;
             __syncthreads();
-            map_row(row, orow, V, vec, [&](float v, int e) __attribute__((always_inline)) {
+            map_row<NT>(row, orow, V, vec, [&](float v, int e) __attribute__((always_inline)) {
                 const uint64_t c = composite(v, e);
                 if (!in_k(c)) return -INFINITY;
                 const int wb = weight_fine(v, M, kb);
@@ -536,14 +561,14 @@ __global__ __launch_bounds__(kTrThreads, 3) void truncate_kernel(TruncArgs a)
             });
             __syncthreads();
             // the range's remaining digits (the weight bin no longer matters inside the list)
-            cstar = finish_in_lds<true>(rp, false, 0, pp, M, kd, in_k, sh);
+            cstar = finish_in_lds<true, NT>(rp, false, 0, pp, M, kd, in_k, sh);
         }
         n_kept = rp.cnt_above + 1;
     }
 
     // the gathered tokens: kept iff C >= C*
     const int n = min((int)sh.s_n, kCap);
-    for (int i = t; i < n; i += kTrThreads) {
+    for (int i = t; i < n; i += NT) {
         const uint64_t c = sh.list[i];
         const int id = comp_id(c);
         orow[id] = c >= cstar ? row[id] : -INFINITY;
@@ -577,6 +602,9 @@ extern "C" sv_status sv_truncate(const sv_trunc_desc *d, void *stream)
     a.vec = (d->V % 4 == 0) && (((uintptr_t)d->logits & 15) == 0) && (((uintptr_t)d->out & 15) == 0);
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(truncate_kernel, dim3((unsigned)d->R), dim3(kTrThreads), 0, s, a);
+    if (d->R <= device_cu_count())
+        hipLaunchKernelGGL(truncate_kernel<kTrThreadsFew>, dim3((unsigned)d->R), dim3(kTrThreadsFew), 0, s, a);
+    else
+        hipLaunchKernelGGL(truncate_kernel<kTrThreadsMany>, dim3((unsigned)d->R), dim3(kTrThreadsMany), 0, s, a);
     return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
 }

@@ -66,6 +66,17 @@ def test_truncate_parity(V, R, k, p):
         _assert_trunc(lg, T, ref, out, kept, "V=%d k=%d p=%g T=%g" % (V, kk, p, T))
 
 
+@pytest.mark.parametrize("V,R", [(5000, 300), (32000, 270)])
+def test_many_rows(V, R):
+    """More rows than compute units: the 256-thread form of the kernel (fewer rows run the
+    1024-thread form, which every other test here exercises)."""
+    lg = synth.logit_rows(V + R, R, V, 3.0)
+    for k, p in [(0, 0.9), (40, 0.9), (1000, 1.0), (2500, 0.95)]:
+        ref = oracle.truncate(lg, 0.9, top_k=k, top_p=p)
+        out, kept = _gpu(lg, 0.9, k, p)
+        _assert_trunc(lg, 0.9, ref, out, kept, "many rows R=%d V=%d k=%d p=%g" % (R, V, k, p))
+
+
 @pytest.mark.parametrize("var", [0.01, 0.25, 1.0])
 def test_flat_rows(var):
     """Nearly flat rows over 128256 tokens: the top-p cut lands where thousands of tokens
