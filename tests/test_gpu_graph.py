@@ -137,3 +137,59 @@ def test_tree_round_graph_replays_match_eager():
                         dev_array(np.asarray(other_par, np.int32)), 6, 0.9, rep, 0)
         sv.sv_build_tree_mask(dev_array(np.asarray(other_par, np.int32)), 11)
         torch.cuda.synchronize()
+
+
+def test_processed_round_graph_replays_match_eager():
+    """Penalties, top-k / top-p and the acceptance on the processed rows, captured once (rows
+    copied into work buffers first, since the processing runs in place) and replayed with
+    eager processing of other rows between replays: every replay equals the eager result."""
+    B, g, V, T = 6, 4, 20000, 0.8
+    acc = synth.accept_inputs(7, B=B, gamma=g, V=V, target_var=3.0, noise_var=1.0, tau=T)
+    src_t, src_d, tok = dev_array(acc["target"]), dev_array(acc["draft"]), dev_array(acc["draft_tokens"])
+    hist = dev_array(np.random.default_rng(3).integers(0, 500, (B, 300)).astype(np.int32))
+    wt, wd = torch.empty_like(src_t), torch.empty_like(src_d)
+    kt = torch.empty(B * (g + 1), dtype=torch.int32, device="cuda")
+    kd = torch.empty(B * g, dtype=torch.int32, device="cuda")
+    alen = torch.empty(B, dtype=torch.int32, device="cuda")
+    otok = torch.empty((B, g + 1), dtype=torch.int32, device="cuda")
+    pen = dict(repetition=1.3, frequency=0.2, presence=0.3)
+    pds = [sv.penalty_desc(w, history=hist, draft_tokens=tok, **pen) for w in (wt, wd)]
+    tds = [sv.trunc_desc(wt.reshape(-1, V), wt.reshape(-1, V), temperature=T, top_k=50, top_p=0.9, kept=kt),
+           sv.trunc_desc(wd.reshape(-1, V), wd.reshape(-1, V), temperature=T, top_k=50, top_p=0.9, kept=kd)]
+    sd = sv.accept_desc(sv.SV_SAMPLE, wt, wd, tok, T, 11, 2, None, alen, otok, None, None)
+    npw = max(sv.lib.sv_penalize_workspace(ctypes.byref(d)) for d in pds)
+    wp = torch.zeros(npw + 256, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(sv.lib.sv_spec_accept_workspace(ctypes.byref(sd)) + 256, dtype=torch.uint8, device="cuda")
+    pp = ctypes.c_void_p(wp.data_ptr() + (-wp.data_ptr()) % 256)
+    ps = ctypes.c_void_p(ws.data_ptr() + (-ws.data_ptr()) % 256)
+
+    def launch(stream):
+        wt.copy_(src_t)
+        wd.copy_(src_d)
+        for d in pds:
+            assert sv.lib.sv_penalize(ctypes.byref(d), pp, npw, stream) == 0
+        for d in tds:
+            assert sv.lib.sv_truncate(ctypes.byref(d), stream) == 0
+        assert sv.lib.sv_spec_accept(ctypes.byref(sd), ps, ws.numel() - 256, stream) == 0
+
+    launch(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in (wt, wd, kt, kd, alen, otok)]
+
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        launch(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    other = synth.accept_inputs(8, B=3, gamma=2, V=5000, target_var=2.0, noise_var=1.0, tau=T)
+    for rep in range(4):
+        for x in (wt, wd, kt, kd, alen, otok):
+            x.zero_()
+        gr.replay()
+        torch.cuda.synchronize()
+        for x, r in zip((wt, wd, kt, kd, alen, otok), ref):
+            assert torch.equal(x, r), rep
+        # eager processing of other rows (the binding's own workspace) between replays
+        o = dev_array(other["target"])
+        sv.sv_penalize(o, history=dev_array(np.arange(40, dtype=np.int32).reshape(1, 40).repeat(3, 0)),
+                       draft_tokens=dev_array(other["draft_tokens"]), repetition=1.5)
+        sv.sv_truncate(o, temperature=T, top_p=0.7, in_place=True)
+        torch.cuda.synchronize()
