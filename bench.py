@@ -280,9 +280,13 @@ def time_truncate(sv, copies, tau, top_k, top_p, steps, sh, dev):
     descs = [[sv.trunc_desc(c[k].reshape(-1, V), outs[k].reshape(-1, V), temperature=tau, top_k=top_k,
                             top_p=top_p, kept=kept[k]) for k in ("target", "draft")] for c in copies]
 
+    nb = max(sv.lib.sv_truncate_workspace(ctypes.byref(d)) for dd in descs for d in dd)
+    ws = torch.zeros(nb + 256, dtype=torch.uint8, device=dev)
+    pw = _aligned(ws)
+
     def call(i):
         for d in descs[i % R]:
-            if sv.lib.sv_truncate(ctypes.byref(d), sh):
+            if sv.lib.sv_truncate(ctypes.byref(d), pw, nb, sh):
                 raise RuntimeError("truncate launch failed")
     ms = median_event_ms(call, steps, sh)
     rows = sum(kept[k].numel() for k in kept)

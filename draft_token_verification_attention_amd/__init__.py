@@ -78,7 +78,7 @@ class sv_penalty_desc(ctypes.Structure):
 
 EXPORTS = ("sv_build_tree_mask", "sv_verify_attention_workspace", "sv_verify_attention",
            "sv_spec_accept_workspace", "sv_spec_accept", "sv_spec_accept_static", "sv_tree_walk_workspace",
-           "sv_tree_walk", "sv_kv_commit", "sv_truncate", "sv_penalize_workspace", "sv_penalize",
+           "sv_tree_walk", "sv_kv_commit", "sv_truncate_workspace", "sv_truncate", "sv_penalize_workspace", "sv_penalize",
            "sv_status_string")
 
 
@@ -105,7 +105,9 @@ def _load():
     L.sv_tree_walk.restype = ctypes.c_int
     L.sv_kv_commit.argtypes = [ctypes.POINTER(sv_commit_desc), _P]
     L.sv_kv_commit.restype = ctypes.c_int
-    L.sv_truncate.argtypes = [ctypes.POINTER(sv_trunc_desc), _P]
+    L.sv_truncate_workspace.argtypes = [ctypes.POINTER(sv_trunc_desc)]
+    L.sv_truncate_workspace.restype = ctypes.c_size_t
+    L.sv_truncate.argtypes = [ctypes.POINTER(sv_trunc_desc), _P, ctypes.c_size_t, _P]
     L.sv_truncate.restype = ctypes.c_int
     L.sv_penalize_workspace.argtypes = [ctypes.POINTER(sv_penalty_desc)]
     L.sv_penalize_workspace.restype = ctypes.c_size_t
@@ -372,9 +374,10 @@ def trunc_desc(logits, out, *, temperature: float, top_k: int = 0, top_p: float 
 
 
 def sv_truncate(logits, *, temperature: float, top_k: int = 0, top_p: float = 1.0, top_k_rows=None,
-                top_p_rows=None, in_place: bool = False):
+                top_p_rows=None, in_place: bool = False, split: bool = True):
     """Top-k then top-p truncation of fp32 logit rows [R][V] (any leading shape is flattened
-    into R).  Returns (out, kept int32 [R]): out holds the kept tokens' logits and -inf
+    into R); split=False runs without a workspace (the first level then stays in one
+    workgroup per row).  Returns (out, kept int32 [R]): out holds the kept tokens' logits and -inf
     elsewhere; with in_place it is `logits` itself (which must then be contiguous fp32)."""
     _need_cuda(logits, top_k_rows, top_p_rows)
     if logits.dtype != torch.float32:
@@ -392,7 +395,9 @@ def sv_truncate(logits, *, temperature: float, top_k: int = 0, top_p: float = 1.
     pr = None if top_p_rows is None else top_p_rows.to(torch.float32).contiguous().reshape(R)
     d = trunc_desc(x, out, temperature=temperature, top_k=top_k, top_p=top_p, top_k_rows=kr, top_p_rows=pr,
                    kept=kept)
-    _check(lib.sv_truncate(ctypes.byref(d), _stream(x.device)), "sv_truncate")
+    nb = lib.sv_truncate_workspace(ctypes.byref(d)) if split else 0
+    ws = workspace(nb, x.device) if nb else None
+    _check(lib.sv_truncate(ctypes.byref(d), _ptr(ws), nb, _stream(x.device)), "sv_truncate")
     return out.reshape(logits.shape), kept
 
 

@@ -19,6 +19,15 @@
 // of each), which spreads them over many more bins than the logit's leading bits do.  LDS stays under 48 KB, so three rows
 // run on each compute unit at once.
 //
+// A few rows leave most of the chip idle, so with a workspace the first level of every row
+// (the row max, the first key digit's counts for top-k, the first weight level for top-p
+// alone) is split over many blocks per row, which add their chunk's histogram into the row's
+// histogram in the workspace.  When that level already leaves at most kCap tokens to gather,
+// the gathering pass is split too: each block walks the row's histogram itself, writes its
+// chunk's outputs and appends its chunk's candidates to the row's list in the workspace; the
+// row's block then finishes on that list.  Otherwise the row's block goes on from the
+// histogram alone.  The sums are exact integers, so the result is the same either way.
+//
 // Top-p weighs token x by w = 2^((l_x - M) log2(e) / T) (M the row's largest logit), in fp64
 // to about 2e-14, and sums the weights as integers in units of 2^-62: every sum is exact and
 // independent of the order of the LDS atomics, so the kept set is deterministic, and the cut
@@ -35,6 +44,9 @@ typedef unsigned __int128 u128;
 // 128256 logits, top-p 0.9: one row 203 -> 121 us, 256 rows 232 -> 152 us; 320 rows 280 us
 // either way, and top-k 50 then top-p 0.9 on 320 rows 135 us with 256 threads, 164 with 1024.
 constexpr int kTrThreadsMany = 256, kTrThreadsFew = 1024;
+constexpr int kMaxSplit = 64;             // chunks per row of the split first level
+constexpr int kSplitMinV = 16384;         // shorter rows are not split
+constexpr int kSplitAlign = 4096;         // chunk starts are multiples of this many tokens
 constexpr int kBins = 2048;               // count histogram bins (digits of at most 11 bits)
 constexpr int kMassBins = 1024;           // mass histogram bins (digits of at most 10 bits)
 constexpr int kCap = 2048;                // candidates gathered into LDS
@@ -67,6 +79,15 @@ struct TruncArgs {
     float *out;
     int32_t *kept;
     int vec;       // 16-byte aligned rows with V % 4 == 0: float4 loads and stores
+    // split first level (S > 0): S chunks of `chunk` tokens per row; per row in the workspace
+    int S, chunk;
+    float *pmax;       // [R][kMaxSplit] chunk maxima
+    uint32_t *ghc;     // [R][kBins] counts of the first key digit (top-k rows)
+    uint32_t *gmc;     // [R][kMassBins] counts of the first weight level (top-p-alone rows)
+    uint64_t *gmhi;    // [R][kMassBins] its masses, high parts
+    uint64_t *gmlo;    // [R][kMassBins] low parts
+    uint64_t *glist;   // [R][kCap] composites gathered by the split gather pass
+    uint32_t *gcount;  // [R] their number
 };
 
 // Ascending with the float value (-0 taken as +0; rows hold no NaN).
@@ -111,12 +132,12 @@ __device__ __forceinline__ int weight_fine(float v, float M, float kb)
 // f(value, token) over the row: each thread takes 4 consecutive tokens of every 1024, and
 // issues kUnroll 16-byte loads before using them.
 template <int NT, typename F>
-__device__ __forceinline__ void for_row(const float *row, int V, bool vec, F f)
+__device__ __forceinline__ void for_range(const float *row, int lo, int V, bool vec, F f)
 {
     constexpr int kStep = 4 * NT;
     const int t4 = 4 * (int)threadIdx.x;
     if (vec) {
-        int e0 = 0;
+        int e0 = lo;
         for (; e0 + kUnroll * kStep <= V; e0 += kUnroll * kStep) {
             float4 x[kUnroll];
 #pragma unroll
@@ -138,21 +159,28 @@ __device__ __forceinline__ void for_row(const float *row, int V, bool vec, F f)
             f(x.w, e + 3);
         }
     } else {
-        for (int e0 = t4; e0 < V; e0 += kStep)
+        for (int e0 = lo + t4; e0 < V; e0 += kStep)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 if (e0 + j < V) f(row[e0 + j], e0 + j);
     }
 }
 
+// (lo a multiple of 4; V the range's end)
+template <int NT, typename F>
+__device__ __forceinline__ void for_row(const float *row, int V, bool vec, F f)
+{
+    for_range<NT>(row, 0, V, vec, f);
+}
+
 // out[e] = g(in[e], e) over the row, with the loads of for_row and 16-byte stores.
 template <int NT, typename G>
-__device__ __forceinline__ void map_row(const float *row, float *orow, int V, bool vec, G g)
+__device__ __forceinline__ void map_range(const float *row, float *orow, int lo, int V, bool vec, G g)
 {
     constexpr int kStep = 4 * NT;
     const int t4 = 4 * (int)threadIdx.x;
     if (vec) {
-        int e0 = 0;
+        int e0 = lo;
         for (; e0 + kUnroll * kStep <= V; e0 += kUnroll * kStep) {
             float4 x[kUnroll];
 #pragma unroll
@@ -178,11 +206,17 @@ __device__ __forceinline__ void map_row(const float *row, float *orow, int V, bo
             *reinterpret_cast<float4 *>(orow + e) = y;
         }
     } else {
-        for (int e0 = t4; e0 < V; e0 += kStep)
+        for (int e0 = lo + t4; e0 < V; e0 += kStep)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 if (e0 + j < V) orow[e0 + j] = g(row[e0 + j], e0 + j);
     }
+}
+
+template <int NT, typename G>
+__device__ __forceinline__ void map_row(const float *row, float *orow, int V, bool vec, G g)
+{
+    map_range<NT>(row, orow, 0, V, vec, g);
 }
 
 // Inclusive scan of one value per thread over the block, in thread order (Hillis-Steele in
@@ -360,6 +394,18 @@ __device__ __forceinline__ void fix_digit(Range &rg, int bin)
     ++rg.level;
 }
 
+// After the first top-k level: whether the whole top-k set is gathered (top-p follows), and
+// whether what is left to gather fits the list.
+__device__ __forceinline__ bool topk_all(bool use_p, const Range &rk)
+{
+    return use_p && rk.cnt_above + rk.n <= (uint64_t)kCap;
+}
+
+__device__ __forceinline__ bool topk_fits(bool use_p, const Range &rk)
+{
+    return topk_all(use_p, rk) || (!use_p && rk.n <= (uint32_t)kCap);
+}
+
 // Finish a selection on the gathered list (sh.list[0 .. sh.s_n), a superset of the range):
 // composite digits until one token is left.  Returns its composite.
 template <bool MASS, int NT, typename Filt>
@@ -409,6 +455,194 @@ __device__ __forceinline__ float blk_max(float v, float *scratch)
     return r;
 }
 
+// ---- split first level ----
+__device__ __forceinline__ void row_setting(const TruncArgs &a, int r, bool &use_k, bool &want_p)
+{
+    const int k = a.k_rows ? a.k_rows[r] : a.top_k;
+    const float pp = a.p_rows ? a.p_rows[r] : a.top_p;
+    use_k = k > 0 && k < a.V;
+    want_p = pp < 1.0f;
+}
+
+// The row's histograms in the workspace start at zero.
+__global__ __launch_bounds__(kTrThreadsMany) void trunc_zero_kernel(TruncArgs a)
+{
+    const int64_t r = blockIdx.x;
+    if (threadIdx.x == 0) a.gcount[r] = 0;
+    for (int i = threadIdx.x; i < kBins; i += kTrThreadsMany) a.ghc[r * kBins + i] = 0;
+    for (int i = threadIdx.x; i < kMassBins; i += kTrThreadsMany) {
+        a.gmc[r * kMassBins + i] = 0;
+        a.gmhi[r * kMassBins + i] = 0;
+        a.gmlo[r * kMassBins + i] = 0;
+    }
+}
+
+// Chunk c of row r: its max (rows with top-p) and, for top-k rows, the counts of the first key
+// digit, added into the row's histogram.
+__global__ __launch_bounds__(kTrThreadsMany) void trunc_split_count_kernel(TruncArgs a)
+{
+    __shared__ uint32_t hc[kBins];
+    __shared__ float smax[kTrThreadsMany / kWave];
+    const int c = blockIdx.x, r = blockIdx.y;
+    bool use_k, want_p;
+    row_setting(a, r, use_k, want_p);
+    const float *row = a.in + (int64_t)r * a.V;
+    const int lo = c * a.chunk, hi = min(lo + a.chunk, a.V);
+    if (use_k) {
+        for (int i = threadIdx.x; i < kBins; i += kTrThreadsMany) hc[i] = 0;
+        __syncthreads();
+    }
+    float mt = -INFINITY;
+    for_range<kTrThreadsMany>(row, lo, hi, a.vec != 0, [&](float v, int e) __attribute__((always_inline)) {
+        mt = fmaxf(mt, v);
+        if (use_k) atomicAdd(&hc[(int)(composite(v, e) >> kShiftC[0])], 1u);
+    });
+    const float m = blk_max<kTrThreadsMany>(mt, smax);
+    if (threadIdx.x == 0) a.pmax[(int64_t)r * kMaxSplit + c] = m;
+    if (use_k) {
+        __syncthreads();
+        for (int i = threadIdx.x; i < kBins; i += kTrThreadsMany)
+            if (hc[i]) atomicAdd(&a.ghc[(int64_t)r * kBins + i], hc[i]);
+    }
+}
+
+// Chunk c of a top-p-alone row: its first weight level, added into the row's histogram.
+__global__ __launch_bounds__(kTrThreadsMany) void trunc_split_mass_kernel(TruncArgs a)
+{
+    __shared__ uint32_t hc[kMassBins];
+    __shared__ uint64_t hhi[kMassBins], hlo[kMassBins];
+    __shared__ float smax[kTrThreadsMany / kWave];
+    const int c = blockIdx.x, r = blockIdx.y;
+    bool use_k, want_p;
+    row_setting(a, r, use_k, want_p);
+    if (use_k || !want_p) return;
+    float mt = -INFINITY;
+    for (int i = threadIdx.x; i < a.S; i += kTrThreadsMany) mt = fmaxf(mt, a.pmax[(int64_t)r * kMaxSplit + i]);
+    const float M = blk_max<kTrThreadsMany>(mt, smax);
+    if (M == -INFINITY) return;   // (the same in every thread)
+    for (int i = threadIdx.x; i < kMassBins; i += kTrThreadsMany) {
+        hc[i] = 0;
+        hhi[i] = 0;
+        hlo[i] = 0;
+    }
+    __syncthreads();
+    const float *row = a.in + (int64_t)r * a.V;
+    const int lo = c * a.chunk, hi = min(lo + a.chunk, a.V);
+    for_range<kTrThreadsMany>(row, lo, hi, a.vec != 0, [&](float v, int) __attribute__((always_inline)) {
+        const int bin = kMassBins - 1 - (weight_fine(v, M, a.kb) >> 10);
+        const uint64_t f = fix_weight(v, M, a.kd);
+        atomicAdd(&hc[bin], 1u);
+        atomicAdd((unsigned long long *)&hhi[bin], (unsigned long long)(f >> kLoBits));
+        atomicAdd((unsigned long long *)&hlo[bin], (unsigned long long)(f & ((1ull << kLoBits) - 1)));
+    });
+    __syncthreads();
+    const int64_t o = (int64_t)r * kMassBins;
+    for (int i = threadIdx.x; i < kMassBins; i += kTrThreadsMany)
+        if (hc[i]) {
+            atomicAdd(&a.gmc[o + i], hc[i]);
+            atomicAdd((unsigned long long *)&a.gmhi[o + i], (unsigned long long)hhi[i]);
+            atomicAdd((unsigned long long *)&a.gmlo[o + i], (unsigned long long)hlo[i]);
+        }
+}
+
+// The row max from the chunk maxima of the split first level.
+template <int NT>
+__device__ __forceinline__ float split_max(const TruncArgs &a, int r, float *scratch)
+{
+    float mt = -INFINITY;
+    for (int i = threadIdx.x; i < a.S; i += NT) mt = fmaxf(mt, a.pmax[(int64_t)r * kMaxSplit + i]);
+    return blk_max<NT>(mt, scratch);
+}
+
+// Chunk c of row r, when the first level leaves at most kCap tokens to gather: walk the
+// row's first-level histogram (as the row's block will), write the chunk's outputs and append
+// its candidates to the row's list (gathered in LDS first, then one global atomic reserves
+// the block's slots: one counter per row would serialize thousands of atomics).
+__global__ __launch_bounds__(kTrThreadsMany, 3) void trunc_split_gather_kernel(TruncArgs a)
+{
+    constexpr int NT = kTrThreadsMany;
+    __shared__ TrShared<NT> sh;
+    const int c = blockIdx.x, r = blockIdx.y, t = threadIdx.x;
+    const int k = a.k_rows ? a.k_rows[r] : a.top_k;
+    const float pp = a.p_rows ? a.p_rows[r] : a.top_p;
+    const bool use_k = k > 0 && k < a.V, want_p = pp < 1.0f;
+    if (!use_k && !want_p) return;
+    const float M = want_p ? split_max<NT>(a, r, sh.s_max) : 0.0f;
+    const bool use_p = want_p && M != -INFINITY;
+    if (!use_k && !use_p) return;
+    const float *row = a.in + (int64_t)r * a.V;
+    float *orow = a.out + (int64_t)r * a.V;
+    const int lo = c * a.chunk, hi = min(lo + a.chunk, a.V);
+    const bool vec = a.vec != 0;
+    if (t == 0) sh.s_n = 0;   // (ordered before any append by the syncs below)
+    auto append = [&](uint64_t cc) {
+        const uint32_t slot = atomicAdd(&sh.s_n, 1u);
+        if (slot < (uint32_t)kCap) sh.list[slot] = cc;
+    };
+    if (use_k) {
+        Range rk{0, 0, 0, 0, 0, 0, 0, 0, (uint32_t)a.V};
+        clear_hist<NT>(sh, kBins, false);
+        __syncthreads();
+        for (int i = t; i < kBins; i += NT) sh.hc[i] = a.ghc[(int64_t)r * kBins + i];
+        __syncthreads();
+        fix_digit<false>(rk, walk<false, NT>(rk, kBins, true, k, 0.0f, sh));
+        if (!topk_fits(use_p, rk)) return;   // (the same in every thread)
+        const bool all = topk_all(use_p, rk);
+        map_range<NT>(row, orow, lo, hi, vec, [&](float v, int e) __attribute__((always_inline)) {
+            const uint64_t cc = composite(v, e);
+            const bool take = all ? (cc & rk.pmask) >= rk.prefix : (cc & rk.pmask) == rk.prefix;
+            if (take) {
+                append(cc);
+                return v;   // decided by the row's block
+            }
+            return (!use_p && (cc & rk.pmask) > rk.prefix) ? v : -INFINITY;
+        });
+    } else {
+        Range rp{0, 0, 0, 0, 0, 0, 0, 0, 0};
+        clear_hist<NT>(sh, kMassBins, true);
+        __syncthreads();
+        const int64_t o = (int64_t)r * kMassBins;
+        for (int i = t; i < kMassBins; i += NT) {
+            sh.hc[i] = a.gmc[o + i];
+            sh.hw_hi[i] = a.gmhi[o + i];
+            sh.hw_lo[i] = a.gmlo[o + i];
+        }
+        __syncthreads();
+        rp.wf = kMassBins - 1 - walk<true, NT>(rp, kMassBins, true, 0, pp, sh);
+        rp.wl = 1;
+        if (rp.n > (uint32_t)kCap) return;
+        map_range<NT>(row, orow, lo, hi, vec, [&](float v, int e) __attribute__((always_inline)) {
+            const uint64_t cc = composite(v, e);
+            const int wb = weight_fine(v, M, a.kb);
+            if (in_range(rp, cc, wb)) {
+                append(cc);
+                return v;
+            }
+            return before_range(rp, cc, wb) ? v : -INFINITY;
+        });
+    }
+    // the block's candidates into the row's list
+    __syncthreads();
+    const uint32_t n = min(sh.s_n, (uint32_t)kCap);
+    if (n == 0) return;
+    if (t == 0) sh.s_bin = atomicAdd(a.gcount + r, n);
+    __syncthreads();
+    const uint32_t base = sh.s_bin;
+    uint64_t *lst = a.glist + (int64_t)r * kCap;
+    for (uint32_t i = t; i < n; i += NT)
+        if (base + i < (uint32_t)kCap) lst[base + i] = sh.list[i];
+}
+
+// The candidates the split gather pass listed, into the block's list.
+template <int NT>
+__device__ __forceinline__ void load_split_list(const TruncArgs &a, int r, TrShared<NT> &sh)
+{
+    const int n = (int)min(a.gcount[r], (uint32_t)kCap);
+    for (int i = threadIdx.x; i < n; i += NT) sh.list[i] = a.glist[(int64_t)r * kCap + i];
+    if (threadIdx.x == 0) sh.s_n = (uint32_t)n;
+    __syncthreads();
+}
+
 template <int NT>
 __global__ __launch_bounds__(NT, NT == kTrThreadsMany ? 3 : 4) void truncate_kernel(TruncArgs a)
 {
@@ -435,16 +669,24 @@ __global__ __launch_bounds__(NT, NT == kTrThreadsMany ? 3 : 4) void truncate_ker
 
     // ---- top-k: count histogram of the first digit over the row (and the row max) ----
     if (use_k) {
-        clear_hist<NT>(sh, kBins, false);
-        __syncthreads();
-        float mt = -INFINITY;
-        for_row<NT>(row, V, vec, [&](float v, int e) __attribute__((always_inline)) {
-            if (want_p) mt = fmaxf(mt, v);
-            atomicAdd(&sh.hc[(int)(composite(v, e) >> kShiftC[0])], 1u);
-        });
-        if (want_p) M = blk_max<NT>(mt, sh.s_max);
+        clear_hist<NT>(sh, kBins, false);   // (also the walk's crossing slots)
+        if (a.S) {  // the first digit's counts came from the split pass
+            __syncthreads();
+            for (int i = t; i < kBins; i += NT) sh.hc[i] = a.ghc[(int64_t)r * kBins + i];
+            if (want_p) M = split_max<NT>(a, r, sh.s_max);
+        } else {
+            __syncthreads();
+            float mt = -INFINITY;
+            for_row<NT>(row, V, vec, [&](float v, int e) __attribute__((always_inline)) {
+                if (want_p) mt = fmaxf(mt, v);
+                atomicAdd(&sh.hc[(int)(composite(v, e) >> kShiftC[0])], 1u);
+            });
+            if (want_p) M = blk_max<NT>(mt, sh.s_max);
+        }
         __syncthreads();
         fix_digit<false>(rk, walk<false, NT>(rk, kBins, true, k, 0.0f, sh));
+    } else if (a.S) {
+        M = split_max<NT>(a, r, sh.s_max);
     } else {
         float mt = -INFINITY;
         for_row<NT>(row, V, vec, [&](float v, int) __attribute__((always_inline)) { mt = fmaxf(mt, v); });
@@ -464,8 +706,10 @@ __global__ __launch_bounds__(NT, NT == kTrThreadsMany ? 3 : 4) void truncate_ker
     bool lds_k = false;
     if (use_k) {
         // whole top-k set in LDS (then top-p runs there too), or only the range
-        const bool all = use_p && rk.cnt_above + rk.n <= (uint64_t)kCap;
-        while (!all && rk.n > (uint32_t)kCap && rk.level < kLevels) {  // one more digit over the row
+        const bool all = topk_all(use_p, rk);
+        // (split, and it fits: the split gather pass has written the outputs and the list)
+        const bool listed = a.S && topk_fits(use_p, rk);
+        while (!listed && !all && rk.n > (uint32_t)kCap && rk.level < kLevels) {  // one more digit over the row
             const int nb = 1 << dwidth<false>(rk.level);
             clear_hist<NT>(sh, nb, false);
             __syncthreads();
@@ -492,7 +736,9 @@ __global__ __launch_bounds__(NT, NT == kTrThreadsMany ? 3 : 4) void truncate_ker
             }
             return (!use_p && (c & rk.pmask) > rk.prefix) ? v : -INFINITY;
         };
-        if (write)
+        if (listed)
+            load_split_list<NT>(a, r, sh);
+        else if (write)
             map_row<NT>(row, orow, V, vec, gather);
         else
             for_row<NT>(row, V, vec, [&](float v, int e) __attribute__((always_inline)) { (void)gather(v, e); });
@@ -510,17 +756,28 @@ __global__ __launch_bounds__(NT, NT == kTrThreadsMany ? 3 : 4) void truncate_ker
             // the whole top-k set is in the list: top-p there, from the first digit
             cstar = finish_in_lds<true, NT>(rp, true, 0, pp, M, kd, in_k, sh);
         } else {
-            // first level over the row: weight bins
+            // first level: weight bins (over the row, or from the split pass for top-p alone)
             clear_hist<NT>(sh, kMassBins, true);
             __syncthreads();
-            for_row<NT>(row, V, vec, [&](float v, int e) __attribute__((always_inline)) {
-                if (in_k(composite(v, e)))
-                    add_token(sh, kMassBins - 1 - (weight_fine(v, M, kb) >> 10), true, fix_weight(v, M, kd));
-            });
+            if (a.S && !use_k) {
+                const int64_t o = (int64_t)r * kMassBins;
+                for (int i = t; i < kMassBins; i += NT) {
+                    sh.hc[i] = a.gmc[o + i];
+                    sh.hw_hi[i] = a.gmhi[o + i];
+                    sh.hw_lo[i] = a.gmlo[o + i];
+                }
+            } else {
+                for_row<NT>(row, V, vec, [&](float v, int e) __attribute__((always_inline)) {
+                    if (in_k(composite(v, e)))
+                        add_token(sh, kMassBins - 1 - (weight_fine(v, M, kb) >> 10), true, fix_weight(v, M, kd));
+                });
+            }
             __syncthreads();
             rp.wf = kMassBins - 1 - walk<true, NT>(rp, kMassBins, true, 0, pp, sh);
             rp.wl = 1;
-            if (rp.n > (uint32_t)kCap) {  // second level: the weight bin's 1024 sub-bins
+            // (split, top-p alone, and it fits: the split gather pass has done the gathering)
+            const bool listed = a.S && !use_k && rp.n <= (uint32_t)kCap;
+            if (!listed && rp.n > (uint32_t)kCap) {  // second level: the weight bin's 1024 sub-bins
                 clear_hist<NT>(sh, kMassBins, true);
                 __syncthreads();
                 for_row<NT>(row, V, vec, [&](float v, int e) __attribute__((always_inline)) {
@@ -546,19 +803,23 @@ __global__ __launch_bounds__(NT, NT == kTrThreadsMany ? 3 : 4) void truncate_ker
                 fix_digit<true>(rp, walk<true, NT>(rp, nb, false, 0, pp, sh));
             }
             // gather the range; write every other token's output
-            if (t == 0) sh.s_n = 0;
-            __syncthreads();
-            map_row<NT>(row, orow, V, vec, [&](float v, int e) __attribute__((always_inline)) {
-                const uint64_t c = composite(v, e);
-                if (!in_k(c)) return -INFINITY;
-                const int wb = weight_fine(v, M, kb);
-                if (in_range(rp, c, wb)) {
-                    const uint32_t slot = atomicAdd(&sh.s_n, 1u);
-                    if (slot < (uint32_t)kCap) sh.list[slot] = c;
-                    return v;   // decided after the selection
-                }
-                return before_range(rp, c, wb) ? v : -INFINITY;
-            });
+            if (listed) {
+                load_split_list<NT>(a, r, sh);
+            } else {
+                if (t == 0) sh.s_n = 0;
+                __syncthreads();
+                map_row<NT>(row, orow, V, vec, [&](float v, int e) __attribute__((always_inline)) {
+                    const uint64_t c = composite(v, e);
+                    if (!in_k(c)) return -INFINITY;
+                    const int wb = weight_fine(v, M, kb);
+                    if (in_range(rp, c, wb)) {
+                        const uint32_t slot = atomicAdd(&sh.s_n, 1u);
+                        if (slot < (uint32_t)kCap) sh.list[slot] = c;
+                        return v;   // decided after the selection
+                    }
+                    return before_range(rp, c, wb) ? v : -INFINITY;
+                });
+            }
             __syncthreads();
             // the range's remaining digits (the weight bin no longer matters inside the list)
             cstar = finish_in_lds<true, NT>(rp, false, 0, pp, M, kd, in_k, sh);
@@ -578,12 +839,39 @@ __global__ __launch_bounds__(NT, NT == kTrThreadsMany ? 3 : 4) void truncate_ker
 
 }  // namespace
 
-extern "C" sv_status sv_truncate(const sv_trunc_desc *d, void *stream)
+namespace {
+
+bool trunc_ok(const sv_trunc_desc *d)
 {
-    if (!d) return SV_ERR_INVALID_ARG;
-    if (d->R < 0 || d->V < 1) return SV_ERR_INVALID_ARG;
-    if (!(d->temperature > 0.0f) || d->temperature == INFINITY) return SV_ERR_INVALID_ARG;
-    if (d->top_p != d->top_p) return SV_ERR_INVALID_ARG;  // NaN
+    if (!d || d->R < 0 || d->V < 1) return false;
+    if (!(d->temperature > 0.0f) || d->temperature == INFINITY) return false;
+    return d->top_p == d->top_p;  // not NaN
+}
+
+// Whether the first level runs split (few rows, long enough), and its workspace.  Measured on
+// rows of 128256 logits (without -> with): top-p 0.9 alone, 1 row 121 -> 61 us, 11 rows 122 ->
+// 68, 64 rows 129 -> 87, 128 rows 134 -> 113, 256 rows 151 -> 171; top-k 50 then top-p 0.9,
+// 1 row 68 -> 45, 64 rows 78 -> 68, 128 rows 81 -> 84.  So up to a quarter of the compute units.
+bool trunc_split(const sv_trunc_desc *d, int cus) { return d->R > 0 && 4 * d->R <= cus && d->V >= kSplitMinV; }
+
+size_t trunc_split_bytes(const sv_trunc_desc *d)
+{
+    const size_t per = kBins * sizeof(uint32_t) + kMassBins * (sizeof(uint32_t) + 2 * sizeof(uint64_t)) +
+                       kMaxSplit * sizeof(float) + kCap * sizeof(uint64_t) + sizeof(uint32_t);
+    return kCounterBytes + (size_t)d->R * per;
+}
+
+}  // namespace
+
+extern "C" size_t sv_truncate_workspace(const sv_trunc_desc *d)
+{
+    if (!trunc_ok(d) || d->V > (1 << kIdBits) || !trunc_split(d, device_cu_count())) return 0;
+    return trunc_split_bytes(d);
+}
+
+extern "C" sv_status sv_truncate(const sv_trunc_desc *d, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!trunc_ok(d)) return SV_ERR_INVALID_ARG;
     if (d->V > (1 << kIdBits)) return SV_ERR_UNSUPPORTED;  // ids in 24 bits; masses below 2^86 units
     if (d->R == 0) return SV_OK;
     if (!d->logits || !d->out) return SV_ERR_INVALID_ARG;
@@ -600,11 +888,49 @@ extern "C" sv_status sv_truncate(const sv_trunc_desc *d, void *stream)
     a.out = d->out;
     a.kept = d->kept;
     a.vec = (d->V % 4 == 0) && (((uintptr_t)d->logits & 15) == 0) && (((uintptr_t)d->out & 15) == 0);
+    a.S = 0;
+    a.chunk = 0;
+    a.pmax = nullptr;
+    a.ghc = nullptr;
+    a.gmc = nullptr;
+    a.gmhi = a.gmlo = nullptr;
+    a.glist = nullptr;
+    a.gcount = nullptr;
+    const int cus = device_cu_count();
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
-    if (d->R <= device_cu_count())
+    if (trunc_split(d, cus) && workspace && workspace_bytes >= trunc_split_bytes(d)) {
+        // about two blocks per compute unit over all rows, chunks a multiple of 4096 tokens
+        const int want = min(kMaxSplit, max(1, 2 * cus / d->R));
+        const int64_t chunk = ((int64_t)(d->V + want - 1) / want + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
+        a.chunk = (int)chunk;
+        a.S = (int)((d->V + chunk - 1) / chunk);
+        char *w = static_cast<char *>(workspace) + kCounterBytes;
+        a.glist = reinterpret_cast<uint64_t *>(w);
+        w += (size_t)d->R * kCap * sizeof(uint64_t);
+        a.ghc = reinterpret_cast<uint32_t *>(w);
+        w += (size_t)d->R * kBins * sizeof(uint32_t);
+        a.gmhi = reinterpret_cast<uint64_t *>(w);
+        w += (size_t)d->R * kMassBins * sizeof(uint64_t);
+        a.gmlo = reinterpret_cast<uint64_t *>(w);
+        w += (size_t)d->R * kMassBins * sizeof(uint64_t);
+        a.gmc = reinterpret_cast<uint32_t *>(w);
+        w += (size_t)d->R * kMassBins * sizeof(uint32_t);
+        a.pmax = reinterpret_cast<float *>(w);
+        w += (size_t)d->R * kMaxSplit * sizeof(float);
+        a.gcount = reinterpret_cast<uint32_t *>(w);
+        const dim3 g((unsigned)a.S, (unsigned)d->R);
+        // top-p alone somewhere: a row without top-k (per-row values may say so) and with top-p
+        const bool mass = (d->top_k_rows || d->top_k <= 0 || d->top_k >= d->V) && (d->top_p_rows || d->top_p < 1.0f);
+        hipLaunchKernelGGL(trunc_zero_kernel, dim3((unsigned)d->R), dim3(kTrThreadsMany), 0, s, a);
+        hipLaunchKernelGGL(trunc_split_count_kernel, g, dim3(kTrThreadsMany), 0, s, a);
+        if (mass) hipLaunchKernelGGL(trunc_split_mass_kernel, g, dim3(kTrThreadsMany), 0, s, a);
+        hipLaunchKernelGGL(trunc_split_gather_kernel, g, dim3(kTrThreadsMany), 0, s, a);
         hipLaunchKernelGGL(truncate_kernel<kTrThreadsFew>, dim3((unsigned)d->R), dim3(kTrThreadsFew), 0, s, a);
-    else
+    } else if (d->R <= cus) {
+        hipLaunchKernelGGL(truncate_kernel<kTrThreadsFew>, dim3((unsigned)d->R), dim3(kTrThreadsFew), 0, s, a);
+    } else {
         hipLaunchKernelGGL(truncate_kernel<kTrThreadsMany>, dim3((unsigned)d->R), dim3(kTrThreadsMany), 0, s, a);
+    }
     return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
 }

@@ -404,8 +404,14 @@ SV_API sv_status sv_kv_commit(const sv_commit_desc *desc, void *stream);
 /* depend on the order of the sums, and it can differ from the exact one only where the  */
 /* cut lies within about 1e-13 of the set's mass, relative.  NaN or +inf logits: results */
 /* unspecified.                                                                           */
+/* Workspace (optional): with at least sv_truncate_workspace(desc) bytes (nonzero only for */
+/* R up to a quarter of the compute units and V >= 16384), the first level and, when it   */
+/* leaves few tokens, the gathering of every row are spread over many workgroups: for a    */
+/* few rows about twice as fast; the result is the same.  With less (or NULL) the call    */
+/* runs without it.  Shared like the other calls' workspaces.                              */
 /* Errors: R < 0, V < 1, T not in (0, inf), NaN top_p, or (R > 0) a null logits or out  */
-/*   -> SV_ERR_INVALID_ARG.  R == 0 launches nothing.                                     */
+/*   -> SV_ERR_INVALID_ARG.  R == 0 launches nothing.  out and logits are the same rows or */
+/*   do not overlap.                                                                        */
 /* Supported: 1 <= V <= 2^24 (else SV_ERR_UNSUPPORTED), R <= 2^31 - 1.                    */
 /* ---------------------------------------------------------------------------------- */
 typedef struct sv_trunc_desc {
@@ -420,7 +426,8 @@ typedef struct sv_trunc_desc {
     int32_t *kept;
 } sv_trunc_desc;
 
-SV_API sv_status sv_truncate(const sv_trunc_desc *desc, void *stream);
+SV_API size_t sv_truncate_workspace(const sv_trunc_desc *desc);
+SV_API sv_status sv_truncate(const sv_trunc_desc *desc, void *workspace, size_t workspace_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------------- */
 /* sv_penalize -- repetition, frequency and presence penalties on logit rows, in place,   */

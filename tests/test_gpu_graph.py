@@ -162,6 +162,9 @@ def test_processed_round_graph_replays_match_eager():
     ws = torch.zeros(sv.lib.sv_spec_accept_workspace(ctypes.byref(sd)) + 256, dtype=torch.uint8, device="cuda")
     pp = ctypes.c_void_p(wp.data_ptr() + (-wp.data_ptr()) % 256)
     ps = ctypes.c_void_p(ws.data_ptr() + (-ws.data_ptr()) % 256)
+    ntw = max(sv.lib.sv_truncate_workspace(ctypes.byref(d)) for d in tds)
+    wtr = torch.zeros(ntw + 256, dtype=torch.uint8, device="cuda")
+    pt = ctypes.c_void_p(wtr.data_ptr() + (-wtr.data_ptr()) % 256)
 
     def launch(stream):
         wt.copy_(src_t)
@@ -169,7 +172,7 @@ def test_processed_round_graph_replays_match_eager():
         for d in pds:
             assert sv.lib.sv_penalize(ctypes.byref(d), pp, npw, stream) == 0
         for d in tds:
-            assert sv.lib.sv_truncate(ctypes.byref(d), stream) == 0
+            assert sv.lib.sv_truncate(ctypes.byref(d), pt, ntw, stream) == 0
         assert sv.lib.sv_spec_accept(ctypes.byref(sd), ps, ws.numel() - 256, stream) == 0
 
     launch(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))

@@ -66,6 +66,30 @@ def test_truncate_parity(V, R, k, p):
         _assert_trunc(lg, T, ref, out, kept, "V=%d k=%d p=%g T=%g" % (V, kk, p, T))
 
 
+@pytest.mark.parametrize("V,R", [(16384, 3), (50257, 11), (128256, 40), (32000, 64)])
+def test_split_first_level_is_the_same(V, R):
+    """With a workspace, few rows spread their first level over many workgroups; the rows,
+    kept counts and the oracle's verdict are the same as without one.  Per-row values mix
+    top-k rows, top-p-alone rows and rows with no cut."""
+    lg = synth.logit_rows(V + 2 * R, R, V, 2.0)
+    g = np.random.default_rng(R)
+    ks = np.where(g.random(R) < 0.5, g.integers(1, 3000, R), 0).astype(np.int32)
+    ps = np.where(g.random(R) < 0.8, g.uniform(0.3, 0.999, R), 1.0).astype(np.float32)
+    for kw in (dict(k=50, p=0.9), dict(k=0, p=0.95), dict(k=7, p=1.0), dict(k=0, p=0.5),
+               dict(k=0, p=1.0, k_rows=ks, p_rows=ps)):
+        x = dev_array(lg)
+        args = dict(temperature=0.9, top_k=kw["k"], top_p=kw["p"],
+                    top_k_rows=None if "k_rows" not in kw else dev_array(kw["k_rows"]),
+                    top_p_rows=None if "p_rows" not in kw else dev_array(kw["p_rows"]))
+        o1, k1 = sv.sv_truncate(x, split=True, **args)
+        o0, k0 = sv.sv_truncate(x, split=False, **args)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o0) and torch.equal(k1, k0), kw
+        ref = oracle.truncate(lg, 0.9, top_k=kw["k"], top_p=kw["p"], top_k_rows=kw.get("k_rows"),
+                              top_p_rows=kw.get("p_rows"))
+        _assert_trunc(lg, 0.9, ref, o1.cpu().numpy(), k1.cpu().numpy(), "split V=%d R=%d %s" % (V, R, kw.get("k")))
+
+
 @pytest.mark.parametrize("V,R", [(5000, 300), (32000, 270)])
 def test_many_rows(V, R):
     """More rows than compute units: the 256-thread form of the kernel (fewer rows run the
