@@ -142,3 +142,17 @@ def test_processed_round(V, B, g):
     keep = ~near
     _assert_parity({kk: v[keep] for kk, v in ref.items() if v is not None},
                    {kk: v[keep] for kk, v in got.items() if v is not None}, "processed V=%d" % V)
+
+
+def test_full_batch_of_the_batched_chain():
+    """The batched chain's rows at full size (64 sequences, 320 target and 256 draft rows of
+    128256 logits) with a 4096-token history per sequence, as bench.py times them."""
+    cfg = synth.WORKLOADS[4]
+    a = synth.accept_inputs(4, B=cfg["B"], gamma=cfg["gamma"], V=cfg["V"], target_var=cfg["target_var"],
+                            noise_var=cfg["noise_var"], tau=cfg["tau"])
+    hist = np.random.default_rng(17).integers(0, cfg["V"], (cfg["B"], 4096)).astype(np.int32)
+    pen = dict(repetition=1.2, frequency=0.3, presence=0.2)
+    for name in ("target", "draft"):
+        ref = oracle.penalize(a[name], history=hist, drafts=a["draft_tokens"], **pen)
+        got = _gpu(a[name], hist, a["draft_tokens"], **pen)
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), name

@@ -194,3 +194,18 @@ def test_processed_round(V, B, g):
     ref_k = {kk: v[keep] for kk, v in ref.items() if v is not None}
     got_k = {kk: v[keep] for kk, v in got.items() if v is not None}
     _assert_parity(ref_k, got_k, "processed V=%d" % V)
+
+
+def test_full_batch_of_the_batched_chain():
+    """The batched chain's whole round at full size, in the configuration bench.py times: the
+    64 sequences' 320 target rows and 256 draft rows of 128256 logits, top-k 50 then top-p
+    0.9, and top-p 0.9 alone, every row against the oracle."""
+    cfg = synth.WORKLOADS[4]
+    a = synth.accept_inputs(4, B=cfg["B"], gamma=cfg["gamma"], V=cfg["V"], target_var=cfg["target_var"],
+                            noise_var=cfg["noise_var"], tau=cfg["tau"])
+    for name in ("target", "draft"):
+        lg = a[name].reshape(-1, cfg["V"])
+        for k, p in [(50, 0.9), (0, 0.9)]:
+            ref = oracle.truncate(lg, cfg["tau"], top_k=k, top_p=p)
+            out, kept = _gpu(lg, cfg["tau"], k, p)
+            _assert_trunc(lg, cfg["tau"], ref, out, kept, "batched chain %s k=%d p=%g" % (name, k, p))
