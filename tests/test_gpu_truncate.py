@@ -209,3 +209,14 @@ def test_full_batch_of_the_batched_chain():
             ref = oracle.truncate(lg, cfg["tau"], top_k=k, top_p=p)
             out, kept = _gpu(lg, cfg["tau"], k, p)
             _assert_trunc(lg, cfg["tau"], ref, out, kept, "batched chain %s k=%d p=%g" % (name, k, p))
+
+
+@pytest.mark.parametrize("T", [0.02, 0.3, 5.0, 50.0])
+def test_extreme_temperatures(T):
+    """Very sharp and very flat weights: at T = 0.02 nearly every token weighs 0 at 2^-62 and
+    the cut sits among the first few; at T = 50 the weights are nearly uniform."""
+    lg = synth.logit_rows(21, 12, 32000, 4.0)
+    for k, p in [(0, 0.9), (40, 0.95), (0, 0.5), (3000, 0.999)]:
+        ref = oracle.truncate(lg, T, top_k=k, top_p=p)
+        out, kept = _gpu(lg, T, k, p)
+        _assert_trunc(lg, T, ref, out, kept, "T=%g k=%d p=%g" % (T, k, p))
