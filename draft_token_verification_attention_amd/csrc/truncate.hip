@@ -7,17 +7,18 @@
 // ways to lose exactness without noticing" (the q of the ratio must be the draft's own
 // truncated distribution, not its logits before truncation).
 //
-// One block per row.  Tokens are ordered by (logit descending, token id ascending), i.e. by a
-// unique 56-bit composite C = (order-preserving key of the logit) << 24 | (2^24 - 1 - id),
-// descending.  Both cuts keep a prefix of that order, so the kept set is {C >= C*} for one
-// threshold token C*, found by a radix select: LDS histograms of one digit of C at a time
-// (11, 11, 10, 8, 8, 8 bits for counts, 10, 10, 10, 10, 8, 8 for masses), each walked from
-// the top to the bin where the running count (top-k) or mass (top-p) reaches its target.  Levels run over the row until the tokens left
-// in the crossing bin number at most kCap; one more pass gathers them into LDS (and writes
+// One workgroup per row (256 threads, or 1024 when there are few rows).  Tokens are ordered
+// by (logit descending, token id ascending), i.e. by a unique 56-bit composite C = (order-
+// preserving key of the logit) << 24 | (2^24 - 1 - id), descending.  Both cuts keep a prefix
+// of that order, so the kept set is {C >= C*} for one threshold token C*, found by a radix
+// select: LDS histograms of one digit of C at a time (11, 11, 10, 8, 8, 8 bits for counts;
+// 10, 10, 10, 10, 8, 8 for masses), each walked from the top to the bin where the running
+// count (top-k) or mass (top-p) reaches its target.  Levels run over the row until the
+// crossing bin holds at most kCap tokens; one more pass gathers them into LDS (and writes
 // every other token's output), and the remaining levels run on that list.  Top-p's first
 // levels bin tokens by their weight instead (16 bins per factor of two, then 1024 sub-bins
-// of each), which spreads them over many more bins than the logit's leading bits do.  LDS stays under 48 KB, so three rows
-// run on each compute unit at once.
+// of each), which spreads them over many more bins than the logit's leading bits do.  LDS
+// stays under 48 KB for 256 threads, so three rows run on each compute unit at once.
 //
 // A few rows leave most of the chip idle, so with a workspace the first level of every row
 // (the row max, the first key digit's counts for top-k, the first weight level for top-p
