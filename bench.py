@@ -320,9 +320,9 @@ def time_penalize(sv, base, toks, hist_tokens, steps, sh, dev):
                 raise RuntimeError("penalize launch failed")
     ms = median_event_ms(call, steps, sh)
     nrows = sum(r.shape[0] * r.shape[1] for r in rows.values())
-    return {"kernel_ms": round(ms, 5), "rows": nrows, "history_tokens": hist_tokens, "launches": 8,
-            "bound": "scattered logits (four dependent launches per call; about one read and write of a "
-                     "logit per distinct history token per row)"}
+    return {"kernel_ms": round(ms, 5), "rows": nrows, "history_tokens": hist_tokens, "launches": 4,
+            "bound": "scattered logits (two dependent launches per call: the history counted in LDS, then "
+                     "about one read and write of a logit per distinct history token per row)"}
 
 
 def time_commit(sv, k, v, kv_off, prefix, acc_len, path, n_q, Hkv, D, kv_sh, kv_st, kv_sb, esize, steps, sh, dev):

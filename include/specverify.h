@@ -448,11 +448,11 @@ SV_API sv_status sv_truncate(const sv_trunc_desc *desc, void *workspace, size_t 
 /*                NULL: hist_stride each                                                   */
 /*   draft_tokens optional device int32 [B][n_drafts]                                     */
 /*   Entries outside [0, V) are skipped.  repetition 1, frequency 0, presence 0: no change. */
-/* Work is proportional to the history's distinct tokens times the rows, not to V (the   */
-/* workspace holds, after the counter region, a count over the vocabulary and a list of  */
-/* distinct tokens per sequence: 4 V + 4 hist_stride bytes each; the call reads only      */
-/* entries it wrote first, so it shares a workspace with the other entry points like     */
-/* they do).                                                                              */
+/* Work is proportional to the history's distinct tokens times the rows, not to V.  Up to */
+/* 8192 history entries per sequence they are counted in LDS; beyond, in a count over the */
+/* vocabulary in the workspace (4 V + 4 hist_stride bytes per sequence).  The call reads  */
+/* only workspace entries it wrote first, so it shares a workspace with the other entry   */
+/* points as they do.                                                                      */
 /* Errors: B, n_rows or hist_stride negative, V < 1, repetition not in (0, inf),          */
 /*   frequency or presence not finite, or (rows > 0) a null logits -> SV_ERR_INVALID_ARG; */
 /*   n_drafts > 64, B > 32768 or more than 65535 chunks of 1024 history entries ->        */

@@ -1,7 +1,8 @@
 """GPU parity of sv_penalize (repetition, frequency, presence; drafted prefix as context)
 against oracle.penalize: bit-exact rows (both sides evaluate the same fp64 expression and
-round once).  Cases: vocabularies up to 128256, histories from empty to several 1024-entry
-chunks with repeats and out-of-range entries, per-sequence history lengths (0, clamped,
+round once).  Cases: vocabularies up to 128256, histories from empty to 20000 entries (both
+ways of counting: in LDS up to 8192 entries, in a vocabulary-sized array beyond) with repeats
+and out-of-range entries, per-sequence history lengths (0, clamped,
 negative), drafts from none to 64, one workspace across calls (left zero), bad arguments,
 and the whole processed round: penalties, top-k / top-p, then the acceptance, against the
 oracle's same three steps.
@@ -48,7 +49,8 @@ PENS = [dict(repetition=1.3), dict(repetition=1.0, frequency=0.4, presence=0.3),
 
 
 @pytest.mark.parametrize("V,B,H,g", [(7, 8, 12, 4), (1000, 16, 300, 5), (32000, 8, 2500, 4), (128256, 4, 5000, 16),
-                                     (128256, 2, 0, 64), (5000, 4, 1024, 0), (5000, 4, 1025, 1)])
+                                     (128256, 2, 0, 64), (5000, 4, 1024, 0), (5000, 4, 1025, 1),
+                                     (32000, 3, 8192, 4), (32000, 3, 8193, 4), (128256, 2, 20000, 8)])
 def test_penalize_parity(V, B, H, g):
     n = g + 1 if g else 3
     lg, hist, drafts = _inputs(V + H + g, B, n, V, H, g)
@@ -75,9 +77,9 @@ def test_one_workspace_across_calls():
     share one explicit workspace."""
     import ctypes
     pen = dict(repetition=1.4, frequency=0.2, presence=0.1)
-    ws = torch.zeros(8 << 20, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(16 << 20, dtype=torch.uint8, device="cuda")
     for seed, B, V, H in [(1, 5, 4000, 800), (2, 5, 4000, 3000), (3, 3, 9000, 2500), (4, 7, 1500, 0),
-                          (5, 2, 20000, 5000), (6, 5, 4000, 2048)]:
+                          (5, 2, 20000, 5000), (6, 5, 4000, 2048), (7, 2, 30000, 9000), (8, 4, 4000, 1200)]:
         ws[128 * 1024:].random_(0, 256)
         lg, hist, drafts = _inputs(seed, B, 4, V, H, 3, spread=V)
         ref = oracle.penalize(lg, history=hist, drafts=drafts, **pen)
