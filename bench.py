@@ -696,8 +696,8 @@ def bench_tree(args, cfg, wl, dev, steps, warmup, cpu):
 # bytes of a plain copy of known size on this GPU) from the rocprofv3 --pmc runs summarized
 # under profiles/, with the SHA-256 of the attention source they were taken on: a changed
 # kernel reports null until the counters are taken again.  "attention" = main + combine.
-TRAFFIC = {4: {"main": 1103936022, "attention": 1114314492}, 2: {"main": 18288963, "attention": 19519876},
-           3: {"main": 13266282, "attention": 17991613}, 5: {"main": 779181154, "attention": 779181154}}
+TRAFFIC = {4: {"main": 1103941555, "attention": 1114320016}, 2: {"main": 18289034, "attention": 19519946},
+           3: {"main": 13266282, "attention": 17991608}, 5: {"main": 779251478, "attention": 779251478}}
 TRAFFIC_SRC_SHA256 = "b781ff54a5bedc1838dda041d566183f866cf24a951f570b44b6966150dc731d"
 
 
