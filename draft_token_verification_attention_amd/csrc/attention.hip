@@ -43,7 +43,7 @@ constexpr int kMaxTiles = 1024;  // tiles per split (split_keys <= 32768)
 constexpr int kMaxSplits = 64;   // key splits per sequence
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
-constexpr float kLazyLog2 = 8.0f;  // online softmax: largest unrescaled weight is 2^8
+constexpr float kPsumMax = 65536.0f;  // online softmax: largest weight against a stale reference
 
 struct AttnArgs {
     const void *q;
@@ -109,11 +109,34 @@ __device__ __forceinline__ float half_swap_sum(float x)
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ __forceinline__ bool node_visible(const AttnArgs &a, const uint32_t *bits_row, int i, int j)
+// Bit k of the result: key t0 + k is visible to the lane's row (query i).  Keys before P
+// (the cached prefix) are visible to every row; keys at or past T are not; a new token
+// j = t - P is visible when j <= i (chain) or when bit j of the row's tree mask is set (tree).
+// Rows past the last (padding, never stored) see every key before T.  t0 < T.
+__device__ __forceinline__ uint32_t tile_visibility(const AttnArgs &a, const uint32_t *bits_row, bool row_ok, int i,
+                                                    int t0, int P, int T)
 {
-    // j = position among the new tokens (0 <= j < n_q)
-    if (a.tree) return (bits_row[j >> 5] >> (j & 31)) & 1u;
-    return j <= i;
+    const int nvalid = T - t0;
+    const uint32_t valid = nvalid >= 32 ? 0xffffffffu : ((1u << nvalid) - 1u);
+    if (!row_ok) return valid;
+    const int j0 = t0 - P;  // new-token index of the tile's first key (negative: prefix keys)
+    const uint32_t pre = j0 >= 0 ? 0u : (j0 <= -32 ? 0xffffffffu : ((1u << -j0) - 1u));
+    uint32_t node;
+    if (!a.tree) {
+        // keys with j0 + k <= i
+        const int last = i - j0;
+        node = last < 0 ? 0u : (last >= 31 ? 0xffffffffu : ((2u << last) - 1u));
+    } else if (j0 >= 0) {
+        // bits j0 .. j0 + 31 of the row's mask (the words past its end read as 0)
+        const int w = j0 >> 5, sh = j0 & 31;
+        const uint32_t lo = bits_row[w];
+        const uint32_t hi = (w + 1 < a.words) ? bits_row[w + 1] : 0u;
+        node = sh ? ((lo >> sh) | (hi << (32 - sh))) : lo;
+    } else {
+        // bits 0 .. 31 + j0 of the row's mask, placed at k = -j0 ...
+        node = j0 <= -32 ? 0u : (bits_row[0] << -j0);
+    }
+    return valid & (pre | node);
 }
 
 // ---------------------------------------------------------------------------
@@ -292,10 +315,12 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
     uint32_t voff[NI];
 #pragma unroll
     for (int j = 0; j < NI; ++j) voff[j] = 2u * ((uint32_t)(ld_key0 + j * KPI) * (uint32_t)a.kv_st + 8u * ld_dc);
+    int t0_cur = 0;  // several row waves: start of the tile loaded last (read from the list once)
     auto issue_loads = [&](int it) {
         const int li = it * NWK + wk;
         if (li < count) {
             const int t0 = tile_start(li);
+            if constexpr (!kDecode) t0_cur = t0;
             const char *kb = reinterpret_cast<const char *>(kbase + (int64_t)t0 * a.kv_st);
             const char *vb = reinterpret_cast<const char *>(vbase + (int64_t)t0 * a.kv_st);
             const int lim = T - 1 - t0;  // >= 0: every tile starts inside the cache
@@ -384,80 +409,98 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
             }
         }
         if (!kDecode) __syncthreads();
+        const int t0 = kDecode ? tile_start(li) : t0_cur;
         if (it + 1 < my_iters) issue_loads(it + 1);
         if (!have) continue;
-        const int t0 = tile_start(li);
 
-        // S^T (32 keys x 32 rows) = K (keys x d) . Q^T (d x rows).  One row wave: two
-        // independent MFMA chains over the even and odd d chunks (half the dependent-MFMA
-        // latency on a latency-bound path); several: one chain (other waves hide its latency,
-        // and the 16 adds that join two chains are VALU time the MFMA-bound path lacks)
-        constexpr bool kTwoChains = kDecode;
-        f32x16 sacc, sacc1;
+        // S^T (32 keys x 32 rows) = K (keys x d) . Q^T (d x rows), masked, into sv.  It reads
+        // K from LDS only, so it can run again while the tile is there.
+        auto scores = [&](float (&sv)[16]) {
+            // One row wave: two independent MFMA chains over the even and odd d chunks (half the dependent-MFMA
+            // latency on a latency-bound path); several: one chain (other waves hide its latency,
+            // and the 16 adds that join two chains are VALU time the MFMA-bound path lacks)
+            constexpr bool kTwoChains = kDecode;
+            f32x16 sacc, sacc1;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            sacc[v] = 0.0f;
-            sacc1[v] = 0.0f;
-        }
-#pragma unroll
-        for (int c = 0; c < NKC; c += 2) {
-            const bf16x8 kf0 = *reinterpret_cast<const bf16x8 *>(gK + l32 * KROW + (16 * c + 8 * h) * 2);
-            const bf16x8 kf1 = *reinterpret_cast<const bf16x8 *>(gK + l32 * KROW + (16 * c + 16 + 8 * h) * 2);
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0, qf[c], sacc, 0, 0, 0);
-            if constexpr (kTwoChains)
-                sacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf1, qf[c + 1], sacc1, 0, 0, 0);
-            else
-                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf1, qf[c + 1], sacc, 0, 0, 0);
-        }
-        if constexpr (kTwoChains) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) sacc[v] += sacc1[v];
-        }
-        // lane (row l32, half h) holds keys 8*(v/4) + 4*h + v%4.  The row max is taken on the
-        // raw scores (scale > 0) and the scale is folded into the exponent's FMA.
-        float sv[16];
-        const bool need_mask = (t0 + kTileKeys > P);
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            float x = sacc[v];
-            if (need_mask) {
-                const int t = t0 + 8 * (v >> 2) + 4 * h + (v & 3);
-                bool vis = t < T;
-                if (vis && t >= P && row_ok) vis = node_visible(a, my_bits, my_i, t - P);
-                if (!vis) x = -INFINITY;
+            for (int v = 0; v < 16; ++v) {
+                sacc[v] = 0.0f;
+                sacc1[v] = 0.0f;
             }
-            sv[v] = x;
-        }
-        float mloc = sv[0];
 #pragma unroll
-        for (int v = 1; v < 16; ++v) mloc = fmaxf(mloc, sv[v]);
-        mloc = half_swap_max(mloc);  // the row's other 16 keys sit in lane l ^ 32
-        // Lazy reference: the running max m_run (log2 units) moves only when a tile's row max
-        // passes it by more than kLazyLog2, so most tiles skip the accumulator rescale; weights
-        // against the stale reference stay below 2^kLazyLog2 (exact in the final l and O).
-        const float m_tile = mloc * a.scale_log2;
-        const float m_new = (m_tile <= m_run + kLazyLog2) ? m_run : m_tile;
-        // Branch-free: a row with no visible key yet (m_new = -inf) subtracts 0 instead, so
-        // its weights are exp2(-inf) = 0 and its alpha 0 (l and O are still zero there); a
-        // branch made the compiler zero all 16 weights ahead of it on every tile.
-        const float m_sub = (m_new == -INFINITY) ? 0.0f : m_new;
-        const float alpha = exp2_fast(m_run - m_sub);  // m_run == -inf gives 0
+            for (int c = 0; c < NKC; c += 2) {
+                const bf16x8 kf0 = *reinterpret_cast<const bf16x8 *>(gK + l32 * KROW + (16 * c + 8 * h) * 2);
+                const bf16x8 kf1 = *reinterpret_cast<const bf16x8 *>(gK + l32 * KROW + (16 * c + 16 + 8 * h) * 2);
+                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0, qf[c], sacc, 0, 0, 0);
+                if constexpr (kTwoChains)
+                    sacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf1, qf[c + 1], sacc1, 0, 0, 0);
+                else
+                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf1, qf[c + 1], sacc, 0, 0, 0);
+            }
+            if constexpr (kTwoChains) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) sacc[v] += sacc1[v];
+            }
+            // lane (row l32, half h) holds keys 8*(v/4) + 4*h + v%4 of the tile
+            if (t0 + kTileKeys > P) {
+                // the tile reaches the new tokens (or the end of the cache): one visibility word
+                // for the lane's row, then a select per score
+                // (shifted by the lane's half first, so each score's bit sits at a constant)
+                const uint32_t vis = tile_visibility(a, my_bits, row_ok, my_i, t0, P, T) >> (4 * h);
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    sv[v] = (vis & (1u << (8 * (v >> 2) + (v & 3)))) ? sacc[v] : -INFINITY;
+            } else {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) sv[v] = sacc[v];
+            }
+        };
+        float sv[16];
+        scores(sv);
+        // Online softmax against a reference m_run (log2 units) that moves only when it must.
+        // Weights are taken against the current reference first; while every lane's 16 weights
+        // sum to at most kPsumMax (a finite sum: the reference is set and no weight overflowed),
+        // they stand, and the tile costs no row max and no rescale.  Otherwise (a row's first
+        // visible keys, or scores far above the reference) the row max of the tile is taken
+        // on the raw scores (scale > 0), the reference moves to it, the weights are taken again
+        // and the accumulators rescaled.  Every weight stands at most kPsumMax, and the result
+        // does not depend on where the reference sits (exact in the final l and O).
         float p[16];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) p[v] = exp2_fast(fmaf(sv[v], a.scale_log2, -m_sub));
-        float psum = 0.0f;
+        for (int v = 0; v < 16; ++v) p[v] = exp2_fast(fmaf(sv[v], a.scale_log2, -m_run));
+        float psum = p[0];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) psum += p[v];
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-        // rescale the accumulators only when some row's running max moved (never needed on
-        // a wave's first tile, where they are still zero)
-        if (it > 0 && __ballot(alpha != 1.0f)) {
+        for (int v = 1; v < 16; ++v) psum += p[v];
+        if (__ballot(!(psum <= kPsumMax))) {
+            // the scores again, from LDS (the memory clobber keeps the compiler from holding
+            // the first pass's K fragments live through the weights instead)
+            asm volatile("" ::: "memory");
+            scores(sv);
+            float mloc = sv[0];
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
+            for (int v = 1; v < 16; ++v) mloc = fmaxf(mloc, sv[v]);
+            mloc = half_swap_max(mloc);  // the row's other 16 keys sit in lane l ^ 32
+            const float m_new = fmaxf(m_run, mloc * a.scale_log2);
+            // a row with no visible key yet (m_new = -inf) subtracts 0 instead, so its weights
+            // are exp2(-inf) = 0 and its alpha 0 (l and O are still zero there)
+            const float m_sub = (m_new == -INFINITY) ? 0.0f : m_new;
+            const float alpha = exp2_fast(m_run - m_sub);  // m_run == -inf gives 0
 #pragma unroll
-                for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
+            for (int v = 0; v < 16; ++v) p[v] = exp2_fast(fmaf(sv[v], a.scale_log2, -m_sub));
+            psum = 0.0f;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) psum += p[v];
+            l_run *= alpha;
+            m_run = m_new;
+            // rescale the accumulators only when some row's reference moved (never needed on
+            // a wave's first tile, where they are still zero)
+            if (it > 0 && __ballot(alpha != 1.0f)) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) oacc[db][v] *= alpha;
+            }
         }
+        l_run += psum;
 
         // P^T as the B operand: k index 8*h + j <-> key 16*c + 8*(j/4) + 4*h + j%4
         bf16x8 pb[2];
