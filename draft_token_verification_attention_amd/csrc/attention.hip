@@ -263,6 +263,31 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
     }
     if (!kDecode && wave == 0) {
         const int ntile = (kend - kstart + kTileKeys - 1) / kTileKeys;
+        // Tree: the OR of the block's node rows over the mask words that cover the split's
+        // new tokens, into LDS (the tile buffers, not in use yet).  Lanes take words; each
+        // lane's rows go in batches of independent loads.
+        uint32_t *or_w = reinterpret_cast<uint32_t *>(smem);
+        const int jbeg = max(kstart - P, 0);  // the split's first new token
+        const int jend = min(kend, T) - P;    // one past its last (<= jbeg: none)
+        const int w0 = jbeg >> 5;
+        const int nw = jend > jbeg ? ((jend - 1) >> 5) - w0 + 1 : 0;
+        if (a.tree) {
+            for (int wl = lane; wl < nw; wl += 64) {
+                const uint32_t *col = bits_b + w0 + wl;
+                uint32_t acc = 0u;
+                int i = i_lo;
+                for (; i + 8 <= i_hi + 1; i += 8) {
+                    uint32_t v[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) v[u] = col[(int64_t)(i + u) * a.words];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) acc |= v[u];
+                }
+                for (; i <= i_hi; ++i) acc |= col[(int64_t)i * a.words];
+                or_w[wl] = acc;
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
         int count = 0;
         for (int t0i = 0; t0i < ntile; t0i += 64) {
             const int tt = t0i + lane;
@@ -276,16 +301,14 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
                     if (!a.tree) {
                         inc = j0 <= i_hi;
                     } else {
+                        // new tokens j0 .. jl, all inside the words or_w holds
                         const int jl = min(j0 + kTileKeys, a.n_q) - 1;
-                        for (int i = i_lo; i <= i_hi && !inc; ++i) {
-                            const uint32_t *br = bits_b + (int64_t)i * a.words;
-                            for (int w = j0 >> 5; w <= (jl >> 5) && !inc; ++w) {
-                                uint32_t word = br[w];
-                                const int lo = max(j0 - 32 * w, 0), hi = min(jl - 32 * w, 31);
-                                const uint32_t m_hi = hi == 31 ? 0xffffffffu : ((1u << (hi + 1)) - 1u);
-                                const uint32_t m_lo = ~((1u << lo) - 1u);
-                                if (word & m_hi & m_lo) inc = true;
-                            }
+                        for (int w = j0 >> 5; w <= (jl >> 5); ++w) {
+                            const uint32_t word = or_w[w - w0];
+                            const int lo = max(j0 - 32 * w, 0), hi = min(jl - 32 * w, 31);
+                            const uint32_t m_hi = hi == 31 ? 0xffffffffu : ((1u << (hi + 1)) - 1u);
+                            const uint32_t m_lo = ~((1u << lo) - 1u);
+                            if (word & m_hi & m_lo) inc = true;
                         }
                     }
                 }
@@ -416,9 +439,10 @@ __global__ __launch_bounds__(64 * NWR * NWK, 2) void attn_bf16_kernel(AttnArgs a
         // S^T (32 keys x 32 rows) = K (keys x d) . Q^T (d x rows), masked, into sv.  It reads
         // K from LDS only, so it can run again while the tile is there.
         auto scores = [&](float (&sv)[16]) {
-            // One row wave: two independent MFMA chains over the even and odd d chunks (half the dependent-MFMA
-            // latency on a latency-bound path); several: one chain (other waves hide its latency,
-            // and the 16 adds that join two chains are VALU time the MFMA-bound path lacks)
+            // One row wave: two independent MFMA chains over the even and odd d chunks (half
+            // the dependent-MFMA latency on a latency-bound path); several: one chain (other
+            // waves hide its latency, and the 16 adds that join two chains are VALU time the
+            // MFMA-bound path lacks)
             constexpr bool kTwoChains = kDecode;
             f32x16 sacc, sacc1;
 #pragma unroll
