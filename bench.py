@@ -696,9 +696,9 @@ def bench_tree(args, cfg, wl, dev, steps, warmup, cpu):
 # bytes of a plain copy of known size on this GPU) from the rocprofv3 --pmc runs summarized
 # under profiles/, with the SHA-256 of the attention source they were taken on: a changed
 # kernel reports null until the counters are taken again.  "attention" = main + combine.
-TRAFFIC = {4: {"main": 1103941555, "attention": 1114320016}, 2: {"main": 18289034, "attention": 19519946},
-           3: {"main": 13266282, "attention": 17991608}, 5: {"main": 779251478, "attention": 779251478}}
-TRAFFIC_SRC_SHA256 = "b781ff54a5bedc1838dda041d566183f866cf24a951f570b44b6966150dc731d"
+TRAFFIC = {4: {"main": 1103898985, "attention": 1114277451}, 2: {"main": 18266520, "attention": 19497433},
+           3: {"main": 13293945, "attention": 18005963}, 5: {"main": 776411919, "attention": 776411919}}
+TRAFFIC_SRC_SHA256 = "cddca2311b8641110dedd77cff0e8e99da8285ac331851d8c33dc49833f8a5c7"
 
 
 def measured_traffic(wl):
