@@ -346,3 +346,59 @@ def test_deterministic_repeats():
     for _ in range(5):
         o, l = attention_on_gpu(inp, 0.088)
         assert np.array_equal(o, first) and np.array_equal(l, fl)
+
+
+# --------------------------------------------------------------------------------------
+# Score profiles that move the online softmax's reference: each query's first dimension is 1
+# and key t's first dimension is profile(t), the rest small noise, so that (scale 1) the
+# scores follow the profile.  Rising scores pass the reference by more than 16 in log2
+# units on every tile (a new reference each tile); a sink or falling scores leave every
+# later weight far below it (underflow to 0); a slow ramp and a sawtooth mix tiles that keep
+# the reference with tiles that move it.
+PROFILES = {
+    "rising": lambda t: 0.38 * t,  # 17.5 in log2 units per 32-key tile
+    "sink": lambda t: np.where(t == 0, 40.0, 0.0),
+    "falling": lambda t: -0.38 * t,
+    "ramp": lambda t: 0.05 * t,
+    "sawtooth": lambda t: 30.0 * ((t // 300) % 2),
+    # rising for 3000 keys, then flat (long caches: scores stay near 1e3, where the fp32
+    # score's own rounding stays well inside the log-sum-exp bound)
+    "rising_flat": lambda t: 0.38 * np.minimum(t, 3000),
+}
+
+
+def _profile_inputs(seed, profile, P, n_q, Hq, Hkv, D=128):
+    inp = synth.attention_inputs(seed, B=1, n_q=n_q, Hq=Hq, Hkv=Hkv, D=D, prefix_len=[P], dtype="f32",
+                                 qkv_scale=0.1)
+    T = P + n_q
+    q = inp["q"].reshape(1, n_q, Hq, D).copy()
+    k = inp["k"].reshape(T, Hkv, D).copy()
+    v = synth.normal(seed, "misc", (T, Hkv, D))
+    q[..., 0] = 1.0
+    k[:, :, 0] = PROFILES[profile](np.arange(T, dtype=np.float64))[:, None]
+    return dict(inp, q=synth.to_bf16_bits(q), k=synth.to_bf16_bits(k).reshape(-1),
+                v=synth.to_bf16_bits(v).reshape(-1), dtype="bf16")
+
+
+@pytest.mark.parametrize("profile", ["rising", "sink", "falling", "ramp", "sawtooth"])
+@pytest.mark.parametrize("split_keys", [0, 512])
+def test_softmax_reference_moves_chain(profile, split_keys):
+    inp = _profile_inputs(31, profile, 3000, 5, 8, 2)
+    _compare(inp, 1.0, split_keys=split_keys)
+
+
+@pytest.mark.parametrize("profile", ["rising", "sink", "sawtooth"])
+def test_softmax_reference_moves_tree(profile):
+    n, P = 40, 1200
+    bits = oracle.tree_mask(synth.random_tree(41, n, branch_p=0.6), P)[0]
+    inp = _profile_inputs(32, profile, P, n, 16, 4)
+    _compare(inp, 1.0, tree_bits=bits, split_keys=256)
+
+
+@pytest.mark.parametrize("profile", ["rising_flat", "ramp", "sawtooth"])
+def test_softmax_reference_moves_many_rows(profile):
+    """A long cache and several hundred rows: the 128-row-block kernel."""
+    n, P = 100, 7000
+    bits = oracle.tree_mask(synth.random_tree(42, n, branch_p=0.5), P)[0]
+    inp = _profile_inputs(33, profile, P, n, 32, 8)
+    _compare(inp, 1.0, tree_bits=bits, rows=rows_of_sample(inp, 300))
