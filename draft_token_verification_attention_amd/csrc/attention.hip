@@ -900,10 +900,12 @@ static bool plan_attention(const sv_attn_desc *d, int cu_count, Plan &p)
         if ((groups >= 64 && Tmax > 2048) || (groups >= 32 && Tmax >= 4096)) sk = sk < 1024 ? 1024 : sk;
         if (groups >= 64 && Tmax <= 2048) sk = (Tmax + unit - 1) / unit * unit;
     } else {
-        // Many rows per block: a partial (32 NWR rows x D, and a (max, sum) pair per row, written and read back)
-        // cost about as much as the K/V of 130 keys in fp32, so a short cache splits only until
-        // every CU has a block, and never below 256 keys (measured on the 64-node Medusa
-        // tree, 2048-key cache: 128-key splits 54 us per round, 256-key 45 us, 512-key 47 us).
+        // Many rows per block: a partial (32 NWR rows x D, and a (max, sum) pair per row,
+        // written and read back) costs about as much as the K/V of 130 keys in fp32, so a short
+        // cache splits only as far as one block per CU, and never below 256 keys.  A CU given
+        // two such blocks runs each at well under half speed: on the 64-node Medusa tree
+        // (2048-key cache, 40 row-tile groups), 7 splits of 320 keys (280 blocks) take 15.8 us,
+        // 6 of 384 (240 blocks) 13.9 us, 11 of 192 (440 blocks) 16.5 us.
         // Long caches split further, to about four blocks per CU with splits of at least
         // 1024 keys (their blocks otherwise walk thousands of tiles one after another).
         // Measured on random trees with a 16384-key cache, 516 / 1028 / 2052 / 4100 rows:
@@ -916,7 +918,8 @@ static bool plan_attention(const sv_attn_desc *d, int cu_count, Plan &p)
         if (groups >= target) {
             sk = Tmax;
         } else {
-            const int64_t nsp = (target + groups - 1) / groups;
+            // long caches: at least `target` blocks; short ones: at most one per CU
+            const int64_t nsp = long_cache ? (target + groups - 1) / groups : target / groups;
             sk = (Tmax + nsp - 1) / nsp;
         }
         sk = (sk + unit - 1) / unit * unit;
