@@ -696,9 +696,9 @@ def bench_tree(args, cfg, wl, dev, steps, warmup, cpu):
 # bytes of a plain copy of known size on this GPU) from the rocprofv3 --pmc runs summarized
 # under profiles/, with the SHA-256 of the attention source they were taken on: a changed
 # kernel reports null until the counters are taken again.  "attention" = main + combine.
-TRAFFIC = {4: {"main": 1103898985, "attention": 1114277451}, 2: {"main": 18266520, "attention": 19497433},
-           3: {"main": 13293945, "attention": 18005963}, 5: {"main": 776411919, "attention": 776411919}}
-TRAFFIC_SRC_SHA256 = "cddca2311b8641110dedd77cff0e8e99da8285ac331851d8c33dc49833f8a5c7"
+TRAFFIC = {4: {"main": 1103885330, "attention": 1114263805}, 2: {"main": 18266437, "attention": 19497351},
+           3: {"main": 12744744, "attention": 16869074}, 5: {"main": 776450927, "attention": 776450927}}
+TRAFFIC_SRC_SHA256 = "be5e9837ae36c5764701e50d2eaff337c0a5c85e8fd5ebe50e596c69a51d279f"
 
 
 def measured_traffic(wl):
