@@ -432,7 +432,9 @@ __global__ __launch_bounds__(kRowThreads) void accept_alpha_kernel(AcceptArgs a,
 // ---------------------------------------------------------------------------
 // SAMPLE decide and residual draw.  Every block of sequence b: row statistics of the
 // 2 gamma + 1 rows, the ratio tests u_i q(x_i) < p(x_i) (all blocks reach the same J),
-// then the residual mass of its chunk of the rows at position J.
+// then the residual mass of its chunks of the rows at position J (chunks x, x + X, ... for
+// block x of X: a grid that fits on the GPU at once, each block taking the statistics and
+// the ratio tests once for several chunks).
 // ---------------------------------------------------------------------------
 // (two waves per SIMD: left unbounded, the large-chunk form takes more than 256 registers and
 // runs one wave per SIMD, 28 -> 35 us on the 64-sequence batch)
@@ -449,7 +451,7 @@ __global__ __launch_bounds__(kRowThreads, 2) void accept_resample_kernel(AcceptA
     __shared__ int last_flag, s_chunk, s_usep, s_seg0, firstbad, bad;
     __shared__ int s_whit[kRowThreads / kWave], s_wlast[kRowThreads / kWave];
     __shared__ double s_base, s_target, s_uextra;
-    const int c = blockIdx.x, b = blockIdx.y;
+    const int b = blockIdx.y;
     const int g = a.gamma;
     const int gb = gamma_of(a, b);  // this sequence's drafts (rows past them are not read)
 
@@ -495,7 +497,7 @@ __global__ __launch_bounds__(kRowThreads, 2) void accept_resample_kernel(AcceptA
     }
     __syncthreads();
     const int J = firstbad;
-    if (c == 0) {
+    if (blockIdx.x == 0) {
         int32_t *out = a.out_tokens + (int64_t)b * (g + 1);
         for (int i = threadIdx.x; i <= g; i += blockDim.x)
             if (i != J) out[i] = i < J ? a.tokens[(int64_t)b * g + i] : -1;
@@ -507,7 +509,6 @@ __global__ __launch_bounds__(kRowThreads, 2) void accept_resample_kernel(AcceptA
 
     const float *prow = a.target + ((int64_t)b * (g + 1) + J) * a.V;
     const float *qrow = J < gb ? a.draft + ((int64_t)b * g + J) * a.V : nullptr;
-    const int base = c * kChunk;
 
     // Weights of token e relative to the rows' maxima, in fp64 (exp2_acc):
     // wp = 2^((l_p(e) - Mp) k), wq likewise (0 with no draft row, J == gamma).  The residual is
@@ -528,51 +529,54 @@ __global__ __launch_bounds__(kRowThreads, 2) void accept_resample_kernel(AcceptA
     auto wp_of = [&](float l) { return exp2_acc(fma((double)l, a.kd, nMpk)); };
     auto wq_of = [&](float l) { return exp2_acc(fma((double)l, a.kd, nMqk)) * qmask; };
 
-    float xp[kPerThread], xq[kPerThread];
-    load_chunk2<VEC, kPerThread>(prow, qrow ? qrow : prow, base, a.V, xp, xq);
-    // branch-free: a position at or beyond V holds -inf, whose weight is 0.  Per thread, the
-    // sums of each float4 group (VEC layout: group k4 of wave w is part of the chunk's
-    // 256-token segment 4 k4 + w, in token order)
-    double ta = 0.0, tb = 0.0, tp = 0.0, tq = 0.0;
-    double a4[kPerThread / 4], b4[kPerThread / 4];
-#pragma unroll
-    for (int k4 = 0; k4 < kPerThread / 4; ++k4) {
-        a4[k4] = 0.0;
-        b4[k4] = 0.0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const double wp = wp_of(xp[4 * k4 + j]), wq = wq_of(xq[4 * k4 + j]);
-            tp += wp;
-            tq += wq;
-            const bool in = wp * iZp_est > wq * iZq_est;
-            a4[k4] += in ? wp : 0.0;
-            b4[k4] += in ? wq : 0.0;
-        }
-        ta += a4[k4];
-        tb += b4[k4];
-    }
-    if (VEC) {
-        const int wv = threadIdx.x / kWave;
-        double *sg = w.seg + 2 * (((int64_t)b * a.rnchunk + c) * kPerThread);
+    for (int c = blockIdx.x; c < a.rnchunk; c += gridDim.x) {
+        const int base = c * kChunk;
+        float xp[kPerThread], xq[kPerThread];
+        load_chunk2<VEC, kPerThread>(prow, qrow ? qrow : prow, base, a.V, xp, xq);
+        // branch-free: a position at or beyond V holds -inf, whose weight is 0.  Per thread, the
+        // sums of each float4 group (VEC layout: group k4 of wave w is part of the chunk's
+        // 256-token segment 4 k4 + w, in token order)
+        double ta = 0.0, tb = 0.0, tp = 0.0, tq = 0.0;
+        double a4[kPerThread / 4], b4[kPerThread / 4];
 #pragma unroll
         for (int k4 = 0; k4 < kPerThread / 4; ++k4) {
-            const double sa = wave_sum(a4[k4]), sb = wave_sum(b4[k4]);
-            if (threadIdx.x % kWave == 0) {
-                st_coherent(&sg[2 * (4 * k4 + wv)], sa);
-                st_coherent(&sg[2 * (4 * k4 + wv) + 1], sb);
+            a4[k4] = 0.0;
+            b4[k4] = 0.0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const double wp = wp_of(xp[4 * k4 + j]), wq = wq_of(xq[4 * k4 + j]);
+                tp += wp;
+                tq += wq;
+                const bool in = wp * iZp_est > wq * iZq_est;
+                a4[k4] += in ? wp : 0.0;
+                b4[k4] += in ? wq : 0.0;
+            }
+            ta += a4[k4];
+            tb += b4[k4];
+        }
+        if (VEC) {
+            const int wv = threadIdx.x / kWave;
+            double *sg = w.seg + 2 * (((int64_t)b * a.rnchunk + c) * kPerThread);
+#pragma unroll
+            for (int k4 = 0; k4 < kPerThread / 4; ++k4) {
+                const double sa = wave_sum(a4[k4]), sb = wave_sum(b4[k4]);
+                if (threadIdx.x % kWave == 0) {
+                    st_coherent(&sg[2 * (4 * k4 + wv)], sa);
+                    st_coherent(&sg[2 * (4 * k4 + wv) + 1], sb);
+                }
             }
         }
+        block_sum2(ta, tb, dscr);
+        block_sum2(tp, tq, dscr);
+        if (threadIdx.x == 0) {
+            ResPart *rp = &w.res[(int64_t)b * a.rnchunk + c];
+            st_coherent(&rp->a, ta);
+            st_coherent(&rp->b, tb);
+            st_coherent(&rp->wp, tp);
+            st_coherent(&rp->wq, tq);
+        }
     }
-    block_sum2(ta, tb, dscr);
-    block_sum2(tp, tq, dscr);
-    if (threadIdx.x == 0) {
-        ResPart *rp = &w.res[(int64_t)b * a.rnchunk + c];
-        st_coherent(&rp->a, ta);
-        st_coherent(&rp->b, tb);
-        st_coherent(&rp->wp, tp);
-        st_coherent(&rp->wq, tq);
-    }
-    if (!arrive_last(&w.cnt[b], a.rnchunk, &last_flag)) return;
+    if (!arrive_last(&w.cnt[b], gridDim.x, &last_flag)) return;
 
     // ---- last block: the exact normalizers, then the extra token ----
     const ResPart *rp = w.res + (int64_t)b * a.rnchunk;
@@ -1358,7 +1362,17 @@ static hipError_t launch_resample(const AcceptArgs &a0, const AcceptWs &w, hipSt
     AcceptArgs a = a0;
     constexpr int RP = (VEC && PER == 16) ? kResPer : 16;
     a.rnchunk = (a.V + RP * kRowThreads - 1) / (RP * kRowThreads);
-    return launch(accept_resample_kernel<VEC, RP>, dim3(a.rnchunk, a.B), s, a, w, lds);
+    // Blocks per sequence: as many as fit on the GPU at once, at most one per chunk.  On the
+    // 64-sequence batch (32 chunks per sequence), a block per chunk took 84 us per call, the
+    // resident grid 76 (its next chunk prefetched meanwhile: no better).
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, accept_resample_kernel<VEC, RP>, kRowThreads, lds) !=
+            hipSuccess || per_cu < 1)
+        per_cu = 2;
+    const int64_t resident = (int64_t)per_cu * device_cu_count();
+    const int64_t per_seq = resident / a.B;
+    const int gx = (int)(per_seq >= a.rnchunk ? a.rnchunk : per_seq < 1 ? 1 : per_seq);
+    return launch(accept_resample_kernel<VEC, RP>, dim3(gx, a.B), s, a, w, lds);
 }
 
 template <bool VEC, int PER>
