@@ -696,8 +696,8 @@ def bench_tree(args, cfg, wl, dev, steps, warmup, cpu):
 # bytes of a plain copy of known size on this GPU) from the rocprofv3 --pmc runs summarized
 # under profiles/, with the SHA-256 of the attention source they were taken on: a changed
 # kernel reports null until the counters are taken again.  "attention" = main + combine.
-TRAFFIC = {4: {"main": 1103885330, "attention": 1114263805}, 2: {"main": 18266437, "attention": 19497351},
-           3: {"main": 12744744, "attention": 16869074}, 5: {"main": 776450927, "attention": 776450927}}
+TRAFFIC = {4: {"main": 1103896940, "attention": 1114275402}, 2: {"main": 18266500, "attention": 19497412},
+           3: {"main": 12744809, "attention": 16869156}, 5: {"main": 776701781, "attention": 776701781}}
 TRAFFIC_SRC_SHA256 = "be5e9837ae36c5764701e50d2eaff337c0a5c85e8fd5ebe50e596c69a51d279f"
 
 
