@@ -698,7 +698,7 @@ def bench_tree(args, cfg, wl, dev, steps, warmup, cpu):
 # kernel reports null until the counters are taken again.  "attention" = main + combine.
 TRAFFIC = {4: {"main": 1103896940, "attention": 1114275402}, 2: {"main": 18266500, "attention": 19497412},
            3: {"main": 12744809, "attention": 16869156}, 5: {"main": 776701781, "attention": 776701781}}
-TRAFFIC_SRC_SHA256 = "be5e9837ae36c5764701e50d2eaff337c0a5c85e8fd5ebe50e596c69a51d279f"
+TRAFFIC_SRC_SHA256 = "0b9ba00c0096b37b8ac6ce277d2dcb6b22bb1040e333491abb568963757e6023"
 
 
 def measured_traffic(wl):

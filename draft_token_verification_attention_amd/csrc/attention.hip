@@ -15,7 +15,8 @@
 //     through LDS (coalesced 16-byte loads, the next tile in registers while the current
 //     one is computed), and each row wave of the group computes S^T = K Q^T and
 //     O^T += V^T P^T for its 32 rows on MFMA.
-//   * Online softmax in registers (log2 domain, lazily moved reference max).  Key groups
+//   * Online softmax in registers (log2 domain; the reference moves only when a row's
+//     weights against it could grow past 2^16).  Key groups
 //     merge through LDS; key splits are merged by attn_combine_kernel (log-sum-exp).
 //   * Tiles the mask hides from every row of the block are never loaded (tree nodes of
 //     other branches; chain positions after the block's last row).
