@@ -65,6 +65,16 @@ def test_sample_parity_shapes(V, gamma):
         _assert_parity(ref, got, "V=%d gamma=%d step=%d" % (V, gamma, step))
 
 
+@pytest.mark.parametrize("B,gamma,V", [(100, 3, 128256), (600, 2, 50257), (3, 4, 128256)])
+def test_residual_draw_grid_shapes(B, gamma, V):
+    """Residual-draw grids whose blocks take several chunks of a sequence's rows, evenly or
+    not: 100 sequences (3 or 4 chunks a block), 600 (every chunk of a sequence in one block),
+    and 3 (a block per chunk)."""
+    a = synth.accept_inputs(B + V, B=B, gamma=gamma, V=V, target_var=3.0, noise_var=1.0, tau=0.9)
+    ref, got = _run_both(SAMPLE, a["target"], a["draft"], a["draft_tokens"], 0.9, seed=5, step=0)
+    _assert_parity(ref, got, "B=%d gamma=%d V=%d" % (B, gamma, V))
+
+
 @pytest.mark.parametrize("V", [1, 3, 1000, 1023, 4097, 128256])
 @pytest.mark.parametrize("gamma", [1, 4, 64])
 def test_greedy_parity_shapes(V, gamma):
