@@ -900,6 +900,17 @@ static bool plan_attention(const sv_attn_desc *d, int cu_count, Plan &p)
         //   1024 keys 72.7 -> 47.8.  (B=2 and B=4 on 2048 keys lose with 1024-key splits.)
         if ((groups >= 64 && Tmax > 2048) || (groups >= 32 && Tmax >= 4096)) sk = sk < 1024 ? 1024 : sk;
         if (groups >= 64 && Tmax <= 2048) sk = (Tmax + unit - 1) / unit * unit;
+        // A grid that 256-key splits leave within the CUs (one sequence, a few): shorter
+        // splits, up to about three quarters of the CUs in blocks, at least 128 keys.  The 8B
+        // chain (8 KV heads, 4102 keys): 256-key splits 10.1 us, 224 9.8, 192 9.5, 160 9.6,
+        // 128 10.4 (more blocks than CUs).
+        if (groups * ((Tmax + 255) / 256) <= cu_count) {
+            const int64_t want = 3 * (int64_t)cu_count / 4;
+            int64_t s2 = (Tmax * groups + want - 1) / want;
+            s2 = (s2 + unit - 1) / unit * unit;
+            if (s2 < 128) s2 = 128;
+            if (s2 < sk) sk = s2;
+        }
     } else {
         // Many rows per block: a partial (32 NWR rows x D, and a (max, sum) pair per row,
         // written and read back) costs about as much as the K/V of 130 keys in fp32, so a short
