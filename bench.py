@@ -696,9 +696,9 @@ def bench_tree(args, cfg, wl, dev, steps, warmup, cpu):
 # bytes of a plain copy of known size on this GPU) from the rocprofv3 --pmc runs summarized
 # under profiles/, with the SHA-256 of the attention source they were taken on: a changed
 # kernel reports null until the counters are taken again.  "attention" = main + combine.
-TRAFFIC = {4: {"main": 1103896940, "attention": 1114275402}, 2: {"main": 18266500, "attention": 19497412},
-           3: {"main": 12744809, "attention": 16869156}, 5: {"main": 776701781, "attention": 776701781}}
-TRAFFIC_SRC_SHA256 = "0b9ba00c0096b37b8ac6ce277d2dcb6b22bb1040e333491abb568963757e6023"
+TRAFFIC = {4: {"main": 1103875984, "attention": 1114254469}, 2: {"main": 18523994, "attention": 20082557},
+           3: {"main": 12744732, "attention": 16869067}, 5: {"main": 779440131, "attention": 779440131}}
+TRAFFIC_SRC_SHA256 = "1da0c4c16669d3df29669342ac71374c7675655c3a0617a6cfe80a1f66b73ead"
 
 
 def measured_traffic(wl):
