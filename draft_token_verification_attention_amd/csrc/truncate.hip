@@ -7,7 +7,7 @@
 // ways to lose exactness without noticing" (the q of the ratio must be the draft's own
 // truncated distribution, not its logits before truncation).
 //
-// One workgroup per row (256 threads, or 1024 when there are few rows).  Tokens are ordered
+// One workgroup per row (256, 512 or 1024 threads: fewer rows, more).  Tokens are ordered
 // by (logit descending, token id ascending), i.e. by a unique 56-bit composite C = (order-
 // preserving key of the logit) << 24 | (2^24 - 1 - id), descending.  Both cuts keep a prefix
 // of that order, so the kept set is {C >= C*} for one threshold token C*, found by a radix
@@ -41,10 +41,13 @@ using namespace sv;
 typedef unsigned __int128 u128;
 
 // Threads per block: 1024 while there are at most as many rows as compute units (a row then
-// has a compute unit to itself), else 256 (three rows per compute unit).  Measured on rows of
-// 128256 logits, top-p 0.9: one row 203 -> 121 us, 256 rows 232 -> 152 us; 320 rows 280 us
+// has a compute unit to itself), 512 up to twice as many (two rows per compute unit), else
+// 256 (three rows per compute unit).  Measured on rows of 128256 logits, top-p 0.9: one row
+// 203 -> 121 us, 256 rows 232 -> 152 us with 1024 threads against 256; 320 rows 280 us
 // either way, and top-k 50 then top-p 0.9 on 320 rows 135 us with 256 threads, 164 with 1024.
-constexpr int kTrThreadsMany = 256, kTrThreadsFew = 1024;
+// 512 threads against 256, top-p 0.9: 320 rows 290 -> 242 us, 400 rows 310 -> 264, 512 rows
+// 352 -> 312 (top-k 50 then top-p 0.9: 2-3% faster).
+constexpr int kTrThreadsMany = 256, kTrThreadsMid = 512, kTrThreadsFew = 1024;
 constexpr int kMaxSplit = 64;             // chunks per row of the split first level
 constexpr int kSplitMinV = 16384;         // shorter rows are not split
 constexpr int kSplitAlign = 4096;         // chunk starts are multiples of this many tokens
@@ -930,6 +933,8 @@ extern "C" sv_status sv_truncate(const sv_trunc_desc *d, void *workspace, size_t
         hipLaunchKernelGGL(truncate_kernel<kTrThreadsFew>, dim3((unsigned)d->R), dim3(kTrThreadsFew), 0, s, a);
     } else if (d->R <= cus) {
         hipLaunchKernelGGL(truncate_kernel<kTrThreadsFew>, dim3((unsigned)d->R), dim3(kTrThreadsFew), 0, s, a);
+    } else if (d->R <= 2 * cus) {
+        hipLaunchKernelGGL(truncate_kernel<kTrThreadsMid>, dim3((unsigned)d->R), dim3(kTrThreadsMid), 0, s, a);
     } else {
         hipLaunchKernelGGL(truncate_kernel<kTrThreadsMany>, dim3((unsigned)d->R), dim3(kTrThreadsMany), 0, s, a);
     }

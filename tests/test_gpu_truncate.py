@@ -90,10 +90,11 @@ def test_split_first_level_is_the_same(V, R):
         _assert_trunc(lg, 0.9, ref, o1.cpu().numpy(), k1.cpu().numpy(), "split V=%d R=%d %s" % (V, R, kw.get("k")))
 
 
-@pytest.mark.parametrize("V,R", [(5000, 300), (32000, 270)])
+@pytest.mark.parametrize("V,R", [(5000, 300), (32000, 270), (128256, 400), (5000, 600), (32000, 1100)])
 def test_many_rows(V, R):
-    """More rows than compute units: the 256-thread form of the kernel (fewer rows run the
-    1024-thread form, which every other test here exercises)."""
+    """More rows than compute units: the 512-thread form of the kernel (up to twice as many
+    rows as compute units) and the 256-thread form (more); fewer rows run the 1024-thread
+    form, which every other test here exercises."""
     lg = synth.logit_rows(V + R, R, V, 3.0)
     for k, p in [(0, 0.9), (40, 0.9), (1000, 1.0), (2500, 0.95)]:
         ref = oracle.truncate(lg, 0.9, top_k=k, top_p=p)
